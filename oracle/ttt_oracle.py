@@ -1,0 +1,313 @@
+"""Plain, slow fp64 CPU oracle of the large-chunk test-time-training (TTT) layer forward.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+may import or run this module. It shares no code with the HIP library: the two meet only
+in the seeded input generator (``ttt_inputs``), which holds none of the layer's arithmetic.
+
+Sources (cited by page and section; the pages' own equation text did not survive
+extraction, so the formulas below are the plain forms the pages describe in words):
+
+* [LaCT] "LaCT技术解析：大块测试时训练提升长序列建模效率" (peacm.com):
+  §1.2 update once per large chunk of 2K-1M tokens; "key implementation tricks":
+  a SwiGLU-MLP fast-weight net updated with Muon; §2.1 the TTT layer's two phases --
+  update (the chunk's summed gradient moves the fast weights, eqs. 4-5) and apply (the
+  fast weights are applied to every query of the chunk, eq. 2); §2.2.1 L2 weight
+  normalisation of the fast weights (eq. 8) and Muon turning the gradient into an
+  orthogonal matrix by approximate SVD (eqs. 9-10); §3.2 shifted block-causal mask
+  (Fig. 3c) for text; §3.1 one whole-sequence chunk for image sets.
+* [TTT layers] "Что такое Test-Time Training (TTT) слои" (aivaro.ru): §3 the per-step
+  recurrence theta_t = theta_{t-1} - eta * grad L, output h_t = f_theta(x_t), an MSE
+  self-supervised loss; §4 a 2-layer MLP inner model trained by SGD; §10 the scalar
+  sine-wave exercise (d = 1, y = w*x, MSE on the previous token, lr 0.01).
+* [Modular TTT] arxivdaily.com abstract "Modular TTT": MSE and inner-product inner
+  losses as interchangeable design dimensions.
+* [TTT-E2E] "TTT-E2E端到端测试时训练方法解析" (jsqmd.com): §2.1.2 delta rule -- a weight
+  change is an outer product of the back-propagated error (times the activation
+  derivative) with the layer input.
+
+Readings where the pages are silent (each one is listed in the design notes):
+* loss of a chunk S: inner product  L = -sum_{t in S} eta_t <f_W(k_t), v_t>,  or
+  MSE  L = sum_{t in S} eta_t ||f_W(k_t) - v_t||^2  (no 1/2, no 1/d, no 1/|S|);
+* one eta per token, shared by all fast-weight matrices; no extra step size, no
+  momentum, no weight decay; the update is W <- W - U with U the gradient (SGD) or
+  its 5-step Newton-Schulz orthogonalisation (Muon) -- no momentum or post-scale;
+* Newton-Schulz: X = G / (||G||_F + 1e-7), transposed to the wide orientation,
+  5 x { A = X X^T ; B = b A + c A^2 ; X = a X + B X } with the quintic coefficients
+  (a, b, c) = (3.4445, -4.7750, 2.0315) published with the Muon optimiser;
+* row renorm: after W' = W - U every row of every matrix is rescaled to the L2 norm
+  that row had before the update; a row whose new norm is 0 is left as it is;
+* shifted block-causal: chunk c's queries see the state after chunks 0..c-1 and the
+  last chunk's update is still made; the image-set order updates first, then applies;
+* SwiGLU  f(x) = W2 (silu(W1 x) * (W3 x));  GELU-MLP  f(x) = W2 gelu(W1 x) with the
+  exact erf GELU; no biases, no norms, no residual inside f.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+from scipy.special import erf
+
+MUON_COEFFS = (3.4445, -4.7750, 2.0315)
+NS_EPS = 1e-7
+
+APPLY_THEN_UPDATE = "apply_then_update"
+UPDATE_THEN_APPLY = "update_then_apply"
+
+
+# ----------------------------------------------------------------------------- activations
+def sigmoid(z):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    return z * sigmoid(z)
+
+
+def silu_prime(z):
+    # d/dz [z s(z)] = s + z s (1 - s)
+    s = sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def gelu(z):
+    return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+
+
+def gelu_prime(z):
+    # d/dz [z Phi(z)] = Phi(z) + z phi(z)
+    return 0.5 * (1.0 + erf(z / np.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+
+
+# ------------------------------------------------------------------------- fast-weight net
+def fw_apply(fw: str, Ws: Sequence[np.ndarray], X: np.ndarray) -> np.ndarray:
+    """f_W applied to every row of X (rows are tokens). [LaCT] §2.1 apply phase (eq. 2);
+    SwiGLU net per [LaCT] "key implementation tricks"; GELU MLP per [TTT layers] §4."""
+    X = np.asarray(X, dtype=np.float64)
+    if fw == "swiglu":
+        W1, W3, W2 = Ws
+        return (silu(X @ W1.T) * (X @ W3.T)) @ W2.T
+    if fw == "gelu":
+        W1, W2 = Ws
+        return gelu(X @ W1.T) @ W2.T
+    if fw == "linear":
+        (W,) = Ws
+        return X @ W.T
+    raise ValueError(fw)
+
+
+def chunk_loss(fw: str, loss: str, Ws, K, V, eta) -> float:
+    """Value of the chunk's inner loss (used by the finite-difference pins)."""
+    F = fw_apply(fw, Ws, K)
+    V = np.asarray(V, np.float64)
+    eta = np.asarray(eta, np.float64)
+    if loss == "dot":
+        return float(-np.sum(eta * np.sum(F * V, axis=1)))
+    if loss == "mse":
+        return float(np.sum(eta * np.sum((F - V) ** 2, axis=1)))
+    raise ValueError(loss)
+
+
+def _output_error(loss: str, F_k: Optional[np.ndarray], V: np.ndarray, eta: np.ndarray):
+    """dL/df(k_t) per token: -eta v (inner product) or 2 eta (f(k) - v) (MSE)."""
+    if loss == "dot":
+        return -eta[:, None] * V
+    if loss == "mse":
+        return 2.0 * eta[:, None] * (F_k - V)
+    raise ValueError(loss)
+
+
+def _block_gradient(fw: str, loss: str, Ws, K, V, eta) -> List[np.ndarray]:
+    """Gradient of the loss over one block of tokens, matrix form (token sums are
+    matrix products). Chain rule through the net; the weight gradients are the
+    token-summed outer products of back-propagated errors with layer inputs
+    ([TTT-E2E] §2.1.2)."""
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    eta = np.asarray(eta, np.float64)
+    if fw == "swiglu":
+        W1, W3, W2 = Ws
+        Z1 = K @ W1.T
+        Z3 = K @ W3.T
+        A = silu(Z1)
+        H = A * Z3
+        E = _output_error(loss, H @ W2.T if loss == "mse" else None, V, eta)
+        g2 = E.T @ H
+        dH = E @ W2
+        dZ3 = dH * A
+        dZ1 = dH * Z3 * silu_prime(Z1)
+        return [dZ1.T @ K, dZ3.T @ K, g2]
+    if fw == "gelu":
+        W1, W2 = Ws
+        Z = K @ W1.T
+        H = gelu(Z)
+        E = _output_error(loss, H @ W2.T if loss == "mse" else None, V, eta)
+        g2 = E.T @ H
+        dZ = (E @ W2) * gelu_prime(Z)
+        return [dZ.T @ K, g2]
+    if fw == "linear":
+        (W,) = Ws
+        E = _output_error(loss, K @ W.T if loss == "mse" else None, V, eta)
+        return [E.T @ K]
+    raise ValueError(fw)
+
+
+def chunk_gradient(fw: str, loss: str, Ws, K, V, eta, block_rows: Optional[int] = None):
+    """Sum of the per-token gradients over the whole chunk ([LaCT] §2.1 update phase,
+    eqs. 4-5). A chunk longer than ``block_rows`` is summed block by block: the
+    gradient of a sum of per-token losses is the sum of the blocks' gradients."""
+    n = len(eta)
+    if block_rows is None or n <= block_rows:
+        return _block_gradient(fw, loss, Ws, K, V, eta)
+    total = None
+    for s in range(0, n, block_rows):
+        g = _block_gradient(fw, loss, Ws, K[s:s + block_rows], V[s:s + block_rows],
+                            eta[s:s + block_rows])
+        total = g if total is None else [t + x for t, x in zip(total, g)]
+    return total
+
+
+# ----------------------------------------------------------------- optimiser and weight norm
+def newton_schulz5(G: np.ndarray, steps: int = 5, coeffs=MUON_COEFFS, eps: float = NS_EPS):
+    """Muon's orthogonalisation of a gradient matrix ([LaCT] §2.2.1, eqs. 9-10): scale
+    to unit Frobenius norm, then ``steps`` quintic Newton-Schulz iterations, run in the
+    wide orientation (rows <= cols) and transposed back."""
+    a, b, c = coeffs
+    X = np.asarray(G, np.float64) / (np.linalg.norm(G) + eps)
+    wide = X.shape[0] <= X.shape[1]
+    if not wide:
+        X = X.T
+    for _ in range(steps):
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X if wide else X.T
+
+
+def renorm_rows(W_prev: np.ndarray, W_new: np.ndarray) -> np.ndarray:
+    """L2 weight normalisation ([LaCT] §2.2.1, eq. 8): each row of the updated matrix
+    is rescaled to the L2 norm the same row had before the update."""
+    n_prev = np.linalg.norm(W_prev, axis=1)
+    n_new = np.linalg.norm(W_new, axis=1)
+    ok = n_new > 0
+    scale = np.where(ok, n_prev / np.where(ok, n_new, 1.0), 1.0)
+    return W_new * scale[:, None]
+
+
+def update_state(Ws, grads, ns_steps: int, renorm: bool) -> List[np.ndarray]:
+    """W <- W - U per matrix, U = NS5(g) under Muon else g; then the optional row renorm."""
+    out = []
+    for W, g in zip(Ws, grads):
+        U = newton_schulz5(g, ns_steps) if ns_steps > 0 else g
+        W_new = W - U
+        out.append(renorm_rows(W, W_new) if renorm else W_new)
+    return out
+
+
+# ------------------------------------------------------------------------- the layer loop
+def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
+                     apply_rows: Optional[np.ndarray] = None, n_chunks: Optional[int] = None):
+    """One (batch, head) problem: the chunk loop of the TTT layer.
+
+    W0s: the problem's initial matrices; Q, K, V: [T, d]; eta: [T].
+    Chunk c covers tokens [c*b, (c+1)*b). Under the shifted block-causal order
+    ([LaCT] §3.2, Fig. 3c) its queries are answered with the state left by chunks
+    0..c-1 and its own update follows; the image-set order ([LaCT] §3.1) updates
+    first and then applies. The state after the last chunk is returned.
+
+    apply_rows: optional sorted token indices; only those rows of O are computed
+    (the others stay 0). n_chunks: stop after that many chunks.
+    Returns (O [T, d] fp64, list of final fp64 matrices)."""
+    T = len(eta)
+    b = cfg.chunk
+    Ws = [np.asarray(w, np.float64) for w in W0s]
+    O = np.zeros((T, cfg.dim), np.float64)
+    nc = T // b if n_chunks is None else n_chunks
+    rows = None if apply_rows is None else np.asarray(apply_rows)
+
+    def apply(lo, hi):
+        if rows is None:
+            for s in range(lo, hi, block_rows or (hi - lo)):
+                e = min(hi, s + (block_rows or (hi - lo)))
+                O[s:e] = fw_apply(cfg.fw, Ws, Q[s:e])
+        else:
+            sel = rows[(rows >= lo) & (rows < hi)]
+            if len(sel):
+                O[sel] = fw_apply(cfg.fw, Ws, Q[sel])
+
+    for c in range(nc):
+        lo, hi = c * b, (c + 1) * b
+        if cfg.order == APPLY_THEN_UPDATE:
+            apply(lo, hi)
+        g = chunk_gradient(cfg.fw, cfg.loss, Ws, K[lo:hi], V[lo:hi], eta[lo:hi], block_rows)
+        Ws = update_state(Ws, g, cfg.ns_steps, cfg.renorm)
+        if cfg.order == UPDATE_THEN_APPLY:
+            apply(lo, hi)
+    return O, Ws
+
+
+def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta):
+    """Per-token version for tiny inputs: every output row and every token's gradient
+    is formed with explicit vector operations in Python loops, and the chunk gradient
+    is the running sum of per-token outer products. Checks the matrix form above."""
+    T = len(eta)
+    b = cfg.chunk
+    Ws = [np.array(w, np.float64) for w in W0s]
+    O = np.zeros((T, cfg.dim))
+
+    def f(x):
+        if cfg.fw == "swiglu":
+            W1, W3, W2 = Ws
+            z1, z3 = W1 @ x, W3 @ x
+            return W2 @ (silu(z1) * z3)
+        if cfg.fw == "gelu":
+            W1, W2 = Ws
+            return W2 @ gelu(W1 @ x)
+        (W,) = Ws
+        return W @ x
+
+    for c in range(T // b):
+        if cfg.order == APPLY_THEN_UPDATE:
+            for t in range(c * b, (c + 1) * b):
+                O[t] = f(np.asarray(Q[t], np.float64))
+        grads = [np.zeros_like(w) for w in Ws]
+        for t in range(c * b, (c + 1) * b):
+            k = np.asarray(K[t], np.float64)
+            v = np.asarray(V[t], np.float64)
+            et = float(eta[t])
+            e = -et * v if cfg.loss == "dot" else 2.0 * et * (f(k) - v)
+            if cfg.fw == "swiglu":
+                W1, W3, W2 = Ws
+                z1, z3 = W1 @ k, W3 @ k
+                h = silu(z1) * z3
+                dh = W2.T @ e
+                grads[2] += np.outer(e, h)
+                grads[0] += np.outer(dh * z3 * silu_prime(z1), k)
+                grads[1] += np.outer(dh * silu(z1), k)
+            elif cfg.fw == "gelu":
+                W1, W2 = Ws
+                z = W1 @ k
+                grads[1] += np.outer(e, gelu(z))
+                grads[0] += np.outer((W2.T @ e) * gelu_prime(z), k)
+            else:
+                grads[0] += np.outer(e, k)
+        Ws = update_state(Ws, grads, cfg.ns_steps, cfg.renorm)
+        if cfg.order == UPDATE_THEN_APPLY:
+            for t in range(c * b, (c + 1) * b):
+                O[t] = f(np.asarray(Q[t], np.float64))
+    return O, Ws
+
+
+def forward_all(cfg, inputs, problems: Optional[Sequence[Tuple[int, int]]] = None,
+                block_rows: Optional[int] = 8192):
+    """Run every (batch, head) problem (or the listed ones) of an input set made by
+    ``ttt_inputs.make_inputs``. Returns {(b, h): (O, [W...])}."""
+    out = {}
+    probs = problems if problems is not None else [
+        (b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    for (b, h) in probs:
+        W0s = [w[h] for w in inputs["w0"]]
+        out[(b, h)] = sequence_forward(cfg, W0s, inputs["q"][b, h], inputs["k"][b, h],
+                                       inputs["v"][b, h], inputs["eta"][b, h], block_rows)
+    return out

@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle to facts fixed outside the oracle itself.
+
+Each pin compares the oracle with an independent route to the same number:
+finite differences of the loss, torch autograd, per-token brute force, closed forms
+of the linear fast weight, the scalar exercise of the TTT-layer explainer page, the
+spectral form of the Newton-Schulz map, and invariants (eta = 0, row norms, causality).
+The mutation tests at the end plant plausible mistakes in the oracle (on the CPU) and
+check that some pin catches each one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.ttt_oracle as orc
+from ttt_inputs import Config
+
+RNG = np.random.default_rng(12345)
+
+
+def _rand_ws(fw, d, dh, rng, scale=0.5):
+    shapes = {"swiglu": [(dh, d), (dh, d), (d, dh)], "gelu": [(dh, d), (d, dh)],
+              "linear": [(d, d)]}[fw]
+    return [rng.standard_normal(s) * scale for s in shapes]
+
+
+def _rand_chunk(n, d, rng):
+    K = rng.standard_normal((n, d))
+    V = rng.standard_normal((n, d))
+    eta = 0.01 + 0.1 * rng.random(n)
+    return K, V, eta
+
+
+# ------------------------------------------------------------------ gradient pins
+def fd_gradient_error(fw, loss, seed=0, d=4, dh=8, n=3, eps=1e-6):
+    rng = np.random.default_rng(seed)
+    Ws = _rand_ws(fw, d, dh, rng)
+    K, V, eta = _rand_chunk(n, d, rng)
+    g = orc.chunk_gradient(fw, loss, Ws, K, V, eta)
+    worst = 0.0
+    for i, W in enumerate(Ws):
+        fd = np.zeros_like(W)
+        for idx in np.ndindex(W.shape):
+            Wp = [w.copy() for w in Ws]
+            Wm = [w.copy() for w in Ws]
+            Wp[i][idx] += eps
+            Wm[i][idx] -= eps
+            fd[idx] = (orc.chunk_loss(fw, loss, Wp, K, V, eta)
+                       - orc.chunk_loss(fw, loss, Wm, K, V, eta)) / (2 * eps)
+        worst = max(worst, np.abs(fd - g[i]).max() / np.abs(fd).max())
+    return worst
+
+
+@pytest.mark.parametrize("fw", ["swiglu", "gelu", "linear"])
+@pytest.mark.parametrize("loss", ["dot", "mse"])
+def test_gradient_matches_finite_differences(fw, loss):
+    assert fd_gradient_error(fw, loss) < 1e-6
+
+
+def _torch_loss(fw, loss, Ws, K, V, eta):
+    F = torch.nn.functional
+    if fw == "swiglu":
+        W1, W3, W2 = Ws
+        out = (F.silu(K @ W1.T) * (K @ W3.T)) @ W2.T
+    elif fw == "gelu":
+        W1, W2 = Ws
+        out = F.gelu(K @ W1.T) @ W2.T
+    else:
+        (W,) = Ws
+        out = K @ W.T
+    if loss == "dot":
+        return -(eta * (out * V).sum(1)).sum()
+    return (eta * ((out - V) ** 2).sum(1)).sum()
+
+
+@pytest.mark.parametrize("fw", ["swiglu", "gelu", "linear"])
+@pytest.mark.parametrize("loss", ["dot", "mse"])
+def test_gradient_matches_torch_autograd(fw, loss):
+    rng = np.random.default_rng(7)
+    Ws = _rand_ws(fw, 6, 10, rng)
+    K, V, eta = _rand_chunk(5, 6, rng)
+    g = orc.chunk_gradient(fw, loss, Ws, K, V, eta)
+    tW = [torch.tensor(w, dtype=torch.float64, requires_grad=True) for w in Ws]
+    L = _torch_loss(fw, loss, tW, torch.tensor(K), torch.tensor(V), torch.tensor(eta))
+    tg = torch.autograd.grad(L, tW)
+    for a, b in zip(g, tg):
+        assert np.abs(a - b.numpy()).max() <= 1e-12 * max(1.0, np.abs(a).max())
+
+
+def test_activations_match_torch():
+    z = np.linspace(-8, 8, 1001)
+    tz = torch.tensor(z, requires_grad=True)
+    F = torch.nn.functional
+    for ours, ours_d, theirs in ((orc.silu, orc.silu_prime, F.silu),
+                                 (orc.gelu, orc.gelu_prime, F.gelu)):
+        y = theirs(tz)
+        (dy,) = torch.autograd.grad(y.sum(), tz)
+        assert np.abs(ours(z) - y.detach().numpy()).max() < 1e-14
+        assert np.abs(ours_d(z) - dy.numpy()).max() < 1e-14
+
+
+# ------------------------------------------------------------------ whole-loop pins
+def _cfg(fw="swiglu", loss="dot", ns=0, renorm=False, order="apply_then_update", chunk=3,
+         d=4, dh=8, T=9):
+    return Config("t", 1, 1, T, chunk, d, dh, fw, loss, ns, renorm, "f32", order)
+
+
+def _rand_problem(cfg, rng, wscale=0.5):
+    Ws = _rand_ws(cfg.fw, cfg.dim, cfg.hidden, rng, wscale)
+    Q = rng.standard_normal((cfg.seq_len, cfg.dim))
+    K, V, eta = _rand_chunk(cfg.seq_len, cfg.dim, rng)
+    return Ws, Q, K, V, eta
+
+
+@pytest.mark.parametrize("fw", ["swiglu", "gelu", "linear"])
+@pytest.mark.parametrize("loss", ["dot", "mse"])
+@pytest.mark.parametrize("ns,renorm", [(0, False), (0, True), (5, True)])
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+def test_matrix_form_matches_per_token_bruteforce(fw, loss, ns, renorm, order):
+    cfg = _cfg(fw, loss, ns, renorm, order, chunk=3, d=4, dh=6, T=12)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(3))
+    O1, W1 = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    O2, W2 = orc.sequence_forward_bruteforce(cfg, Ws, Q, K, V, eta)
+    assert np.abs(O1 - O2).max() <= 1e-12 * max(1, np.abs(O2).max())
+    for a, b in zip(W1, W2):
+        assert np.abs(a - b).max() <= 1e-12 * max(1, np.abs(b).max())
+
+
+def linear_dot_closed_form_error(order="apply_then_update", chunk=4, T=16, d=5, seed=11):
+    """Linear fast weight, inner-product loss, plain SGD, no norm: for any chunking the
+    state is W0 + sum_t eta_t v_t k_t^T over the tokens seen, and chunk c's outputs are
+    that state applied to its queries (before or after its own tokens, by the order)."""
+    cfg = _cfg("linear", "dot", 0, False, order, chunk=chunk, d=d, T=T)
+    rng = np.random.default_rng(seed)
+    Ws, Q, K, V, eta = _rand_problem(cfg, rng)
+    O, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    W = Ws[0].copy()
+    err = 0.0
+    for c in range(T // chunk):
+        S = slice(c * chunk, (c + 1) * chunk)
+        Wn = W + sum(eta[t] * np.outer(V[t], K[t]) for t in range(c * chunk, (c + 1) * chunk))
+        ref = Q[S] @ (W if order == "apply_then_update" else Wn).T
+        err = max(err, np.abs(O[S] - ref).max())
+        W = Wn
+    err = max(err, np.abs(Wf[0] - W).max())
+    return err
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+@pytest.mark.parametrize("chunk", [1, 4, 16])
+def test_linear_dot_closed_form(order, chunk):
+    assert linear_dot_closed_form_error(order, chunk) <= 1e-12
+
+
+def test_scalar_sine_exercise():
+    """The TTT-layer explainer's exercise (aivaro.ru page, §10): d = 1, y = w x,
+    MSE on predicting the next value from the previous one, SGD with lr 0.01, update on
+    the previous token and then output for the current one, over a noisy sine of 1000
+    points. As a TTT layer: chunk = 1, k_t = x_{t-1}, v_t = x_t, q_t = x_t, eta_t = 0.01,
+    update-then-apply, linear fast weight, MSE loss."""
+    rng = np.random.default_rng(5)
+    x = np.sin(np.arange(1000) * 0.05) + 0.1 * rng.standard_normal(1000)
+    w0 = 0.3
+    # the exercise written as a plain scalar loop
+    w, outs = w0, []
+    for t in range(1, 1000):
+        grad = 2.0 * (w * x[t - 1] - x[t]) * x[t - 1]
+        w = w - 0.01 * grad
+        outs.append(w * x[t])
+    cfg = _cfg("linear", "mse", 0, False, "update_then_apply", chunk=1, d=1, T=999)
+    O, Wf = orc.sequence_forward(cfg, [np.array([[w0]])], x[1:, None], x[:-1, None],
+                                 x[1:, None], np.full(999, 0.01))
+    assert np.abs(O[:, 0] - np.array(outs)).max() < 1e-12
+    assert abs(Wf[0][0, 0] - w) < 1e-12
+
+
+@pytest.mark.parametrize("fw,loss", [("swiglu", "dot"), ("gelu", "mse"), ("linear", "dot")])
+@pytest.mark.parametrize("ns,renorm", [(0, False), (0, True), (5, True)])
+def test_eta_zero_leaves_state_bitwise(fw, loss, ns, renorm):
+    cfg = _cfg(fw, loss, ns, renorm, chunk=3, T=9)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(1))
+    O, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, np.zeros_like(eta))
+    for a, b in zip(Wf, Ws):
+        assert np.array_equal(a, b)
+    assert np.array_equal(O, orc.fw_apply(fw, Ws, Q))
+
+
+def test_shifted_causality():
+    """Outputs of chunks <= c do not change when keys, values or eta of chunks >= c
+    change (apply-then-update), and chunk 0 is answered by W0."""
+    cfg = _cfg("swiglu", "dot", 5, True, chunk=4, T=16, d=4, dh=8)
+    rng = np.random.default_rng(2)
+    Ws, Q, K, V, eta = _rand_problem(cfg, rng)
+    O, _ = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    assert np.array_equal(O[:4], orc.fw_apply("swiglu", Ws, Q[:4]))
+    for c in range(4):
+        K2, V2, e2 = K.copy(), V.copy(), eta.copy()
+        K2[c * 4:] += 1.0
+        V2[c * 4:] -= 1.0
+        e2[c * 4:] *= 3.0
+        O2, _ = orc.sequence_forward(cfg, Ws, Q, K2, V2, e2)
+        assert np.array_equal(O2[:(c + 1) * 4], O[:(c + 1) * 4])
+        if c < 3:
+            assert not np.array_equal(O2[(c + 1) * 4:], O[(c + 1) * 4:])
+
+
+def test_block_summation_invariance():
+    """Summing a large chunk's gradient block by block gives the one-block result."""
+    cfg = _cfg("swiglu", "dot", 5, True, chunk=300, T=600, d=8, dh=16)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(4), 0.3)
+    O1, W1 = orc.sequence_forward(cfg, Ws, Q, K, V, eta, block_rows=None)
+    O2, W2 = orc.sequence_forward(cfg, Ws, Q, K, V, eta, block_rows=37)
+    assert np.abs(O1 - O2).max() <= 1e-12 * np.abs(O1).max()
+    for a, b in zip(W1, W2):
+        assert np.abs(a - b).max() <= 1e-12 * np.abs(b).max()
+
+
+# ------------------------------------------------------------------ Newton-Schulz pins
+def ns5_svd_error(shape, seed=0, rank=None):
+    """NS5 acts on singular values only: G = U S V^T maps to U phi^5(S/(|G|_F+eps)) V^T
+    with phi(s) = a s + b s^3 + c s^5 (each step's X X^T, its square and the product
+    with X are diagonal in G's singular bases)."""
+    rng = np.random.default_rng(seed)
+    G = rng.standard_normal(shape)
+    if rank is not None:
+        G = rng.standard_normal((shape[0], rank)) @ rng.standard_normal((rank, shape[1]))
+    U, S, Vt = np.linalg.svd(G, full_matrices=False)
+    s = S / (math.sqrt(float(np.sum(S * S))) + orc.NS_EPS)
+    a, b, c = orc.MUON_COEFFS
+    for _ in range(5):
+        s = a * s + b * s ** 3 + c * s ** 5
+    ref = (U * s) @ Vt
+    return np.abs(orc.newton_schulz5(G) - ref).max()
+
+
+@pytest.mark.parametrize("shape", [(6, 9), (9, 6), (7, 7), (32, 64), (64, 32)])
+def test_ns5_spectral_closed_form(shape):
+    assert ns5_svd_error(shape) < 1e-12
+
+
+def test_ns5_rank_deficient_and_zero():
+    assert ns5_svd_error((12, 20), rank=3) < 1e-12
+    assert np.array_equal(orc.newton_schulz5(np.zeros((4, 6))), np.zeros((4, 6)))
+
+
+def test_ns5_symmetries():
+    G = np.random.default_rng(9).standard_normal((16, 24))
+    U = orc.newton_schulz5(G)
+    assert np.abs(orc.newton_schulz5(-G) + U).max() < 1e-14
+    assert np.abs(orc.newton_schulz5(G.T) - U.T).max() < 1e-14
+    assert np.abs(orc.newton_schulz5(3.7 * G) - U).max() < 1e-7   # scale-free up to eps
+
+
+def test_ns5_singular_values_near_one():
+    """Muon's iteration pushes every singular value that is not tiny into a band around
+    1: for sigma/|G|_F >= 3e-3 the 5-step quintic lands in [0.68, 1.21]."""
+    G = np.random.default_rng(10).standard_normal((64, 128))
+    S = np.linalg.svd(orc.newton_schulz5(G), compute_uv=False)
+    assert S.min() > 0.68 and S.max() < 1.21
+
+
+# ------------------------------------------------------------------ renorm pins
+def test_renorm_restores_row_norms():
+    rng = np.random.default_rng(8)
+    W = rng.standard_normal((20, 30))
+    Wn = W - rng.standard_normal((20, 30))
+    R = orc.renorm_rows(W, Wn)
+    assert np.abs(np.linalg.norm(R, axis=1) / np.linalg.norm(W, axis=1) - 1).max() < 1e-15
+    # direction of every row is that of the updated row
+    cos = np.sum(R * Wn, 1) / np.linalg.norm(R, axis=1) / np.linalg.norm(Wn, axis=1)
+    assert np.abs(cos - 1).max() < 1e-15
+
+
+def test_renorm_zero_row_guard():
+    W = np.ones((3, 4))
+    Wn = W.copy()
+    Wn[1] = 0
+    R = orc.renorm_rows(W, Wn)
+    assert np.array_equal(R[1], np.zeros(4))
+    assert np.allclose(R[[0, 2]], W[[0, 2]], rtol=0, atol=1e-15)
+
+
+def test_sequence_renorm_keeps_initial_norms():
+    cfg = _cfg("swiglu", "dot", 5, True, chunk=4, T=20, d=6, dh=10)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(6))
+    _, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    for a, b in zip(Wf, Ws):
+        assert np.abs(np.linalg.norm(a, axis=1) - np.linalg.norm(b, axis=1)).max() < 1e-13
+        assert np.abs(a - b).max() > 1e-3   # the state did move
+
+
+# ------------------------------------------------------------------ mutation tests
+def _all_pins_pass():
+    try:
+        return _all_pins_pass_inner()
+    except (ValueError, IndexError):   # a shape error is a caught mistake too
+        return False
+
+
+def _all_pins_pass_inner():
+    checks = [
+        fd_gradient_error("swiglu", "dot") < 1e-6,
+        fd_gradient_error("swiglu", "mse") < 1e-6,
+        fd_gradient_error("gelu", "mse") < 1e-6,
+        linear_dot_closed_form_error("apply_then_update") <= 1e-12,
+        linear_dot_closed_form_error("update_then_apply") <= 1e-12,
+        ns5_svd_error((6, 9)) < 1e-12,
+        ns5_svd_error((9, 6)) < 1e-12,
+    ]
+    W = np.random.default_rng(1).standard_normal((5, 7))
+    Wn = W + np.random.default_rng(2).standard_normal((5, 7))
+    R = orc.renorm_rows(W, Wn)
+    checks.append(np.abs(np.linalg.norm(R, axis=1) - np.linalg.norm(W, axis=1)).max() < 1e-14)
+    return all(checks)
+
+
+def test_pins_pass_on_the_unmutated_oracle():
+    assert _all_pins_pass()
+
+
+def _mut_silu_prime(z):  # dropped term of silu'
+    return orc.sigmoid(z)
+
+
+def _mut_output_error(loss, F_k, V, eta):  # sign error in the inner-product error
+    return eta[:, None] * V if loss == "dot" else 2.0 * eta[:, None] * (F_k - V)
+
+
+def _mut_ns(G, steps=5, coeffs=orc.MUON_COEFFS, eps=orc.NS_EPS):  # A instead of A^2
+    a, b, c = coeffs
+    X = G / (np.linalg.norm(G) + eps)
+    wide = X.shape[0] <= X.shape[1]
+    X = X if wide else X.T
+    for _ in range(steps):
+        A = X @ X.T
+        X = a * X + (b * A + c * A) @ X
+    return X if wide else X.T
+
+
+def _mut_ns_transpose(G, steps=5, coeffs=orc.MUON_COEFFS, eps=orc.NS_EPS):  # no undo
+    a, b, c = coeffs
+    X = G / (np.linalg.norm(G) + eps)
+    if X.shape[0] > X.shape[1]:
+        X = X.T
+    for _ in range(steps):
+        A = X @ X.T
+        X = a * X + (b * A + c * A @ A) @ X
+    return X
+
+
+def _mut_renorm(W_prev, W_new):  # renormalises to unit norm
+    return W_new / np.linalg.norm(W_new, axis=1, keepdims=True)
+
+
+def _mut_block_grad_transposed(fw, loss, Ws, K, V, eta):  # g2 = H^T E instead of E^T H
+    g = _ORIG_BLOCK(fw, loss, Ws, K, V, eta)
+    if fw == "swiglu":
+        g[2] = g[2][::-1]
+    return g
+
+
+_ORIG_BLOCK = orc._block_gradient
+
+
+@pytest.mark.parametrize("name,target,mut", [
+    ("silu' term", "silu_prime", _mut_silu_prime),
+    ("error sign", "_output_error", _mut_output_error),
+    ("NS square", "newton_schulz5", _mut_ns),
+    ("NS transpose", "newton_schulz5", _mut_ns_transpose),
+    ("renorm target", "renorm_rows", _mut_renorm),
+    ("g2 index", "_block_gradient", _mut_block_grad_transposed),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, target, mut):
+    monkeypatch.setattr(orc, target, mut)
+    assert not _all_pins_pass(), name
