@@ -1,0 +1,48 @@
+"""GPU parity: libttt against the fp64 oracle on the same seeded inputs.
+
+Tolerances (max relative error, per tensor: |x - y|_inf / |y|_inf, on the outputs O and on
+every final fast-weight matrix): 1e-4 for fp32 activations, 2e-2 for bf16 activations with
+fp32 accumulation. Sizes span several tiles in every dimension and end in ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+import ttt_inputs as ti
+import weight_sequence_layers_amd as W
+from ttt_gpu import device_inputs, parity, read_state, rel_err, run_gpu, small
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _check(cfg, planes=None, problems=None, chunked=False):
+    inp = ti.make_inputs(cfg)
+    O, Ws = run_gpu(cfg, inp, planes, chunked)
+    eo, ew = parity(cfg, inp, O, Ws, problems)
+    tol = TOL[cfg.act]
+    print(f"{cfg.name}: O {eo:.3e} W {[f'{e:.3e}' for e in ew]} (tol {tol})", flush=True)
+    assert eo <= tol and max(ew) <= tol, (eo, ew)
+    return eo, ew
+
+
+def test_tiny_fp32_full_size():
+    _check(ti.CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("fw,loss,ns,renorm", [
+    ("swiglu", "dot", 5, True), ("swiglu", "dot", 0, True), ("swiglu", "mse", 0, False),
+    ("gelu", "mse", 0, False), ("gelu", "dot", 5, True), ("linear", "dot", 0, False),
+    ("linear", "mse", 0, True),
+])
+def test_ragged_shapes(act, fw, loss, ns, renorm):
+    cfg = ti.Config("ragged", 2, 3, 900, 300, 80, 176, fw, loss, ns, renorm, act,
+                    "apply_then_update", 2024)
+    _check(cfg)
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+def test_orders(order):
+    cfg = ti.Config("ord", 1, 2, 1024, 256, 64, 128, "swiglu", "dot", 5, True, "bf16", order, 7)
+    _check(cfg, planes=(1, 2, 2, 2))

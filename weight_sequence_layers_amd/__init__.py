@@ -1,0 +1,202 @@
+"""Python binding of libttt, the large-chunk TTT layer forward for MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of libttt.so.
+PyTorch supplies device memory and the current stream. The functions carry the C names
+(ttt_init_state, ttt_chunk_forward, ttt_sequence_forward, ...) and raise TTTError on any
+non-OK status. If libttt.so is missing or cannot be loaded, every call raises: there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libttt.so")
+
+FW = {"swiglu": 0, "gelu": 1, "linear": 2}
+LOSS = {"dot": 0, "mse": 1}
+ACT = {"f32": 0, "bf16": 1}
+ORDER = {"apply_then_update": 0, "update_then_apply": 1}
+
+STATUS = {0: "TTT_OK", 1: "TTT_E_NULL", 2: "TTT_E_SHAPE", 3: "TTT_E_DTYPE", 4: "TTT_E_CONFIG",
+          5: "TTT_E_UNSUPPORTED", 6: "TTT_E_ALLOC", 7: "TTT_E_HIP", 8: "TTT_E_NONFINITE",
+          9: "TTT_E_ALIGN"}
+
+# bf16 planes per operand class (apply, grad, ns, ns_lead) for the named workloads; chosen
+# as the cheapest setting whose end-to-end error stays well inside the parity bound.
+PRECISION = {
+    "tiny": (3, 3, 3, 3),
+    "lm": (1, 2, 2, 2),
+    "long": (1, 2, 3, 3),
+    "long_alt": (1, 2, 3, 3),
+    "imageset": (1, 1, 2, 2),
+    "smallchunk": (1, 1, 1, 1),
+}
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class ttt_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order", "ns_steps",
+        "row_renorm", "apply_planes", "grad_planes", "ns_planes", "ns_lead_planes")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libttt.so (built in-tree by build.py). Raises if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run weight_sequence_layers_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        cfgp, vp, i64 = ctypes.POINTER(ttt_config), ctypes.c_void_p, ctypes.c_int64
+        sig = {
+            "ttt_validate_config": [cfgp],
+            "ttt_state_numel": [cfgp, ctypes.POINTER(i64)],
+            "ttt_init_state": [cfgp, vp, vp, ctypes.POINTER(vp)],
+            "ttt_chunk_forward": [vp, vp, vp, vp, vp, vp, vp],
+            "ttt_sequence_forward": [vp, vp, vp, vp, vp, vp, i64, vp],
+            "ttt_get_state": [vp, vp, vp],
+            "ttt_set_state": [vp, vp, vp],
+            "ttt_state_health": [vp],
+            "ttt_destroy_state": [vp],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.ttt_status_str.argtypes = [ctypes.c_int]
+        L.ttt_status_str.restype = ctypes.c_char_p
+        L.ttt_last_error.argtypes = []
+        L.ttt_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(st: int):
+    if st != 0:
+        raise TTTError(st, lib().ttt_last_error().decode())
+
+
+def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
+    """ttt_config from an object with the workload fields (batch, heads, dim, hidden, chunk,
+    fw, loss, act, order, ns_steps, renorm), overridden by keyword arguments. `planes` is
+    (apply, grad, ns, ns_lead); by default the preset of the workload's name, else 0s."""
+    f = {}
+    if cfg is not None:
+        for k in ("batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order",
+                  "ns_steps", "renorm"):
+            f[k] = getattr(cfg, k)
+        if planes is None:
+            planes = PRECISION.get(getattr(cfg, "name", ""), None)
+    f.update(kw)
+    planes = planes or (0, 0, 0, 0)
+    c = ttt_config()
+    c.batch, c.heads, c.dim, c.hidden, c.chunk = (int(f["batch"]), int(f["heads"]), int(f["dim"]),
+                                                  int(f["hidden"]), int(f["chunk"]))
+    c.fw = FW[f["fw"]] if isinstance(f["fw"], str) else int(f["fw"])
+    c.loss = LOSS[f["loss"]] if isinstance(f["loss"], str) else int(f["loss"])
+    c.act = ACT[f["act"]] if isinstance(f["act"], str) else int(f["act"])
+    c.order = ORDER[f["order"]] if isinstance(f["order"], str) else int(f["order"])
+    c.ns_steps = int(f.get("ns_steps", 0))
+    c.row_renorm = int(bool(f.get("renorm", False)))
+    c.apply_planes, c.grad_planes, c.ns_planes, c.ns_lead_planes = (int(p) for p in planes)
+    return c
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream)) or None
+
+
+def ttt_validate_config(cfg: ttt_config) -> None:
+    _check(lib().ttt_validate_config(ctypes.byref(cfg)))
+
+
+def ttt_state_numel(cfg: ttt_config) -> int:
+    n = ctypes.c_int64()
+    _check(lib().ttt_state_numel(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+class State:
+    """Owns a ttt_state handle (freed by destroy() or garbage collection)."""
+
+    def __init__(self, handle: int, cfg: ttt_config):
+        self.handle = ctypes.c_void_p(handle)
+        self.cfg = cfg
+
+    def destroy(self):
+        if self.handle:
+            h, self.handle = self.handle, None
+            _check(lib().ttt_destroy_state(h))
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def ttt_init_state(cfg: ttt_config, w0, stream=None) -> State:
+    """w0: contiguous fp32 device tensor with the per-head initial matrices, matrix by
+    matrix (see include/libttt.h)."""
+    h = ctypes.c_void_p()
+    _check(lib().ttt_init_state(ctypes.byref(cfg), _ptr(w0), _stream(stream), ctypes.byref(h)))
+    return State(h.value, cfg)
+
+
+def ttt_chunk_forward(st: State, q, k, v, eta, out, stream=None) -> None:
+    _check(lib().ttt_chunk_forward(st.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(out),
+                                   _stream(stream)))
+
+
+def ttt_sequence_forward(st: State, q, k, v, eta, out, seq_len: int, stream=None) -> None:
+    _check(lib().ttt_sequence_forward(st.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                      _ptr(out), int(seq_len), _stream(stream)))
+
+
+def ttt_get_state(st: State, dst, stream=None) -> None:
+    _check(lib().ttt_get_state(st.handle, _ptr(dst), _stream(stream)))
+
+
+def ttt_set_state(st: State, src, stream=None) -> None:
+    _check(lib().ttt_set_state(st.handle, _ptr(src), _stream(stream)))
+
+
+def ttt_state_health(st: State) -> None:
+    _check(lib().ttt_state_health(st.handle))
+
+
+def ttt_destroy_state(st: State) -> None:
+    st.destroy()
+
+
+def matrix_shapes(cfg: ttt_config):
+    d, dh = cfg.dim, cfg.hidden
+    return {0: [(dh, d), (dh, d), (d, dh)], 1: [(dh, d), (d, dh)], 2: [(d, d)]}[cfg.fw]
+
+
+def split_state(cfg: ttt_config, flat):
+    """Views of a flat state buffer as per-matrix [batch, heads, rows, cols] tensors."""
+    out, o = [], 0
+    for r, c in matrix_shapes(cfg):
+        n = cfg.batch * cfg.heads * r * c
+        out.append(flat[o:o + n].view(cfg.batch, cfg.heads, r, c))
+        o += n
+    return out

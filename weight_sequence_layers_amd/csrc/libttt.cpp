@@ -1,0 +1,727 @@
+// Host side of libttt: argument checks, state and workspace ownership, and the chunk loop
+// that enqueues the stage kernels of ttt_kernels.hip.  See include/libttt.h for the ABI.
+#include "../../include/libttt.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "ttt_internal.h"
+
+using namespace ttt;
+
+namespace {
+
+thread_local std::string g_err;
+
+ttt_status fail(ttt_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(TTT_E_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_),     \
+                  __FILE__, __LINE__);                                                  \
+  } while (0)
+
+constexpr int64_t SUBBLOCK_MAX = 65536;  // tokens per gradient / apply launch
+constexpr int ROW_PAD = 128;            // token padding of transposed buffers
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Dims {
+  int P, nm, d, dh, n;      // problems, matrices, dim, hidden, columns of X orientation
+  int rows[3], cols[3], tr[3];
+  int ap, gp, np, nlp, npm, wp, in_q, in_kv;
+  int64_t sb, bpad;         // tokens per sub-block, padded token rows of transposed buffers
+};
+
+ttt_status resolve(const ttt_config* c, ttt_config* out) {
+  if (!c) return fail(TTT_E_NULL, "config is NULL");
+  ttt_config r = *c;
+  if (r.fw < 0 || r.fw > 2) return fail(TTT_E_CONFIG, "unknown fw %d", r.fw);
+  if (r.loss < 0 || r.loss > 1) return fail(TTT_E_CONFIG, "unknown loss %d", r.loss);
+  if (r.act < 0 || r.act > 1) return fail(TTT_E_DTYPE, "unknown activation dtype %d", r.act);
+  if (r.order < 0 || r.order > 1) return fail(TTT_E_CONFIG, "unknown order %d", r.order);
+  if (r.row_renorm != 0 && r.row_renorm != 1)
+    return fail(TTT_E_CONFIG, "row_renorm must be 0 or 1 (got %d)", r.row_renorm);
+  if (r.ns_steps < 0 || r.ns_steps > 8)
+    return fail(TTT_E_CONFIG, "ns_steps must be in [0, 8] (got %d)", r.ns_steps);
+  if (r.batch < 1 || r.heads < 1) return fail(TTT_E_SHAPE, "batch and heads must be >= 1");
+  if ((int64_t)r.batch * r.heads > 65535)
+    return fail(TTT_E_SHAPE, "batch*heads = %lld exceeds 65535", (long long)r.batch * r.heads);
+  if (r.dim < 16 || r.dim > 1024 || r.dim % 16)
+    return fail(TTT_E_SHAPE, "dim must be a multiple of 16 in [16, 1024] (got %d)", r.dim);
+  if (r.fw == TTT_FW_LINEAR) {
+    r.hidden = r.dim;
+  } else if (r.hidden < 16 || r.hidden > 4096 || r.hidden % 16) {
+    return fail(TTT_E_SHAPE, "hidden must be a multiple of 16 in [16, 4096] (got %d)", r.hidden);
+  }
+  if (r.chunk < 1 || r.chunk > (1 << 30))
+    return fail(TTT_E_SHAPE, "chunk must be in [1, 2^30] (got %d)", r.chunk);
+  if (r.ns_steps > 0 && r.fw != TTT_FW_LINEAR && r.dim > r.hidden)
+    return fail(TTT_E_UNSUPPORTED, "Newton-Schulz needs dim <= hidden (dim %d, hidden %d)",
+                r.dim, r.hidden);
+  const bool f32 = r.act == TTT_F32;
+  int* pl[4] = {&r.apply_planes, &r.grad_planes, &r.ns_planes, &r.ns_lead_planes};
+  const int dflt[4] = {f32 ? 3 : 1, f32 ? 3 : 2, f32 ? 3 : 2, f32 ? 3 : 2};
+  const char* nm[4] = {"apply_planes", "grad_planes", "ns_planes", "ns_lead_planes"};
+  for (int i = 0; i < 4; ++i) {
+    if (*pl[i] == 0) *pl[i] = dflt[i];
+    if (*pl[i] < 1 || *pl[i] > 3)
+      return fail(TTT_E_CONFIG, "%s must be 0 (default) or 1..3 (got %d)", nm[i], *pl[i]);
+  }
+  if (out) *out = r;
+  return TTT_OK;
+}
+
+Dims dims_of(const ttt_config& c) {
+  Dims D{};
+  D.P = c.batch * c.heads;
+  D.d = c.dim;
+  D.dh = c.hidden;
+  if (c.fw == TTT_FW_SWIGLU) {
+    D.nm = 3;
+    D.n = c.hidden;
+    int r[3] = {c.hidden, c.hidden, c.dim}, k[3] = {c.dim, c.dim, c.hidden}, t[3] = {1, 1, 0};
+    for (int i = 0; i < 3; ++i) { D.rows[i] = r[i]; D.cols[i] = k[i]; D.tr[i] = t[i]; }
+  } else if (c.fw == TTT_FW_MLP_GELU) {
+    D.nm = 2;
+    D.n = c.hidden;
+    D.rows[0] = c.hidden; D.cols[0] = c.dim; D.tr[0] = 1;
+    D.rows[1] = c.dim; D.cols[1] = c.hidden; D.tr[1] = 0;
+  } else {
+    D.nm = 1;
+    D.n = c.dim;
+    D.rows[0] = c.dim; D.cols[0] = c.dim; D.tr[0] = 0;
+  }
+  D.ap = c.apply_planes;
+  D.gp = c.grad_planes;
+  D.np = c.ns_planes;
+  D.nlp = c.ns_lead_planes;
+  D.npm = std::max(D.np, D.nlp);
+  D.wp = std::max(D.ap, D.gp);
+  D.in_q = c.act == TTT_F32 ? D.ap : 1;
+  D.in_kv = c.act == TTT_F32 ? D.gp : 1;
+  D.sb = std::min<int64_t>(c.chunk, SUBBLOCK_MAX);
+  D.bpad = round_up(D.sb, ROW_PAD);
+  return D;
+}
+
+int64_t state_numel(const Dims& D) {
+  int64_t n = 0;
+  for (int m = 0; m < D.nm; ++m) n += (int64_t)D.P * D.rows[m] * D.cols[m];
+  return n;
+}
+
+}  // namespace
+
+// ============================================================================ state
+struct ttt_state {
+  ttt_config cfg;
+  Dims D;
+  char* arena = nullptr;
+  size_t arena_bytes = 0;
+  hipStream_t last = nullptr;
+  int device = 0;
+
+  float* W = nullptr;   // [state_numel] matrix by matrix, each [P][rows][cols]
+  float* U = nullptr;   // same layout
+  float* Wm[3] = {};    // per-matrix views
+  float* Um[3] = {};
+  u16* Wpl[3] = {};     // planes [wp][P][rows][cols]
+  u16* W2t = nullptr;   // planes of W2^T [wp][P][hidden][dim]
+  u16 *qpl = nullptr, *kpl = nullptr, *vpl = nullptr;  // fp32 activations as planes
+  u16 *kt = nullptr, *vt = nullptr, *nkt = nullptr;    // [planes][P][d][bpad]
+  u16* hq = nullptr;                                   // [ap][P][sb][dh]
+  u16 *dz1t = nullptr, *dz3t = nullptr, *pt = nullptr; // [gp][P][dh][bpad]
+  u16 *hk = nullptr, *hkt = nullptr, *e = nullptr, *et = nullptr;
+  float *fa = nullptr, *fb = nullptr;
+  float* G = nullptr;     // [nm][P][d][n]
+  float* part = nullptr;  // [nm*P][contract tiles]
+  u16 *xpl[2] = {}, *xtpl[2] = {}, *apl = nullptr, *bpl = nullptr;
+  float* afp = nullptr;
+  int* health = nullptr;
+  int contract_tiles = 0;
+};
+
+namespace {
+
+struct Carver {
+  size_t off = 0;
+  template <class T>
+  size_t take(int64_t count) {
+    size_t o = off;
+    off += round_up(std::max<int64_t>(count, 1) * (int64_t)sizeof(T), 256);
+    return o;
+  }
+};
+
+// Plan the arena layout; with base == nullptr only the size is computed.
+size_t layout(ttt_state* s, char* base) {
+  const Dims& D = s->D;
+  const ttt_config& c = s->cfg;
+  const int64_t P = D.P, d = D.d, dh = D.dh, n = D.n, sb = D.sb, bp = D.bpad;
+  const bool mse = c.loss == TTT_LOSS_MSE;
+  const bool lin = c.fw == TTT_FW_LINEAR;
+  const bool f32 = c.act == TTT_F32;
+  Carver C;
+  size_t oW = C.take<float>(state_numel(D)), oU = C.take<float>(state_numel(D));
+  size_t oWpl[3];
+  for (int m = 0; m < D.nm; ++m) oWpl[m] = C.take<u16>(D.wp * P * D.rows[m] * D.cols[m]);
+  size_t oW2t = lin ? 0 : C.take<u16>(D.wp * P * dh * d);
+  size_t oq = 0, ok = 0, ov = 0;
+  if (f32) {
+    oq = C.take<u16>(D.in_q * P * sb * d);
+    ok = C.take<u16>(D.in_kv * P * sb * d);
+    ov = C.take<u16>(D.in_kv * P * sb * d);
+  }
+  size_t okt = C.take<u16>(D.in_kv * P * d * bp);
+  size_t ovt = (!mse) ? C.take<u16>(D.in_kv * P * d * bp) : 0;
+  size_t onkt = (lin && !mse) ? C.take<u16>(D.gp * P * d * bp) : 0;
+  size_t ohq = lin ? 0 : C.take<u16>(D.ap * P * sb * dh);
+  size_t odz1 = 0, odz3 = 0, opt = 0, ohk = 0, ohkt = 0, ofa = 0, ofb = 0, oe = 0, oet = 0;
+  if (!lin) {
+    odz1 = C.take<u16>(D.gp * P * dh * bp);
+    if (c.fw == TTT_FW_SWIGLU) odz3 = C.take<u16>(D.gp * P * dh * bp);
+    if (!mse) opt = C.take<u16>(D.gp * P * dh * bp);
+  }
+  if (mse) {
+    if (!lin) {
+      ohk = C.take<u16>(D.gp * P * sb * dh);
+      ohkt = C.take<u16>(D.gp * P * dh * bp);
+      ofa = C.take<float>(P * sb * dh);
+      if (c.fw == TTT_FW_SWIGLU) ofb = C.take<float>(P * sb * dh);
+      oe = C.take<u16>(D.gp * P * sb * d);
+    }
+    oet = C.take<u16>(D.gp * P * d * bp);
+  }
+  size_t oG = C.take<float>(D.nm * P * d * n);
+  const int ctiles = (int)(((d + CONTRACT_BM - 1) / CONTRACT_BM) * ((n + CONTRACT_BN - 1) / CONTRACT_BN));
+  size_t opart = C.take<float>(D.nm * P * ctiles);
+  size_t ox[2] = {0, 0}, oxt[2] = {0, 0}, oa = 0, ob = 0, oafp = 0;
+  if (c.ns_steps > 0) {
+    for (int i = 0; i < 2; ++i) {
+      ox[i] = C.take<u16>(D.npm * D.nm * P * d * n);
+      oxt[i] = C.take<u16>(D.npm * D.nm * P * n * d);
+    }
+    oa = C.take<u16>(D.npm * D.nm * P * d * d);
+    ob = C.take<u16>(D.npm * D.nm * P * d * d);
+    oafp = C.take<float>(D.nm * P * d * d);
+  }
+  size_t oh = C.take<int>(1);
+  if (base) {
+    auto F = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
+    auto H = [&](size_t o) { return reinterpret_cast<u16*>(base + o); };
+    s->W = F(oW);
+    s->U = F(oU);
+    int64_t acc = 0;
+    for (int m = 0; m < D.nm; ++m) {
+      s->Wm[m] = s->W + acc;
+      s->Um[m] = s->U + acc;
+      acc += P * D.rows[m] * D.cols[m];
+      s->Wpl[m] = H(oWpl[m]);
+    }
+    s->W2t = lin ? nullptr : H(oW2t);
+    if (f32) { s->qpl = H(oq); s->kpl = H(ok); s->vpl = H(ov); }
+    s->kt = H(okt);
+    s->vt = mse ? nullptr : H(ovt);
+    s->nkt = (lin && !mse) ? H(onkt) : nullptr;
+    s->hq = lin ? nullptr : H(ohq);
+    if (!lin) {
+      s->dz1t = H(odz1);
+      s->dz3t = c.fw == TTT_FW_SWIGLU ? H(odz3) : nullptr;
+      s->pt = mse ? nullptr : H(opt);
+    }
+    if (mse) {
+      if (!lin) {
+        s->hk = H(ohk); s->hkt = H(ohkt); s->fa = F(ofa);
+        s->fb = c.fw == TTT_FW_SWIGLU ? F(ofb) : nullptr;
+        s->e = H(oe);
+      }
+      s->et = H(oet);
+    }
+    s->G = F(oG);
+    s->part = F(opart);
+    s->contract_tiles = ctiles;
+    if (c.ns_steps > 0) {
+      for (int i = 0; i < 2; ++i) { s->xpl[i] = H(ox[i]); s->xtpl[i] = H(oxt[i]); }
+      s->apl = H(oa); s->bpl = H(ob); s->afp = F(oafp);
+    }
+    s->health = reinterpret_cast<int*>(base + oh);
+  }
+  return C.off;
+}
+
+PlaneBuf pbuf(u16* base, int np, int64_t plane_stride, int64_t zstride, int64_t ld) {
+  PlaneBuf b;
+  b.base = base; b.plane_stride = plane_stride; b.zstride = zstride; b.ld = ld; b.np = np;
+  return b;
+}
+
+// Operand over a caller tensor: element (r, k) of problem z at p + z*zstride + r*ld + k.
+Operand act_operand(const void* p, int64_t zstride, int64_t ld, int rows) {
+  const u16* q = static_cast<const u16*>(p);
+  return make_operand(q, q, q, ld, zstride, 1, rows);
+}
+
+ttt_status refresh_planes(ttt_state* s, bool with_update, hipStream_t st) {
+  const Dims& D = s->D;
+  RenormArgs r{};
+  r.P = D.P; r.np = D.wp; r.renorm = with_update && s->cfg.row_renorm; r.nm = D.nm;
+  r.health = s->health;
+  r.max_rows = 0;
+  for (int m = 0; m < D.nm; ++m) {
+    RenormMat& M = r.m[m];
+    M.W = s->Wm[m];
+    M.U = with_update ? s->Um[m] : nullptr;
+    M.rows = D.rows[m]; M.cols = D.cols[m];
+    M.pl = s->Wpl[m];
+    M.pl_stride = (int64_t)D.P * D.rows[m] * D.cols[m];
+    const bool w2 = (s->cfg.fw != TTT_FW_LINEAR) && m == D.nm - 1;
+    M.plt = w2 ? s->W2t : nullptr;
+    M.plt_stride = (int64_t)D.P * D.rows[m] * D.cols[m];
+    r.max_rows = std::max(r.max_rows, D.rows[m]);
+  }
+  HIP_TRY(launch_renorm(r, st));
+  return TTT_OK;
+}
+
+// Tensor views of one token range [t0, t0+nr) of the caller's [B][H][T][d] tensors.
+struct Rows {
+  const char *q, *k, *v;
+  const float* eta;
+  char* out;
+  int64_t T;    // tokens per problem in the caller's tensors
+  int64_t t0;   // first token of the range
+  int nr;       // number of tokens
+};
+
+ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
+  const Dims& D = s->D;
+  const ttt_config& c = s->cfg;
+  const size_t es = c.act == TTT_BF16 ? 2 : 4;
+  const int P = D.P, d = D.d, dh = D.dh;
+  const char* q = R.q + R.t0 * d * es;
+  Operand xq;
+  if (c.act == TTT_F32) {
+    SplitArgs sa{};
+    sa.x = reinterpret_cast<const float*>(q); sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
+    sa.out = pbuf(s->qpl, D.in_q, (int64_t)P * D.sb * d, D.sb * d, d);
+    HIP_TRY(launch_split(sa, P, st));
+    xq = operand_of(sa.out, D.in_q, R.nr);
+  } else {
+    xq = act_operand(q, R.T * d, d, R.nr);
+  }
+  OutArgs o{};
+  o.nrows = R.nr; o.mrows = R.nr; o.N = d;
+  o.out = R.out + R.t0 * d * es; o.out_zstride = R.T * d; o.out_bf16 = c.act == TTT_BF16;
+  if (c.fw == TTT_FW_LINEAR) {
+    o.a = xq;
+    o.b = operand_of(pbuf(s->Wpl[0], D.ap, (int64_t)P * d * d, (int64_t)d * d, d), D.ap, d);
+    o.K = d;
+    HIP_TRY(launch_out(OUT_Q, o, P, st));
+    return TTT_OK;
+  }
+  FrontArgs f{};
+  f.x = xq;
+  f.w1 = operand_of(pbuf(s->Wpl[0], D.ap, (int64_t)P * dh * d, (int64_t)dh * d, d), D.ap, dh);
+  if (c.fw == TTT_FW_SWIGLU)
+    f.w3 = operand_of(pbuf(s->Wpl[1], D.ap, (int64_t)P * dh * d, (int64_t)dh * d, d), D.ap, dh);
+  f.v = f.x;
+  f.w2t = f.w1;
+  f.nrows = R.nr; f.mrows = R.nr; f.K = d; f.N = dh;
+  f.o1 = pbuf(s->hq, D.ap, (int64_t)P * D.sb * dh, D.sb * dh, dh);
+  HIP_TRY(launch_front(c.fw == TTT_FW_SWIGLU ? FW_SWIGLU : FW_GELU, FRONT_Q, f, P, st));
+  const int w2 = D.nm - 1;
+  o.a = operand_of(f.o1, D.ap, R.nr);
+  o.b = operand_of(pbuf(s->Wpl[w2], D.ap, (int64_t)P * d * dh, (int64_t)d * dh, dh), D.ap, d);
+  o.K = dh;
+  HIP_TRY(launch_out(OUT_Q, o, P, st));
+  return TTT_OK;
+}
+
+// Gradient of one token block; the contraction adds into G (first block writes it).
+ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStream_t st) {
+  const Dims& D = s->D;
+  const ttt_config& c = s->cfg;
+  const size_t es = c.act == TTT_BF16 ? 2 : 4;
+  const int P = D.P, d = D.d, dh = D.dh;
+  const int64_t bp = round_up(R.nr, ROW_PAD), BP = D.bpad;
+  const bool mse = c.loss == TTT_LOSS_MSE, lin = c.fw == TTT_FW_LINEAR;
+  const bool sw = c.fw == TTT_FW_SWIGLU;
+  const char* k = R.k + R.t0 * d * es;
+  const char* v = R.v + R.t0 * d * es;
+  const float* eta = R.eta + R.t0;
+  const int gi = D.in_kv, gp = D.gp;
+
+  Operand xk, xv;
+  if (c.act == TTT_F32) {
+    SplitArgs sa{};
+    sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
+    sa.x = reinterpret_cast<const float*>(k);
+    sa.out = pbuf(s->kpl, gi, (int64_t)P * D.sb * d, D.sb * d, d);
+    HIP_TRY(launch_split(sa, P, st));
+    xk = operand_of(sa.out, gi, R.nr);
+    sa.x = reinterpret_cast<const float*>(v);
+    sa.out = pbuf(s->vpl, gi, (int64_t)P * D.sb * d, D.sb * d, d);
+    HIP_TRY(launch_split(sa, P, st));
+    xv = operand_of(sa.out, gi, R.nr);
+  } else {
+    xk = act_operand(k, R.T * d, d, R.nr);
+    xv = act_operand(v, R.T * d, d, R.nr);
+  }
+
+  // token-major -> feature-major copies for the contractions
+  TransposeArgs ta{};
+  ta.x_zstride = R.T * d; ta.x_bf16 = c.act == TTT_BF16; ta.eta = eta; ta.eta_zstride = R.T;
+  ta.n = R.nr; ta.d = d; ta.bpad = (int)bp;
+  PlaneBuf kt = pbuf(s->kt, gi, (int64_t)P * d * BP, (int64_t)d * BP, BP);
+  PlaneBuf vt{}, nkt{};
+  if (!(lin && !mse)) {
+    ta.x = k; ta.neg_eta = 0; ta.out = kt;
+    HIP_TRY(launch_transpose(ta, P, st));
+  }
+  if (!mse) {
+    vt = pbuf(s->vt, gi, (int64_t)P * d * BP, (int64_t)d * BP, BP);
+    ta.x = v; ta.neg_eta = 0; ta.out = vt;
+    HIP_TRY(launch_transpose(ta, P, st));
+  }
+  if (lin && !mse) {
+    nkt = pbuf(s->nkt, gp, (int64_t)P * d * BP, (int64_t)d * BP, BP);
+    ta.x = k; ta.neg_eta = 1; ta.out = nkt;
+    HIP_TRY(launch_transpose(ta, P, st));
+  }
+
+  auto wop = [&](int m, int np) {
+    return operand_of(pbuf(s->Wpl[m], np, (int64_t)P * D.rows[m] * D.cols[m],
+                           (int64_t)D.rows[m] * D.cols[m], D.cols[m]), np, D.rows[m]);
+  };
+  PlaneBuf dz1t{}, dz3t{}, pt{}, hkt{}, et{};
+  if (!lin) {
+    dz1t = pbuf(s->dz1t, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
+    if (sw) dz3t = pbuf(s->dz3t, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
+  }
+  const int w2 = D.nm - 1;
+  Operand w2t{};
+  if (!lin) w2t = operand_of(pbuf(s->W2t, gp, (int64_t)P * dh * d, (int64_t)dh * d, d), gp, dh);
+
+  if (!lin && !mse) {
+    pt = pbuf(s->pt, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
+    FrontArgs f{};
+    f.x = xk; f.v = xv; f.w1 = wop(0, gp);
+    if (sw) f.w3 = wop(1, gp);
+    f.w2t = w2t;
+    f.eta = eta; f.eta_zstride = R.T;
+    f.nrows = R.nr; f.mrows = (int)bp; f.K = d; f.N = dh;
+    f.o1 = dz1t; f.o2 = dz3t; f.o3 = pt;
+    HIP_TRY(launch_front(sw ? FW_SWIGLU : FW_GELU, FRONT_K_DOT, f, P, st));
+  } else if (mse) {
+    Operand ok_a;
+    if (!lin) {
+      hkt = pbuf(s->hkt, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
+      FrontArgs f{};
+      f.x = xk; f.v = xk; f.w1 = wop(0, gp);
+      if (sw) f.w3 = wop(1, gp);
+      f.w2t = f.w1;
+      f.nrows = R.nr; f.mrows = (int)bp; f.K = d; f.N = dh;
+      f.o1 = pbuf(s->hk, gp, (int64_t)P * D.sb * dh, D.sb * dh, dh);
+      f.o2 = hkt;
+      f.fa = s->fa; f.fb = s->fb; f.f_zstride = D.sb * dh;
+      HIP_TRY(launch_front(sw ? FW_SWIGLU : FW_GELU, FRONT_K_MSE, f, P, st));
+      ok_a = operand_of(f.o1, gp, R.nr);
+    } else {
+      ok_a = xk;
+    }
+    et = pbuf(s->et, gp, (int64_t)P * d * BP, (int64_t)d * BP, BP);
+    OutArgs o{};
+    o.a = ok_a;
+    o.b = wop(w2, gp);   // W2 [d][dh] (or W [d][d]) as the [N][K] operand
+    o.nrows = R.nr; o.mrows = (int)bp; o.K = lin ? d : dh; o.N = d;
+    o.vin = v; o.v_zstride = R.T * d; o.v_bf16 = c.act == TTT_BF16;
+    o.eta = eta; o.eta_zstride = R.T;
+    o.e = lin ? et : pbuf(s->e, gp, (int64_t)P * D.sb * d, D.sb * d, d);
+    o.et = et;
+    if (lin) o.e.np = 0;   // the linear net needs only E^T
+    HIP_TRY(launch_out(OUT_K_MSE, o, P, st));
+    if (!lin) {
+      OutArgs h{};
+      h.a = operand_of(o.e, gp, R.nr);
+      h.b = w2t;
+      h.nrows = R.nr; h.mrows = (int)bp; h.K = d; h.N = dh;
+      h.fa = s->fa; h.fb = s->fb; h.f_zstride = D.sb * dh;
+      h.dz1t = dz1t; h.dz3t = dz3t; h.swiglu = sw;
+      HIP_TRY(launch_out(DH_MSE, h, P, st));
+    }
+  }
+
+  // contraction: X_m [d x n] = A_m (feature-major, tokens contiguous) . B_m^T
+  ContractArgs ca{};
+  ca.P = P; ca.M = d; ca.N = D.n; ca.K = (int)bp;
+  auto op = [&](const PlaneBuf& b, int rows) { return operand_of(b, b.np, rows); };
+  if (lin) {
+    if (mse) { ca.a[0] = op(et, d); ca.b[0] = op(kt, d); }
+    else { ca.a[0] = op(vt, d); ca.b[0] = op(nkt, d); }
+  } else {
+    ca.a[0] = op(kt, d); ca.b[0] = op(dz1t, dh);
+    int m = 1;
+    if (sw) { ca.a[1] = op(kt, d); ca.b[1] = op(dz3t, dh); m = 2; }
+    if (mse) { ca.a[m] = op(et, d); ca.b[m] = op(hkt, dh); }
+    else { ca.a[m] = op(vt, d); ca.b[m] = op(pt, dh); }
+  }
+  ca.G = s->G;
+  ca.accum_in = first ? 0 : 1;
+  ca.last = last ? 1 : 0;
+  ca.muon = c.ns_steps > 0;
+  const int64_t Z = (int64_t)D.nm * P;
+  if (ca.muon) {
+    ca.x = pbuf(s->xpl[0], D.nlp, Z * d * D.n, (int64_t)d * D.n, D.n);
+    ca.xt = pbuf(s->xtpl[0], D.nlp, Z * D.n * d, (int64_t)D.n * d, d);
+  }
+  ca.part = s->part;
+  ca.U = s->U;
+  ca.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
+  HIP_TRY(launch_contract(ca, D.nm, st));
+  return TTT_OK;
+}
+
+ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
+  const Dims& D = s->D;
+  const int steps = s->cfg.ns_steps;
+  const int Z = D.nm * D.P, M = D.d, N = D.n;
+  for (int it = 0; it < steps; ++it) {
+    const int pk = it == 0 ? D.nlp : D.np;
+    const int pn = D.np;
+    NsArgs a{};
+    a.Z = Z; a.M = M; a.N = N; a.P = D.P;
+    a.coef_a = 3.4445f; a.coef_b = -4.7750f; a.coef_c = 2.0315f;
+    a.part = s->part; a.nparts = s->contract_tiles; a.first = it == 0; a.last = it == steps - 1;
+    a.eps = 1e-7f;
+    a.xin = pbuf(s->xpl[it & 1], pk, (int64_t)Z * M * N, (int64_t)M * N, N);
+    a.afp = s->afp;
+    a.aout = pbuf(s->apl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
+    HIP_TRY(launch_ns_gram(a, st));
+    a.ain = a.aout;
+    a.aout = pbuf(s->bpl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
+    HIP_TRY(launch_ns_poly(a, st));
+    a.ain = a.aout;
+    a.xtin = pbuf(s->xtpl[it & 1], pk, (int64_t)Z * N * M, (int64_t)N * M, M);
+    a.G = s->G;
+    a.xout = pbuf(s->xpl[(it + 1) & 1], pn, (int64_t)Z * M * N, (int64_t)M * N, N);
+    a.xtout = pbuf(s->xtpl[(it + 1) & 1], pn, (int64_t)Z * N * M, (int64_t)N * M, M);
+    a.U = s->U;
+    a.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
+    HIP_TRY(launch_ns_update(a, st));
+  }
+  return TTT_OK;
+}
+
+ttt_status run_chunk(ttt_state* s, const Rows& R0, hipStream_t st) {
+  const ttt_config& c = s->cfg;
+  const Dims& D = s->D;
+  const int64_t b = c.chunk;
+  ttt_status r;
+  auto apply_all = [&]() -> ttt_status {
+    for (int64_t o = 0; o < b; o += D.sb) {
+      Rows R = R0;
+      R.t0 = R0.t0 + o;
+      R.nr = (int)std::min<int64_t>(D.sb, b - o);
+      ttt_status x = apply_rows(s, R, st);
+      if (x != TTT_OK) return x;
+    }
+    return TTT_OK;
+  };
+  if (c.order == TTT_APPLY_THEN_UPDATE && (r = apply_all()) != TTT_OK) return r;
+  for (int64_t o = 0; o < b; o += D.sb) {
+    Rows R = R0;
+    R.t0 = R0.t0 + o;
+    R.nr = (int)std::min<int64_t>(D.sb, b - o);
+    if ((r = grad_rows(s, R, o == 0, o + D.sb >= b, st)) != TTT_OK) return r;
+  }
+  if (c.ns_steps > 0 && (r = newton_schulz(s, st)) != TTT_OK) return r;
+  if ((r = refresh_planes(s, true, st)) != TTT_OK) return r;
+  if (c.order == TTT_UPDATE_THEN_APPLY && (r = apply_all()) != TTT_OK) return r;
+  return TTT_OK;
+}
+
+ttt_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(TTT_E_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16)
+    return fail(TTT_E_ALIGN, "%s is not 16-byte aligned", name);
+  return TTT_OK;
+}
+
+ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, const float* eta,
+                   void* out, int64_t T, int64_t nchunks, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  if (T == 0) return TTT_OK;
+  ttt_status r;
+  if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v")) ||
+      (r = check_ptr(eta, "eta")) || (r = check_ptr(out, "out")))
+    return r;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s->last = st;
+  Rows R{};
+  R.q = static_cast<const char*>(q);
+  R.k = static_cast<const char*>(k);
+  R.v = static_cast<const char*>(v);
+  R.eta = eta;
+  R.out = static_cast<char*>(out);
+  R.T = T;
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    R.t0 = ci * s->cfg.chunk;
+    if ((r = run_chunk(s, R, st)) != TTT_OK) return r;
+  }
+  return TTT_OK;
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+extern "C" {
+
+ttt_status ttt_validate_config(const ttt_config* cfg) { return resolve(cfg, nullptr); }
+
+ttt_status ttt_state_numel(const ttt_config* cfg, int64_t* numel) {
+  ttt_config r;
+  ttt_status st = resolve(cfg, &r);
+  if (st != TTT_OK) return st;
+  if (!numel) return fail(TTT_E_NULL, "numel is NULL");
+  *numel = state_numel(dims_of(r));
+  return TTT_OK;
+}
+
+ttt_status ttt_init_state(const ttt_config* cfg, const float* w0, void* stream,
+                          ttt_state** out) {
+  if (!out) return fail(TTT_E_NULL, "out is NULL");
+  *out = nullptr;
+  ttt_config r;
+  ttt_status st = resolve(cfg, &r);
+  if (st != TTT_OK) return st;
+  if ((st = check_ptr(w0, "w0")) != TTT_OK) return st;
+  ttt_state* s = new (std::nothrow) ttt_state();
+  if (!s) return fail(TTT_E_ALLOC, "host allocation failed");
+  s->cfg = r;
+  s->D = dims_of(r);
+  s->arena_bytes = layout(s, nullptr);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  s->last = hs;
+  hipError_t e = hipGetDevice(&s->device);
+  if (e == hipSuccess) e = hipMalloc(&s->arena, s->arena_bytes);
+  if (e != hipSuccess) {
+    ttt_status code = (e == hipErrorOutOfMemory) ? TTT_E_ALLOC : TTT_E_HIP;
+    fail(code, "device allocation of %zu bytes failed: %s", s->arena_bytes, hipGetErrorString(e));
+    delete s;
+    return code;
+  }
+  layout(s, s->arena);
+  auto cleanup = [&](ttt_status code) {
+    hipFree(s->arena);
+    delete s;
+    return code;
+  };
+  e = hipMemsetAsync(s->arena, 0, s->arena_bytes, hs);
+  // broadcast the per-head initial matrices over the batch
+  const Dims& D = s->D;
+  const float* src = w0;
+  for (int m = 0; m < D.nm && e == hipSuccess; ++m) {
+    const size_t per_head = (size_t)D.rows[m] * D.cols[m];
+    for (int b = 0; b < r.batch && e == hipSuccess; ++b)
+      e = hipMemcpyAsync(s->Wm[m] + (size_t)b * r.heads * per_head, src,
+                         per_head * r.heads * sizeof(float), hipMemcpyDeviceToDevice, hs);
+    src += per_head * r.heads;
+  }
+  if (e != hipSuccess) return cleanup(fail(TTT_E_HIP, "init copy failed: %s", hipGetErrorString(e)));
+  st = refresh_planes(s, false, hs);
+  if (st != TTT_OK) return cleanup(st);
+  *out = s;
+  return TTT_OK;
+}
+
+ttt_status ttt_chunk_forward(ttt_state* s, const void* q, const void* k, const void* v,
+                             const float* eta, void* out, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  return forward(s, q, k, v, eta, out, s->cfg.chunk, 1, stream);
+}
+
+ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, const void* v,
+                                const float* eta, void* out, int64_t seq_len, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  if (seq_len < 0) return fail(TTT_E_SHAPE, "seq_len is negative");
+  if (seq_len % s->cfg.chunk)
+    return fail(TTT_E_SHAPE, "seq_len %lld is not a multiple of the chunk %d",
+                (long long)seq_len, s->cfg.chunk);
+  return forward(s, q, k, v, eta, out, seq_len, seq_len / s->cfg.chunk, stream);
+}
+
+ttt_status ttt_get_state(const ttt_state* s, float* dst, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  ttt_status st = check_ptr(dst, "dst");
+  if (st != TTT_OK) return st;
+  HIP_TRY(hipMemcpyAsync(dst, s->W, state_numel(s->D) * sizeof(float), hipMemcpyDeviceToDevice,
+                         static_cast<hipStream_t>(stream)));
+  return TTT_OK;
+}
+
+ttt_status ttt_set_state(ttt_state* s, const float* src, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  ttt_status st = check_ptr(src, "src");
+  if (st != TTT_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  s->last = hs;
+  HIP_TRY(hipMemcpyAsync(s->W, src, state_numel(s->D) * sizeof(float), hipMemcpyDeviceToDevice, hs));
+  HIP_TRY(hipMemsetAsync(s->health, 0, sizeof(int), hs));
+  return refresh_planes(s, false, hs);
+}
+
+ttt_status ttt_state_health(ttt_state* s) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  HIP_TRY(hipStreamSynchronize(s->last));
+  int h = 0;
+  HIP_TRY(hipMemcpy(&h, s->health, sizeof(int), hipMemcpyDeviceToHost));
+  if (h) return fail(TTT_E_NONFINITE, "a NaN or Inf reached the fast-weight state");
+  return TTT_OK;
+}
+
+ttt_status ttt_destroy_state(ttt_state* s) {
+  if (!s) return TTT_OK;
+  hipError_t e1 = hipStreamSynchronize(s->last);
+  hipError_t e2 = hipFree(s->arena);
+  delete s;
+  if (e1 != hipSuccess) return fail(TTT_E_HIP, "sync before free failed: %s", hipGetErrorString(e1));
+  if (e2 != hipSuccess) return fail(TTT_E_HIP, "hipFree failed: %s", hipGetErrorString(e2));
+  return TTT_OK;
+}
+
+const char* ttt_status_str(ttt_status st) {
+  switch (st) {
+    case TTT_OK: return "ok";
+    case TTT_E_NULL: return "null pointer";
+    case TTT_E_SHAPE: return "bad shape";
+    case TTT_E_DTYPE: return "bad dtype";
+    case TTT_E_CONFIG: return "bad configuration";
+    case TTT_E_UNSUPPORTED: return "unsupported configuration";
+    case TTT_E_ALLOC: return "allocation failed";
+    case TTT_E_HIP: return "HIP runtime error";
+    case TTT_E_NONFINITE: return "non-finite value in the state";
+    case TTT_E_ALIGN: return "misaligned pointer";
+  }
+  return "unknown status";
+}
+
+const char* ttt_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Internal interface between the host library (libttt.cpp) and the HIP kernels
+// (ttt_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ttt_device.hpp"
+
+namespace ttt {
+
+// A buffer of 1..3 bf16 planes: plane q of problem z, row r, column c lives at
+// base[q * plane_stride + z * zstride + r * ld + c].
+struct PlaneBuf {
+  u16* base;
+  int64_t plane_stride;
+  int64_t zstride;
+  int64_t ld;
+  int32_t np;
+};
+
+__host__ __device__ inline Operand operand_of(const PlaneBuf& b, int np, int rows) {
+  return make_operand(b.base, b.base + b.plane_stride, b.base + 2 * b.plane_stride, b.ld,
+                      b.zstride, np, rows);
+}
+
+enum FwKind { FW_SWIGLU = 0, FW_GELU = 1, FW_LINEAR = 2 };
+enum FrontMode { FRONT_Q = 0, FRONT_K_DOT = 1, FRONT_K_MSE = 2 };
+enum OutMode { OUT_Q = 0, OUT_K_MSE = 1, DH_MSE = 2 };
+
+// Z-GEMMs over rows of Q or K: X W1^T (and X W3^T), plus V W2 for the inner-product loss.
+struct FrontArgs {
+  Operand x, v, w1, w3, w2t;
+  const float* eta;
+  int64_t eta_zstride;
+  int nrows;   // valid token rows
+  int mrows;   // rows the grid covers (rows in [nrows, mrows) produce zeros)
+  int K;       // dim
+  int N;       // hidden
+  int tiles_n;
+  PlaneBuf o1, o2, o3;  // Q: hidden planes | K_DOT: dZ1^T, dZ3^T (or dZ^T), P^T | K_MSE: H, H^T
+  float* fa;            // K_MSE: derivative factors [rows][hidden]
+  float* fb;
+  int64_t f_zstride;
+};
+
+// GEMMs that end in the model dimension (O = H W2^T, Ok = H W2^T) and the hidden-error GEMM
+// dH = E W2 for the MSE loss.
+struct OutArgs {
+  Operand a, b;
+  int nrows, mrows, K, N, tiles_n;
+  // OUT_Q
+  void* out;
+  int64_t out_zstride;
+  int out_bf16;
+  // OUT_K_MSE
+  const void* vin;
+  int64_t v_zstride;
+  int v_bf16;
+  const float* eta;
+  int64_t eta_zstride;
+  PlaneBuf e, et;
+  // DH_MSE
+  const float* fa;
+  const float* fb;
+  int64_t f_zstride;
+  PlaneBuf dz1t, dz3t;
+  int swiglu;
+};
+
+// Token contractions: X_m[i][j] = sum_t A_m[i][t] B_m[j][t] for every matrix m and problem.
+struct ContractArgs {
+  Operand a[3], b[3];
+  int P, M, N, K, tiles_n, tiles;
+  float* G;        // [nm][P][M][N]
+  int accum_in;    // add the running sum held in G
+  int last;        // last token block of the chunk
+  int muon;        // write X0 planes, X0^T planes and per-tile sums of squares
+  PlaneBuf x, xt;
+  float* part;     // [nm*P][tiles]
+  float* U;        // plain step: U in weight orientation [nm][P][rows][cols]
+  int tr_mask;     // bit m: matrix m's weight is the transpose of its X orientation
+};
+
+// Newton-Schulz stages on Z = nm*P matrices X [M x N] (M <= N).
+struct NsArgs {
+  int Z, M, N, tiles_n, tiles;
+  float coef_a, coef_b, coef_c;
+  const float* part;  // iteration 0: per-tile sums of squares of the unscaled gradient
+  int nparts;
+  int first;          // iteration 0 (fold the 1/(|G|_F + eps) scale)
+  int last;           // final iteration: write U instead of planes
+  float eps;
+  PlaneBuf xin;       // gram: X planes [M][N]
+  PlaneBuf ain;       // poly: A planes [M][M] ; update: B planes [M][M]
+  PlaneBuf xtin;      // update: X^T planes [N][M]
+  float* afp;         // gram out / poly in: A fp32 [Z][M][M]
+  PlaneBuf aout;      // gram: A planes ; poly: B planes
+  float* G;           // update: X fp32 [Z][M][N], in/out
+  PlaneBuf xout, xtout;
+  float* U;           // last: U in weight orientation
+  int tr_mask;
+  int P;
+};
+
+struct RenormMat {
+  float* W;        // [P][rows][cols]
+  const float* U;  // same layout, or null (planes refresh only)
+  int rows, cols;
+  u16* pl;         // planes [np][P][rows][cols]
+  int64_t pl_stride;
+  u16* plt;        // transposed planes [np][P][cols][rows], or null
+  int64_t plt_stride;
+};
+struct RenormArgs {
+  RenormMat m[3];
+  int P, np, renorm, nm, max_rows;
+  int* health;
+};
+
+struct TransposeArgs {
+  const void* x;   // rows [n][d] of problem z at x + z * x_zstride (elements)
+  int64_t x_zstride;
+  int x_bf16;
+  const float* eta;
+  int64_t eta_zstride;
+  int neg_eta;     // multiply row t by -eta_t
+  int n, d, bpad;
+  PlaneBuf out;    // [np][Z][d][bpad]
+};
+
+struct SplitArgs {
+  const float* x;
+  int64_t x_zstride;
+  int n, d;
+  PlaneBuf out;    // [np][Z][rows][d]
+};
+
+// ---------------------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  `lds_limit` handling and tile choice are
+// internal.  `Z` is the number of (batch, head) problems.
+hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s);
+hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s);
+hipError_t launch_contract(const ContractArgs& a, int nm, hipStream_t s);
+hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s);
+hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s);
+hipError_t launch_ns_update(const NsArgs& a, hipStream_t s);
+hipError_t launch_renorm(const RenormArgs& a, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, int Z, hipStream_t s);
+hipError_t launch_split(const SplitArgs& a, int Z, hipStream_t s);
+hipError_t prepare_kernels();  // raise dynamic-LDS limits once per process
+
+// tile sizes used by the contraction and Newton-Schulz stages (the host sizes buffers)
+constexpr int CONTRACT_BM = 128, CONTRACT_BN = 128;
+int ns_tile(int Z, int M);     // 64 or 128
+int ns_tri_tiles(int M, int tile);
+
+}  // namespace ttt
