@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Throughput of the large-chunk TTT layer forward on one MI355X.
+
+A step is one ttt_sequence_forward over the whole synthetic batch: every chunk's apply,
+gradient, Newton-Schulz orthogonalisation, update and row renorm, chunk after chunk. The
+state carries over from step to step (the cost of a step does not depend on the state).
+Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line with tokens/s, the roofline of the dominant stage kernel (its
+algorithmic FLOP per launch over its average launch time, taken with HIP events on the
+launch stream during the timed steps) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_flops(cfg) -> dict:
+    """Algorithmic FLOP of one launch of each stage kernel (one chunk, all problems; 2 per
+    multiply-add; Newton-Schulz counted without symmetry savings)."""
+    P, b, d, dh = cfg.batch * cfg.heads, cfg.chunk, cfg.dim, cfg.hidden
+    nz = {"swiglu": 2, "gelu": 1, "linear": 1}[cfg.fw]
+    nm = {"swiglu": 3, "gelu": 2, "linear": 1}[cfg.fw]
+    n = d if cfg.fw == "linear" else dh
+    f = {}
+    if cfg.fw != "linear":
+        f["front_q"] = 2.0 * nz * b * d * dh * P
+        f["front_k"] = 2.0 * (nz + (1 if cfg.loss == "dot" else 0)) * b * d * dh * P
+        f["out"] = 2.0 * b * d * dh * P
+    else:
+        f["out"] = 2.0 * b * d * d * P
+    f["contract"] = 2.0 * nm * b * d * n * P
+    m = d
+    f["ns_gram"] = 2.0 * m * m * n * nm * P
+    f["ns_poly"] = 2.0 * m * m * m * nm * P
+    f["ns_update"] = 2.0 * m * m * n * nm * P
+    return f
+
+
+def total_flops(cfg) -> float:
+    """Algorithmic FLOP of the whole sequence forward (all problems, all chunks)."""
+    d, dh = cfg.dim, cfg.hidden
+    per_tok = {("swiglu", "dot"): 18, ("swiglu", "mse"): 20, ("gelu", "dot"): 12,
+               ("gelu", "mse"): 14}.get((cfg.fw, cfg.loss), 0) * d * dh
+    if cfg.fw == "linear":
+        per_tok = (4 if cfg.loss == "dot" else 6) * d * d
+    nm = {"swiglu": 3, "gelu": 2, "linear": 1}[cfg.fw]
+    n = d if cfg.fw == "linear" else dh
+    ns = cfg.ns_steps * nm * (4.0 * d * d * n + 2.0 * d ** 3)
+    P = cfg.batch * cfg.heads
+    return P * (cfg.seq_len * per_tok + cfg.n_chunks * ns)
+
+
+def cpu_baseline(cfg, budget_chunks=None):
+    """The oracle on the host: one (batch, head) problem over its first chunks."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.ttt_oracle as orc
+    import ttt_inputs as ti
+
+    nc = cfg.n_chunks if budget_chunks is None else min(cfg.n_chunks, budget_chunks)
+    T = nc * cfg.chunk
+    p = ti.make_problem_inputs(cfg, 0, 0, t1=T)
+    w0 = [w[0] for w in ti.make_weights(cfg)]
+    t0 = time.perf_counter()
+    orc.sequence_forward(cfg, w0, p["q"], p["k"], p["v"], p["eta"], n_chunks=nc)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1])
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"1 of {cfg.batch * cfg.heads} (batch, head) problems, {nc} chunks "
+                      f"({T} tokens), numpy fp64, {dt:.1f} s; problems are independent so "
+                      f"the rate is the whole workload's"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="lm")
+    ap.add_argument("--planes", default=None, help="apply,grad,ns,ns_lead bf16 plane counts")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-chunks", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the layer's (batch, head) problems shard across GPUs with no communication, "
+              "but this build measures one GPU only)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ttt_inputs as ti
+    import weight_sequence_layers_amd as W
+
+    cfg = ti.CONFIGS[args.workload]
+    planes = tuple(int(x) for x in args.planes.split(",")) if args.planes else W.PRECISION[cfg.name]
+    c = W.make_config(cfg, planes=planes)
+    torch.cuda.set_device(0)
+    log(f"workload {cfg}  planes {planes}")
+
+    t = time.perf_counter()
+    inp = ti.make_inputs(cfg)
+    log(f"inputs generated in {time.perf_counter() - t:.1f} s")
+    dev = []
+    for n in ("q", "k", "v"):
+        if cfg.act == "bf16":
+            dev.append(torch.from_numpy(inp[n + "_bits"].view(np.int16)).cuda().view(torch.bfloat16))
+        else:
+            dev.append(torch.from_numpy(inp[n]).cuda())
+    eta = torch.from_numpy(inp["eta"]).cuda()
+    w0 = torch.from_numpy(np.concatenate([w.ravel() for w in inp["w0"]])).cuda()
+    out = torch.empty_like(dev[0])
+    del inp
+    st = W.ttt_init_state(c, w0)
+
+    def step():
+        W.ttt_sequence_forward(st, *dev, eta, out, cfg.seq_len)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # find the stage with the largest total time (one traced step per stage, untimed)
+    flops = stage_flops(cfg)
+    totals = {}
+    for name in flops:
+        W.ttt_profile_begin(st, name, 1 << 14)
+        step()
+        n, ms = W.ttt_profile_end(st)
+        if n:
+            totals[name] = (n, ms)
+    dom = max(totals, key=lambda k: totals[k][1])
+    log("per-stage time in one step: " + ", ".join(
+        f"{k} {v[1]:.3f} ms/{v[0]}" for k, v in sorted(totals.items(), key=lambda x: -x[1][1])))
+
+    # timed region, with the dominant stage's launches bracketed by HIP events
+    torch.cuda.synchronize()
+    W.ttt_profile_begin(st, dom, 1 << 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_dom, ms_dom = W.ttt_profile_end(st)
+    W.ttt_state_health(st)
+
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    tokens = cfg.batch * cfg.seq_len
+    value = tokens * args.steps / elapsed
+    tf_layer = total_flops(cfg) / (elapsed / args.steps) / 1e12
+    avg_s = ms_dom / max(n_dom, 1) / 1e3
+    achieved = flops[dom] / avg_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches": n_dom}
+    res = {
+        "metric": "TTT-layer tokens/sec (update+apply) at chunk 2048; % bf16 MFMA peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: batch {cfg.batch}, heads {cfg.heads}, seq "
+                               f"{cfg.seq_len}, chunk {cfg.chunk}, dim {cfg.dim}, hidden "
+                               f"{cfg.hidden}, {cfg.fw}/{cfg.loss}, ns {cfg.ns_steps}, renorm "
+                               f"{int(cfg.renorm)}, {cfg.act}, {cfg.order}",
+                   "global_batch": cfg.batch, "seq_len": cfg.seq_len, "parallelism": "none",
+                   "bf16_planes_apply_grad_ns_nslead": list(planes)},
+        "layer_tflops_algorithmic": round(tf_layer, 2),
+        "pct_bf16_peak_algorithmic": round(100 * tf_layer / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+    }
+    st.destroy()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_chunks)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

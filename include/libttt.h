@@ -134,6 +134,24 @@ ttt_status ttt_state_health(ttt_state* s);
 /* Wait for the state's work and free it.  NULL is accepted.                            */
 ttt_status ttt_destroy_state(ttt_state* s);
 
+/*
+ * Measurement hooks.  Between ttt_profile_begin and ttt_profile_end, every launch of the
+ * chosen stage kernel on the state's stream is bracketed by a pair of HIP events (at most
+ * max_launches launches are timed; later ones run untimed).  ttt_profile_end waits for the
+ * stream and returns the number of timed launches and the sum of their durations in ms.
+ * Stages: 0 front (query rows), 1 front (key rows), 2 output GEMM, 3 token contraction,
+ * 4 Newton-Schulz Gram, 5 Newton-Schulz polynomial, 6 Newton-Schulz update,
+ * 7 update + renorm, 8 token transpose, 9 fp32 plane split, 10 MSE error / dH GEMMs.
+ * The hooks create and destroy HIP events but allocate no device memory.
+ */
+typedef enum {
+  TTT_STAGE_FRONT_Q = 0, TTT_STAGE_FRONT_K = 1, TTT_STAGE_OUT = 2, TTT_STAGE_CONTRACT = 3,
+  TTT_STAGE_NS_GRAM = 4, TTT_STAGE_NS_POLY = 5, TTT_STAGE_NS_UPDATE = 6, TTT_STAGE_RENORM = 7,
+  TTT_STAGE_TRANSPOSE = 8, TTT_STAGE_SPLIT = 9, TTT_STAGE_MSE = 10, TTT_STAGE_COUNT = 11
+} ttt_stage;
+ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches);
+ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms);
+
 /* Static description of a status, and the calling thread's last error message.         */
 const char* ttt_status_str(ttt_status st);
 const char* ttt_last_error(void);

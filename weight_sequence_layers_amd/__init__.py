@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "ttt_set_state": [vp, vp, vp],
             "ttt_state_health": [vp],
             "ttt_destroy_state": [vp],
+            "ttt_profile_begin": [vp, ctypes.c_int32, ctypes.c_int32],
+            "ttt_profile_end": [vp, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -185,6 +187,24 @@ def ttt_state_health(st: State) -> None:
 
 def ttt_destroy_state(st: State) -> None:
     st.destroy()
+
+
+STAGES = {"front_q": 0, "front_k": 1, "out": 2, "contract": 3, "ns_gram": 4, "ns_poly": 5,
+          "ns_update": 6, "renorm": 7, "transpose": 8, "split": 9, "mse": 10}
+
+
+def ttt_profile_begin(st: State, stage, max_launches: int = 4096) -> None:
+    """Bracket every launch of one stage kernel with HIP events (see include/libttt.h)."""
+    sid = STAGES[stage] if isinstance(stage, str) else int(stage)
+    _check(lib().ttt_profile_begin(st.handle, sid, int(max_launches)))
+
+
+def ttt_profile_end(st: State):
+    """Returns (timed launches, total milliseconds)."""
+    n = ctypes.c_int64()
+    ms = ctypes.c_double()
+    _check(lib().ttt_profile_end(st.handle, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def matrix_shapes(cfg: ttt_config):

@@ -38,7 +38,6 @@ ttt_status fail(ttt_status st, const char* fmt, ...) {
   } while (0)
 
 constexpr int64_t SUBBLOCK_MAX = 65536;  // tokens per gradient / apply launch
-constexpr int ROW_PAD = 128;            // token padding of transposed buffers
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -46,7 +45,7 @@ struct Dims {
   int P, nm, d, dh, n;      // problems, matrices, dim, hidden, columns of X orientation
   int rows[3], cols[3], tr[3];
   int ap, gp, np, nlp, npm, wp, in_q, in_kv;
-  int64_t sb, bpad;         // tokens per sub-block, padded token rows of transposed buffers
+  int64_t sb;               // tokens per gradient / apply block
 };
 
 ttt_status resolve(const ttt_config* c, ttt_config* out) {
@@ -117,7 +116,6 @@ Dims dims_of(const ttt_config& c) {
   D.in_q = c.act == TTT_F32 ? D.ap : 1;
   D.in_kv = c.act == TTT_F32 ? D.gp : 1;
   D.sb = std::min<int64_t>(c.chunk, SUBBLOCK_MAX);
-  D.bpad = round_up(D.sb, ROW_PAD);
   return D;
 }
 
@@ -144,18 +142,22 @@ struct ttt_state {
   float* Um[3] = {};
   u16* Wpl[3] = {};     // planes [wp][P][rows][cols]
   u16* W2t = nullptr;   // planes of W2^T [wp][P][hidden][dim]
+  // token-major workspaces, [planes][P][sb][cols]
   u16 *qpl = nullptr, *kpl = nullptr, *vpl = nullptr;  // fp32 activations as planes
-  u16 *kt = nullptr, *vt = nullptr, *nkt = nullptr;    // [planes][P][d][bpad]
-  u16* hq = nullptr;                                   // [ap][P][sb][dh]
-  u16 *dz1t = nullptr, *dz3t = nullptr, *pt = nullptr; // [gp][P][dh][bpad]
-  u16 *hk = nullptr, *hkt = nullptr, *e = nullptr, *et = nullptr;
-  float *fa = nullptr, *fb = nullptr;
+  u16* nk = nullptr;                                   // -eta * K (linear net, dot loss)
+  u16* hq = nullptr;                                   // query hidden [ap][P][sb][dh]
+  u16 *dz1 = nullptr, *dz3 = nullptr, *pk = nullptr;   // [gp][P][sb][dh]
+  u16 *hk = nullptr, *e = nullptr;                     // MSE: hidden, output error
+  float *fa = nullptr, *fb = nullptr;                  // MSE: derivative factors
   float* G = nullptr;     // [nm][P][d][n]
   float* part = nullptr;  // [nm*P][contract tiles]
-  u16 *xpl[2] = {}, *xtpl[2] = {}, *apl = nullptr, *bpl = nullptr;
+  u16 *xpl[2] = {}, *apl = nullptr, *bpl = nullptr;
   float* afp = nullptr;
   int* health = nullptr;
   int contract_tiles = 0;
+  // measurement hooks
+  int prof_stage = -1, prof_cap = 0, prof_n = 0;
+  hipEvent_t* prof_ev = nullptr;
 };
 
 namespace {
@@ -174,7 +176,7 @@ struct Carver {
 size_t layout(ttt_state* s, char* base) {
   const Dims& D = s->D;
   const ttt_config& c = s->cfg;
-  const int64_t P = D.P, d = D.d, dh = D.dh, n = D.n, sb = D.sb, bp = D.bpad;
+  const int64_t P = D.P, d = D.d, dh = D.dh, n = D.n, sb = D.sb;
   const bool mse = c.loss == TTT_LOSS_MSE;
   const bool lin = c.fw == TTT_FW_LINEAR;
   const bool f32 = c.act == TTT_F32;
@@ -189,35 +191,28 @@ size_t layout(ttt_state* s, char* base) {
     ok = C.take<u16>(D.in_kv * P * sb * d);
     ov = C.take<u16>(D.in_kv * P * sb * d);
   }
-  size_t okt = C.take<u16>(D.in_kv * P * d * bp);
-  size_t ovt = (!mse) ? C.take<u16>(D.in_kv * P * d * bp) : 0;
-  size_t onkt = (lin && !mse) ? C.take<u16>(D.gp * P * d * bp) : 0;
+  size_t onk = (lin && !mse) ? C.take<u16>(D.gp * P * sb * d) : 0;
   size_t ohq = lin ? 0 : C.take<u16>(D.ap * P * sb * dh);
-  size_t odz1 = 0, odz3 = 0, opt = 0, ohk = 0, ohkt = 0, ofa = 0, ofb = 0, oe = 0, oet = 0;
+  size_t odz1 = 0, odz3 = 0, opk = 0, ohk = 0, ofa = 0, ofb = 0, oe = 0;
   if (!lin) {
-    odz1 = C.take<u16>(D.gp * P * dh * bp);
-    if (c.fw == TTT_FW_SWIGLU) odz3 = C.take<u16>(D.gp * P * dh * bp);
-    if (!mse) opt = C.take<u16>(D.gp * P * dh * bp);
+    odz1 = C.take<u16>(D.gp * P * sb * dh);
+    if (c.fw == TTT_FW_SWIGLU) odz3 = C.take<u16>(D.gp * P * sb * dh);
+    if (!mse) opk = C.take<u16>(D.gp * P * sb * dh);
   }
   if (mse) {
     if (!lin) {
       ohk = C.take<u16>(D.gp * P * sb * dh);
-      ohkt = C.take<u16>(D.gp * P * dh * bp);
       ofa = C.take<float>(P * sb * dh);
       if (c.fw == TTT_FW_SWIGLU) ofb = C.take<float>(P * sb * dh);
-      oe = C.take<u16>(D.gp * P * sb * d);
     }
-    oet = C.take<u16>(D.gp * P * d * bp);
+    oe = C.take<u16>(D.gp * P * sb * d);
   }
   size_t oG = C.take<float>(D.nm * P * d * n);
   const int ctiles = (int)(((d + CONTRACT_BM - 1) / CONTRACT_BM) * ((n + CONTRACT_BN - 1) / CONTRACT_BN));
   size_t opart = C.take<float>(D.nm * P * ctiles);
-  size_t ox[2] = {0, 0}, oxt[2] = {0, 0}, oa = 0, ob = 0, oafp = 0;
+  size_t ox[2] = {0, 0}, oa = 0, ob = 0, oafp = 0;
   if (c.ns_steps > 0) {
-    for (int i = 0; i < 2; ++i) {
-      ox[i] = C.take<u16>(D.npm * D.nm * P * d * n);
-      oxt[i] = C.take<u16>(D.npm * D.nm * P * n * d);
-    }
+    for (int i = 0; i < 2; ++i) ox[i] = C.take<u16>(D.npm * D.nm * P * d * n);
     oa = C.take<u16>(D.npm * D.nm * P * d * d);
     ob = C.take<u16>(D.npm * D.nm * P * d * d);
     oafp = C.take<float>(D.nm * P * d * d);
@@ -237,28 +232,25 @@ size_t layout(ttt_state* s, char* base) {
     }
     s->W2t = lin ? nullptr : H(oW2t);
     if (f32) { s->qpl = H(oq); s->kpl = H(ok); s->vpl = H(ov); }
-    s->kt = H(okt);
-    s->vt = mse ? nullptr : H(ovt);
-    s->nkt = (lin && !mse) ? H(onkt) : nullptr;
+    s->nk = (lin && !mse) ? H(onk) : nullptr;
     s->hq = lin ? nullptr : H(ohq);
     if (!lin) {
-      s->dz1t = H(odz1);
-      s->dz3t = c.fw == TTT_FW_SWIGLU ? H(odz3) : nullptr;
-      s->pt = mse ? nullptr : H(opt);
+      s->dz1 = H(odz1);
+      s->dz3 = c.fw == TTT_FW_SWIGLU ? H(odz3) : nullptr;
+      s->pk = mse ? nullptr : H(opk);
     }
     if (mse) {
       if (!lin) {
-        s->hk = H(ohk); s->hkt = H(ohkt); s->fa = F(ofa);
+        s->hk = H(ohk); s->fa = F(ofa);
         s->fb = c.fw == TTT_FW_SWIGLU ? F(ofb) : nullptr;
-        s->e = H(oe);
       }
-      s->et = H(oet);
+      s->e = H(oe);
     }
     s->G = F(oG);
     s->part = F(opart);
     s->contract_tiles = ctiles;
     if (c.ns_steps > 0) {
-      for (int i = 0; i < 2; ++i) { s->xpl[i] = H(ox[i]); s->xtpl[i] = H(oxt[i]); }
+      for (int i = 0; i < 2; ++i) s->xpl[i] = H(ox[i]);
       s->apl = H(oa); s->bpl = H(ob); s->afp = F(oafp);
     }
     s->health = reinterpret_cast<int*>(base + oh);
@@ -272,10 +264,26 @@ PlaneBuf pbuf(u16* base, int np, int64_t plane_stride, int64_t zstride, int64_t 
   return b;
 }
 
+// Launch `call` as stage `id`, bracketed by profiling events when that stage is traced.
+template <class F>
+hipError_t staged(ttt_state* s, int id, hipStream_t st, F call) {
+  const bool rec = s->prof_stage == id && s->prof_n < s->prof_cap;
+  if (rec) {
+    hipError_t e = hipEventRecord(s->prof_ev[2 * s->prof_n], st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = call();
+  if (rec && e == hipSuccess) {
+    e = hipEventRecord(s->prof_ev[2 * s->prof_n + 1], st);
+    ++s->prof_n;
+  }
+  return e;
+}
+#define STAGED(id, expr) HIP_TRY(staged(s, id, st, [&]() { return (expr); }))
+
 // Operand over a caller tensor: element (r, k) of problem z at p + z*zstride + r*ld + k.
 Operand act_operand(const void* p, int64_t zstride, int64_t ld, int rows) {
-  const u16* q = static_cast<const u16*>(p);
-  return make_operand(q, q, q, ld, zstride, 1, rows);
+  return make_operand(static_cast<const u16*>(p), 0, ld, zstride, 1, rows);
 }
 
 ttt_status refresh_planes(ttt_state* s, bool with_update, hipStream_t st) {
@@ -296,7 +304,7 @@ ttt_status refresh_planes(ttt_state* s, bool with_update, hipStream_t st) {
     M.plt_stride = (int64_t)D.P * D.rows[m] * D.cols[m];
     r.max_rows = std::max(r.max_rows, D.rows[m]);
   }
-  HIP_TRY(launch_renorm(r, st));
+  STAGED(TTT_STAGE_RENORM, launch_renorm(r, st));
   return TTT_OK;
 }
 
@@ -319,38 +327,36 @@ ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
   Operand xq;
   if (c.act == TTT_F32) {
     SplitArgs sa{};
-    sa.x = reinterpret_cast<const float*>(q); sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
+    sa.x = q; sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
     sa.out = pbuf(s->qpl, D.in_q, (int64_t)P * D.sb * d, D.sb * d, d);
-    HIP_TRY(launch_split(sa, P, st));
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
     xq = operand_of(sa.out, D.in_q, R.nr);
   } else {
     xq = act_operand(q, R.T * d, d, R.nr);
   }
   OutArgs o{};
-  o.nrows = R.nr; o.mrows = R.nr; o.N = d;
+  o.nrows = R.nr; o.N = d;
   o.out = R.out + R.t0 * d * es; o.out_zstride = R.T * d; o.out_bf16 = c.act == TTT_BF16;
   if (c.fw == TTT_FW_LINEAR) {
     o.a = xq;
     o.b = operand_of(pbuf(s->Wpl[0], D.ap, (int64_t)P * d * d, (int64_t)d * d, d), D.ap, d);
     o.K = d;
-    HIP_TRY(launch_out(OUT_Q, o, P, st));
+    STAGED(TTT_STAGE_OUT, launch_out(OUT_Q, o, P, st));
     return TTT_OK;
   }
   FrontArgs f{};
-  f.x = xq;
-  f.w1 = operand_of(pbuf(s->Wpl[0], D.ap, (int64_t)P * dh * d, (int64_t)dh * d, d), D.ap, dh);
+  f.A[0] = xq;
+  f.B[0] = operand_of(pbuf(s->Wpl[0], D.ap, (int64_t)P * dh * d, (int64_t)dh * d, d), D.ap, dh);
   if (c.fw == TTT_FW_SWIGLU)
-    f.w3 = operand_of(pbuf(s->Wpl[1], D.ap, (int64_t)P * dh * d, (int64_t)dh * d, d), D.ap, dh);
-  f.v = f.x;
-  f.w2t = f.w1;
-  f.nrows = R.nr; f.mrows = R.nr; f.K = d; f.N = dh;
+    f.B[1] = operand_of(pbuf(s->Wpl[1], D.ap, (int64_t)P * dh * d, (int64_t)dh * d, d), D.ap, dh);
+  f.nrows = R.nr; f.K = d; f.N = dh;
   f.o1 = pbuf(s->hq, D.ap, (int64_t)P * D.sb * dh, D.sb * dh, dh);
-  HIP_TRY(launch_front(c.fw == TTT_FW_SWIGLU ? FW_SWIGLU : FW_GELU, FRONT_Q, f, P, st));
+  STAGED(TTT_STAGE_FRONT_Q, launch_front(c.fw == TTT_FW_SWIGLU ? FW_SWIGLU : FW_GELU, FRONT_Q, f, P, st));
   const int w2 = D.nm - 1;
   o.a = operand_of(f.o1, D.ap, R.nr);
   o.b = operand_of(pbuf(s->Wpl[w2], D.ap, (int64_t)P * d * dh, (int64_t)d * dh, dh), D.ap, d);
   o.K = dh;
-  HIP_TRY(launch_out(OUT_Q, o, P, st));
+  STAGED(TTT_STAGE_OUT, launch_out(OUT_Q, o, P, st));
   return TTT_OK;
 }
 
@@ -360,7 +366,7 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
   const ttt_config& c = s->cfg;
   const size_t es = c.act == TTT_BF16 ? 2 : 4;
   const int P = D.P, d = D.d, dh = D.dh;
-  const int64_t bp = round_up(R.nr, ROW_PAD), BP = D.bpad;
+  const int64_t SB = D.sb;
   const bool mse = c.loss == TTT_LOSS_MSE, lin = c.fw == TTT_FW_LINEAR;
   const bool sw = c.fw == TTT_FW_SWIGLU;
   const char* k = R.k + R.t0 * d * es;
@@ -368,133 +374,130 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
   const float* eta = R.eta + R.t0;
   const int gi = D.in_kv, gp = D.gp;
 
+  // token-major planes of this block: [planes][P][SB][cols]
+  auto tok = [&](u16* b, int np, int cols) {
+    return pbuf(b, np, (int64_t)P * SB * cols, SB * cols, cols);
+  };
+  SplitArgs sa{};
+  sa.x_zstride = R.T * d; sa.x_bf16 = c.act == TTT_BF16; sa.eta = eta; sa.eta_zstride = R.T;
+  sa.n = R.nr; sa.d = d;
   Operand xk, xv;
   if (c.act == TTT_F32) {
-    SplitArgs sa{};
-    sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
-    sa.x = reinterpret_cast<const float*>(k);
-    sa.out = pbuf(s->kpl, gi, (int64_t)P * D.sb * d, D.sb * d, d);
-    HIP_TRY(launch_split(sa, P, st));
+    sa.x = k; sa.out = tok(s->kpl, gi, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
     xk = operand_of(sa.out, gi, R.nr);
-    sa.x = reinterpret_cast<const float*>(v);
-    sa.out = pbuf(s->vpl, gi, (int64_t)P * D.sb * d, D.sb * d, d);
-    HIP_TRY(launch_split(sa, P, st));
+    sa.x = v; sa.out = tok(s->vpl, gi, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
     xv = operand_of(sa.out, gi, R.nr);
   } else {
     xk = act_operand(k, R.T * d, d, R.nr);
     xv = act_operand(v, R.T * d, d, R.nr);
   }
-
-  // token-major -> feature-major copies for the contractions
-  TransposeArgs ta{};
-  ta.x_zstride = R.T * d; ta.x_bf16 = c.act == TTT_BF16; ta.eta = eta; ta.eta_zstride = R.T;
-  ta.n = R.nr; ta.d = d; ta.bpad = (int)bp;
-  PlaneBuf kt = pbuf(s->kt, gi, (int64_t)P * d * BP, (int64_t)d * BP, BP);
-  PlaneBuf vt{}, nkt{};
-  if (!(lin && !mse)) {
-    ta.x = k; ta.neg_eta = 0; ta.out = kt;
-    HIP_TRY(launch_transpose(ta, P, st));
-  }
-  if (!mse) {
-    vt = pbuf(s->vt, gi, (int64_t)P * d * BP, (int64_t)d * BP, BP);
-    ta.x = v; ta.neg_eta = 0; ta.out = vt;
-    HIP_TRY(launch_transpose(ta, P, st));
-  }
-  if (lin && !mse) {
-    nkt = pbuf(s->nkt, gp, (int64_t)P * d * BP, (int64_t)d * BP, BP);
-    ta.x = k; ta.neg_eta = 1; ta.out = nkt;
-    HIP_TRY(launch_transpose(ta, P, st));
-  }
+  // the same tensors read column-wise by the contractions: rows of the operand = features
+  auto as_cols = [&](Operand o, int cols) { o.rows = cols; return o; };
 
   auto wop = [&](int m, int np) {
     return operand_of(pbuf(s->Wpl[m], np, (int64_t)P * D.rows[m] * D.cols[m],
                            (int64_t)D.rows[m] * D.cols[m], D.cols[m]), np, D.rows[m]);
   };
-  PlaneBuf dz1t{}, dz3t{}, pt{}, hkt{}, et{};
-  if (!lin) {
-    dz1t = pbuf(s->dz1t, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
-    if (sw) dz3t = pbuf(s->dz3t, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
-  }
   const int w2 = D.nm - 1;
   Operand w2t{};
   if (!lin) w2t = operand_of(pbuf(s->W2t, gp, (int64_t)P * dh * d, (int64_t)dh * d, d), gp, dh);
 
+  PlaneBuf dz1{}, dz3{}, pk{}, hk{}, e{}, nk{};
+  if (!lin) {
+    dz1 = tok(s->dz1, gp, dh);
+    if (sw) dz3 = tok(s->dz3, gp, dh);
+  }
   if (!lin && !mse) {
-    pt = pbuf(s->pt, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
+    pk = tok(s->pk, gp, dh);
     FrontArgs f{};
-    f.x = xk; f.v = xv; f.w1 = wop(0, gp);
-    if (sw) f.w3 = wop(1, gp);
-    f.w2t = w2t;
+    f.A[0] = xk; f.A[1] = xv; f.B[0] = wop(0, gp);
+    if (sw) f.B[1] = wop(1, gp);
+    f.B[sw ? 2 : 1] = w2t;
     f.eta = eta; f.eta_zstride = R.T;
-    f.nrows = R.nr; f.mrows = (int)bp; f.K = d; f.N = dh;
-    f.o1 = dz1t; f.o2 = dz3t; f.o3 = pt;
-    HIP_TRY(launch_front(sw ? FW_SWIGLU : FW_GELU, FRONT_K_DOT, f, P, st));
+    f.nrows = R.nr; f.K = d; f.N = dh;
+    f.o1 = dz1; f.o2 = dz3; f.o3 = pk;
+    STAGED(TTT_STAGE_FRONT_K, launch_front(sw ? FW_SWIGLU : FW_GELU, FRONT_K_DOT, f, P, st));
   } else if (mse) {
     Operand ok_a;
     if (!lin) {
-      hkt = pbuf(s->hkt, gp, (int64_t)P * dh * BP, (int64_t)dh * BP, BP);
+      hk = tok(s->hk, gp, dh);
       FrontArgs f{};
-      f.x = xk; f.v = xk; f.w1 = wop(0, gp);
-      if (sw) f.w3 = wop(1, gp);
-      f.w2t = f.w1;
-      f.nrows = R.nr; f.mrows = (int)bp; f.K = d; f.N = dh;
-      f.o1 = pbuf(s->hk, gp, (int64_t)P * D.sb * dh, D.sb * dh, dh);
-      f.o2 = hkt;
-      f.fa = s->fa; f.fb = s->fb; f.f_zstride = D.sb * dh;
-      HIP_TRY(launch_front(sw ? FW_SWIGLU : FW_GELU, FRONT_K_MSE, f, P, st));
-      ok_a = operand_of(f.o1, gp, R.nr);
+      f.A[0] = xk; f.B[0] = wop(0, gp);
+      if (sw) f.B[1] = wop(1, gp);
+      f.nrows = R.nr; f.K = d; f.N = dh;
+      f.o1 = hk;
+      f.fa = s->fa; f.fb = s->fb; f.f_zstride = SB * dh;
+      STAGED(TTT_STAGE_FRONT_K, launch_front(sw ? FW_SWIGLU : FW_GELU, FRONT_K_MSE, f, P, st));
+      ok_a = operand_of(hk, gp, R.nr);
     } else {
       ok_a = xk;
     }
-    et = pbuf(s->et, gp, (int64_t)P * d * BP, (int64_t)d * BP, BP);
+    e = tok(s->e, gp, d);
     OutArgs o{};
     o.a = ok_a;
     o.b = wop(w2, gp);   // W2 [d][dh] (or W [d][d]) as the [N][K] operand
-    o.nrows = R.nr; o.mrows = (int)bp; o.K = lin ? d : dh; o.N = d;
+    o.nrows = R.nr; o.K = lin ? d : dh; o.N = d;
     o.vin = v; o.v_zstride = R.T * d; o.v_bf16 = c.act == TTT_BF16;
     o.eta = eta; o.eta_zstride = R.T;
-    o.e = lin ? et : pbuf(s->e, gp, (int64_t)P * D.sb * d, D.sb * d, d);
-    o.et = et;
-    if (lin) o.e.np = 0;   // the linear net needs only E^T
-    HIP_TRY(launch_out(OUT_K_MSE, o, P, st));
+    o.e = e;
+    STAGED(TTT_STAGE_MSE, launch_out(OUT_K_MSE, o, P, st));
     if (!lin) {
       OutArgs h{};
-      h.a = operand_of(o.e, gp, R.nr);
+      h.a = operand_of(e, gp, R.nr);
       h.b = w2t;
-      h.nrows = R.nr; h.mrows = (int)bp; h.K = d; h.N = dh;
-      h.fa = s->fa; h.fb = s->fb; h.f_zstride = D.sb * dh;
-      h.dz1t = dz1t; h.dz3t = dz3t; h.swiglu = sw;
-      HIP_TRY(launch_out(DH_MSE, h, P, st));
+      h.nrows = R.nr; h.K = d; h.N = dh;
+      h.fa = s->fa; h.fb = s->fb; h.f_zstride = SB * dh;
+      h.dz1 = dz1; h.dz3 = dz3; h.swiglu = sw;
+      STAGED(TTT_STAGE_MSE, launch_out(DH_MSE, h, P, st));
     }
+  } else {  // linear net, inner-product loss: the gradient is V^T (-eta K)
+    nk = tok(s->nk, gp, d);
+    sa.x = k; sa.neg_eta = 1; sa.out = nk;
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
   }
 
-  // contraction: X_m [d x n] = A_m (feature-major, tokens contiguous) . B_m^T
+  // contraction: X_m [d x n] = sum over tokens of A_m[t][:]^T B_m[t][:]
   ContractArgs ca{};
-  ca.P = P; ca.M = d; ca.N = D.n; ca.K = (int)bp;
-  auto op = [&](const PlaneBuf& b, int rows) { return operand_of(b, b.np, rows); };
+  ca.P = P; ca.M = d; ca.N = D.n; ca.K = R.nr;
+  auto colop = [&](const PlaneBuf& b, int cols) {
+    return operand_of(b, b.np, cols);
+  };
   if (lin) {
-    if (mse) { ca.a[0] = op(et, d); ca.b[0] = op(kt, d); }
-    else { ca.a[0] = op(vt, d); ca.b[0] = op(nkt, d); }
+    if (mse) { ca.a[0] = colop(e, d); ca.b[0] = as_cols(xk, d); }
+    else { ca.a[0] = as_cols(xv, d); ca.b[0] = colop(nk, d); }
   } else {
-    ca.a[0] = op(kt, d); ca.b[0] = op(dz1t, dh);
+    ca.a[0] = as_cols(xk, d); ca.b[0] = colop(dz1, dh);
     int m = 1;
-    if (sw) { ca.a[1] = op(kt, d); ca.b[1] = op(dz3t, dh); m = 2; }
-    if (mse) { ca.a[m] = op(et, d); ca.b[m] = op(hkt, dh); }
-    else { ca.a[m] = op(vt, d); ca.b[m] = op(pt, dh); }
+    if (sw) { ca.a[1] = as_cols(xk, d); ca.b[1] = colop(dz3, dh); m = 2; }
+    if (mse) { ca.a[m] = colop(e, d); ca.b[m] = colop(hk, dh); }
+    else { ca.a[m] = as_cols(xv, d); ca.b[m] = colop(pk, dh); }
   }
   ca.G = s->G;
   ca.accum_in = first ? 0 : 1;
   ca.last = last ? 1 : 0;
   ca.muon = c.ns_steps > 0;
   const int64_t Z = (int64_t)D.nm * P;
-  if (ca.muon) {
-    ca.x = pbuf(s->xpl[0], D.nlp, Z * d * D.n, (int64_t)d * D.n, D.n);
-    ca.xt = pbuf(s->xtpl[0], D.nlp, Z * D.n * d, (int64_t)D.n * d, d);
-  }
+  if (ca.muon) ca.x = pbuf(s->xpl[0], D.nlp, Z * d * D.n, (int64_t)d * D.n, D.n);
   ca.part = s->part;
   ca.U = s->U;
   ca.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
-  HIP_TRY(launch_contract(ca, D.nm, st));
+  // operands of one launch share a plane count per side: group the matrices accordingly
+  int m0 = 0;
+  while (m0 < D.nm) {
+    int m1 = m0 + 1;
+    while (m1 < D.nm && ca.a[m1].planes == ca.a[m0].planes && ca.b[m1].planes == ca.b[m0].planes) ++m1;
+    ContractArgs cg = ca;
+    for (int m = m0; m < m1; ++m) { cg.a[m - m0] = ca.a[m]; cg.b[m - m0] = ca.b[m]; }
+    cg.G = s->G + (int64_t)m0 * P * d * D.n;
+    cg.U = s->U + (int64_t)m0 * P * d * D.n;
+    if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
+    cg.part = s->part + (int64_t)m0 * P * s->contract_tiles;
+    cg.tr_mask = ca.tr_mask >> m0;
+    STAGED(TTT_STAGE_CONTRACT, launch_contract(cg, m1 - m0, st));
+    m0 = m1;
+  }
   return TTT_OK;
 }
 
@@ -513,18 +516,16 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
     a.xin = pbuf(s->xpl[it & 1], pk, (int64_t)Z * M * N, (int64_t)M * N, N);
     a.afp = s->afp;
     a.aout = pbuf(s->apl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
-    HIP_TRY(launch_ns_gram(a, st));
+    STAGED(TTT_STAGE_NS_GRAM, launch_ns_gram(a, st));
     a.ain = a.aout;
     a.aout = pbuf(s->bpl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
-    HIP_TRY(launch_ns_poly(a, st));
+    STAGED(TTT_STAGE_NS_POLY, launch_ns_poly(a, st));
     a.ain = a.aout;
-    a.xtin = pbuf(s->xtpl[it & 1], pk, (int64_t)Z * N * M, (int64_t)N * M, M);
     a.G = s->G;
     a.xout = pbuf(s->xpl[(it + 1) & 1], pn, (int64_t)Z * M * N, (int64_t)M * N, N);
-    a.xtout = pbuf(s->xtpl[(it + 1) & 1], pn, (int64_t)Z * N * M, (int64_t)N * M, M);
     a.U = s->U;
     a.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
-    HIP_TRY(launch_ns_update(a, st));
+    STAGED(TTT_STAGE_NS_UPDATE, launch_ns_update(a, st));
   }
   return TTT_OK;
 }
@@ -699,10 +700,59 @@ ttt_status ttt_state_health(ttt_state* s) {
 ttt_status ttt_destroy_state(ttt_state* s) {
   if (!s) return TTT_OK;
   hipError_t e1 = hipStreamSynchronize(s->last);
+  if (s->prof_ev) {
+    for (int i = 0; i < 2 * s->prof_cap; ++i) hipEventDestroy(s->prof_ev[i]);
+    delete[] s->prof_ev;
+  }
   hipError_t e2 = hipFree(s->arena);
   delete s;
   if (e1 != hipSuccess) return fail(TTT_E_HIP, "sync before free failed: %s", hipGetErrorString(e1));
   if (e2 != hipSuccess) return fail(TTT_E_HIP, "hipFree failed: %s", hipGetErrorString(e2));
+  return TTT_OK;
+}
+
+ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  if (stage < 0 || stage >= TTT_STAGE_COUNT) return fail(TTT_E_CONFIG, "unknown stage %d", stage);
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(TTT_E_CONFIG, "max_launches must be in [1, 2^20]");
+  if (s->prof_ev) return fail(TTT_E_CONFIG, "profiling already active");
+  hipEvent_t* ev = new (std::nothrow) hipEvent_t[2 * (size_t)max_launches];
+  if (!ev) return fail(TTT_E_ALLOC, "host allocation failed");
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    hipError_t e = hipEventCreate(&ev[i]);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
+      delete[] ev;
+      return fail(TTT_E_HIP, "hipEventCreate failed: %s", hipGetErrorString(e));
+    }
+  }
+  s->prof_ev = ev;
+  s->prof_cap = max_launches;
+  s->prof_n = 0;
+  s->prof_stage = stage;
+  return TTT_OK;
+}
+
+ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  if (!s->prof_ev) return fail(TTT_E_CONFIG, "profiling is not active");
+  hipError_t e = hipStreamSynchronize(s->last);
+  double tot = 0;
+  for (int i = 0; i < s->prof_n && e == hipSuccess; ++i) {
+    float ms = 0;
+    e = hipEventElapsedTime(&ms, s->prof_ev[2 * i], s->prof_ev[2 * i + 1]);
+    tot += ms;
+  }
+  const int n = s->prof_n;
+  for (int i = 0; i < 2 * s->prof_cap; ++i) hipEventDestroy(s->prof_ev[i]);
+  delete[] s->prof_ev;
+  s->prof_ev = nullptr;
+  s->prof_stage = -1;
+  s->prof_n = s->prof_cap = 0;
+  if (e != hipSuccess) return fail(TTT_E_HIP, "event timing failed: %s", hipGetErrorString(e));
+  if (launches) *launches = n;
+  if (total_ms) *total_ms = tot;
   return TTT_OK;
 }
 

@@ -35,6 +35,13 @@ __device__ __forceinline__ void split_planes(float x, int np, u16 out[3]) {
   }
 }
 
+// Plane q of x alone (the same value split_planes puts in out[q]).
+__device__ __forceinline__ u16 plane_of(float x, int q) {
+  float r = x;
+  for (int i = 0; i < q; ++i) r = r - bf2f(f2bf(r));
+  return f2bf(r);
+}
+
 // ------------------------------------------------------------------------ reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -43,62 +50,154 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ------------------------------------------------------------------------ GEMM operands
-// A K-contiguous operand made of 1..3 bf16 planes: element (r, k) of problem z lives at
-// p[plane][z * zstride + r * ld + k].  Rows >= rows and k >= K read as zero.
+// A K-contiguous operand made of 1..3 bf16 planes: element (r, k) of plane q, problem z
+// lives at p[q * pstride + z * zstride + r * ld + k].  Rows >= rows and k >= K read as zero.
 struct Operand {
-  const u16* p[3];
+  const u16* p;
+  int64_t pstride;
   int64_t ld;
   int64_t zstride;
   int32_t planes;
   int32_t rows;
 };
 
-__host__ __device__ inline Operand make_operand(const u16* p0, const u16* p1, const u16* p2,
-                                                int64_t ld, int64_t zstride, int planes,
-                                                int rows) {
+__host__ __device__ inline Operand make_operand(const u16* p, int64_t pstride, int64_t ld,
+                                                int64_t zstride, int planes, int rows) {
   Operand o;
-  o.p[0] = p0; o.p[1] = p1; o.p[2] = p2;
-  o.ld = ld; o.zstride = zstride; o.planes = planes; o.rows = rows;
+  o.p = p; o.pstride = pstride; o.ld = ld; o.zstride = zstride; o.planes = planes; o.rows = rows;
   return o;
 }
 
-// Multi-product tile GEMM main loop.
-//   NA A-operands (tile rows = M), NB B-operands (tile rows = N), NP products; product p
-//   accumulates  C_p[m][n] += sum_k A_{IA[p]}[m][k] * B_{IB[p]}[n][k]  over all plane pairs
-//   (i, j) with i + j < max(planes of A_{IA[p]}, planes of B_{IB[p]}).
-// Block: 256 threads = 4 waves in a 2 x 2 layout; wave tile (BM/2) x (BN/2) made of 32x32
-// MFMA tiles.  K is walked in steps of 32 through two LDS buffers (double buffering with
-// a register prefetch of the next step's global loads).  LDS rows are padded to 80 bytes
-// so that the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
-template <int BM, int BN, int NA, int NB>
-struct TileShape {
-  static constexpr int BK = 32;
-  static constexpr int BKP = 40;                 // padded row length in elements
-  static constexpr int WM = BM / 2, WN = BN / 2;
-  static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int CA = BM * 4 / 256;        // 16-byte chunks per thread per A plane
-  static constexpr int CB = BN * 4 / 256;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile sizes are multiples of 64");
-  // LDS bytes for one buffer with the given plane counts
-  __host__ __device__ static int stage_bytes(const int* pa, const int* pb) {
-    int n = 0;
-    for (int i = 0; i < NA; ++i) n += pa[i] * BM * BKP * 2;
-    for (int i = 0; i < NB; ++i) n += pb[i] * BN * BKP * 2;
-    return n;
+// A buffer of 1..3 bf16 planes: plane q of problem z, row r, column c lives at
+// base[q * plane_stride + z * zstride + r * ld + c].
+struct PlaneBuf {
+  u16* base;
+  int64_t plane_stride;
+  int64_t zstride;
+  int64_t ld;
+  int32_t np;
+};
+
+// ------------------------------------------------------------------------ GEMM core
+// Multi-product tile GEMM main loop for gfx950.
+//
+//   NA A-operands (tile rows = M) and NB B-operands (tile rows = N); product p < NB
+//   accumulates  C_p[m][n] += sum_k A_{ia(p)}[m][k] * B_p[n][k]  with ia(p) = 1 for the
+//   last product when NA == 2, else 0.
+//
+// Operand layouts in memory (template parameters LA / LB):
+//   L_ROW  element (r, k) at r * ld + k   (rows contiguous along K)
+//   L_COL  element (r, k) at k * ld + r   (K-rows contiguous along the M / N index)
+// Both are staged into LDS without rearrangement and read into MFMA fragments with
+// ds_read_b128 (L_ROW) or the gfx950 transposing ds_read_b64_tr_b16 (L_COL), so no
+// operand is ever transposed in memory.
+//
+// Planes: the A operands share one plane count PA, the B operands one count PB.  The pair
+// (qa, qb) of planes is taken when qa + qb < max(PA, PB); each taken pair is one "segment"
+// of the K loop, so a multi-plane product is a longer K loop over the same LDS tiles and
+// the inner loop has no plane-dependent control flow.
+//
+// Block: WGM x WGN waves, wave tile (BM/WGM) x (BN/WGN) of 32x32x16 MFMA tiles.  K steps of
+// 64 through two LDS stages (register prefetch of the next step).  Global loads are buffer
+// loads: elements outside the operand read as zero.  16-byte LDS chunks are XOR-swizzled
+// by row so that fragment reads spread over the banks.
+enum Layout { L_ROW = 0, L_COL = 1 };
+
+__device__ __forceinline__ int swz_row(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_col(int k) { return (k & 3) << 2; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int L, int R, int NT>
+struct TileLoad {
+  static constexpr int BK = 64;
+  static constexpr int CHUNKS = R * BK / 8;        // 16-byte chunks per tile
+  static constexpr int C = CHUNKS / NT;            // per thread
+  static constexpr int BYTES = R * BK * 2;
+  static_assert(CHUNKS % NT == 0, "uneven tile load");
+  static_assert(L == L_ROW || R >= 128, "column-layout tiles need >= 128 rows");
+  uint32_t off[C];   // byte offset of the chunk at k0 = 0, or an out-of-range value
+  int kk[C];         // k of the chunk's first element relative to k0
+  int lds[C];        // LDS byte offset inside the tile
+  uint32_t kstride;  // bytes per unit of k0
+
+  __device__ __forceinline__ void init(const Operand& o, int row0) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int ch = threadIdx.x + c * NT;
+      if (L == L_ROW) {
+        const int r = ch >> 3, kc = ch & 7;
+        kk[c] = kc * 8;
+        lds[c] = r * 128 + ((kc ^ swz_row(r)) << 4);
+        off[c] = (row0 + r < o.rows) ? (uint32_t)(((int64_t)(row0 + r) * o.ld + kc * 8) * 2)
+                                     : 0xC0000000u;
+      } else {
+        const int k = ch / (R / 8), mc = ch % (R / 8);
+        kk[c] = k;
+        lds[c] = k * R * 2 + ((mc ^ swz_col(k)) << 4);
+        off[c] = (row0 + mc * 8 < o.rows) ? (uint32_t)(((int64_t)k * o.ld + row0 + mc * 8) * 2)
+                                          : 0xC0000000u;
+      }
+    }
+    kstride = L == L_ROW ? 2u : (uint32_t)(o.ld * 2);
   }
 };
 
-template <int BM, int BN, int NA, int NB, int NP>
-struct MultiGemm {
-  using S = TileShape<BM, BN, NA, NB>;
-  static constexpr int BK = S::BK, BKP = S::BKP, TM = S::TM, TN = S::TN;
-  static constexpr int CA = S::CA, CB = S::CB;
+// MFMA fragment (32 rows x 16 k) of a staged tile for k-substep s.
+template <int L, int R>
+__device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int s) {
+  const int lane = threadIdx.x & 63;
+  if (L == L_ROW) {
+    const int r = row_base + (lane & 31);
+    const int ch = 2 * s + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(tile + r * 128 + ((ch ^ swz_row(r)) << 4));
+  } else {
+    const int g = lane >> 4, j = lane & 15;
+    const int m = row_base + 16 * (g & 1) + 4 * (j & 3);
+    const int kb = 16 * s + 8 * (g >> 1) + (j >> 2);
+    s16x4 lo, hi;
+    {
+      const int k = kb;
+      const char* a = tile + k * R * 2 + (((m >> 3) ^ swz_col(k)) << 4) + (m & 7) * 2;
+      lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(a));
+    }
+    {
+      const int k = kb + 4;
+      const char* a = tile + k * R * 2 + (((m >> 3) ^ swz_col(k)) << 4) + (m & 7) * 2;
+      hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(a));
+    }
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
 
-  f32x16 acc[NP][TM][TN];
+template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LA = L_ROW, int LB = L_ROW>
+struct Gemm {
+  static constexpr int NT = WGM * WGN * 64;
+  static constexpr int TBM = BM, TBN = BN, WGN_ = WGN;
+  static constexpr int STORE_LDS = (BM + 8) * (BN + 8) * 2;
+  static constexpr int BK = 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  using TA = TileLoad<LA, BM, NT>;
+  using TB = TileLoad<LB, BN, NT>;
+  static constexpr int A_TILE = TA::BYTES, B_TILE = TB::BYTES;
+  static constexpr int STAGE = NA * A_TILE + NB * B_TILE;
+  static constexpr int LDS_BYTES = 2 * STAGE > STORE_LDS ? 2 * STAGE : STORE_LDS;
+  static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
+
+  f32x16 acc[NB][TM][TN];
+
+  static __device__ __forceinline__ constexpr int ia(int p) {
+    return (NA == 2 && p == NB - 1) ? 1 : 0;
+  }
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int p = 0; p < NB; ++p)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -107,166 +206,122 @@ struct MultiGemm {
           for (int v = 0; v < 16; ++v) acc[p][i][j][v] = 0.f;
   }
 
-  // Run the K loop.  A[] / B[] describe the operands, m0 / n0 the tile origin, z the
-  // problem index, K the contraction length (a multiple of 8), smem the dynamic LDS.
-  __device__ __forceinline__ void run(const Operand (&A)[NA], const Operand (&B)[NB],
-                                      const int (&IA)[NP], const int (&IB)[NP], int m0,
-                                      int n0, int z, int K, char* smem) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm0 = (wave >> 1) * S::WM;
-    const int wn0 = (wave & 1) * S::WN;
+  // A / B point at NA / NB consecutive operands (normally inside the kernel arguments).
+  __device__ __forceinline__ void run(const Operand* __restrict__ A,
+                                      const Operand* __restrict__ B, int m0, int n0, int z,
+                                      int K, char* smem) {
+    const int wave = threadIdx.x >> 6;
+    const int wm0 = (wave / WGN) * WM;
+    const int wn0 = (wave % WGN) * WN;
 
-    int pa[NA], pb[NB];
+    // plane-pair segments
+    const int PA = A[0].planes, PB = B[0].planes;
+    const int PM = PA > PB ? PA : PB;
+    uint32_t segs = 0;  // 4 bits per segment: qa | qb << 2
+    int nseg = 0;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) pa[i] = A[i].planes;
+    for (int qa = 0; qa < 3; ++qa)
 #pragma unroll
-    for (int i = 0; i < NB; ++i) pb[i] = B[i].planes;
-    const int stage = S::stage_bytes(pa, pb);
+      for (int qb = 0; qb < 3; ++qb)
+        if (qa < PA && qb < PB && qa + qb < PM) {
+          segs |= (uint32_t)(qa | (qb << 2)) << (4 * nseg);
+          ++nseg;
+        }
+    const int nk = (K + BK - 1) / BK;
+    const int total = nseg * nk;
+    if (total == 0) return;
 
-    // byte offsets of each operand-plane tile inside one LDS stage
-    int offA[NA][3], offB[NB][3];
-    {
-      int o = 0;
+    TA la[NA];
+    TB lb[NB];
+    const u16* pa_[NA];
+    const u16* pb_[NB];
+    int na_[NA], nb_[NB];
 #pragma unroll
-      for (int i = 0; i < NA; ++i)
+    for (int i = 0; i < NA; ++i) {
+      la[i].init(A[i], m0);
+      pa_[i] = A[i].p + (int64_t)z * A[i].zstride;
+      na_[i] = (int)(LA == L_ROW ? (int64_t)A[i].rows * A[i].ld * 2 : (int64_t)K * A[i].ld * 2);
+    }
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          offA[i][q] = o;
-          if (q < pa[i]) o += BM * BKP * 2;
-        }
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          offB[i][q] = o;
-          if (q < pb[i]) o += BN * BKP * 2;
-        }
+    for (int i = 0; i < NB; ++i) {
+      lb[i].init(B[i], n0);
+      pb_[i] = B[i].p + (int64_t)z * B[i].zstride;
+      nb_[i] = (int)(LB == L_ROW ? (int64_t)B[i].rows * B[i].ld * 2 : (int64_t)K * B[i].ld * 2);
     }
 
-    uint4 ra[NA][3][CA];
-    uint4 rb[NB][3][CB];
-
-    auto gload = [&](int k0) {
+    uint4 ra[NA][TA::C], rb[NB][TB::C];
+    auto gload = [&](int t) __attribute__((always_inline)) {
+      const int sg = t / nk, k0 = (t - sg * nk) * BK;
+      const int qa = (segs >> (4 * sg)) & 3, qb = (segs >> (4 * sg + 2)) & 3;
 #pragma unroll
-      for (int i = 0; i < NA; ++i)
+      for (int i = 0; i < NA; ++i) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(pa_[i] + qa * A[i].pstride), (short)0, na_[i], 0x00020000);
+        const uint32_t kb = (uint32_t)k0 * la[i].kstride;
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
+        for (int c = 0; c < TA::C; ++c) {
+          const uint32_t off = (k0 + la[i].kk[c] < K) ? la[i].off[c] + kb : 0xFFFFFFF0u;
+          ra[i][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        }
+      }
 #pragma unroll
-          for (int c = 0; c < CA; ++c) {
-            if (q < pa[i]) {
-              const int ch = tid + c * 256;
-              const int r = ch >> 2, kc = (ch & 3) * 8;
-              const int gr = m0 + r, gk = k0 + kc;
-              uint4 v = make_uint4(0, 0, 0, 0);
-              if (gr < A[i].rows && gk < K)
-                v = *reinterpret_cast<const uint4*>(A[i].p[q] + (int64_t)z * A[i].zstride +
-                                                    (int64_t)gr * A[i].ld + gk);
-              ra[i][q][c] = v;
-            }
-          }
+      for (int i = 0; i < NB; ++i) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(pb_[i] + qb * B[i].pstride), (short)0, nb_[i], 0x00020000);
+        const uint32_t kb = (uint32_t)k0 * lb[i].kstride;
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-          for (int c = 0; c < CB; ++c) {
-            if (q < pb[i]) {
-              const int ch = tid + c * 256;
-              const int r = ch >> 2, kc = (ch & 3) * 8;
-              const int gr = n0 + r, gk = k0 + kc;
-              uint4 v = make_uint4(0, 0, 0, 0);
-              if (gr < B[i].rows && gk < K)
-                v = *reinterpret_cast<const uint4*>(B[i].p[q] + (int64_t)z * B[i].zstride +
-                                                    (int64_t)gr * B[i].ld + gk);
-              rb[i][q][c] = v;
-            }
-          }
-    };
-    auto sstore = [&](char* buf) {
-#pragma unroll
-      for (int i = 0; i < NA; ++i)
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-          for (int c = 0; c < CA; ++c) {
-            if (q < pa[i]) {
-              const int ch = tid + c * 256;
-              const int r = ch >> 2, kc = (ch & 3) * 8;
-              *reinterpret_cast<uint4*>(buf + offA[i][q] + (r * BKP + kc) * 2) = ra[i][q][c];
-            }
-          }
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-#pragma unroll
-          for (int c = 0; c < CB; ++c) {
-            if (q < pb[i]) {
-              const int ch = tid + c * 256;
-              const int r = ch >> 2, kc = (ch & 3) * 8;
-              *reinterpret_cast<uint4*>(buf + offB[i][q] + (r * BKP + kc) * 2) = rb[i][q][c];
-            }
-          }
-    };
-    auto compute = [&](const char* buf) {
-      const int fr = lane & 31;
-      const int fk = (lane >> 5) * 8;
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        bf16x8 fa[NA][3][TM];
-        bf16x8 fb[NB][3][TN];
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-#pragma unroll
-          for (int q = 0; q < 3; ++q)
-#pragma unroll
-            for (int t = 0; t < TM; ++t)
-              if (q < pa[i])
-                fa[i][q][t] = *reinterpret_cast<const bf16x8*>(
-                    buf + offA[i][q] + ((wm0 + t * 32 + fr) * BKP + s * 16 + fk) * 2);
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int q = 0; q < 3; ++q)
-#pragma unroll
-            for (int t = 0; t < TN; ++t)
-              if (q < pb[i])
-                fb[i][q][t] = *reinterpret_cast<const bf16x8*>(
-                    buf + offB[i][q] + ((wn0 + t * 32 + fr) * BKP + s * 16 + fk) * 2);
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const int ia = IA[p], ib = IB[p];
-          const int P = pa[ia] > pb[ib] ? pa[ia] : pb[ib];
-#pragma unroll
-          for (int qi = 0; qi < 3; ++qi)
-#pragma unroll
-            for (int qj = 0; qj < 3; ++qj) {
-              if (qi < pa[ia] && qj < pb[ib] && qi + qj < P) {
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-                  for (int tn = 0; tn < TN; ++tn)
-                    acc[p][tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        fa[ia][qi][tm], fb[ib][qj][tn], acc[p][tm][tn], 0, 0, 0);
-              }
-            }
+        for (int c = 0; c < TB::C; ++c) {
+          const uint32_t off = (k0 + lb[i].kk[c] < K) ? lb[i].off[c] + kb : 0xFFFFFFF0u;
+          rb[i][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
         }
       }
     };
+    auto sstore = [&](char* st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int c = 0; c < TA::C; ++c)
+          *reinterpret_cast<uint4*>(st + i * A_TILE + la[i].lds[c]) = ra[i][c];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int c = 0; c < TB::C; ++c)
+          *reinterpret_cast<uint4*>(st + NA * A_TILE + i * B_TILE + lb[i].lds[c]) = rb[i][c];
+    };
+    auto compute = [&](const char* st) __attribute__((always_inline)) {
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        bf16x8 fa[NA][TM], fb[NB][TN];
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+          for (int t = 0; t < TM; ++t)
+            fa[i][t] = read_frag<LA, BM>(st + i * A_TILE, wm0 + t * 32, s);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int t = 0; t < TN; ++t)
+            fb[i][t] = read_frag<LB, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s);
+#pragma unroll
+        for (int p = 0; p < NB; ++p)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+              acc[p][tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ia(p)][tm], fb[p][tn],
+                                                                       acc[p][tm][tn], 0, 0, 0);
+      }
+    };
 
-    const int nk = (K + BK - 1) / BK;
-    if (nk == 0) return;
     gload(0);
     sstore(smem);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      char* cur = smem + (kt & 1) * stage;
-      char* nxt = smem + ((kt + 1) & 1) * stage;
-      if (kt + 1 < nk) gload((kt + 1) * BK);
+    for (int t = 0; t < total; ++t) {
+      char* cur = smem + (t & 1) * STAGE;
+      char* nxt = smem + ((t + 1) & 1) * STAGE;
+      if (t + 1 < total) gload(t + 1);
       compute(cur);
-      if (kt + 1 < nk) sstore(nxt);
+      if (t + 1 < total) sstore(nxt);
       __syncthreads();
     }
   }
@@ -278,8 +333,8 @@ struct MultiGemm {
   __device__ __forceinline__ void for_each(F f) const {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm0 = (wave >> 1) * S::WM;
-    const int wn0 = (wave & 1) * S::WN;
+    const int wm0 = (wave / WGN) * WM;
+    const int wn0 = (wave % WGN) * WN;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -292,5 +347,66 @@ struct MultiGemm {
         }
   }
 };
+
+// ------------------------------------------------------------------------ tile stores
+// Write one block tile of fp32 values (held in the MFMA accumulator layout of gemm G) to
+// a bf16-plane buffer through LDS, so that global stores are 16-byte vectors along the
+// buffer's contiguous dimension.
+//   TILE_NORMAL: element (r, c) of the tile goes to row row0 + r, column col0 + c;
+//   TILE_TRANS : it goes to row col0 + c, column row0 + r (the transposed buffer);
+//   TILE_SYM   : square diagonal tile of a symmetric matrix: only elements with r <= c are
+//                taken, each written to (r, c) and (c, r).
+// rlim / clim bound the tile's rows / columns (relative to the tile origin); the limit of
+// the buffer's contiguous dimension must be a multiple of 8.  smem needs
+// (BM + 8) * (BN + 8) * 2 bytes.  Contains __syncthreads: call from every thread.
+enum TileMode { TILE_NORMAL = 0, TILE_TRANS = 1, TILE_SYM = 2 };
+
+template <class G, int MODE>
+__device__ __forceinline__ void store_tile_planes(const f32x16 (&v)[G::TM][G::TN], char* smem,
+                                                  const PlaneBuf& dst, int z, int row0,
+                                                  int col0, int rlim, int clim) {
+  constexpr int TBM = G::TBM, TBN = G::TBN;
+  constexpr bool TR = MODE == TILE_TRANS;
+  constexpr int R = TR ? TBN : TBM;   // rows of the staged tile
+  constexpr int C = TR ? TBM : TBN;   // its contiguous length
+  constexpr int LD = C + 8;
+  u16* t = reinterpret_cast<u16*>(smem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave / G::WGN_) * G::WM, wn0 = (wave % G::WGN_) * G::WN;
+  const int rl = TR ? clim : rlim;   // staged-row limit
+  const int cl = TR ? rlim : clim;   // contiguous limit
+#pragma unroll 1
+  for (int q = 0; q < dst.np; ++q) {
+    __syncthreads();
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < G::TN; ++tn)
+#pragma unroll
+        for (int vi = 0; vi < 16; ++vi) {
+          const int r = wm0 + tm * 32 + 8 * (vi >> 2) + 4 * (lane >> 5) + (vi & 3);
+          const int c = wn0 + tn * 32 + (lane & 31);
+          const u16 hq = plane_of(v[tm][tn][vi], q);
+          if (MODE == TILE_NORMAL) {
+            t[r * LD + c] = hq;
+          } else if (MODE == TILE_TRANS) {
+            t[c * LD + r] = hq;
+          } else if (r <= c) {
+            t[r * LD + c] = hq;
+            t[c * LD + r] = hq;
+          }
+        }
+    __syncthreads();
+    u16* out = dst.base + q * dst.plane_stride + (int64_t)z * dst.zstride;
+    const int grow0 = TR ? col0 : row0, gcol0 = TR ? row0 : col0;
+    for (int ch = threadIdx.x; ch < R * (C / 8); ch += G::NT) {
+      const int rr = ch / (C / 8), cc = (ch % (C / 8)) * 8;
+      if (rr < rl && cc < cl)
+        *reinterpret_cast<uint4*>(out + (int64_t)(grow0 + rr) * dst.ld + gcol0 + cc) =
+            *reinterpret_cast<const uint4*>(t + rr * LD + cc);
+    }
+  }
+  __syncthreads();
+}
 
 }  // namespace ttt

@@ -9,19 +9,8 @@
 
 namespace ttt {
 
-// A buffer of 1..3 bf16 planes: plane q of problem z, row r, column c lives at
-// base[q * plane_stride + z * zstride + r * ld + c].
-struct PlaneBuf {
-  u16* base;
-  int64_t plane_stride;
-  int64_t zstride;
-  int64_t ld;
-  int32_t np;
-};
-
 __host__ __device__ inline Operand operand_of(const PlaneBuf& b, int np, int rows) {
-  return make_operand(b.base, b.base + b.plane_stride, b.base + 2 * b.plane_stride, b.ld,
-                      b.zstride, np, rows);
+  return make_operand(b.base, b.plane_stride, b.ld, b.zstride, np, rows);
 }
 
 enum FwKind { FW_SWIGLU = 0, FW_GELU = 1, FW_LINEAR = 2 };
@@ -30,15 +19,17 @@ enum OutMode { OUT_Q = 0, OUT_K_MSE = 1, DH_MSE = 2 };
 
 // Z-GEMMs over rows of Q or K: X W1^T (and X W3^T), plus V W2 for the inner-product loss.
 struct FrontArgs {
-  Operand x, v, w1, w3, w2t;
+  // A operands: [0] the rows (Q or K), [1] V (inner-product loss only).
+  // B operands in product order: W1, then W3 (SwiGLU), then W2^T (inner-product loss).
+  Operand A[2];
+  Operand B[3];
   const float* eta;
   int64_t eta_zstride;
-  int nrows;   // valid token rows
-  int mrows;   // rows the grid covers (rows in [nrows, mrows) produce zeros)
+  int nrows;   // token rows
   int K;       // dim
   int N;       // hidden
   int tiles_n;
-  PlaneBuf o1, o2, o3;  // Q: hidden planes | K_DOT: dZ1^T, dZ3^T (or dZ^T), P^T | K_MSE: H, H^T
+  PlaneBuf o1, o2, o3;  // Q: hidden | K_DOT: dZ1, dZ3 (or dZ), P | K_MSE: H; all [rows][hidden]
   float* fa;            // K_MSE: derivative factors [rows][hidden]
   float* fb;
   int64_t f_zstride;
@@ -48,7 +39,7 @@ struct FrontArgs {
 // dH = E W2 for the MSE loss.
 struct OutArgs {
   Operand a, b;
-  int nrows, mrows, K, N, tiles_n;
+  int nrows, K, N, tiles_n;
   // OUT_Q
   void* out;
   int64_t out_zstride;
@@ -59,24 +50,25 @@ struct OutArgs {
   int v_bf16;
   const float* eta;
   int64_t eta_zstride;
-  PlaneBuf e, et;
+  PlaneBuf e;      // E [rows][dim]
   // DH_MSE
   const float* fa;
   const float* fb;
   int64_t f_zstride;
-  PlaneBuf dz1t, dz3t;
+  PlaneBuf dz1, dz3;  // [rows][hidden]
   int swiglu;
 };
 
-// Token contractions: X_m[i][j] = sum_t A_m[i][t] B_m[j][t] for every matrix m and problem.
+// Token contractions: X_m[i][j] = sum_t A_m[t][i] B_m[t][j] for every matrix m and problem
+// (both operands token-major, read as columns).
 struct ContractArgs {
   Operand a[3], b[3];
   int P, M, N, K, tiles_n, tiles;
   float* G;        // [nm][P][M][N]
   int accum_in;    // add the running sum held in G
   int last;        // last token block of the chunk
-  int muon;        // write X0 planes, X0^T planes and per-tile sums of squares
-  PlaneBuf x, xt;
+  int muon;        // write X0 planes and per-tile sums of squares
+  PlaneBuf x;
   float* part;     // [nm*P][tiles]
   float* U;        // plain step: U in weight orientation [nm][P][rows][cols]
   int tr_mask;     // bit m: matrix m's weight is the transpose of its X orientation
@@ -91,13 +83,12 @@ struct NsArgs {
   int first;          // iteration 0 (fold the 1/(|G|_F + eps) scale)
   int last;           // final iteration: write U instead of planes
   float eps;
-  PlaneBuf xin;       // gram: X planes [M][N]
+  PlaneBuf xin;       // gram, update: X planes [M][N]
   PlaneBuf ain;       // poly: A planes [M][M] ; update: B planes [M][M]
-  PlaneBuf xtin;      // update: X^T planes [N][M]
   float* afp;         // gram out / poly in: A fp32 [Z][M][M]
   PlaneBuf aout;      // gram: A planes ; poly: B planes
   float* G;           // update: X fp32 [Z][M][N], in/out
-  PlaneBuf xout, xtout;
+  PlaneBuf xout;
   float* U;           // last: U in weight orientation
   int tr_mask;
   int P;
@@ -118,20 +109,13 @@ struct RenormArgs {
   int* health;
 };
 
-struct TransposeArgs {
+struct SplitArgs {
   const void* x;   // rows [n][d] of problem z at x + z * x_zstride (elements)
   int64_t x_zstride;
   int x_bf16;
   const float* eta;
   int64_t eta_zstride;
   int neg_eta;     // multiply row t by -eta_t
-  int n, d, bpad;
-  PlaneBuf out;    // [np][Z][d][bpad]
-};
-
-struct SplitArgs {
-  const float* x;
-  int64_t x_zstride;
   int n, d;
   PlaneBuf out;    // [np][Z][rows][d]
 };
@@ -146,7 +130,6 @@ hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s);
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s);
-hipError_t launch_transpose(const TransposeArgs& a, int Z, hipStream_t s);
 hipError_t launch_split(const SplitArgs& a, int Z, hipStream_t s);
 hipError_t prepare_kernels();  // raise dynamic-LDS limits once per process
 

@@ -50,58 +50,42 @@ struct FrontShape {
   static constexpr int NP = NB;
 };
 
-template <int BM, int BN, int FW, int MODE>
-__global__ __launch_bounds__(256) void k_front(FrontArgs a) {
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using FS = FrontShape<FW, MODE>;
-  constexpr int NA = FS::NA, NB = FS::NB, NP = FS::NP;
+  constexpr int NA = FS::NA, NB = FS::NB;
+  using G = Gemm<BM, BN, WGM, WGN, NA, NB>;
   const int z = blockIdx.y;
   const int m0 = (blockIdx.x / a.tiles_n) * BM;
   const int n0 = (blockIdx.x % a.tiles_n) * BN;
 
-  Operand A[NA];
-  Operand B[NB];
-  int IA[NP], IB[NP];
-  A[0] = a.x;
-  if constexpr (FS::DOT) A[NA - 1] = a.v;
-  B[0] = a.w1;
-  if constexpr (FW == FW_SWIGLU) B[1] = a.w3;
-  if constexpr (FS::DOT) B[NB - 1] = a.w2t;
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    IB[p] = p;
-    IA[p] = (FS::DOT && p == NP - 1) ? 1 : 0;
-  }
-
-  MultiGemm<BM, BN, NA, NB, NP> g;
+  G g;
   g.zero();
-  g.run(A, B, IA, IB, m0, n0, z, a.K, smem);
+  g.run(a.A, a.B, m0, n0, z, a.K, smem);
 
-  g.for_each([&](int i, int j, int v, int r, int c) {
+  const float* eta = a.eta + (int64_t)z * a.eta_zstride;
+  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int row = m0 + r, col = n0 + c;
-    if (row >= a.mrows || col >= a.N) return;
     const float z1 = g.acc[0][i][j][v];
     if constexpr (MODE == FRONT_Q) {
-      float h;
-      if constexpr (FW == FW_SWIGLU) h = z1 * sigm(z1) * g.acc[1][i][j][v];
-      else h = gelu_f(z1);
-      put_planes(a.o1, z, (int64_t)row * a.o1.ld + col, h);
+      if constexpr (FW == FW_SWIGLU) g.acc[0][i][j][v] = z1 * sigm(z1) * g.acc[1][i][j][v];
+      else g.acc[0][i][j][v] = gelu_f(z1);
     } else if constexpr (MODE == FRONT_K_DOT) {
-      const float e = row < a.nrows ? a.eta[(int64_t)z * a.eta_zstride + row] : 0.f;
-      const float y = g.acc[NP - 1][i][j][v];
-      const float dh = -e * y;
+      const float e = row < a.nrows ? eta[row] : 0.f;
+      const float dh = -e * g.acc[NB - 1][i][j][v];
       if constexpr (FW == FW_SWIGLU) {
         const float z3 = g.acc[1][i][j][v];
         const float s = sigm(z1);
         const float act = z1 * s;
-        put_planes(a.o1, z, (int64_t)col * a.o1.ld + row, dh * z3 * s * (1.f + z1 * (1.f - s)));
-        put_planes(a.o2, z, (int64_t)col * a.o2.ld + row, dh * act);
-        put_planes(a.o3, z, (int64_t)col * a.o3.ld + row, -e * act * z3);
+        g.acc[0][i][j][v] = dh * z3 * s * (1.f + z1 * (1.f - s));
+        g.acc[1][i][j][v] = dh * act;
+        g.acc[2][i][j][v] = -e * act * z3;
       } else {
-        put_planes(a.o1, z, (int64_t)col * a.o1.ld + row, dh * gelu_d(z1));
-        put_planes(a.o3, z, (int64_t)col * a.o3.ld + row, -e * gelu_f(z1));
+        g.acc[0][i][j][v] = dh * gelu_d(z1);
+        g.acc[1][i][j][v] = -e * gelu_f(z1);
       }
-    } else {  // FRONT_K_MSE
+    } else {  // FRONT_K_MSE: hidden activation and its derivative factors
       float h, f1, f3 = 0.f;
       if constexpr (FW == FW_SWIGLU) {
         const float z3 = g.acc[1][i][j][v];
@@ -114,111 +98,139 @@ __global__ __launch_bounds__(256) void k_front(FrontArgs a) {
         h = gelu_f(z1);
         f1 = gelu_d(z1);
       }
-      put_planes(a.o2, z, (int64_t)col * a.o2.ld + row, h);
-      if (row < a.nrows) {
-        put_planes(a.o1, z, (int64_t)row * a.o1.ld + col, h);
+      g.acc[0][i][j][v] = h;
+      if (row < a.nrows && col < a.N) {
         const int64_t fo = (int64_t)z * a.f_zstride + (int64_t)row * a.N + col;
         a.fa[fo] = f1;
         if constexpr (FW == FW_SWIGLU) a.fb[fo] = f3;
       }
     }
   });
+  const int cl = min(BN, a.N - n0);
+  const int rn = min(BM, a.nrows - m0);   // rows holding tokens
+  if constexpr (MODE == FRONT_K_DOT) {
+    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.o1, z, m0, n0, rn, cl);
+    if constexpr (FW == FW_SWIGLU) {
+      store_tile_planes<G, TILE_NORMAL>(g.acc[1], smem, a.o2, z, m0, n0, rn, cl);
+      store_tile_planes<G, TILE_NORMAL>(g.acc[2], smem, a.o3, z, m0, n0, rn, cl);
+    } else {
+      store_tile_planes<G, TILE_NORMAL>(g.acc[1], smem, a.o3, z, m0, n0, rn, cl);
+    }
+  } else {
+    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.o1, z, m0, n0, rn, cl);
+  }
 }
 
 // ------------------------------------------------------------------------ out / dH
-template <int BM, int BN, int MODE>
-__global__ __launch_bounds__(256) void k_out(OutArgs a) {
+template <int BM, int BN, int WGM, int WGN, int MODE>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1>;
   const int z = blockIdx.y;
   const int m0 = (blockIdx.x / a.tiles_n) * BM;
   const int n0 = (blockIdx.x % a.tiles_n) * BN;
-  Operand A[1] = {a.a};
-  Operand B[1] = {a.b};
-  const int IA[1] = {0}, IB[1] = {0};
-  MultiGemm<BM, BN, 1, 1, 1> g;
+  G g;
   g.zero();
-  g.run(A, B, IA, IB, m0, n0, z, a.K, smem);
+  g.run(&a.a, &a.b, m0, n0, z, a.K, smem);
 
-  g.for_each([&](int i, int j, int v, int r, int c) {
-    const int row = m0 + r, col = n0 + c;
-    if (row >= a.mrows || col >= a.N) return;
-    const float x = g.acc[0][i][j][v];
-    if constexpr (MODE == OUT_Q) {
-      if (row >= a.nrows) return;
-      const int64_t o = (int64_t)z * a.out_zstride + (int64_t)row * a.N + col;
-      if (a.out_bf16) static_cast<u16*>(a.out)[o] = f2bf(x);
-      else static_cast<float*>(a.out)[o] = x;
-    } else if constexpr (MODE == OUT_K_MSE) {
+  const int cl = min(BN, a.N - n0);
+  const int rn = min(BM, a.nrows - m0);
+  if constexpr (MODE == OUT_Q) {
+    if (a.out_bf16) {
+      PlaneBuf o;
+      o.base = static_cast<u16*>(a.out); o.plane_stride = 0; o.zstride = a.out_zstride;
+      o.ld = a.N; o.np = 1;
+      store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, o, z, m0, n0, rn, cl);
+    } else {
+      g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
+        const int row = m0 + r, col = n0 + c;
+        if (row < a.nrows && col < a.N)
+          static_cast<float*>(a.out)[(int64_t)z * a.out_zstride + (int64_t)row * a.N + col] =
+              g.acc[0][i][j][v];
+      });
+    }
+  } else if constexpr (MODE == OUT_K_MSE) {
+    const float* eta = a.eta + (int64_t)z * a.eta_zstride;
+    g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
+      const int row = m0 + r, col = n0 + c;
       float e = 0.f;
-      if (row < a.nrows) {
+      if (row < a.nrows && col < a.N) {
         const float vv = load_act(a.vin, (int64_t)z * a.v_zstride + (int64_t)row * a.N + col,
                                   a.v_bf16);
-        e = 2.f * a.eta[(int64_t)z * a.eta_zstride + row] * (x - vv);
-        put_planes(a.e, z, (int64_t)row * a.e.ld + col, e);
+        e = 2.f * eta[row] * (g.acc[0][i][j][v] - vv);
       }
-      put_planes(a.et, z, (int64_t)col * a.et.ld + row, e);
-    } else {  // DH_MSE
-      float d1 = 0.f, d3 = 0.f;
-      if (row < a.nrows) {
+      g.acc[0][i][j][v] = e;
+    });
+    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.e, z, m0, n0, rn, cl);
+  } else {  // DH_MSE
+    f32x16 d3[G::TM][G::TN];
+    g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
+      const int row = m0 + r, col = n0 + c;
+      float x1 = 0.f, x3 = 0.f;
+      if (row < a.nrows && col < a.N) {
         const int64_t fo = (int64_t)z * a.f_zstride + (int64_t)row * a.N + col;
-        d1 = x * a.fa[fo];
-        if (a.swiglu) d3 = x * a.fb[fo];
+        x1 = g.acc[0][i][j][v] * a.fa[fo];
+        if (a.swiglu) x3 = g.acc[0][i][j][v] * a.fb[fo];
       }
-      put_planes(a.dz1t, z, (int64_t)col * a.dz1t.ld + row, d1);
-      if (a.swiglu) put_planes(a.dz3t, z, (int64_t)col * a.dz3t.ld + row, d3);
-    }
-  });
+      g.acc[0][i][j][v] = x1;
+      d3[i][j][v] = x3;
+    });
+    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.dz1, z, m0, n0, rn, cl);
+    if (a.swiglu) store_tile_planes<G, TILE_NORMAL>(d3, smem, a.dz3, z, m0, n0, rn, cl);
+  }
 }
 
 // ------------------------------------------------------------------------ block reduction
-__device__ __forceinline__ float block_sum_256(float v, float* scratch) {
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
   if (lane == 0) scratch[wave] = v;
   __syncthreads();
-  const float t = scratch[0] + scratch[1] + scratch[2] + scratch[3];
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += scratch[w];
   __syncthreads();
   return t;
 }
 
 // ------------------------------------------------------------------------ contraction
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void k_contract(ContractArgs a) {
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, L_COL, L_COL>;
   const int zz = blockIdx.y;
   const int m = zz / a.P, p = zz % a.P;
   const int m0 = (blockIdx.x / a.tiles_n) * BM;
   const int n0 = (blockIdx.x % a.tiles_n) * BN;
-  Operand A[1] = {a.a[m]};
-  Operand B[1] = {a.b[m]};
-  const int IA[1] = {0}, IB[1] = {0};
-  MultiGemm<BM, BN, 1, 1, 1> g;
+  G g;
   g.zero();
-  g.run(A, B, IA, IB, m0, n0, p, a.K, smem);
+  g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, smem);
 
   const int M = a.M, N = a.N;
   const int64_t base = (int64_t)zz * M * N;
   const int tr = (a.tr_mask >> m) & 1;
   float ss = 0.f;
-  g.for_each([&](int i, int j, int v, int r, int c) {
+  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int row = m0 + r, col = n0 + c;
-    if (row >= M || col >= N) return;
     float x = g.acc[0][i][j][v];
-    const int64_t off = base + (int64_t)row * N + col;
-    if (a.accum_in) x += a.G[off];
-    if (!a.last) {
-      a.G[off] = x;
-    } else if (a.muon) {
-      a.G[off] = x;
-      put_planes(a.x, zz, (int64_t)row * N + col, x);
-      put_planes(a.xt, zz, (int64_t)col * M + row, x);
-      ss += x * x;
-    } else {
-      a.U[tr ? base + (int64_t)col * M + row : off] = x;
+    if (row < M && col < N) {
+      const int64_t off = base + (int64_t)row * N + col;
+      if (a.accum_in) x += a.G[off];
+      if (!a.last) {
+        a.G[off] = x;
+      } else if (a.muon) {
+        a.G[off] = x;
+        ss += x * x;
+      } else {
+        a.U[tr ? base + (int64_t)col * M + row : off] = x;
+      }
     }
+    g.acc[0][i][j][v] = x;
   });
   if (a.last && a.muon) {
-    const float t = block_sum_256(ss, reinterpret_cast<float*>(smem));
+    const int rl = min(BM, M - m0), cl = min(BN, N - n0);
+    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.x, zz, m0, n0, rl, cl);
+    const float t = block_sum(ss, reinterpret_cast<float*>(smem));
     if (threadIdx.x == 0) a.part[(int64_t)zz * a.tiles + blockIdx.x] = t;
   }
 }
@@ -239,96 +251,109 @@ __device__ __forceinline__ void tri_tile(int t, int nt, int& ti, int& tj) {
   tj = ti + t;
 }
 
-// A = s^2 X X^T, upper tiles computed, both triangles written.
-template <int T>
-__global__ __launch_bounds__(256) void k_ns_gram(NsArgs a) {
+// Store a tile of a symmetric M x M matrix computed at tile (ti, tj), ti <= tj, as planes
+// of the full matrix (upper tile, its mirror, or the symmetrised diagonal tile).
+template <class G>
+__device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char* smem,
+                                          const PlaneBuf& dst, int zz, int m0, int n0, int M,
+                                          bool diag) {
+  const int rl = min(G::TBM, M - m0), cl = min(G::TBN, M - n0);
+  if (diag) {
+    store_tile_planes<G, TILE_SYM>(v, smem, dst, zz, m0, n0, rl, cl);
+  } else {
+    store_tile_planes<G, TILE_NORMAL>(v, smem, dst, zz, m0, n0, rl, cl);
+    store_tile_planes<G, TILE_TRANS>(v, smem, dst, zz, m0, n0, rl, cl);
+  }
+}
+
+// A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
+// the polynomial stage reads); A planes written for the full symmetric matrix.
+template <int T, int WG>
+__global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  using G = Gemm<T, T, WG, WG, 1, 1>;
   const int zz = blockIdx.y;
   const int M = a.M;
   int ti, tj;
   tri_tile(blockIdx.x, (M + T - 1) / T, ti, tj);
   const int m0 = ti * T, n0 = tj * T;
-  Operand X = operand_of(a.xin, a.xin.np, M);
-  Operand A[1] = {X};
-  Operand B[1] = {X};
-  const int IA[1] = {0}, IB[1] = {0};
-  MultiGemm<T, T, 1, 1, 1> g;
+  const Operand X = operand_of(a.xin, a.xin.np, M);
+  G g;
   g.zero();
-  g.run(A, B, IA, IB, m0, n0, zz, a.N, smem);
+  g.run(&X, &X, m0, n0, zz, a.N, smem);
   float s2 = 1.f;
   if (a.first) {
     const float s = ns_scale(a, zz);
     s2 = s * s;
   }
   const int64_t base = (int64_t)zz * M * M;
-  g.for_each([&](int i, int j, int v, int r, int c) {
+  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
-    if (R >= M || C >= M || R > C) return;
     const float x = s2 * g.acc[0][i][j][v];
-    a.afp[base + (int64_t)R * M + C] = x;
-    a.afp[base + (int64_t)C * M + R] = x;
-    put_planes(a.aout, zz, (int64_t)R * M + C, x);
-    put_planes(a.aout, zz, (int64_t)C * M + R, x);
+    g.acc[0][i][j][v] = x;
+    if (R < M && C < M) a.afp[base + (int64_t)R * M + C] = x;
   });
+  store_sym<G>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
 // B = b A + c A A  (A symmetric, so A serves as its own transposed operand).
-template <int T>
-__global__ __launch_bounds__(256) void k_ns_poly(NsArgs a) {
+template <int T, int WG>
+__global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  using G = Gemm<T, T, WG, WG, 1, 1>;
   const int zz = blockIdx.y;
   const int M = a.M;
   int ti, tj;
   tri_tile(blockIdx.x, (M + T - 1) / T, ti, tj);
   const int m0 = ti * T, n0 = tj * T;
-  Operand Ao = operand_of(a.ain, a.ain.np, M);
-  Operand A[1] = {Ao};
-  Operand B[1] = {Ao};
-  const int IA[1] = {0}, IB[1] = {0};
-  MultiGemm<T, T, 1, 1, 1> g;
+  const Operand Ao = operand_of(a.ain, a.ain.np, M);
+  G g;
   g.zero();
-  g.run(A, B, IA, IB, m0, n0, zz, M, smem);
+  g.run(&Ao, &Ao, m0, n0, zz, M, smem);
   const int64_t base = (int64_t)zz * M * M;
-  g.for_each([&](int i, int j, int v, int r, int c) {
+  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
-    if (R >= M || C >= M || R > C) return;
-    const float x = a.coef_b * a.afp[base + (int64_t)R * M + C] + a.coef_c * g.acc[0][i][j][v];
-    put_planes(a.aout, zz, (int64_t)R * M + C, x);
-    put_planes(a.aout, zz, (int64_t)C * M + R, x);
+    float x = 0.f;
+    if (R < M && C < M && (ti != tj || R <= C))
+      x = a.coef_b * a.afp[base + (int64_t)R * M + C] + a.coef_c * g.acc[0][i][j][v];
+    g.acc[0][i][j][v] = x;
   });
+  store_sym<G>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
 // X' = a X + B X  (iteration 0: X = s G with the scale folded into the epilogue).
-template <int T>
-__global__ __launch_bounds__(256) void k_ns_update(NsArgs a) {
+template <int T, int WG>
+__global__ __launch_bounds__(WG * WG * 64) void k_ns_update(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  using G = Gemm<T, T, WG, WG, 1, 1, L_ROW, L_COL>;
   const int zz = blockIdx.y;
   const int M = a.M, N = a.N;
   const int m0 = (blockIdx.x / a.tiles_n) * T;
   const int n0 = (blockIdx.x % a.tiles_n) * T;
-  Operand A[1] = {operand_of(a.ain, a.ain.np, M)};
-  Operand B[1] = {operand_of(a.xtin, a.xtin.np, N)};
-  const int IA[1] = {0}, IB[1] = {0};
-  MultiGemm<T, T, 1, 1, 1> g;
+  const Operand Ao = operand_of(a.ain, a.ain.np, M);
+  const Operand Bo = operand_of(a.xin, a.xin.np, N);   // X [M][N] read as its columns
+  G g;
   g.zero();
-  g.run(A, B, IA, IB, m0, n0, zz, M, smem);
+  g.run(&Ao, &Bo, m0, n0, zz, M, smem);
   const float sc = a.first ? ns_scale(a, zz) : 1.f;
   const int64_t base = (int64_t)zz * M * N;
   const int m = zz / a.P;
   const int tr = (a.tr_mask >> m) & 1;
-  g.for_each([&](int i, int j, int v, int r, int c) {
+  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
-    if (R >= M || C >= N) return;
-    const int64_t off = base + (int64_t)R * N + C;
-    const float x = sc * (a.coef_a * a.G[off] + g.acc[0][i][j][v]);
-    if (!a.last) {
-      a.G[off] = x;
-      put_planes(a.xout, zz, (int64_t)R * N + C, x);
-      put_planes(a.xtout, zz, (int64_t)C * M + R, x);
-    } else {
-      a.U[tr ? base + (int64_t)C * M + R : off] = x;
+    float x = 0.f;
+    if (R < M && C < N) {
+      const int64_t off = base + (int64_t)R * N + C;
+      x = sc * (a.coef_a * a.G[off] + g.acc[0][i][j][v]);
+      if (!a.last) a.G[off] = x;
+      else a.U[tr ? base + (int64_t)C * M + R : off] = x;
     }
+    g.acc[0][i][j][v] = x;
   });
+  if (!a.last) {
+    const int rl = min(T, M - m0), cl = min(T, N - n0);
+    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.xout, zz, m0, n0, rl, cl);
+  }
 }
 
 // ------------------------------------------------------------------------ renorm / update
@@ -377,36 +402,16 @@ __global__ __launch_bounds__(256) void k_renorm(RenormArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------ token transpose
-// Rows [n][d] of a chunk (activation dtype) -> planes [d][bpad], optionally scaled by
-// -eta_t; columns t in [n, bpad) are written as zeros.
-__global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
-  __shared__ float tile[64][65];
-  const int z = blockIdx.z;
-  const int t0 = blockIdx.x * 64, i0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int rr = 0; rr < 16; ++rr) {
-    const int t = t0 + ty + 4 * rr, i = i0 + tx;
-    float val = 0.f;
-    if (t < a.n && i < a.d) {
-      val = load_act(a.x, (int64_t)z * a.x_zstride + (int64_t)t * a.d + i, a.x_bf16);
-      if (a.neg_eta) val *= -a.eta[(int64_t)z * a.eta_zstride + t];
-    }
-    tile[ty + 4 * rr][tx] = val;
-  }
-  __syncthreads();
-  for (int rr = 0; rr < 16; ++rr) {
-    const int i = i0 + ty + 4 * rr, t = t0 + tx;
-    if (i < a.d && t < a.bpad) put_planes(a.out, z, (int64_t)i * a.out.ld + t, tile[tx][ty + 4 * rr]);
-  }
-}
-
-// fp32 rows -> bf16 planes, same layout.
+// Token rows [n][d] (activation dtype) -> bf16 planes in the same layout, optionally with
+// row t scaled by -eta_t.
 __global__ __launch_bounds__(256) void k_split(SplitArgs a) {
   const int z = blockIdx.y;
   const int64_t total = (int64_t)a.n * a.d;
-  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256)
-    put_planes(a.out, z, e, a.x[(int64_t)z * a.x_zstride + e]);
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    float x = load_act(a.x, (int64_t)z * a.x_zstride + e, a.x_bf16);
+    if (a.neg_eta) x *= -a.eta[(int64_t)z * a.eta_zstride + e / a.d];
+    put_planes(a.out, z, e, x);
+  }
 }
 
 // ============================================================================ launchers
@@ -419,47 +424,30 @@ static hipError_t set_lds(K kernel, int bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int BM, int BN, int FW, int MODE>
-static hipError_t front_bm(const FrontArgs& a0, int Z, hipStream_t s) {
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE>
+static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
   using FS = FrontShape<FW, MODE>;
-  using TS = TileShape<BM, BN, FS::NA, FS::NB>;
+  using G = Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB>;
   FrontArgs a = a0;
-  int pa[2] = {a.x.planes, a.v.planes};
-  int pb[3];
-  pb[0] = a.w1.planes;
-  int nb = 1;
-  if (FW == FW_SWIGLU) pb[nb++] = a.w3.planes;
-  if (FS::DOT) pb[nb++] = a.w2t.planes;
-  const int lds = 2 * TS::stage_bytes(pa, pb);
-  if (lds > LDS_MAX) return hipErrorInvalidValue;
-  auto kern = k_front<BM, BN, FW, MODE>;
-  hipError_t e = set_lds(kern, lds);
+  auto kern = k_front<BM, BN, WGM, WGN, FW, MODE>;
+  hipError_t e = set_lds(kern, G::LDS_BYTES);
   if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
-  const int tiles_m = (a.mrows + BM - 1) / BM;
+  const int tiles_m = (a.nrows + BM - 1) / BM;
   if (tiles_m == 0 || Z == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * a.tiles_n, Z), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * a.tiles_n, Z), dim3(G::NT), G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
 template <int FW, int MODE>
 static hipError_t front_fm(const FrontArgs& a, int Z, hipStream_t s) {
-  using FS = FrontShape<FW, MODE>;
-  using TS = TileShape<128, 64, FS::NA, FS::NB>;
-  int pa[2] = {a.x.planes, a.v.planes};
-  int pb[3];
-  pb[0] = a.w1.planes;
-  int nb = 1;
-  if (FW == FW_SWIGLU) pb[nb++] = a.w3.planes;
-  if (FS::DOT) pb[nb++] = a.w2t.planes;
-  if (2 * TS::stage_bytes(pa, pb) <= LDS_MAX) return front_bm<128, 64, FW, MODE>(a, Z, s);
-  return front_bm<64, 64, FW, MODE>(a, Z, s);
+  return front_t<128, 128, 2, 2, FW, MODE>(a, Z, s);
 }
 
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s) {
   if (fw == FW_SWIGLU) {
     if (mode == FRONT_Q) return front_fm<FW_SWIGLU, FRONT_Q>(a, Z, s);
-    if (mode == FRONT_K_DOT) return front_fm<FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
+    if (mode == FRONT_K_DOT) return front_t<128, 64, 2, 2, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
     return front_fm<FW_SWIGLU, FRONT_K_MSE>(a, Z, s);
   }
   if (mode == FRONT_Q) return front_fm<FW_GELU, FRONT_Q>(a, Z, s);
@@ -469,18 +457,16 @@ hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t
 
 template <int MODE>
 static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
-  constexpr int BM = 128, BN = 64;
-  using TS = TileShape<BM, BN, 1, 1>;
+  constexpr int BM = 128, BN = 128;
+  using G = Gemm<BM, BN, 2, 2, 1, 1>;
   OutArgs a = a0;
-  int pa[1] = {a.a.planes}, pb[1] = {a.b.planes};
-  const int lds = 2 * TS::stage_bytes(pa, pb);
-  auto kern = k_out<BM, BN, MODE>;
-  hipError_t e = set_lds(kern, lds);
+  auto kern = k_out<BM, BN, 2, 2, MODE>;
+  hipError_t e = set_lds(kern, G::LDS_BYTES);
   if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
-  const int tiles_m = (a.mrows + BM - 1) / BM;
+  const int tiles_m = (a.nrows + BM - 1) / BM;
   if (tiles_m == 0 || Z == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * a.tiles_n, Z), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * a.tiles_n, Z), dim3(G::NT), G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
@@ -492,27 +478,21 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
-  using TS = TileShape<BM, BN, 1, 1>;
+  using G = Gemm<BM, BN, 2, 2, 1, 1, L_COL, L_COL>;
   ContractArgs a = a0;
-  int lds = 0;
-  for (int m = 0; m < nm; ++m) {
-    int pa[1] = {a.a[m].planes}, pb[1] = {a.b[m].planes};
-    const int l = 2 * TS::stage_bytes(pa, pb);
-    lds = l > lds ? l : lds;
-  }
-  auto kern = k_contract<BM, BN>;
-  hipError_t e = set_lds(kern, lds);
+  auto kern = k_contract<BM, BN, 2, 2>;
+  hipError_t e = set_lds(kern, G::LDS_BYTES);
   if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   if (a.tiles == 0 || a.P == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(a.tiles, nm * a.P), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.tiles, nm * a.P), dim3(G::NT), G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
 int ns_tile(int Z, int M) {
-  const int t128 = (M + 127) / 128;
-  return (Z * t128 * (t128 + 1) / 2 >= 256) ? 128 : 64;
+  (void)Z; (void)M;
+  return 128;
 }
 int ns_tri_tiles(int M, int tile) {
   const int t = (M + tile - 1) / tile;
@@ -521,58 +501,41 @@ int ns_tri_tiles(int M, int tile) {
 
 template <int T, int STAGE>
 static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
-  using TS = TileShape<T, T, 1, 1>;
+  constexpr int WG = 2;
+  using G = Gemm<T, T, WG, WG, 1, 1>;
   NsArgs a = a0;
-  int pa[1], pb[1];
-  if (STAGE == 0) { pa[0] = pb[0] = a.xin.np; }
-  else if (STAGE == 1) { pa[0] = pb[0] = a.ain.np; }
-  else { pa[0] = a.ain.np; pb[0] = a.xtin.np; }
-  const int lds = 2 * TS::stage_bytes(pa, pb);
   if (a.Z == 0) return hipSuccess;
+  hipError_t e;
   if (STAGE == 2) {
+    using GU = Gemm<T, T, WG, WG, 1, 1, L_ROW, L_COL>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T>;
-    hipError_t e = set_lds(kern, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(256), lds, s, a);
+    auto kern = k_ns_update<T, WG>;
+    if ((e = set_lds(kern, GU::LDS_BYTES)) != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(GU::NT), GU::LDS_BYTES, s, a);
   } else {
     a.tiles = ns_tri_tiles(a.M, T);
     if (STAGE == 0) {
-      auto kern = k_ns_gram<T>;
-      hipError_t e = set_lds(kern, lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(256), lds, s, a);
+      auto kern = k_ns_gram<T, WG>;
+      if ((e = set_lds(kern, G::LDS_BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
     } else {
-      auto kern = k_ns_poly<T>;
-      hipError_t e = set_lds(kern, lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(256), lds, s, a);
+      auto kern = k_ns_poly<T, WG>;
+      if ((e = set_lds(kern, G::LDS_BYTES)) != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) {
-  return ns_tile(a.Z, a.M) == 128 ? ns_t<128, 0>(a, s) : ns_t<64, 0>(a, s);
-}
-hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
-  return ns_tile(a.Z, a.M) == 128 ? ns_t<128, 1>(a, s) : ns_t<64, 1>(a, s);
-}
-hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
-  return ns_tile(a.Z, a.M) == 128 ? ns_t<128, 2>(a, s) : ns_t<64, 2>(a, s);
-}
+hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_t<128, 0>(a, s); }
+hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_t<128, 1>(a, s); }
+hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) { return ns_t<128, 2>(a, s); }
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
   if (a.P == 0 || a.nm == 0) return hipSuccess;
   const int blocks = (a.max_rows * a.P + 3) / 4;
   hipLaunchKernelGGL(k_renorm, dim3(blocks, a.nm), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const TransposeArgs& a, int Z, hipStream_t s) {
-  if (Z == 0 || a.bpad == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_transpose, dim3(a.bpad / 64, (a.d + 63) / 64, Z), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
