@@ -36,7 +36,7 @@ def read_state(c, st):
 
 
 def run_gpu(cfg, inp, planes=None, chunked=False):
-    """Whole sequence through libttt. Returns (O [B,H,T,d] fp64, [W per matrix [B,H,r,c]])."""
+    """Whole sequence through libttt. Returns (O [B,H,T,d] fp32, [W per matrix [B,H,r,c]])."""
     c = W.make_config(cfg, planes=planes)
     q, k, v, eta, w0 = device_inputs(cfg, inp)
     out = torch.empty_like(q)
@@ -54,7 +54,7 @@ def run_gpu(cfg, inp, planes=None, chunked=False):
         W.ttt_sequence_forward(st, q, k, v, eta, out, cfg.seq_len)
     Ws, _ = read_state(c, st)
     W.ttt_state_health(st)
-    O = out.float().cpu().numpy().astype(np.float64)
+    O = out.float().cpu().numpy()
     st.destroy()
     return O, Ws
 

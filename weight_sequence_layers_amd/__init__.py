@@ -29,8 +29,8 @@ STATUS = {0: "TTT_OK", 1: "TTT_E_NULL", 2: "TTT_E_SHAPE", 3: "TTT_E_DTYPE", 4: "
 PRECISION = {
     "tiny": (3, 3, 3, 3),
     "lm": (1, 2, 2, 2),
-    "long": (1, 2, 3, 3),
-    "long_alt": (1, 2, 3, 3),
+    "long": (1, 3, 3, 3),
+    "long_alt": (1, 3, 3, 3),
     "imageset": (1, 1, 2, 2),
     "smallchunk": (1, 1, 1, 1),
 }
