@@ -141,7 +141,6 @@ struct ttt_state {
   float* Wm[3] = {};    // per-matrix views
   float* Um[3] = {};
   u16* Wpl[3] = {};     // planes [wp][P][rows][cols]
-  u16* W2t = nullptr;   // planes of W2^T [wp][P][hidden][dim]
   // token-major workspaces, [planes][P][sb][cols]
   u16 *qpl = nullptr, *kpl = nullptr, *vpl = nullptr;  // fp32 activations as planes
   u16* nk = nullptr;                                   // -eta * K (linear net, dot loss)
@@ -184,7 +183,6 @@ size_t layout(ttt_state* s, char* base) {
   size_t oW = C.take<float>(state_numel(D)), oU = C.take<float>(state_numel(D));
   size_t oWpl[3];
   for (int m = 0; m < D.nm; ++m) oWpl[m] = C.take<u16>(D.wp * P * D.rows[m] * D.cols[m]);
-  size_t oW2t = lin ? 0 : C.take<u16>(D.wp * P * dh * d);
   size_t oq = 0, ok = 0, ov = 0;
   if (f32) {
     oq = C.take<u16>(D.in_q * P * sb * d);
@@ -230,7 +228,6 @@ size_t layout(ttt_state* s, char* base) {
       acc += P * D.rows[m] * D.cols[m];
       s->Wpl[m] = H(oWpl[m]);
     }
-    s->W2t = lin ? nullptr : H(oW2t);
     if (f32) { s->qpl = H(oq); s->kpl = H(ok); s->vpl = H(ov); }
     s->nk = (lin && !mse) ? H(onk) : nullptr;
     s->hq = lin ? nullptr : H(ohq);
@@ -299,9 +296,6 @@ ttt_status refresh_planes(ttt_state* s, bool with_update, hipStream_t st) {
     M.rows = D.rows[m]; M.cols = D.cols[m];
     M.pl = s->Wpl[m];
     M.pl_stride = (int64_t)D.P * D.rows[m] * D.cols[m];
-    const bool w2 = (s->cfg.fw != TTT_FW_LINEAR) && m == D.nm - 1;
-    M.plt = w2 ? s->W2t : nullptr;
-    M.plt_stride = (int64_t)D.P * D.rows[m] * D.cols[m];
     r.max_rows = std::max(r.max_rows, D.rows[m]);
   }
   STAGED(TTT_STAGE_RENORM, launch_renorm(r, st));
@@ -401,8 +395,9 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
                            (int64_t)D.rows[m] * D.cols[m], D.cols[m]), np, D.rows[m]);
   };
   const int w2 = D.nm - 1;
-  Operand w2t{};
-  if (!lin) w2t = operand_of(pbuf(s->W2t, gp, (int64_t)P * dh * d, (int64_t)dh * d, d), gp, dh);
+  // W2 [d][dh] read column-wise: the operand's rows are W2's columns (the hidden index)
+  Operand w2c{};
+  if (!lin) w2c = operand_of(pbuf(s->Wpl[w2], gp, (int64_t)P * d * dh, (int64_t)d * dh, dh), gp, dh);
 
   PlaneBuf dz1{}, dz3{}, pk{}, hk{}, e{}, nk{};
   if (!lin) {
@@ -414,7 +409,7 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     FrontArgs f{};
     f.A[0] = xk; f.A[1] = xv; f.B[0] = wop(0, gp);
     if (sw) f.B[1] = wop(1, gp);
-    f.B[sw ? 2 : 1] = w2t;
+    f.B[sw ? 2 : 1] = w2c;
     f.eta = eta; f.eta_zstride = R.T;
     f.nrows = R.nr; f.K = d; f.N = dh;
     f.o1 = dz1; f.o2 = dz3; f.o3 = pk;
@@ -446,7 +441,7 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     if (!lin) {
       OutArgs h{};
       h.a = operand_of(e, gp, R.nr);
-      h.b = w2t;
+      h.b = w2c;
       h.nrows = R.nr; h.K = d; h.N = dh;
       h.fa = s->fa; h.fb = s->fb; h.f_zstride = SB * dh;
       h.dz1 = dz1; h.dz3 = dz3; h.swiglu = sw;
@@ -521,7 +516,6 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
     a.aout = pbuf(s->bpl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
     STAGED(TTT_STAGE_NS_POLY, launch_ns_poly(a, st));
     a.ain = a.aout;
-    a.G = s->G;
     a.xout = pbuf(s->xpl[(it + 1) & 1], pn, (int64_t)Z * M * N, (int64_t)M * N, N);
     a.U = s->U;
     a.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);

@@ -85,7 +85,7 @@ struct PlaneBuf {
 //   accumulates  C_p[m][n] += sum_k A_{ia(p)}[m][k] * B_p[n][k]  with ia(p) = 1 for the
 //   last product when NA == 2, else 0.
 //
-// Operand layouts in memory (template parameters LA / LB):
+// Operand layouts in memory (bit i of the template masks LAM / LBM is operand i's layout):
 //   L_ROW  element (r, k) at r * ld + k   (rows contiguous along K)
 //   L_COL  element (r, k) at k * ld + r   (K-rows contiguous along the M / N index)
 // Both are staged into LDS without rearrangement and read into MFMA fragments with
@@ -104,28 +104,31 @@ struct PlaneBuf {
 enum Layout { L_ROW = 0, L_COL = 1 };
 
 __device__ __forceinline__ int swz_row(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz_col(int k) { return (k & 3) << 2; }
+// column tiles: rows k..k+3 read together by one transposing read land on distinct banks
+template <int R>
+__device__ __forceinline__ int swz_col(int k) { return R >= 128 ? (k & 3) << 2 : (k & 2); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int L, int R, int NT>
+// Per-thread load plan of one operand tile (R rows x 64 k) in either layout.
+template <int R, int NT>
 struct TileLoad {
   static constexpr int BK = 64;
   static constexpr int CHUNKS = R * BK / 8;        // 16-byte chunks per tile
   static constexpr int C = CHUNKS / NT;            // per thread
   static constexpr int BYTES = R * BK * 2;
   static_assert(CHUNKS % NT == 0, "uneven tile load");
-  static_assert(L == L_ROW || R >= 128, "column-layout tiles need >= 128 rows");
+  static_assert(R % 64 == 0, "tile rows must be a multiple of 64");
   uint32_t off[C];   // byte offset of the chunk at k0 = 0, or an out-of-range value
   int kk[C];         // k of the chunk's first element relative to k0
   int lds[C];        // LDS byte offset inside the tile
   uint32_t kstride;  // bytes per unit of k0
 
-  __device__ __forceinline__ void init(const Operand& o, int row0) {
+  __device__ __forceinline__ void init(const Operand& o, int row0, bool col) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int ch = threadIdx.x + c * NT;
-      if (L == L_ROW) {
+      if (!col) {
         const int r = ch >> 3, kc = ch & 7;
         kk[c] = kc * 8;
         lds[c] = r * 128 + ((kc ^ swz_row(r)) << 4);
@@ -134,37 +137,40 @@ struct TileLoad {
       } else {
         const int k = ch / (R / 8), mc = ch % (R / 8);
         kk[c] = k;
-        lds[c] = k * R * 2 + ((mc ^ swz_col(k)) << 4);
+        lds[c] = k * R * 2 + ((mc ^ swz_col<R>(k)) << 4);
         off[c] = (row0 + mc * 8 < o.rows) ? (uint32_t)(((int64_t)k * o.ld + row0 + mc * 8) * 2)
                                           : 0xC0000000u;
       }
     }
-    kstride = L == L_ROW ? 2u : (uint32_t)(o.ld * 2);
+    kstride = col ? (uint32_t)(o.ld * 2) : 2u;
   }
 };
 
 // MFMA fragment (32 rows x 16 k) of a staged tile for k-substep s.
-template <int L, int R>
+template <bool COL, int R>
 __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int s) {
   const int lane = threadIdx.x & 63;
-  if (L == L_ROW) {
+  if (!COL) {
     const int r = row_base + (lane & 31);
     const int ch = 2 * s + (lane >> 5);
     return *reinterpret_cast<const bf16x8*>(tile + r * 128 + ((ch ^ swz_row(r)) << 4));
   } else {
+    // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element (j % 4) of
+    // the 4-element rows addressed by lanes 4e + j/4, e = 0..3.  Lane 4e + q addresses
+    // k-row kb + e at m + 4q, so lane j gets A[m + j][kb + e] for e = 0..3.
     const int g = lane >> 4, j = lane & 15;
     const int m = row_base + 16 * (g & 1) + 4 * (j & 3);
     const int kb = 16 * s + 8 * (g >> 1) + (j >> 2);
     s16x4 lo, hi;
     {
       const int k = kb;
-      const char* a = tile + k * R * 2 + (((m >> 3) ^ swz_col(k)) << 4) + (m & 7) * 2;
+      const char* a = tile + k * R * 2 + (((m >> 3) ^ swz_col<R>(k)) << 4) + (m & 7) * 2;
       lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(a));
     }
     {
       const int k = kb + 4;
-      const char* a = tile + k * R * 2 + (((m >> 3) ^ swz_col(k)) << 4) + (m & 7) * 2;
+      const char* a = tile + k * R * 2 + (((m >> 3) ^ swz_col<R>(k)) << 4) + (m & 7) * 2;
       hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) s16x4*)(a));
     }
@@ -174,7 +180,7 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int 
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LA = L_ROW, int LB = L_ROW>
+template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0>
 struct Gemm {
   static constexpr int NT = WGM * WGN * 64;
   static constexpr int TBM = BM, TBN = BN, WGN_ = WGN;
@@ -182,8 +188,10 @@ struct Gemm {
   static constexpr int BK = 64;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  using TA = TileLoad<LA, BM, NT>;
-  using TB = TileLoad<LB, BN, NT>;
+  using TA = TileLoad<BM, NT>;
+  using TB = TileLoad<BN, NT>;
+  static constexpr bool acol(int i) { return (LAM >> i) & 1; }
+  static constexpr bool bcol(int i) { return (LBM >> i) & 1; }
   static constexpr int A_TILE = TA::BYTES, B_TILE = TB::BYTES;
   static constexpr int STAGE = NA * A_TILE + NB * B_TILE;
   static constexpr int LDS_BYTES = 2 * STAGE > STORE_LDS ? 2 * STAGE : STORE_LDS;
@@ -238,15 +246,15 @@ struct Gemm {
     int na_[NA], nb_[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      la[i].init(A[i], m0);
+      la[i].init(A[i], m0, acol(i));
       pa_[i] = A[i].p + (int64_t)z * A[i].zstride;
-      na_[i] = (int)(LA == L_ROW ? (int64_t)A[i].rows * A[i].ld * 2 : (int64_t)K * A[i].ld * 2);
+      na_[i] = (int)(!acol(i) ? (int64_t)A[i].rows * A[i].ld * 2 : (int64_t)K * A[i].ld * 2);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      lb[i].init(B[i], n0);
+      lb[i].init(B[i], n0, bcol(i));
       pb_[i] = B[i].p + (int64_t)z * B[i].zstride;
-      nb_[i] = (int)(LB == L_ROW ? (int64_t)B[i].rows * B[i].ld * 2 : (int64_t)K * B[i].ld * 2);
+      nb_[i] = (int)(!bcol(i) ? (int64_t)B[i].rows * B[i].ld * 2 : (int64_t)K * B[i].ld * 2);
     }
 
     uint4 ra[NA][TA::C], rb[NB][TB::C];
@@ -296,12 +304,15 @@ struct Gemm {
         for (int i = 0; i < NA; ++i)
 #pragma unroll
           for (int t = 0; t < TM; ++t)
-            fa[i][t] = read_frag<LA, BM>(st + i * A_TILE, wm0 + t * 32, s);
+            fa[i][t] = acol(i) ? read_frag<true, BM>(st + i * A_TILE, wm0 + t * 32, s)
+                               : read_frag<false, BM>(st + i * A_TILE, wm0 + t * 32, s);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
           for (int t = 0; t < TN; ++t)
-            fb[i][t] = read_frag<LB, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s);
+            fb[i][t] = bcol(i)
+                           ? read_frag<true, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s)
+                           : read_frag<false, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s);
 #pragma unroll
         for (int p = 0; p < NB; ++p)
 #pragma unroll

@@ -20,7 +20,8 @@ enum OutMode { OUT_Q = 0, OUT_K_MSE = 1, DH_MSE = 2 };
 // Z-GEMMs over rows of Q or K: X W1^T (and X W3^T), plus V W2 for the inner-product loss.
 struct FrontArgs {
   // A operands: [0] the rows (Q or K), [1] V (inner-product loss only).
-  // B operands in product order: W1, then W3 (SwiGLU), then W2^T (inner-product loss).
+  // B operands in product order: W1, then W3 (SwiGLU), then W2 read column-wise
+  // (inner-product loss).
   Operand A[2];
   Operand B[3];
   const float* eta;
@@ -83,11 +84,10 @@ struct NsArgs {
   int first;          // iteration 0 (fold the 1/(|G|_F + eps) scale)
   int last;           // final iteration: write U instead of planes
   float eps;
-  PlaneBuf xin;       // gram, update: X planes [M][N]
+  PlaneBuf xin;       // gram, update: X planes [M][N] (iteration 0: planes of G)
   PlaneBuf ain;       // poly: A planes [M][M] ; update: B planes [M][M]
   float* afp;         // gram out / poly in: A fp32 [Z][M][M]
   PlaneBuf aout;      // gram: A planes ; poly: B planes
-  float* G;           // update: X fp32 [Z][M][N], in/out
   PlaneBuf xout;
   float* U;           // last: U in weight orientation
   int tr_mask;
@@ -100,8 +100,6 @@ struct RenormMat {
   int rows, cols;
   u16* pl;         // planes [np][P][rows][cols]
   int64_t pl_stride;
-  u16* plt;        // transposed planes [np][P][cols][rows], or null
-  int64_t plt_stride;
 };
 struct RenormArgs {
   RenormMat m[3];

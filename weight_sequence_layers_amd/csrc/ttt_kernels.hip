@@ -55,7 +55,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using FS = FrontShape<FW, MODE>;
   constexpr int NA = FS::NA, NB = FS::NB;
-  using G = Gemm<BM, BN, WGM, WGN, NA, NB>;
+  // the inner-product loss reads W2 [dim][hidden] column-wise for V W2
+  using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0>;
   const int z = blockIdx.y;
   const int m0 = (blockIdx.x / a.tiles_n) * BM;
   const int n0 = (blockIdx.x % a.tiles_n) * BN;
@@ -125,7 +126,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
 template <int BM, int BN, int WGM, int WGN, int MODE>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1>;
+  // dH = E W2 reads W2 [dim][hidden] column-wise
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
   const int z = blockIdx.y;
   const int m0 = (blockIdx.x / a.tiles_n) * BM;
   const int n0 = (blockIdx.x % a.tiles_n) * BN;
@@ -197,7 +199,7 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1, L_COL, L_COL>;
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1>;   // both operands token-major
   const int zz = blockIdx.y;
   const int m = zz / a.P, p = zz % a.P;
   const int m0 = (blockIdx.x / a.tiles_n) * BM;
@@ -219,7 +221,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
       if (!a.last) {
         a.G[off] = x;
       } else if (a.muon) {
-        a.G[off] = x;
         ss += x * x;
       } else {
         a.U[tr ? base + (int64_t)col * M + row : off] = x;
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
   store_sym<G>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
-// B = b A + c A A  (A symmetric, so A serves as its own transposed operand).
+// B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
+// a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
 template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -315,17 +317,18 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
     const int R = m0 + r, C = n0 + c;
     float x = 0.f;
     if (R < M && C < M && (ti != tj || R <= C))
-      x = a.coef_b * a.afp[base + (int64_t)R * M + C] + a.coef_c * g.acc[0][i][j][v];
+      x = a.coef_b * a.afp[base + (int64_t)R * M + C] + a.coef_c * g.acc[0][i][j][v] +
+          (R == C ? a.coef_a : 0.f);
     g.acc[0][i][j][v] = x;
   });
   store_sym<G>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
-// X' = a X + B X  (iteration 0: X = s G with the scale folded into the epilogue).
+// X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
 template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_update(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  using G = Gemm<T, T, WG, WG, 1, 1, L_ROW, L_COL>;
+  using G = Gemm<T, T, WG, WG, 1, 1, 0, 1>;   // X [M][N] read column-wise
   const int zz = blockIdx.y;
   const int M = a.M, N = a.N;
   const int m0 = (blockIdx.x / a.tiles_n) * T;
@@ -343,10 +346,8 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_update(NsArgs a) {
     const int R = m0 + r, C = n0 + c;
     float x = 0.f;
     if (R < M && C < N) {
-      const int64_t off = base + (int64_t)R * N + C;
-      x = sc * (a.coef_a * a.G[off] + g.acc[0][i][j][v]);
-      if (!a.last) a.G[off] = x;
-      else a.U[tr ? base + (int64_t)C * M + R : off] = x;
+      x = sc * g.acc[0][i][j][v];
+      if (a.last) a.U[tr ? base + (int64_t)C * M + R : base + (int64_t)R * N + C] = x;
     }
     g.acc[0][i][j][v] = x;
   });
@@ -365,7 +366,6 @@ __global__ __launch_bounds__(256) void k_renorm(RenormArgs a) {
   const int lane = threadIdx.x & 63;
   const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gr >= M.rows * a.P) return;
-  const int p = gr / M.rows, r = gr % M.rows;
   const int cols = M.cols;
   float* w = M.W + (int64_t)gr * cols;
   const float* u = M.U ? M.U + (int64_t)gr * cols : nullptr;
@@ -392,13 +392,8 @@ __global__ __launch_bounds__(256) void k_renorm(RenormArgs a) {
     u16 h[3];
     split_planes(x, a.np, h);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      if (q < a.np) {
-        M.pl[q * M.pl_stride + (int64_t)gr * cols + c] = h[q];
-        if (M.plt)
-          M.plt[q * M.plt_stride + (int64_t)p * cols * M.rows + (int64_t)c * M.rows + r] = h[q];
-      }
-    }
+    for (int q = 0; q < 3; ++q)
+      if (q < a.np) M.pl[q * M.pl_stride + (int64_t)gr * cols + c] = h[q];
   }
 }
 
@@ -427,7 +422,7 @@ static hipError_t set_lds(K kernel, int bytes) {
 template <int BM, int BN, int WGM, int WGN, int FW, int MODE>
 static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
   using FS = FrontShape<FW, MODE>;
-  using G = Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB>;
+  using G = Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB, 0, FS::DOT ? (1 << (FS::NB - 1)) : 0>;
   FrontArgs a = a0;
   auto kern = k_front<BM, BN, WGM, WGN, FW, MODE>;
   hipError_t e = set_lds(kern, G::LDS_BYTES);
@@ -458,7 +453,7 @@ hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t
 template <int MODE>
 static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
   constexpr int BM = 128, BN = 128;
-  using G = Gemm<BM, BN, 2, 2, 1, 1>;
+  using G = Gemm<BM, BN, 2, 2, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
   OutArgs a = a0;
   auto kern = k_out<BM, BN, 2, 2, MODE>;
   hipError_t e = set_lds(kern, G::LDS_BYTES);
@@ -478,7 +473,7 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
-  using G = Gemm<BM, BN, 2, 2, 1, 1, L_COL, L_COL>;
+  using G = Gemm<BM, BN, 2, 2, 1, 1, 1, 1>;
   ContractArgs a = a0;
   auto kern = k_contract<BM, BN, 2, 2>;
   hipError_t e = set_lds(kern, G::LDS_BYTES);
@@ -507,7 +502,7 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
   if (a.Z == 0) return hipSuccess;
   hipError_t e;
   if (STAGE == 2) {
-    using GU = Gemm<T, T, WG, WG, 1, 1, L_ROW, L_COL>;
+    using GU = Gemm<T, T, WG, WG, 1, 1, 0, 1>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
     auto kern = k_ns_update<T, WG>;
