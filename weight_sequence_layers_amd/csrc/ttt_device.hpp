@@ -359,6 +359,19 @@ struct Gemm {
   }
 };
 
+// ------------------------------------------------------------------------ block order
+// Workgroups of a launch are handed to the 8 XCDs round-robin by linear id, and each XCD
+// has its own L2.  xcd_block() renumbers the launch so that XCD x runs a contiguous range
+// of logical blocks: with logical ids ordered (problem, tile), the tiles that share a
+// problem's operands run on one XCD and hit the same L2.
+constexpr int NUM_XCD = 8;
+
+__device__ __forceinline__ int xcd_block(int id, int total) {
+  const int q = total / NUM_XCD, r = total % NUM_XCD;
+  const int x = id % NUM_XCD, j = id / NUM_XCD;
+  return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
 // ------------------------------------------------------------------------ tile stores
 // Write one block tile of fp32 values (held in the MFMA accumulator layout of gemm G) to
 // a bf16-plane buffer through LDS, so that global stores are 16-byte vectors along the

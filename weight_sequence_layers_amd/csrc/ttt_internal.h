@@ -29,7 +29,7 @@ struct FrontArgs {
   int nrows;   // token rows
   int K;       // dim
   int N;       // hidden
-  int tiles_n;
+  int tiles_n, tiles;
   PlaneBuf o1, o2, o3;  // Q: hidden | K_DOT: dZ1, dZ3 (or dZ), P | K_MSE: H; all [rows][hidden]
   float* fa;            // K_MSE: derivative factors [rows][hidden]
   float* fb;
@@ -40,7 +40,7 @@ struct FrontArgs {
 // dH = E W2 for the MSE loss.
 struct OutArgs {
   Operand a, b;
-  int nrows, K, N, tiles_n;
+  int nrows, K, N, tiles_n, tiles;
   // OUT_Q
   void* out;
   int64_t out_zstride;

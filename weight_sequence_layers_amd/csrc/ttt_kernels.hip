@@ -57,9 +57,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   constexpr int NA = FS::NA, NB = FS::NB;
   // the inner-product loss reads W2 [dim][hidden] column-wise for V W2
   using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0>;
-  const int z = blockIdx.y;
-  const int m0 = (blockIdx.x / a.tiles_n) * BM;
-  const int n0 = (blockIdx.x % a.tiles_n) * BN;
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int z = lid / a.tiles, tile = lid % a.tiles;
+  const int m0 = (tile / a.tiles_n) * BM;
+  const int n0 = (tile % a.tiles_n) * BN;
 
   G g;
   g.zero();
@@ -128,9 +129,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // dH = E W2 reads W2 [dim][hidden] column-wise
   using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
-  const int z = blockIdx.y;
-  const int m0 = (blockIdx.x / a.tiles_n) * BM;
-  const int n0 = (blockIdx.x % a.tiles_n) * BN;
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int z = lid / a.tiles, tile = lid % a.tiles;
+  const int m0 = (tile / a.tiles_n) * BM;
+  const int n0 = (tile % a.tiles_n) * BN;
   G g;
   g.zero();
   g.run(&a.a, &a.b, m0, n0, z, a.K, smem);
@@ -200,10 +202,11 @@ template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1>;   // both operands token-major
-  const int zz = blockIdx.y;
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int m = zz / a.P, p = zz % a.P;
-  const int m0 = (blockIdx.x / a.tiles_n) * BM;
-  const int n0 = (blockIdx.x % a.tiles_n) * BN;
+  const int m0 = (tile / a.tiles_n) * BM;
+  const int n0 = (tile % a.tiles_n) * BN;
   G g;
   g.zero();
   g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, smem);
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
     const int rl = min(BM, M - m0), cl = min(BN, N - n0);
     store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.x, zz, m0, n0, rl, cl);
     const float t = block_sum(ss, reinterpret_cast<float*>(smem));
-    if (threadIdx.x == 0) a.part[(int64_t)zz * a.tiles + blockIdx.x] = t;
+    if (threadIdx.x == 0) a.part[(int64_t)zz * a.tiles + tile] = t;
   }
 }
 
@@ -273,10 +276,11 @@ template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<T, T, WG, WG, 1, 1>;
-  const int zz = blockIdx.y;
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int zz = lid / a.tiles;
   const int M = a.M;
   int ti, tj;
-  tri_tile(blockIdx.x, (M + T - 1) / T, ti, tj);
+  tri_tile(lid % a.tiles, (M + T - 1) / T, ti, tj);
   const int m0 = ti * T, n0 = tj * T;
   const Operand X = operand_of(a.xin, a.xin.np, M);
   G g;
@@ -303,10 +307,11 @@ template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<T, T, WG, WG, 1, 1>;
-  const int zz = blockIdx.y;
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int zz = lid / a.tiles;
   const int M = a.M;
   int ti, tj;
-  tri_tile(blockIdx.x, (M + T - 1) / T, ti, tj);
+  tri_tile(lid % a.tiles, (M + T - 1) / T, ti, tj);
   const int m0 = ti * T, n0 = tj * T;
   const Operand Ao = operand_of(a.ain, a.ain.np, M);
   G g;
@@ -329,10 +334,11 @@ template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_update(NsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<T, T, WG, WG, 1, 1, 0, 1>;   // X [M][N] read column-wise
-  const int zz = blockIdx.y;
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int M = a.M, N = a.N;
-  const int m0 = (blockIdx.x / a.tiles_n) * T;
-  const int n0 = (blockIdx.x % a.tiles_n) * T;
+  const int m0 = (tile / a.tiles_n) * T;
+  const int n0 = (tile % a.tiles_n) * T;
   const Operand Ao = operand_of(a.ain, a.ain.np, M);
   const Operand Bo = operand_of(a.xin, a.xin.np, N);   // X [M][N] read as its columns
   G g;
@@ -429,8 +435,9 @@ static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
   if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
-  if (tiles_m == 0 || Z == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * a.tiles_n, Z), dim3(G::NT), G::LDS_BYTES, s, a);
+  a.tiles = tiles_m * a.tiles_n;
+  if (a.tiles == 0 || Z == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
@@ -460,8 +467,9 @@ static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
   if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
-  if (tiles_m == 0 || Z == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(tiles_m * a.tiles_n, Z), dim3(G::NT), G::LDS_BYTES, s, a);
+  a.tiles = tiles_m * a.tiles_n;
+  if (a.tiles == 0 || Z == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
@@ -481,7 +489,7 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   if (a.tiles == 0 || a.P == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(a.tiles, nm * a.P), dim3(G::NT), G::LDS_BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.tiles * nm * a.P), dim3(G::NT), G::LDS_BYTES, s, a);
   return hipGetLastError();
 }
 
@@ -507,17 +515,17 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
     auto kern = k_ns_update<T, WG>;
     if ((e = set_lds(kern, GU::LDS_BYTES)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(GU::NT), GU::LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(GU::NT), GU::LDS_BYTES, s, a);
   } else {
     a.tiles = ns_tri_tiles(a.M, T);
     if (STAGE == 0) {
       auto kern = k_ns_gram<T, WG>;
       if ((e = set_lds(kern, G::LDS_BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
+      hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
     } else {
       auto kern = k_ns_poly<T, WG>;
       if ((e = set_lds(kern, G::LDS_BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(a.tiles, a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
+      hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
     }
   }
   return hipGetLastError();
