@@ -449,7 +449,7 @@ static hipError_t front_fm(const FrontArgs& a, int Z, hipStream_t s) {
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s) {
   if (fw == FW_SWIGLU) {
     if (mode == FRONT_Q) return front_fm<FW_SWIGLU, FRONT_Q>(a, Z, s);
-    if (mode == FRONT_K_DOT) return front_t<128, 64, 2, 2, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
+    if (mode == FRONT_K_DOT) return front_t<128, 128, 2, 2, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
     return front_fm<FW_SWIGLU, FRONT_K_MSE>(a, Z, s);
   }
   if (mode == FRONT_Q) return front_fm<FW_GELU, FRONT_Q>(a, Z, s);
