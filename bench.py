@@ -67,6 +67,32 @@ def total_flops(cfg) -> float:
     return P * (cfg.seq_len * per_tok + cfg.n_chunks * ns)
 
 
+def source_digest() -> str:
+    """Hash of the kernel sources; counter summaries record the digest they were taken at."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "weight_sequence_layers_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from profiles/<workload>_traffic.md, if that summary
+    was taken from the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    digest, val = None, None
+    for line in open(path):
+        if line.startswith("source digest:"):
+            digest = line.split(":", 1)[1].strip()
+        if line.startswith(f"| {stage} |"):
+            val = float(line.split("|")[-2])
+    return val if digest == source_digest() else None
+
+
 def cpu_baseline(cfg, budget_chunks=None):
     """The oracle on the host: one (batch, head) problem over its first chunks."""
     import numpy as np
@@ -99,6 +125,9 @@ def main():
     ap.add_argument("--planes", default=None, help="apply,grad,ns,ns_lead bf16 plane counts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunks", type=int, default=None)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the steps, run one plain device copy of this many MiB (a "
+                         "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -132,6 +161,15 @@ def main():
     out = torch.empty_like(dev[0])
     del inp
     st = W.ttt_init_state(c, w0)
+    if args.calib_copy_mib:
+        # one elementwise kernel that reads and writes exactly this many bytes each
+        n = (args.calib_copy_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         W.ttt_sequence_forward(st, *dev, eta, out, cfg.seq_len)
@@ -174,7 +212,8 @@ def main():
     achieved = flops[dom] / avg_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2),
+                "traffic": recorded_traffic(cfg.name, dom), "kernel": dom,
+                "avg_launch_us": round(avg_s * 1e6, 2),
                 "launches": n_dom}
     res = {
         "metric": "TTT-layer tokens/sec (update+apply) at chunk 2048; % bf16 MFMA peak",
@@ -187,6 +226,7 @@ def main():
                                f"{int(cfg.renorm)}, {cfg.act}, {cfg.order}",
                    "global_batch": cfg.batch, "seq_len": cfg.seq_len, "parallelism": "none",
                    "bf16_planes_apply_grad_ns_nslead": list(planes)},
+        "source_digest": source_digest(),
         "layer_tflops_algorithmic": round(tf_layer, 2),
         "pct_bf16_peak_algorithmic": round(100 * tf_layer / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
