@@ -33,7 +33,8 @@ def log(*a):
 
 def stage_flops(cfg) -> dict:
     """Algorithmic FLOP of one launch of each stage kernel (one chunk, all problems; 2 per
-    multiply-add; Newton-Schulz counted without symmetry savings)."""
+    multiply-add; Newton-Schulz counted without symmetry savings; the resident loop: the
+    whole sequence)."""
     P, b, d, dh = cfg.batch * cfg.heads, cfg.chunk, cfg.dim, cfg.hidden
     nz = {"swiglu": 2, "gelu": 1, "linear": 1}[cfg.fw]
     nm = {"swiglu": 3, "gelu": 2, "linear": 1}[cfg.fw]
@@ -50,6 +51,8 @@ def stage_flops(cfg) -> dict:
     f["ns_gram"] = 2.0 * m * m * n * nm * P
     f["ns_poly"] = 2.0 * m * m * m * nm * P
     f["ns_update"] = 2.0 * m * m * n * nm * P
+    # the device-resident loop runs every chunk of the call in one launch
+    f["resident"] = total_flops(cfg)
     return f
 
 

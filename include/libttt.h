@@ -61,6 +61,7 @@ typedef enum { TTT_FW_SWIGLU = 0, TTT_FW_MLP_GELU = 1, TTT_FW_LINEAR = 2 } ttt_f
 typedef enum { TTT_LOSS_DOT = 0, TTT_LOSS_MSE = 1 } ttt_loss;
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
 typedef enum { TTT_APPLY_THEN_UPDATE = 0, TTT_UPDATE_THEN_APPLY = 1 } ttt_order;
+typedef enum { TTT_PATH_AUTO = 0, TTT_PATH_STAGED = 1, TTT_PATH_RESIDENT = 2 } ttt_path;
 
 /*
  * Layer configuration.  Limits: batch, heads >= 1; batch*heads <= 65535; dim and hidden
@@ -80,6 +81,15 @@ typedef enum { TTT_APPLY_THEN_UPDATE = 0, TTT_UPDATE_THEN_APPLY = 1 } ttt_order;
  *   ns_lead_planes the first Newton-Schulz iteration
  * A value of 0 selects the default: 3 for fp32 activations, else 1 (apply), 2 (grad),
  * 2 (ns, ns_lead).
+ *
+ * Execution path.  STAGED runs each chunk as a sequence of stage kernels (any supported
+ * configuration).  RESIDENT runs all chunks of a call in one kernel that keeps each
+ * problem's fast weights on chip; it serves the small-chunk GELU-MLP layer only: fw
+ * MLP_GELU, dim 64, hidden 256, chunk <= 64, ns_steps 0, no renorm, bf16 activations,
+ * APPLY_THEN_UPDATE, apply_planes and grad_planes 1 (explicitly or by default they must
+ * resolve to 1).  AUTO picks RESIDENT where it applies, else STAGED; asking for RESIDENT
+ * elsewhere is TTT_E_UNSUPPORTED.  The two paths order their roundings differently;
+ * both keep the bf16 accuracy bound of the single-plane setting.
  */
 typedef struct {
   int32_t batch, heads, dim, hidden, chunk;
@@ -90,6 +100,7 @@ typedef struct {
   int32_t ns_steps;   /* 0: W <- W - grad;  n > 0: W <- W - NS_n(grad)  (Muon uses 5) */
   int32_t row_renorm; /* 0 or 1 */
   int32_t apply_planes, grad_planes, ns_planes, ns_lead_planes;
+  int32_t path;       /* ttt_path */
 } ttt_config;
 
 /* Host-only check of a configuration (no HIP call).  TTT_OK or the first problem found. */
@@ -141,13 +152,15 @@ ttt_status ttt_destroy_state(ttt_state* s);
  * stream and returns the number of timed launches and the sum of their durations in ms.
  * Stages: 0 front (query rows), 1 front (key rows), 2 output GEMM, 3 token contraction,
  * 4 Newton-Schulz Gram, 5 Newton-Schulz polynomial, 6 Newton-Schulz update,
- * 7 update + renorm, 8 token transpose, 9 fp32 plane split, 10 MSE error / dH GEMMs.
+ * 7 update + renorm, 8 (unused), 9 fp32 plane split, 10 MSE error / dH GEMMs,
+ * 11 device-resident chunk loop (one launch per call).
  * The hooks create and destroy HIP events but allocate no device memory.
  */
 typedef enum {
   TTT_STAGE_FRONT_Q = 0, TTT_STAGE_FRONT_K = 1, TTT_STAGE_OUT = 2, TTT_STAGE_CONTRACT = 3,
   TTT_STAGE_NS_GRAM = 4, TTT_STAGE_NS_POLY = 5, TTT_STAGE_NS_UPDATE = 6, TTT_STAGE_RENORM = 7,
-  TTT_STAGE_TRANSPOSE = 8, TTT_STAGE_SPLIT = 9, TTT_STAGE_MSE = 10, TTT_STAGE_COUNT = 11
+  TTT_STAGE_UNUSED_8 = 8, TTT_STAGE_SPLIT = 9, TTT_STAGE_MSE = 10, TTT_STAGE_RESIDENT = 11,
+  TTT_STAGE_COUNT = 12
 } ttt_stage;
 ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches);
 ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms);

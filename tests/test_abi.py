@@ -98,3 +98,33 @@ def test_status_strings():
         s = L.ttt_status_str(code)
         assert s and s != b"unknown status"
     assert L.ttt_status_str(99) == b"unknown status"
+
+
+def test_path_selection_checked():
+    small = dict(fw="gelu", loss="mse", ns_steps=0, renorm=False, dim=64, hidden=256, chunk=64)
+    one = (1, 1, 1, 1)
+    # the resident loop serves the small-chunk GELU layer with one bf16 plane
+    for kw in [small, dict(small, chunk=1), dict(small, chunk=48), dict(small, loss="dot")]:
+        assert _status(W.make_config(None, planes=one, path="resident", **_base(**kw))) == 0, kw
+    # and nothing else
+    for kw in [dict(small, chunk=65), dict(small, dim=128), dict(small, hidden=512),
+               dict(small, ns_steps=5, renorm=True), dict(small, renorm=True),
+               dict(small, act="f32"), dict(small, order="update_then_apply"),
+               dict(small, fw="swiglu")]:
+        assert _status(W.make_config(None, planes=one, path="resident", **_base(**kw))) == 5, kw
+    # two gradient planes (the bf16 default) keep the staged kernels
+    assert _status(W.make_config(None, planes=(1, 2, 2, 2), path="resident",
+                                 **_base(**small))) == 5
+    for path in ("auto", "staged"):
+        assert _status(W.make_config(None, planes=(1, 2, 2, 2), path=path,
+                                     **_base(**small))) == 0
+    c = _cfg()
+    c.path = 3
+    assert _status(c) == 4
+
+
+def _base(**kw):
+    base = dict(batch=2, heads=2, dim=64, hidden=128, chunk=64, fw="swiglu", loss="dot",
+                act="bf16", order="apply_then_update", ns_steps=5, renorm=True)
+    base.update(kw)
+    return base

@@ -35,12 +35,15 @@ def read_state(c, st):
     return [w.cpu().numpy().astype(np.float64) for w in W.split_state(c, flat)], flat
 
 
-def run_gpu(cfg, inp, planes=None, chunked=False):
-    """Whole sequence through libttt. Returns (O [B,H,T,d] fp32, [W per matrix [B,H,r,c]])."""
-    c = W.make_config(cfg, planes=planes)
+def run_gpu(cfg, inp, planes=None, chunked=False, path="auto", launches=None):
+    """Whole sequence through libttt. Returns (O [B,H,T,d] fp32, [W per matrix [B,H,r,c]]).
+    launches: optional stage name; its launch count is appended to `launches_out`."""
+    c = W.make_config(cfg, planes=planes, path=path)
     q, k, v, eta, w0 = device_inputs(cfg, inp)
     out = torch.empty_like(q)
     st = W.ttt_init_state(c, w0)
+    if launches is not None:
+        W.ttt_profile_begin(st, launches[0], 1 << 16)
     if chunked:
         b = cfg.chunk
         for ci in range(cfg.seq_len // b):
@@ -52,6 +55,8 @@ def run_gpu(cfg, inp, planes=None, chunked=False):
             out[:, :, sl] = oc
     else:
         W.ttt_sequence_forward(st, q, k, v, eta, out, cfg.seq_len)
+    if launches is not None:
+        launches.append(W.ttt_profile_end(st)[0])
     Ws, _ = read_state(c, st)
     W.ttt_state_health(st)
     O = out.float().cpu().numpy()

@@ -45,7 +45,7 @@ class TTTError(RuntimeError):
 class ttt_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order", "ns_steps",
-        "row_renorm", "apply_planes", "grad_planes", "ns_planes", "ns_lead_planes")]
+        "row_renorm", "apply_planes", "grad_planes", "ns_planes", "ns_lead_planes", "path")]
 
 
 _lib = None
@@ -89,10 +89,14 @@ def _check(st: int):
         raise TTTError(st, lib().ttt_last_error().decode())
 
 
+PATH = {"auto": 0, "staged": 1, "resident": 2}
+
+
 def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
     """ttt_config from an object with the workload fields (batch, heads, dim, hidden, chunk,
     fw, loss, act, order, ns_steps, renorm), overridden by keyword arguments. `planes` is
-    (apply, grad, ns, ns_lead); by default the preset of the workload's name, else 0s."""
+    (apply, grad, ns, ns_lead); by default the preset of the workload's name, else 0s.
+    `path` is "auto", "staged" or "resident"."""
     f = {}
     if cfg is not None:
         for k in ("batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order",
@@ -112,6 +116,8 @@ def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
     c.ns_steps = int(f.get("ns_steps", 0))
     c.row_renorm = int(bool(f.get("renorm", False)))
     c.apply_planes, c.grad_planes, c.ns_planes, c.ns_lead_planes = (int(p) for p in planes)
+    path = f.get("path", "auto")
+    c.path = PATH[path] if isinstance(path, str) else int(path)
     return c
 
 
@@ -190,7 +196,7 @@ def ttt_destroy_state(st: State) -> None:
 
 
 STAGES = {"front_q": 0, "front_k": 1, "out": 2, "contract": 3, "ns_gram": 4, "ns_poly": 5,
-          "ns_update": 6, "renorm": 7, "transpose": 8, "split": 9, "mse": 10}
+          "ns_update": 6, "renorm": 7, "split": 9, "mse": 10, "resident": 11}
 
 
 def ttt_profile_begin(st: State, stage, max_launches: int = 4096) -> None:

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libttt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ttt_kernels.hip", "libttt.cpp"]
+SOURCES = ["ttt_kernels.hip", "ttt_small.hip", "libttt.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in device code

@@ -83,6 +83,18 @@ ttt_status resolve(const ttt_config* c, ttt_config* out) {
     if (*pl[i] < 1 || *pl[i] > 3)
       return fail(TTT_E_CONFIG, "%s must be 0 (default) or 1..3 (got %d)", nm[i], *pl[i]);
   }
+  if (r.path < TTT_PATH_AUTO || r.path > TTT_PATH_RESIDENT)
+    return fail(TTT_E_CONFIG, "unknown path %d", r.path);
+  const bool resident_ok =
+      small_supported(r.fw == TTT_FW_MLP_GELU ? FW_GELU : -1, r.ns_steps, r.row_renorm,
+                      r.act == TTT_BF16, r.order == TTT_APPLY_THEN_UPDATE, r.dim, r.hidden,
+                      r.chunk, r.apply_planes, r.grad_planes);
+  if (r.path == TTT_PATH_RESIDENT && !resident_ok)
+    return fail(TTT_E_UNSUPPORTED,
+                "the resident path needs the GELU MLP with dim 64, hidden 256, chunk <= 64, "
+                "no Newton-Schulz, no renorm, bf16 activations, apply-then-update and one "
+                "bf16 plane");
+  if (r.path == TTT_PATH_AUTO) r.path = resident_ok ? TTT_PATH_RESIDENT : TTT_PATH_STAGED;
   if (out) *out = r;
   return TTT_OK;
 }
@@ -154,6 +166,7 @@ struct ttt_state {
   float* afp = nullptr;
   int* health = nullptr;
   int contract_tiles = 0;
+  bool resident = false;  // the device-resident chunk loop serves this state (Wpl unused)
   // measurement hooks
   int prof_stage = -1, prof_cap = 0, prof_n = 0;
   hipEvent_t* prof_ev = nullptr;
@@ -569,6 +582,25 @@ ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, co
     return r;
   hipStream_t st = static_cast<hipStream_t>(stream);
   s->last = st;
+  if (s->resident) {
+    // every chunk of the call in one launch; W is updated in place
+    const Dims& D = s->D;
+    SmallArgs a{};
+    a.q = static_cast<const u16*>(q);
+    a.k = static_cast<const u16*>(k);
+    a.v = static_cast<const u16*>(v);
+    a.eta = eta;
+    a.out = static_cast<u16*>(out);
+    a.W1 = s->Wm[0];
+    a.W2 = s->Wm[1];
+    a.health = s->health;
+    a.T = T;
+    a.chunk = s->cfg.chunk;
+    a.nchunks = (int)nchunks;
+    a.P = D.P;
+    STAGED(TTT_STAGE_RESIDENT, launch_small(a, s->cfg.loss == TTT_LOSS_MSE, st));
+    return TTT_OK;
+  }
   Rows R{};
   R.q = static_cast<const char*>(q);
   R.k = static_cast<const char*>(k);
@@ -611,6 +643,7 @@ ttt_status ttt_init_state(const ttt_config* cfg, const float* w0, void* stream,
   if (!s) return fail(TTT_E_ALLOC, "host allocation failed");
   s->cfg = r;
   s->D = dims_of(r);
+  s->resident = r.path == TTT_PATH_RESIDENT;
   s->arena_bytes = layout(s, nullptr);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   s->last = hs;

@@ -118,6 +118,18 @@ struct SplitArgs {
   PlaneBuf out;    // [np][Z][rows][d]
 };
 
+// Device-resident chunk loop (GELU MLP, dim 64, hidden 256, chunk <= 64, plain gradient
+// step, bf16 activations): one workgroup per problem runs every chunk of the call.
+struct SmallArgs {
+  const u16 *q, *k, *v;  // [P][T][64] bf16
+  const float* eta;      // [P][T]
+  u16* out;              // [P][T][64] bf16
+  float *W1, *W2;        // state: W1 [P][256][64], W2 [P][64][256], fp32, updated in place
+  int* health;           // set to 1 if the final state holds a non-finite value
+  int64_t T;             // tokens per problem in the caller's tensors
+  int chunk, nchunks, P;
+};
+
 // ---------------------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  `lds_limit` handling and tile choice are
 // internal.  `Z` is the number of (batch, head) problems.
@@ -129,6 +141,9 @@ hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s);
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s);
 hipError_t launch_split(const SplitArgs& a, int Z, hipStream_t s);
+hipError_t launch_small(const SmallArgs& a, int loss, hipStream_t s);
+bool small_supported(int fw, int ns_steps, int renorm, int act_bf16, int apply_first, int dim,
+                     int hidden, int chunk, int ap, int gp);
 hipError_t prepare_kernels();  // raise dynamic-LDS limits once per process
 
 // tile sizes used by the contraction and Newton-Schulz stages (the host sizes buffers)
