@@ -28,14 +28,18 @@ constexpr int NT = 256;
 constexpr int OFF_QE = 0;                            // Q, then O staging, then -E  [64][S64]
 constexpr int OFF_K = OFF_QE + BT * S64 * 2;         // K                           [64][S64]
 constexpr int OFF_V = OFF_K + BT * S64 * 2;          // V                           [64][S64]
-constexpr int OFF_H = OFF_V + BT * S64 * 2;          // H (queries, keys), then -dZ [64][S256]
-constexpr int OFF_W1 = OFF_H + BT * S256 * 2;        // W1 bf16                     [256][S64]
-constexpr int OFF_W2 = OFF_W1 + DH * S64 * 2;        // W2 bf16                     [64][S256]
-constexpr int OFF_ETA = OFF_W2 + D * S256 * 2;       // eta                         [64] fp32
+// The hidden-by-token and weight buffers are stored transposed (H^T, W1^T, W2^T) so that
+// the four accumulator rows a lane holds side by side land in one 8-byte LDS store.
+constexpr int OFF_HT = OFF_V + BT * S64 * 2;         // H^T (queries, keys), -dZ^T  [256][S64]
+constexpr int OFF_W1T = OFF_HT + DH * S64 * 2;       // W1^T bf16                   [64][S256]
+constexpr int OFF_W2T = OFF_W1T + D * S256 * 2;      // W2^T bf16                   [256][S64]
+constexpr int OFF_ETA = OFF_W2T + DH * S64 * 2;      // eta                         [64] fp32
 constexpr int LDS = OFF_ETA + BT * 4;
 
 typedef __attribute__((address_space(3))) char lds_t;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Every LDS access is lds + (a per-thread byte offset) + (a compile-time constant), so the
 // constant lands in the instruction's offset field.
@@ -44,14 +48,33 @@ __device__ __forceinline__ __attribute__((address_space(3))) T& at(lds_t* lds, u
   return *reinterpret_cast<__attribute__((address_space(3))) T*>(lds + off);
 }
 
-// GELU with the exact (erf) normal CDF, and its derivative Phi(z) + z phi(z).
+// GELU z Phi(z) with the normal CDF Phi, and its derivative Phi(z) + z phi(z).  Phi comes
+// from Abramowitz & Stegun's rational approximation 7.1.26 of erf (absolute error at most
+// 1.5e-7, far below the bf16 rounding these values then take): with x = |z| / sqrt(2),
+// t = 1 / (1 + 0.3275911 x) and e = exp(-x^2) = exp(-z^2 / 2),
+//   Phi(-|z|) = erfc(x) / 2 = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e / 2,
+// one reciprocal and one exponential, no branches; e also gives phi(z) = e / sqrt(2 pi).
+__device__ __forceinline__ float std_normal_tail(float z, float& e) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
+                       -0.284496736f),
+               0.254829592f);
+  e = __expf(-x * x);
+  return 0.5f * poly * e;
+}
 __device__ __forceinline__ float gelu(float z) {
-  return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+  float e;
+  const float h = std_normal_tail(z, e);
+  return z * (z >= 0.f ? 1.f - h : h);
 }
 __device__ __forceinline__ void gelu_and_d(float z, float& g, float& gd) {
-  const float cdf = 0.5f * (1.f + erff(z * 0.70710678118654752f));
+  float e;
+  const float h = std_normal_tail(z, e);
+  const float cdf = z >= 0.f ? 1.f - h : h;
   g = z * cdf;
-  gd = cdf + z * __expf(-0.5f * z * z) * 0.39894228040143268f;
+  gd = fmaf(z * e, 0.39894228040143268f, cdf);
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -81,6 +104,16 @@ __device__ __forceinline__ uint32_t acc_off(int S) {
   return (4 * (l >> 5) * S + (l & 31)) * 2;
 }
 constexpr uint32_t acc_const(int S, int v) { return (8 * (v >> 2) + (v & 3)) * S * 2; }
+// The same tile written transposed ((r, c) at c S + r): elements v = 4q .. 4q + 3 are
+// consecutive and go out as one 8-byte store at per-thread part + 8 q * 2.
+__device__ __forceinline__ uint32_t acc_t_off(int S) {
+  const int l = threadIdx.x & 63;
+  return ((l & 31) * S + 4 * (l >> 5)) * 2;
+}
+__device__ __forceinline__ bf16x4 pack4(const f32x16& x, int q) {
+  return __builtin_convertvector(
+      (f32x4){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]}, bf16x4);
+}
 
 template <int S>
 __device__ __forceinline__ bf16x8 frag_row(lds_t* lds, uint32_t off, int r0, int k0) {
@@ -127,14 +160,15 @@ __device__ __forceinline__ void mma_2x2(f32x16 (&acc)[2][2], lds_t* lds, uint32_
   }
 }
 
-// One 32 x 32 tile of H W2^T over K = 256 (both operands row layout, stride S256).
+// One 32 x 32 tile of H W2^T over K = 256, both operands read from transposed buffers
+// (H^T, W2^T: column layout, stride S64).
 __device__ __forceinline__ f32x16 mma_k256(lds_t* lds, uint32_t h_off, uint32_t w_off) {
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
   for (int k0 = 0; k0 < 256; k0 += 16)
-    acc = mfma(frag_row<S256>(lds, h_off, 0, k0), frag_row<S256>(lds, w_off, 0, k0), acc);
+    acc = mfma(frag_col<S64>(lds, h_off, 0, k0), frag_col<S64>(lds, w_off, 0, k0), acc);
   return acc;
 }
 
@@ -198,41 +232,42 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
       }
 
   // per-thread offset parts; re-laundered at the top of every chunk
-  uint32_t fr64, fr256, fc64, fc256, ac64, ac256, ld64;
+  uint32_t fr64, fc64, fc256, ac64, at64, at256, ld64;
   auto bind = [&]() __attribute__((always_inline)) {
     fr64 = opaque(frag_row_off(S64));
-    fr256 = opaque(frag_row_off(S256));
     fc64 = opaque(frag_col_off(S64));
     fc256 = opaque(frag_col_off(S256));
     ac64 = opaque(acc_off(S64));
-    ac256 = opaque(acc_off(S256));
+    at64 = opaque(acc_t_off(S64));
+    at256 = opaque(acc_t_off(S256));
     ld64 = opaque((lr * S64 + lc) * 2);
   };
 
-  // bf16 copies of the state for the GEMM operands
+  // bf16 copies of the state for the GEMM operands: w1 rows (hidden) become W1^T columns,
+  // w2 rows (dim) become W2^T columns
   auto publish_w = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          at<u16>(lds, OFF_W1 + ac64 + w_rows64 + acc_const(S64, v) + (32 * i * S64 + 32 * j) * 2) =
-              f2bf(w1[i][j][v]);
-          at<u16>(lds, OFF_W2 + ac256 + w_cols + acc_const(S256, v) + (32 * i * S256 + 32 * j) * 2) =
-              f2bf(w2[i][j][v]);
+        for (int q = 0; q < 4; ++q) {
+          at<bf16x4>(lds, OFF_W1T + at256 + w_cols + (32 * j * S256 + 32 * i + 8 * q) * 2) =
+              pack4(w1[i][j], q);
+          at<bf16x4>(lds, OFF_W2T + at64 + w_rows64 + (32 * j * S64 + 32 * i + 8 * q) * 2) =
+              pack4(w2[i][j], q);
         }
   };
-  // a 64 x 256 block (rows: tokens; this wave's columns [64w, +64)) into the H buffer
+  // a 64 x 256 block (rows: tokens; this wave's columns [64w, +64) of hidden) into H^T
   auto put_h = [&](const f32x16 (&x)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          at<u16>(lds, OFF_H + ac256 + w_cols + acc_const(S256, v) + (32 * i * S256 + 32 * j) * 2) =
-              f2bf(x[i][j][v]);
+        for (int q = 0; q < 4; ++q)
+          at<bf16x4>(lds, OFF_HT + at64 + w_rows64 + (32 * j * S64 + 32 * i + 8 * q) * 2) =
+              pack4(x[i][j], q);
   };
   auto load_chunk = [&](int c, ChunkRegs& R) __attribute__((always_inline)) {
     const int64_t base = (int64_t)p * a.T + (int64_t)c * b;
@@ -270,9 +305,9 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
     bind();
     if (c + 1 < a.nchunks) load_chunk(c + 1, nxt);   // in flight during this chunk
 
-    // 1. apply: gelu(Q W1^T) -> H
+    // 1. apply: gelu(Q W1^T) -> H^T
     zero(acc);
-    mma_2x2<false, S64, false, S64, 64>(acc, lds, OFF_QE + fr64, OFF_W1 + fr64 + w_rows64);
+    mma_2x2<false, S64, true, S256, 64>(acc, lds, OFF_QE + fr64, OFF_W1T + fc256 + w_cols);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -284,7 +319,7 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
     __syncthreads();
     // 2. O = H W2^T, staged through the Q buffer, then 16-byte stores
     {
-      const f32x16 o = mma_k256(lds, OFF_H + fr256 + wr * S256 * 2, OFF_W2 + fr256 + wc * S256 * 2);
+      const f32x16 o = mma_k256(lds, OFF_HT + fc64 + wr * 2, OFF_W2T + fc64 + wc * 2);
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         at<u16>(lds, OFF_QE + ac64 + (wr * S64 + wc) * 2 + acc_const(S64, v)) = f2bf(o[v]);
@@ -300,9 +335,9 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
               at<u32x4>(lds, OFF_QE + ld64 + h * 32 * S64 * 2);
       }
     }
-    // 3. keys: Z = K W1^T; gelu(Z) -> H, gelu'(Z) stays in registers
+    // 3. keys: Z = K W1^T; gelu(Z) -> H^T, gelu'(Z) stays in registers
     zero(acc);
-    mma_2x2<false, S64, false, S64, 64>(acc, lds, OFF_K + fr64, OFF_W1 + fr64 + w_rows64);
+    mma_2x2<false, S64, true, S256, 64>(acc, lds, OFF_K + fr64, OFF_W1T + fc256 + w_cols);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -320,7 +355,7 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
     // 4. negated output error -> Q buffer.  MSE: -2 eta (gelu(Z) W2^T - V).  Inner
     //    product: the error of -eta <f, v> is -eta v, negated +eta v.
     if constexpr (LOSS == 1) {
-      const f32x16 o = mma_k256(lds, OFF_H + fr256 + wr * S256 * 2, OFF_W2 + fr256 + wc * S256 * 2);
+      const f32x16 o = mma_k256(lds, OFF_HT + fc64 + wr * 2, OFF_W2T + fc64 + wc * 2);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const uint32_t e_off = OFF_QE + ac64 + (wr * S64 + wc) * 2 + acc_const(S64, v);
@@ -340,10 +375,10 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
     }
     __syncthreads();
     // 5. W2 <- W2 - E^T gelu(Z)
-    mma_2x2<true, S64, true, S256, 64>(w2, lds, OFF_QE + fc64, OFF_H + fc256 + w_cols);
-    // 6. -dH = (-E) W2 with the pre-update bf16 W2; -dZ = -dH gelu'(Z) -> H
+    mma_2x2<true, S64, false, S64, 64>(w2, lds, OFF_QE + fc64, OFF_HT + fr64 + w_rows64);
+    // 6. -dH = (-E) W2 with the pre-update bf16 W2; -dZ = -dH gelu'(Z) -> H^T
     zero(acc);
-    mma_2x2<false, S64, true, S256, 64>(acc, lds, OFF_QE + fr64, OFF_W2 + fc256 + w_cols);
+    mma_2x2<false, S64, false, S64, 64>(acc, lds, OFF_QE + fr64, OFF_W2T + fr64 + w_rows64);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -352,7 +387,7 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
     put_h(acc);
     __syncthreads();
     // 7. W1 <- W1 - dZ^T K
-    mma_2x2<true, S256, true, S64, 64>(w1, lds, OFF_H + fc256 + w_cols, OFF_K + fc64);
+    mma_2x2<false, S64, true, S64, 64>(w1, lds, OFF_HT + fr64 + w_rows64, OFF_K + fc64);
     __syncthreads();                                   // every read of W, K, V, E done
     publish_w();
     if (c + 1 < a.nchunks) stage_chunk(nxt);
