@@ -98,9 +98,9 @@ struct PlaneBuf {
 // the inner loop has no plane-dependent control flow.
 //
 // Block: WGM x WGN waves, wave tile (BM/WGM) x (BN/WGN) of 32x32x16 MFMA tiles.  K steps of
-// 64 through two LDS stages (register prefetch of the next step).  Global loads are buffer
-// loads: elements outside the operand read as zero.  16-byte LDS chunks are XOR-swizzled
-// by row so that fragment reads spread over the banks.
+// 64 through two LDS stages, filled by direct global-to-LDS buffer loads one step ahead.
+// Elements outside an operand read as zero (out-of-range buffer loads return 0).  16-byte
+// LDS chunks are XOR-swizzled by row so that fragment reads spread over the banks.
 enum Layout { L_ROW = 0, L_COL = 1 };
 
 __device__ __forceinline__ int swz_row(int r) { return (r >> 1) & 7; }
@@ -121,23 +121,23 @@ struct TileLoad {
   static_assert(R % 64 == 0, "tile rows must be a multiple of 64");
   uint32_t off[C];   // byte offset of the chunk at k0 = 0, or an out-of-range value
   int kk[C];         // k of the chunk's first element relative to k0
-  int lds[C];        // LDS byte offset inside the tile
   uint32_t kstride;  // bytes per unit of k0
 
+  // Chunks go to LDS by direct (DMA) loads, which write lane l of a wave's load to 16 l
+  // bytes past the wave's base: thread t of round c fills LDS chunk p = c NT + t, so it
+  // loads the global chunk that the swizzled layout keeps at p (XOR is its own inverse).
   __device__ __forceinline__ void init(const Operand& o, int row0, bool col) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int ch = threadIdx.x + c * NT;
       if (!col) {
-        const int r = ch >> 3, kc = ch & 7;
+        const int r = ch >> 3, kc = (ch & 7) ^ swz_row(r);
         kk[c] = kc * 8;
-        lds[c] = r * 128 + ((kc ^ swz_row(r)) << 4);
         off[c] = (row0 + r < o.rows) ? (uint32_t)(((int64_t)(row0 + r) * o.ld + kc * 8) * 2)
                                      : 0xC0000000u;
       } else {
-        const int k = ch / (R / 8), mc = ch % (R / 8);
+        const int k = ch / (R / 8), mc = (ch % (R / 8)) ^ swz_col<R>(k);
         kk[c] = k;
-        lds[c] = k * R * 2 + ((mc ^ swz_col<R>(k)) << 4);
         off[c] = (row0 + mc * 8 < o.rows) ? (uint32_t)(((int64_t)k * o.ld + row0 + mc * 8) * 2)
                                           : 0xC0000000u;
       }
@@ -194,7 +194,10 @@ struct Gemm {
   static constexpr bool bcol(int i) { return (LBM >> i) & 1; }
   static constexpr int A_TILE = TA::BYTES, B_TILE = TB::BYTES;
   static constexpr int STAGE = NA * A_TILE + NB * B_TILE;
-  static constexpr int LDS_BYTES = 2 * STAGE > STORE_LDS ? 2 * STAGE : STORE_LDS;
+  // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffer 1, declared as
+  // two separate __shared__ arrays by the kernel (GEMM_LDS)
+  static constexpr int S0_BYTES = STAGE > STORE_LDS ? STAGE : STORE_LDS;
+  static constexpr int LDS_BYTES = S0_BYTES + STAGE;
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
 
   f32x16 acc[NB][TM][TN];
@@ -215,9 +218,15 @@ struct Gemm {
   }
 
   // A / B point at NA / NB consecutive operands (normally inside the kernel arguments).
+  // st0 / st1: the two stage buffers, distinct __shared__ arrays.  Each K step's tiles
+  // are loaded straight into LDS (buffer loads with the LDS flag) one step ahead: step t
+  // computes from one buffer while step t + 1 lands in the other.  The loop is unrolled
+  // by two so that every LDS access names a fixed buffer, which lets the compiler see
+  // that the fragment reads never touch the buffer being filled and wait for the loads
+  // only at the end of each step.
   __device__ __forceinline__ void run(const Operand* __restrict__ A,
                                       const Operand* __restrict__ B, int m0, int n0, int z,
-                                      int K, char* smem) {
+                                      int K, char* st0, char* st1) {
     const int wave = threadIdx.x >> 6;
     const int wm0 = (wave / WGN) * WM;
     const int wn0 = (wave % WGN) * WN;
@@ -257,8 +266,9 @@ struct Gemm {
       nb_[i] = (int)(!bcol(i) ? (int64_t)B[i].rows * B[i].ld * 2 : (int64_t)K * B[i].ld * 2);
     }
 
-    uint4 ra[NA][TA::C], rb[NB][TB::C];
-    auto gload = [&](int t) __attribute__((always_inline)) {
+    // this wave's 1 KB slice of round c of a tile
+    const int wslice = wave * 64 * 16;
+    auto issue = [&](int t, char* st) __attribute__((always_inline)) {
       const int sg = t / nk, k0 = (t - sg * nk) * BK;
       const int qa = (segs >> (4 * sg)) & 3, qb = (segs >> (4 * sg + 2)) & 3;
 #pragma unroll
@@ -269,7 +279,9 @@ struct Gemm {
 #pragma unroll
         for (int c = 0; c < TA::C; ++c) {
           const uint32_t off = (k0 + la[i].kk[c] < K) ? la[i].off[c] + kb : 0xFFFFFFF0u;
-          ra[i][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(st + i * A_TILE + c * NT * 16 + wslice),
+              16, off, 0, 0, 0);
         }
       }
 #pragma unroll
@@ -280,21 +292,13 @@ struct Gemm {
 #pragma unroll
         for (int c = 0; c < TB::C; ++c) {
           const uint32_t off = (k0 + lb[i].kk[c] < K) ? lb[i].off[c] + kb : 0xFFFFFFF0u;
-          rb[i][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs,
+              (__attribute__((address_space(3))) void*)(st + NA * A_TILE + i * B_TILE +
+                                                        c * NT * 16 + wslice),
+              16, off, 0, 0, 0);
         }
       }
-    };
-    auto sstore = [&](char* st) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < NA; ++i)
-#pragma unroll
-        for (int c = 0; c < TA::C; ++c)
-          *reinterpret_cast<uint4*>(st + i * A_TILE + la[i].lds[c]) = ra[i][c];
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int c = 0; c < TB::C; ++c)
-          *reinterpret_cast<uint4*>(st + NA * A_TILE + i * B_TILE + lb[i].lds[c]) = rb[i][c];
     };
     auto compute = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
@@ -323,17 +327,21 @@ struct Gemm {
                                                                        acc[p][tm][tn], 0, 0, 0);
       }
     };
-
-    gload(0);
-    sstore(smem);
-    __syncthreads();
-    for (int t = 0; t < total; ++t) {
-      char* cur = smem + (t & 1) * STAGE;
-      char* nxt = smem + ((t + 1) & 1) * STAGE;
-      if (t + 1 < total) gload(t + 1);
-      compute(cur);
-      if (t + 1 < total) sstore(nxt);
+    // end of a step: this thread's loads have landed and its LDS reads are done (wait for
+    // every counter), then the whole block meets
+    auto step_end = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+    };
+
+    issue(0, st0);
+    step_end();
+    for (int t = 0; t < total; ++t) {
+      char* cur = (t & 1) ? st1 : st0;
+      char* nxt = (t & 1) ? st0 : st1;
+      if (t + 1 < total) issue(t + 1, nxt);
+      compute(cur);
+      step_end();
     }
   }
 
@@ -358,6 +366,14 @@ struct Gemm {
         }
   }
 };
+
+// The two stage buffers of a Gemm type G as distinct __shared__ arrays (distinct objects
+// are what lets the compiler keep fragment reads of one buffer clear of the loads in
+// flight into the other); `smem`, the first, is also the epilogue's staging area.
+#define GEMM_LDS(G)                                                              \
+  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::S0_BYTES];         \
+  __shared__ __attribute__((aligned(1024))) char gemm_st1_[G::STAGE];            \
+  char* const smem = gemm_st0_
 
 // ------------------------------------------------------------------------ block order
 // Workgroups of a launch are handed to the 8 XCDs round-robin by linear id, and each XCD

@@ -52,11 +52,11 @@ struct FrontShape {
 
 template <int BM, int BN, int WGM, int WGN, int FW, int MODE>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   using FS = FrontShape<FW, MODE>;
   constexpr int NA = FS::NA, NB = FS::NB;
   // the inner-product loss reads W2 [dim][hidden] column-wise for V W2
   using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0>;
+  GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int z = lid / a.tiles, tile = lid % a.tiles;
   const int m0 = (tile / a.tiles_n) * BM;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
 
   G g;
   g.zero();
-  g.run(a.A, a.B, m0, n0, z, a.K, smem);
+  g.run(a.A, a.B, m0, n0, z, a.K, gemm_st0_, gemm_st1_);
 
   const float* eta = a.eta + (int64_t)z * a.eta_zstride;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
@@ -126,16 +126,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
 // ------------------------------------------------------------------------ out / dH
 template <int BM, int BN, int WGM, int WGN, int MODE>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   // dH = E W2 reads W2 [dim][hidden] column-wise
   using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
+  GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int z = lid / a.tiles, tile = lid % a.tiles;
   const int m0 = (tile / a.tiles_n) * BM;
   const int n0 = (tile % a.tiles_n) * BN;
   G g;
   g.zero();
-  g.run(&a.a, &a.b, m0, n0, z, a.K, smem);
+  g.run(&a.a, &a.b, m0, n0, z, a.K, gemm_st0_, gemm_st1_);
 
   const int cl = min(BN, a.N - n0);
   const int rn = min(BM, a.nrows - m0);
@@ -200,8 +200,8 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 // ------------------------------------------------------------------------ contraction
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1>;   // both operands token-major
+  GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int m = zz / a.P, p = zz % a.P;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   const int n0 = (tile % a.tiles_n) * BN;
   G g;
   g.zero();
-  g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, smem);
+  g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, gemm_st0_, gemm_st1_);
 
   const int M = a.M, N = a.N;
   const int64_t base = (int64_t)zz * M * N;
@@ -274,8 +274,8 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 // the polynomial stage reads); A planes written for the full symmetric matrix.
 template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<T, T, WG, WG, 1, 1>;
+  GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
   const int M = a.M;
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
   const Operand X = operand_of(a.xin, a.xin.np, M);
   G g;
   g.zero();
-  g.run(&X, &X, m0, n0, zz, a.N, smem);
+  g.run(&X, &X, m0, n0, zz, a.N, gemm_st0_, gemm_st1_);
   float s2 = 1.f;
   if (a.first) {
     const float s = ns_scale(a, zz);
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
 // a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
 template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<T, T, WG, WG, 1, 1>;
+  GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
   const int M = a.M;
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
   const Operand Ao = operand_of(a.ain, a.ain.np, M);
   G g;
   g.zero();
-  g.run(&Ao, &Ao, m0, n0, zz, M, smem);
+  g.run(&Ao, &Ao, m0, n0, zz, M, gemm_st0_, gemm_st1_);
   const int64_t base = (int64_t)zz * M * M;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
@@ -332,8 +332,8 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
 template <int T, int WG>
 __global__ __launch_bounds__(WG * WG * 64) void k_ns_update(NsArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   using G = Gemm<T, T, WG, WG, 1, 1, 0, 1>;   // X [M][N] read column-wise
+  GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int M = a.M, N = a.N;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_update(NsArgs a) {
   const Operand Bo = operand_of(a.xin, a.xin.np, N);   // X [M][N] read as its columns
   G g;
   g.zero();
-  g.run(&Ao, &Bo, m0, n0, zz, M, smem);
+  g.run(&Ao, &Bo, m0, n0, zz, M, gemm_st0_, gemm_st1_);
   const float sc = a.first ? ns_scale(a, zz) : 1.f;
   const int64_t base = (int64_t)zz * M * N;
   const int m = zz / a.P;
@@ -416,14 +416,9 @@ __global__ __launch_bounds__(256) void k_split(SplitArgs a) {
 }
 
 // ============================================================================ launchers
+// Every GEMM kernel holds its LDS in static __shared__ arrays (GEMM_LDS): launches pass no
+// dynamic LDS.
 static constexpr int LDS_MAX = 160 * 1024;
-
-template <class K>
-static hipError_t set_lds(K kernel, int bytes) {
-  if (bytes <= 64 * 1024) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
 
 template <int BM, int BN, int WGM, int WGN, int FW, int MODE>
 static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
@@ -431,13 +426,11 @@ static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
   using G = Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB, 0, FS::DOT ? (1 << (FS::NB - 1)) : 0>;
   FrontArgs a = a0;
   auto kern = k_front<BM, BN, WGM, WGN, FW, MODE>;
-  hipError_t e = set_lds(kern, G::LDS_BYTES);
-  if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
   if (a.tiles == 0 || Z == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), G::LDS_BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -463,13 +456,11 @@ static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
   using G = Gemm<BM, BN, 2, 2, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
   OutArgs a = a0;
   auto kern = k_out<BM, BN, 2, 2, MODE>;
-  hipError_t e = set_lds(kern, G::LDS_BYTES);
-  if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
   if (a.tiles == 0 || Z == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), G::LDS_BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -484,12 +475,10 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   using G = Gemm<BM, BN, 2, 2, 1, 1, 1, 1>;
   ContractArgs a = a0;
   auto kern = k_contract<BM, BN, 2, 2>;
-  hipError_t e = set_lds(kern, G::LDS_BYTES);
-  if (e != hipSuccess) return e;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   if (a.tiles == 0 || a.P == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(a.tiles * nm * a.P), dim3(G::NT), G::LDS_BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.tiles * nm * a.P), dim3(G::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -508,24 +497,20 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
   using G = Gemm<T, T, WG, WG, 1, 1>;
   NsArgs a = a0;
   if (a.Z == 0) return hipSuccess;
-  hipError_t e;
   if (STAGE == 2) {
     using GU = Gemm<T, T, WG, WG, 1, 1, 0, 1>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
     auto kern = k_ns_update<T, WG>;
-    if ((e = set_lds(kern, GU::LDS_BYTES)) != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(GU::NT), GU::LDS_BYTES, s, a);
+    hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(GU::NT), 0, s, a);
   } else {
     a.tiles = ns_tri_tiles(a.M, T);
     if (STAGE == 0) {
       auto kern = k_ns_gram<T, WG>;
-      if ((e = set_lds(kern, G::LDS_BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
+        hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
     } else {
       auto kern = k_ns_poly<T, WG>;
-      if ((e = set_lds(kern, G::LDS_BYTES)) != hipSuccess) return e;
-      hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), G::LDS_BYTES, s, a);
+        hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
     }
   }
   return hipGetLastError();
