@@ -109,6 +109,12 @@ template <int R>
 __device__ __forceinline__ int swz_col(int k) { return R >= 128 ? (k & 3) << 2 : (k & 2); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte-per-lane direct load from a buffer into LDS (lane l writes dst + 16 l).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+}
 
 // Per-thread load plan of one operand tile (R rows x 64 k) in either layout.
 template <int R, int NT>
@@ -266,37 +272,56 @@ struct Gemm {
       nb_[i] = (int)(!bcol(i) ? (int64_t)B[i].rows * B[i].ld * 2 : (int64_t)K * B[i].ld * 2);
     }
 
-    // this wave's 1 KB slice of round c of a tile
-    const int wslice = wave * 64 * 16;
+    // this wave's 1 KB slice of round c of a tile (wave-uniform, kept in a scalar register
+    // so that the LDS destination is formed with scalar arithmetic)
+    const int wslice = __builtin_amdgcn_readfirstlane(wave) * 64 * 16;
+    // Steps that lie wholly inside K move the buffer's base by the step's k offset (scalar
+    // arithmetic only, no per-lane work); a partial last step checks each chunk against K.
     auto issue = [&](int t, char* st) __attribute__((always_inline)) {
       const int sg = t / nk, k0 = (t - sg * nk) * BK;
       const int qa = (segs >> (4 * sg)) & 3, qb = (segs >> (4 * sg + 2)) & 3;
+      if (k0 + BK <= K) {
 #pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(pa_[i] + qa * A[i].pstride), (short)0, na_[i], 0x00020000);
-        const uint32_t kb = (uint32_t)k0 * la[i].kstride;
+        for (int i = 0; i < NA; ++i) {
+          const uint32_t kb = (uint32_t)k0 * la[i].kstride;
+          const char* base = reinterpret_cast<const char*>(pa_[i] + qa * A[i].pstride) + kb;
+          const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)base, (short)0, na_[i] - (int)kb, 0x00020000);
 #pragma unroll
-        for (int c = 0; c < TA::C; ++c) {
-          const uint32_t off = (k0 + la[i].kk[c] < K) ? la[i].off[c] + kb : 0xFFFFFFF0u;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (__attribute__((address_space(3))) void*)(st + i * A_TILE + c * NT * 16 + wslice),
-              16, off, 0, 0, 0);
+          for (int c = 0; c < TA::C; ++c)
+            dma16(rk, (lds_void_t*)(st + i * A_TILE + c * NT * 16 + wslice), la[i].off[c]);
         }
-      }
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(pb_[i] + qb * B[i].pstride), (short)0, nb_[i], 0x00020000);
-        const uint32_t kb = (uint32_t)k0 * lb[i].kstride;
+        for (int i = 0; i < NB; ++i) {
+          const uint32_t kb = (uint32_t)k0 * lb[i].kstride;
+          const char* base = reinterpret_cast<const char*>(pb_[i] + qb * B[i].pstride) + kb;
+          const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)base, (short)0, nb_[i] - (int)kb, 0x00020000);
 #pragma unroll
-        for (int c = 0; c < TB::C; ++c) {
-          const uint32_t off = (k0 + lb[i].kk[c] < K) ? lb[i].off[c] + kb : 0xFFFFFFF0u;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs,
-              (__attribute__((address_space(3))) void*)(st + NA * A_TILE + i * B_TILE +
-                                                        c * NT * 16 + wslice),
-              16, off, 0, 0, 0);
+          for (int c = 0; c < TB::C; ++c)
+            dma16(rk, (lds_void_t*)(st + NA * A_TILE + i * B_TILE + c * NT * 16 + wslice),
+                  lb[i].off[c]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          const uint32_t kb = (uint32_t)k0 * la[i].kstride;
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(pa_[i] + qa * A[i].pstride), (short)0, na_[i], 0x00020000);
+#pragma unroll
+          for (int c = 0; c < TA::C; ++c)
+            dma16(rs, (lds_void_t*)(st + i * A_TILE + c * NT * 16 + wslice),
+                  (k0 + la[i].kk[c] < K) ? la[i].off[c] + kb : 0xFFFFFFF0u);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const uint32_t kb = (uint32_t)k0 * lb[i].kstride;
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(pb_[i] + qb * B[i].pstride), (short)0, nb_[i], 0x00020000);
+#pragma unroll
+          for (int c = 0; c < TB::C; ++c)
+            dma16(rs, (lds_void_t*)(st + NA * A_TILE + i * B_TILE + c * NT * 16 + wslice),
+                  (k0 + lb[i].kk[c] < K) ? lb[i].off[c] + kb : 0xFFFFFFF0u);
         }
       }
     };

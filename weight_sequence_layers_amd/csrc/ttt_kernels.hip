@@ -516,8 +516,8 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_t<128, 0>(a, s); }
-hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_t<128, 1>(a, s); }
+hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_t<64, 0>(a, s); }
+hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_t<64, 1>(a, s); }
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) { return ns_t<128, 2>(a, s); }
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
