@@ -70,17 +70,6 @@ def total_flops(cfg) -> float:
     return P * (cfg.seq_len * per_tok + cfg.n_chunks * ns)
 
 
-def source_digest() -> str:
-    """Hash of the kernel sources; counter summaries record the digest they were taken at."""
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "weight_sequence_layers_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def recorded_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from profiles/<workload>_traffic.md, if that summary
     was taken from the current kernel sources; else None."""
@@ -93,6 +82,7 @@ def recorded_traffic(workload: str, stage: str):
             digest = line.split(":", 1)[1].strip()
         if line.startswith(f"| {stage} |"):
             val = float(line.split("|")[-2])
+    from weight_sequence_layers_amd.profiling import source_digest
     return val if digest == source_digest() else None
 
 
@@ -143,6 +133,7 @@ def main():
 
     import ttt_inputs as ti
     import weight_sequence_layers_amd as W
+    from weight_sequence_layers_amd.profiling import source_digest
 
     cfg = ti.CONFIGS[args.workload]
     planes = tuple(int(x) for x in args.planes.split(",")) if args.planes else W.PRECISION[cfg.name]

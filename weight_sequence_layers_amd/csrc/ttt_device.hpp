@@ -277,8 +277,15 @@ struct Gemm {
     const int wslice = __builtin_amdgcn_readfirstlane(wave) * 64 * 16;
     // Steps that lie wholly inside K move the buffer's base by the step's k offset (scalar
     // arithmetic only, no per-lane work); a partial last step checks each chunk against K.
-    auto issue = [&](int t, char* st) __attribute__((always_inline)) {
-      const int sg = t / nk, k0 = (t - sg * nk) * BK;
+    // The steps are loaded in order; (sg_n, k0_n) is the next one's segment and k offset.
+    int sg_n = 0, k0_n = 0;
+    auto issue = [&](char* st) __attribute__((always_inline)) {
+      const int sg = sg_n, k0 = k0_n;
+      k0_n += BK;
+      if (k0_n >= K) {
+        k0_n = 0;
+        ++sg_n;
+      }
       const int qa = (segs >> (4 * sg)) & 3, qb = (segs >> (4 * sg + 2)) & 3;
       if (k0 + BK <= K) {
 #pragma unroll
@@ -359,12 +366,12 @@ struct Gemm {
       __syncthreads();
     };
 
-    issue(0, st0);
+    issue(st0);
     step_end();
     for (int t = 0; t < total; ++t) {
       char* cur = (t & 1) ? st1 : st0;
       char* nxt = (t & 1) ? st0 : st1;
-      if (t + 1 < total) issue(t + 1, nxt);
+      if (t + 1 < total) issue(nxt);
       compute(cur);
       step_end();
     }
