@@ -86,6 +86,48 @@ def recorded_traffic(workload: str, stage: str):
     return val if digest == source_digest() else None
 
 
+def blas_reference(cfg, planes, reps: int = 10) -> dict:
+    """hipBLASLt (torch.bmm, bf16) on the GEMM shapes of each stage, with the K dimension
+    multiplied by the plane products the stage executes; context for the stage kernels'
+    rates (no epilogues, no symmetry savings, no fusion)."""
+    import torch
+    P, b, d, dh = cfg.batch * cfg.heads, cfg.chunk, cfg.dim, cfg.hidden
+    nm = {"swiglu": 3, "gelu": 2, "linear": 1}[cfg.fw]
+    nz = {"swiglu": 2, "gelu": 1, "linear": 1}[cfg.fw]
+    n = d if cfg.fw == "linear" else dh
+    ap, gp, npl = planes[0], planes[1], planes[2]
+    ns_prod = npl * (npl + 1) // 2
+    b = min(b, 8192)
+    shapes = {}
+    if cfg.fw != "linear":
+        shapes["front_q"] = (P * nz, b, dh, d * ap)
+        shapes["front_k"] = (P * (nz + (cfg.loss == "dot")), b, dh, d * gp)
+        shapes["out"] = (P, b, d, dh * ap)
+    shapes["contract"] = (P * nm, d, n, b * gp)
+    if cfg.ns_steps:
+        shapes["ns_gram"] = (P * nm, d, d, n * ns_prod)
+        shapes["ns_poly"] = (P * nm, d, d, d * ns_prod)
+        shapes["ns_update"] = (P * nm, d, n, d * ns_prod)
+    out = {}
+    for name, (B, M, N, K) in shapes.items():
+        x = torch.randn(B, M, K, device="cuda", dtype=torch.bfloat16)
+        y = torch.randn(B, K, N, device="cuda", dtype=torch.bfloat16)
+        for _ in range(2):
+            torch.bmm(x, y)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.bmm(x, y)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        tf = 2.0 * B * M * N * K / us / 1e6
+        out[name] = {"bmm": [B, M, N, K], "us": round(us, 1), "tflops": round(tf, 1),
+                     "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 3)}
+        del x, y
+    return out
+
+
 def cpu_baseline(cfg, budget_chunks=None):
     """The oracle on the host: one (batch, head) problem over its first chunks."""
     import numpy as np
@@ -118,6 +160,8 @@ def main():
     ap.add_argument("--planes", default=None, help="apply,grad,ns,ns_lead bf16 plane counts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunks", type=int, default=None)
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time hipBLASLt (torch.bmm) on each stage's GEMM shapes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the steps, run one plain device copy of this many MiB (a "
                          "known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -226,6 +270,8 @@ def main():
         "roofline": roofline,
     }
     st.destroy()
+    if args.blas_reference:
+        res["blas_reference"] = blas_reference(cfg, planes)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_chunks)
     print(json.dumps(res), flush=True)

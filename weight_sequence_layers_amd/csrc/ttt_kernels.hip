@@ -330,9 +330,9 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
 }
 
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
-template <int T, int WG>
-__global__ __launch_bounds__(WG * WG * 64) void k_ns_update(NsArgs a) {
-  using G = Gemm<T, T, WG, WG, 1, 1, 0, 1>;   // X [M][N] read column-wise
+template <int T, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
+  using G = Gemm<T, T, WGM, WGN, 1, 1, 0, 1>;   // X [M][N] read column-wise
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
@@ -436,13 +436,13 @@ static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
 
 template <int FW, int MODE>
 static hipError_t front_fm(const FrontArgs& a, int Z, hipStream_t s) {
-  return front_t<128, 128, 2, 2, FW, MODE>(a, Z, s);
+  return front_t<128, 128, 2, 4, FW, MODE>(a, Z, s);
 }
 
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s) {
   if (fw == FW_SWIGLU) {
     if (mode == FRONT_Q) return front_fm<FW_SWIGLU, FRONT_Q>(a, Z, s);
-    if (mode == FRONT_K_DOT) return front_t<128, 128, 2, 2, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
+    if (mode == FRONT_K_DOT) return front_t<128, 128, 2, 4, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
     return front_fm<FW_SWIGLU, FRONT_K_MSE>(a, Z, s);
   }
   if (mode == FRONT_Q) return front_fm<FW_GELU, FRONT_Q>(a, Z, s);
@@ -472,9 +472,9 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
-  using G = Gemm<BM, BN, 2, 2, 1, 1, 1, 1>;
+  using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;
   ContractArgs a = a0;
-  auto kern = k_contract<BM, BN, 2, 2>;
+  auto kern = k_contract<BM, BN, 2, 4>;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   if (a.tiles == 0 || a.P == 0) return hipSuccess;
@@ -498,10 +498,11 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
   NsArgs a = a0;
   if (a.Z == 0) return hipSuccess;
   if (STAGE == 2) {
-    using GU = Gemm<T, T, WG, WG, 1, 1, 0, 1>;
+    constexpr int UWN = T >= 128 ? 4 : 2;   // 8 waves on 128-wide tiles
+    using GU = Gemm<T, T, WG, UWN, 1, 1, 0, 1>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T, WG>;
+    auto kern = k_ns_update<T, WG, UWN>;
     hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(GU::NT), 0, s, a);
   } else {
     a.tiles = ns_tri_tiles(a.M, T);
