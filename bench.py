@@ -32,26 +32,26 @@ def log(*a):
 
 
 def stage_flops(cfg) -> dict:
-    """Algorithmic FLOP of one launch of each stage kernel (one chunk, all problems; 2 per
-    multiply-add; Newton-Schulz counted without symmetry savings; the resident loop: the
-    whole sequence)."""
+    """Algorithmic FLOP of each stage per step (the whole sequence, all problems; 2 per
+    multiply-add; Newton-Schulz counted without symmetry savings). The resident loop is
+    one stage that does everything."""
     P, b, d, dh = cfg.batch * cfg.heads, cfg.chunk, cfg.dim, cfg.hidden
     nz = {"swiglu": 2, "gelu": 1, "linear": 1}[cfg.fw]
     nm = {"swiglu": 3, "gelu": 2, "linear": 1}[cfg.fw]
     n = d if cfg.fw == "linear" else dh
+    nc = cfg.n_chunks
     f = {}
     if cfg.fw != "linear":
-        f["front_q"] = 2.0 * nz * b * d * dh * P
-        f["front_k"] = 2.0 * (nz + (1 if cfg.loss == "dot" else 0)) * b * d * dh * P
-        f["out"] = 2.0 * b * d * dh * P
+        f["front_q"] = 2.0 * nz * b * d * dh * P * nc
+        f["front_k"] = 2.0 * (nz + (1 if cfg.loss == "dot" else 0)) * b * d * dh * P * nc
+        f["out"] = 2.0 * b * d * dh * P * nc
     else:
-        f["out"] = 2.0 * b * d * d * P
-    f["contract"] = 2.0 * nm * b * d * n * P
-    m = d
-    f["ns_gram"] = 2.0 * m * m * n * nm * P
-    f["ns_poly"] = 2.0 * m * m * m * nm * P
-    f["ns_update"] = 2.0 * m * m * n * nm * P
-    # the device-resident loop runs every chunk of the call in one launch
+        f["out"] = 2.0 * b * d * d * P * nc
+    f["contract"] = 2.0 * nm * b * d * n * P * nc
+    m, it = d, cfg.ns_steps * nc
+    f["ns_gram"] = 2.0 * m * m * n * nm * P * it
+    f["ns_poly"] = 2.0 * m * m * m * nm * P * it
+    f["ns_update"] = 2.0 * m * m * n * nm * P * it
     f["resident"] = total_flops(cfg)
     return f
 
@@ -247,7 +247,9 @@ def main():
     value = tokens * args.steps / elapsed
     tf_layer = total_flops(cfg) / (elapsed / args.steps) / 1e12
     avg_s = ms_dom / max(n_dom, 1) / 1e3
-    achieved = flops[dom] / avg_s / 1e12
+    # algorithmic FLOP of one launch: the stage's FLOP per step over its launches per step
+    per_launch = flops[dom] / (n_dom / args.steps)
+    achieved = per_launch / avg_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": recorded_traffic(cfg.name, dom), "kernel": dom,

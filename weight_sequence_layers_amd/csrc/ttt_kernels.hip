@@ -272,9 +272,9 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 
 // A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
 // the polynomial stage reads); A planes written for the full symmetric matrix.
-template <int T, int WG>
-__global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
-  using G = Gemm<T, T, WG, WG, 1, 1>;
+template <int T, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
+  using G = Gemm<T, T, WGM, WGN, 1, 1>;
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -303,9 +303,9 @@ __global__ __launch_bounds__(WG * WG * 64) void k_ns_gram(NsArgs a) {
 
 // B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
 // a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
-template <int T, int WG>
-__global__ __launch_bounds__(WG * WG * 64) void k_ns_poly(NsArgs a) {
-  using G = Gemm<T, T, WG, WG, 1, 1>;
+template <int T, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
+  using G = Gemm<T, T, WGM, WGN, 1, 1>;
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -453,9 +453,9 @@ hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t
 template <int MODE>
 static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
   constexpr int BM = 128, BN = 128;
-  using G = Gemm<BM, BN, 2, 2, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
+  using G = Gemm<BM, BN, 2, 4, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
   OutArgs a = a0;
-  auto kern = k_out<BM, BN, 2, 2, MODE>;
+  auto kern = k_out<BM, BN, 2, 4, MODE>;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
@@ -482,10 +482,6 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   return hipGetLastError();
 }
 
-int ns_tile(int Z, int M) {
-  (void)Z; (void)M;
-  return 128;
-}
 int ns_tri_tiles(int M, int tile) {
   const int t = (M + tile - 1) / tile;
   return t * (t + 1) / 2;
@@ -493,33 +489,38 @@ int ns_tri_tiles(int M, int tile) {
 
 template <int T, int STAGE>
 static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
-  constexpr int WG = 2;
-  using G = Gemm<T, T, WG, WG, 1, 1>;
+  constexpr int WGM = 2, WGN = T >= 128 ? 4 : 2;   // 8 waves on 128-wide tiles
+  using G = Gemm<T, T, WGM, WGN, 1, 1>;
   NsArgs a = a0;
   if (a.Z == 0) return hipSuccess;
   if (STAGE == 2) {
-    constexpr int UWN = T >= 128 ? 4 : 2;   // 8 waves on 128-wide tiles
-    using GU = Gemm<T, T, WG, UWN, 1, 1, 0, 1>;
+    using GU = Gemm<T, T, WGM, WGN, 1, 1, 0, 1>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T, WG, UWN>;
+    auto kern = k_ns_update<T, WGM, WGN>;
     hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(GU::NT), 0, s, a);
   } else {
     a.tiles = ns_tri_tiles(a.M, T);
+    const dim3 grid(a.tiles * a.Z);
     if (STAGE == 0) {
-      auto kern = k_ns_gram<T, WG>;
-        hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
+      auto kern = k_ns_gram<T, WGM, WGN>;
+      hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     } else {
-      auto kern = k_ns_poly<T, WG>;
-        hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
+      auto kern = k_ns_poly<T, WGM, WGN>;
+      hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_t<64, 0>(a, s); }
-hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_t<64, 1>(a, s); }
-hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) { return ns_t<128, 2>(a, s); }
+hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_t<NS_SYM_TILE, 0>(a, s); }
+hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_t<NS_SYM_TILE, 1>(a, s); }
+// The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs),
+// else 64x64 tiles (few problems, e.g. one or two heads).
+hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
+  const int64_t big = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.Z;
+  return big >= 512 ? ns_t<128, 2>(a, s) : ns_t<64, 2>(a, s);
+}
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
   if (a.P == 0 || a.nm == 0) return hipSuccess;
