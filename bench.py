@@ -145,10 +145,18 @@ def cpu_baseline(cfg, budget_chunks=None):
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1])
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"1 of {cfg.batch * cfg.heads} (batch, head) problems, {nc} chunks "
-                      f"({T} tokens), numpy fp64, {dt:.1f} s; problems are independent so "
-                      f"the rate is the whole workload's"}
+                      f"({T} tokens), numpy fp64, {dt:.1f} s on {model}; problems are "
+                      f"independent so the rate is the whole workload's"}
 
 
 def main():

@@ -3,6 +3,7 @@
     python -m weight_sequence_layers_amd.profiling stats  OUT.md  TRACE_DIR   "<command>"
     python -m weight_sequence_layers_amd.profiling traffic OUT.md FETCH_DIR WRITE_DIR \
         WORKLOAD "<fetch command>" "<write command>"
+    python -m weight_sequence_layers_amd.profiling mfma   OUT.md  PMC_DIR     "<command>"
 
 `stats` turns a `rocprofv3 --kernel-trace --stats` directory into a table of kernel
 durations. `traffic` turns one `--pmc FETCH_SIZE` and one `--pmc WRITE_SIZE` run of
@@ -120,9 +121,37 @@ def traffic_md(fetch_dir: str, write_dir: str, workload: str, fetch_cmd: str,
     return "\n".join(out) + "\n"
 
 
+def mfma_md(pmc_dir: str, command: str, cus: int = 256, simds_per_cu: int = 4,
+            xcds: int = 8) -> str:
+    """Executed MFMA utilisation per kernel: SQ_VALU_MFMA_BUSY_CYCLES summed over SIMDs
+    over (GRBM_GUI_ACTIVE per XCD x SIMD count), plus instruction mix per MFMA."""
+    per = defaultdict(lambda: defaultdict(float))
+    disp = defaultdict(set)
+    for r in csv.DictReader(open(_one("*counter_collection.csv", pmc_dir))):
+        k = _short(r["Kernel_Name"])
+        per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    out = ["# Executed MFMA utilisation per kernel", "", "Command (repository root, one MI355X):",
+           "", f"    {command}", "", f"source digest: {source_digest()}", "",
+           "utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs), summed "
+           "over the kernel's dispatches; it counts the MFMA work the kernel executes, plane "
+           "products included.", "",
+           "| kernel | dispatches | MFMA busy % | VALU / MFMA | LDS / MFMA |", "|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", 0)):
+        m = v.get("SQ_INSTS_MFMA", 0)
+        if not m or "GRBM_GUI_ACTIVE" not in v:
+            continue
+        util = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (v["GRBM_GUI_ACTIVE"] / xcds * cus * simds_per_cu)
+        out.append(f"| `{k}` | {len(disp[k])} | {100 * util:.1f} | "
+                   f"{v.get('SQ_INSTS_VALU', 0) / m:.2f} | {v.get('SQ_INSTS_LDS', 0) / m:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if len(argv) >= 4 and argv[1] == "stats":
         text = stats_md(argv[3], argv[4] if len(argv) > 4 else "")
+    elif len(argv) >= 4 and argv[1] == "mfma":
+        text = mfma_md(argv[3], argv[4] if len(argv) > 4 else "")
     elif len(argv) >= 8 and argv[1] == "traffic":
         text = traffic_md(argv[3], argv[4], argv[5], argv[6], argv[7])
     else:
