@@ -186,7 +186,11 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int 
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0>
+// PL > 0 selects the plane-resident product: A[0..PL) and B[0..PL) are the bf16 planes of
+// one A and one B (each operand with planes = 1); every K step loads all 2 PL plane tiles
+// once and accumulates the plane products (i, j) with i + j < PL into one accumulator.
+// PL = 0 keeps one accumulator per B operand and runs plane pairs as K segments.
+template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0>
 struct Gemm {
   static constexpr int NT = WGM * WGN * 64;
   static constexpr int TBM = BM, TBN = BN, WGN_ = WGN;
@@ -205,8 +209,10 @@ struct Gemm {
   static constexpr int S0_BYTES = STAGE > STORE_LDS ? STAGE : STORE_LDS;
   static constexpr int LDS_BYTES = S0_BYTES + STAGE;
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
+  static_assert(PL == 0 || (NA == PL && NB == PL), "plane-resident mode takes PL planes a side");
+  static constexpr int NACC = PL ? 1 : NB;
 
-  f32x16 acc[NB][TM][TN];
+  f32x16 acc[NACC][TM][TN];
 
   static __device__ __forceinline__ constexpr int ia(int p) {
     return (NA == 2 && p == NB - 1) ? 1 : 0;
@@ -214,7 +220,7 @@ struct Gemm {
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
-    for (int p = 0; p < NB; ++p)
+    for (int p = 0; p < NACC; ++p)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -349,14 +355,29 @@ struct Gemm {
             fb[i][t] = bcol(i)
                            ? read_frag<true, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s)
                            : read_frag<false, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s);
+        if constexpr (PL > 0) {
 #pragma unroll
-        for (int p = 0; p < NB; ++p)
+          for (int i = 0; i < PL; ++i)
 #pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
+            for (int j = 0; j < PL; ++j)
+              if (i + j < PL) {
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-              acc[p][tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ia(p)][tm], fb[p][tn],
-                                                                       acc[p][tm][tn], 0, 0, 0);
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                  for (int tn = 0; tn < TN; ++tn)
+                    acc[0][tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        fa[i][tm], fb[j][tn], acc[0][tm][tn], 0, 0, 0);
+              }
+        } else {
+#pragma unroll
+          for (int p = 0; p < NB; ++p)
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+              for (int tn = 0; tn < TN; ++tn)
+                acc[p][tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    fa[ia(p)][tm], fb[p][tn], acc[p][tm][tn], 0, 0, 0);
+        }
       }
     };
     // end of a step: this thread's loads have landed and its LDS reads are done (wait for

@@ -12,6 +12,10 @@ namespace ttt {
 __host__ __device__ inline Operand operand_of(const PlaneBuf& b, int np, int rows) {
   return make_operand(b.base, b.plane_stride, b.ld, b.zstride, np, rows);
 }
+// plane q of b alone, as a one-plane operand
+__host__ __device__ inline Operand plane_operand(const PlaneBuf& b, int q, int rows) {
+  return make_operand(b.base + q * b.plane_stride, 0, b.ld, b.zstride, 1, rows);
+}
 
 enum FwKind { FW_SWIGLU = 0, FW_GELU = 1, FW_LINEAR = 2 };
 enum FrontMode { FRONT_Q = 0, FRONT_K_DOT = 1, FRONT_K_MSE = 2 };

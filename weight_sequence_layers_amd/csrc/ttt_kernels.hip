@@ -272,9 +272,9 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 
 // A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
 // the polynomial stage reads); A planes written for the full symmetric matrix.
-template <int T, int WGM, int WGN>
+template <int T, int WGM, int WGN, int PL>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, 1, 1>;
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -282,10 +282,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
   int ti, tj;
   tri_tile(lid % a.tiles, (M + T - 1) / T, ti, tj);
   const int m0 = ti * T, n0 = tj * T;
-  const Operand X = operand_of(a.xin, a.xin.np, M);
+  Operand X[PL];
+#pragma unroll
+  for (int q = 0; q < PL; ++q) X[q] = plane_operand(a.xin, q, M);
   G g;
   g.zero();
-  g.run(&X, &X, m0, n0, zz, a.N, gemm_st0_, gemm_st1_);
+  g.run(X, X, m0, n0, zz, a.N, gemm_st0_, gemm_st1_);
   float s2 = 1.f;
   if (a.first) {
     const float s = ns_scale(a, zz);
@@ -303,9 +305,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
 
 // B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
 // a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
-template <int T, int WGM, int WGN>
+template <int T, int WGM, int WGN, int PL>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, 1, 1>;
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -313,10 +315,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
   int ti, tj;
   tri_tile(lid % a.tiles, (M + T - 1) / T, ti, tj);
   const int m0 = ti * T, n0 = tj * T;
-  const Operand Ao = operand_of(a.ain, a.ain.np, M);
+  Operand Ao[PL];
+#pragma unroll
+  for (int q = 0; q < PL; ++q) Ao[q] = plane_operand(a.ain, q, M);
   G g;
   g.zero();
-  g.run(&Ao, &Ao, m0, n0, zz, M, gemm_st0_, gemm_st1_);
+  g.run(Ao, Ao, m0, n0, zz, M, gemm_st0_, gemm_st1_);
   const int64_t base = (int64_t)zz * M * M;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
@@ -330,20 +334,25 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
 }
 
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
-template <int T, int WGM, int WGN>
+template <int T, int WGM, int WGN, int PL>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, 1, 1, 0, 1>;   // X [M][N] read column-wise
+  // X [M][N] read column-wise
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL>;
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int M = a.M, N = a.N;
   const int m0 = (tile / a.tiles_n) * T;
   const int n0 = (tile % a.tiles_n) * T;
-  const Operand Ao = operand_of(a.ain, a.ain.np, M);
-  const Operand Bo = operand_of(a.xin, a.xin.np, N);   // X [M][N] read as its columns
+  Operand Ao[PL], Bo[PL];   // B' planes; X [M][N] planes read as their columns
+#pragma unroll
+  for (int q = 0; q < PL; ++q) {
+    Ao[q] = plane_operand(a.ain, q, M);
+    Bo[q] = plane_operand(a.xin, q, N);
+  }
   G g;
   g.zero();
-  g.run(&Ao, &Bo, m0, n0, zz, M, gemm_st0_, gemm_st1_);
+  g.run(Ao, Bo, m0, n0, zz, M, gemm_st0_, gemm_st1_);
   const float sc = a.first ? ns_scale(a, zz) : 1.f;
   const int64_t base = (int64_t)zz * M * N;
   const int m = zz / a.P;
@@ -487,39 +496,54 @@ int ns_tri_tiles(int M, int tile) {
   return t * (t + 1) / 2;
 }
 
-template <int T, int STAGE>
+template <int T, int STAGE, int PL>
 static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
   constexpr int WGM = 2, WGN = T >= 128 ? 4 : 2;   // 8 waves on 128-wide tiles
-  using G = Gemm<T, T, WGM, WGN, 1, 1>;
   NsArgs a = a0;
   if (a.Z == 0) return hipSuccess;
-  if (STAGE == 2) {
-    using GU = Gemm<T, T, WGM, WGN, 1, 1, 0, 1>;
+  if constexpr (STAGE == 2) {
+    using GU = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T, WGM, WGN>;
+    auto kern = k_ns_update<T, WGM, WGN, PL>;
     hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(GU::NT), 0, s, a);
   } else {
+    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
     a.tiles = ns_tri_tiles(a.M, T);
     const dim3 grid(a.tiles * a.Z);
-    if (STAGE == 0) {
-      auto kern = k_ns_gram<T, WGM, WGN>;
+    if constexpr (STAGE == 0) {
+      auto kern = k_ns_gram<T, WGM, WGN, PL>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     } else {
-      auto kern = k_ns_poly<T, WGM, WGN>;
+      auto kern = k_ns_poly<T, WGM, WGN, PL>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     }
   }
   return hipGetLastError();
 }
 
-hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_t<NS_SYM_TILE, 0>(a, s); }
-hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_t<NS_SYM_TILE, 1>(a, s); }
-// The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs),
-// else 64x64 tiles (few problems, e.g. one or two heads).
+// the plane count of the iteration's operands picks the plane-resident instantiation
+template <int T, int STAGE>
+static hipError_t ns_planes(const NsArgs& a, int np, hipStream_t s) {
+  if (np == 1) return ns_t<T, STAGE, 1>(a, s);
+  if (np == 2) return ns_t<T, STAGE, 2>(a, s);
+  if (np == 3) return ns_t<T, STAGE, 3>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) {
+  return ns_planes<NS_SYM_TILE, 0>(a, a.xin.np, s);
+}
+hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
+  return ns_planes<NS_SYM_TILE, 1>(a, a.ain.np, s);
+}
+// The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs)
+// and the operands have at most two planes (three would not fit LDS); else 64x64 tiles.
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
   const int64_t big = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.Z;
-  return big >= 512 ? ns_t<128, 2>(a, s) : ns_t<64, 2>(a, s);
+  if (a.ain.np != a.xin.np) return hipErrorInvalidValue;
+  if (big < 512 || a.xin.np > 2) return ns_planes<64, 2>(a, a.xin.np, s);
+  return a.xin.np == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2>(a, s);
 }
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
