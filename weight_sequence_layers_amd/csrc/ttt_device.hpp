@@ -423,9 +423,11 @@ struct Gemm {
 // The two stage buffers of a Gemm type G as distinct __shared__ arrays (distinct objects
 // are what lets the compiler keep fragment reads of one buffer clear of the loads in
 // flight into the other); `smem`, the first, is also the epilogue's staging area.
-#define GEMM_LDS(G)                                                              \
-  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::S0_BYTES];         \
-  __shared__ __attribute__((aligned(1024))) char gemm_st1_[G::STAGE];            \
+#define GEMM_LDS(G) GEMM_LDS_EPI(G, G::STORE_LDS)
+// the same with the first buffer large enough for an epilogue that needs EPI bytes
+#define GEMM_LDS_EPI(G, EPI)                                                                  \
+  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::STAGE > (EPI) ? G::STAGE : (EPI)]; \
+  __shared__ __attribute__((aligned(1024))) char gemm_st1_[G::STAGE];                         \
   char* const smem = gemm_st0_
 
 // ------------------------------------------------------------------------ block order
@@ -442,34 +444,40 @@ __device__ __forceinline__ int xcd_block(int id, int total) {
 }
 
 // ------------------------------------------------------------------------ tile stores
-// Write one block tile of fp32 values (held in the MFMA accumulator layout of gemm G) to
-// a bf16-plane buffer through LDS, so that global stores are 16-byte vectors along the
-// buffer's contiguous dimension.
+// Write one block tile of fp32 values (held in the MFMA accumulator layout of gemm G) as
+// bf16 planes through LDS, so that global stores are 16-byte vectors along the buffer's
+// contiguous dimension.
 //   TILE_NORMAL: element (r, c) of the tile goes to row row0 + r, column col0 + c;
-//   TILE_TRANS : it goes to row col0 + c, column row0 + r (the transposed buffer);
 //   TILE_SYM   : square diagonal tile of a symmetric matrix: only elements with r <= c are
-//                taken, each written to (r, c) and (c, r).
-// rlim / clim bound the tile's rows / columns (relative to the tile origin); the limit of
-// the buffer's contiguous dimension must be a multiple of 8.  smem needs
-// (BM + 8) * (BN + 8) * 2 bytes.  Contains __syncthreads: call from every thread.
-enum TileMode { TILE_NORMAL = 0, TILE_TRANS = 1, TILE_SYM = 2 };
+//                taken, each written to (r, c) and (c, r);
+//   TILE_BOTH  : square tile written at (row0 + r, col0 + c) and, transposed, at
+//                (col0 + c, row0 + r) (an off-diagonal tile of a symmetric matrix).
+// Up to MAXP planes are staged per pass (each value is split once); more planes take more
+// passes. rlim / clim bound the tile's rows / columns (relative to the tile origin); the
+// limit of the buffer's contiguous dimension must be a multiple of 8. smem needs
+// store_lds_bytes<G, MODE, MAXP>() bytes. Contains __syncthreads: call from every thread.
+enum TileMode { TILE_NORMAL = 0, TILE_SYM = 1, TILE_BOTH = 2 };
 
-template <class G, int MODE>
-__device__ __forceinline__ void store_tile_planes(const f32x16 (&v)[G::TM][G::TN], char* smem,
-                                                  const PlaneBuf& dst, int z, int row0,
-                                                  int col0, int rlim, int clim) {
-  constexpr int TBM = G::TBM, TBN = G::TBN;
-  constexpr bool TR = MODE == TILE_TRANS;
-  constexpr int R = TR ? TBN : TBM;   // rows of the staged tile
-  constexpr int C = TR ? TBM : TBN;   // its contiguous length
-  constexpr int LD = C + 8;
+template <class G, int MODE, int MAXP>
+constexpr int store_lds_bytes() {
+  return MAXP * (MODE == TILE_BOTH ? 2 : 1) * G::TBM * (G::TBN + 8) * 2;
+}
+
+template <class G, int MODE, int MAXP>
+__device__ __forceinline__ void store_planes(const f32x16 (&v)[G::TM][G::TN], char* smem,
+                                             const PlaneBuf& dst, int z, int row0, int col0,
+                                             int rlim, int clim) {
+  constexpr int TBM = G::TBM, TBN = G::TBN, LD = TBN + 8;
+  constexpr int NO = MODE == TILE_BOTH ? 2 : 1;    // staged orientations
+  constexpr int REG = TBM * LD;                    // elements per staged region
+  constexpr int CPR = TBN / 8;                     // 16-byte chunks per staged row
+  static_assert(MODE == TILE_NORMAL || TBM == TBN, "symmetric stores take square tiles");
   u16* t = reinterpret_cast<u16*>(smem);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm0 = (wave / G::WGN_) * G::WM, wn0 = (wave % G::WGN_) * G::WN;
-  const int rl = TR ? clim : rlim;   // staged-row limit
-  const int cl = TR ? rlim : clim;   // contiguous limit
 #pragma unroll 1
-  for (int q = 0; q < dst.np; ++q) {
+  for (int q0 = 0; q0 < dst.np; q0 += MAXP) {
+    const int nq = dst.np - q0 < MAXP ? dst.np - q0 : MAXP;
     __syncthreads();
 #pragma unroll
     for (int tm = 0; tm < G::TM; ++tm)
@@ -479,27 +487,52 @@ __device__ __forceinline__ void store_tile_planes(const f32x16 (&v)[G::TM][G::TN
         for (int vi = 0; vi < 16; ++vi) {
           const int r = wm0 + tm * 32 + 8 * (vi >> 2) + 4 * (lane >> 5) + (vi & 3);
           const int c = wn0 + tn * 32 + (lane & 31);
-          const u16 hq = plane_of(v[tm][tn][vi], q);
-          if (MODE == TILE_NORMAL) {
-            t[r * LD + c] = hq;
-          } else if (MODE == TILE_TRANS) {
-            t[c * LD + r] = hq;
-          } else if (r <= c) {
-            t[r * LD + c] = hq;
-            t[c * LD + r] = hq;
+          float x = v[tm][tn][vi];
+          for (int i = 0; i < q0; ++i) x -= bf2f(f2bf(x));   // planes of earlier passes
+#pragma unroll
+          for (int qq = 0; qq < MAXP; ++qq) {
+            if (qq < nq) {
+              const u16 h = f2bf(x);
+              x -= bf2f(h);
+              u16* tq = t + qq * NO * REG;
+              if (MODE == TILE_NORMAL) {
+                tq[r * LD + c] = h;
+              } else if (MODE == TILE_BOTH) {
+                tq[r * LD + c] = h;
+                tq[REG + c * LD + r] = h;
+              } else if (r <= c) {
+                tq[r * LD + c] = h;
+                tq[c * LD + r] = h;
+              }
+            }
           }
         }
     __syncthreads();
-    u16* out = dst.base + q * dst.plane_stride + (int64_t)z * dst.zstride;
-    const int grow0 = TR ? col0 : row0, gcol0 = TR ? row0 : col0;
-    for (int ch = threadIdx.x; ch < R * (C / 8); ch += G::NT) {
-      const int rr = ch / (C / 8), cc = (ch % (C / 8)) * 8;
-      if (rr < rl && cc < cl)
-        *reinterpret_cast<uint4*>(out + (int64_t)(grow0 + rr) * dst.ld + gcol0 + cc) =
-            *reinterpret_cast<const uint4*>(t + rr * LD + cc);
+    const int total = nq * NO * TBM * CPR;
+    for (int ch = threadIdx.x; ch < total; ch += G::NT) {
+      const int qq = ch / (NO * TBM * CPR);
+      int rem = ch - qq * (NO * TBM * CPR);
+      const int o = rem / (TBM * CPR);
+      rem -= o * (TBM * CPR);
+      const int rr = rem / CPR, cc = (rem % CPR) * 8;
+      const int rl = o ? clim : rlim, cl = o ? rlim : clim;
+      if (rr < rl && cc < cl) {
+        u16* out = dst.base + (q0 + qq) * dst.plane_stride + (int64_t)z * dst.zstride;
+        const int gr = o ? col0 + rr : row0 + rr, gc = o ? row0 + cc : col0 + cc;
+        *reinterpret_cast<uint4*>(out + (int64_t)gr * dst.ld + gc) =
+            *reinterpret_cast<const uint4*>(t + (qq * NO + o) * REG + rr * LD + cc);
+      }
     }
   }
   __syncthreads();
+}
+
+// one plane per pass: the least LDS (the Gemm's STORE_LDS)
+template <class G, int MODE>
+__device__ __forceinline__ void store_tile_planes(const f32x16 (&v)[G::TM][G::TN], char* smem,
+                                                  const PlaneBuf& dst, int z, int row0,
+                                                  int col0, int rlim, int clim) {
+  store_planes<G, MODE, 1>(v, smem, dst, z, row0, col0, rlim, clim);
 }
 
 }  // namespace ttt

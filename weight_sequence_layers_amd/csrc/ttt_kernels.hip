@@ -57,6 +57,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   // the inner-product loss reads W2 [dim][hidden] column-wise for V W2
   using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0>;
   GEMM_LDS(G);
+  // two planes per store pass where the stage buffer already has room for them
+  constexpr int SP = G::STAGE >= store_lds_bytes<G, TILE_NORMAL, 2>() ? 2 : 1;
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int z = lid / a.tiles, tile = lid % a.tiles;
   const int m0 = (tile / a.tiles_n) * BM;
@@ -111,15 +113,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   const int cl = min(BN, a.N - n0);
   const int rn = min(BM, a.nrows - m0);   // rows holding tokens
   if constexpr (MODE == FRONT_K_DOT) {
-    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.o1, z, m0, n0, rn, cl);
+    store_planes<G, TILE_NORMAL, SP>(g.acc[0], smem, a.o1, z, m0, n0, rn, cl);
     if constexpr (FW == FW_SWIGLU) {
-      store_tile_planes<G, TILE_NORMAL>(g.acc[1], smem, a.o2, z, m0, n0, rn, cl);
-      store_tile_planes<G, TILE_NORMAL>(g.acc[2], smem, a.o3, z, m0, n0, rn, cl);
+      store_planes<G, TILE_NORMAL, SP>(g.acc[1], smem, a.o2, z, m0, n0, rn, cl);
+      store_planes<G, TILE_NORMAL, SP>(g.acc[2], smem, a.o3, z, m0, n0, rn, cl);
     } else {
-      store_tile_planes<G, TILE_NORMAL>(g.acc[1], smem, a.o3, z, m0, n0, rn, cl);
+      store_planes<G, TILE_NORMAL, SP>(g.acc[1], smem, a.o3, z, m0, n0, rn, cl);
     }
   } else {
-    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.o1, z, m0, n0, rn, cl);
+    store_planes<G, TILE_NORMAL, SP>(g.acc[0], smem, a.o1, z, m0, n0, rn, cl);
   }
 }
 
@@ -256,18 +258,15 @@ __device__ __forceinline__ void tri_tile(int t, int nt, int& ti, int& tj) {
 }
 
 // Store a tile of a symmetric M x M matrix computed at tile (ti, tj), ti <= tj, as planes
-// of the full matrix (upper tile, its mirror, or the symmetrised diagonal tile).
-template <class G>
+// of the full matrix (the symmetrised diagonal tile, or an upper tile and its mirror), all
+// planes in one pass.
+template <class G, int NP>
 __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char* smem,
                                           const PlaneBuf& dst, int zz, int m0, int n0, int M,
                                           bool diag) {
   const int rl = min(G::TBM, M - m0), cl = min(G::TBN, M - n0);
-  if (diag) {
-    store_tile_planes<G, TILE_SYM>(v, smem, dst, zz, m0, n0, rl, cl);
-  } else {
-    store_tile_planes<G, TILE_NORMAL>(v, smem, dst, zz, m0, n0, rl, cl);
-    store_tile_planes<G, TILE_TRANS>(v, smem, dst, zz, m0, n0, rl, cl);
-  }
+  if (diag) store_planes<G, TILE_SYM, NP>(v, smem, dst, zz, m0, n0, rl, cl);
+  else store_planes<G, TILE_BOTH, NP>(v, smem, dst, zz, m0, n0, rl, cl);
 }
 
 // A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
@@ -275,7 +274,7 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 template <int T, int WGM, int WGN, int PL>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
   using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
-  GEMM_LDS(G);
+  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, PL>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
   const int M = a.M;
@@ -300,7 +299,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
     g.acc[0][i][j][v] = x;
     if (R < M && C < M) a.afp[base + (int64_t)R * M + C] = x;
   });
-  store_sym<G>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
+  store_sym<G, PL>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
 // B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
@@ -308,7 +307,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
 template <int T, int WGM, int WGN, int PL>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
   using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
-  GEMM_LDS(G);
+  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, PL>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
   const int M = a.M;
@@ -330,7 +329,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
           (R == C ? a.coef_a : 0.f);
     g.acc[0][i][j][v] = x;
   });
-  store_sym<G>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
+  store_sym<G, PL>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
@@ -338,7 +337,8 @@ template <int T, int WGM, int WGN, int PL>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
   // X [M][N] read column-wise
   using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL>;
-  GEMM_LDS(G);
+  constexpr int SP = PL;   // all planes in one store pass
+  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_NORMAL, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int M = a.M, N = a.N;
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
   });
   if (!a.last) {
     const int rl = min(T, M - m0), cl = min(T, N - n0);
-    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.xout, zz, m0, n0, rl, cl);
+    store_planes<G, TILE_NORMAL, SP>(g.acc[0], smem, a.xout, zz, m0, n0, rl, cl);
   }
 }
 
