@@ -54,15 +54,16 @@ __device__ __forceinline__ __attribute__((address_space(3))) T& at(lds_t* lds, u
 // t = 1 / (1 + 0.3275911 x) and e = exp(-x^2) = exp(-z^2 / 2),
 //   Phi(-|z|) = erfc(x) / 2 = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) e / 2,
 // one reciprocal and one exponential, no branches; e also gives phi(z) = e / sqrt(2 pi).
+// The constants below fold 1/sqrt(2) into 0.3275911, the 1/2 into a1..a5, and log2(e)
+// into the exponent (exp2 is the native instruction).
 __device__ __forceinline__ float std_normal_tail(float z, float& e) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.f));
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.2316418883f, fabsf(z), 1.f));   // 0.3275911 / sqrt 2
   const float poly =
-      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f),
-                       -0.284496736f),
-               0.254829592f);
-  e = __expf(-x * x);
-  return 0.5f * poly * e;
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5307027145f, -0.7265760135f), 0.7107068705f),
+                       -0.142248368f),
+               0.127414796f);                                                  // a_i / 2
+  e = __builtin_amdgcn_exp2f(z * z * -0.72134752044f);                        // -log2(e) / 2
+  return poly * e;
 }
 __device__ __forceinline__ float gelu(float z) {
   float e;
