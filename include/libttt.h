@@ -152,15 +152,14 @@ ttt_status ttt_destroy_state(ttt_state* s);
  * stream and returns the number of timed launches and the sum of their durations in ms.
  * Stages: 0 front (query rows), 1 front (key rows), 2 output GEMM, 3 token contraction,
  * 4 Newton-Schulz Gram, 5 Newton-Schulz polynomial, 6 Newton-Schulz update,
- * 7 update + renorm, 8 (unused), 9 fp32 plane split, 10 MSE error / dH GEMMs,
- * 11 device-resident chunk loop (one launch per call).
+ * 7 update + renorm, 8 fp32 plane split, 9 MSE error / dH GEMMs,
+ * 10 device-resident chunk loop (one launch per call).
  * The hooks create and destroy HIP events but allocate no device memory.
  */
 typedef enum {
   TTT_STAGE_FRONT_Q = 0, TTT_STAGE_FRONT_K = 1, TTT_STAGE_OUT = 2, TTT_STAGE_CONTRACT = 3,
   TTT_STAGE_NS_GRAM = 4, TTT_STAGE_NS_POLY = 5, TTT_STAGE_NS_UPDATE = 6, TTT_STAGE_RENORM = 7,
-  TTT_STAGE_UNUSED_8 = 8, TTT_STAGE_SPLIT = 9, TTT_STAGE_MSE = 10, TTT_STAGE_RESIDENT = 11,
-  TTT_STAGE_COUNT = 12
+  TTT_STAGE_SPLIT = 8, TTT_STAGE_MSE = 9, TTT_STAGE_RESIDENT = 10, TTT_STAGE_COUNT = 11
 } ttt_stage;
 ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches);
 ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms);

@@ -1,6 +1,6 @@
 // Host side of libttt: argument checks, state and workspace ownership, and the chunk loop
 // that enqueues the stage kernels of ttt_kernels.hip.  See include/libttt.h for the ABI.
-#include "../../include/libttt.h"
+#include "libttt.h"
 
 #include <hip/hip_runtime.h>
 
