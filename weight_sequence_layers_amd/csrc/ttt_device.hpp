@@ -11,6 +11,7 @@ namespace ttt {
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------------ bf16 helpers
 __device__ __forceinline__ u16 f2bf(float x) {
@@ -98,12 +99,16 @@ struct PlaneBuf {
 // the inner loop has no plane-dependent control flow.
 //
 // Block: WGM x WGN waves, wave tile (BM/WGM) x (BN/WGN) of 32x32x16 MFMA tiles.  K steps of
-// 64 through two LDS stages, filled by direct global-to-LDS buffer loads one step ahead.
+// BK (64 or 32) through S LDS stages (2 to 4), filled by direct global-to-LDS buffer loads
+// S - 1 steps ahead.
 // Elements outside an operand read as zero (out-of-range buffer loads return 0).  16-byte
 // LDS chunks are XOR-swizzled by row so that fragment reads spread over the banks.
 enum Layout { L_ROW = 0, L_COL = 1 };
 
-__device__ __forceinline__ int swz_row(int r) { return (r >> 1) & 7; }
+// row tiles (BK / 8 chunks of 16 bytes per row): the rows one 16-lane read phase touches
+// land on distinct banks
+template <int BK>
+__device__ __forceinline__ int swz_row(int r) { return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
 // column tiles: rows k..k+3 read together by one transposing read land on distinct banks
 template <int R>
 __device__ __forceinline__ int swz_col(int k) { return R >= 128 ? (k & 3) << 2 : (k & 2); }
@@ -116,10 +121,29 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
 }
 
-// Per-thread load plan of one operand tile (R rows x 64 k) in either layout.
-template <int R, int NT>
+// Wait until at most N vector-memory operations of this thread are outstanding and all of
+// its LDS operations are done (s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at
+// its maximum, lgkmcnt 11:8 zero).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release part waits
+// for every outstanding vector-memory operation): the caller has waited for what the
+// other waves must see.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-thread load plan of one operand tile (R rows x BK k) in either layout.
+template <int R, int NT, int BK = 64>
 struct TileLoad {
-  static constexpr int BK = 64;
+  static_assert(BK == 64 || BK == 32, "K step of 64 or 32");
   static constexpr int CHUNKS = R * BK / 8;        // 16-byte chunks per tile
   static constexpr int C = CHUNKS / NT;            // per thread
   static constexpr int BYTES = R * BK * 2;
@@ -137,7 +161,7 @@ struct TileLoad {
     for (int c = 0; c < C; ++c) {
       const int ch = threadIdx.x + c * NT;
       if (!col) {
-        const int r = ch >> 3, kc = (ch & 7) ^ swz_row(r);
+        const int r = ch / (BK / 8), kc = (ch % (BK / 8)) ^ swz_row<BK>(r);
         kk[c] = kc * 8;
         off[c] = (row0 + r < o.rows) ? (uint32_t)(((int64_t)(row0 + r) * o.ld + kc * 8) * 2)
                                      : 0xC0000000u;
@@ -153,13 +177,14 @@ struct TileLoad {
 };
 
 // MFMA fragment (32 rows x 16 k) of a staged tile for k-substep s.
-template <bool COL, int R>
+template <bool COL, int R, int BK = 64>
 __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int s) {
   const int lane = threadIdx.x & 63;
   if (!COL) {
     const int r = row_base + (lane & 31);
     const int ch = 2 * s + (lane >> 5);
-    return *reinterpret_cast<const bf16x8*>(tile + r * 128 + ((ch ^ swz_row(r)) << 4));
+    return *reinterpret_cast<const bf16x8*>(tile + r * (BK * 2) +
+                                            ((ch ^ swz_row<BK>(r)) << 4));
   } else {
     // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element (j % 4) of
     // the 4-element rows addressed by lanes 4e + j/4, e = 0..3.  Lane 4e + q addresses
@@ -190,24 +215,45 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int 
 // one A and one B (each operand with planes = 1); every K step loads all 2 PL plane tiles
 // once and accumulates the plane products (i, j) with i + j < PL into one accumulator.
 // PL = 0 keeps one accumulator per B operand and runs plane pairs as K segments.
-template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0>
+//
+// WGK > 1 splits every K step among WGK groups of WGM x WGN waves: group k takes the
+// k-substeps [k, k + 1) * BK / 16 / WGK of the step for the whole wave tile, so each wave
+// holds a larger tile (fewer LDS fragment reads per MFMA) while the block keeps its wave
+// count.  reduce() then sums the groups' partial tiles through LDS, each 32 x 32 tile
+// ending in one group (tile t of a wave tile in group t mod WGK): for_each and the tile
+// stores visit only the tiles a wave owns.
+template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0,
+          int BK_ = 64, int S_ = 2, int WGK_ = 1>
 struct Gemm {
-  static constexpr int NT = WGM * WGN * 64;
+  static constexpr int WGK = WGK_;
+  static constexpr int NT = WGM * WGN * WGK * 64;
   static constexpr int TBM = BM, TBN = BN, WGN_ = WGN;
   static constexpr int STORE_LDS = (BM + 8) * (BN + 8) * 2;
-  static constexpr int BK = 64;
+  static constexpr int BK = BK_;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  using TA = TileLoad<BM, NT>;
-  using TB = TileLoad<BN, NT>;
+  static constexpr int SPW = BK / 16 / WGK;   // k-substeps per wave per K step
+  static_assert(SPW >= 1 && SPW * 16 * WGK == BK, "K step must split evenly among groups");
+  static_assert((TM * TN) % WGK == 0, "wave tile must split evenly among groups");
+  // LDS the reduction of the groups' partial tiles takes (one accumulator at a time)
+  static constexpr int RED_LDS = WGK > 1 ? BM * BN * 4 * (WGK - 1) : 0;
+  using TA = TileLoad<BM, NT, BK>;
+  using TB = TileLoad<BN, NT, BK>;
   static constexpr bool acol(int i) { return (LAM >> i) & 1; }
   static constexpr bool bcol(int i) { return (LBM >> i) & 1; }
   static constexpr int A_TILE = TA::BYTES, B_TILE = TB::BYTES;
   static constexpr int STAGE = NA * A_TILE + NB * B_TILE;
-  // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffer 1, declared as
-  // two separate __shared__ arrays by the kernel (GEMM_LDS)
-  static constexpr int S0_BYTES = STAGE > STORE_LDS ? STAGE : STORE_LDS;
-  static constexpr int LDS_BYTES = S0_BYTES + STAGE;
+  static constexpr int S = S_;
+  static_assert(S >= 2 && S <= 4, "2 to 4 stages");
+  // direct loads one thread issues per K step; S - 2 steps' worth stay in flight while a
+  // step computes, counted by vmcnt (at most 63)
+  static constexpr int DMA_STEP = NA * TA::C + NB * TB::C;
+  static_assert(DMA_STEP * (S - 2) < 64, "too many loads in flight for vmcnt");
+  // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffers 1 .. S - 1,
+  // declared as separate __shared__ arrays by the kernel (GEMM_LDS)
+  static constexpr int S0_MIN = STAGE > RED_LDS ? STAGE : RED_LDS;
+  static constexpr int S0_BYTES = S0_MIN > STORE_LDS ? S0_MIN : STORE_LDS;
+  static constexpr int LDS_BYTES = S0_BYTES + (S - 1) * STAGE;
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
   static_assert(PL == 0 || (NA == PL && NB == PL), "plane-resident mode takes PL planes a side");
   static constexpr int NACC = PL ? 1 : NB;
@@ -216,6 +262,20 @@ struct Gemm {
 
   static __device__ __forceinline__ constexpr int ia(int p) {
     return (NA == 2 && p == NB - 1) ? 1 : 0;
+  }
+
+  // this wave's K group, its place in the WGM x WGN grid, and its wave tile's origin
+  static __device__ __forceinline__ int wave_k() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / (WGM * WGN));
+  }
+  static __device__ __forceinline__ int wave_mn() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) % (WGM * WGN));
+  }
+  static __device__ __forceinline__ int wm0() { return (wave_mn() / WGN) * WM; }
+  static __device__ __forceinline__ int wn0() { return (wave_mn() % WGN) * WN; }
+  // whether this wave holds the final value of its tile (tm, tn) after reduce()
+  static __device__ __forceinline__ bool owns(int tm, int tn) {
+    return WGK == 1 || (tm * TN + tn) % WGK == wave_k();
   }
 
   __device__ __forceinline__ void zero() {
@@ -230,18 +290,19 @@ struct Gemm {
   }
 
   // A / B point at NA / NB consecutive operands (normally inside the kernel arguments).
-  // st0 / st1: the two stage buffers, distinct __shared__ arrays.  Each K step's tiles
-  // are loaded straight into LDS (buffer loads with the LDS flag) one step ahead: step t
-  // computes from one buffer while step t + 1 lands in the other.  The loop is unrolled
-  // by two so that every LDS access names a fixed buffer, which lets the compiler see
-  // that the fragment reads never touch the buffer being filled and wait for the loads
-  // only at the end of each step.
+  // st0 .. st3: the stage buffers, distinct __shared__ arrays (the last 4 - S unused).
+  // Each K step's tiles are loaded straight into LDS (buffer loads with the LDS flag)
+  // S - 1 steps ahead: step t computes from buffer t mod S while steps t + 1 .. t + S - 1
+  // are in flight.  One barrier per step: before it each thread waits for its own loads of
+  // step t (vmcnt, in issue order) and its LDS reads; after it every load of step t has
+  // landed and every wave has finished step t - 1, whose buffer then takes step t + S - 1.
   __device__ __forceinline__ void run(const Operand* __restrict__ A,
                                       const Operand* __restrict__ B, int m0, int n0, int z,
-                                      int K, char* st0, char* st1) {
+                                      int K, char* st0, char* st1, char* st2, char* st3) {
     const int wave = threadIdx.x >> 6;
-    const int wm0 = (wave / WGN) * WM;
-    const int wn0 = (wave % WGN) * WN;
+    const int wm0 = this->wm0();
+    const int wn0 = this->wn0();
+    const int s0 = wave_k() * SPW;   // this wave's first k-substep of a step
 
     // plane-pair segments
     const int PA = A[0].planes, PB = B[0].planes;
@@ -340,21 +401,23 @@ struct Gemm {
     };
     auto compute = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
+      for (int ss = 0; ss < SPW; ++ss) {
+        const int s = s0 + ss;
         bf16x8 fa[NA][TM], fb[NB][TN];
 #pragma unroll
         for (int i = 0; i < NA; ++i)
 #pragma unroll
           for (int t = 0; t < TM; ++t)
-            fa[i][t] = acol(i) ? read_frag<true, BM>(st + i * A_TILE, wm0 + t * 32, s)
-                               : read_frag<false, BM>(st + i * A_TILE, wm0 + t * 32, s);
+            fa[i][t] = acol(i) ? read_frag<true, BM, BK>(st + i * A_TILE, wm0 + t * 32, s)
+                               : read_frag<false, BM, BK>(st + i * A_TILE, wm0 + t * 32, s);
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
           for (int t = 0; t < TN; ++t)
-            fb[i][t] = bcol(i)
-                           ? read_frag<true, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s)
-                           : read_frag<false, BN>(st + NA * A_TILE + i * B_TILE, wn0 + t * 32, s);
+            fb[i][t] = bcol(i) ? read_frag<true, BN, BK>(st + NA * A_TILE + i * B_TILE,
+                                                        wn0 + t * 32, s)
+                               : read_frag<false, BN, BK>(st + NA * A_TILE + i * B_TILE,
+                                                         wn0 + t * 32, s);
         if constexpr (PL > 0) {
 #pragma unroll
           for (int i = 0; i < PL; ++i)
@@ -387,13 +450,33 @@ struct Gemm {
       __syncthreads();
     };
 
-    issue(st0);
-    step_end();
-    for (int t = 0; t < total; ++t) {
-      char* cur = (t & 1) ? st1 : st0;
-      char* nxt = (t & 1) ? st0 : st1;
-      if (t + 1 < total) issue(nxt);
-      compute(cur);
+    if constexpr (S == 2) {
+      issue(st0);
+      step_end();
+      for (int t = 0; t < total; ++t) {
+        char* cur = (t & 1) ? st1 : st0;
+        char* nxt = (t & 1) ? st0 : st1;
+        if (t + 1 < total) issue(nxt);
+        compute(cur);
+        step_end();
+      }
+    } else {
+      auto buf = [&](int i) __attribute__((always_inline)) {
+        return i == 0 ? st0 : i == 1 ? st1 : (S == 3 || i == 2) ? st2 : st3;
+      };
+      const int pre = total < S - 1 ? total : S - 1;
+      for (int p = 0; p < pre; ++p) issue(buf(p));
+      int bc = 0, bi = S - 1;  // buffers of the step computed and of the step issued
+      for (int t = 0; t < total; ++t) {
+        if (t + S - 2 < total) wait_vm_lgkm0<DMA_STEP * (S - 2)>();
+        else wait_vm_lgkm0<0>();
+        block_barrier();
+        if (t + S - 1 < total) issue(buf(bi));
+        compute(buf(bc));
+        bc = bc == S - 1 ? 0 : bc + 1;
+        bi = bi == S - 1 ? 0 : bi + 1;
+      }
+      // the epilogue may reuse stage buffer 0
       step_end();
     }
   }
@@ -404,19 +487,65 @@ struct Gemm {
   template <class F>
   __device__ __forceinline__ void for_each(F f) const {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm0 = (wave / WGN) * WM;
-    const int wn0 = (wave % WGN) * WN;
+    const int wm0 = this->wm0();
+    const int wn0 = this->wn0();
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
+      for (int tn = 0; tn < TN; ++tn) {
+        if (!owns(tm, tn)) continue;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = wm0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           const int col = wn0 + tn * 32 + (lane & 31);
           f(tm, tn, v, row, col);
         }
+      }
+  }
+
+  // Sum the K groups' partial tiles (WGK > 1) into the owning group, through red (at least
+  // RED_LDS bytes of LDS that no wave still reads).  Every other group sends its partial
+  // of tile t to slot ((wave_mn TM TN + t) (WGK - 1) + rank), 64 lanes x 64 bytes, each
+  // lane's 16 floats as four 16-byte pieces strided by 1 KB so that a wave's writes and
+  // reads cover whole bank rows.  Contains barriers: call from every thread.
+  __device__ __forceinline__ void reduce(char* red) {
+    if constexpr (WGK > 1) {
+      const int lane = threadIdx.x & 63;
+      const int wk = wave_k(), wmn = wave_mn();
+#pragma unroll
+      for (int p = 0; p < NACC; ++p) {
+        if (p) __syncthreads();   // the previous accumulator's slots have been read
+#pragma unroll
+        for (int t = 0; t < TM * TN; ++t) {
+          const int owner = t % WGK;
+          if (owner == wk) continue;
+          const int rank = (wk - owner - 1 + WGK) % WGK;
+          char* slot = red + ((wmn * TM * TN + t) * (WGK - 1) + rank) * 4096;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 x = {acc[p][t / TN][t % TN][4 * q], acc[p][t / TN][t % TN][4 * q + 1],
+                       acc[p][t / TN][t % TN][4 * q + 2], acc[p][t / TN][t % TN][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(slot + q * 1024 + lane * 16) = x;
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TM * TN; ++t) {
+          if (t % WGK != wk) continue;
+#pragma unroll
+          for (int rank = 0; rank < WGK - 1; ++rank) {
+            const char* slot = red + ((wmn * TM * TN + t) * (WGK - 1) + rank) * 4096;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 x = *reinterpret_cast<const f32x4*>(slot + q * 1024 + lane * 16);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[p][t / TN][t % TN][4 * q + e] += x[e];
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
 };
 
@@ -426,9 +555,13 @@ struct Gemm {
 #define GEMM_LDS(G) GEMM_LDS_EPI(G, G::STORE_LDS)
 // the same with the first buffer large enough for an epilogue that needs EPI bytes
 #define GEMM_LDS_EPI(G, EPI)                                                                  \
-  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::STAGE > (EPI) ? G::STAGE : (EPI)]; \
+  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::S0_MIN > (EPI) ? G::S0_MIN : (EPI)]; \
   __shared__ __attribute__((aligned(1024))) char gemm_st1_[G::STAGE];                         \
+  __shared__ __attribute__((aligned(1024))) char gemm_st2_[G::S > 2 ? G::STAGE : 16];         \
+  __shared__ __attribute__((aligned(1024))) char gemm_st3_[G::S > 3 ? G::STAGE : 16];         \
   char* const smem = gemm_st0_
+// the stage buffers GEMM_LDS declares, as Gemm::run takes them
+#define GEMM_STAGES gemm_st0_, gemm_st1_, gemm_st2_, gemm_st3_
 
 // ------------------------------------------------------------------------ block order
 // Workgroups of a launch are handed to the 8 XCDs round-robin by linear id, and each XCD
@@ -473,8 +606,8 @@ __device__ __forceinline__ void store_planes(const f32x16 (&v)[G::TM][G::TN], ch
   constexpr int CPR = TBN / 8;                     // 16-byte chunks per staged row
   static_assert(MODE == TILE_NORMAL || TBM == TBN, "symmetric stores take square tiles");
   u16* t = reinterpret_cast<u16*>(smem);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave / G::WGN_) * G::WM, wn0 = (wave % G::WGN_) * G::WN;
+  const int lane = threadIdx.x & 63;
+  const int wm0 = G::wm0(), wn0 = G::wn0();
 #pragma unroll 1
   for (int q0 = 0; q0 < dst.np; q0 += MAXP) {
     const int nq = dst.np - q0 < MAXP ? dst.np - q0 : MAXP;
@@ -485,6 +618,7 @@ __device__ __forceinline__ void store_planes(const f32x16 (&v)[G::TM][G::TN], ch
       for (int tn = 0; tn < G::TN; ++tn)
 #pragma unroll
         for (int vi = 0; vi < 16; ++vi) {
+          if (!G::owns(tm, tn)) continue;
           const int r = wm0 + tm * 32 + 8 * (vi >> 2) + 4 * (lane >> 5) + (vi & 3);
           const int c = wn0 + tn * 32 + (lane & 31);
           float x = v[tm][tn][vi];

@@ -50,12 +50,12 @@ struct FrontShape {
   static constexpr int NP = NB;
 };
 
-template <int BM, int BN, int WGM, int WGN, int FW, int MODE>
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK, int S>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   using FS = FrontShape<FW, MODE>;
   constexpr int NA = FS::NA, NB = FS::NB;
   // the inner-product loss reads W2 [dim][hidden] column-wise for V W2
-  using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0>;
+  using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0, 0, BK, S>;
   GEMM_LDS(G);
   // two planes per store pass where the stage buffer already has room for them
   constexpr int SP = G::STAGE >= store_lds_bytes<G, TILE_NORMAL, 2>() ? 2 : 1;
@@ -66,7 +66,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
 
   G g;
   g.zero();
-  g.run(a.A, a.B, m0, n0, z, a.K, gemm_st0_, gemm_st1_);
+  g.run(a.A, a.B, m0, n0, z, a.K, GEMM_STAGES);
+  g.reduce(smem);
 
   const float* eta = a.eta + (int64_t)z * a.eta_zstride;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
@@ -137,7 +138,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   const int n0 = (tile % a.tiles_n) * BN;
   G g;
   g.zero();
-  g.run(&a.a, &a.b, m0, n0, z, a.K, gemm_st0_, gemm_st1_);
+  g.run(&a.a, &a.b, m0, n0, z, a.K, GEMM_STAGES);
+  g.reduce(smem);
 
   const int cl = min(BN, a.N - n0);
   const int rn = min(BM, a.nrows - m0);
@@ -200,9 +202,9 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 }
 
 // ------------------------------------------------------------------------ contraction
-template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1>;   // both operands token-major
+template <int BM, int BN, int WGM, int WGN, int WGK>
+__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_contract(ContractArgs a) {
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1, 0, 64, 2, WGK>;   // both operands token-major
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
@@ -211,7 +213,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   const int n0 = (tile % a.tiles_n) * BN;
   G g;
   g.zero();
-  g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, gemm_st0_, gemm_st1_);
+  g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, GEMM_STAGES);
+  g.reduce(smem);
 
   const int M = a.M, N = a.N;
   const int64_t base = (int64_t)zz * M * N;
@@ -271,9 +274,9 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 
 // A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
 // the polynomial stage reads); A planes written for the full symmetric matrix.
-template <int T, int WGM, int WGN, int PL>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
+template <int T, int WGM, int WGN, int PL, int BK, int S, int WGK>
+__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, BK, S, WGK>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, PL>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -286,7 +289,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
   for (int q = 0; q < PL; ++q) X[q] = plane_operand(a.xin, q, M);
   G g;
   g.zero();
-  g.run(X, X, m0, n0, zz, a.N, gemm_st0_, gemm_st1_);
+  g.run(X, X, m0, n0, zz, a.N, GEMM_STAGES);
+  g.reduce(smem);
   float s2 = 1.f;
   if (a.first) {
     const float s = ns_scale(a, zz);
@@ -304,9 +308,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
 
 // B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
 // a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
-template <int T, int WGM, int WGN, int PL>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
+template <int T, int WGM, int WGN, int PL, int BK, int S, int WGK>
+__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, BK, S, WGK>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, PL>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -319,7 +323,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
   for (int q = 0; q < PL; ++q) Ao[q] = plane_operand(a.ain, q, M);
   G g;
   g.zero();
-  g.run(Ao, Ao, m0, n0, zz, M, gemm_st0_, gemm_st1_);
+  g.run(Ao, Ao, m0, n0, zz, M, GEMM_STAGES);
+  g.reduce(smem);
   const int64_t base = (int64_t)zz * M * M;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
@@ -333,11 +338,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
 }
 
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
-template <int T, int WGM, int WGN, int PL>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
+template <int T, int WGM, int WGN, int PL, int BK, int S, int SP, int WGK>
+__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
   // X [M][N] read column-wise
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL>;
-  constexpr int SP = PL;   // all planes in one store pass
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, S, WGK>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_NORMAL, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
@@ -352,7 +356,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
   }
   G g;
   g.zero();
-  g.run(Ao, Bo, m0, n0, zz, M, gemm_st0_, gemm_st1_);
+  g.run(Ao, Bo, m0, n0, zz, M, GEMM_STAGES);
+  g.reduce(smem);
   const float sc = a.first ? ns_scale(a, zz) : 1.f;
   const int64_t base = (int64_t)zz * M * N;
   const int m = zz / a.P;
@@ -429,12 +434,13 @@ __global__ __launch_bounds__(256) void k_split(SplitArgs a) {
 // dynamic LDS.
 static constexpr int LDS_MAX = 160 * 1024;
 
-template <int BM, int BN, int WGM, int WGN, int FW, int MODE>
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK = 64, int S = 2>
 static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
   using FS = FrontShape<FW, MODE>;
-  using G = Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB, 0, FS::DOT ? (1 << (FS::NB - 1)) : 0>;
+  using G =
+      Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB, 0, FS::DOT ? (1 << (FS::NB - 1)) : 0, 0, BK, S>;
   FrontArgs a = a0;
-  auto kern = k_front<BM, BN, WGM, WGN, FW, MODE>;
+  auto kern = k_front<BM, BN, WGM, WGN, FW, MODE, BK, S>;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
@@ -443,9 +449,12 @@ static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Fronts step K by 32, which keeps their LDS low enough for two workgroups per CU (61 KB
+// for the SwiGLU apply front), except the SwiGLU inner-product gradient front: its three
+// accumulators limit it to one workgroup per CU, and it keeps steps of 64.
 template <int FW, int MODE>
 static hipError_t front_fm(const FrontArgs& a, int Z, hipStream_t s) {
-  return front_t<128, 128, 2, 4, FW, MODE>(a, Z, s);
+  return front_t<128, 128, 2, 4, FW, MODE, 32>(a, Z, s);
 }
 
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s) {
@@ -480,10 +489,10 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 }
 
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
-  constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
-  using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;
+  constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN, WGM = 2, WGN = 4, WGK = 1;
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1, 0, 64, 2, WGK>;
   ContractArgs a = a0;
-  auto kern = k_contract<BM, BN, 2, 4>;
+  auto kern = k_contract<BM, BN, WGM, WGN, WGK>;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   if (a.tiles == 0 || a.P == 0) return hipSuccess;
@@ -496,26 +505,28 @@ int ns_tri_tiles(int M, int tile) {
   return t * (t + 1) / 2;
 }
 
-template <int T, int STAGE, int PL>
+// One Newton-Schulz stage (0 Gram, 1 polynomial, 2 update) on T x T tiles of
+// WGM x WGN x WGK waves, K steps of BK through S stages; the update stores SP planes per
+// pass.
+template <int T, int STAGE, int PL, int WGM = 2, int WGN = (T >= 128 ? 4 : 2), int BK = 64,
+          int S = 2, int SP = PL, int WGK = 1>
 static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
-  constexpr int WGM = 2, WGN = T >= 128 ? 4 : 2;   // 8 waves on 128-wide tiles
   NsArgs a = a0;
   if (a.Z == 0) return hipSuccess;
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, STAGE == 2 ? (1 << PL) - 1 : 0, PL, BK, S, WGK>;
   if constexpr (STAGE == 2) {
-    using GU = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T, WGM, WGN, PL>;
-    hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(GU::NT), 0, s, a);
+    auto kern = k_ns_update<T, WGM, WGN, PL, BK, S, SP, WGK>;
+    hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
   } else {
-    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
     a.tiles = ns_tri_tiles(a.M, T);
     const dim3 grid(a.tiles * a.Z);
     if constexpr (STAGE == 0) {
-      auto kern = k_ns_gram<T, WGM, WGN, PL>;
+      auto kern = k_ns_gram<T, WGM, WGN, PL, BK, S, WGK>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     } else {
-      auto kern = k_ns_poly<T, WGM, WGN, PL>;
+      auto kern = k_ns_poly<T, WGM, WGN, PL, BK, S, WGK>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     }
   }
@@ -523,11 +534,11 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
 }
 
 // the plane count of the iteration's operands picks the plane-resident instantiation
-template <int T, int STAGE>
+template <int T, int STAGE, int WGM = 2, int WGN = (T >= 128 ? 4 : 2), int WGK = 1>
 static hipError_t ns_planes(const NsArgs& a, int np, hipStream_t s) {
-  if (np == 1) return ns_t<T, STAGE, 1>(a, s);
-  if (np == 2) return ns_t<T, STAGE, 2>(a, s);
-  if (np == 3) return ns_t<T, STAGE, 3>(a, s);
+  if (np == 1) return ns_t<T, STAGE, 1, WGM, WGN, 64, 2, 1, WGK>(a, s);
+  if (np == 2) return ns_t<T, STAGE, 2, WGM, WGN, 64, 2, 2, WGK>(a, s);
+  if (np == 3) return ns_t<T, STAGE, 3, WGM, WGN, 64, 2, 3, WGK>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -539,11 +550,14 @@ hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
 }
 // The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs)
 // and the operands have at most two planes (three would not fit LDS); else 64x64 tiles.
+// With two planes the 128x128 kernel steps K by 32 and stores one plane per pass, which
+// keeps its LDS at 66 KB: two workgroups share a CU, one's epilogue overlapping the
+// other's main loop.
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
   const int64_t big = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.Z;
   if (a.ain.np != a.xin.np) return hipErrorInvalidValue;
   if (big < 512 || a.xin.np > 2) return ns_planes<64, 2>(a, a.xin.np, s);
-  return a.xin.np == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2>(a, s);
+  return a.xin.np == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2, 2, 4, 32, 2, 1>(a, s);
 }
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
