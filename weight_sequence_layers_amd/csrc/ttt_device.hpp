@@ -99,8 +99,8 @@ struct PlaneBuf {
 // the inner loop has no plane-dependent control flow.
 //
 // Block: WGM x WGN waves, wave tile (BM/WGM) x (BN/WGN) of 32x32x16 MFMA tiles.  K steps of
-// BK (64 or 32) through S LDS stages (2 to 4), filled by direct global-to-LDS buffer loads
-// S - 1 steps ahead.
+// BK (64, or 32 to halve the LDS of a stage) through two LDS stages, filled by direct
+// global-to-LDS buffer loads one step ahead.
 // Elements outside an operand read as zero (out-of-range buffer loads return 0).  16-byte
 // LDS chunks are XOR-swizzled by row so that fragment reads spread over the banks.
 enum Layout { L_ROW = 0, L_COL = 1 };
@@ -119,25 +119,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // One 16-byte-per-lane direct load from a buffer into LDS (lane l writes dst + 16 l).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void_t* dst, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
-}
-
-// Wait until at most N vector-memory operations of this thread are outstanding and all of
-// its LDS operations are done (s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at
-// its maximum, lgkmcnt 11:8 zero).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (whose release part waits
-// for every outstanding vector-memory operation): the caller has waited for what the
-// other waves must see.  The empty asm statements keep the compiler from moving memory
-// accesses across it.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // Per-thread load plan of one operand tile (R rows x BK k) in either layout.
@@ -216,44 +197,32 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int 
 // once and accumulates the plane products (i, j) with i + j < PL into one accumulator.
 // PL = 0 keeps one accumulator per B operand and runs plane pairs as K segments.
 //
-// WGK > 1 splits every K step among WGK groups of WGM x WGN waves: group k takes the
-// k-substeps [k, k + 1) * BK / 16 / WGK of the step for the whole wave tile, so each wave
-// holds a larger tile (fewer LDS fragment reads per MFMA) while the block keeps its wave
-// count.  reduce() then sums the groups' partial tiles through LDS, each 32 x 32 tile
-// ending in one group (tile t of a wave tile in group t mod WGK): for_each and the tile
-// stores visit only the tiles a wave owns.
+// SW selects the accumulator layout.  The MFMA computes D = A B with A's fragment giving
+// D's rows and B's its columns.  SW = false feeds the A tile as A: element v of a lane's
+// 32 x 32 tile sits at row 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32.  SW = true
+// feeds the B tile as A, computing the transposed tile: element v then sits at row
+// lane % 32, column 8 (v / 4) + 4 (lane / 32) + v % 4, so each lane holds runs of four
+// consecutive columns, which the tile stores write to LDS four at a time.
 template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0,
-          int BK_ = 64, int S_ = 2, int WGK_ = 1>
+          int BK_ = 64, bool SW_ = false>
 struct Gemm {
-  static constexpr int WGK = WGK_;
-  static constexpr int NT = WGM * WGN * WGK * 64;
+  static constexpr bool SW = SW_;
+  static constexpr int NT = WGM * WGN * 64;
   static constexpr int TBM = BM, TBN = BN, WGN_ = WGN;
   static constexpr int STORE_LDS = (BM + 8) * (BN + 8) * 2;
   static constexpr int BK = BK_;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int SPW = BK / 16 / WGK;   // k-substeps per wave per K step
-  static_assert(SPW >= 1 && SPW * 16 * WGK == BK, "K step must split evenly among groups");
-  static_assert((TM * TN) % WGK == 0, "wave tile must split evenly among groups");
-  // LDS the reduction of the groups' partial tiles takes (one accumulator at a time)
-  static constexpr int RED_LDS = WGK > 1 ? BM * BN * 4 * (WGK - 1) : 0;
   using TA = TileLoad<BM, NT, BK>;
   using TB = TileLoad<BN, NT, BK>;
   static constexpr bool acol(int i) { return (LAM >> i) & 1; }
   static constexpr bool bcol(int i) { return (LBM >> i) & 1; }
   static constexpr int A_TILE = TA::BYTES, B_TILE = TB::BYTES;
   static constexpr int STAGE = NA * A_TILE + NB * B_TILE;
-  static constexpr int S = S_;
-  static_assert(S >= 2 && S <= 4, "2 to 4 stages");
-  // direct loads one thread issues per K step; S - 2 steps' worth stay in flight while a
-  // step computes, counted by vmcnt (at most 63)
-  static constexpr int DMA_STEP = NA * TA::C + NB * TB::C;
-  static_assert(DMA_STEP * (S - 2) < 64, "too many loads in flight for vmcnt");
-  // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffers 1 .. S - 1,
-  // declared as separate __shared__ arrays by the kernel (GEMM_LDS)
-  static constexpr int S0_MIN = STAGE > RED_LDS ? STAGE : RED_LDS;
-  static constexpr int S0_BYTES = S0_MIN > STORE_LDS ? S0_MIN : STORE_LDS;
-  static constexpr int LDS_BYTES = S0_BYTES + (S - 1) * STAGE;
+  // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffer 1, declared as
+  // two separate __shared__ arrays by the kernel (GEMM_LDS)
+  static constexpr int S0_BYTES = STAGE > STORE_LDS ? STAGE : STORE_LDS;
+  static constexpr int LDS_BYTES = S0_BYTES + STAGE;
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
   static_assert(PL == 0 || (NA == PL && NB == PL), "plane-resident mode takes PL planes a side");
   static constexpr int NACC = PL ? 1 : NB;
@@ -264,19 +233,22 @@ struct Gemm {
     return (NA == 2 && p == NB - 1) ? 1 : 0;
   }
 
-  // this wave's K group, its place in the WGM x WGN grid, and its wave tile's origin
-  static __device__ __forceinline__ int wave_k() {
-    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / (WGM * WGN));
+  // one 32 x 32 x 16 product of an A-tile fragment and a B-tile fragment into c
+  static __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return SW ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0)
+              : __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  static __device__ __forceinline__ int wave_mn() {
-    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) % (WGM * WGN));
+  // row and column of element v of this lane's 32 x 32 tile, relative to the tile
+  static __device__ __forceinline__ int elem_row(int v, int lane) {
+    return SW ? (lane & 31) : 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
   }
-  static __device__ __forceinline__ int wm0() { return (wave_mn() / WGN) * WM; }
-  static __device__ __forceinline__ int wn0() { return (wave_mn() % WGN) * WN; }
-  // whether this wave holds the final value of its tile (tm, tn) after reduce()
-  static __device__ __forceinline__ bool owns(int tm, int tn) {
-    return WGK == 1 || (tm * TN + tn) % WGK == wave_k();
+  static __device__ __forceinline__ int elem_col(int v, int lane) {
+    return SW ? 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3) : (lane & 31);
   }
+
+  // origin of this wave's tile in the block tile
+  static __device__ __forceinline__ int wm0() { return ((threadIdx.x >> 6) / WGN) * WM; }
+  static __device__ __forceinline__ int wn0() { return ((threadIdx.x >> 6) % WGN) * WN; }
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -290,19 +262,17 @@ struct Gemm {
   }
 
   // A / B point at NA / NB consecutive operands (normally inside the kernel arguments).
-  // st0 .. st3: the stage buffers, distinct __shared__ arrays (the last 4 - S unused).
-  // Each K step's tiles are loaded straight into LDS (buffer loads with the LDS flag)
-  // S - 1 steps ahead: step t computes from buffer t mod S while steps t + 1 .. t + S - 1
-  // are in flight.  One barrier per step: before it each thread waits for its own loads of
-  // step t (vmcnt, in issue order) and its LDS reads; after it every load of step t has
-  // landed and every wave has finished step t - 1, whose buffer then takes step t + S - 1.
+  // st0 / st1: the two stage buffers, distinct __shared__ arrays.  Each K step's tiles
+  // are loaded straight into LDS (buffer loads with the LDS flag) one step ahead: step t
+  // computes from one buffer while step t + 1 lands in the other.  Every LDS access names
+  // one of two distinct arrays, which lets the compiler see that the fragment reads never
+  // touch the buffer being filled and wait for the loads only at the end of each step.
   __device__ __forceinline__ void run(const Operand* __restrict__ A,
                                       const Operand* __restrict__ B, int m0, int n0, int z,
-                                      int K, char* st0, char* st1, char* st2, char* st3) {
+                                      int K, char* st0, char* st1) {
     const int wave = threadIdx.x >> 6;
     const int wm0 = this->wm0();
     const int wn0 = this->wn0();
-    const int s0 = wave_k() * SPW;   // this wave's first k-substep of a step
 
     // plane-pair segments
     const int PA = A[0].planes, PB = B[0].planes;
@@ -401,8 +371,7 @@ struct Gemm {
     };
     auto compute = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ss = 0; ss < SPW; ++ss) {
-        const int s = s0 + ss;
+      for (int s = 0; s < BK / 16; ++s) {
         bf16x8 fa[NA][TM], fb[NB][TN];
 #pragma unroll
         for (int i = 0; i < NA; ++i)
@@ -428,8 +397,7 @@ struct Gemm {
                 for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
                   for (int tn = 0; tn < TN; ++tn)
-                    acc[0][tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        fa[i][tm], fb[j][tn], acc[0][tm][tn], 0, 0, 0);
+                    acc[0][tm][tn] = mma(fa[i][tm], fb[j][tn], acc[0][tm][tn]);
               }
         } else {
 #pragma unroll
@@ -438,8 +406,7 @@ struct Gemm {
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
               for (int tn = 0; tn < TN; ++tn)
-                acc[p][tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    fa[ia(p)][tm], fb[p][tn], acc[p][tm][tn], 0, 0, 0);
+                acc[p][tm][tn] = mma(fa[ia(p)][tm], fb[p][tn], acc[p][tm][tn]);
         }
       }
     };
@@ -450,40 +417,19 @@ struct Gemm {
       __syncthreads();
     };
 
-    if constexpr (S == 2) {
-      issue(st0);
-      step_end();
-      for (int t = 0; t < total; ++t) {
-        char* cur = (t & 1) ? st1 : st0;
-        char* nxt = (t & 1) ? st0 : st1;
-        if (t + 1 < total) issue(nxt);
-        compute(cur);
-        step_end();
-      }
-    } else {
-      auto buf = [&](int i) __attribute__((always_inline)) {
-        return i == 0 ? st0 : i == 1 ? st1 : (S == 3 || i == 2) ? st2 : st3;
-      };
-      const int pre = total < S - 1 ? total : S - 1;
-      for (int p = 0; p < pre; ++p) issue(buf(p));
-      int bc = 0, bi = S - 1;  // buffers of the step computed and of the step issued
-      for (int t = 0; t < total; ++t) {
-        if (t + S - 2 < total) wait_vm_lgkm0<DMA_STEP * (S - 2)>();
-        else wait_vm_lgkm0<0>();
-        block_barrier();
-        if (t + S - 1 < total) issue(buf(bi));
-        compute(buf(bc));
-        bc = bc == S - 1 ? 0 : bc + 1;
-        bi = bi == S - 1 ? 0 : bi + 1;
-      }
-      // the epilogue may reuse stage buffer 0
+    issue(st0);
+    step_end();
+    for (int t = 0; t < total; ++t) {
+      char* cur = (t & 1) ? st1 : st0;
+      char* nxt = (t & 1) ? st0 : st1;
+      if (t + 1 < total) issue(nxt);
+      compute(cur);
       step_end();
     }
   }
 
   // Visit every accumulator element owned by this thread:
   //   f(tm, tn, v, row, col)  with row/col relative to the block tile origin.
-  // Element v of a 32x32 MFMA tile sits at row 8*(v/4) + 4*(lane/32) + v%4, col lane%32.
   template <class F>
   __device__ __forceinline__ void for_each(F f) const {
     const int lane = threadIdx.x & 63;
@@ -492,60 +438,11 @@ struct Gemm {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        if (!owns(tm, tn)) continue;
+      for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = wm0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const int col = wn0 + tn * 32 + (lane & 31);
-          f(tm, tn, v, row, col);
+          f(tm, tn, v, wm0 + tm * 32 + elem_row(v, lane), wn0 + tn * 32 + elem_col(v, lane));
         }
-      }
-  }
-
-  // Sum the K groups' partial tiles (WGK > 1) into the owning group, through red (at least
-  // RED_LDS bytes of LDS that no wave still reads).  Every other group sends its partial
-  // of tile t to slot ((wave_mn TM TN + t) (WGK - 1) + rank), 64 lanes x 64 bytes, each
-  // lane's 16 floats as four 16-byte pieces strided by 1 KB so that a wave's writes and
-  // reads cover whole bank rows.  Contains barriers: call from every thread.
-  __device__ __forceinline__ void reduce(char* red) {
-    if constexpr (WGK > 1) {
-      const int lane = threadIdx.x & 63;
-      const int wk = wave_k(), wmn = wave_mn();
-#pragma unroll
-      for (int p = 0; p < NACC; ++p) {
-        if (p) __syncthreads();   // the previous accumulator's slots have been read
-#pragma unroll
-        for (int t = 0; t < TM * TN; ++t) {
-          const int owner = t % WGK;
-          if (owner == wk) continue;
-          const int rank = (wk - owner - 1 + WGK) % WGK;
-          char* slot = red + ((wmn * TM * TN + t) * (WGK - 1) + rank) * 4096;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 x = {acc[p][t / TN][t % TN][4 * q], acc[p][t / TN][t % TN][4 * q + 1],
-                       acc[p][t / TN][t % TN][4 * q + 2], acc[p][t / TN][t % TN][4 * q + 3]};
-            *reinterpret_cast<f32x4*>(slot + q * 1024 + lane * 16) = x;
-          }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < TM * TN; ++t) {
-          if (t % WGK != wk) continue;
-#pragma unroll
-          for (int rank = 0; rank < WGK - 1; ++rank) {
-            const char* slot = red + ((wmn * TM * TN + t) * (WGK - 1) + rank) * 4096;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 x = *reinterpret_cast<const f32x4*>(slot + q * 1024 + lane * 16);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[p][t / TN][t % TN][4 * q + e] += x[e];
-            }
-          }
-        }
-      }
-      __syncthreads();
-    }
   }
 };
 
@@ -555,13 +452,11 @@ struct Gemm {
 #define GEMM_LDS(G) GEMM_LDS_EPI(G, G::STORE_LDS)
 // the same with the first buffer large enough for an epilogue that needs EPI bytes
 #define GEMM_LDS_EPI(G, EPI)                                                                  \
-  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::S0_MIN > (EPI) ? G::S0_MIN : (EPI)]; \
+  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::STAGE > (EPI) ? G::STAGE : (EPI)]; \
   __shared__ __attribute__((aligned(1024))) char gemm_st1_[G::STAGE];                         \
-  __shared__ __attribute__((aligned(1024))) char gemm_st2_[G::S > 2 ? G::STAGE : 16];         \
-  __shared__ __attribute__((aligned(1024))) char gemm_st3_[G::S > 3 ? G::STAGE : 16];         \
   char* const smem = gemm_st0_
 // the stage buffers GEMM_LDS declares, as Gemm::run takes them
-#define GEMM_STAGES gemm_st0_, gemm_st1_, gemm_st2_, gemm_st3_
+#define GEMM_STAGES gemm_st0_, gemm_st1_
 
 // ------------------------------------------------------------------------ block order
 // Workgroups of a launch are handed to the 8 XCDs round-robin by linear id, and each XCD
@@ -596,10 +491,11 @@ constexpr int store_lds_bytes() {
   return MAXP * (MODE == TILE_BOTH ? 2 : 1) * G::TBM * (G::TBN + 8) * 2;
 }
 
-template <class G, int MODE, int MAXP>
-__device__ __forceinline__ void store_planes(const f32x16 (&v)[G::TM][G::TN], char* smem,
-                                             const PlaneBuf& dst, int z, int row0, int col0,
-                                             int rlim, int clim) {
+// store_planes with the plane count NP fixed, P planes per pass.
+template <class G, int MODE, int NP, int P>
+__device__ __forceinline__ void store_planes_n(const f32x16 (&v)[G::TM][G::TN], char* smem,
+                                               const PlaneBuf& dst, int z, int row0, int col0,
+                                               int rlim, int clim) {
   constexpr int TBM = G::TBM, TBN = G::TBN, LD = TBN + 8;
   constexpr int NO = MODE == TILE_BOTH ? 2 : 1;    // staged orientations
   constexpr int REG = TBM * LD;                    // elements per staged region
@@ -608,35 +504,58 @@ __device__ __forceinline__ void store_planes(const f32x16 (&v)[G::TM][G::TN], ch
   u16* t = reinterpret_cast<u16*>(smem);
   const int lane = threadIdx.x & 63;
   const int wm0 = G::wm0(), wn0 = G::wn0();
-#pragma unroll 1
-  for (int q0 = 0; q0 < dst.np; q0 += MAXP) {
-    const int nq = dst.np - q0 < MAXP ? dst.np - q0 : MAXP;
+#pragma unroll
+  for (int q0 = 0; q0 < NP; q0 += P) {
+    const int nq = NP - q0 < P ? NP - q0 : P;
     __syncthreads();
 #pragma unroll
     for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
       for (int tn = 0; tn < G::TN; ++tn)
 #pragma unroll
-        for (int vi = 0; vi < 16; ++vi) {
-          if (!G::owns(tm, tn)) continue;
-          const int r = wm0 + tm * 32 + 8 * (vi >> 2) + 4 * (lane >> 5) + (vi & 3);
-          const int c = wn0 + tn * 32 + (lane & 31);
-          float x = v[tm][tn][vi];
-          for (int i = 0; i < q0; ++i) x -= bf2f(f2bf(x));   // planes of earlier passes
+        for (int g = 0; g < 4; ++g) {
+          // elements 4g .. 4g + 3: four consecutive columns of one row (SW) or four
+          // consecutive rows of one column
+          float x[4];
 #pragma unroll
-          for (int qq = 0; qq < MAXP; ++qq) {
-            if (qq < nq) {
-              const u16 h = f2bf(x);
-              x -= bf2f(h);
-              u16* tq = t + qq * NO * REG;
-              if (MODE == TILE_NORMAL) {
-                tq[r * LD + c] = h;
-              } else if (MODE == TILE_BOTH) {
-                tq[r * LD + c] = h;
-                tq[REG + c * LD + r] = h;
-              } else if (r <= c) {
-                tq[r * LD + c] = h;
-                tq[c * LD + r] = h;
+          for (int e = 0; e < 4; ++e) {
+            x[e] = v[tm][tn][4 * g + e];
+            for (int i = 0; i < q0; ++i) x[e] -= bf2f(f2bf(x[e]));   // earlier passes' planes
+          }
+          const int r = wm0 + tm * 32 + G::elem_row(4 * g, lane);
+          const int c = wn0 + tn * 32 + G::elem_col(4 * g, lane);
+#pragma unroll
+          for (int qq = 0; qq < P; ++qq) {
+            if (qq >= nq) continue;
+            u16 h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              h[e] = f2bf(x[e]);
+              x[e] -= bf2f(h[e]);
+            }
+            u16* tq = t + qq * NO * REG;
+            if constexpr (G::SW && MODE != TILE_SYM) {
+              uint2 w;
+              w.x = h[0] | ((uint32_t)h[1] << 16);
+              w.y = h[2] | ((uint32_t)h[3] << 16);
+              *reinterpret_cast<uint2*>(tq + r * LD + c) = w;
+              if (MODE == TILE_BOTH) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tq[REG + (c + e) * LD + r] = h[e];
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int re = G::SW ? r : r + e, ce = G::SW ? c + e : c;
+                if (MODE == TILE_NORMAL) {
+                  tq[re * LD + ce] = h[e];
+                } else if (MODE == TILE_BOTH) {
+                  tq[re * LD + ce] = h[e];
+                  tq[REG + ce * LD + re] = h[e];
+                } else if (re <= ce) {
+                  tq[re * LD + ce] = h[e];
+                  tq[ce * LD + re] = h[e];
+                }
               }
             }
           }
@@ -659,6 +578,19 @@ __device__ __forceinline__ void store_planes(const f32x16 (&v)[G::TM][G::TN], ch
     }
   }
   __syncthreads();
+}
+
+// The plane count of dst (the same for the whole block) picks the store_planes_n
+// instance, whose per-element work then has no plane-count branches.
+template <class G, int MODE, int MAXP>
+__device__ __forceinline__ void store_planes(const f32x16 (&v)[G::TM][G::TN], char* smem,
+                                             const PlaneBuf& dst, int z, int row0, int col0,
+                                             int rlim, int clim) {
+  if (dst.np == 1) store_planes_n<G, MODE, 1, 1>(v, smem, dst, z, row0, col0, rlim, clim);
+  else if (dst.np == 2)
+    store_planes_n<G, MODE, 2, (MAXP < 2 ? MAXP : 2)>(v, smem, dst, z, row0, col0, rlim, clim);
+  else if (dst.np == 3)
+    store_planes_n<G, MODE, 3, (MAXP < 3 ? MAXP : 3)>(v, smem, dst, z, row0, col0, rlim, clim);
 }
 
 // one plane per pass: the least LDS (the Gemm's STORE_LDS)

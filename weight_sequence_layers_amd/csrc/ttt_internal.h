@@ -153,7 +153,5 @@ hipError_t prepare_kernels();  // raise dynamic-LDS limits once per process
 // tile sizes used by the contraction and Newton-Schulz stages (the host sizes buffers)
 constexpr int CONTRACT_BM = 128, CONTRACT_BN = 128;
 int ns_tri_tiles(int M, int tile);
-// tile edge of the Gram and polynomial stages (symmetric outputs, upper tiles only)
-constexpr int NS_SYM_TILE = 64;
 
 }  // namespace ttt

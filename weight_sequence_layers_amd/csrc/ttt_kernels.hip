@@ -19,7 +19,11 @@
 namespace ttt {
 
 // ------------------------------------------------------------------------ elementwise math
-__device__ __forceinline__ float sigm(float z) { return 1.f / (1.f + __expf(-z)); }
+// logistic function; the hardware reciprocal (about 1 ulp) in place of an IEEE division,
+// whose fix-up sequence dominated the gradient front's epilogue
+__device__ __forceinline__ float sigm(float z) {
+  return __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
 __device__ __forceinline__ float gelu_f(float z) {
   return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
 }
@@ -50,12 +54,13 @@ struct FrontShape {
   static constexpr int NP = NB;
 };
 
-template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK, int S>
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   using FS = FrontShape<FW, MODE>;
   constexpr int NA = FS::NA, NB = FS::NB;
-  // the inner-product loss reads W2 [dim][hidden] column-wise for V W2
-  using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0, 0, BK, S>;
+  // the inner-product loss reads W2 [dim][hidden] column-wise for V W2; the epilogue
+  // stores planes only, which the swapped accumulator layout packs
+  using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0, 0, BK, true>;
   GEMM_LDS(G);
   // two planes per store pass where the stage buffer already has room for them
   constexpr int SP = G::STAGE >= store_lds_bytes<G, TILE_NORMAL, 2>() ? 2 : 1;
@@ -67,7 +72,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   G g;
   g.zero();
   g.run(a.A, a.B, m0, n0, z, a.K, GEMM_STAGES);
-  g.reduce(smem);
 
   const float* eta = a.eta + (int64_t)z * a.eta_zstride;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
@@ -139,7 +143,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   G g;
   g.zero();
   g.run(&a.a, &a.b, m0, n0, z, a.K, GEMM_STAGES);
-  g.reduce(smem);
 
   const int cl = min(BN, a.N - n0);
   const int rn = min(BM, a.nrows - m0);
@@ -202,9 +205,9 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 }
 
 // ------------------------------------------------------------------------ contraction
-template <int BM, int BN, int WGM, int WGN, int WGK>
-__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_contract(ContractArgs a) {
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1, 0, 64, 2, WGK>;   // both operands token-major
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1>;   // both operands token-major
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
@@ -214,7 +217,6 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_contract(ContractArgs 
   G g;
   g.zero();
   g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, GEMM_STAGES);
-  g.reduce(smem);
 
   const int M = a.M, N = a.N;
   const int64_t base = (int64_t)zz * M * N;
@@ -261,8 +263,8 @@ __device__ __forceinline__ void tri_tile(int t, int nt, int& ti, int& tj) {
 }
 
 // Store a tile of a symmetric M x M matrix computed at tile (ti, tj), ti <= tj, as planes
-// of the full matrix (the symmetrised diagonal tile, or an upper tile and its mirror), all
-// planes in one pass.
+// of the full matrix (the symmetrised diagonal tile, or an upper tile and its mirror), NP
+// planes per pass.
 template <class G, int NP>
 __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char* smem,
                                           const PlaneBuf& dst, int zz, int m0, int n0, int M,
@@ -274,10 +276,10 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 
 // A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
 // the polynomial stage reads); A planes written for the full symmetric matrix.
-template <int T, int WGM, int WGN, int PL, int BK, int S, int WGK>
-__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, BK, S, WGK>;
-  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, PL>()));
+template <int T, int WGM, int WGN, int PL, int SP>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
+  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
   const int M = a.M;
@@ -290,7 +292,6 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
   G g;
   g.zero();
   g.run(X, X, m0, n0, zz, a.N, GEMM_STAGES);
-  g.reduce(smem);
   float s2 = 1.f;
   if (a.first) {
     const float s = ns_scale(a, zz);
@@ -303,15 +304,15 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
     g.acc[0][i][j][v] = x;
     if (R < M && C < M) a.afp[base + (int64_t)R * M + C] = x;
   });
-  store_sym<G, PL>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
+  store_sym<G, SP>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
 // B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
 // a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
-template <int T, int WGM, int WGN, int PL, int BK, int S, int WGK>
-__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, BK, S, WGK>;
-  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, PL>()));
+template <int T, int WGM, int WGN, int PL, int SP>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
+  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
   const int M = a.M;
@@ -324,7 +325,6 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
   G g;
   g.zero();
   g.run(Ao, Ao, m0, n0, zz, M, GEMM_STAGES);
-  g.reduce(smem);
   const int64_t base = (int64_t)zz * M * M;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
@@ -334,14 +334,14 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
           (R == C ? a.coef_a : 0.f);
     g.acc[0][i][j][v] = x;
   });
-  store_sym<G, PL>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
+  store_sym<G, SP>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
-template <int T, int WGM, int WGN, int PL, int BK, int S, int SP, int WGK>
-__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
-  // X [M][N] read column-wise
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, S, WGK>;
+template <int T, int WGM, int WGN, int PL, int BK, int SP>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
+  // X [M][N] read column-wise; swapped accumulator layout for packed plane stores
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, true>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_NORMAL, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
@@ -357,7 +357,6 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
   G g;
   g.zero();
   g.run(Ao, Bo, m0, n0, zz, M, GEMM_STAGES);
-  g.reduce(smem);
   const float sc = a.first ? ns_scale(a, zz) : 1.f;
   const int64_t base = (int64_t)zz * M * N;
   const int m = zz / a.P;
@@ -434,13 +433,12 @@ __global__ __launch_bounds__(256) void k_split(SplitArgs a) {
 // dynamic LDS.
 static constexpr int LDS_MAX = 160 * 1024;
 
-template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK = 64, int S = 2>
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK = 64>
 static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
   using FS = FrontShape<FW, MODE>;
-  using G =
-      Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB, 0, FS::DOT ? (1 << (FS::NB - 1)) : 0, 0, BK, S>;
+  using G = Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB, 0, FS::DOT ? (1 << (FS::NB - 1)) : 0, 0, BK>;
   FrontArgs a = a0;
-  auto kern = k_front<BM, BN, WGM, WGN, FW, MODE, BK, S>;
+  auto kern = k_front<BM, BN, WGM, WGN, FW, MODE, BK>;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
@@ -489,10 +487,10 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 }
 
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
-  constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN, WGM = 2, WGN = 4, WGK = 1;
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1, 0, 64, 2, WGK>;
+  constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
+  using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;
   ContractArgs a = a0;
-  auto kern = k_contract<BM, BN, WGM, WGN, WGK>;
+  auto kern = k_contract<BM, BN, 2, 4>;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   if (a.tiles == 0 || a.P == 0) return hipSuccess;
@@ -505,28 +503,28 @@ int ns_tri_tiles(int M, int tile) {
   return t * (t + 1) / 2;
 }
 
-// One Newton-Schulz stage (0 Gram, 1 polynomial, 2 update) on T x T tiles of
-// WGM x WGN x WGK waves, K steps of BK through S stages; the update stores SP planes per
-// pass.
+// One Newton-Schulz stage (0 Gram, 1 polynomial, 2 update) on T x T tiles of WGM x WGN
+// waves, storing SP planes per pass; the update steps K by BK.
 template <int T, int STAGE, int PL, int WGM = 2, int WGN = (T >= 128 ? 4 : 2), int BK = 64,
-          int S = 2, int SP = PL, int WGK = 1>
+          int SP = PL>
 static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
   NsArgs a = a0;
   if (a.Z == 0) return hipSuccess;
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, STAGE == 2 ? (1 << PL) - 1 : 0, PL, BK, S, WGK>;
   if constexpr (STAGE == 2) {
+    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T, WGM, WGN, PL, BK, S, SP, WGK>;
+    auto kern = k_ns_update<T, WGM, WGN, PL, BK, SP>;
     hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
   } else {
+    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
     a.tiles = ns_tri_tiles(a.M, T);
     const dim3 grid(a.tiles * a.Z);
     if constexpr (STAGE == 0) {
-      auto kern = k_ns_gram<T, WGM, WGN, PL, BK, S, WGK>;
+      auto kern = k_ns_gram<T, WGM, WGN, PL, SP>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     } else {
-      auto kern = k_ns_poly<T, WGM, WGN, PL, BK, S, WGK>;
+      auto kern = k_ns_poly<T, WGM, WGN, PL, SP>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     }
   }
@@ -534,19 +532,31 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
 }
 
 // the plane count of the iteration's operands picks the plane-resident instantiation
-template <int T, int STAGE, int WGM = 2, int WGN = (T >= 128 ? 4 : 2), int WGK = 1>
+template <int T, int STAGE>
 static hipError_t ns_planes(const NsArgs& a, int np, hipStream_t s) {
-  if (np == 1) return ns_t<T, STAGE, 1, WGM, WGN, 64, 2, 1, WGK>(a, s);
-  if (np == 2) return ns_t<T, STAGE, 2, WGM, WGN, 64, 2, 2, WGK>(a, s);
-  if (np == 3) return ns_t<T, STAGE, 3, WGM, WGN, 64, 2, 3, WGK>(a, s);
+  if (np == 1) return ns_t<T, STAGE, 1>(a, s);
+  if (np == 2) return ns_t<T, STAGE, 2>(a, s);
+  if (np == 3) return ns_t<T, STAGE, 3>(a, s);
   return hipErrorInvalidValue;
 }
 
+// The Gram and polynomial stages take 128x128 upper tiles (eight waves, one plane per
+// store pass) when the operands have at most two planes and the launch has enough such
+// tiles to cover most CUs; else 64x64 upper tiles.
+static bool ns_sym_wide(const NsArgs& a, int np) {
+  return np <= 2 && (int64_t)ns_tri_tiles(a.M, 128) * a.Z >= 192;
+}
 hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) {
-  return ns_planes<NS_SYM_TILE, 0>(a, a.xin.np, s);
+  const int np = a.xin.np;
+  if (ns_sym_wide(a, np))
+    return np == 1 ? ns_t<128, 0, 1, 2, 4, 64, 1>(a, s) : ns_t<128, 0, 2, 2, 4, 64, 1>(a, s);
+  return ns_planes<64, 0>(a, np, s);
 }
 hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
-  return ns_planes<NS_SYM_TILE, 1>(a, a.ain.np, s);
+  const int np = a.ain.np;
+  if (ns_sym_wide(a, np))
+    return np == 1 ? ns_t<128, 1, 1, 2, 4, 64, 1>(a, s) : ns_t<128, 1, 2, 2, 4, 64, 1>(a, s);
+  return ns_planes<64, 1>(a, np, s);
 }
 // The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs)
 // and the operands have at most two planes (three would not fit LDS); else 64x64 tiles.
@@ -557,7 +567,7 @@ hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
   const int64_t big = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.Z;
   if (a.ain.np != a.xin.np) return hipErrorInvalidValue;
   if (big < 512 || a.xin.np > 2) return ns_planes<64, 2>(a, a.xin.np, s);
-  return a.xin.np == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2, 2, 4, 32, 2, 1>(a, s);
+  return a.xin.np == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2, 2, 4, 32, 1>(a, s);
 }
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
