@@ -162,6 +162,8 @@ struct ttt_state {
   float *fa = nullptr, *fb = nullptr;                  // MSE: derivative factors
   float* G = nullptr;     // [nm][P][d][n]
   float* part = nullptr;  // [nm*P][contract tiles]
+  float* gpart = nullptr; // token-split partial sums [ksplit][nm][P][d][n]
+  int ksplit = 1;
   u16 *xpl[2] = {}, *apl = nullptr, *bpl = nullptr;
   float* afp = nullptr;
   int* health = nullptr;
@@ -221,6 +223,8 @@ size_t layout(ttt_state* s, char* base) {
   size_t oG = C.take<float>(D.nm * P * d * n);
   const int ctiles = (int)(((d + CONTRACT_BM - 1) / CONTRACT_BM) * ((n + CONTRACT_BN - 1) / CONTRACT_BN));
   size_t opart = C.take<float>(D.nm * P * ctiles);
+  const int ksp = contract_split_max(ctiles, (int)(D.nm * P));
+  size_t ogp = ksp > 1 ? C.take<float>(ksp * D.nm * P * d * n) : 0;
   size_t ox[2] = {0, 0}, oa = 0, ob = 0, oafp = 0;
   if (c.ns_steps > 0) {
     for (int i = 0; i < 2; ++i) ox[i] = C.take<u16>(D.npm * D.nm * P * d * n);
@@ -259,6 +263,8 @@ size_t layout(ttt_state* s, char* base) {
     s->G = F(oG);
     s->part = F(opart);
     s->contract_tiles = ctiles;
+    s->ksplit = ksp;
+    s->gpart = ksp > 1 ? F(ogp) : nullptr;
     if (c.ns_steps > 0) {
       for (int i = 0; i < 2; ++i) s->xpl[i] = H(ox[i]);
       s->apl = H(oa); s->bpl = H(ob); s->afp = F(oafp);
@@ -490,6 +496,9 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
   if (ca.muon) ca.x = pbuf(s->xpl[0], D.nlp, Z * d * D.n, (int64_t)d * D.n, D.n);
   ca.part = s->part;
   ca.U = s->U;
+  ca.gpart = s->gpart;
+  ca.gpart_stride = (int64_t)D.nm * P * d * D.n;
+  ca.ksplit = s->ksplit;
   ca.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
   // operands of one launch share a plane count per side: group the matrices accordingly
   int m0 = 0;
@@ -499,6 +508,7 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     ContractArgs cg = ca;
     for (int m = m0; m < m1; ++m) { cg.a[m - m0] = ca.a[m]; cg.b[m - m0] = ca.b[m]; }
     cg.G = s->G + (int64_t)m0 * P * d * D.n;
+    if (s->gpart) cg.gpart = s->gpart + (int64_t)m0 * P * d * D.n;
     cg.U = s->U + (int64_t)m0 * P * d * D.n;
     if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
     cg.part = s->part + (int64_t)m0 * P * s->contract_tiles;

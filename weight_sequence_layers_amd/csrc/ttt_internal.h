@@ -77,6 +77,14 @@ struct ContractArgs {
   float* part;     // [nm*P][tiles]
   float* U;        // plain step: U in weight orientation [nm][P][rows][cols]
   int tr_mask;     // bit m: matrix m's weight is the transpose of its X orientation
+  // Token split: with ksplit > 1 the launch sums ksplit token ranges of kchunk tokens in
+  // separate workgroups, which write partial tiles to gpart [ksplit][nm][P][M][N] (splits
+  // gpart_stride elements apart); a second kernel adds them and applies the epilogue.
+  // The caller sets ksplit to the capacity of gpart; launch_contract picks the split.
+  float* gpart;
+  int64_t gpart_stride;
+  int ksplit, kchunk;
+  int nz;          // nm * P of the launch (set by launch_contract)
 };
 
 // Newton-Schulz stages on Z = nm*P matrices X [M x N] (M <= N).
@@ -140,6 +148,9 @@ struct SmallArgs {
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s);
 hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s);
 hipError_t launch_contract(const ContractArgs& a, int nm, hipStream_t s);
+// token ranges a contraction of `tiles` output tiles per matrix over nz matrices may split
+// into (the host sizes the partial-sum buffer with it)
+int contract_split_max(int tiles, int nz);
 hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s);

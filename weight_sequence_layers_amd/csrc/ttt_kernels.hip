@@ -209,17 +209,28 @@ template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1>;   // both operands token-major
   GEMM_LDS(G);
+  // logical block order (token range, matrix and problem, tile)
   const int lid = xcd_block(blockIdx.x, gridDim.x);
-  const int zz = lid / a.tiles, tile = lid % a.tiles;
+  const int tile = lid % a.tiles, zk = lid / a.tiles;
+  const int zz = zk % a.nz, ks = zk / a.nz;
   const int m = zz / a.P, p = zz % a.P;
   const int m0 = (tile / a.tiles_n) * BM;
   const int n0 = (tile % a.tiles_n) * BN;
+  // this workgroup's token range: the operands' token-major rows k0 ..
+  Operand A = a.a[m], B = a.b[m];
+  const int k0 = ks * a.kchunk;
+  A.p += (int64_t)k0 * A.ld;
+  B.p += (int64_t)k0 * B.ld;
   G g;
   g.zero();
-  g.run(&a.a[m], &a.b[m], m0, n0, p, a.K, GEMM_STAGES);
+  g.run(&A, &B, m0, n0, p, min(a.kchunk, a.K - k0), GEMM_STAGES);
 
   const int M = a.M, N = a.N;
   const int64_t base = (int64_t)zz * M * N;
+  // a token range's partial tile goes to its slice of gpart, with no epilogue
+  const bool split = a.ksplit > 1;
+  float* const gout = split ? a.gpart + ks * a.gpart_stride : a.G;
+  const bool accum = !split && a.accum_in, last = !split && a.last;
   const int tr = (a.tr_mask >> m) & 1;
   float ss = 0.f;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
@@ -227,9 +238,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
     float x = g.acc[0][i][j][v];
     if (row < M && col < N) {
       const int64_t off = base + (int64_t)row * N + col;
-      if (a.accum_in) x += a.G[off];
-      if (!a.last) {
-        a.G[off] = x;
+      if (accum) x += a.G[off];
+      if (!last) {
+        gout[off] = x;
       } else if (a.muon) {
         ss += x * x;
       } else {
@@ -238,10 +249,80 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
     }
     g.acc[0][i][j][v] = x;
   });
-  if (a.last && a.muon) {
+  if (last && a.muon) {
     const int rl = min(BM, M - m0), cl = min(BN, N - n0);
     store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.x, zz, m0, n0, rl, cl);
     const float t = block_sum(ss, reinterpret_cast<float*>(smem));
+    if (threadIdx.x == 0) a.part[(int64_t)zz * a.tiles + tile] = t;
+  }
+}
+
+// Second pass of a token-split contraction: one workgroup per output tile adds the
+// ksplit partial tiles and applies the same epilogue as k_contract (the running sum in G,
+// or the X0 planes with the tile's sum of squares, or U).  Each thread takes runs of 8
+// columns (N is a multiple of 16).
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void k_contract_sum(ContractArgs a) {
+  __shared__ float red[4];
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int zz = lid / a.tiles, tile = lid % a.tiles;
+  const int m = zz / a.P;
+  const int m0 = (tile / a.tiles_n) * BM;
+  const int n0 = (tile % a.tiles_n) * BN;
+  const int M = a.M, N = a.N;
+  const int64_t base = (int64_t)zz * M * N;
+  const int tr = (a.tr_mask >> m) & 1;
+  float ss = 0.f;
+  for (int gi = threadIdx.x; gi < BM * BN / 8; gi += 256) {
+    const int row = m0 + gi / (BN / 8), col = n0 + (gi % (BN / 8)) * 8;
+    if (row >= M || col >= N) continue;
+    const int64_t off = base + (int64_t)row * N + col;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int k = 0; k < a.ksplit; ++k) {
+      const float4* src = reinterpret_cast<const float4*>(a.gpart + k * a.gpart_stride + off);
+      const float4 u = src[0], w = src[1];
+      x[0] += u.x; x[1] += u.y; x[2] += u.z; x[3] += u.w;
+      x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
+    }
+    if (a.accum_in) {
+      const float4* src = reinterpret_cast<const float4*>(a.G + off);
+      const float4 u = src[0], w = src[1];
+      x[0] += u.x; x[1] += u.y; x[2] += u.z; x[3] += u.w;
+      x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
+    }
+    if (!a.last) {
+      float4* dst = reinterpret_cast<float4*>(a.G + off);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+    } else if (a.muon) {
+      u16 h[8][3];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ss += x[e] * x[e];
+        split_planes(x[e], a.x.np, h[e]);
+      }
+      for (int q = 0; q < a.x.np; ++q) {
+        uint4 w;
+        w.x = h[0][q] | ((uint32_t)h[1][q] << 16);
+        w.y = h[2][q] | ((uint32_t)h[3][q] << 16);
+        w.z = h[4][q] | ((uint32_t)h[5][q] << 16);
+        w.w = h[6][q] | ((uint32_t)h[7][q] << 16);
+        *reinterpret_cast<uint4*>(a.x.base + q * a.x.plane_stride + (int64_t)zz * a.x.zstride +
+                                  (int64_t)row * a.x.ld + col) = w;
+      }
+    } else if (tr) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a.U[base + (int64_t)(col + e) * M + row] = x[e];
+    } else {
+      float4* dst = reinterpret_cast<float4*>(a.U + off);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+  }
+  if (a.last && a.muon) {
+    const float t = block_sum(ss, red);
     if (threadIdx.x == 0) a.part[(int64_t)zz * a.tiles + tile] = t;
   }
 }
@@ -486,6 +567,16 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
   return out_m<DH_MSE>(a, Z, s);
 }
 
+// Token ranges: enough for about two workgroups per CU (256 CUs) when the output tiles
+// alone are fewer, at most 8, each range at least 256 tokens.
+constexpr int CONTRACT_SLOTS = 512, CONTRACT_SPLIT_MAX = 8, CONTRACT_RANGE_MIN = 256;
+
+int contract_split_max(int tiles, int nz) {
+  const int64_t wgs = (int64_t)tiles * nz;
+  if (wgs <= 0) return 1;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(CONTRACT_SPLIT_MAX, CONTRACT_SLOTS / wgs));
+}
+
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
   using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;
@@ -493,8 +584,17 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   auto kern = k_contract<BM, BN, 2, 4>;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
-  if (a.tiles == 0 || a.P == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(a.tiles * nm * a.P), dim3(G::NT), 0, s, a);
+  a.nz = nm * a.P;
+  if (a.tiles == 0 || a.nz == 0 || a.K <= 0) return hipSuccess;
+  int ks = std::min(a.gpart ? a.ksplit : 1, contract_split_max(a.tiles, a.nz));
+  ks = std::max(1, std::min(ks, a.K / CONTRACT_RANGE_MIN));
+  a.kchunk = ks > 1 ? (((a.K + ks - 1) / ks + 63) / 64) * 64 : a.K;
+  a.ksplit = (a.K + a.kchunk - 1) / a.kchunk;
+  hipLaunchKernelGGL(kern, dim3(a.tiles * a.nz * a.ksplit), dim3(G::NT), 0, s, a);
+  if (a.ksplit > 1) {
+    auto sum = k_contract_sum<BM, BN>;
+    hipLaunchKernelGGL(sum, dim3(a.tiles * a.nz), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
