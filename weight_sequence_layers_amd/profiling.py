@@ -27,11 +27,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 
 # stage name -> pattern of the kernels that implement it
 STAGE_KERNELS = [
-    ("front_q", r"k_front<.*, 0>$"),
-    ("front_k", r"k_front<.*, [12]>$"),
+    # k_front<BM, BN, WGM, WGN, FW, MODE, BK>: MODE 0 applies, 1 and 2 take gradients
+    ("front_q", r"k_front<(\d+, ){5}0, \d+>$"),
+    ("front_k", r"k_front<(\d+, ){5}[12], \d+>$"),
     ("out", r"k_out<.*, 0>$"),
     ("mse", r"k_out<.*, [12]>$"),
-    ("contract", r"k_contract<"),
+    ("contract", r"k_contract(_sum)?<"),
     ("ns_gram", r"k_ns_gram<"),
     ("ns_poly", r"k_ns_poly<"),
     ("ns_update", r"k_ns_update<"),
