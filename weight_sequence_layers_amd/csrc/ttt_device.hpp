@@ -428,6 +428,24 @@ struct Gemm {
     }
   }
 
+  // Swapped layout only: visit this thread's runs of four consecutive columns,
+  //   f(tm, tn, g, row, col): elements 4g .. 4g + 3 of tile (tm, tn) at (row, col .. col + 3)
+  // relative to the block tile origin.
+  template <class F>
+  __device__ __forceinline__ void for_each4(F f) const {
+    static_assert(SW, "runs of columns need the swapped layout");
+    const int lane = threadIdx.x & 63;
+    const int wm0 = this->wm0();
+    const int wn0 = this->wn0();
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          f(tm, tn, g, wm0 + tm * 32 + elem_row(4 * g, lane), wn0 + tn * 32 + elem_col(4 * g, lane));
+  }
+
   // Visit every accumulator element owned by this thread:
   //   f(tm, tn, v, row, col)  with row/col relative to the block tile origin.
   template <class F>

@@ -359,7 +359,8 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 // the polynomial stage reads); A planes written for the full symmetric matrix.
 template <int T, int WGM, int WGN, int PL, int SP>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
+  // swapped accumulator layout: runs of four columns, stored as 16-byte vectors
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, 64, true>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -379,11 +380,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
     s2 = s * s;
   }
   const int64_t base = (int64_t)zz * M * M;
-  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
+  // M is a multiple of 16, so a run of four columns lies wholly inside or outside
+  g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
-    const float x = s2 * g.acc[0][i][j][v];
-    g.acc[0][i][j][v] = x;
-    if (R < M && C < M) a.afp[base + (int64_t)R * M + C] = x;
+    float4 x;
+    x.x = g.acc[0][i][j][4 * q] *= s2;
+    x.y = g.acc[0][i][j][4 * q + 1] *= s2;
+    x.z = g.acc[0][i][j][4 * q + 2] *= s2;
+    x.w = g.acc[0][i][j][4 * q + 3] *= s2;
+    if (R < M && C < M) *reinterpret_cast<float4*>(a.afp + base + (int64_t)R * M + C) = x;
   });
   store_sym<G, SP>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
@@ -392,7 +397,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
 // a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
 template <int T, int WGM, int WGN, int PL, int SP>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
+  // swapped accumulator layout: runs of four columns, read as 16-byte vectors
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, 64, true>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -407,13 +413,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
   g.zero();
   g.run(Ao, Ao, m0, n0, zz, M, GEMM_STAGES);
   const int64_t base = (int64_t)zz * M * M;
-  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
+  g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
-    float x = 0.f;
-    if (R < M && C < M && (ti != tj || R <= C))
-      x = a.coef_b * a.afp[base + (int64_t)R * M + C] + a.coef_c * g.acc[0][i][j][v] +
-          (R == C ? a.coef_a : 0.f);
-    g.acc[0][i][j][v] = x;
+    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (R < M && C < M) A = *reinterpret_cast<const float4*>(a.afp + base + (int64_t)R * M + C);
+    const float av[4] = {A.x, A.y, A.z, A.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = 0.f;
+      if (R < M && C + e < M && (ti != tj || R <= C + e))
+        x = a.coef_b * av[e] + a.coef_c * g.acc[0][i][j][4 * q + e] +
+            (R == C + e ? a.coef_a : 0.f);
+      g.acc[0][i][j][4 * q + e] = x;
+    }
   });
   store_sym<G, SP>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
