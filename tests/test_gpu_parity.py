@@ -46,3 +46,12 @@ def test_ragged_shapes(act, fw, loss, ns, renorm):
 def test_orders(order):
     cfg = ti.Config("ord", 1, 2, 1024, 256, 64, 128, "swiglu", "dot", 5, True, "bf16", order, 7)
     _check(cfg, planes=(1, 2, 2, 2))
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_token_split_contraction(act):
+    # few output tiles and 1000-token chunks: the gradient contraction splits each chunk's
+    # tokens into ranges of 384, 384 and 232 summed by a second pass (ragged last range)
+    cfg = ti.Config("split", 1, 2, 2000, 1000, 64, 128, "swiglu", "dot", 5, True, act,
+                    "apply_then_update", 31)
+    _check(cfg)
