@@ -431,16 +431,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
 }
 
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
-template <int T, int WGM, int WGN, int PL, int BK, int SP>
+template <int BM, int BN, int WGM, int WGN, int PL, int BK, int SP>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
   // X [M][N] read column-wise; swapped accumulator layout for packed plane stores
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, true>;
+  using G = Gemm<BM, BN, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, true>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_NORMAL, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int M = a.M, N = a.N;
-  const int m0 = (tile / a.tiles_n) * T;
-  const int n0 = (tile % a.tiles_n) * T;
+  const int m0 = (tile / a.tiles_n) * BM;
+  const int n0 = (tile % a.tiles_n) * BN;
   Operand Ao[PL], Bo[PL];   // B' planes; X [M][N] planes read as their columns
 #pragma unroll
   for (int q = 0; q < PL; ++q) {
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
     g.acc[0][i][j][v] = x;
   });
   if (!a.last) {
-    const int rl = min(T, M - m0), cl = min(T, N - n0);
+    const int rl = min(BM, M - m0), cl = min(BN, N - n0);
     store_planes<G, TILE_NORMAL, SP>(g.acc[0], smem, a.xout, zz, m0, n0, rl, cl);
   }
 }
@@ -626,7 +626,7 @@ static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
     using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T, WGM, WGN, PL, BK, SP>;
+    auto kern = k_ns_update<T, T, WGM, WGN, PL, BK, SP>;
     hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
   } else {
     using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
