@@ -133,8 +133,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
 // ------------------------------------------------------------------------ out / dH
 template <int BM, int BN, int WGM, int WGN, int MODE>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
-  // dH = E W2 reads W2 [dim][hidden] column-wise
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
+  // dH = E W2 reads W2 [dim][hidden] column-wise; the query output (a plane store) takes
+  // the swapped accumulator layout
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0, 0, 64, MODE == OUT_Q>;
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int z = lid / a.tiles, tile = lid % a.tiles;
