@@ -36,12 +36,6 @@ __device__ __forceinline__ void split_planes(float x, int np, u16 out[3]) {
   }
 }
 
-// Plane q of x alone (the same value split_planes puts in out[q]).
-__device__ __forceinline__ u16 plane_of(float x, int q) {
-  float r = x;
-  for (int i = 0; i < q; ++i) r = r - bf2f(f2bf(r));
-  return f2bf(r);
-}
 
 // ------------------------------------------------------------------------ reductions
 __device__ __forceinline__ float wave_sum(float v) {
@@ -208,7 +202,7 @@ template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM
 struct Gemm {
   static constexpr bool SW = SW_;
   static constexpr int NT = WGM * WGN * 64;
-  static constexpr int TBM = BM, TBN = BN, WGN_ = WGN;
+  static constexpr int TBM = BM, TBN = BN;
   static constexpr int STORE_LDS = (BM + 8) * (BN + 8) * 2;
   static constexpr int BK = BK_;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
@@ -221,8 +215,6 @@ struct Gemm {
   static constexpr int STAGE = NA * A_TILE + NB * B_TILE;
   // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffer 1, declared as
   // two separate __shared__ arrays by the kernel (GEMM_LDS)
-  static constexpr int S0_BYTES = STAGE > STORE_LDS ? STAGE : STORE_LDS;
-  static constexpr int LDS_BYTES = S0_BYTES + STAGE;
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
   static_assert(PL == 0 || (NA == PL && NB == PL), "plane-resident mode takes PL planes a side");
   static constexpr int NACC = PL ? 1 : NB;

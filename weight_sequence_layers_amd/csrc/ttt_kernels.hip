@@ -525,7 +525,6 @@ __global__ __launch_bounds__(256) void k_split(SplitArgs a) {
 // ============================================================================ launchers
 // Every GEMM kernel holds its LDS in static __shared__ arrays (GEMM_LDS): launches pass no
 // dynamic LDS.
-static constexpr int LDS_MAX = 160 * 1024;
 
 template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK = 64>
 static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
