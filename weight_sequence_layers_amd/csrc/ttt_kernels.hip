@@ -678,7 +678,9 @@ hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
   const int64_t big = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.Z;
   if (a.ain.np != a.xin.np) return hipErrorInvalidValue;
-  if (big < 512 || a.xin.np > 2) return ns_planes<64, 2>(a, a.xin.np, s);
+  // three planes: 64x64 tiles stepping K by 32 (52 KB of LDS, three workgroups per CU)
+  if (a.xin.np == 3) return ns_t<64, 2, 3, 2, 2, 32, 3>(a, s);
+  if (big < 512) return ns_planes<64, 2>(a, a.xin.np, s);
   return a.xin.np == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2, 2, 4, 32, 1>(a, s);
 }
 
