@@ -55,3 +55,12 @@ def test_token_split_contraction(act):
     cfg = ti.Config("split", 1, 2, 2000, 1000, 64, 128, "swiglu", "dot", 5, True, act,
                     "apply_then_update", 31)
     _check(cfg)
+
+
+def test_wide_tiles_ragged_edges():
+    # 30 (batch, head) problems at dim 144, hidden 288: enough matrices that the Gram,
+    # polynomial and update stages take their 128-wide tiles, whose second tile row and
+    # column hold only 16 of 144 rows (and the hidden tiles 32 of 128)
+    cfg = ti.Config("wide", 10, 3, 256, 128, 144, 288, "swiglu", "dot", 5, True, "bf16",
+                    "apply_then_update", 41)
+    _check(cfg, planes=(1, 2, 2, 2), problems=[(0, 0), (4, 1), (9, 2)])
