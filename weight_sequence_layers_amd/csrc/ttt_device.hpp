@@ -481,6 +481,17 @@ __device__ __forceinline__ int xcd_block(int id, int total) {
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
+// ------------------------------------------------------------------------ LDS barrier
+// Workgroup barrier for LDS reuse: each thread first waits for its own LDS operations only,
+// not for its outstanding global stores (which __syncthreads' release fence would wait
+// for).  The empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------------ tile stores
 // Write one block tile of fp32 values (held in the MFMA accumulator layout of gemm G) as
 // bf16 planes through LDS, so that global stores are 16-byte vectors along the buffer's
@@ -493,7 +504,7 @@ __device__ __forceinline__ int xcd_block(int id, int total) {
 // Up to MAXP planes are staged per pass (each value is split once); more planes take more
 // passes. rlim / clim bound the tile's rows / columns (relative to the tile origin); the
 // limit of the buffer's contiguous dimension must be a multiple of 8. smem needs
-// store_lds_bytes<G, MODE, MAXP>() bytes. Contains __syncthreads: call from every thread.
+// store_lds_bytes<G, MODE, MAXP>() bytes. Contains barriers: call from every thread.
 enum TileMode { TILE_NORMAL = 0, TILE_SYM = 1, TILE_BOTH = 2 };
 
 template <class G, int MODE, int MAXP>
@@ -517,7 +528,7 @@ __device__ __forceinline__ void store_planes_n(const f32x16 (&v)[G::TM][G::TN], 
 #pragma unroll
   for (int q0 = 0; q0 < NP; q0 += P) {
     const int nq = NP - q0 < P ? NP - q0 : P;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int tm = 0; tm < G::TM; ++tm)
 #pragma unroll
@@ -570,7 +581,7 @@ __device__ __forceinline__ void store_planes_n(const f32x16 (&v)[G::TM][G::TN], 
             }
           }
         }
-    __syncthreads();
+    lds_barrier();
     const int total = nq * NO * TBM * CPR;
     for (int ch = threadIdx.x; ch < total; ch += G::NT) {
       const int qq = ch / (NO * TBM * CPR);
@@ -587,7 +598,7 @@ __device__ __forceinline__ void store_planes_n(const f32x16 (&v)[G::TM][G::TN], 
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // The plane count of dst (the same for the whole block) picks the store_planes_n

@@ -196,12 +196,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
 __device__ __forceinline__ float block_sum(float v, float* scratch) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
+  lds_barrier();
   if (lane == 0) scratch[wave] = v;
-  __syncthreads();
+  lds_barrier();
   float t = 0.f;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += scratch[w];
-  __syncthreads();
+  lds_barrier();
   return t;
 }
 
