@@ -498,7 +498,7 @@ __device__ __forceinline__ void lds_barrier() {
 // contiguous dimension.
 //   TILE_NORMAL: element (r, c) of the tile goes to row row0 + r, column col0 + c;
 //   TILE_SYM   : square diagonal tile of a symmetric matrix: only elements with r <= c are
-//                taken, each written to (r, c) and (c, r);
+//                taken, each written to (r, c) and (c, r) (smem as for TILE_BOTH);
 //   TILE_BOTH  : square tile written at (row0 + r, col0 + c) and, transposed, at
 //                (col0 + c, row0 + r) (an off-diagonal tile of a symmetric matrix).
 // Up to MAXP planes are staged per pass (each value is split once); more planes take more
@@ -573,9 +573,13 @@ __device__ __forceinline__ void store_planes_n(const f32x16 (&v)[G::TM][G::TN], 
                 } else if (MODE == TILE_BOTH) {
                   tq[re * LD + ce] = h[e];
                   tq[REG + ce * LD + re] = h[e];
-                } else if (re <= ce) {
-                  tq[re * LD + ce] = h[e];
-                  tq[ce * LD + re] = h[e];
+                } else {
+                  // TILE_SYM: an element below the diagonal writes to this lane's scratch
+                  // word instead (an address select, not a branch)
+                  const bool up = re <= ce;
+                  u16* const scr = t + P * REG + 2 * lane;
+                  *(up ? tq + re * LD + ce : scr) = h[e];
+                  *(up ? tq + ce * LD + re : scr) = h[e];
                 }
               }
             }
