@@ -652,22 +652,22 @@ static hipError_t ns_planes(const NsArgs& a, int np, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// The Gram and polynomial stages take 128x128 upper tiles (eight waves, one plane per
-// store pass) when the operands have at most two planes and the launch has enough such
-// tiles to cover most CUs; else 64x64 upper tiles.
+// The Gram and polynomial stages take 128x128 upper tiles (sixteen waves of 32x32 tiles,
+// four a SIMD, one plane per store pass) when the operands have at most two planes and
+// the launch has enough such tiles to cover most CUs; else 64x64 upper tiles.
 static bool ns_sym_wide(const NsArgs& a, int np) {
   return np <= 2 && (int64_t)ns_tri_tiles(a.M, 128) * a.Z >= 192;
 }
 hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) {
   const int np = a.xin.np;
   if (ns_sym_wide(a, np))
-    return np == 1 ? ns_t<128, 0, 1, 2, 4, 64, 1>(a, s) : ns_t<128, 0, 2, 2, 4, 64, 1>(a, s);
+    return np == 1 ? ns_t<128, 0, 1, 4, 4, 64, 1>(a, s) : ns_t<128, 0, 2, 4, 4, 64, 1>(a, s);
   return ns_planes<64, 0>(a, np, s);
 }
 hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
   const int np = a.ain.np;
   if (ns_sym_wide(a, np))
-    return np == 1 ? ns_t<128, 1, 1, 2, 4, 64, 1>(a, s) : ns_t<128, 1, 2, 2, 4, 64, 1>(a, s);
+    return np == 1 ? ns_t<128, 1, 1, 4, 4, 64, 1>(a, s) : ns_t<128, 1, 2, 4, 4, 64, 1>(a, s);
   return ns_planes<64, 1>(a, np, s);
 }
 // The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs)
