@@ -120,22 +120,37 @@ template <int R, int NT, int BK = 64>
 struct TileLoad {
   static_assert(BK == 64 || BK == 32, "K step of 64 or 32");
   static constexpr int CHUNKS = R * BK / 8;        // 16-byte chunks per tile
-  static constexpr int C = CHUNKS / NT;            // per thread
+  static constexpr int NW = NT / 64;               // waves of the block
+  // PART: fewer chunks than threads; CHUNKS / 64 of the waves load the tile, one chunk a
+  // lane, starting at wave rot (so that the tiles of one step spread over all waves)
+  static constexpr bool PART = CHUNKS < NT;
+  static constexpr int C = PART ? 1 : CHUNKS / NT;  // per thread
   static constexpr int BYTES = R * BK * 2;
-  static_assert(CHUNKS % NT == 0, "uneven tile load");
+  static_assert(PART ? NT % CHUNKS == 0 && CHUNKS % 64 == 0 : CHUNKS % NT == 0,
+                "uneven tile load");
   static_assert(R % 64 == 0, "tile rows must be a multiple of 64");
   uint32_t off[C];   // byte offset of the chunk at k0 = 0, or an out-of-range value
   int kk[C];         // k of the chunk's first element relative to k0
   uint32_t kstride;  // bytes per unit of k0
+  int slice;         // LDS byte offset of this wave's 1 KB slice in round 0 (wave-uniform)
+  bool act;          // whether this wave loads the tile (wave-uniform)
 
   // Chunks go to LDS by direct (DMA) loads, which write lane l of a wave's load to 16 l
-  // bytes past the wave's base: thread t of round c fills LDS chunk p = c NT + t, so it
-  // loads the global chunk that the swizzled layout keeps at p (XOR is its own inverse).
-  __device__ __forceinline__ void init(const Operand& o, int row0, bool col) {
+  // bytes past the wave's base: the wave at loader position w fills LDS chunk
+  // p = c NT + 64 w + lane in round c, so it loads the global chunk that the swizzled
+  // layout keeps at p (XOR is its own inverse).
+  __device__ __forceinline__ void init(const Operand& o, int row0, bool col, int rot = 0) {
+    const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+    const int w = PART ? (wave - rot % NW + NW) % NW : wave;
+    act = !PART || w < CHUNKS / 64;
+    slice = __builtin_amdgcn_readfirstlane(w) * 64 * 16;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const int ch = threadIdx.x + c * NT;
-      if (!col) {
+      const int ch = w * 64 + lane + c * NT;
+      if (!act) {
+        kk[c] = 0;
+        off[c] = 0xC0000000u;
+      } else if (!col) {
         const int r = ch / (BK / 8), kc = (ch % (BK / 8)) ^ swz_row<BK>(r);
         kk[c] = kc * 8;
         off[c] = (row0 + r < o.rows) ? (uint32_t)(((int64_t)(row0 + r) * o.ld + kc * 8) * 2)
@@ -186,6 +201,17 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int 
   }
 }
 
+// ------------------------------------------------------------------------ LDS barrier
+// Workgroup barrier for LDS reuse: each thread first waits for its own LDS operations only,
+// not for its outstanding global stores (which __syncthreads' release fence would wait
+// for).  The empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // PL > 0 selects the plane-resident product: A[0..PL) and B[0..PL) are the bf16 planes of
 // one A and one B (each operand with planes = 1); every K step loads all 2 PL plane tiles
 // once and accumulates the plane products (i, j) with i + j < PL into one accumulator.
@@ -197,16 +223,28 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int row_base, int 
 // feeds the B tile as A, computing the transposed tile: element v then sits at row
 // lane % 32, column 8 (v / 4) + 4 (lane / 32) + v % 4, so each lane holds runs of four
 // consecutive columns, which the tile stores write to LDS four at a time.
+//
+// WGK > 1 splits every K step among WGK groups of WGM x WGN waves (group k takes
+// k-substeps [k, k + 1) BK / 16 / WGK of each step for its whole wave tile), for blocks
+// that would otherwise run too few waves per CU.  reduce() then sums the groups' partial
+// tiles through LDS into one owner per run of four accumulator elements (run g of tile t
+// to group (4 t + g) mod WGK); for_each, for_each4 and the tile stores visit the owned
+// runs only.
 template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0,
-          int BK_ = 64, bool SW_ = false>
+          int BK_ = 64, bool SW_ = false, int WGK_ = 1>
 struct Gemm {
   static constexpr bool SW = SW_;
-  static constexpr int NT = WGM * WGN * 64;
+  static constexpr int WGK = WGK_;
+  static constexpr int NT = WGM * WGN * WGK * 64;
   static constexpr int TBM = BM, TBN = BN;
   static constexpr int STORE_LDS = (BM + 8) * (BN + 8) * 2;
   static constexpr int BK = BK_;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int SPW = BK / 16 / WGK;   // k-substeps of a step per wave
+  static_assert(SPW >= 1 && SPW * 16 * WGK == BK, "K step must split evenly among groups");
+  // LDS the reduction of the groups' partial tiles takes (one accumulator at a time)
+  static constexpr int RED_LDS = WGK > 1 ? BM * BN * 4 * (WGK - 1) : 0;
   using TA = TileLoad<BM, NT, BK>;
   using TB = TileLoad<BN, NT, BK>;
   static constexpr bool acol(int i) { return (LAM >> i) & 1; }
@@ -239,8 +277,20 @@ struct Gemm {
   }
 
   // origin of this wave's tile in the block tile
-  static __device__ __forceinline__ int wm0() { return ((threadIdx.x >> 6) / WGN) * WM; }
-  static __device__ __forceinline__ int wn0() { return ((threadIdx.x >> 6) % WGN) * WN; }
+  // this wave's K group and its place in the WGM x WGN grid
+  static __device__ __forceinline__ int wave_k() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / (WGM * WGN));
+  }
+  static __device__ __forceinline__ int wave_mn() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) % (WGM * WGN));
+  }
+  static __device__ __forceinline__ int wm0() { return (wave_mn() / WGN) * WM; }
+  static __device__ __forceinline__ int wn0() { return (wave_mn() % WGN) * WN; }
+  // whether this wave holds the final value of run g (elements 4g .. 4g + 3) of its tile
+  // (tm, tn) after reduce()
+  static __device__ __forceinline__ bool owns(int tm, int tn, int g) {
+    return WGK == 1 || ((tm * TN + tn) * 4 + g) % WGK == wave_k();
+  }
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -262,7 +312,6 @@ struct Gemm {
   __device__ __forceinline__ void run(const Operand* __restrict__ A,
                                       const Operand* __restrict__ B, int m0, int n0, int z,
                                       int K, char* st0, char* st1) {
-    const int wave = threadIdx.x >> 6;
     const int wm0 = this->wm0();
     const int wn0 = this->wn0();
 
@@ -290,20 +339,17 @@ struct Gemm {
     int na_[NA], nb_[NB];
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      la[i].init(A[i], m0, acol(i));
+      la[i].init(A[i], m0, acol(i), i * (TA::CHUNKS / 64));
       pa_[i] = A[i].p + (int64_t)z * A[i].zstride;
       na_[i] = (int)(!acol(i) ? (int64_t)A[i].rows * A[i].ld * 2 : (int64_t)K * A[i].ld * 2);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      lb[i].init(B[i], n0, bcol(i));
+      lb[i].init(B[i], n0, bcol(i), NA * (TA::CHUNKS / 64) + i * (TB::CHUNKS / 64));
       pb_[i] = B[i].p + (int64_t)z * B[i].zstride;
       nb_[i] = (int)(!bcol(i) ? (int64_t)B[i].rows * B[i].ld * 2 : (int64_t)K * B[i].ld * 2);
     }
 
-    // this wave's 1 KB slice of round c of a tile (wave-uniform, kept in a scalar register
-    // so that the LDS destination is formed with scalar arithmetic)
-    const int wslice = __builtin_amdgcn_readfirstlane(wave) * 64 * 16;
     // Steps that lie wholly inside K move the buffer's base by the step's k offset (scalar
     // arithmetic only, no per-lane work); a partial last step checks each chunk against K.
     // The steps are loaded in order; (sg_n, k0_n) is the next one's segment and k offset.
@@ -325,7 +371,8 @@ struct Gemm {
               (void*)base, (short)0, na_[i] - (int)kb, 0x00020000);
 #pragma unroll
           for (int c = 0; c < TA::C; ++c)
-            dma16(rk, (lds_void_t*)(st + i * A_TILE + c * NT * 16 + wslice), la[i].off[c]);
+            if (la[i].act)
+              dma16(rk, (lds_void_t*)(st + i * A_TILE + c * NT * 16 + la[i].slice), la[i].off[c]);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -335,8 +382,9 @@ struct Gemm {
               (void*)base, (short)0, nb_[i] - (int)kb, 0x00020000);
 #pragma unroll
           for (int c = 0; c < TB::C; ++c)
-            dma16(rk, (lds_void_t*)(st + NA * A_TILE + i * B_TILE + c * NT * 16 + wslice),
-                  lb[i].off[c]);
+            if (lb[i].act)
+              dma16(rk, (lds_void_t*)(st + NA * A_TILE + i * B_TILE + c * NT * 16 + lb[i].slice),
+                    lb[i].off[c]);
         }
       } else {
 #pragma unroll
@@ -346,8 +394,9 @@ struct Gemm {
               (void*)(pa_[i] + qa * A[i].pstride), (short)0, na_[i], 0x00020000);
 #pragma unroll
           for (int c = 0; c < TA::C; ++c)
-            dma16(rs, (lds_void_t*)(st + i * A_TILE + c * NT * 16 + wslice),
-                  (k0 + la[i].kk[c] < K) ? la[i].off[c] + kb : 0xFFFFFFF0u);
+            if (la[i].act)
+              dma16(rs, (lds_void_t*)(st + i * A_TILE + c * NT * 16 + la[i].slice),
+                    (k0 + la[i].kk[c] < K) ? la[i].off[c] + kb : 0xFFFFFFF0u);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -356,14 +405,16 @@ struct Gemm {
               (void*)(pb_[i] + qb * B[i].pstride), (short)0, nb_[i], 0x00020000);
 #pragma unroll
           for (int c = 0; c < TB::C; ++c)
-            dma16(rs, (lds_void_t*)(st + NA * A_TILE + i * B_TILE + c * NT * 16 + wslice),
-                  (k0 + lb[i].kk[c] < K) ? lb[i].off[c] + kb : 0xFFFFFFF0u);
+            if (lb[i].act)
+              dma16(rs, (lds_void_t*)(st + NA * A_TILE + i * B_TILE + c * NT * 16 + lb[i].slice),
+                    (k0 + lb[i].kk[c] < K) ? lb[i].off[c] + kb : 0xFFFFFFF0u);
         }
       }
     };
     auto compute = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
+      for (int ss = 0; ss < SPW; ++ss) {
+        const int s = wave_k() * SPW + ss;
         bf16x8 fa[NA][TM], fb[NB][TN];
 #pragma unroll
         for (int i = 0; i < NA; ++i)
@@ -435,7 +486,9 @@ struct Gemm {
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          f(tm, tn, g, wm0 + tm * 32 + elem_row(4 * g, lane), wn0 + tn * 32 + elem_col(4 * g, lane));
+          if (owns(tm, tn, g))
+            f(tm, tn, g, wm0 + tm * 32 + elem_row(4 * g, lane),
+              wn0 + tn * 32 + elem_col(4 * g, lane));
   }
 
   // Visit every accumulator element owned by this thread:
@@ -451,8 +504,51 @@ struct Gemm {
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          f(tm, tn, v, wm0 + tm * 32 + elem_row(v, lane), wn0 + tn * 32 + elem_col(v, lane));
+          if (owns(tm, tn, v >> 2))
+            f(tm, tn, v, wm0 + tm * 32 + elem_row(v, lane), wn0 + tn * 32 + elem_col(v, lane));
         }
+  }
+
+  // Sum the K groups' partial tiles (WGK > 1) into the owners of their runs, through red
+  // (RED_LDS bytes of LDS that no wave still reads).  A non-owner of run g of tile t sends
+  // it to slot ((wave_mn TM TN + t) 4 + g) (WGK - 1) + rank, 64 lanes x 16 bytes.
+  // Contains barriers: call from every thread.
+  __device__ __forceinline__ void reduce(char* red) {
+    if constexpr (WGK > 1) {
+      const int lane = threadIdx.x & 63;
+      const int wk = wave_k(), wmn = wave_mn();
+#pragma unroll
+      for (int p = 0; p < NACC; ++p) {
+        if (p) lds_barrier();   // the previous accumulator's slots have been read
+#pragma unroll
+        for (int t = 0; t < TM * TN; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int owner = (t * 4 + g) % WGK;
+            if (owner == wk) continue;
+            const int rank = (wk - owner - 1 + WGK) % WGK;
+            char* slot = red + (((wmn * TM * TN + t) * 4 + g) * (WGK - 1) + rank) * 1024;
+            const f32x16& a = acc[p][t / TN][t % TN];
+            *reinterpret_cast<f32x4*>(slot + lane * 16) =
+                f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          }
+        lds_barrier();
+#pragma unroll
+        for (int t = 0; t < TM * TN; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            if ((t * 4 + g) % WGK != wk) continue;
+#pragma unroll
+            for (int rank = 0; rank < WGK - 1; ++rank) {
+              const char* slot = red + (((wmn * TM * TN + t) * 4 + g) * (WGK - 1) + rank) * 1024;
+              const f32x4 x = *reinterpret_cast<const f32x4*>(slot + lane * 16);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[p][t / TN][t % TN][4 * g + e] += x[e];
+            }
+          }
+      }
+      lds_barrier();
+    }
   }
 };
 
@@ -462,7 +558,10 @@ struct Gemm {
 #define GEMM_LDS(G) GEMM_LDS_EPI(G, G::STORE_LDS)
 // the same with the first buffer large enough for an epilogue that needs EPI bytes
 #define GEMM_LDS_EPI(G, EPI)                                                                  \
-  __shared__ __attribute__((aligned(1024))) char gemm_st0_[G::STAGE > (EPI) ? G::STAGE : (EPI)]; \
+  __shared__ __attribute__((aligned(1024)))                                                    \
+  char gemm_st0_[(G::STAGE > G::RED_LDS ? G::STAGE : G::RED_LDS) > (EPI)                      \
+                     ? (G::STAGE > G::RED_LDS ? G::STAGE : G::RED_LDS)                        \
+                     : (EPI)];                                                                \
   __shared__ __attribute__((aligned(1024))) char gemm_st1_[G::STAGE];                         \
   char* const smem = gemm_st0_
 // the stage buffers GEMM_LDS declares, as Gemm::run takes them
@@ -479,17 +578,6 @@ __device__ __forceinline__ int xcd_block(int id, int total) {
   const int q = total / NUM_XCD, r = total % NUM_XCD;
   const int x = id % NUM_XCD, j = id / NUM_XCD;
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
-}
-
-// ------------------------------------------------------------------------ LDS barrier
-// Workgroup barrier for LDS reuse: each thread first waits for its own LDS operations only,
-// not for its outstanding global stores (which __syncthreads' release fence would wait
-// for).  The empty asm statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maximum
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 // ------------------------------------------------------------------------ tile stores
@@ -535,6 +623,7 @@ __device__ __forceinline__ void store_planes_n(const f32x16 (&v)[G::TM][G::TN], 
       for (int tn = 0; tn < G::TN; ++tn)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+          if (!G::owns(tm, tn, g)) continue;
           // elements 4g .. 4g + 3: four consecutive columns of one row (SW) or four
           // consecutive rows of one column
           float x[4];

@@ -358,10 +358,10 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
 
 // A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
 // the polynomial stage reads); A planes written for the full symmetric matrix.
-template <int T, int WGM, int WGN, int PL, int SP>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
+template <int T, int WGM, int WGN, int PL, int SP, int WGK>
+__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
   // swapped accumulator layout: runs of four columns, stored as 16-byte vectors
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, 64, true>;
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, 64, true, WGK>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -375,6 +375,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
   G g;
   g.zero();
   g.run(X, X, m0, n0, zz, a.N, GEMM_STAGES);
+  g.reduce(smem);
   float s2 = 1.f;
   if (a.first) {
     const float s = ns_scale(a, zz);
@@ -396,10 +397,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_gram(NsArgs a) {
 
 // B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
 // a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
-template <int T, int WGM, int WGN, int PL, int SP>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
+template <int T, int WGM, int WGN, int PL, int SP, int WGK>
+__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
   // swapped accumulator layout: runs of four columns, read as 16-byte vectors
-  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, 64, true>;
+  using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, 64, true, WGK>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_BOTH, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles;
@@ -413,6 +414,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
   G g;
   g.zero();
   g.run(Ao, Ao, m0, n0, zz, M, GEMM_STAGES);
+  g.reduce(smem);
   const int64_t base = (int64_t)zz * M * M;
   g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
@@ -432,10 +434,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_poly(NsArgs a) {
 }
 
 // X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
-template <int BM, int BN, int WGM, int WGN, int PL, int BK, int SP>
-__global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
+template <int BM, int BN, int WGM, int WGN, int PL, int BK, int SP, int WGK>
+__global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
   // X [M][N] read column-wise; swapped accumulator layout for packed plane stores
-  using G = Gemm<BM, BN, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, true>;
+  using G = Gemm<BM, BN, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, true, WGK>;
   GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_NORMAL, SP>()));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
@@ -451,6 +453,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_ns_update(NsArgs a) {
   G g;
   g.zero();
   g.run(Ao, Bo, m0, n0, zz, M, GEMM_STAGES);
+  g.reduce(smem);
   const float sc = a.first ? ns_scale(a, zz) : 1.f;
   const int64_t base = (int64_t)zz * M * N;
   const int m = zz / a.P;
@@ -618,25 +621,25 @@ int ns_tri_tiles(int M, int tile) {
 // One Newton-Schulz stage (0 Gram, 1 polynomial, 2 update) on T x T tiles of WGM x WGN
 // waves, storing SP planes per pass; the update steps K by BK.
 template <int T, int STAGE, int PL, int WGM = 2, int WGN = (T >= 128 ? 4 : 2), int BK = 64,
-          int SP = PL>
+          int SP = PL, int WGK = 1>
 static hipError_t ns_t(const NsArgs& a0, hipStream_t s) {
   NsArgs a = a0;
   if (a.Z == 0) return hipSuccess;
   if constexpr (STAGE == 2) {
-    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK>;
+    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, true, WGK>;
     a.tiles_n = (a.N + T - 1) / T;
     a.tiles = ((a.M + T - 1) / T) * a.tiles_n;
-    auto kern = k_ns_update<T, T, WGM, WGN, PL, BK, SP>;
+    auto kern = k_ns_update<T, T, WGM, WGN, PL, BK, SP, WGK>;
     hipLaunchKernelGGL(kern, dim3(a.tiles * a.Z), dim3(G::NT), 0, s, a);
   } else {
-    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL>;
+    using G = Gemm<T, T, WGM, WGN, PL, PL, 0, 0, PL, 64, true, WGK>;
     a.tiles = ns_tri_tiles(a.M, T);
     const dim3 grid(a.tiles * a.Z);
     if constexpr (STAGE == 0) {
-      auto kern = k_ns_gram<T, WGM, WGN, PL, SP>;
+      auto kern = k_ns_gram<T, WGM, WGN, PL, SP, WGK>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     } else {
-      auto kern = k_ns_poly<T, WGM, WGN, PL, SP>;
+      auto kern = k_ns_poly<T, WGM, WGN, PL, SP, WGK>;
       hipLaunchKernelGGL(kern, grid, dim3(G::NT), 0, s, a);
     }
   }
@@ -654,22 +657,25 @@ static hipError_t ns_planes(const NsArgs& a, int np, hipStream_t s) {
 
 // The Gram and polynomial stages take 128x128 upper tiles (sixteen waves of 32x32 tiles,
 // four a SIMD, one plane per store pass) when the operands have at most two planes and
-// the launch has enough such tiles to cover most CUs; else 64x64 upper tiles.
+// the launch has enough such tiles to cover most CUs.  Else they take 64x64 upper tiles
+// on eight waves: two groups of 2 x 2 waves, each group taking half of every K step,
+// whose partial tiles are summed through LDS before the epilogue (such launches have
+// fewer workgroups than CUs, so each workgroup's time is the stage's time).
 static bool ns_sym_wide(const NsArgs& a, int np) {
   return np <= 2 && (int64_t)ns_tri_tiles(a.M, 128) * a.Z >= 192;
 }
-hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) {
-  const int np = a.xin.np;
+template <int STAGE>
+static hipError_t ns_sym(const NsArgs& a, int np, hipStream_t s) {
   if (ns_sym_wide(a, np))
-    return np == 1 ? ns_t<128, 0, 1, 4, 4, 64, 1>(a, s) : ns_t<128, 0, 2, 4, 4, 64, 1>(a, s);
-  return ns_planes<64, 0>(a, np, s);
+    return np == 1 ? ns_t<128, STAGE, 1, 4, 4, 64, 1>(a, s)
+                   : ns_t<128, STAGE, 2, 4, 4, 64, 1>(a, s);
+  if (np == 1) return ns_t<64, STAGE, 1, 2, 2, 64, 1, 2>(a, s);
+  if (np == 2) return ns_t<64, STAGE, 2, 2, 2, 64, 2, 2>(a, s);
+  if (np == 3) return ns_t<64, STAGE, 3, 2, 2, 64, 3, 2>(a, s);
+  return hipErrorInvalidValue;
 }
-hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
-  const int np = a.ain.np;
-  if (ns_sym_wide(a, np))
-    return np == 1 ? ns_t<128, 1, 1, 4, 4, 64, 1>(a, s) : ns_t<128, 1, 2, 4, 4, 64, 1>(a, s);
-  return ns_planes<64, 1>(a, np, s);
-}
+hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_sym<0>(a, a.xin.np, s); }
+hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_sym<1>(a, a.ain.np, s); }
 // The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs)
 // and the operands have at most two planes (three would not fit LDS); else 64x64 tiles.
 // With two planes the 128x128 kernel steps K by 32 and stores one plane per pass, which
