@@ -243,14 +243,24 @@ struct Gemm {
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int SPW = BK / 16 / WGK;   // k-substeps of a step per wave
   static_assert(SPW >= 1 && SPW * 16 * WGK == BK, "K step must split evenly among groups");
-  // LDS the reduction of the groups' partial tiles takes (one accumulator at a time)
-  static constexpr int RED_LDS = WGK > 1 ? BM * BN * 4 * (WGK - 1) : 0;
   using TA = TileLoad<BM, NT, BK>;
   using TB = TileLoad<BN, NT, BK>;
   static constexpr bool acol(int i) { return (LAM >> i) & 1; }
   static constexpr bool bcol(int i) { return (LBM >> i) & 1; }
   static constexpr int A_TILE = TA::BYTES, B_TILE = TB::BYTES;
   static constexpr int STAGE = NA * A_TILE + NB * B_TILE;
+  // The reduction of the groups' partial tiles (WGK > 1) runs one accumulator at a time,
+  // in RED_R rounds over each wave's 32 x 32 tiles, so that a round's slots fit in
+  // max(STAGE, 32 KB) where whole accumulators would not.
+  static constexpr int RED_FULL = WGK > 1 ? BM * BN * 4 * (WGK - 1) : 0;
+  static constexpr int red_rounds() {
+    const int cap = STAGE > 32768 ? STAGE : 32768;
+    int r = 1;
+    while (r < TM * TN && ((TM * TN) % r != 0 || RED_FULL / r > cap)) ++r;
+    return r;
+  }
+  static constexpr int RED_R = red_rounds();
+  static constexpr int RED_LDS = RED_FULL / RED_R;   // LDS the reduction takes
   // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffer 1, declared as
   // two separate __shared__ arrays by the kernel (GEMM_LDS)
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
@@ -510,43 +520,49 @@ struct Gemm {
   }
 
   // Sum the K groups' partial tiles (WGK > 1) into the owners of their runs, through red
-  // (RED_LDS bytes of LDS that no wave still reads).  A non-owner of run g of tile t sends
-  // it to slot ((wave_mn TM TN + t) 4 + g) (WGK - 1) + rank, 64 lanes x 16 bytes.
+  // (RED_LDS bytes of LDS that no wave still reads).  In the round that covers tile t (t
+  // counted over the wave's TM x TN tiles), a non-owner of run g sends it to slot
+  // ((wave_mn TPR + t mod TPR) 4 + g) (WGK - 1) + rank, 64 lanes x 16 bytes.
   // Contains barriers: call from every thread.
   __device__ __forceinline__ void reduce(char* red) {
     if constexpr (WGK > 1) {
+      constexpr int TPR = TM * TN / RED_R;   // tiles per round
       const int lane = threadIdx.x & 63;
       const int wk = wave_k(), wmn = wave_mn();
 #pragma unroll
-      for (int p = 0; p < NACC; ++p) {
-        if (p) lds_barrier();   // the previous accumulator's slots have been read
+      for (int p = 0; p < NACC; ++p)
 #pragma unroll
-        for (int t = 0; t < TM * TN; ++t)
+        for (int rr = 0; rr < RED_R; ++rr) {
+          if (p || rr) lds_barrier();   // the previous round's slots have been read
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int owner = (t * 4 + g) % WGK;
-            if (owner == wk) continue;
-            const int rank = (wk - owner - 1 + WGK) % WGK;
-            char* slot = red + (((wmn * TM * TN + t) * 4 + g) * (WGK - 1) + rank) * 1024;
-            const f32x16& a = acc[p][t / TN][t % TN];
-            *reinterpret_cast<f32x4*>(slot + lane * 16) =
-                f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-          }
-        lds_barrier();
+          for (int tt = 0; tt < TPR; ++tt)
 #pragma unroll
-        for (int t = 0; t < TM * TN; ++t)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            if ((t * 4 + g) % WGK != wk) continue;
-#pragma unroll
-            for (int rank = 0; rank < WGK - 1; ++rank) {
-              const char* slot = red + (((wmn * TM * TN + t) * 4 + g) * (WGK - 1) + rank) * 1024;
-              const f32x4 x = *reinterpret_cast<const f32x4*>(slot + lane * 16);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[p][t / TN][t % TN][4 * g + e] += x[e];
+            for (int g = 0; g < 4; ++g) {
+              const int t = rr * TPR + tt;
+              const int owner = (t * 4 + g) % WGK;
+              if (owner == wk) continue;
+              const int rank = (wk - owner - 1 + WGK) % WGK;
+              char* slot = red + (((wmn * TPR + tt) * 4 + g) * (WGK - 1) + rank) * 1024;
+              const f32x16& a = acc[p][t / TN][t % TN];
+              *reinterpret_cast<f32x4*>(slot + lane * 16) =
+                  f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
             }
-          }
-      }
+          lds_barrier();
+#pragma unroll
+          for (int tt = 0; tt < TPR; ++tt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int t = rr * TPR + tt;
+              if ((t * 4 + g) % WGK != wk) continue;
+#pragma unroll
+              for (int rank = 0; rank < WGK - 1; ++rank) {
+                const char* slot = red + (((wmn * TPR + tt) * 4 + g) * (WGK - 1) + rank) * 1024;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(slot + lane * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[p][t / TN][t % TN][4 * g + e] += x[e];
+              }
+            }
+        }
       lds_barrier();
     }
   }
