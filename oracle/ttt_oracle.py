@@ -28,14 +28,18 @@ extraction, so the formulas below are the plain forms the pages describe in word
 Readings where the pages are silent (each one is listed in the design notes):
 * loss of a chunk S: inner product  L = -sum_{t in S} eta_t <f_W(k_t), v_t>,  or
   MSE  L = sum_{t in S} eta_t ||f_W(k_t) - v_t||^2  (no 1/2, no 1/d, no 1/|S|);
-* one eta per token, shared by all fast-weight matrices; no extra step size, no
-  momentum, no weight decay; the update is W <- W - U with U the gradient (SGD) or
-  its 5-step Newton-Schulz orthogonalisation (Muon) -- no momentum or post-scale;
+* one eta per token, shared by all fast-weight matrices; no momentum; the update is
+  W <- (1 - lambda) W - lr_i U with U the gradient (SGD) or its 5-step Newton-Schulz
+  orthogonalisation (Muon), lr_i a step size per matrix (default 1: the step the pages
+  describe) and lambda a weight decay (default 0) -- [Modular TTT] names the learning
+  rate and the weight decay as design dimensions of the inner learner, and [LaCT] §4.2
+  suggests a smaller Muon step when the loss oscillates; the decay scales the state
+  before the step, and the row renorm's reference is the norm before decay and step;
 * Newton-Schulz: X = G / (||G||_F + 1e-7), transposed to the wide orientation,
   5 x { A = X X^T ; B = b A + c A^2 ; X = a X + B X } with the quintic coefficients
   (a, b, c) = (3.4445, -4.7750, 2.0315) published with the Muon optimiser;
-* row renorm: after W' = W - U every row of every matrix is rescaled to the L2 norm
-  that row had before the update; a row whose new norm is 0 is left as it is;
+* row renorm: after W' = (1 - lambda) W - lr U every row of every matrix is rescaled to
+  the L2 norm that row had before the update; a row whose new norm is 0 is left as it is;
 * shifted block-causal: chunk c's queries see the state after chunks 0..c-1 and the
   last chunk's update is still made; the image-set order updates first, then applies;
 * SwiGLU  f(x) = W2 (silu(W1 x) * (W3 x));  GELU-MLP  f(x) = W2 gelu(W1 x) with the
@@ -195,12 +199,16 @@ def renorm_rows(W_prev: np.ndarray, W_new: np.ndarray) -> np.ndarray:
     return W_new * scale[:, None]
 
 
-def update_state(Ws, grads, ns_steps: int, renorm: bool) -> List[np.ndarray]:
-    """W <- W - U per matrix, U = NS5(g) under Muon else g; then the optional row renorm."""
+def update_state(Ws, grads, ns_steps: int, renorm: bool, lr: Optional[Sequence[float]] = None,
+                 weight_decay: float = 0.0) -> List[np.ndarray]:
+    """W <- (1 - weight_decay) W - lr_i U per matrix, U = NS5(g) under Muon else g
+    ([LaCT] §2.2.1; step size and weight decay as in [Modular TTT]); then the optional
+    row renorm against the norms of W before this update."""
     out = []
-    for W, g in zip(Ws, grads):
+    steps = [1.0] * len(Ws) if lr is None else list(lr)
+    for W, g, step in zip(Ws, grads, steps):
         U = newton_schulz5(g, ns_steps) if ns_steps > 0 else g
-        W_new = W - U
+        W_new = (1.0 - weight_decay) * W - step * U
         out.append(renorm_rows(W, W_new) if renorm else W_new)
     return out
 
@@ -241,7 +249,7 @@ def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
         if cfg.order == APPLY_THEN_UPDATE:
             apply(lo, hi)
         g = chunk_gradient(cfg.fw, cfg.loss, Ws, K[lo:hi], V[lo:hi], eta[lo:hi], block_rows)
-        Ws = update_state(Ws, g, cfg.ns_steps, cfg.renorm)
+        Ws = update_state(Ws, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
         if cfg.order == UPDATE_THEN_APPLY:
             apply(lo, hi)
     return O, Ws
@@ -292,7 +300,8 @@ def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta):
                 grads[0] += np.outer((W2.T @ e) * gelu_prime(z), k)
             else:
                 grads[0] += np.outer(e, k)
-        Ws = update_state(Ws, grads, cfg.ns_steps, cfg.renorm)
+        Ws = update_state(Ws, grads, cfg.ns_steps, cfg.renorm, cfg.step_sizes(),
+                          cfg.weight_decay)
         if cfg.order == UPDATE_THEN_APPLY:
             for t in range(c * b, (c + 1) * b):
                 O[t] = f(np.asarray(Q[t], np.float64))

@@ -102,8 +102,9 @@ def test_activations_match_torch():
 
 # ------------------------------------------------------------------ whole-loop pins
 def _cfg(fw="swiglu", loss="dot", ns=0, renorm=False, order="apply_then_update", chunk=3,
-         d=4, dh=8, T=9):
-    return Config("t", 1, 1, T, chunk, d, dh, fw, loss, ns, renorm, "f32", order)
+         d=4, dh=8, T=9, lr=(), wd=0.0):
+    return Config("t", 1, 1, T, chunk, d, dh, fw, loss, ns, renorm, "f32", order,
+                  lr=tuple(lr), weight_decay=wd)
 
 
 def _rand_problem(cfg, rng, wscale=0.5):
@@ -290,6 +291,94 @@ def test_sequence_renorm_keeps_initial_norms():
         assert np.abs(a - b).max() > 1e-3   # the state did move
 
 
+# ------------------------------------------------------------------ step size, weight decay
+def linear_dot_step_closed_form_error(order="apply_then_update", chunk=4, T=16, d=5, seed=12,
+                                      lr=0.37, wd=0.15):
+    """Linear fast weight, inner-product loss, no Muon, no norm, with step size lr and
+    weight decay wd: the chunk gradient is -sum_t eta_t v_t k_t^T in closed form, so the
+    state after chunk c is (1 - wd) W_c + lr sum_t eta_t v_t k_t^T, summed token by
+    token here."""
+    cfg = _cfg("linear", "dot", 0, False, order, chunk=chunk, d=d, T=T, lr=(lr,), wd=wd)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(seed))
+    O, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    W = Ws[0].copy()
+    err = 0.0
+    for c in range(T // chunk):
+        S = slice(c * chunk, (c + 1) * chunk)
+        step = np.zeros_like(W)
+        for t in range(c * chunk, (c + 1) * chunk):
+            step += eta[t] * np.outer(V[t], K[t])
+        Wn = (1.0 - wd) * W + lr * step
+        ref = Q[S] @ (W if order == "apply_then_update" else Wn).T
+        err = max(err, np.abs(O[S] - ref).max())
+        W = Wn
+    return max(err, np.abs(Wf[0] - W).max())
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+@pytest.mark.parametrize("lr,wd", [(0.37, 0.15), (2.0, 0.0), (1.0, 0.5)])
+def test_linear_dot_step_size_and_decay_closed_form(order, lr, wd):
+    assert linear_dot_step_closed_form_error(order, lr=lr, wd=wd) <= 1e-12
+
+
+@pytest.mark.parametrize("fw,loss", [("swiglu", "dot"), ("gelu", "mse")])
+@pytest.mark.parametrize("ns", [0, 5])
+def test_decay_alone_is_a_power(fw, loss, ns):
+    """eta = 0 makes every gradient (and its orthogonalisation) zero, so with no renorm
+    n chunks leave exactly (1 - wd)^n W0."""
+    wd = 0.05
+    cfg = _cfg(fw, loss, ns, False, chunk=3, T=12, lr=(0.7, 1.3, 0.2), wd=wd)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(21))
+    _, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, np.zeros_like(eta))
+    for a, b in zip(Wf, Ws):
+        assert np.abs(a - (1.0 - wd) ** 4 * b).max() <= 1e-15 * np.abs(b).max()
+
+
+def test_decay_alone_is_undone_by_renorm():
+    """With the row renorm, a pure decay (eta = 0) is rescaled back to the norms before
+    the step: the state does not move."""
+    cfg = _cfg("swiglu", "dot", 5, True, chunk=3, T=12, wd=0.3)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(22))
+    _, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, np.zeros_like(eta))
+    for a, b in zip(Wf, Ws):
+        assert np.abs(a - b).max() <= 1e-14 * np.abs(b).max()
+
+
+@pytest.mark.parametrize("fw,loss", [("swiglu", "dot"), ("gelu", "mse"), ("swiglu", "mse")])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_uniform_step_size_equals_scaled_eta_without_muon(fw, loss, renorm):
+    """Without Muon the step is lr times a gradient that is linear in eta, so step size c
+    with eta is the same run as step size 1 with c eta."""
+    c = 0.35
+    cfg = _cfg(fw, loss, 0, renorm, chunk=3, T=12, d=4, dh=6, lr=(c, c, c))
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(23))
+    O1, W1 = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    O2, W2 = orc.sequence_forward(cfg.replace(lr=()), Ws, Q, K, V, c * eta)
+    assert np.abs(O1 - O2).max() <= 1e-12 * np.abs(O2).max()
+    for a, b in zip(W1, W2):
+        assert np.abs(a - b).max() <= 1e-12 * np.abs(b).max()
+
+
+def muon_step_band(lr=(0.3, 0.5, 2.0), seed=24):
+    """Muon with step sizes and no norm, one chunk: (W0 - W1) / lr_i is the orthogonalised
+    gradient, whose singular values lie in the Newton-Schulz band [0.68, 1.21] whatever
+    the gradient's scale (the step size multiplies the orthogonalised step, it is not
+    normalised away). Returns the extreme singular values over the matrices."""
+    cfg = _cfg("swiglu", "dot", 5, False, chunk=32, T=32, d=8, dh=16, lr=lr)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(seed))
+    _, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    lo, hi = np.inf, 0.0
+    for a, b, step in zip(Wf, Ws, lr):
+        S = np.linalg.svd((b - a) / step, compute_uv=False)
+        lo, hi = min(lo, S.min()), max(hi, S.max())
+    return lo, hi
+
+
+def test_muon_step_size_scales_the_orthogonalised_step():
+    lo, hi = muon_step_band()
+    assert lo > 0.68 and hi < 1.21
+
+
 # ------------------------------------------------------------------ mutation tests
 def _all_pins_pass():
     try:
@@ -312,6 +401,9 @@ def _all_pins_pass_inner():
     Wn = W + np.random.default_rng(2).standard_normal((5, 7))
     R = orc.renorm_rows(W, Wn)
     checks.append(np.abs(np.linalg.norm(R, axis=1) - np.linalg.norm(W, axis=1)).max() < 1e-14)
+    checks.append(linear_dot_step_closed_form_error("apply_then_update") <= 1e-12)
+    lo, hi = muon_step_band()
+    checks.append(lo > 0.68 and hi < 1.21)
     return all(checks)
 
 
@@ -363,6 +455,28 @@ def _mut_block_grad_transposed(fw, loss, Ws, K, V, eta):  # g2 = H^T E instead o
 _ORIG_BLOCK = orc._block_gradient
 
 
+def _mut_decay_after_step(Ws, grads, ns_steps, renorm, lr=None, weight_decay=0.0):
+    # the decay applied to the stepped state instead of before the step
+    steps = [1.0] * len(Ws) if lr is None else list(lr)
+    out = []
+    for W, g, step in zip(Ws, grads, steps):
+        U = orc.newton_schulz5(g, ns_steps) if ns_steps > 0 else g
+        W_new = (1.0 - weight_decay) * (W - step * U)
+        out.append(orc.renorm_rows(W, W_new) if renorm else W_new)
+    return out
+
+
+def _mut_step_before_ns(Ws, grads, ns_steps, renorm, lr=None, weight_decay=0.0):
+    # the step size applied to the gradient before the orthogonalisation
+    steps = [1.0] * len(Ws) if lr is None else list(lr)
+    out = []
+    for W, g, step in zip(Ws, grads, steps):
+        U = orc.newton_schulz5(step * g, ns_steps) if ns_steps > 0 else step * g
+        W_new = (1.0 - weight_decay) * W - U
+        out.append(orc.renorm_rows(W, W_new) if renorm else W_new)
+    return out
+
+
 @pytest.mark.parametrize("name,target,mut", [
     ("silu' term", "silu_prime", _mut_silu_prime),
     ("error sign", "_output_error", _mut_output_error),
@@ -370,6 +484,8 @@ _ORIG_BLOCK = orc._block_gradient
     ("NS transpose", "newton_schulz5", _mut_ns_transpose),
     ("renorm target", "renorm_rows", _mut_renorm),
     ("g2 index", "_block_gradient", _mut_block_grad_transposed),
+    ("decay after the step", "update_state", _mut_decay_after_step),
+    ("step size before NS", "update_state", _mut_step_before_ns),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, target, mut):
     monkeypatch.setattr(orc, target, mut)

@@ -21,7 +21,7 @@ Distributions (the workloads' stated inputs):
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -47,6 +47,14 @@ class Config:
     act: str = "f32"    # 'f32' | 'bf16'
     order: str = "apply_then_update"  # | 'update_then_apply'
     seed: int = 1000
+    lr: Tuple[float, ...] = ()   # step size per matrix (state order); () or 0 entries: 1
+    weight_decay: float = 0.0    # decay of the state per chunk, in [0, 1)
+
+    def step_sizes(self) -> List[float]:
+        """The step size of each matrix, defaults filled in."""
+        n = len(self.matrix_names())
+        lr = list(self.lr) + [0.0] * (n - len(self.lr))
+        return [x if x != 0 else 1.0 for x in lr[:n]]
 
     @property
     def n_chunks(self) -> int:
