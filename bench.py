@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lm")
     ap.add_argument("--planes", default=None, help="apply,grad,ns,ns_lead bf16 plane counts")
+    ap.add_argument("--lr", default=None,
+                    help="comma-separated step sizes per matrix (state order); default 1")
+    ap.add_argument("--weight-decay", type=float, default=0.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chunks", type=int, default=None)
     ap.add_argument("--blas-reference", action="store_true",
@@ -188,6 +191,9 @@ def main():
     from weight_sequence_layers_amd.profiling import source_digest
 
     cfg = ti.CONFIGS[args.workload]
+    if args.lr or args.weight_decay:
+        cfg = cfg.replace(lr=tuple(float(x) for x in (args.lr or "").split(",") if x),
+                          weight_decay=args.weight_decay)
     planes = tuple(int(x) for x in args.planes.split(",")) if args.planes else W.PRECISION[cfg.name]
     c = W.make_config(cfg, planes=planes)
     torch.cuda.set_device(0)
@@ -273,7 +279,9 @@ def main():
                                f"{cfg.hidden}, {cfg.fw}/{cfg.loss}, ns {cfg.ns_steps}, renorm "
                                f"{int(cfg.renorm)}, {cfg.act}, {cfg.order}",
                    "global_batch": cfg.batch, "seq_len": cfg.seq_len, "parallelism": "none",
-                   "bf16_planes_apply_grad_ns_nslead": list(planes)},
+                   "bf16_planes_apply_grad_ns_nslead": list(planes),
+                   **({"lr": list(cfg.step_sizes()), "weight_decay": cfg.weight_decay}
+                      if (cfg.lr or cfg.weight_decay) else {})},
         "source_digest": source_digest(),
         "layer_tflops_algorithmic": round(tf_layer, 2),
         "pct_bf16_peak_algorithmic": round(100 * tf_layer / PEAK_BF16_TFLOPS, 2),

@@ -101,6 +101,16 @@ typedef struct {
   int32_t row_renorm; /* 0 or 1 */
   int32_t apply_planes, grad_planes, ns_planes, ns_lead_planes;
   int32_t path;       /* ttt_path */
+  /* Step.  Per chunk every matrix i of the state becomes (1 - weight_decay) W_i - lr[i] U_i
+   * (U_i the summed gradient, or its Newton-Schulz orthogonalisation), then the optional
+   * row renorm rescales each row to its norm before the step.  lr[i] is indexed in the
+   * state's matrix order (SwiGLU W1, W3, W2; GELU W1, W2; linear W); 0 selects 1, and
+   * entries past the net's matrices are ignored.  Each lr[i] must be finite and >= 0;
+   * weight_decay finite and in [0, 1).  Zero-initialised fields give the plain step
+   * W <- W - U.  (Modular TTT: learning rate and weight decay as design dimensions of the
+   * inner learner; LaCT §4.2: a smaller Muon step when the loss oscillates.)            */
+  float lr[3];
+  float weight_decay;
 } ttt_config;
 
 /* Host-only check of a configuration (no HIP call).  TTT_OK or the first problem found. */

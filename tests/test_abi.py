@@ -59,6 +59,23 @@ def test_invalid_configs_rejected(kw, code):
     assert e.value.status == code and len(str(e.value)) > 12
 
 
+@pytest.mark.parametrize("kw,ok", [
+    (dict(lr=(0.5, 2.0, 0.0)), True), (dict(lr=(0.0,)), True), (dict(weight_decay=0.0), True),
+    (dict(weight_decay=0.999), True), (dict(lr=(1.0, -0.1)), False),
+    (dict(lr=(float("nan"),)), False), (dict(lr=(1.0, 1.0, float("inf"))), False),
+    (dict(weight_decay=1.0), False), (dict(weight_decay=-1e-3), False),
+    (dict(weight_decay=float("nan")), False),
+])
+def test_step_size_and_decay_checked(kw, ok):
+    assert _status(_cfg(**kw)) == (0 if ok else 4), kw
+
+
+def test_step_size_fields_reach_the_struct():
+    c = _cfg(lr=(0.25, 0.5), weight_decay=0.125)
+    assert list(c.lr) == [0.25, 0.5, 0.0] and c.weight_decay == 0.125
+    assert ctypes.sizeof(W.ttt_config) == 16 * 4 + 4 * 4
+
+
 def test_plane_counts_checked():
     c = _cfg()
     c.grad_planes = 4

@@ -64,3 +64,17 @@ def test_wide_tiles_ragged_edges():
     cfg = ti.Config("wide", 10, 3, 256, 128, 144, 288, "swiglu", "dot", 5, True, "bf16",
                     "apply_then_update", 41)
     _check(cfg, planes=(1, 2, 2, 2), problems=[(0, 0), (4, 1), (9, 2)])
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("fw,loss,ns,renorm,lr,wd", [
+    ("swiglu", "dot", 5, True, (0.5, 1.5, 0.8), 0.05),
+    ("swiglu", "mse", 0, False, (0.7, 0.4, 1.3), 0.1),
+    ("gelu", "mse", 0, False, (0.6, 1.7), 0.02),
+    ("linear", "dot", 0, False, (0.3,), 0.2),
+])
+def test_step_size_and_weight_decay(act, fw, loss, ns, renorm, lr, wd):
+    # per-matrix step sizes and a weight decay: W <- (1 - wd) W - lr_i U, then the renorm
+    cfg = ti.Config("step", 2, 2, 600, 200, 80, 176, fw, loss, ns, renorm, act,
+                    "apply_then_update", 77, lr=lr, weight_decay=wd)
+    _check(cfg)

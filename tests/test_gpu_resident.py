@@ -35,6 +35,9 @@ def _resident(cfg, inp, **kw):
     ("mse chunk 17", {"chunk": 17, "seq_len": 17 * 9}),
     ("dot loss chunk 64", {"loss": "dot"}),
     ("one problem, one chunk", {"batch": 1, "heads": 1, "seq_len": 64}),
+    ("mse, step sizes and decay", {"lr": (0.5, 1.8), "weight_decay": 0.03}),
+    ("dot, step sizes and decay", {"loss": "dot", "lr": (2.0, 0.25), "weight_decay": 0.1,
+                                   "chunk": 33, "seq_len": 33 * 7}),
 ])
 def test_resident_parity(name, kw):
     cfg = BASE.replace(**kw)

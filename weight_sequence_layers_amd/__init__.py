@@ -45,7 +45,8 @@ class TTTError(RuntimeError):
 class ttt_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order", "ns_steps",
-        "row_renorm", "apply_planes", "grad_planes", "ns_planes", "ns_lead_planes", "path")]
+        "row_renorm", "apply_planes", "grad_planes", "ns_planes", "ns_lead_planes", "path")
+    ] + [("lr", ctypes.c_float * 3), ("weight_decay", ctypes.c_float)]
 
 
 _lib = None
@@ -94,14 +95,18 @@ PATH = {"auto": 0, "staged": 1, "resident": 2}
 
 def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
     """ttt_config from an object with the workload fields (batch, heads, dim, hidden, chunk,
-    fw, loss, act, order, ns_steps, renorm), overridden by keyword arguments. `planes` is
-    (apply, grad, ns, ns_lead); by default the preset of the workload's name, else 0s.
-    `path` is "auto", "staged" or "resident"."""
+    fw, loss, act, order, ns_steps, renorm and optionally lr, weight_decay), overridden by
+    keyword arguments. `planes` is (apply, grad, ns, ns_lead); by default the preset of
+    the workload's name, else 0s. `path` is "auto", "staged" or "resident". `lr` is a
+    sequence of up to 3 step sizes in the state's matrix order (0 or missing: 1)."""
     f = {}
     if cfg is not None:
         for k in ("batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order",
                   "ns_steps", "renorm"):
             f[k] = getattr(cfg, k)
+        for k in ("lr", "weight_decay"):
+            if hasattr(cfg, k):
+                f[k] = getattr(cfg, k)
         if planes is None:
             planes = PRECISION.get(getattr(cfg, "name", ""), None)
     f.update(kw)
@@ -118,6 +123,12 @@ def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
     c.apply_planes, c.grad_planes, c.ns_planes, c.ns_lead_planes = (int(p) for p in planes)
     path = f.get("path", "auto")
     c.path = PATH[path] if isinstance(path, str) else int(path)
+    lr = list(f.get("lr", ()) or ())
+    if len(lr) > 3:
+        raise ValueError("at most 3 step sizes")
+    for i, x in enumerate(lr):
+        c.lr[i] = float(x)
+    c.weight_decay = float(f.get("weight_decay", 0.0))
     return c
 
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -85,6 +86,13 @@ ttt_status resolve(const ttt_config* c, ttt_config* out) {
   }
   if (r.path < TTT_PATH_AUTO || r.path > TTT_PATH_RESIDENT)
     return fail(TTT_E_CONFIG, "unknown path %d", r.path);
+  for (int i = 0; i < 3; ++i) {
+    if (!std::isfinite(r.lr[i]) || r.lr[i] < 0.f)
+      return fail(TTT_E_CONFIG, "lr[%d] must be finite and >= 0 (got %g)", i, (double)r.lr[i]);
+    if (r.lr[i] == 0.f) r.lr[i] = 1.f;
+  }
+  if (!std::isfinite(r.weight_decay) || r.weight_decay < 0.f || r.weight_decay >= 1.f)
+    return fail(TTT_E_CONFIG, "weight_decay must be in [0, 1) (got %g)", (double)r.weight_decay);
   const bool resident_ok =
       small_supported(r.fw == TTT_FW_MLP_GELU ? FW_GELU : -1, r.ns_steps, r.row_renorm,
                       r.act == TTT_BF16, r.order == TTT_APPLY_THEN_UPDATE, r.dim, r.hidden,
@@ -306,12 +314,14 @@ ttt_status refresh_planes(ttt_state* s, bool with_update, hipStream_t st) {
   const Dims& D = s->D;
   RenormArgs r{};
   r.P = D.P; r.np = D.wp; r.renorm = with_update && s->cfg.row_renorm; r.nm = D.nm;
+  r.keep = 1.f - s->cfg.weight_decay;
   r.health = s->health;
   r.max_rows = 0;
   for (int m = 0; m < D.nm; ++m) {
     RenormMat& M = r.m[m];
     M.W = s->Wm[m];
     M.U = with_update ? s->Um[m] : nullptr;
+    M.lr = s->cfg.lr[m];
     M.rows = D.rows[m]; M.cols = D.cols[m];
     M.pl = s->Wpl[m];
     M.pl_stride = (int64_t)D.P * D.rows[m] * D.cols[m];
@@ -608,6 +618,9 @@ ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, co
     a.chunk = s->cfg.chunk;
     a.nchunks = (int)nchunks;
     a.P = D.P;
+    a.e_scale = s->cfg.lr[1];
+    a.dz_scale = s->cfg.lr[0] / s->cfg.lr[1];
+    a.keep = 1.f - s->cfg.weight_decay;
     STAGED(TTT_STAGE_RESIDENT, launch_small(a, s->cfg.loss == TTT_LOSS_MSE, st));
     return TTT_OK;
   }

@@ -112,10 +112,12 @@ struct RenormMat {
   int rows, cols;
   u16* pl;         // planes [np][P][rows][cols]
   int64_t pl_stride;
+  float lr;        // step size: W' = keep W - lr U
 };
 struct RenormArgs {
   RenormMat m[3];
   int P, np, renorm, nm, max_rows;
+  float keep;      // 1 - weight decay
   int* health;
 };
 
@@ -140,6 +142,9 @@ struct SmallArgs {
   int* health;           // set to 1 if the final state holds a non-finite value
   int64_t T;             // tokens per problem in the caller's tensors
   int chunk, nchunks, P;
+  float e_scale;         // step size of W2: scales the negated output error
+  float dz_scale;        // step size of W1 over that of W2: scales the negated dZ
+  float keep;            // 1 - weight decay, applied to the state before each step
 };
 
 // ---------------------------------------------------------------------------- launchers

@@ -485,11 +485,12 @@ __global__ __launch_bounds__(256) void k_renorm(RenormArgs a) {
   const int cols = M.cols;
   float* w = M.W + (int64_t)gr * cols;
   const float* u = M.U ? M.U + (int64_t)gr * cols : nullptr;
+  const float keep = a.keep, step = M.lr;
   float so = 0.f, sn = 0.f;
   if (u) {
     for (int c = lane; c < cols; c += 64) {
       const float x = w[c];
-      const float y = x - u[c];
+      const float y = keep * x - step * u[c];
       so += x * x;
       sn += y * y;
     }
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(256) void k_renorm(RenormArgs a) {
   for (int c = lane; c < cols; c += 64) {
     float x = w[c];
     if (u) {
-      x = (x - u[c]) * scale;
+      x = (keep * x - step * u[c]) * scale;
       w[c] = x;
     }
     u16 h[3];

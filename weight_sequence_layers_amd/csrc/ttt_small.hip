@@ -139,6 +139,14 @@ __device__ __forceinline__ void zero(f32x16 (&acc)[2][2]) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 }
 
+// weight decay of register-resident state (keep = 1 leaves it bitwise unchanged)
+__device__ __forceinline__ void scale_state(f32x16 (&w)[2][2], float keep) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) w[i][j] *= keep;
+}
+
 // acc[i][j] += A(32 i + [0, 32), :) B(32 j + [0, 32), :)^T over k in [0, KLEN): a 64 x 64
 // block of a product per wave.  a_off / b_off: byte offsets of the operands' (0, 0)
 // elements including this thread's fragment part.
@@ -205,6 +213,7 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
   const int wr = 32 * (w >> 1), wc = 32 * (w & 1);   // this wave's 32 x 32 tile of a 64 x 64
   // chunk rows moved by this thread: tid / 8 and 32 + tid / 8, 16-byte column block tid % 8
   const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const float es = a.e_scale;   // step size of W2, folded into the stored -E
 
   // fp32 state, as gradient-GEMM accumulators:
   //   w1: W1 rows (hidden) [64w, +64) x all 64 columns;  w2: all 64 rows x W2 columns
@@ -362,12 +371,12 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
         const uint32_t e_off = OFF_QE + ac64 + (wr * S64 + wc) * 2 + acc_const(S64, v);
         const uint32_t v_off = e_off - OFF_QE + OFF_V;
         const float eta = at<float>(lds, OFF_ETA + (wr + 4 * hl + 8 * (v >> 2) + (v & 3)) * 4);
-        at<u16>(lds, e_off) = f2bf(2.f * eta * (bf2f(at<u16>(lds, v_off)) - o[v]));
+        at<u16>(lds, e_off) = f2bf(es * (2.f * eta * (bf2f(at<u16>(lds, v_off)) - o[v])));
       }
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float eta = at<float>(lds, OFF_ETA + (lr + 32 * h) * 4);
+        const float eta = es * at<float>(lds, OFF_ETA + (lr + 32 * h) * 4);
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8)
           at<u16>(lds, OFF_QE + ld64 + (h * 32 * S64 + e8) * 2) =
@@ -375,7 +384,8 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
       }
     }
     __syncthreads();
-    // 5. W2 <- W2 - E^T gelu(Z)
+    // 5. W2 <- keep W2 - lr2 E^T gelu(Z)  (the step size is in the stored -E)
+    scale_state(w2, a.keep);
     mma_2x2<true, S64, false, S64, 64>(w2, lds, OFF_QE + fc64, OFF_HT + fr64 + w_rows64);
     // 6. -dH = (-E) W2 with the pre-update bf16 W2; -dZ = -dH gelu'(Z) -> H^T
     zero(acc);
@@ -383,11 +393,12 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] *= gd[i][j];
+      for (int j = 0; j < 2; ++j) acc[i][j] *= gd[i][j] * a.dz_scale;
     __syncthreads();                                   // gelu(Z) read by every wave
     put_h(acc);
     __syncthreads();
-    // 7. W1 <- W1 - dZ^T K
+    // 7. W1 <- keep W1 - lr1 dZ^T K
+    scale_state(w1, a.keep);
     mma_2x2<false, S64, true, S64, 64>(w1, lds, OFF_HT + fr64 + w_rows64, OFF_K + fc64);
     __syncthreads();                                   // every read of W, K, V, E done
     publish_w();
