@@ -458,14 +458,27 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
   const int64_t base = (int64_t)zz * M * N;
   const int m = zz / a.P;
   const int tr = (a.tr_mask >> m) & 1;
-  g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
+  // runs of four columns (N is a multiple of 16, so a run lies wholly inside or outside):
+  // U in the weight orientation is written as one 16-byte store per run, or transposed as
+  // four 4-byte stores that consecutive lanes (consecutive rows) make contiguous
+  g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
-    float x = 0.f;
-    if (R < M && C < N) {
-      x = sc * g.acc[0][i][j][v];
-      if (a.last) a.U[tr ? base + (int64_t)C * M + R : base + (int64_t)R * N + C] = x;
+    const bool in = R < M && C < N;
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = in ? sc * g.acc[0][i][j][4 * q + e] : 0.f;
+      g.acc[0][i][j][4 * q + e] = x[e];
     }
-    g.acc[0][i][j][v] = x;
+    if (a.last && in) {
+      if (tr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a.U[base + (int64_t)(C + e) * M + R] = x[e];
+      } else {
+        *reinterpret_cast<float4*>(a.U + base + (int64_t)R * N + C) =
+            make_float4(x[0], x[1], x[2], x[3]);
+      }
+    }
   });
   if (!a.last) {
     const int rl = min(BM, M - m0), cl = min(BN, N - n0);
