@@ -487,43 +487,72 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
 }
 
 // ------------------------------------------------------------------------ renorm / update
-// One wavefront per weight row (rows of all problems flattened).  Both norms are summed
-// by the same code over the same element order, so a zero update leaves the row bit-exact.
+// W <- keep W - lr U for every row of every matrix, then (renorm) each row back to its
+// norm before the step; the bf16 planes of the new W for the next chunk's GEMMs.  One wave
+// per row (rows of all problems flattened): the row's W and U are held in registers (CPL
+// 16-byte chunks per lane, rows of up to 256 CPL values), so each is read once and
+// written once with 16-byte accesses.  Both norms are summed by the same code over the
+// same element order, so a zero update with no decay leaves the row bit-exact.  With U
+// null only the planes are refreshed.
+template <int CPL>
 __global__ __launch_bounds__(256) void k_renorm(RenormArgs a) {
   const int m = blockIdx.y;
   const RenormMat& M = a.m[m];
   const int lane = threadIdx.x & 63;
   const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (gr >= M.rows * a.P) return;
-  const int cols = M.cols;
-  float* w = M.W + (int64_t)gr * cols;
-  const float* u = M.U ? M.U + (int64_t)gr * cols : nullptr;
-  const float keep = a.keep, step = M.lr;
-  float so = 0.f, sn = 0.f;
-  if (u) {
-    for (int c = lane; c < cols; c += 64) {
-      const float x = w[c];
-      const float y = keep * x - step * u[c];
-      so += x * x;
-      sn += y * y;
+  const int n4 = M.cols / 4;   // 16-byte chunks in the row (cols is a multiple of 16)
+  float4* w = reinterpret_cast<float4*>(M.W + (int64_t)gr * M.cols);
+  float4 x[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int i = lane + 64 * k;
+    x[k] = i < n4 ? w[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (M.U) {
+    const float4* u = reinterpret_cast<const float4*>(M.U + (int64_t)gr * M.cols);
+    const float keep = a.keep, step = M.lr;
+    float so = 0.f, sn = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int i = lane + 64 * k;
+      const float4 d = i < n4 ? u[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 y = make_float4(fmaf(-step, d.x, keep * x[k].x), fmaf(-step, d.y, keep * x[k].y),
+                                   fmaf(-step, d.z, keep * x[k].z), fmaf(-step, d.w, keep * x[k].w));
+      // explicit fused steps in one order for both sums, so that y == x gives so == sn
+      so = fmaf(x[k].w, x[k].w, fmaf(x[k].z, x[k].z, fmaf(x[k].y, x[k].y, fmaf(x[k].x, x[k].x, so))));
+      sn = fmaf(y.w, y.w, fmaf(y.z, y.z, fmaf(y.y, y.y, fmaf(y.x, y.x, sn))));
+      x[k] = y;
+    }
+    so = wave_sum(so);
+    sn = wave_sum(sn);
+    float scale = 1.f;
+    if (a.renorm && sn > 0.f) scale = sqrtf(so) / sqrtf(sn);
+    if (lane == 0 && (!isfinite(so) || !isfinite(sn))) *a.health = 1;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int i = lane + 64 * k;
+      x[k] = make_float4(x[k].x * scale, x[k].y * scale, x[k].z * scale, x[k].w * scale);
+      if (i < n4) w[i] = x[k];
     }
   }
-  so = wave_sum(so);
-  sn = wave_sum(sn);
-  float scale = 1.f;
-  if (u && a.renorm && sn > 0.f) scale = sqrtf(so) / sqrtf(sn);
-  if (u && lane == 0 && (!isfinite(so) || !isfinite(sn))) *a.health = 1;
-  for (int c = lane; c < cols; c += 64) {
-    float x = w[c];
-    if (u) {
-      x = (keep * x - step * u[c]) * scale;
-      w[c] = x;
-    }
-    u16 h[3];
-    split_planes(x, a.np, h);
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int i = lane + 64 * k;
+    if (i >= n4) continue;
+    u16 h[4][3];
+    split_planes(x[k].x, a.np, h[0]);
+    split_planes(x[k].y, a.np, h[1]);
+    split_planes(x[k].z, a.np, h[2]);
+    split_planes(x[k].w, a.np, h[3]);
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      if (q < a.np) M.pl[q * M.pl_stride + (int64_t)gr * cols + c] = h[q];
+      if (q < a.np) {
+        uint2 v;
+        v.x = h[0][q] | ((uint32_t)h[1][q] << 16);
+        v.y = h[2][q] | ((uint32_t)h[3][q] << 16);
+        *reinterpret_cast<uint2*>(M.pl + q * M.pl_stride + (int64_t)gr * M.cols + 4 * i) = v;
+      }
   }
 }
 
@@ -706,8 +735,15 @@ hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
   if (a.P == 0 || a.nm == 0) return hipSuccess;
-  const int blocks = (a.max_rows * a.P + 3) / 4;
-  hipLaunchKernelGGL(k_renorm, dim3(blocks, a.nm), dim3(256), 0, s, a);
+  int cols = 0;
+  for (int m = 0; m < a.nm; ++m) cols = std::max(cols, a.m[m].cols);
+  const dim3 grid((a.max_rows * a.P + 3) / 4, a.nm);
+  if (cols <= 256) hipLaunchKernelGGL(k_renorm<1>, grid, dim3(256), 0, s, a);
+  else if (cols <= 512) hipLaunchKernelGGL(k_renorm<2>, grid, dim3(256), 0, s, a);
+  else if (cols <= 1024) hipLaunchKernelGGL(k_renorm<4>, grid, dim3(256), 0, s, a);
+  else if (cols <= 2048) hipLaunchKernelGGL(k_renorm<8>, grid, dim3(256), 0, s, a);
+  else if (cols <= 4096) hipLaunchKernelGGL(k_renorm<16>, grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
