@@ -213,9 +213,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// PL > 0 selects the plane-resident product: A[0..PL) and B[0..PL) are the bf16 planes of
-// one A and one B (each operand with planes = 1); every K step loads all 2 PL plane tiles
-// once and accumulates the plane products (i, j) with i + j < PL into one accumulator.
+// PL > 0 selects the plane-resident product: A[0..NA) and B[0..NB) are the bf16 planes of
+// one A and one B (each operand with planes = 1), PL = max(NA, NB); every K step loads all
+// NA + NB plane tiles once and accumulates the plane products (i, j) with i + j < PL into
+// one accumulator.
 // PL = 0 keeps one accumulator per B operand and runs plane pairs as K segments.
 //
 // SW selects the accumulator layout.  The MFMA computes D = A B with A's fragment giving
@@ -266,7 +267,7 @@ struct Gemm {
   // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffer 1, declared as
   // two separate __shared__ arrays by the kernel (GEMM_LDS)
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
-  static_assert(PL == 0 || (NA == PL && NB == PL), "plane-resident mode takes PL planes a side");
+  static_assert(PL == 0 || PL == (NA > NB ? NA : NB), "plane-resident mode: PL = max(NA, NB)");
   static constexpr int NACC = PL ? 1 : NB;
 
   f32x16 acc[NACC][TM][TN];
@@ -444,9 +445,9 @@ struct Gemm {
                                                          wn0 + t * 32, s);
         if constexpr (PL > 0) {
 #pragma unroll
-          for (int i = 0; i < PL; ++i)
+          for (int i = 0; i < NA; ++i)
 #pragma unroll
-            for (int j = 0; j < PL; ++j)
+            for (int j = 0; j < NB; ++j)
               if (i + j < PL) {
 #pragma unroll
                 for (int tm = 0; tm < TM; ++tm)

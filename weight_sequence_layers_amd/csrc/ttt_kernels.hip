@@ -206,9 +206,19 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 }
 
 // ------------------------------------------------------------------------ contraction
-template <int BM, int BN, int WGM, int WGN>
+// PA = PB = 0: the operands' plane pairs run as K segments (any plane counts, K step 64).
+// Else A has PA planes and B has PB, all loaded once per K step of 32 (plane-resident).
+template <int PA, int PB>
+struct ContractGemm {
+  static constexpr int NA = PA ? PA : 1, NB = PB ? PB : 1;
+  static constexpr int PL = PA ? (PA > PB ? PA : PB) : 0;
+};
+template <int BM, int BN, int WGM, int WGN, int PA, int PB>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 1, 1>;   // both operands token-major
+  using CG = ContractGemm<PA, PB>;
+  // both operands token-major (read column-wise)
+  using G = Gemm<BM, BN, WGM, WGN, CG::NA, CG::NB, (1 << CG::NA) - 1, (1 << CG::NB) - 1, CG::PL,
+                 PA ? 32 : 64>;
   GEMM_LDS(G);
   // logical block order (token range, matrix and problem, tile)
   const int lid = xcd_block(blockIdx.x, gridDim.x);
@@ -224,7 +234,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   B.p += (int64_t)k0 * B.ld;
   G g;
   g.zero();
-  g.run(&A, &B, m0, n0, p, min(a.kchunk, a.K - k0), GEMM_STAGES);
+  if constexpr (PA == 0) {
+    g.run(&A, &B, m0, n0, p, min(a.kchunk, a.K - k0), GEMM_STAGES);
+  } else {
+    Operand Aq[PA], Bq[PB];   // one operand per plane
+#pragma unroll
+    for (int q = 0; q < PA; ++q) {
+      Aq[q] = A;
+      Aq[q].p += q * A.pstride;
+      Aq[q].planes = 1;
+    }
+#pragma unroll
+    for (int q = 0; q < PB; ++q) {
+      Bq[q] = B;
+      Bq[q].p += q * B.pstride;
+      Bq[q].planes = 1;
+    }
+    g.run(Aq, Bq, m0, n0, p, min(a.kchunk, a.K - k0), GEMM_STAGES);
+  }
 
   const int M = a.M, N = a.N;
   const int64_t base = (int64_t)zz * M * N;
@@ -637,9 +664,16 @@ int contract_split_max(int tiles, int nz) {
 
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
-  using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;
+  using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;   // block size (the same for every instance)
   ContractArgs a = a0;
-  auto kern = k_contract<BM, BN, 2, 4>;
+  // one bf16 plane on one side and 2 or 3 on the other: plane-resident (NA + NB tiles a
+  // K step instead of two per plane product); else plane pairs as K segments
+  const int pa = a.a[0].planes, pb = a.b[0].planes;
+  auto kern = k_contract<BM, BN, 2, 4, 0, 0>;
+  if (pa == 1 && pb == 2) kern = k_contract<BM, BN, 2, 4, 1, 2>;
+  else if (pa == 1 && pb == 3) kern = k_contract<BM, BN, 2, 4, 1, 3>;
+  else if (pa == 2 && pb == 1) kern = k_contract<BM, BN, 2, 4, 2, 1>;
+  else if (pa == 3 && pb == 1) kern = k_contract<BM, BN, 2, 4, 3, 1>;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   a.nz = nm * a.P;
