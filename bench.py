@@ -128,8 +128,9 @@ def blas_reference(cfg, planes, reps: int = 10) -> dict:
     return out
 
 
-def cpu_baseline(cfg, budget_chunks=None):
-    """The oracle on the host: one (batch, head) problem over its first chunks."""
+def cpu_baseline(cfg, budget_chunks=None, min_seconds=10.0):
+    """The oracle on the host: (batch, head) problems in order, each over its first
+    chunks, until min_seconds of oracle time have been spent or every problem is done."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -138,11 +139,19 @@ def cpu_baseline(cfg, budget_chunks=None):
 
     nc = cfg.n_chunks if budget_chunks is None else min(cfg.n_chunks, budget_chunks)
     T = nc * cfg.chunk
-    p = ti.make_problem_inputs(cfg, 0, 0, t1=T)
-    w0 = [w[0] for w in ti.make_weights(cfg)]
-    t0 = time.perf_counter()
-    orc.sequence_forward(cfg, w0, p["q"], p["k"], p["v"], p["eta"], n_chunks=nc)
-    dt = time.perf_counter() - t0
+    weights = ti.make_weights(cfg)
+    problems = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    dt, done = 0.0, 0
+    for (b, h) in problems:
+        p = ti.make_problem_inputs(cfg, b, h, t1=T)
+        w0 = [w[h] for w in weights]
+        t0 = time.perf_counter()
+        orc.sequence_forward(cfg, w0, p["q"], p["k"], p["v"], p["eta"], n_chunks=nc)
+        dt += time.perf_counter() - t0
+        done += 1
+        if dt >= min_seconds:
+            break
+    T *= done
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("internal_api") in ("openblas", "mkl", "blis")] or [1])
     model = "unknown CPU"
@@ -154,7 +163,7 @@ def cpu_baseline(cfg, budget_chunks=None):
     except OSError:
         pass
     return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of {cfg.batch * cfg.heads} (batch, head) problems, {nc} chunks "
+            "sample": f"{done} of {len(problems)} (batch, head) problems, {nc} chunks each "
                       f"({T} tokens), numpy fp64, {dt:.1f} s on {model}; problems are "
                       f"independent so the rate is the whole workload's"}
 
