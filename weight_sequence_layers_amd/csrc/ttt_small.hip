@@ -139,7 +139,7 @@ __device__ __forceinline__ void zero(f32x16 (&acc)[2][2]) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 }
 
-// weight decay of register-resident state (keep = 1 leaves it bitwise unchanged)
+// scale a register-resident 64 x 64 block (weight decay of the state, step-size ratio)
 __device__ __forceinline__ void scale_state(f32x16 (&w)[2][2], float keep) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -197,7 +197,9 @@ struct ChunkRegs {
   float eta;
 };
 
-template <int LOSS>
+// SCALED: step sizes other than 1 or a weight decay (a separate instance, so that the
+// plain step compiles without any of it)
+template <int LOSS, bool SCALED>
 __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
   using namespace small;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
   const int wr = 32 * (w >> 1), wc = 32 * (w & 1);   // this wave's 32 x 32 tile of a 64 x 64
   // chunk rows moved by this thread: tid / 8 and 32 + tid / 8, 16-byte column block tid % 8
   const int lr = tid >> 3, lc = (tid & 7) * 8;
-  const float es = a.e_scale;   // step size of W2, folded into the stored -E
+  const float es = a.e_scale;   // step size of W2, folded into the staged eta (so into -E)
 
   // fp32 state, as gradient-GEMM accumulators:
   //   w1: W1 rows (hidden) [64w, +64) x all 64 columns;  w2: all 64 rows x W2 columns
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
       at<u32x4>(lds, OFF_K + ld64 + h * 32 * S64 * 2) = R.k[h];
       at<u32x4>(lds, OFF_V + ld64 + h * 32 * S64 * 2) = R.v[h];
     }
-    if (tid < BT) at<float>(lds, OFF_ETA + tid * 4) = R.eta;
+    if (tid < BT) at<float>(lds, OFF_ETA + tid * 4) = SCALED ? es * R.eta : R.eta;
   };
 
   bind();
@@ -371,12 +373,12 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
         const uint32_t e_off = OFF_QE + ac64 + (wr * S64 + wc) * 2 + acc_const(S64, v);
         const uint32_t v_off = e_off - OFF_QE + OFF_V;
         const float eta = at<float>(lds, OFF_ETA + (wr + 4 * hl + 8 * (v >> 2) + (v & 3)) * 4);
-        at<u16>(lds, e_off) = f2bf(es * (2.f * eta * (bf2f(at<u16>(lds, v_off)) - o[v])));
+        at<u16>(lds, e_off) = f2bf(2.f * eta * (bf2f(at<u16>(lds, v_off)) - o[v]));
       }
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float eta = es * at<float>(lds, OFF_ETA + (lr + 32 * h) * 4);
+        const float eta = at<float>(lds, OFF_ETA + (lr + 32 * h) * 4);
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8)
           at<u16>(lds, OFF_QE + ld64 + (h * 32 * S64 + e8) * 2) =
@@ -384,8 +386,8 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
       }
     }
     __syncthreads();
-    // 5. W2 <- keep W2 - lr2 E^T gelu(Z)  (the step size is in the stored -E)
-    scale_state(w2, a.keep);
+    // 5. W2 <- keep W2 - lr2 E^T gelu(Z)  (the step size is in the staged eta, so in -E)
+    if constexpr (SCALED) scale_state(w2, a.keep);
     mma_2x2<true, S64, false, S64, 64>(w2, lds, OFF_QE + fc64, OFF_HT + fr64 + w_rows64);
     // 6. -dH = (-E) W2 with the pre-update bf16 W2; -dZ = -dH gelu'(Z) -> H^T
     zero(acc);
@@ -393,12 +395,13 @@ __global__ __launch_bounds__(256) void k_small_gelu(SmallArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] *= gd[i][j] * a.dz_scale;
+      for (int j = 0; j < 2; ++j) acc[i][j] *= gd[i][j];
+    if constexpr (SCALED) scale_state(acc, a.dz_scale);   // W1's step size over W2's
     __syncthreads();                                   // gelu(Z) read by every wave
     put_h(acc);
     __syncthreads();
     // 7. W1 <- keep W1 - lr1 dZ^T K
-    scale_state(w1, a.keep);
+    if constexpr (SCALED) scale_state(w1, a.keep);
     mma_2x2<false, S64, true, S64, 64>(w1, lds, OFF_HT + fr64 + w_rows64, OFF_K + fc64);
     __syncthreads();                                   // every read of W, K, V, E done
     publish_w();
@@ -432,24 +435,22 @@ bool small_supported(int fw, int ns_steps, int renorm, int act_bf16, int apply_f
          ap == 1 && gp == 1;
 }
 
+template <int LOSS, bool SCALED>
+static hipError_t launch_small_t(const SmallArgs& a, hipStream_t s) {
+  auto kern = k_small_gelu<LOSS, SCALED>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, small::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.P), dim3(small::NT), small::LDS, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_small(const SmallArgs& a, int loss, hipStream_t s) {
   if (a.P == 0 || a.nchunks == 0) return hipSuccess;
   if (a.chunk < 1 || a.chunk > small::BT) return hipErrorInvalidValue;
-  hipError_t e;
-  if (loss == 1) {
-    auto kern = k_small_gelu<1>;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, small::LDS)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(kern, dim3(a.P), dim3(small::NT), small::LDS, s, a);
-  } else {
-    auto kern = k_small_gelu<0>;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, small::LDS)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(kern, dim3(a.P), dim3(small::NT), small::LDS, s, a);
-  }
-  return hipGetLastError();
+  const bool scaled = a.e_scale != 1.f || a.dz_scale != 1.f || a.keep != 1.f;
+  if (loss == 1) return scaled ? launch_small_t<1, true>(a, s) : launch_small_t<1, false>(a, s);
+  return scaled ? launch_small_t<0, true>(a, s) : launch_small_t<0, false>(a, s);
 }
 
 }  // namespace ttt
