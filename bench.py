@@ -189,7 +189,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the layer's (batch, head) problems shard across GPUs with no communication, "
-              "but this build measures one GPU only)", file=sys.stderr)
+              "and this benchmark measures one GPU's throughput)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

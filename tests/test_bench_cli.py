@@ -1,0 +1,27 @@
+"""Host-side checks of bench.py's command line (no GPU is touched)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("n", ["2", "8", "0"])
+def test_more_than_one_gpu_is_refused(n):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", n],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_cpu_baseline_leg_reports_its_sample():
+    sys.path.insert(0, ROOT)
+    import bench
+    import ttt_inputs as ti
+    res = bench.cpu_baseline(ti.CONFIGS["tiny"], min_seconds=0.0)
+    assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
+    assert res["cores"] >= 1 and "1 of 1" in res["sample"]
+    json.dumps(res)
