@@ -78,3 +78,19 @@ def test_step_size_and_weight_decay(act, fw, loss, ns, renorm, lr, wd):
     cfg = ti.Config("step", 2, 2, 600, 200, 80, 176, fw, loss, ns, renorm, act,
                     "apply_then_update", 77, lr=lr, weight_decay=wd)
     _check(cfg)
+
+
+@pytest.mark.parametrize("shape", ["narrow", "wide"])
+def test_single_plane_newton_schulz_one_chunk(shape):
+    # Newton-Schulz with one bf16 plane everywhere: the 64-wide symmetric kernels (two
+    # K groups of four waves) for a few matrices, the 128-wide ones for many. One chunk,
+    # so that the plain-bf16 rounding does not compound over chunks.
+    if shape == "narrow":
+        cfg = ti.Config("np1", 1, 2, 400, 400, 80, 176, "swiglu", "dot", 5, True, "bf16",
+                        "apply_then_update", 51)
+        problems = None
+    else:
+        cfg = ti.Config("np1w", 10, 3, 256, 256, 144, 288, "swiglu", "dot", 5, True, "bf16",
+                        "apply_then_update", 52)
+        problems = [(0, 0), (9, 2)]
+    _check(cfg, planes=(1, 1, 1, 1), problems=problems)
