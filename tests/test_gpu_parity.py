@@ -94,3 +94,29 @@ def test_single_plane_newton_schulz_one_chunk(shape):
                         "apply_then_update", 52)
         problems = [(0, 0), (9, 2)]
     _check(cfg, planes=(1, 1, 1, 1), problems=problems)
+
+
+def _random_case(i):
+    # seeded draw of a configuration: every net, loss, order, precision and the optional
+    # Muon and renorm, with dims that are not tile multiples and chunks of any length
+    rng = np.random.default_rng(900 + i)
+    fw = ["swiglu", "gelu", "linear"][i % 3]
+    loss = ["dot", "mse"][(i // 3) % 2]
+    act = ["f32", "bf16"][(i // 2) % 2]
+    dim = int(16 * rng.integers(1, 13))
+    hidden = max(dim, int(16 * rng.integers(1, 21)))
+    ns = 5 if (fw != "linear" and rng.random() < 0.6) else 0
+    renorm = bool(rng.random() < 0.5)
+    chunk = int(rng.integers(1, 300))
+    n_chunks = int(rng.integers(1, 4))
+    order = ["apply_then_update", "update_then_apply"][int(rng.integers(0, 2))]
+    batch, heads = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    return ti.Config(f"rand{i}", batch, heads, chunk * n_chunks, chunk, dim, hidden, fw, loss,
+                     ns, renorm, act, order, 3000 + i)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shapes(i):
+    cfg = _random_case(i)
+    print(cfg, flush=True)
+    _check(cfg)
