@@ -173,7 +173,6 @@ struct ttt_state {
   float* gpart = nullptr; // token-split partial sums [ksplit][nm][P][d][n]
   int ksplit = 1;
   u16 *xpl[2] = {}, *apl = nullptr, *bpl = nullptr;
-  float* afp = nullptr;
   int* health = nullptr;
   int contract_tiles = 0;
   bool resident = false;  // the device-resident chunk loop serves this state (Wpl unused)
@@ -233,12 +232,11 @@ size_t layout(ttt_state* s, char* base) {
   size_t opart = C.take<float>(D.nm * P * ctiles);
   const int ksp = contract_split_max(ctiles, (int)(D.nm * P));
   size_t ogp = ksp > 1 ? C.take<float>(ksp * D.nm * P * d * n) : 0;
-  size_t ox[2] = {0, 0}, oa = 0, ob = 0, oafp = 0;
+  size_t ox[2] = {0, 0}, oa = 0, ob = 0;
   if (c.ns_steps > 0) {
     for (int i = 0; i < 2; ++i) ox[i] = C.take<u16>(D.npm * D.nm * P * d * n);
     oa = C.take<u16>(D.npm * D.nm * P * d * d);
     ob = C.take<u16>(D.npm * D.nm * P * d * d);
-    oafp = C.take<float>(D.nm * P * d * d);
   }
   size_t oh = C.take<int>(1);
   if (base) {
@@ -275,7 +273,7 @@ size_t layout(ttt_state* s, char* base) {
     s->gpart = ksp > 1 ? F(ogp) : nullptr;
     if (c.ns_steps > 0) {
       for (int i = 0; i < 2; ++i) s->xpl[i] = H(ox[i]);
-      s->apl = H(oa); s->bpl = H(ob); s->afp = F(oafp);
+      s->apl = H(oa); s->bpl = H(ob);
     }
     s->health = reinterpret_cast<int*>(base + oh);
   }
@@ -542,7 +540,6 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
     a.part = s->part; a.nparts = s->contract_tiles; a.first = it == 0; a.last = it == steps - 1;
     a.eps = 1e-7f;
     a.xin = pbuf(s->xpl[it & 1], pk, (int64_t)Z * M * N, (int64_t)M * N, N);
-    a.afp = s->afp;
     a.aout = pbuf(s->apl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
     STAGED(TTT_STAGE_NS_GRAM, launch_ns_gram(a, st));
     a.ain = a.aout;

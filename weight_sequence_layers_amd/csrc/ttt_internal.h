@@ -98,7 +98,6 @@ struct NsArgs {
   float eps;
   PlaneBuf xin;       // gram, update: X planes [M][N] (iteration 0: planes of G)
   PlaneBuf ain;       // poly: A planes [M][M] ; update: B planes [M][M]
-  float* afp;         // gram out / poly in: A fp32 [Z][M][M]
   PlaneBuf aout;      // gram: A planes ; poly: B planes
   PlaneBuf xout;
   float* U;           // last: U in weight orientation

@@ -383,8 +383,7 @@ __device__ __forceinline__ void store_sym(const f32x16 (&v)[G::TM][G::TN], char*
   else store_planes<G, TILE_BOTH, NP>(v, smem, dst, zz, m0, n0, rl, cl);
 }
 
-// A = s^2 X X^T: upper tiles computed; A fp32 kept for the upper tiles (the only part
-// the polynomial stage reads); A planes written for the full symmetric matrix.
+// A = s^2 X X^T: upper tiles computed; A planes written for the full symmetric matrix.
 template <int T, int WGM, int WGN, int PL, int SP, int WGK>
 __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
   // swapped accumulator layout: runs of four columns, stored as 16-byte vectors
@@ -408,17 +407,12 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
     const float s = ns_scale(a, zz);
     s2 = s * s;
   }
-  const int64_t base = (int64_t)zz * M * M;
-  // M is a multiple of 16, so a run of four columns lies wholly inside or outside
-  g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
-    const int R = m0 + r, C = n0 + c;
-    float4 x;
-    x.x = g.acc[0][i][j][4 * q] *= s2;
-    x.y = g.acc[0][i][j][4 * q + 1] *= s2;
-    x.z = g.acc[0][i][j][4 * q + 2] *= s2;
-    x.w = g.acc[0][i][j][4 * q + 3] *= s2;
-    if (R < M && C < M) *reinterpret_cast<float4*>(a.afp + base + (int64_t)R * M + C) = x;
-  });
+  if (a.first) {
+    g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g.acc[0][i][j][4 * q + e] *= s2;
+    });
+  }
   store_sym<G, SP>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
@@ -442,12 +436,23 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
   g.zero();
   g.run(Ao, Ao, m0, n0, zz, M, GEMM_STAGES);
   g.reduce(smem);
-  const int64_t base = (int64_t)zz * M * M;
+  // the linear term b A reads A from its planes (the sum of the planes holds A to about
+  // 16 significant bits with two planes, as the products do)
+  const u16* ap = a.ain.base + (int64_t)zz * a.ain.zstride;
   g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
-    float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (R < M && C < M) A = *reinterpret_cast<const float4*>(a.afp + base + (int64_t)R * M + C);
-    const float av[4] = {A.x, A.y, A.z, A.w};
+    float av[4] = {0.f, 0.f, 0.f, 0.f};
+    if (R < M && C < M) {
+#pragma unroll
+      for (int pq = 0; pq < PL; ++pq) {
+        const uint2 h = *reinterpret_cast<const uint2*>(ap + pq * a.ain.plane_stride +
+                                                        (int64_t)R * a.ain.ld + C);
+        av[0] += bf2f((u16)(h.x & 0xFFFFu));
+        av[1] += bf2f((u16)(h.x >> 16));
+        av[2] += bf2f((u16)(h.y & 0xFFFFu));
+        av[3] += bf2f((u16)(h.y >> 16));
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float x = 0.f;
