@@ -12,7 +12,6 @@ typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------------ bf16 helpers
 __device__ __forceinline__ u16 f2bf(float x) {
@@ -233,11 +232,10 @@ __device__ __forceinline__ void lds_barrier() {
 // to group (4 t + g) mod WGK); for_each, for_each4 and the tile stores visit the owned
 // runs only.
 template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0,
-          int BK_ = 64, bool SW_ = false, int WGK_ = 1, bool RL_ = false>
+          int BK_ = 64, bool SW_ = false, int WGK_ = 1>
 struct Gemm {
   static constexpr bool SW = SW_;
   static constexpr int WGK = WGK_;
-  static constexpr bool RL = RL_;
   static constexpr int NT = WGM * WGN * WGK * 64;
   static constexpr int TBM = BM, TBN = BN;
   static constexpr int STORE_LDS = (BM + 8) * (BN + 8) * 2;
@@ -473,101 +471,14 @@ struct Gemm {
       __syncthreads();
     };
 
-    if constexpr (!RL) {
-      issue(st0);
+    issue(st0);
+    step_end();
+    for (int t = 0; t < total; ++t) {
+      char* cur = (t & 1) ? st1 : st0;
+      char* nxt = (t & 1) ? st0 : st1;
+      if (t + 1 < total) issue(nxt);
+      compute(cur);
       step_end();
-      for (int t = 0; t < total; ++t) {
-        char* cur = (t & 1) ? st1 : st0;
-        char* nxt = (t & 1) ? st0 : st1;
-        if (t + 1 < total) issue(nxt);
-        compute(cur);
-        step_end();
-      }
-    } else {
-      // Register-staged loads: each step's chunks are loaded into registers two steps
-      // ahead and written to LDS one step ahead, so a chunk has two steps of compute to
-      // land instead of one, at no extra LDS.  Two register slots alternate with the two
-      // LDS buffers.  Loads past the last step read an empty range (zeros, no memory
-      // access) so that every step issues the same loads and the compiler can wait for
-      // the older slot only.
-      u32x4 ra[2][NA][TA::C], rb[2][NB][TB::C];
-      int step_n = 0;   // step the next gload fetches
-      auto gload = [&](u32x4 (&ga)[NA][TA::C], u32x4 (&gb)[NB][TB::C])
-          __attribute__((always_inline)) {
-        const int sg = sg_n, k0 = k0_n;
-        const bool live = step_n < total;
-        ++step_n;
-        k0_n += BK;
-        if (k0_n >= K) {
-          k0_n = 0;
-          ++sg_n;
-        }
-        const int qa = live ? (segs >> (4 * sg)) & 3 : 0, qb = live ? (segs >> (4 * sg + 2)) & 3 : 0;
-        const bool whole = k0 + BK <= K;
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-          const uint32_t kb = (uint32_t)k0 * la[i].kstride;
-          const char* base = reinterpret_cast<const char*>(pa_[i] + qa * A[i].pstride);
-          const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)base, (short)0, live ? na_[i] : 0, 0x00020000);
-#pragma unroll
-          for (int c = 0; c < TA::C; ++c) {
-            // whole step: the k offset goes in the scalar offset; else per chunk
-            const uint32_t vo = whole ? la[i].off[c]
-                                      : (k0 + la[i].kk[c] < K ? la[i].off[c] + kb : 0xFFFFFFF0u);
-            ga[i][c] = __builtin_amdgcn_raw_buffer_load_b128(r, vo, whole ? (int)kb : 0, 0);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const uint32_t kb = (uint32_t)k0 * lb[i].kstride;
-          const char* base = reinterpret_cast<const char*>(pb_[i] + qb * B[i].pstride);
-          const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)base, (short)0, live ? nb_[i] : 0, 0x00020000);
-#pragma unroll
-          for (int c = 0; c < TB::C; ++c) {
-            // whole step: the k offset goes in the scalar offset; else per chunk
-            const uint32_t vo = whole ? lb[i].off[c]
-                                      : (k0 + lb[i].kk[c] < K ? lb[i].off[c] + kb : 0xFFFFFFF0u);
-            gb[i][c] = __builtin_amdgcn_raw_buffer_load_b128(r, vo, whole ? (int)kb : 0, 0);
-          }
-        }
-      };
-      const int lane16 = (int)(threadIdx.x & 63) * 16;
-      auto lwrite = [&](const u32x4 (&ga)[NA][TA::C], const u32x4 (&gb)[NB][TB::C], char* st)
-          __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-#pragma unroll
-          for (int c = 0; c < TA::C; ++c)
-            if (la[i].act)
-              *reinterpret_cast<u32x4*>(st + i * A_TILE + c * NT * 16 + la[i].slice + lane16) =
-                  ga[i][c];
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int c = 0; c < TB::C; ++c)
-            if (lb[i].act)
-              *reinterpret_cast<u32x4*>(st + NA * A_TILE + i * B_TILE + c * NT * 16 +
-                                        lb[i].slice + lane16) = gb[i][c];
-      };
-      gload(ra[0], rb[0]);   // step 0
-      gload(ra[1], rb[1]);   // step 1
-      lwrite(ra[0], rb[0], st0);
-      gload(ra[0], rb[0]);   // step 2
-      lds_barrier();
-      // steps in pairs: an odd count computes one more step on zero tiles, which adds
-      // exact zeros (a branch out of the pair would make the compiler wait for every load)
-      for (int t = 0; t < total; t += 2) {
-        compute(st0);                // step t
-        lwrite(ra[1], rb[1], st1);   // step t + 1
-        gload(ra[1], rb[1]);         // step t + 3
-        lds_barrier();
-        compute(st1);                // step t + 1
-        lwrite(ra[0], rb[0], st0);   // step t + 2
-        gload(ra[0], rb[0]);         // step t + 4
-        lds_barrier();
-      }
     }
   }
 
