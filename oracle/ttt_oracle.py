@@ -157,6 +157,34 @@ def _block_gradient(fw: str, loss: str, Ws, K, V, eta) -> List[np.ndarray]:
     raise ValueError(fw)
 
 
+def apply_vjp(fw: str, Ws, Q, dO):
+    """Backward of one chunk's apply step O = f_W(Q) ([LaCT] §2.1 apply phase; the
+    query-view rule that [Modular TTT] composes into the layer's backward): given dO, the
+    gradients of sum_t <dO_t, f_W(q_t)> with respect to Q and to every matrix of W, by the
+    chain rule through the net. Returns (dQ [n, d], [dW per matrix])."""
+    Q = np.asarray(Q, np.float64)
+    dO = np.asarray(dO, np.float64)
+    if fw == "swiglu":
+        W1, W3, W2 = Ws
+        Z1 = Q @ W1.T
+        Z3 = Q @ W3.T
+        A = silu(Z1)
+        H = A * Z3
+        dH = dO @ W2
+        dZ3 = dH * A
+        dZ1 = dH * Z3 * silu_prime(Z1)
+        return dZ1 @ W1 + dZ3 @ W3, [dZ1.T @ Q, dZ3.T @ Q, dO.T @ H]
+    if fw == "gelu":
+        W1, W2 = Ws
+        Z = Q @ W1.T
+        dZ = (dO @ W2) * gelu_prime(Z)
+        return dZ @ W1, [dZ.T @ Q, dO.T @ gelu(Z)]
+    if fw == "linear":
+        (W,) = Ws
+        return dO @ W, [dO.T @ Q]
+    raise ValueError(fw)
+
+
 def chunk_gradient(fw: str, loss: str, Ws, K, V, eta, block_rows: Optional[int] = None):
     """Sum of the per-token gradients over the whole chunk ([LaCT] §2.1 update phase,
     eqs. 4-5). A chunk longer than ``block_rows`` is summed block by block: the

@@ -379,6 +379,76 @@ def test_muon_step_size_scales_the_orthogonalised_step():
     assert lo > 0.68 and hi < 1.21
 
 
+# ------------------------------------------------------------------ apply backward
+def apply_vjp_fd_error(fw, seed=31, d=4, dh=6, n=5, eps=1e-6):
+    """Central finite differences of sum <dO, f_W(Q)> in every entry of Q and of W."""
+    rng = np.random.default_rng(seed)
+    Ws = _rand_ws(fw, d, dh, rng)
+    Q = rng.standard_normal((n, d))
+    dO = rng.standard_normal((n, d))
+    dQ, dW = orc.apply_vjp(fw, Ws, Q, dO)
+    f = lambda Ws_, Q_: float(np.sum(dO * orc.fw_apply(fw, Ws_, Q_)))
+    worst = 0.0
+    fdq = np.zeros_like(Q)
+    for idx in np.ndindex(Q.shape):
+        Qp, Qm = Q.copy(), Q.copy()
+        Qp[idx] += eps
+        Qm[idx] -= eps
+        fdq[idx] = (f(Ws, Qp) - f(Ws, Qm)) / (2 * eps)
+    worst = max(worst, np.abs(fdq - dQ).max() / np.abs(fdq).max())
+    for i, W in enumerate(Ws):
+        fd = np.zeros_like(W)
+        for idx in np.ndindex(W.shape):
+            Wp = [w.copy() for w in Ws]
+            Wm = [w.copy() for w in Ws]
+            Wp[i][idx] += eps
+            Wm[i][idx] -= eps
+            fd[idx] = (f(Wp, Q) - f(Wm, Q)) / (2 * eps)
+        worst = max(worst, np.abs(fd - dW[i]).max() / np.abs(fd).max())
+    return worst
+
+
+@pytest.mark.parametrize("fw", ["swiglu", "gelu", "linear"])
+def test_apply_backward_matches_finite_differences(fw):
+    assert apply_vjp_fd_error(fw) < 1e-7
+
+
+@pytest.mark.parametrize("fw", ["swiglu", "gelu", "linear"])
+def test_apply_backward_matches_torch_autograd(fw):
+    rng = np.random.default_rng(32)
+    Ws = _rand_ws(fw, 6, 10, rng)
+    Q = rng.standard_normal((7, 6))
+    dO = rng.standard_normal((7, 6))
+    dQ, dW = orc.apply_vjp(fw, Ws, Q, dO)
+    F = torch.nn.functional
+    tq = torch.tensor(Q, requires_grad=True)
+    tw = [torch.tensor(w, requires_grad=True) for w in Ws]
+    if fw == "swiglu":
+        out = (F.silu(tq @ tw[0].T) * (tq @ tw[1].T)) @ tw[2].T
+    elif fw == "gelu":
+        out = F.gelu(tq @ tw[0].T) @ tw[1].T
+    else:
+        out = tq @ tw[0].T
+    grads = torch.autograd.grad((out * torch.tensor(dO)).sum(), [tq] + tw)
+    assert np.abs(grads[0].numpy() - dQ).max() < 1e-12
+    for g, w in zip(grads[1:], dW):
+        assert np.abs(g.numpy() - w).max() < 1e-12
+
+
+def test_apply_backward_weights_equal_the_inner_product_gradient_at_eta_minus_one():
+    """The weight part of the apply backward is the inner-product loss gradient with keys
+    Q, values dO and eta = -1 (the loss is then +sum <f(q), dO>)."""
+    rng = np.random.default_rng(33)
+    for fw in ("swiglu", "gelu", "linear"):
+        Ws = _rand_ws(fw, 5, 9, rng)
+        Q = rng.standard_normal((8, 5))
+        dO = rng.standard_normal((8, 5))
+        _, dW = orc.apply_vjp(fw, Ws, Q, dO)
+        g = orc.chunk_gradient(fw, "dot", Ws, Q, dO, -np.ones(8))
+        for a, b in zip(dW, g):
+            assert np.abs(a - b).max() < 1e-13
+
+
 # ------------------------------------------------------------------ mutation tests
 def _all_pins_pass():
     try:
