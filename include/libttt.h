@@ -143,6 +143,24 @@ ttt_status ttt_chunk_forward(ttt_state* s, const void* q, const void* k, const v
 ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, const void* v,
                                 const float* eta, void* out, int64_t seq_len, void* stream);
 
+/*
+ * Backward of one chunk's apply step ([LaCT] §2.1 apply phase, eq. 2; the query-view rule
+ * of Modular TTT's train-view forward / backward / query-view decomposition).  With the
+ * state as it stands (the state that chunk's queries were answered with: call it before
+ * that chunk's ttt_chunk_forward, or restore it with ttt_set_state), computes for every
+ * (batch, head) problem
+ *   dq = d/dQ  sum_t <dout_t, f_W(q_t)>      [B][H][chunk][dim], activation dtype
+ *   dw = d/dW  sum_t <dout_t, f_W(q_t)>      fp32, the ttt_get_state layout (every matrix)
+ * q, dout: [B][H][chunk][dim] device tensors in the activation dtype.  All four pointers
+ * are device pointers, caller-owned, 16-byte aligned.  The state is not changed.  Only the
+ * backward through the apply is computed, not through the fast-weight updates (those
+ * gradients with respect to k, v, eta and W0 are not provided).  States served by the
+ * resident path return TTT_E_UNSUPPORTED (create them with path STAGED).  Enqueued on
+ * stream with no host synchronisation; status codes as for the forward calls.
+ */
+ttt_status ttt_apply_backward(ttt_state* s, const void* q, const void* dout, void* dq,
+                              float* dw, void* stream);
+
 /* Copy the fp32 state out / in.  Layout: matrix by matrix, each [batch][heads][rows][cols]
  * with the shapes listed under ttt_init_state.  dst/src: device, ttt_state_numel values. */
 ttt_status ttt_get_state(const ttt_state* s, float* dst, void* stream);
@@ -169,7 +187,8 @@ ttt_status ttt_destroy_state(ttt_state* s);
 typedef enum {
   TTT_STAGE_FRONT_Q = 0, TTT_STAGE_FRONT_K = 1, TTT_STAGE_OUT = 2, TTT_STAGE_CONTRACT = 3,
   TTT_STAGE_NS_GRAM = 4, TTT_STAGE_NS_POLY = 5, TTT_STAGE_NS_UPDATE = 6, TTT_STAGE_RENORM = 7,
-  TTT_STAGE_SPLIT = 8, TTT_STAGE_MSE = 9, TTT_STAGE_RESIDENT = 10, TTT_STAGE_COUNT = 11
+  TTT_STAGE_SPLIT = 8, TTT_STAGE_MSE = 9, TTT_STAGE_RESIDENT = 10, TTT_STAGE_DQ = 11,
+  TTT_STAGE_COUNT = 12
 } ttt_stage;
 ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches);
 ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms);

@@ -1,0 +1,81 @@
+"""GPU parity of the apply-step backward (ttt_apply_backward) against the oracle's
+apply_vjp: dq and every matrix of dw, max relative error per tensor, 1e-4 for fp32
+activations and 2e-2 for bf16, at the initial state and after one forward chunk (the
+oracle takes its own state after that chunk). dO is the seeded values tensor."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.ttt_oracle as orc
+import ttt_inputs as ti
+import weight_sequence_layers_amd as W
+from ttt_gpu import DEV, device_inputs, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _oracle_state(cfg, inp, b, h, n_chunks):
+    W0s = [w[h] for w in inp["w0"]]
+    if n_chunks == 0:
+        return [np.asarray(w, np.float64) for w in W0s]
+    _, Ws = orc.sequence_forward(cfg, W0s, inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
+                                 inp["eta"][b, h], n_chunks=n_chunks)
+    return Ws
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("fw,loss,ns,renorm", [
+    ("swiglu", "dot", 5, True), ("gelu", "mse", 0, False), ("linear", "dot", 0, False),
+])
+def test_apply_backward_parity(act, fw, loss, ns, renorm):
+    cfg = ti.Config("bwd", 2, 2, 600, 300, 80, 176, fw, loss, ns, renorm, act,
+                    "apply_then_update", 61)
+    inp = ti.make_inputs(cfg)
+    c = W.make_config(cfg, path="staged")
+    q, k, v, eta, w0 = device_inputs(cfg, inp)
+    st = W.ttt_init_state(c, w0)
+    n = W.ttt_state_numel(c)
+    b = cfg.chunk
+    tol = TOL[act]
+    for ci in range(2):
+        sl = slice(ci * b, (ci + 1) * b)
+        qc, dout = q[:, :, sl].contiguous(), v[:, :, sl].contiguous()
+        dq = torch.empty_like(qc)
+        dw = torch.empty(n, dtype=torch.float32, device=DEV)
+        W.ttt_apply_backward(st, qc, dout, dq, dw)
+        torch.cuda.synchronize()
+        dq_g = dq.float().cpu().numpy()
+        dw_g = [x.cpu().numpy() for x in W.split_state(c, dw)]
+        worst = 0.0
+        for bb in range(cfg.batch):
+            for h in range(cfg.heads):
+                Ws = _oracle_state(cfg, inp, bb, h, ci)
+                dQ, dWs = orc.apply_vjp(fw, Ws, inp["q"][bb, h, sl], inp["v"][bb, h, sl])
+                errs = [rel_err(dq_g[bb, h], dQ)] + [rel_err(g[bb, h], r)
+                                                     for g, r in zip(dw_g, dWs)]
+                worst = max(worst, max(errs))
+                assert max(errs) <= tol, (ci, bb, h, errs)
+        print(f"{fw} {act} chunk {ci}: max rel err {worst:.3e} (tol {tol})", flush=True)
+        if ci == 0:
+            out = torch.empty_like(qc)
+            W.ttt_chunk_forward(st, qc, k[:, :, sl].contiguous(), dout,
+                                eta[:, :, sl].contiguous(), out)
+    W.ttt_state_health(st)
+    st.destroy()
+
+
+def test_apply_backward_rejects_resident_states():
+    cfg = ti.Config("bwdres", 1, 2, 64, 64, 64, 256, "gelu", "mse", 0, False, "bf16",
+                    "apply_then_update", 62)
+    c = W.make_config(cfg, planes=(1, 1, 1, 1), path="resident")
+    inp = ti.make_inputs(cfg)
+    q, k, v, eta, w0 = device_inputs(cfg, inp)
+    st = W.ttt_init_state(c, w0)
+    dq = torch.empty_like(q)
+    dw = torch.empty(W.ttt_state_numel(c), dtype=torch.float32, device=DEV)
+    with pytest.raises(W.TTTError) as e:
+        W.ttt_apply_backward(st, q, v, dq, dw)
+    assert e.value.status == 5
+    st.destroy()

@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "ttt_init_state": [cfgp, vp, vp, ctypes.POINTER(vp)],
             "ttt_chunk_forward": [vp, vp, vp, vp, vp, vp, vp],
             "ttt_sequence_forward": [vp, vp, vp, vp, vp, vp, i64, vp],
+            "ttt_apply_backward": [vp, vp, vp, vp, vp, vp],
             "ttt_get_state": [vp, vp, vp],
             "ttt_set_state": [vp, vp, vp],
             "ttt_state_health": [vp],
@@ -185,6 +186,13 @@ def ttt_chunk_forward(st: State, q, k, v, eta, out, stream=None) -> None:
                                    _stream(stream)))
 
 
+def ttt_apply_backward(st: State, q, dout, dq, dw, stream=None) -> None:
+    """Backward of one chunk's apply step with the state as it stands: dq [B,H,chunk,d] and
+    dw (state-shaped fp32) of sum <dout, f_W(q)> (see include/libttt.h)."""
+    _check(lib().ttt_apply_backward(st.handle, _ptr(q), _ptr(dout), _ptr(dq), _ptr(dw),
+                                    _stream(stream)))
+
+
 def ttt_sequence_forward(st: State, q, k, v, eta, out, seq_len: int, stream=None) -> None:
     _check(lib().ttt_sequence_forward(st.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                       _ptr(out), int(seq_len), _stream(stream)))
@@ -207,7 +215,7 @@ def ttt_destroy_state(st: State) -> None:
 
 
 STAGES = {"front_q": 0, "front_k": 1, "out": 2, "contract": 3, "ns_gram": 4, "ns_poly": 5,
-          "ns_update": 6, "renorm": 7, "split": 8, "mse": 9, "resident": 10}
+          "ns_update": 6, "renorm": 7, "split": 8, "mse": 9, "resident": 10, "dq": 11}
 
 
 def ttt_profile_begin(st: State, stage, max_launches: int = 4096) -> None:

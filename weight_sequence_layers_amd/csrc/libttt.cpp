@@ -11,6 +11,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "ttt_internal.h"
 
@@ -174,6 +175,7 @@ struct ttt_state {
   int ksplit = 1;
   u16 *xpl[2] = {}, *apl = nullptr, *bpl = nullptr;
   int* health = nullptr;
+  float* neg1 = nullptr;  // [sb] of -1: the apply backward's eta
   int contract_tiles = 0;
   bool resident = false;  // the device-resident chunk loop serves this state (Wpl unused)
   // measurement hooks
@@ -239,6 +241,7 @@ size_t layout(ttt_state* s, char* base) {
     ob = C.take<u16>(D.npm * D.nm * P * d * d);
   }
   size_t oh = C.take<int>(1);
+  const size_t on1 = s->resident ? 0 : C.take<float>(D.sb);
   if (base) {
     auto F = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
     auto H = [&](size_t o) { return reinterpret_cast<u16*>(base + o); };
@@ -276,6 +279,7 @@ size_t layout(ttt_state* s, char* base) {
       s->apl = H(oa); s->bpl = H(ob);
     }
     s->health = reinterpret_cast<int*>(base + oh);
+    if (!s->resident) s->neg1 = F(on1);
   }
   return C.off;
 }
@@ -382,6 +386,44 @@ ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
 }
 
 // Gradient of one token block; the contraction adds into G (first block writes it).
+// The chunk-summed contractions of one token block into G, and after the chunk's last
+// block into U (plain step; weight orientation) or the first Newton-Schulz input (muon).
+// ca holds the per-matrix operands and sizes.
+ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool first,
+                        bool last, hipStream_t st) {
+  const Dims& D = s->D;
+  const int P = D.P, d = D.d;
+  ca.G = s->G;
+  ca.accum_in = first ? 0 : 1;
+  ca.last = last ? 1 : 0;
+  ca.muon = muon;
+  const int64_t Z = (int64_t)D.nm * P;
+  if (ca.muon) ca.x = pbuf(s->xpl[0], D.nlp, Z * d * D.n, (int64_t)d * D.n, D.n);
+  ca.part = s->part;
+  ca.U = U;
+  ca.gpart = s->gpart;
+  ca.gpart_stride = (int64_t)D.nm * P * d * D.n;
+  ca.ksplit = s->ksplit;
+  ca.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
+  // operands of one launch share a plane count per side: group the matrices accordingly
+  int m0 = 0;
+  while (m0 < D.nm) {
+    int m1 = m0 + 1;
+    while (m1 < D.nm && ca.a[m1].planes == ca.a[m0].planes && ca.b[m1].planes == ca.b[m0].planes) ++m1;
+    ContractArgs cg = ca;
+    for (int m = m0; m < m1; ++m) { cg.a[m - m0] = ca.a[m]; cg.b[m - m0] = ca.b[m]; }
+    cg.G = s->G + (int64_t)m0 * P * d * D.n;
+    if (s->gpart) cg.gpart = s->gpart + (int64_t)m0 * P * d * D.n;
+    cg.U = U + (int64_t)m0 * P * d * D.n;
+    if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
+    cg.part = s->part + (int64_t)m0 * P * s->contract_tiles;
+    cg.tr_mask = ca.tr_mask >> m0;
+    STAGED(TTT_STAGE_CONTRACT, launch_contract(cg, m1 - m0, st));
+    m0 = m1;
+  }
+  return TTT_OK;
+}
+
 ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStream_t st) {
   const Dims& D = s->D;
   const ttt_config& c = s->cfg;
@@ -496,35 +538,7 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     if (mse) { ca.a[m] = colop(e, d); ca.b[m] = colop(hk, dh); }
     else { ca.a[m] = as_cols(xv, d); ca.b[m] = colop(pk, dh); }
   }
-  ca.G = s->G;
-  ca.accum_in = first ? 0 : 1;
-  ca.last = last ? 1 : 0;
-  ca.muon = c.ns_steps > 0;
-  const int64_t Z = (int64_t)D.nm * P;
-  if (ca.muon) ca.x = pbuf(s->xpl[0], D.nlp, Z * d * D.n, (int64_t)d * D.n, D.n);
-  ca.part = s->part;
-  ca.U = s->U;
-  ca.gpart = s->gpart;
-  ca.gpart_stride = (int64_t)D.nm * P * d * D.n;
-  ca.ksplit = s->ksplit;
-  ca.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
-  // operands of one launch share a plane count per side: group the matrices accordingly
-  int m0 = 0;
-  while (m0 < D.nm) {
-    int m1 = m0 + 1;
-    while (m1 < D.nm && ca.a[m1].planes == ca.a[m0].planes && ca.b[m1].planes == ca.b[m0].planes) ++m1;
-    ContractArgs cg = ca;
-    for (int m = m0; m < m1; ++m) { cg.a[m - m0] = ca.a[m]; cg.b[m - m0] = ca.b[m]; }
-    cg.G = s->G + (int64_t)m0 * P * d * D.n;
-    if (s->gpart) cg.gpart = s->gpart + (int64_t)m0 * P * d * D.n;
-    cg.U = s->U + (int64_t)m0 * P * d * D.n;
-    if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
-    cg.part = s->part + (int64_t)m0 * P * s->contract_tiles;
-    cg.tr_mask = ca.tr_mask >> m0;
-    STAGED(TTT_STAGE_CONTRACT, launch_contract(cg, m1 - m0, st));
-    m0 = m1;
-  }
-  return TTT_OK;
+  return contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
 }
 
 ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
@@ -551,6 +565,90 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
     a.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
     STAGED(TTT_STAGE_NS_UPDATE, launch_ns_update(a, st));
   }
+  return TTT_OK;
+}
+
+// Backward of the apply step over one block of query rows: dQ rows, and the weight
+// gradients of sum <dO, f_W(Q)> summed into dw over the chunk's blocks.  It reuses the
+// gradient path: the key-row front takes the queries as keys, dO as values and eta = -1
+// (the inner-product loss is then +sum <f(q), dO>), the contractions sum the weight
+// gradients (their plain-step output is the gradient itself), and k_dq forms
+// dQ = sum_m dZ_m W_m.
+ttt_status apply_bwd_rows(ttt_state* s, const Rows& R, bool first, bool last, float* dw,
+                          hipStream_t st) {
+  const Dims& D = s->D;
+  const ttt_config& c = s->cfg;
+  const size_t es = c.act == TTT_BF16 ? 2 : 4;
+  const int P = D.P, d = D.d, dh = D.dh;
+  const int64_t SB = D.sb;
+  const bool lin = c.fw == TTT_FW_LINEAR, sw = c.fw == TTT_FW_SWIGLU;
+  const char* q = R.q + R.t0 * d * es;
+  const char* o = R.v + R.t0 * d * es;   // dO rows
+  const int gi = D.in_kv, gp = D.gp;
+  auto tok = [&](u16* b, int np, int cols) {
+    return pbuf(b, np, (int64_t)P * SB * cols, SB * cols, cols);
+  };
+  Operand xq, xo;
+  if (c.act == TTT_F32) {
+    SplitArgs sa{};
+    sa.x_zstride = R.T * d; sa.x_bf16 = 0; sa.n = R.nr; sa.d = d;
+    sa.x = q; sa.out = tok(s->kpl, gi, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    xq = operand_of(sa.out, gi, R.nr);
+    sa.x = o; sa.out = tok(s->vpl, gi, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    xo = operand_of(sa.out, gi, R.nr);
+  } else {
+    xq = act_operand(q, R.T * d, d, R.nr);
+    xo = act_operand(o, R.T * d, d, R.nr);
+  }
+  auto as_cols = [&](Operand op, int cols) { op.rows = cols; return op; };
+  auto wop = [&](int m, int np) {
+    return operand_of(pbuf(s->Wpl[m], np, (int64_t)P * D.rows[m] * D.cols[m],
+                           (int64_t)D.rows[m] * D.cols[m], D.cols[m]), np, D.rows[m]);
+  };
+  auto colop = [&](const PlaneBuf& b, int cols) { return operand_of(b, b.np, cols); };
+  ContractArgs ca{};
+  ca.P = P; ca.M = d; ca.N = D.n; ca.K = R.nr;
+  DqArgs da{};
+  da.nrows = R.nr; da.N = d;
+  da.out = R.out + R.t0 * d * es; da.out_zstride = R.T * d; da.out_bf16 = c.act == TTT_BF16;
+  int np = 1;
+  if (lin) {
+    ca.a[0] = as_cols(xo, d); ca.b[0] = as_cols(xq, d);
+    da.a[0] = xo; da.b[0] = as_cols(wop(0, gp), d); da.K = d;
+  } else {
+    // P = H_q lands in the inner-product loss's P buffer, or for an MSE state in its
+    // hidden-activation buffer (the same shape; the MSE forward path has no P buffer)
+    u16* const pbuf_q = s->pk ? s->pk : s->hk;
+    if (!s->dz1 || !pbuf_q || (sw && !s->dz3))
+      return fail(TTT_E_HIP, "apply backward: gradient workspace missing");
+    const PlaneBuf dz1 = tok(s->dz1, gp, dh), pk = tok(pbuf_q, gp, dh);
+    PlaneBuf dz3{};
+    if (sw) dz3 = tok(s->dz3, gp, dh);
+    const int w2 = D.nm - 1;
+    FrontArgs f{};
+    f.A[0] = xq; f.A[1] = xo; f.B[0] = wop(0, gp);
+    if (sw) f.B[1] = wop(1, gp);
+    f.B[sw ? 2 : 1] =
+        operand_of(pbuf(s->Wpl[w2], gp, (int64_t)P * d * dh, (int64_t)d * dh, dh), gp, dh);
+    f.eta = s->neg1; f.eta_zstride = 0;
+    f.nrows = R.nr; f.K = d; f.N = dh;
+    f.o1 = dz1; f.o2 = dz3; f.o3 = pk;
+    STAGED(TTT_STAGE_FRONT_K, launch_front(sw ? FW_SWIGLU : FW_GELU, FRONT_K_DOT, f, P, st));
+    ca.a[0] = as_cols(xq, d); ca.b[0] = colop(dz1, dh);
+    int m = 1;
+    if (sw) { ca.a[1] = as_cols(xq, d); ca.b[1] = colop(dz3, dh); m = 2; }
+    ca.a[m] = as_cols(xo, d); ca.b[m] = colop(pk, dh);
+    da.a[0] = operand_of(dz1, gp, R.nr); da.b[0] = as_cols(wop(0, gp), d); da.K = dh;
+    if (sw) {
+      da.a[1] = operand_of(dz3, gp, R.nr); da.b[1] = as_cols(wop(1, gp), d);
+      np = 2;
+    }
+  }
+  ttt_status r = contract_all(s, ca, dw, false, first, last, st);
+  if (r != TTT_OK) return r;
+  STAGED(TTT_STAGE_DQ, launch_dq(da, np, P, st));
   return TTT_OK;
 }
 
@@ -692,6 +790,11 @@ ttt_status ttt_init_state(const ttt_config* cfg, const float* w0, void* stream,
                          per_head * r.heads * sizeof(float), hipMemcpyDeviceToDevice, hs);
     src += per_head * r.heads;
   }
+  if (e == hipSuccess && s->neg1) {
+    std::vector<float> m1((size_t)D.sb, -1.f);
+    e = hipMemcpyAsync(s->neg1, m1.data(), m1.size() * sizeof(float), hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);   // m1 is released on return
+  }
   if (e != hipSuccess) return cleanup(fail(TTT_E_HIP, "init copy failed: %s", hipGetErrorString(e)));
   st = refresh_planes(s, false, hs);
   if (st != TTT_OK) return cleanup(st);
@@ -703,6 +806,32 @@ ttt_status ttt_chunk_forward(ttt_state* s, const void* q, const void* k, const v
                              const float* eta, void* out, void* stream) {
   if (!s) return fail(TTT_E_NULL, "state is NULL");
   return forward(s, q, k, v, eta, out, s->cfg.chunk, 1, stream);
+}
+
+ttt_status ttt_apply_backward(ttt_state* s, const void* q, const void* dout, void* dq,
+                              float* dw, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  ttt_status r;
+  if ((r = check_ptr(q, "q")) || (r = check_ptr(dout, "dout")) || (r = check_ptr(dq, "dq")) ||
+      (r = check_ptr(dw, "dw")))
+    return r;
+  if (s->resident)
+    return fail(TTT_E_UNSUPPORTED, "the apply backward needs a state on the staged path");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s->last = st;
+  const Dims& D = s->D;
+  const int64_t b = s->cfg.chunk;
+  for (int64_t o = 0; o < b; o += D.sb) {
+    Rows R{};
+    R.q = static_cast<const char*>(q);
+    R.v = static_cast<const char*>(dout);
+    R.out = static_cast<char*>(dq);
+    R.T = b;
+    R.t0 = o;
+    R.nr = (int)std::min<int64_t>(D.sb, b - o);
+    if ((r = apply_bwd_rows(s, R, o == 0, o + D.sb >= b, dw, st)) != TTT_OK) return r;
+  }
+  return TTT_OK;
 }
 
 ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, const void* v,

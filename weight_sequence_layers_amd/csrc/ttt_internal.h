@@ -64,6 +64,16 @@ struct OutArgs {
   int swiglu;
 };
 
+// Backward of the apply step with respect to the queries: dQ [rows][dim] = sum over the
+// NP pairs of A_m [rows][hidden] (row-wise) times B_m = W_m [hidden][dim] (column-wise).
+struct DqArgs {
+  Operand a[2], b[2];
+  int nrows, K, N, tiles_n, tiles;
+  void* out;            // [problems][rows][dim] in the activation dtype
+  int64_t out_zstride;
+  int out_bf16;
+};
+
 // Token contractions: X_m[i][j] = sum_t A_m[t][i] B_m[t][j] for every matrix m and problem
 // (both operands token-major, read as columns).
 struct ContractArgs {
@@ -152,6 +162,7 @@ struct SmallArgs {
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s);
 hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s);
 hipError_t launch_contract(const ContractArgs& a, int nm, hipStream_t s);
+hipError_t launch_dq(const DqArgs& a, int np, int Z, hipStream_t s);
 // token ranges a contraction of `tiles` output tiles per matrix over nz matrices may split
 // into (the host sizes the partial-sum buffer with it)
 int contract_split_max(int tiles, int nz);

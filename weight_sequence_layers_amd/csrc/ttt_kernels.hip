@@ -205,6 +205,44 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
   return t;
 }
 
+// ------------------------------------------------------------------------ apply backward
+// dQ = sum_m dZ_m W_m for the NP (dZ_m, W_m) pairs: accumulator m takes pair m, and the
+// epilogue adds them and stores dQ like the apply output.
+template <int BM, int BN, int WGM, int WGN, int NP>
+__global__ __launch_bounds__(WGM * WGN * 64) void k_dq(DqArgs a) {
+  // W_m [hidden][dim] read column-wise; swapped accumulator layout for the packed store
+  using G = Gemm<BM, BN, WGM, WGN, NP, NP, 0, (1 << NP) - 1, 0, 64, true>;
+  GEMM_LDS(G);
+  const int lid = xcd_block(blockIdx.x, gridDim.x);
+  const int z = lid / a.tiles, tile = lid % a.tiles;
+  const int m0 = (tile / a.tiles_n) * BM;
+  const int n0 = (tile % a.tiles_n) * BN;
+  G g;
+  g.zero();
+  g.run(a.a, a.b, m0, n0, z, a.K, GEMM_STAGES);
+  if constexpr (NP == 2) {
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) g.acc[0][i][j] += g.acc[1][i][j];
+  }
+  const int cl = min(BN, a.N - n0);
+  const int rn = min(BM, a.nrows - m0);
+  if (a.out_bf16) {
+    PlaneBuf o;
+    o.base = static_cast<u16*>(a.out); o.plane_stride = 0; o.zstride = a.out_zstride;
+    o.ld = a.N; o.np = 1;
+    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, o, z, m0, n0, rn, cl);
+  } else {
+    g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
+      const int row = m0 + r, col = n0 + c;
+      if (row < a.nrows && col < a.N)
+        static_cast<float*>(a.out)[(int64_t)z * a.out_zstride + (int64_t)row * a.N + col] =
+            g.acc[0][i][j][v];
+    });
+  }
+}
+
 // ------------------------------------------------------------------------ contraction
 // PA = PB = 0: the operands' plane pairs run as K segments (any plane counts, K step 64).
 // Else A has PA planes and B has PB, all loaded once per K step of 32 (plane-resident).
@@ -647,6 +685,19 @@ static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
   if (a.tiles == 0 || Z == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq(const DqArgs& a0, int np, int Z, hipStream_t s) {
+  constexpr int BM = 128, BN = 128;
+  using G = Gemm<BM, BN, 2, 4, 1, 1>;   // block size
+  DqArgs a = a0;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  a.tiles = ((a.nrows + BM - 1) / BM) * a.tiles_n;
+  if (a.tiles == 0 || Z == 0) return hipSuccess;
+  if (np < 1 || np > 2) return hipErrorInvalidValue;
+  auto kern = np == 2 ? k_dq<BM, BN, 2, 4, 2> : k_dq<BM, BN, 2, 4, 1>;
   hipLaunchKernelGGL(kern, dim3(a.tiles * Z), dim3(G::NT), 0, s, a);
   return hipGetLastError();
 }
