@@ -70,6 +70,78 @@ def total_flops(cfg) -> float:
     return P * (cfg.seq_len * per_tok + cfg.n_chunks * ns)
 
 
+def apply_backward_flops(cfg) -> dict:
+    """Algorithmic FLOP of one apply-backward call (one chunk, all problems) per stage: the
+    front's Z and dH products, the weight-gradient contractions and dQ."""
+    P, b, d, dh = cfg.batch * cfg.heads, cfg.chunk, cfg.dim, cfg.hidden
+    nz = {"swiglu": 2, "gelu": 1, "linear": 1}[cfg.fw]
+    nm = {"swiglu": 3, "gelu": 2, "linear": 1}[cfg.fw]
+    if cfg.fw == "linear":
+        return {"contract": 2.0 * b * d * d * P, "dq": 2.0 * b * d * d * P}
+    return {"front_k": 2.0 * (nz + 1) * b * d * dh * P, "contract": 2.0 * nm * b * d * dh * P,
+            "dq": 2.0 * nz * b * d * dh * P}
+
+
+def bench_apply_backward(args, cfg, planes):
+    """Times ttt_apply_backward on the workload's first chunk (the queries and, as dO, the
+    values of that chunk) and prints one JSON line of its own."""
+    import numpy as np
+    import torch
+
+    import ttt_inputs as ti
+    import weight_sequence_layers_amd as W
+
+    c = W.make_config(cfg, planes=planes, path="staged")
+    b = cfg.chunk
+    P = cfg.batch * cfg.heads
+    dev = []
+    for name in ("q", "v"):
+        blocks = [ti.make_problem_inputs(cfg, bb, h, t1=b) for bb in range(cfg.batch)
+                  for h in range(cfg.heads)]
+        if cfg.act == "bf16":
+            x = np.stack([blk[name + "_bits"] for blk in blocks]).reshape(cfg.batch, cfg.heads, b, -1)
+            dev.append(torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16))
+        else:
+            x = np.stack([blk[name] for blk in blocks]).reshape(cfg.batch, cfg.heads, b, -1)
+            dev.append(torch.from_numpy(x).cuda())
+    w0 = torch.from_numpy(np.concatenate([w.ravel() for w in ti.make_weights(cfg)])).cuda()
+    st = W.ttt_init_state(c, w0)
+    dq = torch.empty_like(dev[0])
+    dw = torch.empty(W.ttt_state_numel(c), dtype=torch.float32, device="cuda")
+
+    def call():
+        W.ttt_apply_backward(st, dev[0], dev[1], dq, dw)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    flops = apply_backward_flops(cfg)
+    totals = {}
+    for name in flops:
+        W.ttt_profile_begin(st, name, 1 << 12)
+        call()
+        n, ms = W.ttt_profile_end(st)
+        if n:
+            totals[name] = (n, ms)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    st.destroy()
+    total = sum(flops.values())
+    print(json.dumps({
+        "metric": "apply-step backward tokens/sec (dq and dw of one chunk)",
+        "value": round(P * b / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_call": round(1e3 * dt, 3), "higher_is_better": True,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} (one chunk of {b} tokens, {P} problems)"},
+        "tflops_algorithmic": round(total / dt / 1e12, 2),
+        "per_stage_ms": {k: round(v[1], 3) for k, v in totals.items()},
+    }), flush=True)
+
+
 def recorded_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from profiles/<workload>_traffic.md, if that summary
     was taken from the current kernel sources; else None."""
@@ -179,6 +251,8 @@ def main():
                     help="comma-separated step sizes per matrix (state order); default 1")
     ap.add_argument("--weight-decay", type=float, default=0.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--apply-backward", action="store_true",
+                    help="time the apply-step backward on the workload's first chunk instead")
     ap.add_argument("--cpu-chunks", type=int, default=None)
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time hipBLASLt (torch.bmm) on each stage's GEMM shapes")
@@ -204,6 +278,9 @@ def main():
         cfg = cfg.replace(lr=tuple(float(x) for x in (args.lr or "").split(",") if x),
                           weight_decay=args.weight_decay)
     planes = tuple(int(x) for x in args.planes.split(",")) if args.planes else W.PRECISION[cfg.name]
+    if args.apply_backward:
+        bench_apply_backward(args, cfg, planes)
+        return
     c = W.make_config(cfg, planes=planes)
     torch.cuda.set_device(0)
     log(f"workload {cfg}  planes {planes}")
