@@ -79,3 +79,40 @@ def test_apply_backward_rejects_resident_states():
         W.ttt_apply_backward(st, q, v, dq, dw)
     assert e.value.status == 5
     st.destroy()
+
+
+def _backward_vs_oracle(cfg, problems, planes=None):
+    inp = ti.make_inputs(cfg)
+    c = W.make_config(cfg, planes=planes, path="staged")
+    q, k, v, eta, w0 = device_inputs(cfg, inp)
+    st = W.ttt_init_state(c, w0)
+    b = cfg.chunk
+    qc, dout = q[:, :, :b].contiguous(), v[:, :, :b].contiguous()
+    dq = torch.empty_like(qc)
+    dw = torch.empty(W.ttt_state_numel(c), dtype=torch.float32, device=DEV)
+    W.ttt_apply_backward(st, qc, dout, dq, dw)
+    torch.cuda.synchronize()
+    dq_g = dq.float().cpu().numpy()
+    dw_g = [x.cpu().numpy() for x in W.split_state(c, dw)]
+    st.destroy()
+    worst = 0.0
+    for bb, h in problems:
+        dQ, dWs = orc.apply_vjp(cfg.fw, [w[h] for w in inp["w0"]], inp["q"][bb, h, :b],
+                                inp["v"][bb, h, :b])
+        errs = [rel_err(dq_g[bb, h], dQ)] + [rel_err(g[bb, h], r) for g, r in zip(dw_g, dWs)]
+        worst = max(worst, max(errs))
+    print(f"{cfg.name}: apply backward max rel err {worst:.3e}", flush=True)
+    return worst
+
+
+def test_apply_backward_lm_full_size():
+    # the LM layer's chunk (2048 tokens, 8 problems, dim 512, hidden 1024) in its preset
+    cfg = ti.CONFIGS["lm"].replace(seq_len=2048)
+    assert _backward_vs_oracle(cfg, [(0, 0), (3, 1)]) <= TOL["bf16"]
+
+
+def test_apply_backward_chunk_longer_than_a_block():
+    # 140000 tokens: blocks of 65536, 65536 and 8928 whose weight gradients accumulate
+    cfg = ti.Config("bwdlong", 1, 1, 140000, 140000, 64, 128, "swiglu", "dot", 5, True,
+                    "bf16", "update_then_apply", 63)
+    assert _backward_vs_oracle(cfg, [(0, 0)]) <= TOL["bf16"]
