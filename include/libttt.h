@@ -107,8 +107,9 @@ typedef struct {
    * state's matrix order (SwiGLU W1, W3, W2; GELU W1, W2; linear W); 0 selects 1, and
    * entries past the net's matrices are ignored.  Each lr[i] must be finite and >= 0;
    * weight_decay finite and in [0, 1).  Zero-initialised fields give the plain step
-   * W <- W - U.  (Modular TTT: learning rate and weight decay as design dimensions of the
-   * inner learner; LaCT §4.2: a smaller Muon step when the loss oscillates.)            */
+   * W <- W - U.  (The Modular TTT abstract names the learning rate and the weight decay as
+   * design dimensions of the inner learner; the LaCT explainer page, §4.2, suggests a
+   * smaller Muon step when the loss oscillates.)                                         */
   float lr[3];
   float weight_decay;
 } ttt_config;
@@ -144,10 +145,11 @@ ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, cons
                                 const float* eta, void* out, int64_t seq_len, void* stream);
 
 /*
- * Backward of one chunk's apply step ([LaCT] §2.1 apply phase, eq. 2; the query-view rule
- * of Modular TTT's train-view forward / backward / query-view decomposition).  With the
- * state as it stands (the state that chunk's queries were answered with: call it before
- * that chunk's ttt_chunk_forward, or restore it with ttt_set_state), computes for every
+ * Backward of one chunk's apply step (the LaCT explainer page, §2.1, eq. 2; the query-view
+ * rule of the train-view forward / backward / query-view split the Modular TTT abstract
+ * describes).  With the state as it stands -- the state that chunk's queries were answered
+ * with: before that chunk's ttt_chunk_forward under the shifted order, after it under the
+ * update-then-apply order, or any state restored with ttt_set_state -- computes for every
  * (batch, head) problem
  *   dq = d/dQ  sum_t <dout_t, f_W(q_t)>      [B][H][chunk][dim], activation dtype
  *   dw = d/dW  sum_t <dout_t, f_W(q_t)>      fp32, the ttt_get_state layout (every matrix)
