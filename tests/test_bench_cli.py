@@ -25,3 +25,15 @@ def test_cpu_baseline_leg_reports_its_sample():
     assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
     assert res["cores"] >= 1 and "1 of 1" in res["sample"]
     json.dumps(res)
+
+
+@pytest.mark.parametrize("name", ["tiny", "lm", "long", "imageset"])
+def test_stage_flops_add_up_to_the_layer_total(name):
+    # the per-stage algorithmic FLOP the roofline uses sum to the layer's total
+    sys.path.insert(0, ROOT)
+    import bench
+    import ttt_inputs as ti
+    cfg = ti.CONFIGS[name]
+    f = bench.stage_flops(cfg)
+    total = sum(v for k, v in f.items() if k != "resident")
+    assert abs(total - bench.total_flops(cfg)) <= 1e-9 * total

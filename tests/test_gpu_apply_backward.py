@@ -116,3 +116,30 @@ def test_apply_backward_chunk_longer_than_a_block():
     cfg = ti.Config("bwdlong", 1, 1, 140000, 140000, 64, 128, "swiglu", "dot", 5, True,
                     "bf16", "update_then_apply", 63)
     assert _backward_vs_oracle(cfg, [(0, 0)]) <= TOL["bf16"]
+
+
+def test_apply_backward_leaves_state_and_is_linear_in_dout_bitwise():
+    # the state is not touched; dO scaled by 2 (exact in bf16) scales dq and dw by exactly 2
+    cfg = ti.Config("bwdinv", 2, 2, 256, 256, 80, 176, "swiglu", "dot", 5, True, "bf16",
+                    "apply_then_update", 64)
+    inp = ti.make_inputs(cfg)
+    c = W.make_config(cfg, path="staged")
+    q, k, v, eta, w0 = device_inputs(cfg, inp)
+    st = W.ttt_init_state(c, w0)
+    n = W.ttt_state_numel(c)
+    before = torch.empty(n, dtype=torch.float32, device=DEV)
+    after = torch.empty_like(before)
+    W.ttt_get_state(st, before)
+    res = []
+    for scale in (1.0, 2.0):
+        dout = (v * scale).contiguous()
+        dq = torch.empty_like(q)
+        dw = torch.empty(n, dtype=torch.float32, device=DEV)
+        W.ttt_apply_backward(st, q, dout, dq, dw)
+        res.append((dq.float().cpu(), dw.cpu()))
+    W.ttt_get_state(st, after)
+    torch.cuda.synchronize()
+    st.destroy()
+    assert torch.equal(before, after)
+    assert torch.equal(res[1][0], 2.0 * res[0][0])
+    assert torch.equal(res[1][1], 2.0 * res[0][1])
