@@ -143,3 +143,25 @@ def test_apply_backward_leaves_state_and_is_linear_in_dout_bitwise():
     assert torch.equal(before, after)
     assert torch.equal(res[1][0], 2.0 * res[0][0])
     assert torch.equal(res[1][1], 2.0 * res[0][1])
+
+
+def test_apply_backward_argument_checks():
+    # null and misaligned pointers are refused on the host, before anything is enqueued
+    cfg = ti.Config("bwdarg", 1, 1, 64, 64, 64, 128, "swiglu", "dot", 0, False, "f32",
+                    "apply_then_update", 65)
+    inp = ti.make_inputs(cfg)
+    c = W.make_config(cfg, path="staged")
+    q, k, v, eta, w0 = device_inputs(cfg, inp)
+    st = W.ttt_init_state(c, w0)
+    dq = torch.empty_like(q)
+    dw = torch.empty(W.ttt_state_numel(c) + 4, dtype=torch.float32, device=DEV)
+    L = W.lib()
+    assert L.ttt_apply_backward(st.handle, q.data_ptr(), v.data_ptr(), None, dw.data_ptr(),
+                                None) == 1
+    assert L.ttt_apply_backward(st.handle, q.data_ptr(), v.data_ptr(), dq.data_ptr(),
+                                dw.data_ptr() + 4, None) == 9
+    assert L.ttt_apply_backward(None, q.data_ptr(), v.data_ptr(), dq.data_ptr(),
+                                dw.data_ptr(), None) == 1
+    W.ttt_apply_backward(st, q, v, dq, dw[:W.ttt_state_numel(c)])
+    torch.cuda.synchronize()
+    st.destroy()
