@@ -123,7 +123,11 @@ ttt_status ttt_state_numel(const ttt_config* cfg, int64_t* numel);
 
 /*
  * Create a state: allocate the fast weights and every workspace buffer on the current
- * HIP device, and copy the initial weights.  w0 (device, fp32) holds the per-head initial
+ * HIP device, and copy the initial weights.  The fast weights are the layer's hidden
+ * state: the inner model's parameters, changed by every update (TTT-layer explainer page,
+ * aivaro.ru, §3 step 2 and §4 "hidden state"); their size does not grow with the context
+ * (the second TTT-E2E page, intelliparadigm.com, §3.2: constant memory in the sequence
+ * length), so the whole state and workspace are sized here, once, from the configuration.  w0 (device, fp32) holds the per-head initial
  * matrices, matrix by matrix, each [heads][rows][cols] row-major:
  *   SWIGLU: W1 [H][hidden][dim], W3 [H][hidden][dim], W2 [H][dim][hidden]
  *   GELU:   W1 [H][hidden][dim], W2 [H][dim][hidden];   LINEAR: W [H][dim][dim]
@@ -134,13 +138,19 @@ ttt_status ttt_init_state(const ttt_config* cfg, const float* w0, void* stream,
                           ttt_state** out);
 
 /* One chunk: q, k, v, out [batch][heads][chunk][dim]; eta [batch][heads][chunk].  out
- * receives the chunk's outputs, the state advances by one update.                   */
+ * receives the chunk's outputs, the state advances by one update: the LaCT page's apply
+ * and update phases (§2.1) for one chunk, with the state passed in and carried out
+ * explicitly as in the forward(x, state) of the TTT-E2E page (jsqmd.com, §2.1.1).     */
 ttt_status ttt_chunk_forward(ttt_state* s, const void* q, const void* k, const void* v,
                              const float* eta, void* out, void* stream);
 
 /* A whole sequence: tensors [batch][heads][seq_len][dim], eta [batch][heads][seq_len];
  * seq_len must be a multiple of the chunk size (0 is allowed and does nothing).  Equal,
- * bit for bit, to seq_len/chunk calls of ttt_chunk_forward on the consecutive chunks.  */
+ * bit for bit, to seq_len/chunk calls of ttt_chunk_forward on the consecutive chunks:
+ * the chunk loop of the LaCT page (§3.2, Fig. 3c, shifted block-causal; §3.1 a single
+ * whole-sequence chunk for image sets), consecutive blocks sharing one fast-weight state
+ * (TTT-E2E page, jsqmd.com, §3.2.2; the overlap between blocks that section also
+ * describes is not made).                                                            */
 ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, const void* v,
                                 const float* eta, void* out, int64_t seq_len, void* stream);
 
@@ -164,12 +174,17 @@ ttt_status ttt_apply_backward(ttt_state* s, const void* q, const void* dout, voi
                               float* dw, void* stream);
 
 /* Copy the fp32 state out / in.  Layout: matrix by matrix, each [batch][heads][rows][cols]
- * with the shapes listed under ttt_init_state.  dst/src: device, ttt_state_numel values. */
+ * with the shapes listed under ttt_init_state.  dst/src: device, ttt_state_numel values.
+ * The state is what carries over from one step to the next (TTT-layer explainer page,
+ * §3 step 5): reading it and writing it back resumes a sequence where it stopped.      */
 ttt_status ttt_get_state(const ttt_state* s, float* dst, void* stream);
 ttt_status ttt_set_state(ttt_state* s, const float* src, void* stream);
 
 /* Wait for the state's work and report TTT_E_NONFINITE if any update so far produced a
- * NaN or Inf row norm in the fast weights (the flag is sticky until ttt_set_state).    */
+ * NaN or Inf row norm in the fast weights (the flag is sticky until ttt_set_state).
+ * An update step too large for the inner learner is the instability the TTT-E2E page
+ * (jsqmd.com, §4.2) lists first among its failure modes, and the second TTT-E2E page
+ * closes by advising to watch the size of the parameter updates; this is that watch.   */
 ttt_status ttt_state_health(ttt_state* s);
 
 /* Wait for the state's work and free it.  NULL is accepted.                            */
@@ -183,7 +198,7 @@ ttt_status ttt_destroy_state(ttt_state* s);
  * Stages: 0 front (query rows), 1 front (key rows), 2 output GEMM, 3 token contraction,
  * 4 Newton-Schulz Gram, 5 Newton-Schulz polynomial, 6 Newton-Schulz update,
  * 7 update + renorm, 8 fp32 plane split, 9 MSE error / dH GEMMs,
- * 10 device-resident chunk loop (one launch per call).
+ * 10 device-resident chunk loop (one launch per call), 11 the apply backward's dQ GEMM.
  * The hooks create and destroy HIP events but allocate no device memory.
  */
 typedef enum {

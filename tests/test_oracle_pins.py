@@ -449,6 +449,59 @@ def test_apply_backward_weights_equal_the_inner_product_gradient_at_eta_minus_on
             assert np.abs(a - b).max() < 1e-13
 
 
+# ------------------------------------------------------------------ sampled rows, all problems
+SAMPLE_ROWS = np.array([0, 5, 7, 8, 13, 15, 16, 23, 24, 30, 31])
+
+
+def apply_rows_error(order, seed=41):
+    """The apply_rows branch of the sequence loop (it writes stored samples of runs too long
+    to keep whole) against the per-token brute force, which computes every row: rows in
+    every chunk, each chunk's first and last token among them, token blocks shorter than
+    a chunk, and rows outside the sample left at zero."""
+    cfg = _cfg("swiglu", "dot", 5, True, order, chunk=8, T=32, d=4, dh=6)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(seed))
+    O, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, eta, block_rows=3, apply_rows=SAMPLE_ROWS)
+    Ob, Wb = orc.sequence_forward_bruteforce(cfg, Ws, Q, K, V, eta)
+    rest = np.setdiff1d(np.arange(cfg.seq_len), SAMPLE_ROWS)
+    if np.any(O[rest] != 0.0):
+        return np.inf
+    err = np.abs(O[SAMPLE_ROWS] - Ob[SAMPLE_ROWS]).max() / np.abs(Ob).max()
+    for a, b in zip(Wf, Wb):
+        err = max(err, np.abs(a - b).max() / np.abs(b).max())
+    return err
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+def test_apply_rows_match_the_bruteforce_rows(order):
+    assert apply_rows_error(order) <= 1e-12
+
+
+def forward_all_error(seed=1234):
+    """forward_all over a batch of 2 and 3 heads against the per-token brute force run on
+    each problem's own inputs regenerated alone (its token blocks, and its head's initial
+    weights), so that a wrong head, batch element or tensor fails."""
+    import ttt_inputs as ti
+    cfg = Config("fa", 2, 3, 12, 4, 4, 6, "swiglu", "dot", 5, True, "f32",
+                 "apply_then_update", seed)
+    res = orc.forward_all(cfg, ti.make_inputs(cfg))
+    weights = ti.make_weights(cfg)
+    err = 0.0
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            p = ti.make_problem_inputs(cfg, b, h)
+            Ob, Wb = orc.sequence_forward_bruteforce(cfg, [w[h] for w in weights], p["q"], p["k"],
+                                                     p["v"], p["eta"])
+            Og, Wg = res[(b, h)]
+            err = max(err, np.abs(Og - Ob).max() / np.abs(Ob).max())
+            for a, c in zip(Wg, Wb):
+                err = max(err, np.abs(a - c).max() / np.abs(c).max())
+    return err
+
+
+def test_forward_all_runs_each_problem_on_its_own_inputs():
+    assert forward_all_error() <= 1e-12
+
+
 # ------------------------------------------------------------------ mutation tests
 def _all_pins_pass():
     try:
@@ -474,6 +527,9 @@ def _all_pins_pass_inner():
     checks.append(linear_dot_step_closed_form_error("apply_then_update") <= 1e-12)
     lo, hi = muon_step_band()
     checks.append(lo > 0.68 and hi < 1.21)
+    checks.append(apply_rows_error("apply_then_update") <= 1e-12)
+    checks.append(apply_rows_error("update_then_apply") <= 1e-12)
+    checks.append(forward_all_error() <= 1e-12)
     return all(checks)
 
 
@@ -547,6 +603,40 @@ def _mut_step_before_ns(Ws, grads, ns_steps, renorm, lr=None, weight_decay=0.0):
     return out
 
 
+_ORIG_SEQ = orc.sequence_forward
+
+
+def _mut_rows_offset(cfg, W0s, Q, K, V, eta, block_rows=8192, apply_rows=None, n_chunks=None):
+    # the sampled rows of chunk c answered with the queries at (row - chunk start)
+    if apply_rows is not None:
+        Q = np.array(Q, np.float64)
+        rows = np.asarray(apply_rows)
+        Q[rows] = Q[rows - (rows // cfg.chunk) * cfg.chunk]
+    return _ORIG_SEQ(cfg, W0s, Q, K, V, eta, block_rows, apply_rows, n_chunks)
+
+
+def _mut_forward_all_head(cfg, inputs, problems=None, block_rows=8192):
+    # the initial weights indexed by the batch element instead of the head
+    out = {}
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            W0s = [w[b % cfg.heads] for w in inputs["w0"]]
+            out[(b, h)] = orc.sequence_forward(cfg, W0s, inputs["q"][b, h], inputs["k"][b, h],
+                                               inputs["v"][b, h], inputs["eta"][b, h], block_rows)
+    return out
+
+
+def _mut_forward_all_qk(cfg, inputs, problems=None, block_rows=8192):
+    # keys passed where the queries go
+    out = {}
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            W0s = [w[h] for w in inputs["w0"]]
+            out[(b, h)] = orc.sequence_forward(cfg, W0s, inputs["k"][b, h], inputs["k"][b, h],
+                                               inputs["v"][b, h], inputs["eta"][b, h], block_rows)
+    return out
+
+
 @pytest.mark.parametrize("name,target,mut", [
     ("silu' term", "silu_prime", _mut_silu_prime),
     ("error sign", "_output_error", _mut_output_error),
@@ -556,6 +646,9 @@ def _mut_step_before_ns(Ws, grads, ns_steps, renorm, lr=None, weight_decay=0.0):
     ("g2 index", "_block_gradient", _mut_block_grad_transposed),
     ("decay after the step", "update_state", _mut_decay_after_step),
     ("step size before NS", "update_state", _mut_step_before_ns),
+    ("sampled rows offset", "sequence_forward", _mut_rows_offset),
+    ("forward_all head index", "forward_all", _mut_forward_all_head),
+    ("forward_all keys as queries", "forward_all", _mut_forward_all_qk),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, target, mut):
     monkeypatch.setattr(orc, target, mut)

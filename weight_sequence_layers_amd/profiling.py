@@ -39,6 +39,7 @@ STAGE_KERNELS = [
     ("renorm", r"k_renorm"),
     ("split", r"k_split"),
     ("resident", r"k_small_gelu<"),
+    ("dq", r"k_dq<"),
 ]
 
 
