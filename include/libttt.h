@@ -191,6 +191,31 @@ ttt_status ttt_state_health(ttt_state* s);
 ttt_status ttt_destroy_state(ttt_state* s);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): ttt_sequence_forward without a state
+ * object and without any allocation.
+ *   state  device fp32, ttt_state_numel(cfg) values in the ttt_get_state layout: read as the
+ *          initial fast weights of every (batch, head) problem, overwritten with the final
+ *          ones.  Caller-owned, 16-byte aligned.
+ *   q, k, v, eta, out, seq_len, stream: as for ttt_sequence_forward.
+ * All workspace comes from one static device array of TTT_NOALLOC_SCRATCH_BYTES bytes (64
+ * MiB), which each GPU the library runs on holds from the first call until the process
+ * ends.  A configuration whose workspace is larger (e.g. the LaCT language-model layer
+ * with 8 problems of dim 512 and hidden 1024) returns TTT_E_SHAPE, with both sizes in
+ * ttt_last_error; that and every other argument check runs on the host before any HIP
+ * call.  The call makes no hipMalloc, hipFree or memset; it enqueues kernels on stream and
+ * returns without waiting.  All calls on one GPU share that GPU's array and it keeps the
+ * last call's contents: calls that overlap on one GPU (two streams, two threads) race and
+ * corrupt each other's results, so serialise them.  There is no health flag to query.
+ * Given the same configuration, weights and inputs, the results equal those of
+ * ttt_sequence_forward on a state created by ttt_init_state, bit for bit.
+ */
+#define TTT_NOALLOC_SCRATCH_BYTES 67108864
+ttt_status ttt_sequence_forward_noalloc(const ttt_config* cfg, float* state, const void* q,
+                                        const void* k, const void* v, const float* eta,
+                                        void* out, int64_t seq_len, void* stream);
+
+/*
  * Measurement hooks.  Between ttt_profile_begin and ttt_profile_end, every launch of the
  * chosen stage kernel on the state's stream is bracketed by a pair of HIP events (at most
  * max_launches launches are timed; later ones run untimed).  ttt_profile_end waits for the

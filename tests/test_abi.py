@@ -145,3 +145,28 @@ def _base(**kw):
                 act="bf16", order="apply_then_update", ns_steps=5, renorm=True)
     base.update(kw)
     return base
+
+
+def test_noalloc_call_rejects_on_the_host():
+    """The allocation-free call checks its arguments and its workspace limit before any HIP
+    call, so these run without a GPU: the LaCT language-model layer (8 problems of dim 512,
+    hidden 1024) needs more workspace than the call holds."""
+    L = W.lib()
+    lm = _cfg(batch=4, heads=2, dim=512, hidden=1024, chunk=2048)
+    p = 0x10000
+    assert L.ttt_sequence_forward_noalloc(ctypes.byref(lm), p, p, p, p, p, p, 4096, None) == 2
+    msg = L.ttt_last_error().decode()
+    assert "workspace" in msg and str(W.NOALLOC_SCRATCH_BYTES) in msg
+    small = _cfg()
+    assert L.ttt_sequence_forward_noalloc(None, p, p, p, p, p, p, 64, None) == 1
+    assert L.ttt_sequence_forward_noalloc(ctypes.byref(small), None, p, p, p, p, p, 64, None) == 1
+    assert L.ttt_sequence_forward_noalloc(ctypes.byref(small), p + 8, p, p, p, p, p, 64, None) == 9
+    assert L.ttt_sequence_forward_noalloc(ctypes.byref(small), p, p, p, p, p, p, 65, None) == 2
+    assert L.ttt_sequence_forward_noalloc(ctypes.byref(small), p, None, p, p, p, p, 64, None) == 1
+    assert L.ttt_sequence_forward_noalloc(ctypes.byref(_cfg(dim=72)), p, p, p, p, p, p, 64,
+                                          None) == 2
+
+
+def test_noalloc_limit_matches_the_header():
+    m = re.search(r"#define\s+TTT_NOALLOC_SCRATCH_BYTES\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == W.NOALLOC_SCRATCH_BYTES

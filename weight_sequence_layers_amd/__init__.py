@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "ttt_set_state": [vp, vp, vp],
             "ttt_state_health": [vp],
             "ttt_destroy_state": [vp],
+            "ttt_sequence_forward_noalloc": [cfgp, vp, vp, vp, vp, vp, vp, i64, vp],
             "ttt_profile_begin": [vp, ctypes.c_int32, ctypes.c_int32],
             "ttt_profile_end": [vp, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)],
         }
@@ -196,6 +197,20 @@ def ttt_apply_backward(st: State, q, dout, dq, dw, stream=None) -> None:
 def ttt_sequence_forward(st: State, q, k, v, eta, out, seq_len: int, stream=None) -> None:
     _check(lib().ttt_sequence_forward(st.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                       _ptr(out), int(seq_len), _stream(stream)))
+
+
+# workspace bytes the allocation-free call holds per GPU (TTT_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def ttt_sequence_forward_noalloc(cfg: ttt_config, state, q, k, v, eta, out, seq_len: int,
+                                 stream=None) -> None:
+    """ttt_sequence_forward with no state object and no allocation: `state` (fp32 device
+    tensor, the ttt_get_state layout) holds the initial weights and receives the final ones
+    (see include/libttt.h)."""
+    _check(lib().ttt_sequence_forward_noalloc(ctypes.byref(cfg), _ptr(state), _ptr(q), _ptr(k),
+                                              _ptr(v), _ptr(eta), _ptr(out), int(seq_len),
+                                              _stream(stream)))
 
 
 def ttt_get_state(st: State, dst, stream=None) -> None:

@@ -195,8 +195,10 @@ struct Carver {
   }
 };
 
-// Plan the arena layout; with base == nullptr only the size is computed.
-size_t layout(ttt_state* s, char* base) {
+// Plan the arena layout; with base == nullptr only the size is computed.  With ext_w the
+// fp32 state lives in that caller buffer instead of the arena (and no apply-backward
+// buffer is carved: only the allocation-free sequence call lays a state out so).
+size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
   const Dims& D = s->D;
   const ttt_config& c = s->cfg;
   const int64_t P = D.P, d = D.d, dh = D.dh, n = D.n, sb = D.sb;
@@ -204,7 +206,8 @@ size_t layout(ttt_state* s, char* base) {
   const bool lin = c.fw == TTT_FW_LINEAR;
   const bool f32 = c.act == TTT_F32;
   Carver C;
-  size_t oW = C.take<float>(state_numel(D)), oU = C.take<float>(state_numel(D));
+  size_t oW = ext_w ? 0 : C.take<float>(state_numel(D));
+  size_t oU = C.take<float>(state_numel(D));
   size_t oWpl[3];
   for (int m = 0; m < D.nm; ++m) oWpl[m] = C.take<u16>(D.wp * P * D.rows[m] * D.cols[m]);
   size_t oq = 0, ok = 0, ov = 0;
@@ -241,11 +244,11 @@ size_t layout(ttt_state* s, char* base) {
     ob = C.take<u16>(D.npm * D.nm * P * d * d);
   }
   size_t oh = C.take<int>(1);
-  const size_t on1 = s->resident ? 0 : C.take<float>(D.sb);
+  const size_t on1 = (s->resident || ext_w) ? 0 : C.take<float>(D.sb);
   if (base) {
     auto F = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
     auto H = [&](size_t o) { return reinterpret_cast<u16*>(base + o); };
-    s->W = F(oW);
+    s->W = ext_w ? ext_w : F(oW);
     s->U = F(oU);
     int64_t acc = 0;
     for (int m = 0; m < D.nm; ++m) {
@@ -279,7 +282,7 @@ size_t layout(ttt_state* s, char* base) {
       s->apl = H(oa); s->bpl = H(ob);
     }
     s->health = reinterpret_cast<int*>(base + oh);
-    if (!s->resident) s->neg1 = F(on1);
+    if (!s->resident && !ext_w) s->neg1 = F(on1);
   }
   return C.off;
 }
@@ -734,6 +737,55 @@ ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, co
 }
 
 }  // namespace
+
+// ============================================================================ workspace-only runs
+namespace ttt {
+
+// A whole sequence with the fp32 state in the caller's buffer w (read, then overwritten
+// with the final state) and every workspace buffer carved from ws (ws_bytes long); no
+// allocation.  With ws == nullptr only the checks run and *need receives the workspace
+// size.  The host checks (configuration, pointers, seq_len, workspace size) all run
+// before any HIP call.
+ttt_status sequence_in_workspace(const ttt_config* cfg, float* w, const void* q, const void* k,
+                                 const void* v, const float* eta, void* out, int64_t seq_len,
+                                 char* ws, size_t ws_bytes, size_t* need, void* stream) {
+  ttt_config r;
+  ttt_status st = resolve(cfg, &r);
+  if (st != TTT_OK) return st;
+  if ((st = check_ptr(w, "state")) != TTT_OK) return st;
+  if (seq_len < 0) return fail(TTT_E_SHAPE, "seq_len is negative");
+  if (seq_len % r.chunk)
+    return fail(TTT_E_SHAPE, "seq_len %lld is not a multiple of the chunk %d",
+                (long long)seq_len, r.chunk);
+  if (seq_len > 0 && ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) ||
+                      (st = check_ptr(v, "v")) || (st = check_ptr(eta, "eta")) ||
+                      (st = check_ptr(out, "out"))))
+    return st;
+  ttt_state s;
+  s.cfg = r;
+  s.D = dims_of(r);
+  s.resident = r.path == TTT_PATH_RESIDENT;
+  const size_t bytes = layout(&s, nullptr, w);
+  if (need) *need = bytes;
+  if (bytes > ws_bytes)
+    return fail(TTT_E_SHAPE,
+                "this configuration needs %zu bytes of workspace; the allocation-free call "
+                "holds %zu", bytes, ws_bytes);
+  if (!ws) return TTT_OK;
+  layout(&s, ws, w);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  s.last = hs;
+  // the array keeps the previous call's contents: the health flag is the one buffer read
+  // before it is written
+  HIP_TRY(launch_fill_zero(s.health, 1, hs));
+  if (!s.resident && (st = refresh_planes(&s, false, hs)) != TTT_OK) return st;
+  if (seq_len == 0) return TTT_OK;
+  return forward(&s, q, k, v, eta, out, seq_len, seq_len / r.chunk, stream);
+}
+
+ttt_status report(ttt_status st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace ttt
 
 // ============================================================================ C ABI
 extern "C" {

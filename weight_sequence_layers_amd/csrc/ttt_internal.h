@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "libttt.h"
 #include "ttt_device.hpp"
 
 namespace ttt {
@@ -175,6 +176,17 @@ hipError_t launch_small(const SmallArgs& a, int loss, hipStream_t s);
 bool small_supported(int fw, int ns_steps, int renorm, int act_bf16, int apply_first, int dim,
                      int hidden, int chunk, int ap, int gp);
 hipError_t prepare_kernels();  // raise dynamic-LDS limits once per process
+// n int32 zeros at p (a kernel, not a memset: also safe inside a captured graph)
+hipError_t launch_fill_zero(int* p, int n, hipStream_t s);
+
+// A whole sequence with the fp32 state in the caller's buffer w and all workspace carved
+// from ws (ws_bytes), allocating nothing; with ws == nullptr only the host checks run and
+// *need gets the workspace size (libttt.cpp).
+// Set the calling thread's last-error message (ttt_last_error) and return st.
+ttt_status report(ttt_status st, const char* msg);
+ttt_status sequence_in_workspace(const ttt_config* cfg, float* w, const void* q, const void* k,
+                                 const void* v, const float* eta, void* out, int64_t seq_len,
+                                 char* ws, size_t ws_bytes, size_t* need, void* stream);
 
 // tile sizes used by the contraction and Newton-Schulz stages (the host sizes buffers)
 constexpr int CONTRACT_BM = 128, CONTRACT_BN = 128;

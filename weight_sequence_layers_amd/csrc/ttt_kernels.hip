@@ -846,6 +846,16 @@ hipError_t launch_split(const SplitArgs& a, int Z, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_fill_zero(int* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+hipError_t launch_fill_zero(int* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_zero, dim3(std::min(1024, (n + 255) / 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t prepare_kernels() { return hipSuccess; }
 
 }  // namespace ttt
