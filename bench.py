@@ -247,7 +247,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lm")
-    ap.add_argument("--planes", default=None, help="apply,grad,ns,ns_lead bf16 plane counts")
+    ap.add_argument("--planes", default=None, help="apply,grad,ns bf16 plane counts and the ns_one_plane iteration mask")
     ap.add_argument("--lr", default=None,
                     help="comma-separated step sizes per matrix (state order); default 1")
     ap.add_argument("--weight-decay", type=float, default=0.0)
@@ -375,7 +375,7 @@ def main():
                                f"{cfg.hidden}, {cfg.fw}/{cfg.loss}, ns {cfg.ns_steps}, renorm "
                                f"{int(cfg.renorm)}, {cfg.act}, {cfg.order}",
                    "global_batch": cfg.batch, "seq_len": cfg.seq_len, "parallelism": "none",
-                   "bf16_planes_apply_grad_ns_nslead": list(planes),
+                   "bf16_planes_apply_grad_ns": list(planes[:3]), "ns_one_plane_iterations": [i for i in range(8) if (planes[3] >> i) & 1],
                    **({"lr": list(cfg.step_sizes()), "weight_decay": cfg.weight_decay}
                       if (cfg.lr or cfg.weight_decay) else {})},
         "source_digest": source_digest(),

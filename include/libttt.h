@@ -73,14 +73,20 @@ typedef enum { TTT_PATH_AUTO = 0, TTT_PATH_STAGED = 1, TTT_PATH_RESIDENT = 2 } t
  * elementwise math is fp32; the state is fp32.  An fp32 operand is fed to the MFMA as a
  * sum of `planes` bf16 numbers (1: plain bf16; 2: hi+lo, ~16 significant bits; 3: ~24
  * bits), and products of planes i, j are kept when i + j < max(planes of the two sides).
- * bf16 activations are exact in one plane.  Each field below is 1, 2 or 3:
+ * bf16 activations are exact in one plane.  Each of the first three fields is 1, 2 or 3:
  *   apply_planes   fast weights and hidden activations on the query (apply) path
  *   grad_planes    fast weights, back-propagated errors and fp32 activations on the
  *                  gradient path (the one that carries the state from chunk to chunk)
- *   ns_planes      every Newton-Schulz iteration after the first
- *   ns_lead_planes the first Newton-Schulz iteration
+ *   ns_planes      the Newton-Schulz iterates X (stored between iterations) and the
+ *                  operands of every iteration not named in ns_one_plane
  * A value of 0 selects the default: 3 for fp32 activations, else 1 (apply), 2 (grad),
- * 2 (ns, ns_lead).
+ * 2 (ns).
+ *   ns_one_plane   bit i set: Newton-Schulz iteration i multiplies one bf16 plane of each
+ *                  operand (X X^T, A A and B X), and its linear term a X is added outside
+ *                  the products from X's ns_planes planes.  An early iteration acts on small
+ *                  singular values, where b A + c A^2 is small beside a I, so its products
+ *                  tolerate plain bf16 as long as a X keeps the stored precision.  Bits at
+ *                  or above ns_steps, or with ns_planes 1, change nothing.  0..255.
  *
  * Execution path.  STAGED runs each chunk as a sequence of stage kernels (any supported
  * configuration).  RESIDENT runs all chunks of a call in one kernel that keeps each
@@ -99,7 +105,7 @@ typedef struct {
   int32_t order;      /* ttt_order */
   int32_t ns_steps;   /* 0: W <- W - grad;  n > 0: W <- W - NS_n(grad)  (Muon uses 5) */
   int32_t row_renorm; /* 0 or 1 */
-  int32_t apply_planes, grad_planes, ns_planes, ns_lead_planes;
+  int32_t apply_planes, grad_planes, ns_planes, ns_one_plane;
   int32_t path;       /* ttt_path */
   /* Step.  Per chunk every matrix i of the state becomes (1 - weight_decay) W_i - lr[i] U_i
    * (U_i the summed gradient, or its Newton-Schulz orthogonalisation), then the optional

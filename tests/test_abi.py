@@ -86,6 +86,13 @@ def test_plane_counts_checked():
     assert _status(c) == 0
 
 
+def test_one_plane_mask_checked():
+    c = _cfg()
+    for mask, code in ((0, 0), (3, 0), (255, 0), (256, 4), (-1, 4)):
+        c.ns_one_plane = mask
+        assert _status(c) == code, mask
+
+
 def test_null_config_and_pointers():
     L = W.lib()
     assert L.ttt_validate_config(None) == 1
@@ -119,7 +126,7 @@ def test_status_strings():
 
 def test_path_selection_checked():
     small = dict(fw="gelu", loss="mse", ns_steps=0, renorm=False, dim=64, hidden=256, chunk=64)
-    one = (1, 1, 1, 1)
+    one = (1, 1, 1, 0)
     # the resident loop serves the small-chunk GELU layer with one bf16 plane
     for kw in [small, dict(small, chunk=1), dict(small, chunk=48), dict(small, loss="dot")]:
         assert _status(W.make_config(None, planes=one, path="resident", **_base(**kw))) == 0, kw
@@ -130,10 +137,10 @@ def test_path_selection_checked():
                dict(small, fw="swiglu")]:
         assert _status(W.make_config(None, planes=one, path="resident", **_base(**kw))) == 5, kw
     # two gradient planes (the bf16 default) keep the staged kernels
-    assert _status(W.make_config(None, planes=(1, 2, 2, 2), path="resident",
+    assert _status(W.make_config(None, planes=(1, 2, 2, 0), path="resident",
                                  **_base(**small))) == 5
     for path in ("auto", "staged"):
-        assert _status(W.make_config(None, planes=(1, 2, 2, 2), path=path,
+        assert _status(W.make_config(None, planes=(1, 2, 2, 0), path=path,
                                      **_base(**small))) == 0
     c = _cfg()
     c.path = 3

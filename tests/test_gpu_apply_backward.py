@@ -69,7 +69,7 @@ def test_apply_backward_parity(act, fw, loss, ns, renorm):
 def test_apply_backward_rejects_resident_states():
     cfg = ti.Config("bwdres", 1, 2, 64, 64, 64, 256, "gelu", "mse", 0, False, "bf16",
                     "apply_then_update", 62)
-    c = W.make_config(cfg, planes=(1, 1, 1, 1), path="resident")
+    c = W.make_config(cfg, planes=(1, 1, 1, 0), path="resident")
     inp = ti.make_inputs(cfg)
     q, k, v, eta, w0 = device_inputs(cfg, inp)
     st = W.ttt_init_state(c, w0)

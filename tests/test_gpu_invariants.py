@@ -145,7 +145,7 @@ def test_chunk_longer_than_one_token_block():
     cfg = ti.Config("long_chunk", 1, 1, 70000, 70000, 16, 32, "swiglu", "dot", 5, True, "bf16",
                     "update_then_apply", 5)
     inp = ti.make_inputs(cfg)
-    O, Ws = _run(cfg, inp, planes=(1, 2, 2, 2))
+    O, Ws = _run(cfg, inp, planes=(1, 2, 2, 0))
     eo, ew = parity(cfg, inp, O, Ws)
     assert eo <= 2e-2 and max(ew) <= 2e-2, (eo, ew)
 

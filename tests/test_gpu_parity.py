@@ -45,7 +45,7 @@ def test_ragged_shapes(act, fw, loss, ns, renorm):
 @pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
 def test_orders(order):
     cfg = ti.Config("ord", 1, 2, 1024, 256, 64, 128, "swiglu", "dot", 5, True, "bf16", order, 7)
-    _check(cfg, planes=(1, 2, 2, 2))
+    _check(cfg, planes=(1, 2, 2, 0))
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
@@ -63,7 +63,7 @@ def test_wide_tiles_ragged_edges():
     # column hold only 16 of 144 rows (and the hidden tiles 32 of 128)
     cfg = ti.Config("wide", 10, 3, 256, 128, 144, 288, "swiglu", "dot", 5, True, "bf16",
                     "apply_then_update", 41)
-    _check(cfg, planes=(1, 2, 2, 2), problems=[(0, 0), (4, 1), (9, 2)])
+    _check(cfg, planes=(1, 2, 2, 0), problems=[(0, 0), (4, 1), (9, 2)])
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
@@ -93,7 +93,26 @@ def test_single_plane_newton_schulz_one_chunk(shape):
         cfg = ti.Config("np1w", 10, 3, 256, 256, 144, 288, "swiglu", "dot", 5, True, "bf16",
                         "apply_then_update", 52)
         problems = [(0, 0), (9, 2)]
-    _check(cfg, planes=(1, 1, 1, 1), problems=problems)
+    _check(cfg, planes=(1, 1, 1, 0), problems=problems)
+
+
+@pytest.mark.parametrize("case", ["narrow_lead2", "narrow_all_one_chunk", "wide_lead2",
+                                  "wide_mixed"])
+def test_one_plane_newton_schulz_iterations(case):
+    # Newton-Schulz iterations named in ns_one_plane multiply one bf16 plane and add the
+    # linear term a X from the iterate's two stored planes; the others keep two planes.
+    # Narrow: 12 matrices of 128 x 256 (64-wide tiles); wide: 90 matrices of 144 x 288
+    # (128-wide tiles with ragged second rows and columns).
+    if case.startswith("narrow"):
+        one_chunk = case == "narrow_all_one_chunk"
+        cfg = ti.Config("onep", 2, 2, 512 if one_chunk else 1024, 512 if one_chunk else 256,
+                        128, 256, "swiglu", "dot", 5, True, "bf16", "apply_then_update", 61)
+        mask, problems = (0b11111 if one_chunk else 0b00011), None
+    else:
+        cfg = ti.Config("onepw", 10, 3, 512, 128, 144, 288, "swiglu", "dot", 5, True, "bf16",
+                        "apply_then_update", 62)
+        mask, problems = (0b00011 if case == "wide_lead2" else 0b01010), [(0, 0), (9, 2)]
+    _check(cfg, planes=(1, 2, 2, mask), problems=problems)
 
 
 def _random_case(i):

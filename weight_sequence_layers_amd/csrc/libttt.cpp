@@ -46,7 +46,8 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 struct Dims {
   int P, nm, d, dh, n;      // problems, matrices, dim, hidden, columns of X orientation
   int rows[3], cols[3], tr[3];
-  int ap, gp, np, nlp, npm, wp, in_q, in_kv;
+  int ap, gp, np, wp, in_q, in_kv;
+  int ns_one;               // bit i: Newton-Schulz iteration i on one bf16 plane
   int64_t sb;               // tokens per gradient / apply block
 };
 
@@ -77,14 +78,17 @@ ttt_status resolve(const ttt_config* c, ttt_config* out) {
     return fail(TTT_E_UNSUPPORTED, "Newton-Schulz needs dim <= hidden (dim %d, hidden %d)",
                 r.dim, r.hidden);
   const bool f32 = r.act == TTT_F32;
-  int* pl[4] = {&r.apply_planes, &r.grad_planes, &r.ns_planes, &r.ns_lead_planes};
-  const int dflt[4] = {f32 ? 3 : 1, f32 ? 3 : 2, f32 ? 3 : 2, f32 ? 3 : 2};
-  const char* nm[4] = {"apply_planes", "grad_planes", "ns_planes", "ns_lead_planes"};
-  for (int i = 0; i < 4; ++i) {
+  int* pl[3] = {&r.apply_planes, &r.grad_planes, &r.ns_planes};
+  const int dflt[3] = {f32 ? 3 : 1, f32 ? 3 : 2, f32 ? 3 : 2};
+  const char* nm[3] = {"apply_planes", "grad_planes", "ns_planes"};
+  for (int i = 0; i < 3; ++i) {
     if (*pl[i] == 0) *pl[i] = dflt[i];
     if (*pl[i] < 1 || *pl[i] > 3)
       return fail(TTT_E_CONFIG, "%s must be 0 (default) or 1..3 (got %d)", nm[i], *pl[i]);
   }
+  if (r.ns_one_plane < 0 || r.ns_one_plane > 255)
+    return fail(TTT_E_CONFIG, "ns_one_plane must be a bit mask in [0, 255] (got %d)",
+                r.ns_one_plane);
   if (r.path < TTT_PATH_AUTO || r.path > TTT_PATH_RESIDENT)
     return fail(TTT_E_CONFIG, "unknown path %d", r.path);
   for (int i = 0; i < 3; ++i) {
@@ -131,8 +135,7 @@ Dims dims_of(const ttt_config& c) {
   D.ap = c.apply_planes;
   D.gp = c.grad_planes;
   D.np = c.ns_planes;
-  D.nlp = c.ns_lead_planes;
-  D.npm = std::max(D.np, D.nlp);
+  D.ns_one = c.ns_planes > 1 ? c.ns_one_plane & ((1 << c.ns_steps) - 1) : 0;
   D.wp = std::max(D.ap, D.gp);
   D.in_q = c.act == TTT_F32 ? D.ap : 1;
   D.in_kv = c.act == TTT_F32 ? D.gp : 1;
@@ -239,9 +242,9 @@ size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
   size_t ogp = ksp > 1 ? C.take<float>(ksp * D.nm * P * d * n) : 0;
   size_t ox[2] = {0, 0}, oa = 0, ob = 0;
   if (c.ns_steps > 0) {
-    for (int i = 0; i < 2; ++i) ox[i] = C.take<u16>(D.npm * D.nm * P * d * n);
-    oa = C.take<u16>(D.npm * D.nm * P * d * d);
-    ob = C.take<u16>(D.npm * D.nm * P * d * d);
+    for (int i = 0; i < 2; ++i) ox[i] = C.take<u16>(D.np * D.nm * P * d * n);
+    oa = C.take<u16>(D.np * D.nm * P * d * d);
+    ob = C.take<u16>(D.np * D.nm * P * d * d);
   }
   size_t oh = C.take<int>(1);
   const size_t on1 = (s->resident || ext_w) ? 0 : C.take<float>(D.sb);
@@ -401,7 +404,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   ca.last = last ? 1 : 0;
   ca.muon = muon;
   const int64_t Z = (int64_t)D.nm * P;
-  if (ca.muon) ca.x = pbuf(s->xpl[0], D.nlp, Z * d * D.n, (int64_t)d * D.n, D.n);
+  if (ca.muon) ca.x = pbuf(s->xpl[0], D.np, Z * d * D.n, (int64_t)d * D.n, D.n);
   ca.part = s->part;
   ca.U = U;
   ca.gpart = s->gpart;
@@ -549,21 +552,23 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
   const int steps = s->cfg.ns_steps;
   const int Z = D.nm * D.P, M = D.d, N = D.n;
   for (int it = 0; it < steps; ++it) {
-    const int pk = it == 0 ? D.nlp : D.np;
-    const int pn = D.np;
+    // products on pk planes; the iterates X keep D.np planes between iterations
+    const int pk = ((D.ns_one >> it) & 1) ? 1 : D.np;
     NsArgs a{};
     a.Z = Z; a.M = M; a.N = N; a.P = D.P;
+    a.pl = pk;
+    a.fold = pk == D.np;   // a I folded into B' where B' holds X's precision
     a.coef_a = 3.4445f; a.coef_b = -4.7750f; a.coef_c = 2.0315f;
     a.part = s->part; a.nparts = s->contract_tiles; a.first = it == 0; a.last = it == steps - 1;
     a.eps = 1e-7f;
-    a.xin = pbuf(s->xpl[it & 1], pk, (int64_t)Z * M * N, (int64_t)M * N, N);
+    a.xin = pbuf(s->xpl[it & 1], D.np, (int64_t)Z * M * N, (int64_t)M * N, N);
     a.aout = pbuf(s->apl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
     STAGED(TTT_STAGE_NS_GRAM, launch_ns_gram(a, st));
     a.ain = a.aout;
     a.aout = pbuf(s->bpl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
     STAGED(TTT_STAGE_NS_POLY, launch_ns_poly(a, st));
     a.ain = a.aout;
-    a.xout = pbuf(s->xpl[(it + 1) & 1], pn, (int64_t)Z * M * N, (int64_t)M * N, N);
+    a.xout = pbuf(s->xpl[(it + 1) & 1], D.np, (int64_t)Z * M * N, (int64_t)M * N, N);
     a.U = s->U;
     a.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
     STAGED(TTT_STAGE_NS_UPDATE, launch_ns_update(a, st));

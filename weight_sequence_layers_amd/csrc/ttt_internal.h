@@ -101,13 +101,17 @@ struct ContractArgs {
 // Newton-Schulz stages on Z = nm*P matrices X [M x N] (M <= N).
 struct NsArgs {
   int Z, M, N, tiles_n, tiles;
+  int pl;             // bf16 planes of every product operand in this iteration
+  int fold;           // B' = a I + b A + c A^2 (else B = b A + c A^2 and the update adds
+                      // a X from all of xin's planes in its epilogue)
   float coef_a, coef_b, coef_c;
   const float* part;  // iteration 0: per-tile sums of squares of the unscaled gradient
   int nparts;
   int first;          // iteration 0 (fold the 1/(|G|_F + eps) scale)
   int last;           // final iteration: write U instead of planes
   float eps;
-  PlaneBuf xin;       // gram, update: X planes [M][N] (iteration 0: planes of G)
+  PlaneBuf xin;       // gram, update: X planes [M][N] (iteration 0: planes of G); the
+                      // products read its first pl planes
   PlaneBuf ain;       // poly: A planes [M][M] ; update: B planes [M][M]
   PlaneBuf aout;      // gram: A planes ; poly: B planes
   PlaneBuf xout;

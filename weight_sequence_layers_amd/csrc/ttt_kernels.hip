@@ -455,7 +455,9 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_gram(NsArgs a) {
 }
 
 // B' = a I + b A + c A A  (A symmetric, so A serves as its own transposed operand); the
-// a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.
+// a I term folds the iteration's a X into the update GEMM: X' = a X + B X = B' X.  Without
+// fold the stage writes B = b A + c A A and the update adds a X itself (a one-plane B' would
+// round a, and with it every row of X', to bf16).
 template <int T, int WGM, int WGN, int PL, int SP, int WGK>
 __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
   // swapped accumulator layout: runs of four columns, read as 16-byte vectors
@@ -496,19 +498,117 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
       float x = 0.f;
       if (R < M && C + e < M && (ti != tj || R <= C + e))
         x = a.coef_b * av[e] + a.coef_c * g.acc[0][i][j][4 * q + e] +
-            (R == C + e ? a.coef_a : 0.f);
+            (a.fold && R == C + e ? a.coef_a : 0.f);
       g.acc[0][i][j][4 * q + e] = x;
     }
   });
   store_sym<G, SP>(g.acc[0], smem, a.aout, zz, m0, n0, M, ti == tj);
 }
 
-// X' = B' X  (iteration 0: X = s G, with the scale s applied in the epilogue).
+// Store the tile v (swapped layout, already scaled) plus ca X as planes of dst, X being
+// the sum of xin's XNP planes at the same place: the fp32 tile goes through LDS in passes
+// of PR rows, and each thread then takes runs of 8 columns of one row, so that X is read,
+// and the planes written, with 16-byte row-contiguous accesses.  Each pass issues its X
+// loads before staging the tile, so their latency overlaps the LDS work.  smem needs
+// PR (TBN + 4) 4 bytes.  Contains barriers: call from every thread.
+template <class G, int PR, int XNP>
+__device__ __forceinline__ void store_planes_lin(const f32x16 (&v)[G::TM][G::TN], char* smem,
+                                                 const PlaneBuf& dst, const PlaneBuf& xin,
+                                                 int z, int row0, int col0, int rlim, int clim,
+                                                 float ca) {
+  static_assert(G::SW, "runs of columns need the swapped layout");
+  constexpr int TBN = G::TBN, LD = TBN + 4, CPR = TBN / 8;
+  constexpr int ITER = (PR * CPR + G::NT - 1) / G::NT;   // row runs per thread and pass
+  float* t = reinterpret_cast<float*>(smem);
+  const int lane = threadIdx.x & 63;
+  const int wm0 = G::wm0(), wn0 = G::wn0();
+  const u16* const xz = xin.base + (int64_t)z * xin.zstride;
+  u16* const dz = dst.base + (int64_t)z * dst.zstride;
+#pragma unroll
+  for (int p0 = 0; p0 < G::TBM; p0 += PR) {
+    uint4 xv[ITER][XNP];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int ch = threadIdx.x + it * G::NT;
+      const int rr = ch / CPR, cc = (ch % CPR) * 8;
+      const bool ok = ch < PR * CPR && p0 + rr < rlim && cc < clim;
+      const int64_t off = (int64_t)(row0 + p0 + rr) * xin.ld + col0 + cc;
+#pragma unroll
+      for (int q = 0; q < XNP; ++q)
+        xv[it][q] = ok ? *reinterpret_cast<const uint4*>(xz + q * xin.plane_stride + off)
+                       : make_uint4(0u, 0u, 0u, 0u);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int tm = 0; tm < G::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < G::TN; ++tn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (!G::owns(tm, tn, g)) continue;
+          const int r = wm0 + tm * 32 + G::elem_row(4 * g, lane) - p0;
+          const int c = wn0 + tn * 32 + G::elem_col(4 * g, lane);
+          if (r >= 0 && r < PR)
+            *reinterpret_cast<f32x4*>(t + r * LD + c) =
+                f32x4{v[tm][tn][4 * g], v[tm][tn][4 * g + 1], v[tm][tn][4 * g + 2],
+                      v[tm][tn][4 * g + 3]};
+        }
+    lds_barrier();
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int ch = threadIdx.x + it * G::NT;
+      const int rr = ch / CPR, cc = (ch % CPR) * 8;
+      const int gr = p0 + rr;
+      if (ch >= PR * CPR || gr >= rlim || cc >= clim) continue;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(t + rr * LD + cc);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(t + rr * LD + cc + 4);
+      const float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      float lin[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < XNP; ++q) {
+        const uint32_t w[4] = {xv[it][q].x, xv[it][q].y, xv[it][q].z, xv[it][q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lin[2 * e] += bf2f((u16)(w[e] & 0xFFFFu));
+          lin[2 * e + 1] += bf2f((u16)(w[e] >> 16));
+        }
+      }
+      u16 hq[8][XNP];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float r = fmaf(ca, lin[e], x[e]);
+#pragma unroll
+        for (int q = 0; q < XNP; ++q) {
+          hq[e][q] = f2bf(r);
+          r -= bf2f(hq[e][q]);
+        }
+      }
+      const int64_t off = (int64_t)(row0 + gr) * dst.ld + col0 + cc;
+#pragma unroll
+      for (int q = 0; q < XNP; ++q) {
+        uint4 o;
+        o.x = hq[0][q] | ((uint32_t)hq[1][q] << 16);
+        o.y = hq[2][q] | ((uint32_t)hq[3][q] << 16);
+        o.z = hq[4][q] | ((uint32_t)hq[5][q] << 16);
+        o.w = hq[6][q] | ((uint32_t)hq[7][q] << 16);
+        *reinterpret_cast<uint4*>(dz + q * dst.plane_stride + off) = o;
+      }
+    }
+  }
+  lds_barrier();
+}
+
+// X' = B' X, or X' = B X + a X without fold, a X taken from all of xin's planes
+// (iteration 0: X = s G, with the scale s applied in the epilogue).
 template <int BM, int BN, int WGM, int WGN, int PL, int BK, int SP, int WGK>
 __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
   // X [M][N] read column-wise; swapped accumulator layout for packed plane stores
   using G = Gemm<BM, BN, WGM, WGN, PL, PL, 0, (1 << PL) - 1, PL, BK, true, WGK>;
-  GEMM_LDS_EPI(G, (store_lds_bytes<G, TILE_NORMAL, SP>()));
+  constexpr int LIN_ROWS = BM / 2;   // rows per LDS pass of the a X epilogue
+  constexpr int EPI = store_lds_bytes<G, TILE_NORMAL, SP>() > LIN_ROWS * (BN + 4) * 4
+                          ? store_lds_bytes<G, TILE_NORMAL, SP>()
+                          : LIN_ROWS * (BN + 4) * 4;
+  GEMM_LDS_EPI(G, EPI);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int M = a.M, N = a.N;
@@ -531,13 +631,25 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
   // runs of four columns (N is a multiple of 16, so a run lies wholly inside or outside):
   // U in the weight orientation is written as one 16-byte store per run, or transposed as
   // four 4-byte stores that consecutive lanes (consecutive rows) make contiguous
+  const u16* const xp = a.xin.base + (int64_t)zz * a.xin.zstride;
   g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
     const bool in = R < M && C < N;
+    float lin[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!a.fold && a.last && in) {   // (otherwise a X is added by store_planes_lin)
+      for (int pq = 0; pq < a.xin.np; ++pq) {
+        const uint2 h = *reinterpret_cast<const uint2*>(xp + pq * a.xin.plane_stride +
+                                                        (int64_t)R * a.xin.ld + C);
+        lin[0] += bf2f((u16)(h.x & 0xFFFFu));
+        lin[1] += bf2f((u16)(h.x >> 16));
+        lin[2] += bf2f((u16)(h.y & 0xFFFFu));
+        lin[3] += bf2f((u16)(h.y >> 16));
+      }
+    }
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = in ? sc * g.acc[0][i][j][4 * q + e] : 0.f;
+      x[e] = in ? sc * fmaf(a.coef_a, lin[e], g.acc[0][i][j][4 * q + e]) : 0.f;
       g.acc[0][i][j][4 * q + e] = x[e];
     }
     if (a.last && in) {
@@ -552,7 +664,14 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_update(NsArgs a) {
   });
   if (!a.last) {
     const int rl = min(BM, M - m0), cl = min(BN, N - n0);
-    store_planes<G, TILE_NORMAL, SP>(g.acc[0], smem, a.xout, zz, m0, n0, rl, cl);
+    if (a.fold)
+      store_planes<G, TILE_NORMAL, SP>(g.acc[0], smem, a.xout, zz, m0, n0, rl, cl);
+    else if (a.xin.np == 2)   // (one-plane iterates are always folded)
+      store_planes_lin<G, LIN_ROWS, 2>(g.acc[0], smem, a.xout, a.xin, zz, m0, n0, rl, cl,
+                                       a.coef_a * sc);
+    else
+      store_planes_lin<G, LIN_ROWS, 3>(g.acc[0], smem, a.xout, a.xin, zz, m0, n0, rl, cl,
+                                       a.coef_a * sc);
   }
 }
 
@@ -807,8 +926,14 @@ static hipError_t ns_sym(const NsArgs& a, int np, hipStream_t s) {
   if (np == 3) return ns_t<64, STAGE, 3, 2, 2, 64, 3, 2>(a, s);
   return hipErrorInvalidValue;
 }
-hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) { return ns_sym<0>(a, a.xin.np, s); }
-hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_sym<1>(a, a.ain.np, s); }
+hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s) {
+  if (a.pl > a.xin.np || a.aout.np != a.pl) return hipErrorInvalidValue;
+  return ns_sym<0>(a, a.pl, s);
+}
+hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) {
+  if (a.ain.np != a.pl || a.aout.np != a.pl) return hipErrorInvalidValue;
+  return ns_sym<1>(a, a.pl, s);
+}
 // The update takes 128x128 tiles when they give at least two workgroups per CU (256 CUs)
 // and the operands have at most two planes (three would not fit LDS); else 64x64 tiles.
 // With two planes the 128x128 kernel steps K by 32 and stores one plane per pass, which
@@ -816,11 +941,12 @@ hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s) { return ns_sym<1>(a, 
 // other's main loop.
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s) {
   const int64_t big = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.Z;
-  if (a.ain.np != a.xin.np) return hipErrorInvalidValue;
+  if (a.ain.np != a.pl || a.pl > a.xin.np || (!a.last && a.xout.np != a.xin.np))
+    return hipErrorInvalidValue;
   // three planes: 64x64 tiles stepping K by 32 (52 KB of LDS, three workgroups per CU)
-  if (a.xin.np == 3) return ns_t<64, 2, 3, 2, 2, 32, 3>(a, s);
-  if (big < 512) return ns_planes<64, 2>(a, a.xin.np, s);
-  return a.xin.np == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2, 2, 4, 32, 1>(a, s);
+  if (a.pl == 3) return ns_t<64, 2, 3, 2, 2, 32, 3>(a, s);
+  if (big < 512) return ns_planes<64, 2>(a, a.pl, s);
+  return a.pl == 1 ? ns_t<128, 2, 1>(a, s) : ns_t<128, 2, 2, 2, 4, 32, 1>(a, s);
 }
 
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s) {
