@@ -161,6 +161,24 @@ ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, cons
                                 const float* eta, void* out, int64_t seq_len, void* stream);
 
 /*
+ * ttt_sequence_forward in which only chosen chunks update the fast weights.  update: HOST
+ * array of seq_len/chunk bytes, read before the call returns; chunk c updates when
+ * update[c] != 0 (NULL: every chunk updates, the same as ttt_sequence_forward).  A chunk
+ * whose flag is 0 answers its queries with the state as it stands and leaves the state
+ * unchanged: no gradient, no Newton-Schulz, no decay, no renorm.  The LaCT page (§3.3)
+ * adapts a video diffusion model so that the fast weights are updated on the clean-frame
+ * chunks only, every chunk still being answered; a flag per chunk states that.  Together
+ * with either order it also expresses updates on every s-th chunk only, each chunk's
+ * queries seeing the updates up to their own chunk (UPDATE_THEN_APPLY) or before it.
+ * With no weight decay, a chunk without update gives the same result, bit for bit, as the
+ * same chunk with every eta set to 0.  Other arguments and errors as for
+ * ttt_sequence_forward.
+ */
+ttt_status ttt_sequence_forward_masked(ttt_state* s, const void* q, const void* k,
+                                       const void* v, const float* eta, void* out,
+                                       int64_t seq_len, const uint8_t* update, void* stream);
+
+/*
  * Backward of one chunk's apply step (the LaCT explainer page, §2.1, eq. 2; the query-view
  * rule of the train-view forward / backward / query-view split the Modular TTT abstract
  * describes).  With the state as it stands -- the state that chunk's queries were answered

@@ -243,7 +243,8 @@ def update_state(Ws, grads, ns_steps: int, renorm: bool, lr: Optional[Sequence[f
 
 # ------------------------------------------------------------------------- the layer loop
 def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
-                     apply_rows: Optional[np.ndarray] = None, n_chunks: Optional[int] = None):
+                     apply_rows: Optional[np.ndarray] = None, n_chunks: Optional[int] = None,
+                     update_chunks: Optional[Sequence[bool]] = None):
     """One (batch, head) problem: the chunk loop of the TTT layer.
 
     W0s: the problem's initial matrices; Q, K, V: [T, d]; eta: [T].
@@ -252,6 +253,10 @@ def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
     0..c-1 and its own update follows; the image-set order ([LaCT] §3.1) updates
     first and then applies. The state after the last chunk is returned.
 
+    update_chunks: optional flag per chunk; a chunk whose flag is false answers its
+    queries with the state as it stands and leaves the state unchanged (no gradient, no
+    decay, no renorm): the fast weights are updated on chosen chunks only, as [LaCT] §3.3
+    does for the clean-frame chunks of an autoregressive video sequence.
     apply_rows: optional sorted token indices; only those rows of O are computed
     (the others stay 0). n_chunks: stop after that many chunks.
     Returns (O [T, d] fp64, list of final fp64 matrices)."""
@@ -274,6 +279,9 @@ def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
 
     for c in range(nc):
         lo, hi = c * b, (c + 1) * b
+        if update_chunks is not None and not update_chunks[c]:
+            apply(lo, hi)
+            continue
         if cfg.order == APPLY_THEN_UPDATE:
             apply(lo, hi)
         g = chunk_gradient(cfg.fw, cfg.loss, Ws, K[lo:hi], V[lo:hi], eta[lo:hi], block_rows)
@@ -283,7 +291,7 @@ def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
     return O, Ws
 
 
-def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta):
+def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta, update_chunks=None):
     """Per-token version for tiny inputs: every output row and every token's gradient
     is formed with explicit vector operations in Python loops, and the chunk gradient
     is the running sum of per-token outer products. Checks the matrix form above."""
@@ -304,9 +312,12 @@ def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta):
         return W @ x
 
     for c in range(T // b):
-        if cfg.order == APPLY_THEN_UPDATE:
+        updates = update_chunks is None or bool(update_chunks[c])
+        if cfg.order == APPLY_THEN_UPDATE or not updates:
             for t in range(c * b, (c + 1) * b):
                 O[t] = f(np.asarray(Q[t], np.float64))
+        if not updates:
+            continue
         grads = [np.zeros_like(w) for w in Ws]
         for t in range(c * b, (c + 1) * b):
             k = np.asarray(K[t], np.float64)
@@ -337,7 +348,7 @@ def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta):
 
 
 def forward_all(cfg, inputs, problems: Optional[Sequence[Tuple[int, int]]] = None,
-                block_rows: Optional[int] = 8192):
+                block_rows: Optional[int] = 8192, update_chunks=None):
     """Run every (batch, head) problem (or the listed ones) of an input set made by
     ``ttt_inputs.make_inputs``. Returns {(b, h): (O, [W...])}."""
     out = {}
@@ -346,5 +357,6 @@ def forward_all(cfg, inputs, problems: Optional[Sequence[Tuple[int, int]]] = Non
     for (b, h) in probs:
         W0s = [w[h] for w in inputs["w0"]]
         out[(b, h)] = sequence_forward(cfg, W0s, inputs["q"][b, h], inputs["k"][b, h],
-                                       inputs["v"][b, h], inputs["eta"][b, h], block_rows)
+                                       inputs["v"][b, h], inputs["eta"][b, h], block_rows,
+                                       update_chunks=update_chunks)
     return out

@@ -103,6 +103,7 @@ def test_null_config_and_pointers():
     assert L.ttt_init_state(ctypes.byref(_cfg()), 0x1000, None, None) == 1
     assert L.ttt_chunk_forward(None, 16, 16, 16, 16, 16, None) == 1
     assert L.ttt_sequence_forward(None, 16, 16, 16, 16, 16, 64, None) == 1
+    assert L.ttt_sequence_forward_masked(None, 16, 16, 16, 16, 16, 64, None, None) == 1
     assert L.ttt_get_state(None, 16, None) == 1
     assert L.ttt_set_state(None, 16, None) == 1
     assert L.ttt_state_health(None) == 1

@@ -502,6 +502,75 @@ def test_forward_all_runs_each_problem_on_its_own_inputs():
     assert forward_all_error() <= 1e-12
 
 
+# ------------------------------------------------------------------ chunks that do not update
+MASKS = [(0, 1, 0, 1), (1, 0, 0, 1), (0, 0, 0, 0), (1, 1, 1, 1), (1, 0, 1, 0)]
+
+
+def masked_linear_closed_form_error(order, mask, chunk=3, T=12, d=4, seed=13, lr=0.6, wd=0.1):
+    """Linear fast weight, inner-product loss, no Muon, no norm: only the chunks whose flag
+    is set move the state, each to (1 - wd) W + lr sum_t eta_t v_t k_t^T over its own
+    tokens (summed token by token here); a chunk without the flag is answered by the state
+    as it stands and neither steps nor decays it."""
+    cfg = _cfg("linear", "dot", 0, False, order, chunk=chunk, d=d, T=T, lr=(lr,), wd=wd)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(seed))
+    O, Wf = orc.sequence_forward(cfg, Ws, Q, K, V, eta, update_chunks=mask)
+    W = Ws[0].copy()
+    err = 0.0
+    for c in range(T // chunk):
+        S = slice(c * chunk, (c + 1) * chunk)
+        Wn = W
+        if mask[c]:
+            step = np.zeros_like(W)
+            for t in range(c * chunk, (c + 1) * chunk):
+                step += eta[t] * np.outer(V[t], K[t])
+            Wn = (1.0 - wd) * W + lr * step
+        ref = Q[S] @ (W if order == "apply_then_update" else Wn).T
+        err = max(err, np.abs(O[S] - ref).max())
+        W = Wn
+    return max(err, np.abs(Wf[0] - W).max())
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+@pytest.mark.parametrize("mask", MASKS)
+def test_update_flags_linear_closed_form(order, mask):
+    assert masked_linear_closed_form_error(order, mask) <= 1e-12
+
+
+@pytest.mark.parametrize("fw,loss", [("swiglu", "dot"), ("gelu", "mse"), ("linear", "mse")])
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+def test_update_flags_match_the_bruteforce(fw, loss, order):
+    cfg = _cfg(fw, loss, 5 if fw != "linear" else 0, True, order, chunk=3, d=4, dh=6, T=12)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(14))
+    for mask in MASKS:
+        O1, W1 = orc.sequence_forward(cfg, Ws, Q, K, V, eta, update_chunks=mask)
+        O2, W2 = orc.sequence_forward_bruteforce(cfg, Ws, Q, K, V, eta, update_chunks=mask)
+        assert np.abs(O1 - O2).max() <= 1e-12 * max(1, np.abs(O2).max())
+        for a, b in zip(W1, W2):
+            assert np.abs(a - b).max() <= 1e-12 * max(1, np.abs(b).max())
+
+
+@pytest.mark.parametrize("ns,renorm", [(0, False), (5, True)])
+def test_a_chunk_without_update_equals_eta_zero(ns, renorm):
+    """With no weight decay, a chunk that does not update is the same run as that chunk's
+    eta set to zero (a zero gradient, and NS5(0) = 0, leave the state bitwise), and all
+    flags set is the run with no flags."""
+    cfg = _cfg("swiglu", "dot", ns, renorm, chunk=3, T=12, d=4, dh=6)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(15))
+    mask = (1, 0, 1, 0)
+    O1, W1 = orc.sequence_forward(cfg, Ws, Q, K, V, eta, update_chunks=mask)
+    e0 = eta.copy()
+    for c, m in enumerate(mask):
+        if not m:
+            e0[c * 3:(c + 1) * 3] = 0.0
+    O2, W2 = orc.sequence_forward(cfg, Ws, Q, K, V, e0)
+    assert np.array_equal(O1, O2)
+    for a, b in zip(W1, W2):
+        assert np.array_equal(a, b)
+    O3, W3 = orc.sequence_forward(cfg, Ws, Q, K, V, eta, update_chunks=(1, 1, 1, 1))
+    O4, W4 = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    assert np.array_equal(O3, O4) and all(np.array_equal(a, b) for a, b in zip(W3, W4))
+
+
 # ------------------------------------------------------------------ mutation tests
 def _all_pins_pass():
     try:
@@ -530,6 +599,9 @@ def _all_pins_pass_inner():
     checks.append(apply_rows_error("apply_then_update") <= 1e-12)
     checks.append(apply_rows_error("update_then_apply") <= 1e-12)
     checks.append(forward_all_error() <= 1e-12)
+    for order in ("apply_then_update", "update_then_apply"):
+        checks.append(masked_linear_closed_form_error(order, (0, 1, 0, 1)) <= 1e-12)
+        checks.append(masked_linear_closed_form_error(order, (1, 0, 0, 1)) <= 1e-12)
     return all(checks)
 
 
@@ -606,13 +678,28 @@ def _mut_step_before_ns(Ws, grads, ns_steps, renorm, lr=None, weight_decay=0.0):
 _ORIG_SEQ = orc.sequence_forward
 
 
-def _mut_rows_offset(cfg, W0s, Q, K, V, eta, block_rows=8192, apply_rows=None, n_chunks=None):
+def _mut_rows_offset(cfg, W0s, Q, K, V, eta, block_rows=8192, apply_rows=None, n_chunks=None,
+                     update_chunks=None):
     # the sampled rows of chunk c answered with the queries at (row - chunk start)
     if apply_rows is not None:
         Q = np.array(Q, np.float64)
         rows = np.asarray(apply_rows)
         Q[rows] = Q[rows - (rows // cfg.chunk) * cfg.chunk]
-    return _ORIG_SEQ(cfg, W0s, Q, K, V, eta, block_rows, apply_rows, n_chunks)
+    return _ORIG_SEQ(cfg, W0s, Q, K, V, eta, block_rows, apply_rows, n_chunks, update_chunks)
+
+
+def _mut_mask_ignored(cfg, W0s, Q, K, V, eta, block_rows=8192, apply_rows=None, n_chunks=None,
+                      update_chunks=None):
+    # every chunk updates whatever its flag says
+    return _ORIG_SEQ(cfg, W0s, Q, K, V, eta, block_rows, apply_rows, n_chunks, None)
+
+
+def _mut_mask_shifted(cfg, W0s, Q, K, V, eta, block_rows=8192, apply_rows=None, n_chunks=None,
+                      update_chunks=None):
+    # chunk c takes chunk c-1's flag
+    if update_chunks is not None:
+        update_chunks = [True] + list(update_chunks)[:-1]
+    return _ORIG_SEQ(cfg, W0s, Q, K, V, eta, block_rows, apply_rows, n_chunks, update_chunks)
 
 
 def _mut_forward_all_head(cfg, inputs, problems=None, block_rows=8192):
@@ -649,6 +736,8 @@ def _mut_forward_all_qk(cfg, inputs, problems=None, block_rows=8192):
     ("sampled rows offset", "sequence_forward", _mut_rows_offset),
     ("forward_all head index", "forward_all", _mut_forward_all_head),
     ("forward_all keys as queries", "forward_all", _mut_forward_all_qk),
+    ("update flags ignored", "sequence_forward", _mut_mask_ignored),
+    ("update flags shifted", "sequence_forward", _mut_mask_shifted),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, target, mut):
     monkeypatch.setattr(orc, target, mut)

@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "ttt_init_state": [cfgp, vp, vp, ctypes.POINTER(vp)],
             "ttt_chunk_forward": [vp, vp, vp, vp, vp, vp, vp],
             "ttt_sequence_forward": [vp, vp, vp, vp, vp, vp, i64, vp],
+            "ttt_sequence_forward_masked": [vp, vp, vp, vp, vp, vp, i64, vp, vp],
             "ttt_apply_backward": [vp, vp, vp, vp, vp, vp],
             "ttt_get_state": [vp, vp, vp],
             "ttt_set_state": [vp, vp, vp],
@@ -212,6 +213,23 @@ def ttt_sequence_forward_noalloc(cfg: ttt_config, state, q, k, v, eta, out, seq_
     _check(lib().ttt_sequence_forward_noalloc(ctypes.byref(cfg), _ptr(state), _ptr(q), _ptr(k),
                                               _ptr(v), _ptr(eta), _ptr(out), int(seq_len),
                                               _stream(stream)))
+
+
+def ttt_sequence_forward_masked(st: State, q, k, v, eta, out, seq_len: int, update,
+                                stream=None) -> None:
+    """ttt_sequence_forward in which chunk c updates the state only if update[c] is true
+    (a sequence of seq_len/chunk flags, or None for all; see include/libttt.h)."""
+    n = int(seq_len) // st.cfg.chunk
+    arr = None
+    if update is not None:
+        flags = [1 if u else 0 for u in update]
+        if len(flags) != n:
+            raise ValueError(f"{len(flags)} update flags for {n} chunks")
+        arr = (ctypes.c_uint8 * max(n, 1))(*flags)
+    _check(lib().ttt_sequence_forward_masked(st.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                             _ptr(out), int(seq_len),
+                                             ctypes.cast(arr, ctypes.c_void_p) if arr else None,
+                                             _stream(stream)))
 
 
 def ttt_get_state(st: State, dst, stream=None) -> None:

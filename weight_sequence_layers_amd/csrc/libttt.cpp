@@ -660,7 +660,9 @@ ttt_status apply_bwd_rows(ttt_state* s, const Rows& R, bool first, bool last, fl
   return TTT_OK;
 }
 
-ttt_status run_chunk(ttt_state* s, const Rows& R0, hipStream_t st) {
+// One chunk: apply and update in the configured order, or (update == false) apply only
+// with the state as it stands.
+ttt_status run_chunk(ttt_state* s, const Rows& R0, hipStream_t st, bool update = true) {
   const ttt_config& c = s->cfg;
   const Dims& D = s->D;
   const int64_t b = c.chunk;
@@ -675,6 +677,7 @@ ttt_status run_chunk(ttt_state* s, const Rows& R0, hipStream_t st) {
     }
     return TTT_OK;
   };
+  if (!update) return apply_all();
   if (c.order == TTT_APPLY_THEN_UPDATE && (r = apply_all()) != TTT_OK) return r;
   for (int64_t o = 0; o < b; o += D.sb) {
     Rows R = R0;
@@ -695,8 +698,36 @@ ttt_status check_ptr(const void* p, const char* name) {
   return TTT_OK;
 }
 
+// Chunks [c0, c1) on the resident path (one launch; every chunk updates).
+ttt_status resident_run(ttt_state* s, const void* q, const void* k, const void* v,
+                        const float* eta, void* out, int64_t T, int64_t c0, int64_t c1,
+                        hipStream_t st) {
+  const Dims& D = s->D;
+  const int64_t t0 = c0 * s->cfg.chunk;
+  SmallArgs a{};
+  a.q = static_cast<const u16*>(q) + t0 * D.d;
+  a.k = static_cast<const u16*>(k) + t0 * D.d;
+  a.v = static_cast<const u16*>(v) + t0 * D.d;
+  a.eta = eta + t0;
+  a.out = static_cast<u16*>(out) + t0 * D.d;
+  a.W1 = s->Wm[0];
+  a.W2 = s->Wm[1];
+  a.health = s->health;
+  a.T = T;
+  a.chunk = s->cfg.chunk;
+  a.nchunks = (int)(c1 - c0);
+  a.P = D.P;
+  a.e_scale = s->cfg.lr[1];
+  a.dz_scale = s->cfg.lr[0] / s->cfg.lr[1];
+  a.keep = 1.f - s->cfg.weight_decay;
+  STAGED(TTT_STAGE_RESIDENT, launch_small(a, s->cfg.loss == TTT_LOSS_MSE, st));
+  return TTT_OK;
+}
+
+// update: NULL (every chunk updates) or one flag per chunk of the call (host memory).
 ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, const float* eta,
-                   void* out, int64_t T, int64_t nchunks, void* stream) {
+                   void* out, int64_t T, int64_t nchunks, void* stream,
+                   const uint8_t* update = nullptr) {
   if (!s) return fail(TTT_E_NULL, "state is NULL");
   if (T == 0) return TTT_OK;
   ttt_status r;
@@ -705,28 +736,6 @@ ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, co
     return r;
   hipStream_t st = static_cast<hipStream_t>(stream);
   s->last = st;
-  if (s->resident) {
-    // every chunk of the call in one launch; W is updated in place
-    const Dims& D = s->D;
-    SmallArgs a{};
-    a.q = static_cast<const u16*>(q);
-    a.k = static_cast<const u16*>(k);
-    a.v = static_cast<const u16*>(v);
-    a.eta = eta;
-    a.out = static_cast<u16*>(out);
-    a.W1 = s->Wm[0];
-    a.W2 = s->Wm[1];
-    a.health = s->health;
-    a.T = T;
-    a.chunk = s->cfg.chunk;
-    a.nchunks = (int)nchunks;
-    a.P = D.P;
-    a.e_scale = s->cfg.lr[1];
-    a.dz_scale = s->cfg.lr[0] / s->cfg.lr[1];
-    a.keep = 1.f - s->cfg.weight_decay;
-    STAGED(TTT_STAGE_RESIDENT, launch_small(a, s->cfg.loss == TTT_LOSS_MSE, st));
-    return TTT_OK;
-  }
   Rows R{};
   R.q = static_cast<const char*>(q);
   R.k = static_cast<const char*>(k);
@@ -734,9 +743,29 @@ ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, co
   R.eta = eta;
   R.out = static_cast<char*>(out);
   R.T = T;
+  if (s->resident) {
+    // every run of updating chunks in one launch (W updated in place, on chip); a chunk
+    // that does not update is answered by the staged apply kernels from planes of W
+    for (int64_t c0 = 0; c0 < nchunks;) {
+      const bool up = !update || update[c0];
+      int64_t c1 = c0 + 1;
+      while (c1 < nchunks && (!update || update[c1]) == up) ++c1;
+      if (up) {
+        if ((r = resident_run(s, q, k, v, eta, out, T, c0, c1, st)) != TTT_OK) return r;
+      } else {
+        if ((r = refresh_planes(s, false, st)) != TTT_OK) return r;
+        for (int64_t ci = c0; ci < c1; ++ci) {
+          R.t0 = ci * s->cfg.chunk;
+          if ((r = run_chunk(s, R, st, false)) != TTT_OK) return r;
+        }
+      }
+      c0 = c1;
+    }
+    return TTT_OK;
+  }
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     R.t0 = ci * s->cfg.chunk;
-    if ((r = run_chunk(s, R, st)) != TTT_OK) return r;
+    if ((r = run_chunk(s, R, st, !update || update[ci])) != TTT_OK) return r;
   }
   return TTT_OK;
 }
@@ -899,6 +928,17 @@ ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, cons
     return fail(TTT_E_SHAPE, "seq_len %lld is not a multiple of the chunk %d",
                 (long long)seq_len, s->cfg.chunk);
   return forward(s, q, k, v, eta, out, seq_len, seq_len / s->cfg.chunk, stream);
+}
+
+ttt_status ttt_sequence_forward_masked(ttt_state* s, const void* q, const void* k,
+                                       const void* v, const float* eta, void* out,
+                                       int64_t seq_len, const uint8_t* update, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  if (seq_len < 0) return fail(TTT_E_SHAPE, "seq_len is negative");
+  if (seq_len % s->cfg.chunk)
+    return fail(TTT_E_SHAPE, "seq_len %lld is not a multiple of the chunk %d",
+                (long long)seq_len, s->cfg.chunk);
+  return forward(s, q, k, v, eta, out, seq_len, seq_len / s->cfg.chunk, stream, update);
 }
 
 ttt_status ttt_get_state(const ttt_state* s, float* dst, void* stream) {
