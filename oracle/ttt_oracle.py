@@ -360,3 +360,233 @@ def forward_all(cfg, inputs, problems: Optional[Sequence[Tuple[int, int]]] = Non
                                        inputs["v"][b, h], inputs["eta"][b, h], block_rows,
                                        update_chunks=update_chunks)
     return out
+
+
+# ---------------------------------------------------------- backward through one chunk's update
+# The outer loop of [E2E-2] §2.2 trains through the inner updates: the gradient of an outer
+# loss reaches the inputs and the initial fast weights through every chunk's apply and update
+# (the second-order gradients [E2E-2] §5.1 names as the cost of meta-learning); [Modular TTT]
+# composes the layer's backward from the train view's forward and backward. These functions
+# take one chunk's step backward with the chain rule, step by step in the forward's order.
+
+def silu_second(z):
+    # d/dz [s (1 + z (1 - s))] = s (1 - s) (2 + z (1 - 2 s))
+    s = sigmoid(z)
+    return s * (1.0 - s) * (2.0 + z * (1.0 - 2.0 * s))
+
+
+def gelu_second(z):
+    # d/dz [Phi(z) + z phi(z)] = phi(z) (2 - z^2)
+    return np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi) * (2.0 - z * z)
+
+
+def gradient_vjp(fw: str, loss: str, Ws, K, V, eta, dG):
+    """Backward of the chunk gradient g(W, K, V, eta) = grad_W L (the update phase of [LaCT]
+    §2.1) for a cotangent dG (one array per matrix, shaped like W): the gradients of
+    phi = sum_m <dG_m, g_m> with respect to W, K, V and eta. phi is the derivative of L
+    along the weight direction dG, so with J_t the forward-mode tangent of f_W(k_t) along dG
+    and e_t = dL/df(k_t) the per-token output error, phi = sum_t <e_t, J_t>; its gradients
+    follow by the chain rule through J_t (second derivatives of the activation) and, for the
+    MSE loss, through e_t. Returns ([dW per matrix], dK, dV, deta)."""
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    eta = np.asarray(eta, np.float64)
+    dG = [np.asarray(x, np.float64) for x in dG]
+    if fw == "swiglu":
+        W1, W3, W2 = Ws
+        D1, D3, D2 = dG
+        Z1, Z3 = K @ W1.T, K @ W3.T
+        S, S1, S2 = silu(Z1), silu_prime(Z1), silu_second(Z1)
+        H = S * Z3
+        F = H @ W2.T
+        E = _output_error(loss, F, V, eta)
+        Dl = E @ W2                                  # hidden error, per token W2^T e_t
+        Zd1, Zd3 = K @ D1.T, K @ D3.T                # tangents of Z1, Z3 along dG
+        Hd = S1 * Zd1 * Z3 + S * Zd3                 # tangent of H
+        J = H @ D2.T + Hd @ W2.T                     # tangent of f(k_t)
+        G2 = E @ D2                                  # per token D2^T e_t
+        dZ1, dZ3 = Dl * S1 * Z3, Dl * S              # the forward's back-propagated errors
+        A1 = G2 * S1 * Z3 + Dl * (S2 * Zd1 * Z3 + S1 * Zd3)   # d phi / d Z1
+        A3 = G2 * S + Dl * S1 * Zd1                           # d phi / d Z3
+        dW = [A1.T @ K, A3.T @ K, E.T @ Hd]
+        dK = A1 @ W1 + A3 @ W3 + dZ1 @ D1 + dZ3 @ D3
+    elif fw == "gelu":
+        W1, W2 = Ws
+        D1, D2 = dG
+        Z = K @ W1.T
+        H, G1, Gs = gelu(Z), gelu_prime(Z), gelu_second(Z)
+        F = H @ W2.T
+        E = _output_error(loss, F, V, eta)
+        Dl = E @ W2
+        Zd = K @ D1.T
+        Hd = G1 * Zd
+        J = H @ D2.T + Hd @ W2.T
+        G2 = E @ D2
+        A1 = G2 * G1 + Dl * Gs * Zd
+        dW = [A1.T @ K, E.T @ Hd]
+        dK = A1 @ W1 + (Dl * G1) @ D1
+    elif fw == "linear":
+        (W,) = Ws
+        (D,) = dG
+        F = K @ W.T
+        E = _output_error(loss, F, V, eta)
+        J = K @ D.T
+        dW = [np.zeros_like(W)]
+        dK = E @ D
+    else:
+        raise ValueError(fw)
+    if loss == "dot":                                # e_t = -eta_t v_t
+        dV = -eta[:, None] * J
+        deta = -np.sum(V * J, axis=1)
+    elif loss == "mse":                              # e_t = 2 eta_t (f(k_t) - v_t)
+        C = 2.0 * eta[:, None] * J                   # cotangent reaching f(k_t) through e_t
+        dKf, dWf = apply_vjp(fw, Ws, K, C)
+        dK = dK + dKf
+        dW = [a + b for a, b in zip(dW, dWf)]
+        dV = -C
+        deta = 2.0 * np.sum((F - V) * J, axis=1)
+    else:
+        raise ValueError(loss)
+    return dW, dK, dV, deta
+
+
+def newton_schulz5_vjp(G: np.ndarray, dU: np.ndarray, steps: int = 5, coeffs=MUON_COEFFS,
+                       eps: float = NS_EPS) -> np.ndarray:
+    """Backward of newton_schulz5 ([LaCT] §2.2.1, eqs. 9-10) for a cotangent dU on its
+    output: the iterates are recomputed, then each step X' = a X + (b A + c A A) X with
+    A = X X^T is taken back (B symmetric), and finally the Frobenius scaling and the
+    transposition to the wide orientation."""
+    a, b, c = coeffs
+    G = np.asarray(G, np.float64)
+    nrm = np.linalg.norm(G)
+    X = G / (nrm + eps)
+    dX = np.asarray(dU, np.float64)
+    wide = X.shape[0] <= X.shape[1]
+    if not wide:
+        X, dX = X.T, dX.T
+    iterates = []
+    for _ in range(steps):
+        iterates.append(X)
+        A = X @ X.T
+        X = a * X + (b * A + c * (A @ A)) @ X
+    for X in reversed(iterates):
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        dB = dX @ X.T                               # X' = a X + B X
+        dA = b * dB + c * (dB @ A + A @ dB)         # B = b A + c A A
+        dX = a * dX + B.T @ dX + (dA + dA.T) @ X    # A = X X^T
+    if not wide:
+        dX = dX.T
+    # X0 = G / (|G|_F + eps)
+    if nrm == 0.0:
+        return dX / eps
+    return dX / (nrm + eps) - G * (np.sum(G * dX) / (nrm * (nrm + eps) ** 2))
+
+
+def renorm_rows_vjp(W_prev: np.ndarray, W_new: np.ndarray, dOut: np.ndarray):
+    """Backward of renorm_rows ([LaCT] §2.2.1, eq. 8): out_r = y_r |w_r| / |y_r| with
+    y = W_new, w = W_prev (rows of zero new norm passed through). Returns (dW_prev, dW_new):
+    the cotangent of y loses its component along y and is scaled by |w_r| / |y_r|; the
+    reference norm |w_r| sends <y_r / |y_r|, dout_r> w_r / |w_r| to w_r."""
+    W_prev = np.asarray(W_prev, np.float64)
+    Y = np.asarray(W_new, np.float64)
+    dOut = np.asarray(dOut, np.float64)
+    n_prev = np.linalg.norm(W_prev, axis=1)
+    n_new = np.linalg.norm(Y, axis=1)
+    ok = n_new > 0
+    yh = Y / np.where(ok, n_new, 1.0)[:, None]
+    proj = np.sum(yh * dOut, axis=1)
+    dY = np.where(ok[:, None], (n_prev / np.where(ok, n_new, 1.0))[:, None]
+                  * (dOut - yh * proj[:, None]), dOut)
+    scale_w = np.where(ok & (n_prev > 0), proj / np.where(n_prev > 0, n_prev, 1.0), 0.0)
+    dW_prev = W_prev * scale_w[:, None]
+    return dW_prev, dY
+
+
+def update_state_vjp(Ws, grads, dWs_new, ns_steps: int, renorm: bool,
+                     lr: Optional[Sequence[float]] = None, weight_decay: float = 0.0):
+    """Backward of update_state for cotangents on the new matrices: returns (dW on the
+    matrices before the update, dG on the chunk gradients)."""
+    steps = [1.0] * len(Ws) if lr is None else list(lr)
+    dW_out, dG_out = [], []
+    for W, g, dWn, step in zip(Ws, grads, dWs_new, steps):
+        W = np.asarray(W, np.float64)
+        U = newton_schulz5(g, ns_steps) if ns_steps > 0 else np.asarray(g, np.float64)
+        Y = (1.0 - weight_decay) * W - step * U
+        if renorm:
+            dW, dY = renorm_rows_vjp(W, Y, dWn)
+        else:
+            dW, dY = np.zeros_like(W), np.asarray(dWn, np.float64)
+        dW = dW + (1.0 - weight_decay) * dY
+        dU = -step * dY
+        dG_out.append(newton_schulz5_vjp(g, dU, ns_steps) if ns_steps > 0 else dU)
+        dW_out.append(dW)
+    return dW_out, dG_out
+
+
+def chunk_step(cfg, Ws, Q, K, V, eta, update: bool = True):
+    """One chunk of the layer loop (sequence_forward's body): (O, new matrices)."""
+    Ws = [np.asarray(w, np.float64) for w in Ws]
+    if not update:
+        return fw_apply(cfg.fw, Ws, Q), Ws
+    O = fw_apply(cfg.fw, Ws, Q) if cfg.order == APPLY_THEN_UPDATE else None
+    g = chunk_gradient(cfg.fw, cfg.loss, Ws, K, V, eta)
+    Wn = update_state(Ws, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
+    if O is None:
+        O = fw_apply(cfg.fw, Wn, Q)
+    return O, Wn
+
+
+def chunk_vjp(cfg, Ws, Q, K, V, eta, dO, dWs_new, update: bool = True):
+    """Backward of chunk_step: given the cotangents dO of the chunk's outputs and dWs_new of
+    the state after it, the gradients of <dO, O> + sum_m <dW_new_m, W_new_m> with respect
+    to the chunk's inputs and the state before it. The apply's part comes from apply_vjp
+    (with the state the queries saw: before the update under the shifted order, after it
+    under the update-then-apply order), the update's from update_state_vjp and
+    gradient_vjp. Returns (dQ, dK, dV, deta, [dW before the chunk])."""
+    Ws = [np.asarray(w, np.float64) for w in Ws]
+    dWs_new = [np.asarray(x, np.float64) for x in dWs_new]
+    n = len(eta)
+    if not update:
+        dQ, dWa = apply_vjp(cfg.fw, Ws, Q, dO)
+        return (dQ, np.zeros((n, cfg.dim)), np.zeros((n, cfg.dim)), np.zeros(n),
+                [a + b for a, b in zip(dWs_new, dWa)])
+    g = chunk_gradient(cfg.fw, cfg.loss, Ws, K, V, eta)
+    if cfg.order == APPLY_THEN_UPDATE:
+        dQ, dW_apply = apply_vjp(cfg.fw, Ws, Q, dO)
+        dW_into_new = dWs_new
+    else:
+        Wn = update_state(Ws, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
+        dQ, dWa_new = apply_vjp(cfg.fw, Wn, Q, dO)
+        dW_apply = [np.zeros_like(w) for w in Ws]
+        dW_into_new = [a + b for a, b in zip(dWs_new, dWa_new)]
+    dW_step, dG = update_state_vjp(Ws, g, dW_into_new, cfg.ns_steps, cfg.renorm,
+                                   cfg.step_sizes(), cfg.weight_decay)
+    dW_grad, dK, dV, deta = gradient_vjp(cfg.fw, cfg.loss, Ws, K, V, eta, dG)
+    dW = [a + b + c for a, b, c in zip(dW_apply, dW_step, dW_grad)]
+    return dQ, dK, dV, deta, dW
+
+
+def sequence_vjp(cfg, W0s, Q, K, V, eta, dO, dW_final=None, update_chunks=None):
+    """Backward of sequence_forward for one problem: the states before every chunk are
+    recomputed forward, then the chunks are taken back from the last to the first.
+    Returns (dQ, dK, dV, deta, [dW0])."""
+    T = len(eta)
+    b = cfg.chunk
+    Ws = [np.asarray(w, np.float64) for w in W0s]
+    states = []
+    for c in range(T // b):
+        states.append(Ws)
+        S = slice(c * b, (c + 1) * b)
+        up = update_chunks is None or bool(update_chunks[c])
+        _, Ws = chunk_step(cfg, Ws, Q[S], K[S], V[S], eta[S], up)
+    dW = [np.zeros_like(w) for w in Ws] if dW_final is None else \
+        [np.asarray(x, np.float64) for x in dW_final]
+    dQ, dK, dV = np.zeros((T, cfg.dim)), np.zeros((T, cfg.dim)), np.zeros((T, cfg.dim))
+    deta = np.zeros(T)
+    for c in reversed(range(T // b)):
+        S = slice(c * b, (c + 1) * b)
+        up = update_chunks is None or bool(update_chunks[c])
+        dQ[S], dK[S], dV[S], deta[S], dW = chunk_vjp(cfg, states[c], Q[S], K[S], V[S], eta[S],
+                                                     dO[S], dW, up)
+    return dQ, dK, dV, deta, dW
