@@ -197,6 +197,35 @@ ttt_status ttt_sequence_forward_masked(ttt_state* s, const void* q, const void* 
 ttt_status ttt_apply_backward(ttt_state* s, const void* q, const void* dout, void* dq,
                               float* dw, void* stream);
 
+/*
+ * Backward through one chunk (apply and update), for training through the inner updates:
+ * the outer loop of the second TTT-E2E page (intelliparadigm.com, §2.2: inner TTT on copied
+ * weights, outer update through them; §5.1: the second-order gradients this needs) and the
+ * train-view backward the Modular TTT abstract composes into the layer's backward.  With the
+ * state as it stands taken as the state before the chunk (restore it with ttt_set_state),
+ * and the chunk's q, k, v, eta ([B][H][chunk][dim], eta [B][H][chunk]), computes the
+ * gradients of
+ *     sum_t <dout_t, o_t> + <dw, W_after>
+ * (o the chunk's outputs, W_after the state after the chunk's update) with respect to the
+ * chunk's inputs and the state before it:
+ *   dout  in,  [B][H][chunk][dim] activation dtype
+ *   dw    in:  fp32, ttt_get_state layout, the cotangent of the state after the chunk;
+ *         out: overwritten with the cotangent of the state before the chunk
+ *   dq, dk, dv  out, [B][H][chunk][dim] activation dtype;  deta  out, fp32 [B][H][chunk]
+ * The update is taken back step by step: the row renorm, the step with its step size and
+ * weight decay, Muon's Newton-Schulz iteration, and the chunk gradient itself (second order
+ * in the net).  Chaining calls from the last chunk to the first, each with the state before
+ * its chunk, gives the gradients of a whole sequence.  Serves the SwiGLU net with the
+ * inner-product loss under the shifted (apply-then-update) order on the staged path, with
+ * chunks of at most 65536 tokens; other configurations return TTT_E_UNSUPPORTED.  The state
+ * is not changed.  The first call on a state allocates the backward's workspace (about
+ * 3 GB for the LaCT language-model layer; TTT_E_ALLOC if it cannot); later calls allocate
+ * nothing.  All pointers device, caller-owned, 16-byte aligned; enqueued on stream.
+ */
+ttt_status ttt_chunk_backward(ttt_state* s, const void* q, const void* k, const void* v,
+                              const float* eta, const void* dout, float* dw, void* dq,
+                              void* dk, void* dv, float* deta, void* stream);
+
 /* Copy the fp32 state out / in.  Layout: matrix by matrix, each [batch][heads][rows][cols]
  * with the shapes listed under ttt_init_state.  dst/src: device, ttt_state_numel values.
  * The state is what carries over from one step to the next (TTT-layer explainer page,
@@ -247,14 +276,16 @@ ttt_status ttt_sequence_forward_noalloc(const ttt_config* cfg, float* state, con
  * Stages: 0 front (query rows), 1 front (key rows), 2 output GEMM, 3 token contraction,
  * 4 Newton-Schulz Gram, 5 Newton-Schulz polynomial, 6 Newton-Schulz update,
  * 7 update + renorm, 8 fp32 plane split, 9 MSE error / dH GEMMs,
- * 10 device-resident chunk loop (one launch per call), 11 the apply backward's dQ GEMM.
+ * 10 device-resident chunk loop (one launch per call), 11 the backward's dQ, dK and dV
+ * GEMMs, 12 the chunk backward's tangent front (and its eta sums), 13 its Newton-Schulz
+ * backward GEMMs.
  * The hooks create and destroy HIP events but allocate no device memory.
  */
 typedef enum {
   TTT_STAGE_FRONT_Q = 0, TTT_STAGE_FRONT_K = 1, TTT_STAGE_OUT = 2, TTT_STAGE_CONTRACT = 3,
   TTT_STAGE_NS_GRAM = 4, TTT_STAGE_NS_POLY = 5, TTT_STAGE_NS_UPDATE = 6, TTT_STAGE_RENORM = 7,
   TTT_STAGE_SPLIT = 8, TTT_STAGE_MSE = 9, TTT_STAGE_RESIDENT = 10, TTT_STAGE_DQ = 11,
-  TTT_STAGE_COUNT = 12
+  TTT_STAGE_TFRONT = 12, TTT_STAGE_NS_BWD = 13, TTT_STAGE_COUNT = 14
 } ttt_stage;
 ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches);
 ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms);

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "ttt_sequence_forward": [vp, vp, vp, vp, vp, vp, i64, vp],
             "ttt_sequence_forward_masked": [vp, vp, vp, vp, vp, vp, i64, vp, vp],
             "ttt_apply_backward": [vp, vp, vp, vp, vp, vp],
+            "ttt_chunk_backward": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "ttt_get_state": [vp, vp, vp],
             "ttt_set_state": [vp, vp, vp],
             "ttt_state_health": [vp],
@@ -196,6 +197,15 @@ def ttt_apply_backward(st: State, q, dout, dq, dw, stream=None) -> None:
                                     _stream(stream)))
 
 
+def ttt_chunk_backward(st: State, q, k, v, eta, dout, dw, dq, dk, dv, deta, stream=None) -> None:
+    """Backward through one chunk with the state as it stands (the state before the chunk):
+    dw holds the cotangent of the state after the chunk and receives that of the state
+    before it; dq, dk, dv, deta receive the input gradients (see include/libttt.h)."""
+    _check(lib().ttt_chunk_backward(st.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(dout),
+                                    _ptr(dw), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
+                                    _stream(stream)))
+
+
 def ttt_sequence_forward(st: State, q, k, v, eta, out, seq_len: int, stream=None) -> None:
     _check(lib().ttt_sequence_forward(st.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                       _ptr(out), int(seq_len), _stream(stream)))
@@ -249,7 +259,8 @@ def ttt_destroy_state(st: State) -> None:
 
 
 STAGES = {"front_q": 0, "front_k": 1, "out": 2, "contract": 3, "ns_gram": 4, "ns_poly": 5,
-          "ns_update": 6, "renorm": 7, "split": 8, "mse": 9, "resident": 10, "dq": 11}
+          "ns_update": 6, "renorm": 7, "split": 8, "mse": 9, "resident": 10, "dq": 11,
+          "tfront": 12, "ns_bwd": 13}
 
 
 def ttt_profile_begin(st: State, stage, max_launches: int = 4096) -> None:

@@ -181,6 +181,16 @@ struct ttt_state {
   float* neg1 = nullptr;  // [sb] of -1: the apply backward's eta
   int contract_tiles = 0;
   bool resident = false;  // the device-resident chunk loop serves this state (Wpl unused)
+  // backward through an update: workspace allocated by the first ttt_chunk_backward call
+  struct Bwd {
+    char* arena = nullptr;
+    float *g32 = nullptr, *du = nullptr, *dx32[2] = {}, *t32 = nullptr, *dg32 = nullptr;
+    float *dws = nullptr, *dwg = nullptr, *dwa = nullptr;
+    float *dotpart = nullptr, *eta_part = nullptr;
+    u16* xit[8] = {};               // Newton-Schulz iterates 1..steps-1 (0 is xpl[0])
+    u16 *dxp[2] = {}, *tp = nullptr, *sp = nullptr, *dgp = nullptr;
+    u16 *pd = nullptr, *a1 = nullptr, *a3 = nullptr;
+  } bw;
   // measurement hooks
   int prof_stage = -1, prof_cap = 0, prof_n = 0;
   hipEvent_t* prof_ev = nullptr;
@@ -396,7 +406,7 @@ ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
 // block into U (plain step; weight orientation) or the first Newton-Schulz input (muon).
 // ca holds the per-matrix operands and sizes.
 ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool first,
-                        bool last, hipStream_t st) {
+                        bool last, hipStream_t st, bool weight_orient = true) {
   const Dims& D = s->D;
   const int P = D.P, d = D.d;
   ca.G = s->G;
@@ -410,7 +420,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   ca.gpart = s->gpart;
   ca.gpart_stride = (int64_t)D.nm * P * d * D.n;
   ca.ksplit = s->ksplit;
-  ca.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
+  ca.tr_mask = weight_orient ? (D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2)) : 0;
   // operands of one launch share a plane count per side: group the matrices accordingly
   int m0 = 0;
   while (m0 < D.nm) {
@@ -430,7 +440,10 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   return TTT_OK;
 }
 
-ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStream_t st) {
+// g32: also sum the gradient, in the X orientation, into this fp32 buffer (the backward's
+// Newton-Schulz scaling needs it).
+ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStream_t st,
+                     float* g32 = nullptr) {
   const Dims& D = s->D;
   const ttt_config& c = s->cfg;
   const size_t es = c.act == TTT_BF16 ? 2 : 4;
@@ -544,13 +557,18 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     if (mse) { ca.a[m] = colop(e, d); ca.b[m] = colop(hk, dh); }
     else { ca.a[m] = as_cols(xv, d); ca.b[m] = colop(pk, dh); }
   }
-  return contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
+  ttt_status r = contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
+  if (r != TTT_OK || !g32) return r;
+  return contract_all(s, ca, g32, false, first, last, st, false);
 }
 
-ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
+// keep: write iterate it + 1 to keep[it + 1] (kept for the backward) instead of the
+// ping-pong buffers; iterate 0 stays in xpl[0].
+ttt_status newton_schulz(ttt_state* s, hipStream_t st, u16* const* keep = nullptr) {
   const Dims& D = s->D;
   const int steps = s->cfg.ns_steps;
   const int Z = D.nm * D.P, M = D.d, N = D.n;
+  auto iterate = [&](int i) { return (keep && i > 0) ? keep[i] : s->xpl[i & 1]; };
   for (int it = 0; it < steps; ++it) {
     // products on pk planes; the iterates X keep D.np planes between iterations
     const int pk = ((D.ns_one >> it) & 1) ? 1 : D.np;
@@ -561,14 +579,15 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st) {
     a.coef_a = 3.4445f; a.coef_b = -4.7750f; a.coef_c = 2.0315f;
     a.part = s->part; a.nparts = s->contract_tiles; a.first = it == 0; a.last = it == steps - 1;
     a.eps = 1e-7f;
-    a.xin = pbuf(s->xpl[it & 1], D.np, (int64_t)Z * M * N, (int64_t)M * N, N);
+    a.xin = pbuf(iterate(it), D.np, (int64_t)Z * M * N, (int64_t)M * N, N);
     a.aout = pbuf(s->apl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
     STAGED(TTT_STAGE_NS_GRAM, launch_ns_gram(a, st));
     a.ain = a.aout;
     a.aout = pbuf(s->bpl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
     STAGED(TTT_STAGE_NS_POLY, launch_ns_poly(a, st));
     a.ain = a.aout;
-    a.xout = pbuf(s->xpl[(it + 1) & 1], D.np, (int64_t)Z * M * N, (int64_t)M * N, N);
+    a.xout = pbuf(it + 1 < steps ? iterate(it + 1) : s->xpl[(it + 1) & 1], D.np,
+                  (int64_t)Z * M * N, (int64_t)M * N, N);
     a.U = s->U;
     a.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
     STAGED(TTT_STAGE_NS_UPDATE, launch_ns_update(a, st));
@@ -695,6 +714,286 @@ ttt_status check_ptr(const void* p, const char* name) {
   if (!p) return fail(TTT_E_NULL, "%s is NULL", name);
   if (reinterpret_cast<uintptr_t>(p) % 16)
     return fail(TTT_E_ALIGN, "%s is not 16-byte aligned", name);
+  return TTT_OK;
+}
+
+// ---------------------------------------------------------------- backward through an update
+// Workspace of the chunk backward, carved from one allocation made by the first call.
+ttt_status ensure_bwd(ttt_state* s) {
+  if (s->bw.arena) return TTT_OK;
+  const Dims& D = s->D;
+  const ttt_config& c = s->cfg;
+  const int64_t P = D.P, d = D.d, dh = D.dh, n = D.n, sb = D.sb, Z = (int64_t)D.nm * P;
+  const int64_t xs = Z * d * n;   // one X-orientation tensor
+  const bool muon = c.ns_steps > 0;
+  Carver C;
+  size_t og = muon ? C.take<float>(xs) : 0, odu = C.take<float>(xs);
+  size_t odx[2] = {0, 0}, ot = 0, odxp[2] = {0, 0}, otp = 0, osp = 0, odot = 0;
+  size_t oit[8] = {};
+  if (muon) {
+    for (int i = 0; i < 2; ++i) odx[i] = C.take<float>(xs);
+    ot = C.take<float>(Z * d * d);
+    for (int i = 0; i < 2; ++i) odxp[i] = C.take<u16>(D.np * xs);
+    otp = C.take<u16>(D.np * Z * d * d);
+    osp = C.take<u16>(D.np * Z * d * d);
+    odot = C.take<float>(Z * gemm2_tiles(d, n));
+    for (int i = 1; i < c.ns_steps; ++i) oit[i] = C.take<u16>(D.np * xs);
+  }
+  size_t odg = C.take<float>(xs), odgp = C.take<u16>(D.gp * xs);
+  const int64_t sn = state_numel(D);
+  size_t ows = C.take<float>(sn), owg = C.take<float>(sn), owa = C.take<float>(sn);
+  size_t oep = C.take<float>(P * sb * ((dh + 63) / 64));
+  size_t opd = C.take<u16>(D.gp * P * sb * dh), oa1 = C.take<u16>(D.gp * P * sb * dh),
+         oa3 = C.take<u16>(D.gp * P * sb * dh);
+  char* base = nullptr;
+  hipError_t e = hipMalloc(&base, C.off);
+  if (e != hipSuccess)
+    return fail(e == hipErrorOutOfMemory ? TTT_E_ALLOC : TTT_E_HIP,
+                "backward workspace of %zu bytes: %s", C.off, hipGetErrorString(e));
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(base + o); };
+  auto H = [&](size_t o) { return reinterpret_cast<u16*>(base + o); };
+  ttt_state::Bwd& b = s->bw;
+  b.arena = base;
+  b.g32 = muon ? F(og) : nullptr;
+  b.du = F(odu);
+  if (muon) {
+    for (int i = 0; i < 2; ++i) { b.dx32[i] = F(odx[i]); b.dxp[i] = H(odxp[i]); }
+    b.t32 = F(ot); b.tp = H(otp); b.sp = H(osp); b.dotpart = F(odot);
+    b.xit[0] = s->xpl[0];
+    for (int i = 1; i < c.ns_steps; ++i) b.xit[i] = H(oit[i]);
+  }
+  b.dg32 = F(odg); b.dgp = H(odgp);
+  b.dws = F(ows); b.dwg = F(owg); b.dwa = F(owa);
+  b.eta_part = F(oep);
+  b.pd = H(opd); b.a1 = H(oa1); b.a3 = H(oa3);
+  return TTT_OK;
+}
+
+// Backward of the Newton-Schulz iteration: from dU (X orientation, in bw.du) to dG (bw.dg32
+// and its planes), with the iterates kept by the forward recompute.
+ttt_status ns_backward(ttt_state* s, hipStream_t st) {
+  const Dims& D = s->D;
+  ttt_state::Bwd& b = s->bw;
+  const int steps = s->cfg.ns_steps;
+  const int Z = D.nm * D.P, M = D.d, N = D.n, np = D.np;
+  const int64_t xs = (int64_t)Z * M * N, as = (int64_t)Z * M * M;
+  const float ca = 3.4445f, cb = -4.7750f, cc = 2.0315f, eps = 1e-7f;
+  auto xpb = [&](u16* p) { return pbuf(p, np, xs, (int64_t)M * N, N); };
+  auto apb = [&](u16* p) { return pbuf(p, np, as, (int64_t)M * M, M); };
+  // dX_5 = dU, as planes for the products
+  SplitArgs sa{};
+  sa.x = b.du; sa.x_zstride = (int64_t)M * N; sa.n = M; sa.d = N;
+  sa.out = xpb(b.dxp[0]);
+  STAGED(TTT_STAGE_SPLIT, launch_split(sa, Z, st));
+  const float* dx32 = b.du;
+  int cur = 0;
+  for (int it = steps - 1; it >= 0; --it) {
+    const bool first = it == 0;
+    // A and B' = a I + b A + c A^2 of this iteration, from its iterate (iteration 0's
+    // iterate holds G, the Gram's scale s^2 applied in its epilogue)
+    NsArgs a{};
+    a.Z = Z; a.M = M; a.N = N; a.P = D.P; a.pl = np; a.fold = 1;
+    a.coef_a = ca; a.coef_b = cb; a.coef_c = cc;
+    a.part = s->part; a.nparts = s->contract_tiles; a.first = first; a.last = 0; a.eps = eps;
+    a.xin = xpb(b.xit[it]);
+    a.aout = apb(s->apl);
+    STAGED(TTT_STAGE_NS_GRAM, launch_ns_gram(a, st));
+    a.ain = a.aout;
+    a.aout = apb(s->bpl);
+    STAGED(TTT_STAGE_NS_POLY, launch_ns_poly(a, st));
+    const Operand X = operand_of(xpb(b.xit[it]), np, M);        // rows of X, K = N
+    const Operand dX = operand_of(xpb(b.dxp[cur]), np, M);
+    // T = dX X^T + X dX^T   (iteration 0: X = s G, s from the forward's tile sums)
+    Gemm2Args g{};
+    g.M = M; g.N = M; g.K = N; g.Z = Z;
+    g.a[0] = dX; g.b[0] = X; g.a[1] = X; g.b[1] = dX;
+    g.alpha = 1.f; g.beta = 0.f;
+    g.cout = b.t32; g.pout = apb(b.tp);
+    g.spart = first ? s->part : nullptr; g.nspart = s->contract_tiles; g.eps = eps;
+    STAGED(TTT_STAGE_NS_BWD, launch_gemm2(g, false, st));
+    // S = b T + c (T A + A T) (A, T symmetric: rows serve as columns); iteration 0 takes
+    // the factor s of X0 = s G here, so that the next product can use G's planes
+    Gemm2Args h{};
+    h.M = M; h.N = M; h.K = M; h.Z = Z;
+    h.a[0] = operand_of(apb(b.tp), np, M); h.b[0] = operand_of(apb(s->apl), np, M);
+    h.a[1] = h.b[0]; h.b[1] = h.a[0];
+    h.alpha = cc; h.beta = cb; h.cin = b.t32;
+    h.pout = apb(b.sp);
+    h.spart = first ? s->part : nullptr; h.nspart = s->contract_tiles; h.eps = eps;
+    STAGED(TTT_STAGE_NS_BWD, launch_gemm2(h, false, st));
+    // dX_prev = B' dX + S X, the X-side operands read by columns (K = M)
+    Gemm2Args u{};
+    u.M = M; u.N = N; u.K = M; u.Z = Z;
+    u.a[0] = operand_of(apb(s->bpl), np, M); u.b[0] = operand_of(xpb(b.dxp[cur]), np, N);
+    u.a[1] = operand_of(apb(b.sp), np, M); u.b[1] = operand_of(xpb(b.xit[it]), np, N);
+    u.alpha = 1.f; u.beta = 0.f;
+    u.cout = b.dx32[1 - cur];
+    if (!first) u.pout = xpb(b.dxp[1 - cur]);
+    if (first) { u.gref = b.g32; u.gpart = b.dotpart; }
+    STAGED(TTT_STAGE_NS_BWD, launch_gemm2(u, true, st));
+    dx32 = b.dx32[1 - cur];
+    cur = 1 - cur;
+  }
+  NsFinArgs f{};
+  f.G = b.g32; f.dX = dx32;
+  f.ss_part = s->part; f.nss = s->contract_tiles;
+  f.dot_part = b.dotpart; f.ndot = gemm2_tiles(M, N);
+  f.per = (int64_t)M * N; f.eps = eps;
+  f.dG = b.dg32;
+  f.pout = pbuf(b.dgp, D.gp, xs, (int64_t)M * N, N);
+  STAGED(TTT_STAGE_NS_BWD, launch_ns_fin(f, Z, st));
+  return TTT_OK;
+}
+
+// The gradient's backward over one block of key rows: the tangent front, then dK, dV, d eta
+// and the weight gradients (summed into bw.dwg over the chunk's blocks).
+ttt_status grad_bwd_rows(ttt_state* s, const Rows& R, bool first, bool last, void* dk,
+                         void* dv, float* deta, hipStream_t st) {
+  const Dims& D = s->D;
+  const ttt_config& c = s->cfg;
+  ttt_state::Bwd& b = s->bw;
+  const size_t es = c.act == TTT_BF16 ? 2 : 4;
+  const int P = D.P, d = D.d, dh = D.dh, gp = D.gp;
+  const int64_t SB = D.sb, Z = (int64_t)D.nm * P, xs = Z * d * D.n;
+  const char* k = R.k + R.t0 * d * es;
+  const char* v = R.v + R.t0 * d * es;
+  const float* eta = R.eta + R.t0;
+  auto tok = [&](u16* p, int cols) { return pbuf(p, gp, (int64_t)P * SB * cols, SB * cols, cols); };
+  Operand xk, xv;
+  if (c.act == TTT_F32) {
+    SplitArgs sa{};
+    sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
+    sa.x = k; sa.out = pbuf(s->kpl, D.in_kv, (int64_t)P * SB * d, SB * d, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    xk = operand_of(sa.out, D.in_kv, R.nr);
+    sa.x = v; sa.out = pbuf(s->vpl, D.in_kv, (int64_t)P * SB * d, SB * d, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    xv = operand_of(sa.out, D.in_kv, R.nr);
+  } else {
+    xk = act_operand(k, R.T * d, d, R.nr);
+    xv = act_operand(v, R.T * d, d, R.nr);
+  }
+  auto as_cols = [&](Operand o, int cols) { o.rows = cols; return o; };
+  auto wop = [&](int m) {
+    return operand_of(pbuf(s->Wpl[m], gp, (int64_t)P * D.rows[m] * D.cols[m],
+                           (int64_t)D.rows[m] * D.cols[m], D.cols[m]), gp, D.rows[m]);
+  };
+  // D_m, the gradient's cotangent, X orientation [d][dh] per (matrix, problem)
+  auto dop = [&](int m, int rows) {
+    PlaneBuf pb = pbuf(b.dgp + (int64_t)m * P * d * D.n, gp, xs, (int64_t)d * D.n, D.n);
+    return operand_of(pb, gp, rows);
+  };
+  const PlaneBuf pp = tok(s->pk, dh), ppd = tok(b.pd, dh), pa1 = tok(b.a1, dh),
+                 pa3 = tok(b.a3, dh), pz1 = tok(s->dz1, dh), pz3 = tok(s->dz3, dh);
+  TFrontArgs t{};
+  t.A[0] = xk; t.A[1] = xv;
+  t.B[0] = wop(0); t.B[1] = wop(1);
+  t.B[2] = dop(0, dh); t.B[3] = dop(1, dh);            // read by columns: rows = hidden
+  t.B[4] = operand_of(pbuf(s->Wpl[2], gp, (int64_t)P * d * dh, (int64_t)d * dh, dh), gp, dh);
+  t.B[5] = dop(2, dh);
+  t.eta = eta; t.eta_zstride = R.T;
+  t.nrows = R.nr; t.K = d; t.N = dh;
+  t.p = pp; t.pd = ppd; t.a1 = pa1; t.a3 = pa3; t.dz1 = pz1; t.dz3 = pz3;
+  const int ntn = (dh + 63) / 64;
+  t.eta_part = b.eta_part; t.part_zstride = SB * ntn;
+  STAGED(TTT_STAGE_TFRONT, launch_tfront(t, P, st));
+  EtaSumArgs es_{};
+  es_.part = b.eta_part; es_.part_zstride = SB * ntn; es_.nparts = ntn; es_.nrows = R.nr;
+  es_.deta = deta + R.t0; es_.deta_zstride = R.T;
+  STAGED(TTT_STAGE_TFRONT, launch_eta_sum(es_, P, st));
+  // dK = A1 W1 + A3 W3 + dZ1 D1 + dZ3 D3: W by columns, D (X orientation) by rows
+  DqArgs kq{};
+  kq.a[0] = operand_of(pa1, gp, R.nr); kq.b[0] = as_cols(wop(0), d);
+  kq.a[1] = operand_of(pa3, gp, R.nr); kq.b[1] = as_cols(wop(1), d);
+  kq.a[2] = operand_of(pz1, gp, R.nr); kq.b[2] = dop(0, d);
+  kq.a[3] = operand_of(pz3, gp, R.nr); kq.b[3] = dop(1, d);
+  kq.nrows = R.nr; kq.K = dh; kq.N = d;
+  kq.out = static_cast<char*>(dk) + R.t0 * d * es; kq.out_zstride = R.T * d;
+  kq.out_bf16 = c.act == TTT_BF16;
+  STAGED(TTT_STAGE_DQ, launch_rowgemm(kq, 4, P, st));
+  // dV = P D2^T + Pd W2^T (-eta J), both by rows
+  DqArgs vq{};
+  vq.a[0] = operand_of(pp, gp, R.nr); vq.b[0] = dop(2, d);
+  vq.a[1] = operand_of(ppd, gp, R.nr); vq.b[1] = wop(2);
+  vq.nrows = R.nr; vq.K = dh; vq.N = d;
+  vq.out = static_cast<char*>(dv) + R.t0 * d * es; vq.out_zstride = R.T * d;
+  vq.out_bf16 = c.act == TTT_BF16;
+  STAGED(TTT_STAGE_DQ, launch_rowgemm(vq, 2, P, st));
+  // weight gradients: A1^T K, A3^T K, V^T Pd, as the forward's contractions
+  ContractArgs ca{};
+  ca.P = P; ca.M = d; ca.N = D.n; ca.K = R.nr;
+  ca.a[0] = as_cols(xk, d); ca.b[0] = operand_of(pa1, gp, dh);
+  ca.a[1] = as_cols(xk, d); ca.b[1] = operand_of(pa3, gp, dh);
+  ca.a[2] = as_cols(xv, d); ca.b[2] = operand_of(ppd, gp, dh);
+  return contract_all(s, ca, b.dwg, false, first, last, st);
+}
+
+ttt_status chunk_backward(ttt_state* s, const void* q, const void* k, const void* v,
+                          const float* eta, const void* dout, float* dw, void* dq, void* dk,
+                          void* dv, float* deta, hipStream_t st) {
+  const ttt_config& c = s->cfg;
+  const Dims& D = s->D;
+  ttt_status r;
+  if ((r = ensure_bwd(s)) != TTT_OK) return r;
+  ttt_state::Bwd& b = s->bw;
+  const int64_t ch = c.chunk;
+  const bool muon = c.ns_steps > 0;
+  Rows R0{};
+  R0.q = static_cast<const char*>(q);
+  R0.k = static_cast<const char*>(k);
+  R0.v = static_cast<const char*>(v);
+  R0.eta = eta;
+  R0.T = ch;
+  auto block = [&](int64_t o) {
+    Rows R = R0;
+    R.t0 = o;
+    R.nr = (int)std::min<int64_t>(D.sb, ch - o);
+    return R;
+  };
+  // 1. the chunk's update again: gradient (and G in the X orientation), Newton-Schulz with
+  //    its iterates kept, U in the weight orientation
+  for (int64_t o = 0; o < ch; o += D.sb)
+    if ((r = grad_rows(s, block(o), o == 0, o + D.sb >= ch, st, muon ? b.g32 : nullptr)) != TTT_OK)
+      return r;
+  if (muon && (r = newton_schulz(s, st, b.xit)) != TTT_OK) return r;
+  // 2. step and renorm: dW_step, and dU in the X orientation
+  StepBwdArgs sb{};
+  sb.P = D.P; sb.nm = D.nm; sb.renorm = c.row_renorm; sb.keep = 1.f - c.weight_decay;
+  int64_t off = 0, xoff = 0;
+  for (int m = 0; m < D.nm; ++m) {
+    StepBwdMat& M = sb.m[m];
+    M.W = s->Wm[m]; M.U = s->Um[m]; M.dout = dw + off; M.dw = b.dws + off;
+    M.du = b.du + xoff;
+    M.rows = D.rows[m]; M.cols = D.cols[m]; M.tr = D.tr[m]; M.lr = c.lr[m];
+    sb.max_rows = std::max(sb.max_rows, D.rows[m]);
+    off += (int64_t)D.P * D.rows[m] * D.cols[m];
+    xoff += (int64_t)D.P * D.d * D.n;
+  }
+  STAGED(TTT_STAGE_RENORM, launch_step_bwd(sb, st));
+  // 3. Newton-Schulz backward (or the plain step's dG = dU), planes for the products
+  if (muon) {
+    if ((r = ns_backward(s, st)) != TTT_OK) return r;
+  } else {
+    SplitArgs sa{};
+    sa.x = b.du; sa.x_zstride = (int64_t)D.d * D.n; sa.n = D.d; sa.d = D.n;
+    sa.out = pbuf(b.dgp, D.gp, (int64_t)D.nm * D.P * D.d * D.n, (int64_t)D.d * D.n, D.n);
+    STAGED(TTT_STAGE_SPLIT, launch_split(sa, D.nm * D.P, st));
+  }
+  // 4. the gradient's backward per block of key rows
+  for (int64_t o = 0; o < ch; o += D.sb)
+    if ((r = grad_bwd_rows(s, block(o), o == 0, o + D.sb >= ch, dk, dv, deta, st)) != TTT_OK)
+      return r;
+  // 5. the apply step (the shifted order answers with the state before the update)
+  for (int64_t o = 0; o < ch; o += D.sb) {
+    Rows R = block(o);
+    R.v = static_cast<const char*>(dout);
+    R.out = static_cast<char*>(dq);
+    if ((r = apply_bwd_rows(s, R, o == 0, o + D.sb >= ch, b.dwa, st)) != TTT_OK) return r;
+  }
+  // 6. dW before the chunk
+  Add3Args ad{};
+  ad.x = b.dwa; ad.y = b.dws; ad.w = b.dwg; ad.out = dw; ad.n = state_numel(D);
+  STAGED(TTT_STAGE_RENORM, launch_add3(ad, st));
   return TTT_OK;
 }
 
@@ -920,6 +1219,28 @@ ttt_status ttt_apply_backward(ttt_state* s, const void* q, const void* dout, voi
   return TTT_OK;
 }
 
+ttt_status ttt_chunk_backward(ttt_state* s, const void* q, const void* k, const void* v,
+                              const float* eta, const void* dout, float* dw, void* dq,
+                              void* dk, void* dv, float* deta, void* stream) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  ttt_status r;
+  if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v")) ||
+      (r = check_ptr(eta, "eta")) || (r = check_ptr(dout, "dout")) || (r = check_ptr(dw, "dw")) ||
+      (r = check_ptr(dq, "dq")) || (r = check_ptr(dk, "dk")) || (r = check_ptr(dv, "dv")) ||
+      (r = check_ptr(deta, "deta")))
+    return r;
+  const ttt_config& c = s->cfg;
+  if (s->resident || c.fw != TTT_FW_SWIGLU || c.loss != TTT_LOSS_DOT ||
+      c.order != TTT_APPLY_THEN_UPDATE || c.chunk > SUBBLOCK_MAX)
+    return fail(TTT_E_UNSUPPORTED,
+                "the chunk backward serves the SwiGLU net with the inner-product loss under "
+                "the shifted (apply-then-update) order, on the staged path, with chunks of "
+                "at most %lld tokens", (long long)SUBBLOCK_MAX);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s->last = st;
+  return chunk_backward(s, q, k, v, eta, dout, dw, dq, dk, dv, deta, st);
+}
+
 ttt_status ttt_sequence_forward(ttt_state* s, const void* q, const void* k, const void* v,
                                 const float* eta, void* out, int64_t seq_len, void* stream) {
   if (!s) return fail(TTT_E_NULL, "state is NULL");
@@ -978,6 +1299,7 @@ ttt_status ttt_destroy_state(ttt_state* s) {
     delete[] s->prof_ev;
   }
   hipError_t e2 = hipFree(s->arena);
+  if (e2 == hipSuccess && s->bw.arena) e2 = hipFree(s->bw.arena);
   delete s;
   if (e1 != hipSuccess) return fail(TTT_E_HIP, "sync before free failed: %s", hipGetErrorString(e1));
   if (e2 != hipSuccess) return fail(TTT_E_HIP, "hipFree failed: %s", hipGetErrorString(e2));

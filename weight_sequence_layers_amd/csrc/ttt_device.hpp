@@ -44,6 +44,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum of v over the workgroup (every thread gets it); scratch: one float per wave of LDS.
+// Contains barriers: call from every thread.
+__device__ __forceinline__ void lds_barrier();
+__device__ __forceinline__ float block_sum(float v, float* scratch);
+
 // ------------------------------------------------------------------------ GEMM operands
 // A K-contiguous operand made of 1..3 bf16 planes: element (r, k) of plane q, problem z
 // lives at p[q * pstride + z * zstride + r * ld + k].  Rows >= rows and k >= K read as zero.
@@ -212,6 +217,18 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+__device__ __forceinline__ float block_sum(float v, float* scratch) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  lds_barrier();
+  if (lane == 0) scratch[wave] = v;
+  lds_barrier();
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += scratch[w];
+  lds_barrier();
+  return t;
+}
+
 // PL > 0 selects the plane-resident product: A[0..NA) and B[0..NB) are the bf16 planes of
 // one A and one B (each operand with planes = 1), PL = max(NA, NB); every K step loads all
 // NA + NB plane tiles once and accumulates the plane products (i, j) with i + j < PL into
@@ -231,8 +248,15 @@ __device__ __forceinline__ void lds_barrier() {
 // tiles through LDS into one owner per run of four accumulator elements (run g of tile t
 // to group (4 t + g) mod WGK); for_each, for_each4 and the tile stores visit the owned
 // runs only.
+//
+// SUM = true (PL = 0) accumulates every product into one accumulator (the kernel wants only
+// their sum).
+//
+// Pairing of A operands with products (PL = 0): NB0 >= 0 gives products p < NB0 A[0] and
+// the others A[1]; else with NA == NB product p takes A[p], and otherwise every product
+// takes A[0] except, with NA == 2, the last, which takes A[1].
 template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0,
-          int BK_ = 64, bool SW_ = false, int WGK_ = 1>
+          int BK_ = 64, bool SW_ = false, int WGK_ = 1, int NB0 = -1, bool SUM = false>
 struct Gemm {
   static constexpr bool SW = SW_;
   static constexpr int WGK = WGK_;
@@ -266,12 +290,12 @@ struct Gemm {
   // two separate __shared__ arrays by the kernel (GEMM_LDS)
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
   static_assert(PL == 0 || PL == (NA > NB ? NA : NB), "plane-resident mode: PL = max(NA, NB)");
-  static constexpr int NACC = PL ? 1 : NB;
+  static constexpr int NACC = (PL || SUM) ? 1 : NB;
 
   f32x16 acc[NACC][TM][TN];
 
   static __device__ __forceinline__ constexpr int ia(int p) {
-    return (NA == 2 && p == NB - 1) ? 1 : 0;
+    return NB0 >= 0 ? (p < NB0 ? 0 : 1) : NA == NB ? p : (NA == 2 && p == NB - 1) ? 1 : 0;
   }
 
   // one 32 x 32 x 16 product of an A-tile fragment and a B-tile fragment into c
@@ -460,7 +484,8 @@ struct Gemm {
             for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
               for (int tn = 0; tn < TN; ++tn)
-                acc[p][tm][tn] = mma(fa[ia(p)][tm], fb[p][tn], acc[p][tm][tn]);
+                acc[SUM ? 0 : p][tm][tn] =
+                    mma(fa[ia(p)][tm], fb[p][tn], acc[SUM ? 0 : p][tm][tn]);
         }
       }
     };

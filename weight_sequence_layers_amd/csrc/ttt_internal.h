@@ -67,12 +67,97 @@ struct OutArgs {
 
 // Backward of the apply step with respect to the queries: dQ [rows][dim] = sum over the
 // NP pairs of A_m [rows][hidden] (row-wise) times B_m = W_m [hidden][dim] (column-wise).
+// Also the chunk backward's dK (four pairs) and dV (two pairs) GEMMs: out = sum_m A_m B_m^T
+// with each B_m read by rows or by columns (the launcher's layout mask).
 struct DqArgs {
-  Operand a[2], b[2];
+  Operand a[4], b[4];
   int nrows, K, N, tiles_n, tiles;
   void* out;            // [problems][rows][dim] in the activation dtype
   int64_t out_zstride;
   int out_bf16;
+};
+
+// ---------------------------------------------------------------- backward through an update
+// Tangent front of the chunk backward (SwiGLU net, inner-product loss): on the chunk's key
+// rows, the six products Z1 = K W1^T, Z3 = K W3^T, Zd1 = K D1^T, Zd3 = K D3^T (D the
+// cotangent of the chunk gradient), V W2 and V D2, and in the epilogue the per-token terms
+// of the gradient's backward.
+struct TFrontArgs {
+  Operand A[2];         // K rows, V rows
+  Operand B[6];         // W1, W3 (rows); D1, D3, W2, D2 (read by columns)
+  const float* eta;
+  int64_t eta_zstride;
+  int nrows, K, N, tiles_n, tiles;
+  PlaneBuf p, pd, a1, a3, dz1, dz3;   // [rows][hidden]: -eta H, -eta Hd, A1, A3, dZ1, dZ3
+  float* eta_part;      // [Z][rows][tiles_n]: the tile's share of -sum_h (V D2 . H + V W2 . Hd)
+  int64_t part_zstride;
+};
+
+// Sum of the eta partials: deta[z][t] = sum_j part[z][t][j] (j < nparts), fixed order.
+struct EtaSumArgs {
+  const float* part;
+  int64_t part_zstride;
+  int nparts, nrows;
+  float* deta;          // [Z][T] caller tensor (stride deta_zstride)
+  int64_t deta_zstride;
+};
+
+// Backward of the step and row renorm for one matrix kind (one wave per row, like k_renorm):
+// Y = keep W - lr U, out = renorm(Y) (or Y).  Writes dW_step = (renorm: <yh, dOut> / |w| w)
+// + keep dY and dU = -lr dY (the latter in the X orientation: transposed when tr).
+struct StepBwdMat {
+  const float* W;       // [P][rows][cols]
+  const float* U;
+  const float* dout;    // cotangent of the new matrix
+  float* dw;            // dW_step
+  float* du;            // dU, X orientation
+  int rows, cols, tr;
+  float lr;
+};
+struct StepBwdArgs {
+  StepBwdMat m[3];
+  int P, nm, renorm, max_rows;
+  float keep;
+};
+
+// Generic two-pair GEMM of the Newton-Schulz backward: out = alpha (A0 B0^T + A1 B1^T) + beta cin
+// over Z matrices of M x N, B operands read by rows or columns (the launcher's mask); fp32
+// and/or plane outputs; optionally per-tile sums of out * gref (the Frobenius inner product).
+struct Gemm2Args {
+  Operand a[2], b[2];
+  int M, N, K, Z, tiles_n, tiles;
+  float alpha, beta;
+  const float* cin;     // [Z][M][N] or null
+  float* cout;          // [Z][M][N] or null
+  PlaneBuf pout;        // planes, or np = 0
+  const float* gref;    // [Z][M][N] or null
+  float* gpart;         // [Z][tiles] per-tile sums of out * gref
+  // optional per-matrix factor 1 / (sqrt(sum of spart[z][0 .. nspart)) + eps) on the whole
+  // output (the Newton-Schulz scale of iteration 0, from the forward's tile sums)
+  const float* spart;
+  int nspart;
+  float eps;
+};
+
+// Backward of X0 = G / (|G|_F + eps): dG = dX0 s - G <G, dX0> s^2 / |G|_F, s = 1 / (|G|_F + eps).
+struct NsFinArgs {
+  const float* G;       // [Z][M][N] X orientation
+  const float* dX;      // [Z][M][N]
+  const float* ss_part; // [Z][nss] sums of squares of G (forward contraction tiles)
+  int nss;
+  const float* dot_part;  // [Z][ndot] sums of G . dX0
+  int ndot;
+  int64_t per;          // M * N
+  float eps;
+  float* dG;            // [Z][M][N] fp32
+  PlaneBuf pout;        // planes of dG
+};
+
+// out[i] = x[i] + y[i] + w[i] over n values (any of y, w may be null).
+struct Add3Args {
+  const float *x, *y, *w;
+  float* out;
+  int64_t n;
 };
 
 // Token contractions: X_m[i][j] = sum_t A_m[t][i] B_m[t][j] for every matrix m and problem
@@ -168,6 +253,17 @@ hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t
 hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s);
 hipError_t launch_contract(const ContractArgs& a, int nm, hipStream_t s);
 hipError_t launch_dq(const DqArgs& a, int np, int Z, hipStream_t s);
+// backward through an update (ttt_backward.hip)
+hipError_t launch_tfront(const TFrontArgs& a, int Z, hipStream_t s);
+hipError_t launch_eta_sum(const EtaSumArgs& a, int Z, hipStream_t s);
+// dK (np 4: B0, B1 by columns, B2, B3 by rows) and dV (np 2, both by rows)
+hipError_t launch_rowgemm(const DqArgs& a, int np, int Z, hipStream_t s);
+hipError_t launch_step_bwd(const StepBwdArgs& a, hipStream_t s);
+// bcols: B operands read by columns (the dX update) or by rows (T and S)
+hipError_t launch_gemm2(const Gemm2Args& a, bool bcols, hipStream_t s);
+hipError_t launch_ns_fin(const NsFinArgs& a, int Z, hipStream_t s);
+hipError_t launch_add3(const Add3Args& a, hipStream_t s);
+int gemm2_tiles(int M, int N);
 // token ranges a contraction of `tiles` output tiles per matrix over nz matrices may split
 // into (the host sizes the partial-sum buffer with it)
 int contract_split_max(int tiles, int nz);

@@ -192,19 +192,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------ block reduction
-__device__ __forceinline__ float block_sum(float v, float* scratch) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  lds_barrier();
-  if (lane == 0) scratch[wave] = v;
-  lds_barrier();
-  float t = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += scratch[w];
-  lds_barrier();
-  return t;
-}
-
 // ------------------------------------------------------------------------ apply backward
 // dQ = sum_m dZ_m W_m for the NP (dZ_m, W_m) pairs: accumulator m takes pair m, and the
 // epilogue adds them and stores dQ like the apply output.
