@@ -143,6 +143,109 @@ def bench_apply_backward(args, cfg, planes):
     }), flush=True)
 
 
+def chunk_backward_flops(cfg) -> dict:
+    """Algorithmic FLOP of one ttt_chunk_backward call (one chunk, all problems) per stage, 2
+    per multiply-add: the update recomputed (gradient front and contractions, Newton-Schulz
+    with its iterates), the Newton-Schulz backward (per iteration A and B' again, then
+    T = dX X^T + X dX^T, S = b T + c (T A + A T) and B' dX + S X), the tangent front (six
+    products), dK (four), dV (two), the weight contractions (three), and the apply step's
+    backward (front, contractions, dQ)."""
+    P, b, d, dh = cfg.batch * cfg.heads, cfg.chunk, cfg.dim, cfg.hidden
+    m, n, it = d, dh, cfg.ns_steps
+    bdh = 2.0 * b * d * dh * P
+    f = {
+        "front_k": 3 * bdh + 3 * bdh,              # recompute + apply backward's front
+        "contract": 3 * bdh + 3 * bdh + 3 * bdh,   # recompute + weight gradients + apply's
+        "tfront": 6 * bdh,
+        "dq": 4 * bdh + 2 * bdh + 2 * bdh,         # dK, dV, dQ
+    }
+    if it:
+        nm3 = 3 * P * it
+        f["ns_gram"] = nm3 * 2.0 * m * m * n * 2   # forward iterates + backward's A
+        f["ns_poly"] = nm3 * 2.0 * m ** 3 * 2
+        f["ns_update"] = nm3 * 2.0 * m * m * n
+        f["ns_bwd"] = nm3 * (2 * 2.0 * m * m * n + 2 * 2.0 * m ** 3 + 2 * 2.0 * m * m * n)
+    return f
+
+
+def bench_chunk_backward(args, cfg, planes):
+    """Times ttt_chunk_backward on the workload's first chunk (state W0, cotangents drawn
+    from a seeded normal) and prints one JSON line of its own."""
+    import numpy as np
+    import torch
+
+    import ttt_inputs as ti
+    import weight_sequence_layers_amd as W
+
+    c = W.make_config(cfg, planes=planes, path="staged")
+    b = cfg.chunk
+    P = cfg.batch * cfg.heads
+    blocks = [ti.make_problem_inputs(cfg, bb, h, t1=b) for bb in range(cfg.batch)
+              for h in range(cfg.heads)]
+    dev = {}
+    for name in ("q", "k", "v"):
+        if cfg.act == "bf16":
+            x = np.stack([blk[name + "_bits"] for blk in blocks]).reshape(cfg.batch, cfg.heads, b, -1)
+            dev[name] = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            x = np.stack([blk[name] for blk in blocks]).reshape(cfg.batch, cfg.heads, b, -1)
+            dev[name] = torch.from_numpy(x).cuda()
+    eta = torch.from_numpy(np.stack([blk["eta"] for blk in blocks]).reshape(
+        cfg.batch, cfg.heads, b)).cuda()
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dout = torch.randn(dev["q"].shape, generator=g, device="cuda").to(dev["q"].dtype)
+    w0 = torch.from_numpy(np.concatenate([w.ravel() for w in ti.make_weights(cfg)])).cuda()
+    st = W.ttt_init_state(c, w0)
+    n = W.ttt_state_numel(c)
+    dw_in = torch.randn(n, generator=g, device="cuda")
+    dw = torch.empty_like(dw_in)
+    grads = [torch.empty_like(dev["q"]) for _ in range(3)]
+    deta = torch.empty_like(eta)
+
+    def call():
+        dw.copy_(dw_in)
+        W.ttt_chunk_backward(st, dev["q"], dev["k"], dev["v"], eta, dout, dw, *grads, deta)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    flops = chunk_backward_flops(cfg)
+    totals = {}
+    for name in flops:
+        W.ttt_profile_begin(st, name, 1 << 12)
+        call()
+        k, ms = W.ttt_profile_end(st)
+        if k:
+            totals[name] = (k, ms)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    W.ttt_state_health(st)
+    st.destroy()
+    total = sum(flops.values())
+    dom = max(totals, key=lambda x: totals[x][1])
+    per_launch = flops[dom] / totals[dom][0]
+    achieved = per_launch / (totals[dom][1] / totals[dom][0] / 1e3) / 1e12
+    print(json.dumps({
+        "metric": "chunk backward tokens/sec (dq, dk, dv, deta and the state cotangent)",
+        "value": round(P * b / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_call": round(1e3 * dt, 3), "higher_is_better": True,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} (one chunk of {b} tokens, {P} problems)",
+                   "bf16_planes_apply_grad_ns": list(planes[:3]),
+                   "ns_one_plane_iterations": [i for i in range(8) if (planes[3] >> i) & 1]},
+        "tflops_algorithmic": round(total / dt / 1e12, 2),
+        "pct_bf16_peak_algorithmic": round(100 * total / dt / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "kernel": dom},
+        "per_stage_ms": {k: round(v[1], 3) for k, v in totals.items()},
+    }), flush=True)
+
+
 def recorded_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from profiles/<workload>_traffic.md, if that summary
     was taken from the current kernel sources; else None."""
@@ -254,6 +357,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--apply-backward", action="store_true",
                     help="time the apply-step backward on the workload's first chunk instead")
+    ap.add_argument("--chunk-backward", action="store_true",
+                    help="time the backward through one chunk on the workload's first chunk")
     ap.add_argument("--cpu-chunks", type=int, default=None)
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time hipBLASLt (torch.bmm) on each stage's GEMM shapes")
@@ -281,6 +386,9 @@ def main():
     planes = tuple(int(x) for x in args.planes.split(",")) if args.planes else W.PRECISION[cfg.name]
     if args.apply_backward:
         bench_apply_backward(args, cfg, planes)
+        return
+    if args.chunk_backward:
+        bench_chunk_backward(args, cfg, planes)
         return
     c = W.make_config(cfg, planes=planes)
     torch.cuda.set_device(0)

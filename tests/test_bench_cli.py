@@ -37,3 +37,16 @@ def test_stage_flops_add_up_to_the_layer_total(name):
     f = bench.stage_flops(cfg)
     total = sum(v for k, v in f.items() if k != "resident")
     assert abs(total - bench.total_flops(cfg)) <= 1e-9 * total
+
+
+def test_chunk_backward_flop_accounting():
+    """The chunk backward's per-stage FLOP sum to 58 b d dh per problem for the GEMMs on
+    tokens and 15 (14 m^2 n + 8 m^3) for Newton-Schulz (five iterations forward and back,
+    three matrices)."""
+    import bench
+    import ttt_inputs as ti
+    cfg = ti.CONFIGS["lm"].replace(seq_len=2048)
+    P, b, d, dh = 8, 2048, 512, 1024
+    total = sum(bench.chunk_backward_flops(cfg).values())
+    expect = P * (58.0 * b * d * dh + 15 * (14.0 * d * d * dh + 8.0 * d ** 3))
+    assert abs(total - expect) <= 1e-9 * expect

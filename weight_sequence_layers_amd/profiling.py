@@ -39,7 +39,9 @@ STAGE_KERNELS = [
     ("renorm", r"k_renorm"),
     ("split", r"k_split"),
     ("resident", r"k_small_gelu<"),
-    ("dq", r"k_dq<"),
+    ("dq", r"k_dq<|k_rowgemm<"),
+    ("tfront", r"k_tfront<|k_eta_sum"),
+    ("ns_bwd", r"k_gemm2<|k_ns_fin"),
 ]
 
 
