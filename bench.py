@@ -357,6 +357,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--apply-backward", action="store_true",
                     help="time the apply-step backward on the workload's first chunk instead")
+    ap.add_argument("--replay", action="store_true",
+                    help="record each step's launches in a HIP graph and replay it")
     ap.add_argument("--chunk-backward", action="store_true",
                     help="time the backward through one chunk on the workload's first chunk")
     ap.add_argument("--cpu-chunks", type=int, default=None)
@@ -390,7 +392,7 @@ def main():
     if args.chunk_backward:
         bench_chunk_backward(args, cfg, planes)
         return
-    c = W.make_config(cfg, planes=planes)
+    c = W.make_config(cfg, planes=planes, replay=args.replay)
     torch.cuda.set_device(0)
     log(f"workload {cfg}  planes {planes}")
 
@@ -484,6 +486,7 @@ def main():
                                f"{int(cfg.renorm)}, {cfg.act}, {cfg.order}",
                    "global_batch": cfg.batch, "seq_len": cfg.seq_len, "parallelism": "none",
                    "bf16_planes_apply_grad_ns": list(planes[:3]), "ns_one_plane_iterations": [i for i in range(8) if (planes[3] >> i) & 1],
+                   "replay": bool(args.replay),
                    **({"lr": list(cfg.step_sizes()), "weight_decay": cfg.weight_decay}
                       if (cfg.lr or cfg.weight_decay) else {})},
         "source_digest": source_digest(),

@@ -118,6 +118,16 @@ typedef struct {
    * smaller Muon step when the loss oscillates.)                                         */
   float lr[3];
   float weight_decay;
+  /* Replay (0 or 1).  With 1, the first forward call with a given set of tensor pointers,
+   * length and update flags records its kernel launches into a HIP graph (captured on an
+   * internal stream of default priority; nothing captured is a memset), and a later call
+   * with the same pointers, length and flags replays that graph on the caller's stream:
+   * the same kernels on the same arguments, so the results equal the direct launches'
+   * bit for bit, whatever the tensors hold.  A call with other pointers records a new
+   * graph in place of the old one.  Meant for shapes whose kernels are short enough that
+   * launching them one by one dominates (small heads, many chunks).  Calls made while a
+   * measurement hook is active launch directly.                                         */
+  int32_t replay;
 } ttt_config;
 
 /* Host-only check of a configuration (no HIP call).  TTT_OK or the first problem found. */

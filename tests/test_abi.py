@@ -73,7 +73,15 @@ def test_step_size_and_decay_checked(kw, ok):
 def test_step_size_fields_reach_the_struct():
     c = _cfg(lr=(0.25, 0.5), weight_decay=0.125)
     assert list(c.lr) == [0.25, 0.5, 0.0] and c.weight_decay == 0.125
-    assert ctypes.sizeof(W.ttt_config) == 16 * 4 + 4 * 4
+    assert ctypes.sizeof(W.ttt_config) == 16 * 4 + 4 * 4 + 4
+
+
+def test_replay_flag_checked():
+    c = _cfg()
+    for val, code in ((0, 0), (1, 0), (2, 4), (-1, 4)):
+        c.replay = val
+        assert _status(c) == code, val
+    assert W.make_config(None, replay=True, **_base()).replay == 1
 
 
 def test_plane_counts_checked():

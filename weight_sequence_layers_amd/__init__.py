@@ -47,7 +47,7 @@ class ttt_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order", "ns_steps",
         "row_renorm", "apply_planes", "grad_planes", "ns_planes", "ns_one_plane", "path")
-    ] + [("lr", ctypes.c_float * 3), ("weight_decay", ctypes.c_float)]
+    ] + [("lr", ctypes.c_float * 3), ("weight_decay", ctypes.c_float), ("replay", ctypes.c_int32)]
 
 
 _lib = None
@@ -103,7 +103,8 @@ def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
     fw, loss, act, order, ns_steps, renorm and optionally lr, weight_decay), overridden by
     keyword arguments. `planes` is (apply, grad, ns, ns_one_plane); by default the preset of
     the workload's name, else 0s. `path` is "auto", "staged" or "resident". `lr` is a
-    sequence of up to 3 step sizes in the state's matrix order (0 or missing: 1)."""
+    sequence of up to 3 step sizes in the state's matrix order (0 or missing: 1). `replay`
+    records each call's launches in a HIP graph and replays it for repeated pointers."""
     f = {}
     if cfg is not None:
         for k in ("batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order",
@@ -134,6 +135,7 @@ def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
     for i, x in enumerate(lr):
         c.lr[i] = float(x)
     c.weight_decay = float(f.get("weight_decay", 0.0))
+    c.replay = int(bool(f.get("replay", False)))
     return c
 
 

@@ -108,6 +108,8 @@ ttt_status resolve(const ttt_config* c, ttt_config* out) {
                 "no Newton-Schulz, no renorm, bf16 activations, apply-then-update and one "
                 "bf16 plane");
   if (r.path == TTT_PATH_AUTO) r.path = resident_ok ? TTT_PATH_RESIDENT : TTT_PATH_STAGED;
+  if (r.replay != 0 && r.replay != 1)
+    return fail(TTT_E_CONFIG, "replay must be 0 or 1 (got %d)", r.replay);
   if (out) *out = r;
   return TTT_OK;
 }
@@ -194,6 +196,18 @@ struct ttt_state {
   // measurement hooks
   int prof_stage = -1, prof_cap = 0, prof_n = 0;
   hipEvent_t* prof_ev = nullptr;
+  // replay: the last recorded forward call's graph and what it was recorded for
+  hipStream_t cap = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  struct GraphKey {
+    const void *q, *k, *v, *eta, *out;
+    int64_t T;
+    uint64_t flags;   // hash of the update flags (0: none)
+    bool operator==(const GraphKey& o) const {
+      return q == o.q && k == o.k && v == o.v && eta == o.eta && out == o.out && T == o.T &&
+             flags == o.flags;
+    }
+  } gkey{};
 };
 
 namespace {
@@ -1023,18 +1037,12 @@ ttt_status resident_run(ttt_state* s, const void* q, const void* k, const void* 
   return TTT_OK;
 }
 
-// update: NULL (every chunk updates) or one flag per chunk of the call (host memory).
-ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, const float* eta,
-                   void* out, int64_t T, int64_t nchunks, void* stream,
-                   const uint8_t* update = nullptr) {
-  if (!s) return fail(TTT_E_NULL, "state is NULL");
-  if (T == 0) return TTT_OK;
+// The chunk loop's launches on st.  update: NULL (every chunk updates) or one flag per
+// chunk of the call (host memory).
+ttt_status forward_body(ttt_state* s, const void* q, const void* k, const void* v,
+                        const float* eta, void* out, int64_t T, int64_t nchunks,
+                        hipStream_t st, const uint8_t* update) {
   ttt_status r;
-  if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v")) ||
-      (r = check_ptr(eta, "eta")) || (r = check_ptr(out, "out")))
-    return r;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  s->last = st;
   Rows R{};
   R.q = static_cast<const char*>(q);
   R.k = static_cast<const char*>(k);
@@ -1069,6 +1077,50 @@ ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, co
   return TTT_OK;
 }
 
+ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, const float* eta,
+                   void* out, int64_t T, int64_t nchunks, void* stream,
+                   const uint8_t* update = nullptr) {
+  if (!s) return fail(TTT_E_NULL, "state is NULL");
+  if (T == 0) return TTT_OK;
+  ttt_status r;
+  if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v")) ||
+      (r = check_ptr(eta, "eta")) || (r = check_ptr(out, "out")))
+    return r;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s->last = st;
+  if (!s->cfg.replay || s->prof_ev)
+    return forward_body(s, q, k, v, eta, out, T, nchunks, st, update);
+  ttt_state::GraphKey key{q, k, v, eta, out, T, 0};
+  if (update) {
+    uint64_t h = 1469598103934665603ull;   // FNV-1a over the flags
+    for (int64_t i = 0; i < nchunks; ++i) h = (h ^ (update[i] ? 1u : 0u)) * 1099511628211ull;
+    key.flags = h | 1;
+  }
+  if (s->gexec && key == s->gkey) {
+    HIP_TRY(hipGraphLaunch(s->gexec, st));
+    return TTT_OK;
+  }
+  if (!s->cap) HIP_TRY(hipStreamCreateWithFlags(&s->cap, hipStreamNonBlocking));
+  HIP_TRY(hipStreamBeginCapture(s->cap, hipStreamCaptureModeThreadLocal));
+  r = forward_body(s, q, k, v, eta, out, T, nchunks, s->cap, update);
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(s->cap, &g);
+  if (r != TTT_OK) {
+    if (g) hipGraphDestroy(g);
+    return r;
+  }
+  if (e != hipSuccess) return fail(TTT_E_HIP, "graph capture failed: %s", hipGetErrorString(e));
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(TTT_E_HIP, "graph instantiation failed: %s", hipGetErrorString(e));
+  if (s->gexec) hipGraphExecDestroy(s->gexec);
+  s->gexec = ex;
+  s->gkey = key;
+  HIP_TRY(hipGraphLaunch(ex, st));
+  return TTT_OK;
+}
+
 }  // namespace
 
 // ============================================================================ workspace-only runs
@@ -1095,6 +1147,7 @@ ttt_status sequence_in_workspace(const ttt_config* cfg, float* w, const void* q,
                       (st = check_ptr(out, "out"))))
     return st;
   ttt_state s;
+  r.replay = 0;   // a graph would outlive this call's stack state
   s.cfg = r;
   s.D = dims_of(r);
   s.resident = r.path == TTT_PATH_RESIDENT;
@@ -1298,6 +1351,8 @@ ttt_status ttt_destroy_state(ttt_state* s) {
     for (int i = 0; i < 2 * s->prof_cap; ++i) hipEventDestroy(s->prof_ev[i]);
     delete[] s->prof_ev;
   }
+  if (s->gexec) hipGraphExecDestroy(s->gexec);
+  if (s->cap) hipStreamDestroy(s->cap);
   hipError_t e2 = hipFree(s->arena);
   if (e2 == hipSuccess && s->bw.arena) e2 = hipFree(s->bw.arena);
   delete s;
