@@ -241,6 +241,14 @@ def update_state(Ws, grads, ns_steps: int, renorm: bool, lr: Optional[Sequence[f
     return out
 
 
+def momentum_step(Ms, grads, beta: float):
+    """Heavy-ball accumulation of the chunk gradients, M <- beta M + g per matrix: the
+    ordinary momentum optimiser that [LaCT] §2.2.1 compares its Muon variant with; under
+    Muon the orthogonalisation is applied to M, as the published Muon optimiser does with
+    its momentum buffer."""
+    return [beta * np.asarray(M, np.float64) + g for M, g in zip(Ms, grads)]
+
+
 # ------------------------------------------------------------------------- the layer loop
 def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
                      apply_rows: Optional[np.ndarray] = None, n_chunks: Optional[int] = None,
@@ -259,10 +267,15 @@ def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
     does for the clean-frame chunks of an autoregressive video sequence.
     apply_rows: optional sorted token indices; only those rows of O are computed
     (the others stay 0). n_chunks: stop after that many chunks.
+    With cfg.momentum = beta > 0 the chunk gradients pass through momentum_step (the
+    buffers start at zero) and the returned matrices are the fast weights followed by the
+    momentum buffers.
     Returns (O [T, d] fp64, list of final fp64 matrices)."""
     T = len(eta)
     b = cfg.chunk
     Ws = [np.asarray(w, np.float64) for w in W0s]
+    beta = float(getattr(cfg, "momentum", 0.0))
+    Ms = [np.zeros_like(w) for w in Ws] if beta else None
     O = np.zeros((T, cfg.dim), np.float64)
     nc = T // b if n_chunks is None else n_chunks
     rows = None if apply_rows is None else np.asarray(apply_rows)
@@ -285,10 +298,13 @@ def sequence_forward(cfg, W0s, Q, K, V, eta, block_rows: Optional[int] = 8192,
         if cfg.order == APPLY_THEN_UPDATE:
             apply(lo, hi)
         g = chunk_gradient(cfg.fw, cfg.loss, Ws, K[lo:hi], V[lo:hi], eta[lo:hi], block_rows)
+        if Ms is not None:
+            Ms = momentum_step(Ms, g, beta)
+            g = Ms
         Ws = update_state(Ws, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
         if cfg.order == UPDATE_THEN_APPLY:
             apply(lo, hi)
-    return O, Ws
+    return O, (Ws + Ms if Ms is not None else Ws)
 
 
 def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta, update_chunks=None):
@@ -299,6 +315,8 @@ def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta, update_chunks=None):
     b = cfg.chunk
     Ws = [np.array(w, np.float64) for w in W0s]
     O = np.zeros((T, cfg.dim))
+    beta = float(getattr(cfg, "momentum", 0.0))
+    Ms = [np.zeros_like(w) for w in Ws]
 
     def f(x):
         if cfg.fw == "swiglu":
@@ -339,12 +357,17 @@ def sequence_forward_bruteforce(cfg, W0s, Q, K, V, eta, update_chunks=None):
                 grads[0] += np.outer((W2.T @ e) * gelu_prime(z), k)
             else:
                 grads[0] += np.outer(e, k)
+        if beta:
+            for i in range(len(Ms)):          # the momentum buffer, entry by entry
+                for idx in np.ndindex(Ms[i].shape):
+                    Ms[i][idx] = beta * Ms[i][idx] + grads[i][idx]
+            grads = [M.copy() for M in Ms]
         Ws = update_state(Ws, grads, cfg.ns_steps, cfg.renorm, cfg.step_sizes(),
                           cfg.weight_decay)
         if cfg.order == UPDATE_THEN_APPLY:
             for t in range(c * b, (c + 1) * b):
                 O[t] = f(np.asarray(Q[t], np.float64))
-    return O, Ws
+    return O, (Ws + Ms if beta else Ws)
 
 
 def forward_all(cfg, inputs, problems: Optional[Sequence[Tuple[int, int]]] = None,
@@ -544,6 +567,8 @@ def chunk_vjp(cfg, Ws, Q, K, V, eta, dO, dWs_new, update: bool = True):
     (with the state the queries saw: before the update under the shifted order, after it
     under the update-then-apply order), the update's from update_state_vjp and
     gradient_vjp. Returns (dQ, dK, dV, deta, [dW before the chunk])."""
+    if getattr(cfg, "momentum", 0.0):
+        raise ValueError("the chunk backward takes configurations without momentum")
     Ws = [np.asarray(w, np.float64) for w in Ws]
     dWs_new = [np.asarray(x, np.float64) for x in dWs_new]
     n = len(eta)

@@ -571,6 +571,79 @@ def test_a_chunk_without_update_equals_eta_zero(ns, renorm):
     assert np.array_equal(O3, O4) and all(np.array_equal(a, b) for a, b in zip(W3, W4))
 
 
+# ------------------------------------------------------------------ momentum over chunks
+def momentum_linear_closed_form_error(order="apply_then_update", beta=0.6, lr=0.7, wd=0.1,
+                                      chunk=3, T=12, d=4, seed=16):
+    """Linear fast weight, inner-product loss, no Muon, no norm, heavy-ball momentum: the
+    buffer is M_c = beta M_{c-1} + g_c with g_c = -sum_t eta_t v_t k_t^T over chunk c's
+    tokens (summed token by token here), and W_c = (1 - wd) W_{c-1} - lr M_c; the returned
+    state is W followed by M."""
+    cfg = _cfg("linear", "dot", 0, False, order, chunk=chunk, d=d, T=T, lr=(lr,), wd=wd)
+    cfg = cfg.replace(momentum=beta)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(seed))
+    O, out = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    W, M = Ws[0].copy(), np.zeros_like(Ws[0])
+    err = 0.0
+    for c in range(T // chunk):
+        S = slice(c * chunk, (c + 1) * chunk)
+        g = np.zeros_like(W)
+        for t in range(c * chunk, (c + 1) * chunk):
+            g -= eta[t] * np.outer(V[t], K[t])
+        M = beta * M + g
+        Wn = (1.0 - wd) * W - lr * M
+        ref = Q[S] @ (W if order == "apply_then_update" else Wn).T
+        err = max(err, np.abs(O[S] - ref).max())
+        W = Wn
+    err = max(err, np.abs(out[0] - W).max())
+    if not beta:                       # no momentum: the state is the fast weights alone
+        return err if len(out) == 1 else np.inf
+    return max(err, np.abs(out[1] - M).max())
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+@pytest.mark.parametrize("beta", [0.0, 0.5, 0.9])
+def test_momentum_linear_closed_form(order, beta):
+    assert momentum_linear_closed_form_error(order, beta) <= 1e-12
+
+
+@pytest.mark.parametrize("fw,loss,ns,renorm", [("swiglu", "dot", 5, True),
+                                               ("gelu", "mse", 0, False),
+                                               ("swiglu", "mse", 5, False)])
+def test_momentum_matches_the_bruteforce(fw, loss, ns, renorm):
+    cfg = _cfg(fw, loss, ns, renorm, chunk=3, d=4, dh=6, T=12).replace(momentum=0.7)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(17))
+    O1, W1 = orc.sequence_forward(cfg, Ws, Q, K, V, eta)
+    O2, W2 = orc.sequence_forward_bruteforce(cfg, Ws, Q, K, V, eta)
+    assert len(W1) == 2 * len(Ws) == len(W2)
+    assert np.abs(O1 - O2).max() <= 1e-12 * max(1, np.abs(O2).max())
+    for a, b in zip(W1, W2):
+        assert np.abs(a - b).max() <= 1e-12 * max(1, np.abs(b).max())
+
+
+def muon_momentum_band(beta=0.8, lr=(0.3, 0.5, 2.0), seed=25):
+    """Muon on the momentum buffer, no norm: each chunk's step (W_prev - W) / lr_i is
+    NS5 of the buffer, whose singular values lie in the Newton-Schulz band. Returns the
+    extreme singular values over chunks and matrices."""
+    cfg = _cfg("swiglu", "dot", 5, False, chunk=8, T=24, d=6, dh=12, lr=lr).replace(
+        momentum=beta)
+    Ws, Q, K, V, eta = _rand_problem(cfg, np.random.default_rng(seed))
+    lo, hi = np.inf, 0.0
+    prev = Ws
+    for c in range(3):
+        _, out = orc.sequence_forward(cfg, Ws, Q, K, V, eta, n_chunks=c + 1)
+        cur = out[:3]
+        for a, b, step in zip(cur, prev, lr):
+            S = np.linalg.svd((b - a) / step, compute_uv=False)
+            lo, hi = min(lo, S.min()), max(hi, S.max())
+        prev = cur
+    return lo, hi
+
+
+def test_muon_orthogonalises_the_momentum_buffer():
+    lo, hi = muon_momentum_band()
+    assert lo > 0.68 and hi < 1.21
+
+
 # ------------------------------------------------------------------ mutation tests
 def _all_pins_pass():
     try:
@@ -602,6 +675,9 @@ def _all_pins_pass_inner():
     for order in ("apply_then_update", "update_then_apply"):
         checks.append(masked_linear_closed_form_error(order, (0, 1, 0, 1)) <= 1e-12)
         checks.append(masked_linear_closed_form_error(order, (1, 0, 0, 1)) <= 1e-12)
+        checks.append(momentum_linear_closed_form_error(order) <= 1e-12)
+    lo, hi = muon_momentum_band()
+    checks.append(lo > 0.68 and hi < 1.21)
     return all(checks)
 
 
@@ -724,6 +800,10 @@ def _mut_forward_all_qk(cfg, inputs, problems=None, block_rows=8192):
     return out
 
 
+def _mut_momentum_on_g(Ms, grads, beta):      # beta scales the new gradient, not the buffer
+    return [np.asarray(M, np.float64) + beta * g for M, g in zip(Ms, grads)]
+
+
 @pytest.mark.parametrize("name,target,mut", [
     ("silu' term", "silu_prime", _mut_silu_prime),
     ("error sign", "_output_error", _mut_output_error),
@@ -738,6 +818,7 @@ def _mut_forward_all_qk(cfg, inputs, problems=None, block_rows=8192):
     ("forward_all keys as queries", "forward_all", _mut_forward_all_qk),
     ("update flags ignored", "sequence_forward", _mut_mask_ignored),
     ("update flags shifted", "sequence_forward", _mut_mask_shifted),
+    ("momentum on the gradient", "momentum_step", _mut_momentum_on_g),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, target, mut):
     monkeypatch.setattr(orc, target, mut)

@@ -49,6 +49,7 @@ class Config:
     seed: int = 1000
     lr: Tuple[float, ...] = ()   # step size per matrix (state order); () or 0 entries: 1
     weight_decay: float = 0.0    # decay of the state per chunk, in [0, 1)
+    momentum: float = 0.0        # heavy-ball coefficient over chunk gradients, in [0, 1)
 
     def step_sizes(self) -> List[float]:
         """The step size of each matrix, defaults filled in."""
