@@ -128,6 +128,15 @@ typedef struct {
    * launching them one by one dominates (small heads, many chunks).  Calls made while a
    * measurement hook is active launch directly.                                         */
   int32_t replay;
+  /* Momentum (the LaCT page, §2.2.1, compares its Muon variant with an ordinary momentum
+   * optimiser).  0 (the default) or beta in (0, 1): every matrix keeps a buffer
+   * M <- beta M + g of the chunk gradients, starting at 0, and the step takes U = NS(M)
+   * under Newton-Schulz, else M.  The buffers are part of the state: with beta > 0,
+   * ttt_state_numel counts them, and ttt_get_state / ttt_set_state (and the state of the
+   * allocation-free call) hold every fast-weight matrix followed by every buffer, in the
+   * same matrix order and layout.  The resident path and the chunk backward take no
+   * momentum.  A chunk without update leaves its buffer as it is.                       */
+  float momentum;
 } ttt_config;
 
 /* Host-only check of a configuration (no HIP call).  TTT_OK or the first problem found. */

@@ -73,7 +73,19 @@ def test_step_size_and_decay_checked(kw, ok):
 def test_step_size_fields_reach_the_struct():
     c = _cfg(lr=(0.25, 0.5), weight_decay=0.125)
     assert list(c.lr) == [0.25, 0.5, 0.0] and c.weight_decay == 0.125
-    assert ctypes.sizeof(W.ttt_config) == 16 * 4 + 4 * 4 + 4
+    assert ctypes.sizeof(W.ttt_config) == 16 * 4 + 4 * 4 + 4 + 4
+
+
+def test_momentum_checked_and_counted_in_the_state():
+    for beta, code in ((0.0, 0), (0.5, 0), (0.999, 0), (1.0, 4), (-0.1, 4),
+                       (float("nan"), 4)):
+        assert _status(_cfg(momentum=beta)) == code, beta
+    assert W.ttt_state_numel(_cfg(momentum=0.9)) == 2 * W.ttt_state_numel(_cfg())
+    small = dict(fw="gelu", loss="mse", ns_steps=0, renorm=False, dim=64, hidden=256, chunk=64)
+    assert _status(W.make_config(None, planes=(1, 1, 1, 0), path="resident", momentum=0.5,
+                                 **_base(**small))) == 5
+    c = W.make_config(None, planes=(1, 1, 1, 0), momentum=0.5, **_base(**small))
+    assert _status(c) == 0
 
 
 def test_replay_flag_checked():

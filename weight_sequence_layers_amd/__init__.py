@@ -47,7 +47,8 @@ class ttt_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order", "ns_steps",
         "row_renorm", "apply_planes", "grad_planes", "ns_planes", "ns_one_plane", "path")
-    ] + [("lr", ctypes.c_float * 3), ("weight_decay", ctypes.c_float), ("replay", ctypes.c_int32)]
+    ] + [("lr", ctypes.c_float * 3), ("weight_decay", ctypes.c_float), ("replay", ctypes.c_int32),
+         ("momentum", ctypes.c_float)]
 
 
 _lib = None
@@ -110,7 +111,7 @@ def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
         for k in ("batch", "heads", "dim", "hidden", "chunk", "fw", "loss", "act", "order",
                   "ns_steps", "renorm"):
             f[k] = getattr(cfg, k)
-        for k in ("lr", "weight_decay"):
+        for k in ("lr", "weight_decay", "momentum"):
             if hasattr(cfg, k):
                 f[k] = getattr(cfg, k)
         if planes is None:
@@ -136,6 +137,7 @@ def make_config(cfg=None, *, planes=None, **kw) -> ttt_config:
         c.lr[i] = float(x)
     c.weight_decay = float(f.get("weight_decay", 0.0))
     c.replay = int(bool(f.get("replay", False)))
+    c.momentum = float(f.get("momentum", 0.0))
     return c
 
 
@@ -285,9 +287,11 @@ def matrix_shapes(cfg: ttt_config):
 
 
 def split_state(cfg: ttt_config, flat):
-    """Views of a flat state buffer as per-matrix [batch, heads, rows, cols] tensors."""
+    """Views of a flat state buffer as per-matrix [batch, heads, rows, cols] tensors: the
+    fast weights, then (with momentum) their buffers."""
     out, o = [], 0
-    for r, c in matrix_shapes(cfg):
+    shapes = matrix_shapes(cfg)
+    for r, c in shapes + (shapes if cfg.momentum > 0 else []):
         n = cfg.batch * cfg.heads * r * c
         out.append(flat[o:o + n].view(cfg.batch, cfg.heads, r, c))
         o += n

@@ -49,6 +49,7 @@ struct Dims {
   int ap, gp, np, wp, in_q, in_kv;
   int ns_one;               // bit i: Newton-Schulz iteration i on one bf16 plane
   int64_t sb;               // tokens per gradient / apply block
+  bool mom;                 // momentum buffers follow the weights in the state
 };
 
 ttt_status resolve(const ttt_config* c, ttt_config* out) {
@@ -98,7 +99,7 @@ ttt_status resolve(const ttt_config* c, ttt_config* out) {
   }
   if (!std::isfinite(r.weight_decay) || r.weight_decay < 0.f || r.weight_decay >= 1.f)
     return fail(TTT_E_CONFIG, "weight_decay must be in [0, 1) (got %g)", (double)r.weight_decay);
-  const bool resident_ok =
+  const bool resident_ok = r.momentum == 0.f &&
       small_supported(r.fw == TTT_FW_MLP_GELU ? FW_GELU : -1, r.ns_steps, r.row_renorm,
                       r.act == TTT_BF16, r.order == TTT_APPLY_THEN_UPDATE, r.dim, r.hidden,
                       r.chunk, r.apply_planes, r.grad_planes);
@@ -110,6 +111,10 @@ ttt_status resolve(const ttt_config* c, ttt_config* out) {
   if (r.path == TTT_PATH_AUTO) r.path = resident_ok ? TTT_PATH_RESIDENT : TTT_PATH_STAGED;
   if (r.replay != 0 && r.replay != 1)
     return fail(TTT_E_CONFIG, "replay must be 0 or 1 (got %d)", r.replay);
+  if (!std::isfinite(r.momentum) || r.momentum < 0.f || r.momentum >= 1.f)
+    return fail(TTT_E_CONFIG, "momentum must be in [0, 1) (got %g)", (double)r.momentum);
+  if (r.momentum > 0.f && r.path == TTT_PATH_RESIDENT)
+    return fail(TTT_E_UNSUPPORTED, "the resident path takes no momentum");
   if (out) *out = r;
   return TTT_OK;
 }
@@ -142,14 +147,17 @@ Dims dims_of(const ttt_config& c) {
   D.in_q = c.act == TTT_F32 ? D.ap : 1;
   D.in_kv = c.act == TTT_F32 ? D.gp : 1;
   D.sb = std::min<int64_t>(c.chunk, SUBBLOCK_MAX);
+  D.mom = c.momentum > 0.f;
   return D;
 }
 
-int64_t state_numel(const Dims& D) {
+// values of the fast-weight matrices alone, and of the whole state (with the buffers)
+int64_t weights_numel(const Dims& D) {
   int64_t n = 0;
   for (int m = 0; m < D.nm; ++m) n += (int64_t)D.P * D.rows[m] * D.cols[m];
   return n;
 }
+int64_t state_numel(const Dims& D) { return weights_numel(D) * (D.mom ? 2 : 1); }
 
 }  // namespace
 
@@ -165,6 +173,7 @@ struct ttt_state {
   float* W = nullptr;   // [state_numel] matrix by matrix, each [P][rows][cols]
   float* U = nullptr;   // same layout
   float* Wm[3] = {};    // per-matrix views
+  float* Mm[3] = {};    // momentum buffers (after the weights in W), or null
   float* Um[3] = {};
   u16* Wpl[3] = {};     // planes [wp][P][rows][cols]
   // token-major workspaces, [planes][P][sb][cols]
@@ -234,7 +243,7 @@ size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
   const bool f32 = c.act == TTT_F32;
   Carver C;
   size_t oW = ext_w ? 0 : C.take<float>(state_numel(D));
-  size_t oU = C.take<float>(state_numel(D));
+  size_t oU = C.take<float>(weights_numel(D));
   size_t oWpl[3];
   for (int m = 0; m < D.nm; ++m) oWpl[m] = C.take<u16>(D.wp * P * D.rows[m] * D.cols[m]);
   size_t oq = 0, ok = 0, ov = 0;
@@ -280,6 +289,7 @@ size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
     int64_t acc = 0;
     for (int m = 0; m < D.nm; ++m) {
       s->Wm[m] = s->W + acc;
+      s->Mm[m] = D.mom ? s->W + weights_numel(D) + acc : nullptr;
       s->Um[m] = s->U + acc;
       acc += P * D.rows[m] * D.cols[m];
       s->Wpl[m] = H(oWpl[m]);
@@ -445,6 +455,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
     cg.G = s->G + (int64_t)m0 * P * d * D.n;
     if (s->gpart) cg.gpart = s->gpart + (int64_t)m0 * P * d * D.n;
     cg.U = U + (int64_t)m0 * P * d * D.n;
+    if (ca.mom) cg.mom = ca.mom + (int64_t)m0 * P * d * D.n;
     if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
     cg.part = s->part + (int64_t)m0 * P * s->contract_tiles;
     cg.tr_mask = ca.tr_mask >> m0;
@@ -571,8 +582,13 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     if (mse) { ca.a[m] = colop(e, d); ca.b[m] = colop(hk, dh); }
     else { ca.a[m] = as_cols(xv, d); ca.b[m] = colop(pk, dh); }
   }
+  if (D.mom) {   // the chunk's gradient enters the momentum buffers in the last epilogue
+    ca.mom = s->Mm[0];
+    ca.beta = c.momentum;
+  }
   ttt_status r = contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
   if (r != TTT_OK || !g32) return r;
+  ca.mom = nullptr;
   return contract_all(s, ca, g32, false, first, last, st, false);
 }
 
@@ -754,7 +770,7 @@ ttt_status ensure_bwd(ttt_state* s) {
     for (int i = 1; i < c.ns_steps; ++i) oit[i] = C.take<u16>(D.np * xs);
   }
   size_t odg = C.take<float>(xs), odgp = C.take<u16>(D.gp * xs);
-  const int64_t sn = state_numel(D);
+  const int64_t sn = weights_numel(D);
   size_t ows = C.take<float>(sn), owg = C.take<float>(sn), owa = C.take<float>(sn);
   size_t oep = C.take<float>(P * sb * ((dh + 63) / 64));
   size_t opd = C.take<u16>(D.gp * P * sb * dh), oa1 = C.take<u16>(D.gp * P * sb * dh),
@@ -1006,7 +1022,7 @@ ttt_status chunk_backward(ttt_state* s, const void* q, const void* k, const void
   }
   // 6. dW before the chunk
   Add3Args ad{};
-  ad.x = b.dwa; ad.y = b.dws; ad.w = b.dwg; ad.out = dw; ad.n = state_numel(D);
+  ad.x = b.dwa; ad.y = b.dws; ad.w = b.dwg; ad.out = dw; ad.n = weights_numel(D);
   STAGED(TTT_STAGE_RENORM, launch_add3(ad, st));
   return TTT_OK;
 }
@@ -1284,11 +1300,11 @@ ttt_status ttt_chunk_backward(ttt_state* s, const void* q, const void* k, const 
     return r;
   const ttt_config& c = s->cfg;
   if (s->resident || c.fw != TTT_FW_SWIGLU || c.loss != TTT_LOSS_DOT ||
-      c.order != TTT_APPLY_THEN_UPDATE || c.chunk > SUBBLOCK_MAX)
+      c.order != TTT_APPLY_THEN_UPDATE || c.chunk > SUBBLOCK_MAX || c.momentum > 0.f)
     return fail(TTT_E_UNSUPPORTED,
                 "the chunk backward serves the SwiGLU net with the inner-product loss under "
                 "the shifted (apply-then-update) order, on the staged path, with chunks of "
-                "at most %lld tokens", (long long)SUBBLOCK_MAX);
+                "at most %lld tokens and no momentum", (long long)SUBBLOCK_MAX);
   hipStream_t st = static_cast<hipStream_t>(stream);
   s->last = st;
   return chunk_backward(s, q, k, v, eta, dout, dw, dq, dk, dv, deta, st);

@@ -181,6 +181,10 @@ struct ContractArgs {
   int64_t gpart_stride;
   int ksplit, kchunk;
   int nz;          // nm * P of the launch (set by launch_contract)
+  // momentum: with mom, the last epilogue replaces the sum x by beta M + x and stores it in
+  // M (weight orientation, like U) before using it
+  float* mom;
+  float beta;
 };
 
 // Newton-Schulz stages on Z = nm*P matrices X [M x N] (M <= N).

@@ -291,13 +291,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
     float x = g.acc[0][i][j][v];
     if (row < M && col < N) {
       const int64_t off = base + (int64_t)row * N + col;
+      const int64_t widx = tr ? base + (int64_t)col * M + row : off;   // weight orientation
       if (accum) x += a.G[off];
+      if (last && a.mom) {
+        x = fmaf(a.beta, a.mom[widx], x);
+        a.mom[widx] = x;
+      }
       if (!last) {
         gout[off] = x;
       } else if (a.muon) {
         ss += x * x;
       } else {
-        a.U[tr ? base + (int64_t)col * M + row : off] = x;
+        a.U[widx] = x;
       }
     }
     g.acc[0][i][j][v] = x;
@@ -344,6 +349,14 @@ __global__ __launch_bounds__(256) void k_contract_sum(ContractArgs a) {
       const float4 u = src[0], w = src[1];
       x[0] += u.x; x[1] += u.y; x[2] += u.z; x[3] += u.w;
       x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
+    }
+    if (a.last && a.mom) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t widx = tr ? base + (int64_t)(col + e) * M + row : off + e;
+        x[e] = fmaf(a.beta, a.mom[widx], x[e]);
+        a.mom[widx] = x[e];
+      }
     }
     if (!a.last) {
       float4* dst = reinterpret_cast<float4*>(a.G + off);
