@@ -28,7 +28,8 @@ extraction, so the formulas below are the plain forms the pages describe in word
 Readings where the pages are silent (each one is listed in the design notes):
 * loss of a chunk S: inner product  L = -sum_{t in S} eta_t <f_W(k_t), v_t>,  or
   MSE  L = sum_{t in S} eta_t ||f_W(k_t) - v_t||^2  (no 1/2, no 1/d, no 1/|S|);
-* one eta per token, shared by all fast-weight matrices; no momentum; the update is
+* one eta per token, shared by all fast-weight matrices; momentum off unless the config
+  sets it (heavy-ball over chunks, momentum_step); the update is
   W <- (1 - lambda) W - lr_i U with U the gradient (SGD) or its 5-step Newton-Schulz
   orthogonalisation (Muon), lr_i a step size per matrix (default 1: the step the pages
   describe) and lambda a weight decay (default 0) -- [Modular TTT] names the learning
