@@ -4,6 +4,7 @@
     python -m weight_sequence_layers_amd.profiling traffic OUT.md FETCH_DIR WRITE_DIR \
         WORKLOAD "<fetch command>" "<write command>"
     python -m weight_sequence_layers_amd.profiling mfma   OUT.md  PMC_DIR     "<command>"
+    python -m weight_sequence_layers_amd.profiling counters OUT.md TITLE DIR... -- "<cmd>"...
 
 `stats` turns a `rocprofv3 --kernel-trace --stats` directory into a table of kernel
 durations. `traffic` turns one `--pmc FETCH_SIZE` and one `--pmc WRITE_SIZE` run of
@@ -151,11 +152,62 @@ def mfma_md(pmc_dir: str, command: str, cus: int = 256, simds_per_cu: int = 4,
     return "\n".join(out) + "\n"
 
 
+def counters_md(pmc_dirs, command_lines, title: str) -> str:
+    """Per-kernel averages (per dispatch, each counter summed over its instances) of every
+    counter in one or more `rocprofv3 --pmc` directories, plus derived ratios when their
+    counters are present: L2 hit rate, average latency of the L2's memory reads in cycles
+    (outstanding-request level over requests), share of requests that went to DRAM, and the
+    share of wave cycles spent waiting."""
+    vals = defaultdict(dict)
+    disp = defaultdict(int)
+    for d in pmc_dirs:
+        per = defaultdict(lambda: defaultdict(float))
+        ids = defaultdict(set)
+        for r in csv.DictReader(open(_one("*counter_collection.csv", d))):
+            k = _short(r["Kernel_Name"])
+            per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            ids[k].add(r["Dispatch_Id"])
+        for k, cs in per.items():
+            n = len(ids[k])
+            disp[k] = max(disp[k], n)
+            for c, v in cs.items():
+                vals[k][c] = v / n
+    names = sorted({c for v in vals.values() for c in v})
+    out = [f"# {title}", "", "Commands (repository root, one MI355X), one counter set per run:",
+           ""] + [f"    {c}" for c in command_lines] + [
+           "", f"source digest: {source_digest()}", "",
+           "Per dispatch, each counter summed over its instances and averaged over the "
+           "kernel's dispatches. Derived: L2 hit % = TCC_HIT / (TCC_HIT + TCC_MISS); "
+           "read latency (cycles) = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ; DRAM % = "
+           "TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ; wait % = SQ_WAIT_ANY / SQ_WAVE_CYCLES.", ""]
+    derived = ["L2 hit %", "read latency", "DRAM %", "wait %"]
+    out.append("| kernel | dispatches | " + " | ".join(derived + names) + " |")
+    out.append("|---|---|" + "---|" * (len(derived) + len(names)))
+    for k in sorted(vals, key=lambda k: -vals[k].get("SQ_WAVE_CYCLES", vals[k].get(
+            "TCC_EA0_RDREQ_sum", 0))):
+        v = vals[k]
+        g = lambda *cs: [v.get(c, v.get(c + "_sum")) for c in cs]
+        hit, miss = g("TCC_HIT", "TCC_MISS")
+        lvl, req, dram = g("TCC_EA0_RDREQ_LEVEL", "TCC_EA0_RDREQ", "TCC_EA0_RDREQ_DRAM")
+        wa, wc = g("SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+        d = [f"{100 * hit / (hit + miss):.1f}" if hit is not None and miss is not None and hit + miss else "",
+             f"{lvl / req:.0f}" if lvl is not None and req else "",
+             f"{100 * dram / req:.1f}" if dram is not None and req else "",
+             f"{100 * wa / wc:.1f}" if wa is not None and wc else ""]
+        out.append(f"| `{k}` | {disp[k]} | " + " | ".join(d) + " | " +
+                   " | ".join(f"{v[c]:.4g}" if c in v else "" for c in names) + " |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if len(argv) >= 4 and argv[1] == "stats":
         text = stats_md(argv[3], argv[4] if len(argv) > 4 else "")
     elif len(argv) >= 4 and argv[1] == "mfma":
         text = mfma_md(argv[3], argv[4] if len(argv) > 4 else "")
+    elif len(argv) >= 5 and argv[1] == "counters":
+        # counters OUT.md TITLE DIR1 [DIR2 ...] -- CMD1 [CMD2 ...]
+        sep = argv.index("--") if "--" in argv else len(argv)
+        text = counters_md(argv[4:sep], argv[sep + 1:], argv[3])
     elif len(argv) >= 8 and argv[1] == "traffic":
         text = traffic_md(argv[3], argv[4], argv[5], argv[6], argv[7])
     else:
