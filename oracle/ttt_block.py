@@ -113,13 +113,15 @@ def ttt_inputs(X, w_qkv, w_eta, heads: int, dim: int):
 def ttt_layer(X, w_qkv, w_eta, w_out, tcfg, W0s_per_head):
     """The TTT sub-layer on rows of X [T, D]: ttt_inputs, the oracle's sequence_forward per
     head ([LaCT] §2.1 large-chunk TTT layer), output projection. Returns (the layer's bf16
-    outputs [T, H d], the projected output)."""
+    outputs [T, H d], the projected output, each head's state at the end)."""
     H, d = tcfg.heads, tcfg.dim
     O = np.zeros((len(X), H * d))
+    states = []
     for h, (q, k, v, e) in enumerate(ttt_inputs(X, w_qkv, w_eta, H, d)):
-        Oh, _ = orc.sequence_forward(tcfg, W0s_per_head[h], q, k, v, e)
+        Oh, Wh = orc.sequence_forward(tcfg, W0s_per_head[h], q, k, v, e)
         O[:, h * d:(h + 1) * d] = bf16(Oh)
-    return O, O @ np.asarray(w_out, np.float64).T
+        states.append(Wh)
+    return O, O @ np.asarray(w_out, np.float64).T, states
 
 
 def ffn_layer(X, w_up, w_down):
@@ -127,13 +129,15 @@ def ffn_layer(X, w_up, w_down):
     return bf16(gelu(X @ np.asarray(w_up, np.float64).T)) @ np.asarray(w_down, np.float64).T
 
 
-def block_forward(bcfg, weights, X, W0s_per_head):
-    """One block for one sequence X [T, D] (bf16 values): returns y [T, D] (bf16 values)."""
+def block_forward(bcfg, weights, X, W0s_per_head, return_states: bool = False):
+    """One block for one sequence X [T, D] (bf16 values): returns y [T, D] (bf16 values),
+    and with return_states also the TTT heads' states at the sequence's end."""
     X = np.asarray(X, np.float64)
     _, a = attention_layer(bf16(rmsnorm(X)), weights["attn_qkv"], weights["attn_out"],
                            bcfg.window, bcfg.window_mode)
     h = bf16(X + a)
-    _, t = ttt_layer(bf16(rmsnorm(h)), weights["ttt_qkv"], weights["ttt_eta"],
-                     weights["ttt_out"], bcfg.ttt, W0s_per_head)
+    _, t, states = ttt_layer(bf16(rmsnorm(h)), weights["ttt_qkv"], weights["ttt_eta"],
+                             weights["ttt_out"], bcfg.ttt, W0s_per_head)
     h = bf16(h + t)
-    return bf16(h + ffn_layer(bf16(rmsnorm(h)), weights["ffn_up"], weights["ffn_down"]))
+    y = bf16(h + ffn_layer(bf16(rmsnorm(h)), weights["ffn_up"], weights["ffn_down"]))
+    return (y, states) if return_states else y

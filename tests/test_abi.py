@@ -10,18 +10,21 @@ import weight_sequence_layers_amd as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "libttt.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
-def _declared():
-    src = open(HEADER).read()
+def _declared(path=HEADER):
+    src = open(path).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(ttt_[a-z_0-9]+)\s*\(", src)))
 
 
-def test_library_exports_every_declared_function():
+@pytest.mark.parametrize("header", HEADERS, ids=os.path.basename)
+def test_library_exports_every_declared_function(header):
     L = W.lib()
-    names = _declared()
-    assert "ttt_init_state" in names and "ttt_sequence_forward" in names
+    names = _declared(header)
+    assert names
     for n in names:
         assert hasattr(L, n), n
 
@@ -198,3 +201,57 @@ def test_noalloc_call_rejects_on_the_host():
 def test_noalloc_limit_matches_the_header():
     m = re.search(r"#define\s+TTT_NOALLOC_SCRATCH_BYTES\s+(\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == W.NOALLOC_SCRATCH_BYTES
+
+
+def test_block_struct_layout():
+    """ttt_block_config: six int32 fields, the int64 max_seq_len, then the layer's config."""
+    assert ctypes.sizeof(W.ttt_block_config) == 6 * 4 + 8 + ctypes.sizeof(W.ttt_config)
+    assert W.ttt_block_config.ttt.offset == 32
+    assert ctypes.sizeof(W.ttt_block_weights) == 7 * ctypes.sizeof(ctypes.c_void_p)
+
+
+def test_block_calls_reject_on_the_host():
+    """Every block call checks its arguments before any HIP call."""
+    L = W.lib()
+    p = 0x10000
+    # window attention: heads of 128 need ld >= heads * 128; unknown mode; window 0
+    assert L.ttt_window_attention(p, p, p, 128, p, 128, 1, 2, 64, 8, 0, None) == 2
+    assert L.ttt_window_attention(p, p, p, 384, p, 128, 1, 1, 64, 8, 2, None) == 4
+    assert L.ttt_window_attention(p, p, p, 384, p, 128, 1, 1, 64, 0, 0, None) == 2
+    assert L.ttt_window_attention(p, p, p, 388, p, 128, 1, 1, 64, 8, 0, None) == 2
+    assert L.ttt_window_attention(None, p, p, 384, p, 128, 1, 1, 64, 8, 0, None) == 1
+    assert L.ttt_window_attention(p + 2, p, p, 384, p, 128, 1, 1, 64, 8, 0, None) == 9
+    assert L.ttt_window_attention(None, None, None, 384, None, 128, 1, 1, 0, 8, 0, None) == 0
+    # projections: feature counts multiples of 8; epilogue; residual pointer; overlap
+    assert L.ttt_linear(p, p, None, p, 4, 12, 8, 0, None) == 2
+    assert L.ttt_linear(p, p, None, p, 4, 8, 12, 0, None) == 2
+    assert L.ttt_linear(p, p, None, p, 4, 8, 8, 3, None) == 4
+    assert L.ttt_linear(p, p, None, p + 4096, 4, 8, 8, 1, None) == 1
+    assert L.ttt_linear(p, p + 4096, None, p, 4, 8, 8, 0, None) == 4
+    assert L.ttt_linear(None, None, None, None, 0, 8, 8, 0, None) == 0
+    # block configs
+    t = _cfg(batch=2, heads=2, dim=128, hidden=256, chunk=64)
+    w = W.ttt_block_weights(*([p] * 7))
+    h = ctypes.c_void_p()
+
+    def init(**kw):
+        c = W.make_block_config(t, **{**dict(dim=256, window=64, max_seq_len=256), **kw})
+        return L.ttt_block_init(ctypes.byref(c), ctypes.byref(w), p, None, ctypes.byref(h))
+    assert init(dim=192) == 2                  # not a multiple of 128
+    assert init(dim=384) == 2                  # ttt.heads * ttt.dim differs
+    assert init(window=0) == 2
+    assert init(mode=5) == 4
+    assert init(ffn_hidden=12) == 2
+    c = W.make_block_config(t, dim=256, window=64, max_seq_len=256)
+    c.reserved = 1
+    assert L.ttt_block_init(ctypes.byref(c), ctypes.byref(w), p, None, ctypes.byref(h)) == 4
+    c32 = W.make_block_config(_cfg(batch=2, heads=2, dim=128, hidden=256, chunk=64, act="f32"),
+                              dim=256, window=64, max_seq_len=256)
+    assert L.ttt_block_init(ctypes.byref(c32), ctypes.byref(w), p, None, ctypes.byref(h)) == 3
+    wb = W.ttt_block_weights(*([p] * 6 + [None]))
+    c = W.make_block_config(t, dim=256, window=64, max_seq_len=256)
+    assert L.ttt_block_init(ctypes.byref(c), ctypes.byref(wb), p, None, ctypes.byref(h)) == 1
+    assert h.value is None
+    assert L.ttt_block_forward(None, p, p, 64, None) == 1
+    assert L.ttt_block_destroy(None) == 0
+    assert L.ttt_block_ttt_state(None) is None

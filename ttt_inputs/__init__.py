@@ -17,6 +17,10 @@ Distributions (the workloads' stated inputs):
     the activation dtype with round-to-nearest-even;
   * v ~ N(0, 1), stored in the activation dtype;
   * eta_t = 0.01 * sigmoid(N(0, 1)), fp32.
+For the block around the layer (make_block_inputs):
+  * the block input x ~ N(0, 1) per token and channel, bf16;
+  * every projection weight [out][in] ~ N(0, 1 / in), bf16 (the usual fan-in scaling, so
+    each projection keeps the scale of its input).
 """
 from __future__ import annotations
 
@@ -28,7 +32,9 @@ import numpy as np
 TOKEN_BLOCK = 65536
 
 # tensor ids used as the first spawn-key element
-_TID = {"W1": 0, "W3": 1, "W2": 2, "q": 3, "k": 4, "v": 5, "eta": 6, "W": 7}
+_TID = {"W1": 0, "W3": 1, "W2": 2, "q": 3, "k": 4, "v": 5, "eta": 6, "W": 7,
+        "x": 8, "attn_qkv": 9, "attn_out": 10, "ttt_qkv": 11, "ttt_eta": 12, "ttt_out": 13,
+        "ffn_up": 14, "ffn_down": 15}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -185,3 +191,33 @@ def make_inputs(cfg: Config, seed: Optional[int] = None) -> Dict[str, np.ndarray
             for key, val in p.items():
                 res[key][b, h] = val
     return res
+
+
+BLOCK_WEIGHT_NAMES = ("attn_qkv", "attn_out", "ttt_qkv", "ttt_eta", "ttt_out", "ffn_up",
+                      "ffn_down")
+
+
+def block_weight_shapes(dim: int, ffn_hidden: int, ttt_heads: int) -> Dict[str, tuple]:
+    D, F = dim, ffn_hidden
+    return {"attn_qkv": (3 * D, D), "attn_out": (D, D), "ttt_qkv": (3 * D, D),
+            "ttt_eta": (ttt_heads, D), "ttt_out": (D, D), "ffn_up": (F, D), "ffn_down": (D, F)}
+
+
+def make_block_inputs(batch: int, seq_len: int, dim: int, ffn_hidden: int, ttt_heads: int,
+                      seed: int) -> Dict[str, np.ndarray]:
+    """The block's input x [batch, seq_len, dim] and its projection weights, as float32
+    arrays of bf16 values (plus '<name>_bits' uint16). x is drawn per (batch, token block),
+    so any batch element or token block regenerates on its own."""
+    out: Dict[str, np.ndarray] = {}
+    for name, (o, i) in block_weight_shapes(dim, ffn_hidden, ttt_heads).items():
+        w = _rng(seed, _TID[name]).standard_normal((o, i), dtype=np.float32) / np.float32(np.sqrt(i))
+        out[name], out[name + "_bits"] = bf16_round(w)
+    x = np.empty((batch, seq_len, dim), np.float32)
+    for b in range(batch):
+        for blk in range((seq_len + TOKEN_BLOCK - 1) // TOKEN_BLOCK):
+            lo = blk * TOKEN_BLOCK
+            n = min(TOKEN_BLOCK, seq_len - lo)
+            x[b, lo:lo + n] = _rng(seed, _TID["x"], b, blk).standard_normal((n, dim),
+                                                                            dtype=np.float32)
+    out["x"], out["x_bits"] = bf16_round(x)
+    return out

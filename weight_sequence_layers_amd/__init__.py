@@ -51,6 +51,23 @@ class ttt_config(ctypes.Structure):
          ("momentum", ctypes.c_float)]
 
 
+class ttt_block_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "dim", "window", "window_mode", "ffn_hidden", "reserved")
+    ] + [("max_seq_len", ctypes.c_int64), ("ttt", ttt_config)]
+
+
+BLOCK_WEIGHTS = ("attn_qkv", "attn_out", "ttt_qkv", "ttt_eta", "ttt_out", "ffn_up", "ffn_down")
+
+
+class ttt_block_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BLOCK_WEIGHTS]
+
+
+WINDOW = {"sliding": 0, "block": 1}
+LINEAR_EPI = {"plain": 0, "residual": 1, "gelu": 2}
+ATTN_HEAD_DIM = 128
+
 _lib = None
 
 
@@ -62,6 +79,7 @@ def lib() -> ctypes.CDLL:
             raise ImportError(f"{LIB_PATH} is missing: run weight_sequence_layers_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         cfgp, vp, i64 = ctypes.POINTER(ttt_config), ctypes.c_void_p, ctypes.c_int64
+        i32 = ctypes.c_int32
         sig = {
             "ttt_validate_config": [cfgp],
             "ttt_state_numel": [cfgp, ctypes.POINTER(i64)],
@@ -78,11 +96,19 @@ def lib() -> ctypes.CDLL:
             "ttt_sequence_forward_noalloc": [cfgp, vp, vp, vp, vp, vp, vp, i64, vp],
             "ttt_profile_begin": [vp, ctypes.c_int32, ctypes.c_int32],
             "ttt_profile_end": [vp, ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)],
+            "ttt_window_attention": [vp, vp, vp, i64, vp, i64, i32, i32, i64, i32, i32, vp],
+            "ttt_linear": [vp, vp, vp, vp, i64, i32, i32, i32, vp],
+            "ttt_block_init": [ctypes.POINTER(ttt_block_config),
+                               ctypes.POINTER(ttt_block_weights), vp, vp, ctypes.POINTER(vp)],
+            "ttt_block_forward": [vp, vp, vp, i64, vp],
+            "ttt_block_destroy": [vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        L.ttt_block_ttt_state.argtypes = [vp]
+        L.ttt_block_ttt_state.restype = vp
         L.ttt_status_str.argtypes = [ctypes.c_int]
         L.ttt_status_str.restype = ctypes.c_char_p
         L.ttt_last_error.argtypes = []
@@ -163,16 +189,19 @@ def ttt_state_numel(cfg: ttt_config) -> int:
 
 
 class State:
-    """Owns a ttt_state handle (freed by destroy() or garbage collection)."""
+    """Owns a ttt_state handle (freed by destroy() or garbage collection), or, with
+    owner set, refers to one that object owns (destroy() then only drops the reference)."""
 
-    def __init__(self, handle: int, cfg: ttt_config):
+    def __init__(self, handle: int, cfg: ttt_config, owner=None):
         self.handle = ctypes.c_void_p(handle)
         self.cfg = cfg
+        self.owner = owner
 
     def destroy(self):
         if self.handle:
             h, self.handle = self.handle, None
-            _check(lib().ttt_destroy_state(h))
+            if self.owner is None:
+                _check(lib().ttt_destroy_state(h))
 
     def __del__(self):
         try:
@@ -296,3 +325,83 @@ def split_state(cfg: ttt_config, flat):
         out.append(flat[o:o + n].view(cfg.batch, cfg.heads, r, c))
         o += n
     return out
+
+
+# ---------------------------------------------------------------- the LaCT block (ttt_block.h)
+def ttt_window_attention(q, k, v, ld: int, out, ld_out: int, batch: int, heads: int,
+                         seq_len: int, window: int, mode="sliding", stream=None) -> None:
+    """Window attention over heads of 128: q, k, v, out bf16 device tensors whose element
+    (b, t, h, e) sits at (b seq_len + t) ld + 128 h + e (ld_out for out); mode "sliding" or
+    "block" (see include/ttt_block.h)."""
+    m = WINDOW[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().ttt_window_attention(_ptr(q), _ptr(k), _ptr(v), int(ld), _ptr(out),
+                                      int(ld_out), int(batch), int(heads), int(seq_len),
+                                      int(window), m, _stream(stream)))
+
+
+def ttt_linear(x, w, resid, y, rows: int, in_features: int, out_features: int,
+               epilogue="plain", stream=None) -> None:
+    """y = epilogue(x w^T) in bf16 with fp32 accumulation; epilogue "plain", "residual"
+    (adds resid) or "gelu" (see include/ttt_block.h)."""
+    e = LINEAR_EPI[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    _check(lib().ttt_linear(_ptr(x), _ptr(w), _ptr(resid), _ptr(y), int(rows), int(in_features),
+                            int(out_features), e, _stream(stream)))
+
+
+def make_block_config(ttt: ttt_config, *, dim: int, window: int, mode="sliding",
+                      ffn_hidden: int = 0, max_seq_len: int) -> ttt_block_config:
+    c = ttt_block_config()
+    c.batch = ttt.batch
+    c.dim = int(dim)
+    c.window = int(window)
+    c.window_mode = WINDOW[mode] if isinstance(mode, str) else int(mode)
+    c.ffn_hidden = int(ffn_hidden)
+    c.reserved = 0
+    c.max_seq_len = int(max_seq_len)
+    c.ttt = ttt
+    return c
+
+
+class Block:
+    """Owns a ttt_block handle and keeps the weight tensors it references alive."""
+
+    def __init__(self, handle: int, cfg: ttt_block_config, weights):
+        self.handle = ctypes.c_void_p(handle)
+        self.cfg = cfg
+        self.weights = weights
+
+    def destroy(self):
+        if self.handle:
+            h, self.handle = self.handle, None
+            _check(lib().ttt_block_destroy(h))
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def ttt_block_init(cfg: ttt_block_config, weights, w0, stream=None) -> Block:
+    """weights: mapping from the names in BLOCK_WEIGHTS to contiguous bf16 device tensors;
+    w0: the TTT sub-layer's initial matrices (the layout ttt_init_state takes)."""
+    w = ttt_block_weights()
+    for n in BLOCK_WEIGHTS:
+        setattr(w, n, _ptr(weights[n]))
+    h = ctypes.c_void_p()
+    _check(lib().ttt_block_init(ctypes.byref(cfg), ctypes.byref(w), _ptr(w0), _stream(stream),
+                                ctypes.byref(h)))
+    return Block(h.value, cfg, dict(weights))
+
+
+def ttt_block_forward(blk: Block, x, y, seq_len: int, stream=None) -> None:
+    _check(lib().ttt_block_forward(blk.handle, _ptr(x), _ptr(y), int(seq_len), _stream(stream)))
+
+
+def ttt_block_ttt_state(blk: Block) -> State:
+    """The block's TTT state, for ttt_get_state and the other state calls."""
+    return State(lib().ttt_block_ttt_state(blk.handle), blk.cfg.ttt, owner=blk)
+
+
+def ttt_block_destroy(blk: Block) -> None:
+    blk.destroy()

@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libttt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["ttt_kernels.hip", "ttt_backward.hip", "ttt_small.hip", "ttt_noalloc.hip",
-           "libttt.cpp"]
+           "ttt_block.hip", "libttt.cpp", "ttt_block.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in device code
@@ -39,7 +39,7 @@ def build(verbose: bool = False) -> str:
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
     for src in SOURCES:
-        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, src.replace(".", "_") + ".o")
         out = _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
