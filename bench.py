@@ -246,6 +246,167 @@ def bench_chunk_backward(args, cfg, planes):
     }), flush=True)
 
 
+# The LaCT block around each workload's TTT layer: model width = heads x dim, attention
+# heads of 128, the window of the page's reading (text: a sliding window of one chunk;
+# image sets: one image of 8040 tokens, 1,029,120 / 128), MLP hidden 4 x width.
+BLOCK_WINDOW = {"lm": (2048, "sliding"), "long": (4096, "sliding"),
+                "imageset": (8040, "block"), "smallchunk": (64, "sliding")}
+
+
+def block_part_flops(cfg, dim: int, F: int, window: int, mode: str) -> dict:
+    """Algorithmic FLOP per step of each part of the block (2 per multiply-add): the
+    projections, the attention (4 x 128 per head and allowed (query, key) pair) and the
+    TTT layer (total_flops)."""
+    B, T, H = cfg.batch, cfg.seq_len, cfg.heads
+    rows = B * T
+    if mode == "sliding":
+        pairs = sum(min(t + 1, window) for t in range(T)) if T <= 1 << 20 else T * window
+    else:
+        full, rest = divmod(T, window)
+        pairs = full * window * window + rest * rest
+    return {"proj_qkv": 2 * 2.0 * rows * dim * 3 * dim,      # attention and TTT q, k, v
+            "proj_out": 2 * 2.0 * rows * dim * dim,          # attention and TTT outputs
+            "ffn_up": 2.0 * rows * dim * F, "ffn_down": 2.0 * rows * F * dim,
+            "attention": 4.0 * 128 * pairs * B * (dim // 128),
+            "ttt_layer": total_flops(cfg)}
+
+
+def bench_block(args, cfg, planes):
+    """Times ttt_block_forward over the workload's whole batch (one step = one block over
+    every sequence) and each of its parts on its own, and prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import oracle.ttt_block as blk_oracle
+    import ttt_inputs as ti
+    import weight_sequence_layers_amd as W
+
+    if cfg.name not in BLOCK_WINDOW:
+        sys.exit(f"no block shape for workload {cfg.name}")
+    window, mode = BLOCK_WINDOW[cfg.name]
+    D = cfg.heads * cfg.dim
+    F = 4 * D
+    B, T = cfg.batch, cfg.seq_len
+    c = W.make_config(cfg, planes=planes)
+    bc = W.make_block_config(c, dim=D, window=window, mode=mode, ffn_hidden=F, max_seq_len=T)
+    t = time.perf_counter()
+    inp = ti.make_block_inputs(B, T, D, F, cfg.heads, cfg.seed)
+    log(f"block inputs generated in {time.perf_counter() - t:.1f} s")
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+    weights = {n: dev(inp[n + "_bits"]) for n in ti.BLOCK_WEIGHT_NAMES}
+    x = dev(inp["x_bits"])
+    y = torch.empty_like(x)
+    w0list = ti.make_weights(cfg)
+    w0 = torch.from_numpy(np.concatenate([w.ravel() for w in w0list])).cuda()
+    blk = W.ttt_block_init(bc, weights, w0)
+
+    def step():
+        W.ttt_block_forward(blk, x, y, T)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    W.ttt_state_health(W.ttt_block_ttt_state(blk))
+
+    # each part on its own, with HIP events on the current stream (torch's, which the
+    # calls launch on)
+    rows = B * T
+    g = torch.Generator(device="cuda").manual_seed(3)
+    qkv = torch.randn(rows, 3 * D, generator=g, device="cuda").to(torch.bfloat16)
+    a_out = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+    h = torch.empty(rows, F, dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, reps=max(args.steps, 3)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    xr = x.view(rows, D)
+    parts = {
+        "attention": (1, timed(lambda: W.ttt_window_attention(
+            qkv, qkv[:, D:], qkv[:, 2 * D:], 3 * D, a_out, D, B, D // 128, T, window, mode))),
+        "proj_qkv": (2, timed(lambda: W.ttt_linear(xr, weights["attn_qkv"], None, qkv, rows,
+                                                   D, 3 * D, "plain"))),
+        "proj_out": (2, timed(lambda: W.ttt_linear(xr, weights["attn_out"], a_out, a_out, rows,
+                                                   D, D, "residual"))),
+        "ffn_up": (1, timed(lambda: W.ttt_linear(xr, weights["ffn_up"], None, h, rows, D, F,
+                                                 "gelu"))),
+        "ffn_down": (1, timed(lambda: W.ttt_linear(h, weights["ffn_down"], a_out, a_out, rows,
+                                                   F, D, "residual"))),
+    }
+    del qkv, h
+    tin = ti.make_inputs(cfg)
+    tdev = [torch.from_numpy(tin[n + "_bits"].view(np.int16)).cuda().view(torch.bfloat16)
+            for n in ("q", "k", "v")]
+    teta = torch.from_numpy(tin["eta"]).cuda()
+    tout = torch.empty_like(tdev[0])
+    del tin
+    st = W.ttt_init_state(c, w0)
+    parts["ttt_layer"] = (1, timed(lambda: W.ttt_sequence_forward(st, *tdev, teta, tout, T)))
+    st.destroy()
+    del tdev, tout
+    flops = block_part_flops(cfg, D, F, window, mode)
+    own = {k: v for k, v in parts.items() if k != "ttt_layer"}
+    dom = max(own, key=lambda k: own[k][0] * own[k][1])
+    per_launch = flops[dom] / parts[dom][0]
+    achieved = per_launch / (parts[dom][1] / 1e3) / 1e12
+    total = sum(flops.values())
+
+    # the oracle: one sequence's first two chunks (or the first 4096 tokens of one image
+    # set), the same weights and initial fast weights
+    Tc = min(T, 2 * cfg.chunk if cfg.chunk < T else 4096)
+    cpu = None
+    if not args.no_cpu_baseline and (cfg.order == "apply_then_update" or Tc == T):
+        class BC:
+            pass
+        bco = BC()
+        bco.ttt = cfg.replace(seq_len=Tc, batch=1)
+        bco.window, bco.window_mode = window, mode
+        per_head = [[w[hh] for w in w0list] for hh in range(cfg.heads)]
+        t1 = time.perf_counter()
+        blk_oracle.block_forward(bco, inp, inp["x"][0, :Tc].astype(np.float64), per_head)
+        odt = time.perf_counter() - t1
+        cpu = {"value": Tc / odt, "unit": "tokens/s", "cores": os.cpu_count(), "kind": "oracle",
+               "sample": f"one sequence's first {Tc} tokens through the block oracle "
+                         f"(numpy fp64), {odt:.1f} s"}
+    blk.destroy()
+    res = {
+        "metric": "LaCT block tokens/sec (window attention + TTT layer + MLP)",
+        "value": round(B * T / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * dt, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} block: batch {B}, seq {T}, width {D} "
+                               f"({D // 128} attention heads, {cfg.heads} TTT heads of "
+                               f"{cfg.dim}), {mode} window {window}, MLP {F}, TTT chunk "
+                               f"{cfg.chunk}",
+                   "bf16_planes_apply_grad_ns": list(planes[:3])},
+        "block_tflops_algorithmic": round(total / dt / 1e12, 2),
+        "parts_ms_per_step": {k: round(n * ms, 3) for k, (n, ms) in parts.items()},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": dom,
+                     "avg_launch_us": round(1e3 * parts[dom][1], 2)},
+        "parts_tflops": {k: round(flops[k] / (n * ms / 1e3) / 1e12, 1)
+                         for k, (n, ms) in parts.items()},
+    }
+    if cpu:
+        res["cpu_baseline"] = cpu
+    print(json.dumps(res), flush=True)
+
+
 def recorded_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from profiles/<workload>_traffic.md, if that summary
     was taken from the current kernel sources; else None."""
@@ -361,6 +522,8 @@ def main():
                     help="record each step's launches in a HIP graph and replay it")
     ap.add_argument("--chunk-backward", action="store_true",
                     help="time the backward through one chunk on the workload's first chunk")
+    ap.add_argument("--block", action="store_true",
+                    help="time the LaCT block around the workload's layer instead")
     ap.add_argument("--cpu-chunks", type=int, default=None)
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time hipBLASLt (torch.bmm) on each stage's GEMM shapes")
@@ -391,6 +554,9 @@ def main():
         return
     if args.chunk_backward:
         bench_chunk_backward(args, cfg, planes)
+        return
+    if args.block:
+        bench_block(args, cfg, planes)
         return
     c = W.make_config(cfg, planes=planes, replay=args.replay)
     torch.cuda.set_device(0)

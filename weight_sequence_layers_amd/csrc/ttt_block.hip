@@ -47,7 +47,8 @@ __device__ __forceinline__ bf16x8 read_vt_frag(const char* tile, int dim_base, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__global__ __launch_bounds__(256) void k_window_attention(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void k_window_attention(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0[ATT_STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[ATT_STAGE];
   const int id = xcd_block(blockIdx.x, a.total);
@@ -76,6 +77,22 @@ __global__ __launch_bounds__(256) void k_window_attention(AttnArgs a) {
   if (t >= T) lo_t = hi_t = 0;   // padding rows: every key masked, nothing stored
   const int len_t = hi_t - lo_t;
   const int nsteps = (hi - lo + ATT_KV - 1) / ATT_KV;
+  // keys [in_lo, in_hi) lie inside the window of every query of this wave: a step wholly in
+  // that range needs no mask (empty range for a wave of padding rows)
+  int in_lo, in_hi;
+  {
+    const int w0 = q0 + 32 * w, wl = min(w0 + 31, T - 1);
+    if (w0 >= T) {
+      in_lo = 1;
+      in_hi = 0;
+    } else if (a.mode == TTT_WINDOW_SLIDING) {
+      in_lo = wl - W + 1;
+      in_hi = w0 + 1;
+    } else {
+      in_lo = (wl / W) * W;
+      in_hi = (int)min<int64_t>(T, ((int64_t)(w0 / W) + 1) * W);
+    }
+  }
 
   const int64_t row0 = (int64_t)b * T;
   const u16* kb = a.k + row0 * a.ld + (int64_t)h * ATT_D;
@@ -136,28 +153,36 @@ __global__ __launch_bounds__(256) void k_window_attention(AttnArgs a) {
         sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             read_frag<false, ATT_KV, 64>(kh, 32 * kt, s & 3), qf[s], sc[kt], 0, 0, 0);
     }
-    // element v of tile kt: key kv0 + 32 kt + 8 (v / 4) + 4 (lane / 32) + v % 4
-    const int base = kv0 + 4 * hl - lo_t;
+    // element v of tile kt: key kv0 + 32 kt + 8 (v / 4) + 4 (lane / 32) + v % 4.  Scores
+    // stay unscaled until the exponent: the scale is positive, so the maximum is taken on
+    // raw scores and p = exp2(s scale2 - m) is one fused multiply-add and one exp2.
+    if (kv0 < in_lo || kv0 + ATT_KV > in_hi) {   // wave-uniform: a window edge in this step
+      const int base = kv0 + 4 * hl - lo_t;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int dk = base + 32 * kt + 8 * (v >> 2) + (v & 3);
+          if ((unsigned)dk >= (unsigned)len_t) sc[kt][v] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int dk = base + 32 * kt + 8 * (v >> 2) + (v & 3);
-        const float x = ((unsigned)dk < (unsigned)len_t) ? sc[kt][v] * a.scale2 : -INFINITY;
-        sc[kt][v] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kt][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale2;
     const float mnew = fmaxf(m, mx);
     const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
+    if (__any(mnew != m)) {   // wave-uniform: some running maximum moved
+      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[d][v] *= alpha;
+    }
     m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[d][v] *= alpha;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -165,7 +190,8 @@ __global__ __launch_bounds__(256) void k_window_attention(AttnArgs a) {
         bf16x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const __bf16 p = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[kt][8 * sp + e] - mref));
+          const __bf16 p = static_cast<__bf16>(
+              __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * sp + e], a.scale2, -mref)));
           pf[e] = p;
           l += static_cast<float>(p);
         }
@@ -200,7 +226,37 @@ __global__ __launch_bounds__(256) void k_window_attention(AttnArgs a) {
 // K (input features) in steps of 64 through two LDS stages.  The tile's rows and weight
 // rows are addressed from the tile's origin, so offsets stay within 32 bits for any
 // number of rows.
+//
+// Tile order: each XCD runs a contiguous range of tiles (xcd_block), and within it the
+// tiles go in groups of group_m row tiles that walk the output features together, row
+// tile fastest: the workgroups resident on an XCD at one time then read a few row panels
+// and a few weight panels, each from its L2 several times, instead of one row panel and
+// a stream through the whole weight matrix (larger than an XCD's L2 for the block's
+// widths).  Groups of 8 row tiles took the block's projections at width 1024 from
+// 700-950 to 900-1040 TFLOP/s.
 using GL = Gemm<128, 128, 2, 2, 1, 1, L_ROW, L_ROW, 0, 64, true>;
+
+// GELU(x) = x Phi(x) with Phi(x) = erfc(-x / sqrt 2) / 2, erfc from the Chebyshev fit of
+// Numerical Recipes (erfcc, fractional error below 1.2e-7 for every argument), so the
+// function has no branches: t = 1 / (1 + z / 2), erfc(z) = t exp(-z^2 + P(t)), z = |x| /
+// sqrt 2, and erfc(-z) = 2 - erfc(z).
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(1.f + 0.5f * z);
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  const float ec = t * __builtin_amdgcn_exp2f((p - z * z) * 1.44269504088896341f);
+  const float phi = x >= 0.f ? 1.f - 0.5f * ec : 0.5f * ec;
+  return x * phi;
+}
 
 // Two workgroups fit a CU's LDS; the register budget is held to the same two waves per SIMD
 // (the GELU epilogue alone would take more).
@@ -209,7 +265,11 @@ __global__ __launch_bounds__(GL::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void k_linear(LinearArgs a) {
   GEMM_LDS(GL);
   const int id = xcd_block(blockIdx.x, (int)a.tiles);
-  const int tm = id / a.tiles_n, tn = id % a.tiles_n;
+  // group of group_m row tiles (the last group may be shorter), row tile fastest
+  const int gsz = a.group_m * a.tiles_n;
+  const int grp = id / gsz, in = id - grp * gsz;
+  const int gm = min(a.group_m, a.tiles_m - grp * a.group_m);
+  const int tm = grp * a.group_m + in % gm, tn = in / gm;
   const int64_t m0 = (int64_t)tm * GL::TBM;
   const int n0 = tn * GL::TBN;
   const int rl = (int)min<int64_t>(GL::TBM, a.rows - m0), cl = min(GL::TBN, a.N - n0);
@@ -220,8 +280,7 @@ void k_linear(LinearArgs a) {
   g.run(&A, &B, 0, 0, 0, a.K, GEMM_STAGES);
   if constexpr (EPI == TTT_LINEAR_GELU) {
     g.for_each([&](int i, int j, int v, int, int) __attribute__((always_inline)) {
-      const float x = g.acc[0][i][j][v];
-      g.acc[0][i][j][v] = 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+      g.acc[0][i][j][v] = gelu_erf(g.acc[0][i][j][v]);
     });
   }
   if constexpr (EPI == TTT_LINEAR_RESIDUAL) {

@@ -28,7 +28,7 @@ struct LinearArgs {
   const u16* resid;
   u16* y;
   int64_t rows;
-  int32_t K, N, tiles_n;
+  int32_t K, N, tiles_n, tiles_m, group_m;
   int64_t tiles;
 };
 
