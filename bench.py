@@ -53,8 +53,17 @@ def stage_flops(cfg) -> dict:
     f["ns_gram"] = 2.0 * m * m * n * nm * P * it
     f["ns_poly"] = 2.0 * m * m * m * nm * P * it
     f["ns_update"] = 2.0 * m * m * n * nm * P * it
+    if ns_small(cfg):   # every iteration in one launch per chunk
+        f["ns_small"] = f.pop("ns_gram") + f.pop("ns_poly") + f.pop("ns_update")
     f["resident"] = total_flops(cfg)
     return f
+
+
+def ns_small(cfg) -> bool:
+    """Whether the forward orthogonalises with the fused small-matrix launch (matrices of
+    at most 64 x 128 in their [dim][hidden] orientation)."""
+    n = cfg.dim if cfg.fw == "linear" else cfg.hidden
+    return cfg.ns_steps > 0 and cfg.dim <= 64 and n <= 128
 
 
 def total_flops(cfg) -> float:

@@ -297,14 +297,16 @@ ttt_status ttt_sequence_forward_noalloc(const ttt_config* cfg, float* state, con
  * 7 update + renorm, 8 fp32 plane split, 9 MSE error / dH GEMMs,
  * 10 device-resident chunk loop (one launch per call), 11 the backward's dQ, dK and dV
  * GEMMs, 12 the chunk backward's tangent front (and its eta sums), 13 its Newton-Schulz
- * backward GEMMs.
+ * backward GEMMs, 14 every Newton-Schulz iteration of a small matrix in one launch (the
+ * forward's orthogonalisation when the matrices in their [dim][hidden] orientation are at
+ * most 64 x 128; stages 4-6 then do not run).
  * The hooks create and destroy HIP events but allocate no device memory.
  */
 typedef enum {
   TTT_STAGE_FRONT_Q = 0, TTT_STAGE_FRONT_K = 1, TTT_STAGE_OUT = 2, TTT_STAGE_CONTRACT = 3,
   TTT_STAGE_NS_GRAM = 4, TTT_STAGE_NS_POLY = 5, TTT_STAGE_NS_UPDATE = 6, TTT_STAGE_RENORM = 7,
   TTT_STAGE_SPLIT = 8, TTT_STAGE_MSE = 9, TTT_STAGE_RESIDENT = 10, TTT_STAGE_DQ = 11,
-  TTT_STAGE_TFRONT = 12, TTT_STAGE_NS_BWD = 13, TTT_STAGE_COUNT = 14
+  TTT_STAGE_TFRONT = 12, TTT_STAGE_NS_BWD = 13, TTT_STAGE_NS_SMALL = 14, TTT_STAGE_COUNT = 15
 } ttt_stage;
 ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches);
 ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms);

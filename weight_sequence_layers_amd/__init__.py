@@ -293,7 +293,7 @@ def ttt_destroy_state(st: State) -> None:
 
 STAGES = {"front_q": 0, "front_k": 1, "out": 2, "contract": 3, "ns_gram": 4, "ns_poly": 5,
           "ns_update": 6, "renorm": 7, "split": 8, "mse": 9, "resident": 10, "dq": 11,
-          "tfront": 12, "ns_bwd": 13}
+          "tfront": 12, "ns_bwd": 13, "ns_small": 14}
 
 
 def ttt_profile_begin(st: State, stage, max_launches: int = 4096) -> None:

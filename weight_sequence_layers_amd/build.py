@@ -15,7 +15,7 @@ LIB = os.path.join(PKG, "libttt.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["ttt_kernels.hip", "ttt_backward.hip", "ttt_small.hip", "ttt_noalloc.hip",
-           "ttt_block.hip", "libttt.cpp", "ttt_block.cpp"]
+           "ttt_ns_small.hip", "ttt_block.hip", "libttt.cpp", "ttt_block.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in device code

@@ -599,6 +599,21 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st, u16* const* keep = nullpt
   const int steps = s->cfg.ns_steps;
   const int Z = D.nm * D.P, M = D.d, N = D.n;
   auto iterate = [&](int i) { return (keep && i > 0) ? keep[i] : s->xpl[i & 1]; };
+  if (!keep && M <= NS_SMALL_M && N <= NS_SMALL_N) {
+    // every iteration of each matrix in one workgroup (the iterates stay in LDS)
+    NsArgs a{};
+    a.Z = Z; a.M = M; a.N = N; a.P = D.P;
+    a.coef_a = 3.4445f; a.coef_b = -4.7750f; a.coef_c = 2.0315f;
+    a.part = s->part; a.nparts = s->contract_tiles;
+    a.eps = 1e-7f;
+    a.steps = steps;
+    a.one = D.ns_one;
+    a.xin = pbuf(s->xpl[0], D.np, (int64_t)Z * M * N, (int64_t)M * N, N);
+    a.U = s->U;
+    a.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
+    STAGED(TTT_STAGE_NS_SMALL, launch_ns_small(a, st));
+    return TTT_OK;
+  }
   for (int it = 0; it < steps; ++it) {
     // products on pk planes; the iterates X keep D.np planes between iterations
     const int pk = ((D.ns_one >> it) & 1) ? 1 : D.np;

@@ -262,7 +262,7 @@ __device__ __forceinline__ float gelu_erf(float x) {
 // (the GELU epilogue alone would take more).
 template <int EPI>
 __global__ __launch_bounds__(GL::NT) __attribute__((amdgpu_waves_per_eu(2)))
-void k_linear(LinearArgs a) {
+void k_blk_linear(LinearArgs a) {
   GEMM_LDS(GL);
   const int id = xcd_block(blockIdx.x, (int)a.tiles);
   // group of group_m row tiles (the last group may be shorter), row tile fastest
@@ -308,7 +308,7 @@ void k_linear(LinearArgs a) {
 // ------------------------------------------------------------------------ RMS norm
 // One wave per row: the sum of squares, then the normalised row rounded to bf16 and, for
 // the TTT sub-layer, its dot product with each head's step-size weights.
-__global__ __launch_bounds__(256) void k_rmsnorm(RmsArgs a) {
+__global__ __launch_bounds__(256) void k_blk_rmsnorm(RmsArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
   const int lane = threadIdx.x & 63;
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(RmsArgs a) {
 
 // ------------------------------------------------------------------------ head moves
 // One wave per (row, TTT head): q and k scaled to unit length (fp32 norms), v copied.
-__global__ __launch_bounds__(256) void k_split(HeadSplitArgs a) {
+__global__ __launch_bounds__(256) void k_blk_split(HeadSplitArgs a) {
   const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t rows = (int64_t)a.B * a.T;
   if (id >= rows * a.H) return;
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(256) void k_split(HeadSplitArgs a) {
 }
 
 // One thread per 8 outputs: [B][H][T][d] -> [B T][H d].
-__global__ __launch_bounds__(256) void k_merge(HeadMergeArgs a) {
+__global__ __launch_bounds__(256) void k_blk_merge(HeadMergeArgs a) {
   const int D = a.H * a.d;
   const int64_t total = (int64_t)a.B * a.T * D / 8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -428,31 +428,31 @@ hipError_t launch_linear(const LinearArgs& a, int epilogue, hipStream_t st) {
   if (a.tiles == 0) return hipSuccess;
   const dim3 grid((unsigned)a.tiles), block(GL::NT);
   if (epilogue == TTT_LINEAR_RESIDUAL)
-    hipLaunchKernelGGL(k_linear<TTT_LINEAR_RESIDUAL>, grid, block, 0, st, a);
+    hipLaunchKernelGGL(k_blk_linear<TTT_LINEAR_RESIDUAL>, grid, block, 0, st, a);
   else if (epilogue == TTT_LINEAR_GELU)
-    hipLaunchKernelGGL(k_linear<TTT_LINEAR_GELU>, grid, block, 0, st, a);
+    hipLaunchKernelGGL(k_blk_linear<TTT_LINEAR_GELU>, grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(k_linear<TTT_LINEAR_PLAIN>, grid, block, 0, st, a);
+    hipLaunchKernelGGL(k_blk_linear<TTT_LINEAR_PLAIN>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(const RmsArgs& a, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_blk_rmsnorm, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_split(const HeadSplitArgs& a, hipStream_t st) {
   const int64_t waves = (int64_t)a.B * a.T * a.H;
   if (waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_split, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_blk_split, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const HeadMergeArgs& a, hipStream_t st) {
   const int64_t n = (int64_t)a.B * a.T * a.H * a.d / 8;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_blk_merge, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

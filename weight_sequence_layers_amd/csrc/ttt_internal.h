@@ -207,7 +207,12 @@ struct NsArgs {
   float* U;           // last: U in weight orientation
   int tr_mask;
   int P;
+  int steps;          // fused small-matrix launch: all iterations, and
+  int one;            // the one-plane iteration mask
 };
+
+// matrices the fused Newton-Schulz launch takes: X orientation up to 64 x 128
+constexpr int NS_SMALL_M = 64, NS_SMALL_N = 128;
 
 struct RenormMat {
   float* W;        // [P][rows][cols]
@@ -273,6 +278,7 @@ int gemm2_tiles(int M, int N);
 int contract_split_max(int tiles, int nz);
 hipError_t launch_ns_gram(const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_poly(const NsArgs& a, hipStream_t s);
+hipError_t launch_ns_small(const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_update(const NsArgs& a, hipStream_t s);
 hipError_t launch_renorm(const RenormArgs& a, hipStream_t s);
 hipError_t launch_split(const SplitArgs& a, int Z, hipStream_t s);
@@ -294,6 +300,7 @@ ttt_status sequence_in_workspace(const ttt_config* cfg, float* w, const void* q,
 
 // tile sizes used by the contraction and Newton-Schulz stages (the host sizes buffers)
 constexpr int CONTRACT_BM = 128, CONTRACT_BN = 128;
+constexpr int CONTRACT_SPLIT_MAX = 16;   // token ranges of one contraction at most
 int ns_tri_tiles(int M, int tile);
 
 }  // namespace ttt

@@ -320,8 +320,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
 // or the X0 planes with the tile's sum of squares, or U).  Each thread takes runs of 8
 // columns (N is a multiple of 16).
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void k_contract_sum(ContractArgs a) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(1024) void k_contract_sum(ContractArgs a) {
+  __shared__ float red[16];
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int m = zz / a.P;
@@ -331,18 +331,34 @@ __global__ __launch_bounds__(256) void k_contract_sum(ContractArgs a) {
   const int64_t base = (int64_t)zz * M * N;
   const int tr = (a.tr_mask >> m) & 1;
   float ss = 0.f;
-  for (int gi = threadIdx.x; gi < BM * BN / 8; gi += 256) {
+  for (int gi = threadIdx.x; gi < BM * BN / 8; gi += blockDim.x) {
     const int row = m0 + gi / (BN / 8), col = n0 + (gi % (BN / 8)) * 8;
     if (row >= M || col >= N) continue;
     const int64_t off = base + (int64_t)row * N + col;
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    for (int k = 0; k < a.ksplit; ++k) {
-      const float4* src = reinterpret_cast<const float4*>(a.gpart + k * a.gpart_stride + off);
-      const float4 u = src[0], w = src[1];
-      x[0] += u.x; x[1] += u.y; x[2] += u.z; x[3] += u.w;
-      x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
+    // the partials in split order, eight at a time, each batch's loads issued before its
+    // first add
+    for (int k0 = 0; k0 < a.ksplit; k0 += 8) {
+      float4 pu[8], pw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (k0 + k < a.ksplit) {
+          const float4* src =
+              reinterpret_cast<const float4*>(a.gpart + (k0 + k) * a.gpart_stride + off);
+          pu[k] = src[0];
+          pw[k] = src[1];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (k0 + k < a.ksplit) {
+          const float4 u = pu[k], w = pw[k];
+          x[0] += u.x; x[1] += u.y; x[2] += u.z; x[3] += u.w;
+          x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
+        }
+      }
     }
     if (a.accum_in) {
       const float4* src = reinterpret_cast<const float4*>(a.G + off);
@@ -829,7 +845,7 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 
 // Token ranges: enough for about two workgroups per CU (256 CUs) when the output tiles
 // alone are fewer, at most 8, each range at least 256 tokens.
-constexpr int CONTRACT_SLOTS = 512, CONTRACT_SPLIT_MAX = 8, CONTRACT_RANGE_MIN = 256;
+constexpr int CONTRACT_SLOTS = 512, CONTRACT_RANGE_MIN = 256;
 
 int contract_split_max(int tiles, int nz) {
   const int64_t wgs = (int64_t)tiles * nz;
@@ -860,7 +876,7 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(a.tiles * a.nz * a.ksplit), dim3(G::NT), 0, s, a);
   if (a.ksplit > 1) {
     auto sum = k_contract_sum<BM, BN>;
-    hipLaunchKernelGGL(sum, dim3(a.tiles * a.nz), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(sum, dim3(a.tiles * a.nz), dim3(1024), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -37,6 +37,7 @@ STAGE_KERNELS = [
     ("ns_gram", r"k_ns_gram<"),
     ("ns_poly", r"k_ns_poly<"),
     ("ns_update", r"k_ns_update<"),
+    ("ns_small", r"k_ns_small<"),
     ("renorm", r"k_renorm"),
     ("split", r"k_split"),
     ("resident", r"k_small_gelu<"),
