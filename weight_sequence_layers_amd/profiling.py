@@ -47,11 +47,14 @@ STAGE_KERNELS = [
 ]
 
 
-def source_digest() -> str:
-    """Hash of the kernel sources (every file under csrc/)."""
+def source_digest(part: str = "layer") -> str:
+    """Hash of the kernel sources: part "layer" covers every file under csrc/ that the TTT
+    layer is built from, "block" the files of the block around it (ttt_block*)."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f.startswith("ttt_block") != (part == "block"):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -71,7 +74,7 @@ def _one(pattern: str, d: str) -> str:
 def stats_md(trace_dir: str, command: str) -> str:
     rows = list(csv.DictReader(open(_one("*kernel_stats.csv", trace_dir))))
     out = ["# Kernel durations", "", "Command (repository root, one MI355X):", "",
-           f"    {command}", "", f"source digest: {source_digest()}", "",
+           f"    {command}", "", f"source digest: {source_digest()}", f"block source digest: {source_digest('block')}", "",
            "| kernel | calls | average us | total ms | % |", "|---|---|---|---|---|"]
     for r in rows:
         out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | "
@@ -108,7 +111,7 @@ def traffic_md(fetch_dir: str, write_dir: str, workload: str, fetch_cmd: str,
            f"Calibration: the reference kernel reads and writes {calib_mib} MiB; it read "
            f"{fetch[calib[0]][1]:.0f} KiB on FETCH_SIZE and {write[calib[0]][1]:.0f} KiB on "
            f"WRITE_SIZE, so fetch values are scaled by {f_scale:.4f} and write values by "
-           f"{w_scale:.4f}.", "", f"source digest: {source_digest()}", "",
+           f"{w_scale:.4f}.", "", f"source digest: {source_digest()}", f"block source digest: {source_digest('block')}", "",
            "Each counter is summed over its instances per dispatch and averaged over "
            "dispatches; a stage served by several kernels sums them. The last column is "
            "scaled fetch + write in bytes.", "",
@@ -138,7 +141,7 @@ def mfma_md(pmc_dir: str, command: str, cus: int = 256, simds_per_cu: int = 4,
         per[k][r["Counter_Name"]] += float(r["Counter_Value"])
         disp[k].add(r["Dispatch_Id"])
     out = ["# Executed MFMA utilisation per kernel", "", "Command (repository root, one MI355X):",
-           "", f"    {command}", "", f"source digest: {source_digest()}", "",
+           "", f"    {command}", "", f"source digest: {source_digest()}", f"block source digest: {source_digest('block')}", "",
            "utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs), summed "
            "over the kernel's dispatches; it counts the MFMA work the kernel executes, plane "
            "products included.", "",
@@ -176,7 +179,7 @@ def counters_md(pmc_dirs, command_lines, title: str) -> str:
     names = sorted({c for v in vals.values() for c in v})
     out = [f"# {title}", "", "Commands (repository root, one MI355X), one counter set per run:",
            ""] + [f"    {c}" for c in command_lines] + [
-           "", f"source digest: {source_digest()}", "",
+           "", f"source digest: {source_digest()}", f"block source digest: {source_digest('block')}", "",
            "Per dispatch, each counter summed over its instances and averaged over the "
            "kernel's dispatches. Derived: L2 hit % = TCC_HIT / (TCC_HIT + TCC_MISS); "
            "read latency (cycles) = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ; DRAM % = "
