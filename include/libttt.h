@@ -311,8 +311,9 @@ typedef enum {
 ttt_status ttt_profile_begin(ttt_state* s, int32_t stage, int32_t max_launches);
 ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms);
 
-/* Static description of a status, and the calling thread's last error message.         */
-const char* ttt_status_str(ttt_status st);
+/* Static description of a status code (any int32_t: codes that are not a ttt_status give
+ * "unknown status"), and the calling thread's last error message.                       */
+const char* ttt_status_str(int32_t st);
 const char* ttt_last_error(void);
 
 #ifdef __cplusplus

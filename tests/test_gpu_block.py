@@ -247,3 +247,31 @@ def test_block_empty_and_rejected_lengths():
         with pytest.raises(W.TTTError):
             W.ttt_block_forward(blkh, x, y, bad)
     W.ttt_block_destroy(blkh)
+
+
+def test_block_full_size_first_chunk():
+    """The LaCT language-model block at the benchmark's shape (4 sequences of 32768 tokens,
+    width 1024, TTT heads 2 x 512, chunk 2048, sliding window 2048, MLP 4096) through the same
+    call the benchmark times. Under the shifted order the first chunk's queries see the
+    initial fast weights and the window is causal, so rows t < 2048 depend on x[0..2047]
+    alone: the oracle computes them from a 2048-token sequence, for the first and last
+    sequence of the batch."""
+    cfg = ti.CONFIGS["lm"]
+    B, T, D, F, H = cfg.batch, cfg.seq_len, cfg.heads * cfg.dim, 4 * cfg.heads * cfg.dim, cfg.heads
+    inp = ti.make_block_inputs(B, T, D, F, H, cfg.seed)
+    w0 = ti.make_weights(cfg)
+    print(f"block full size B={B} T={T} D={D}", flush=True)
+    y, _ = _run_block(cfg, F, inp, w0, D, cfg.chunk, "sliding", T)
+    b0 = cfg.chunk
+
+    class BC:
+        pass
+    bc = BC()
+    bc.ttt, bc.window, bc.window_mode = cfg.replace(seq_len=b0, batch=1), cfg.chunk, "sliding"
+    per_head = [[w[h] for w in w0] for h in range(H)]
+    for b in (0, B - 1):
+        y_ref = blk.block_forward(bc, inp, inp["x"][b, :b0].astype(np.float64), per_head)
+        err = _rel(y[b, :b0], y_ref)
+        print(f"  sequence {b}: first chunk max rel err {err:.3e}", flush=True)
+        assert err <= 2e-2, (b, err)
+    assert np.isfinite(y).all()

@@ -13,7 +13,8 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libttt.so")
+# LIBTTT_PATH selects another build of the library (the host-sanitized copy of the CPU tests)
+LIB_PATH = os.environ.get("LIBTTT_PATH") or os.path.join(PKG, "libttt.so")
 
 FW = {"swiglu": 0, "gelu": 1, "linear": 2}
 LOSS = {"dot": 0, "mse": 1}

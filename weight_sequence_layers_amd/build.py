@@ -50,5 +50,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+HOST_SOURCES = [f for f in SOURCES if f.endswith(".cpp")]
+# sanitizers compiled into the host code only; the device code is built as always.
+# "ubsan": undefined-behaviour checks as traps (no runtime library); "asan": address checks,
+# whose runtime (asan_runtime()) must be preloaded into the process that loads the library
+HOST_SANITIZE = {
+    "ubsan": ["-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fsanitize-trap=undefined",
+              "-Xarch_host", "-fno-sanitize=vptr"],
+    "asan": ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"],
+}
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared address-sanitizer runtime."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       stdout=subprocess.PIPE, text=True)
+    return r.stdout.strip()
+
+
+def build_host_sanitized(out_path: str, kind: str = "ubsan") -> str:
+    """A copy of the library at out_path whose host sources (argument checks, state and
+    workspace handling, launch order) carry the sanitizer `kind`, linked with the kernel
+    objects of the last build(). For CPU tests of the host logic."""
+    build_dir = os.path.join(PKG, "_build")
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src.replace(".", "_") + ".o")
+        if src in HOST_SOURCES:
+            obj = out_path + "." + src.replace(".", "_") + ".o"
+            _run([HIPCC, *FLAGS, "-O1", "-g", *HOST_SANITIZE[kind], "-c",
+                  os.path.join(CSRC, src), "-o", obj])
+        elif not os.path.exists(obj):
+            raise FileNotFoundError(f"{obj} missing: run build() first")
+        objs.append(obj)
+    link = ["-shared-libsan", "-Xarch_host", "-fsanitize=address"] if kind == "asan" else []
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link, *objs, "-o", out_path])
+    return out_path
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -1137,7 +1137,7 @@ ttt_status forward(ttt_state* s, const void* q, const void* k, const void* v, co
   hipGraph_t g = nullptr;
   hipError_t e = hipStreamEndCapture(s->cap, &g);
   if (r != TTT_OK) {
-    if (g) hipGraphDestroy(g);
+    if (g) (void)hipGraphDestroy(g);
     return r;
   }
   if (e != hipSuccess) return fail(TTT_E_HIP, "graph capture failed: %s", hipGetErrorString(e));
@@ -1437,7 +1437,7 @@ ttt_status ttt_profile_end(ttt_state* s, int64_t* launches, double* total_ms) {
   return TTT_OK;
 }
 
-const char* ttt_status_str(ttt_status st) {
+const char* ttt_status_str(int32_t st) {
   switch (st) {
     case TTT_OK: return "ok";
     case TTT_E_NULL: return "null pointer";
