@@ -374,9 +374,9 @@ def bench_block(args, cfg, planes):
     achieved = per_launch / (parts[dom][1] / 1e3) / 1e12
     total = sum(flops.values())
 
-    # the oracle: one sequence's first two chunks (or the first 4096 tokens of one image
+    # the oracle: one sequence's first four chunks (or the first 8192 tokens of one image
     # set), the same weights and initial fast weights
-    Tc = min(T, 2 * cfg.chunk if cfg.chunk < T else 4096)
+    Tc = min(T, 4 * cfg.chunk if cfg.chunk < T else 8192)
     cpu = None
     if not args.no_cpu_baseline and (cfg.order == "apply_then_update" or Tc == T):
         class BC:

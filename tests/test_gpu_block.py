@@ -87,6 +87,23 @@ def test_window_attention_matches_oracle(B, heads, T, window, mode, qscale):
     print(f"  worst error / bar {worst:.3f}", flush=True)
 
 
+@pytest.mark.parametrize("window", [777, 64])
+def test_window_attention_eight_wave_workgroups(window):
+    """Sliding windows over a launch of at least 512 workgroups of 256 queries run eight
+    waves a workgroup: 4 sequences x 8 heads x 4000 tokens (a ragged last workgroup), whole
+    heads compared."""
+    B, heads, T = 4, 8, 4000
+    qkv, got = _attention_case(B, heads, T, window, "sliding", 31 + window)
+    D = heads * 128
+    for b, h in ((0, 0), (3, 7), (2, 5)):
+        s = slice(h * 128, (h + 1) * 128)
+        q, k, v = qkv[b, :, s], qkv[b, :, D:][:, s], qkv[b, :, 2 * D:][:, s]
+        ref = blk.window_attention(q, k, v, window, "sliding")
+        err = np.abs(got[b, :, s] - ref)
+        bar = _attention_bar(ref, np.abs(v).max())
+        assert np.all(err <= bar), (b, h, float((err - bar).max()))
+
+
 def test_window_attention_empty_sequence_writes_nothing():
     out = torch.full((1, 4, 128), 7.0, dtype=torch.bfloat16, device=DEV)
     x = torch.zeros(1, 4, 3 * 128, dtype=torch.bfloat16, device=DEV)

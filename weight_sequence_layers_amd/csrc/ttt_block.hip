@@ -8,7 +8,7 @@ namespace ttt {
 namespace {
 
 // ------------------------------------------------------------------------ window attention
-// One workgroup: 4 waves, 128 consecutive queries of one (batch, head), 32 per wave.  The
+// One workgroup: 4 or 8 waves, 32 consecutive queries of one (batch, head) per wave.  The
 // keys the window allows for any of them are visited in steps of 64; each step's K and V
 // tiles are loaded straight into LDS one step ahead (two stages).  Per step a wave
 //   S^T = K Q^T  on the MFMA with K as the A operand, so each lane holds one query
@@ -47,8 +47,11 @@ __device__ __forceinline__ bf16x8 read_vt_frag(const char* tile, int dim_base, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// AW waves per workgroup (32 AW queries): the K and V tiles of a step serve all of them.
+template <int AW>
+__global__ __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(2)))
 void k_window_attention(AttnArgs a) {
+  constexpr int NT = 64 * AW, QB = 32 * AW;
   __shared__ __attribute__((aligned(1024))) char st0[ATT_STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[ATT_STAGE];
   const int id = xcd_block(blockIdx.x, a.total);
@@ -57,11 +60,11 @@ void k_window_attention(AttnArgs a) {
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int T = a.T, W = a.window;
-  const int q0 = qb * ATT_Q;
+  const int q0 = qb * QB;
   const int t = q0 + 32 * w + (lane & 31);
 
   // keys the workgroup visits, and each lane's own window [lo_t, hi_t)
-  const int qlast = min(q0 + ATT_Q, T) - 1;
+  const int qlast = min(q0 + QB, T) - 1;
   int lo, hi, lo_t, hi_t;
   if (a.mode == TTT_WINDOW_SLIDING) {
     lo = max(0, q0 - W + 1);
@@ -109,8 +112,8 @@ void k_window_attention(AttnArgs a) {
     }
   }
 
-  TileLoad<ATT_KV, 256, 64> lk;
-  TileLoad<ATT_D, 256, 64> lv;
+  TileLoad<ATT_KV, NT, 64> lk;
+  TileLoad<ATT_D, NT, 64> lv;
   lk.init(make_operand(nullptr, 0, a.ld, 0, 1, ATT_KV), 0, false, 0);
   lv.init(make_operand(nullptr, 0, a.ld, 0, 1, ATT_D), 0, true, 0);
   // keys at or past the end of the sequence lie past the resource's end and load as 0
@@ -122,12 +125,12 @@ void k_window_attention(AttnArgs a) {
         (void*)(vb + (int64_t)kv0 * a.ld), (short)0, (int)nrec, 0x00020000);
 #pragma unroll
     for (int c = 0; c < lk.C; ++c) {
-      dma16(rk, (lds_void_t*)(st + c * 256 * 16 + lk.slice), lk.off[c]);
-      dma16(rk, (lds_void_t*)(st + KT_BYTES + c * 256 * 16 + lk.slice), lk.off[c] + 128);
+      dma16(rk, (lds_void_t*)(st + c * NT * 16 + lk.slice), lk.off[c]);
+      dma16(rk, (lds_void_t*)(st + KT_BYTES + c * NT * 16 + lk.slice), lk.off[c] + 128);
     }
 #pragma unroll
     for (int c = 0; c < lv.C; ++c)
-      dma16(rv, (lds_void_t*)(st + 2 * KT_BYTES + c * 256 * 16 + lv.slice), lv.off[c]);
+      dma16(rv, (lds_void_t*)(st + 2 * KT_BYTES + c * NT * 16 + lv.slice), lv.off[c]);
   };
 
   f32x16 o[4];
@@ -420,7 +423,8 @@ __global__ __launch_bounds__(256) void k_blk_merge(HeadMergeArgs a) {
 
 hipError_t launch_window_attention(const AttnArgs& a, hipStream_t st) {
   if (a.total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_window_attention, dim3(a.total), dim3(256), 0, st, a);
+  if (a.aw == 8) hipLaunchKernelGGL(k_window_attention<8>, dim3(a.total), dim3(512), 0, st, a);
+  else hipLaunchKernelGGL(k_window_attention<4>, dim3(a.total), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
