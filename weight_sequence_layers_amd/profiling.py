@@ -61,7 +61,11 @@ def source_digest(part: str = "layer") -> str:
 
 
 def _short(name: str) -> str:
-    return re.sub(r"\(.*", "", name).strip()
+    """The kernel's name without its argument list and anonymous-namespace qualifier."""
+    name = name.replace("(anonymous namespace)::", "")
+    if name.endswith(")") and "(" in name:
+        name = name[:name.rindex("(")]
+    return name.strip()
 
 
 def _one(pattern: str, d: str) -> str:
