@@ -344,9 +344,13 @@ struct Gemm {
   // computes from one buffer while step t + 1 lands in the other.  Every LDS access names
   // one of two distinct arrays, which lets the compiler see that the fragment reads never
   // touch the buffer being filled and wait for the loads only at the end of each step.
+  //
+  // krot rotates the K order: the steps cover k0 = krot, krot + BK, ... modulo K (the same
+  // sum in another order).  A caller passing krot != 0 must have K a multiple of BK and one
+  // plane segment.
   __device__ __forceinline__ void run(const Operand* __restrict__ A,
                                       const Operand* __restrict__ B, int m0, int n0, int z,
-                                      int K, char* st0, char* st1) {
+                                      int K, char* st0, char* st1, int krot = 0) {
     const int wm0 = this->wm0();
     const int wn0 = this->wn0();
 
@@ -390,7 +394,9 @@ struct Gemm {
     // The steps are loaded in order; (sg_n, k0_n) is the next one's segment and k offset.
     int sg_n = 0, k0_n = 0;
     auto issue = [&](char* st) __attribute__((always_inline)) {
-      const int sg = sg_n, k0 = k0_n;
+      const int sg = sg_n;
+      int k0 = k0_n + krot;
+      if (k0 >= K) k0 -= K;
       k0_n += BK;
       if (k0_n >= K) {
         k0_n = 0;

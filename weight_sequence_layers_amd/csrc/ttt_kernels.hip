@@ -488,25 +488,49 @@ __global__ __launch_bounds__(WGM * WGN * WGK * 64) void k_ns_poly(NsArgs a) {
   Operand Ao[PL];
 #pragma unroll
   for (int q = 0; q < PL; ++q) Ao[q] = plane_operand(a.ain, q, M);
+  // The linear term b A reads A from its planes (the sum of the planes holds A to about
+  // 16 significant bits with two planes, as the products do).  A(ti, tj) is the A-operand
+  // tile of the K steps k0 in [n0, n0 + T): with K a multiple of the step, the K order is
+  // rotated so that those are the last one or two steps, whose tiles the two stage buffers
+  // still hold when the loop ends, and the epilogue reads A there instead of from memory.
+  constexpr bool LDS_A = T == 128 && WGK == 1 && G::BK == 64;
+  const int ncs = (min(n0 + T, M) - n0 + 63) / 64;   // steps that cover the tile's columns
+  const bool from_lds = LDS_A && M % 64 == 0;
+  const int krot = from_lds ? (n0 + 64 * ncs) % M : 0;
   G g;
   g.zero();
-  g.run(Ao, Ao, m0, n0, zz, M, GEMM_STAGES);
+  g.run(Ao, Ao, m0, n0, zz, M, GEMM_STAGES, krot);
   g.reduce(smem);
-  // the linear term b A reads A from its planes (the sum of the planes holds A to about
-  // 16 significant bits with two planes, as the products do)
+  const int nk = M / 64;   // (from_lds only) steps of the loop; step t used stage t & 1
   const u16* ap = a.ain.base + (int64_t)zz * a.ain.zstride;
   g.for_each4([&](int i, int j, int q, int r, int c) __attribute__((always_inline)) {
     const int R = m0 + r, C = n0 + c;
     float av[4] = {0.f, 0.f, 0.f, 0.f};
     if (R < M && C < M) {
+      if (LDS_A && from_lds) {
+        // column c lies in step nk - ncs + c / 64; row r, k-column c % 64 of its A tile
+        const int t = nk - ncs + c / 64;
+        const char* st = (t & 1) ? gemm_st1_ : gemm_st0_;
+        const int kc = c % 64;
 #pragma unroll
-      for (int pq = 0; pq < PL; ++pq) {
-        const uint2 h = *reinterpret_cast<const uint2*>(ap + pq * a.ain.plane_stride +
-                                                        (int64_t)R * a.ain.ld + C);
-        av[0] += bf2f((u16)(h.x & 0xFFFFu));
-        av[1] += bf2f((u16)(h.x >> 16));
-        av[2] += bf2f((u16)(h.y & 0xFFFFu));
-        av[3] += bf2f((u16)(h.y >> 16));
+        for (int pq = 0; pq < PL; ++pq) {
+          const uint2 h = *reinterpret_cast<const uint2*>(
+              st + pq * G::A_TILE + r * 128 + (((kc >> 3) ^ swz_row<64>(r)) << 4) + (kc & 7) * 2);
+          av[0] += bf2f((u16)(h.x & 0xFFFFu));
+          av[1] += bf2f((u16)(h.x >> 16));
+          av[2] += bf2f((u16)(h.y & 0xFFFFu));
+          av[3] += bf2f((u16)(h.y >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int pq = 0; pq < PL; ++pq) {
+          const uint2 h = *reinterpret_cast<const uint2*>(ap + pq * a.ain.plane_stride +
+                                                          (int64_t)R * a.ain.ld + C);
+          av[0] += bf2f((u16)(h.x & 0xFFFFu));
+          av[1] += bf2f((u16)(h.x >> 16));
+          av[2] += bf2f((u16)(h.y & 0xFFFFu));
+          av[3] += bf2f((u16)(h.y >> 16));
+        }
       }
     }
 #pragma unroll
