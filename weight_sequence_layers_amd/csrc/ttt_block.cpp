@@ -118,8 +118,8 @@ LinearArgs linear_args(const void* x, const void* w, const void* resid, void* y,
   a.tiles_n = (N + 127) / 128;
   a.tiles_m = (int32_t)((rows + 127) / 128);
   a.tiles = (int64_t)a.tiles_m * a.tiles_n;
-  // row tiles per group: 8 measured best or within 5 % of it for every projection of the
-  // block at width 1024 (in 1024 or 4096 features, out 1024 to 4096)
+  // row tiles per group: 8 measured best or within a few percent of it for every projection
+  // of the block at width 1024 (in 1024 or 4096 features, out 1024 to 4096)
   a.group_m = std::min<int32_t>(a.tiles_m, 8);
   return a;
 }

@@ -235,8 +235,9 @@ void k_window_attention(AttnArgs a) {
 // tile fastest: the workgroups resident on an XCD at one time then read a few row panels
 // and a few weight panels, each from its L2 several times, instead of one row panel and
 // a stream through the whole weight matrix (larger than an XCD's L2 for the block's
-// widths).  Groups of 8 row tiles took the block's projections at width 1024 from
-// 700-950 to 900-1040 TFLOP/s.
+// widths).  Groups of 8 row tiles, against one row tile at a time, at the LM block's
+// shapes (warm, interleaved, normally distributed data): q/k/v 809 -> 913, MLP up 690 ->
+// 790, MLP down 866 -> 925 TFLOP/s; the 1024-wide output projection unchanged.
 using GL = Gemm<128, 128, 2, 2, 1, 1, L_ROW, L_ROW, 0, 64, true>;
 
 // GELU(x) = x Phi(x) with Phi(x) = erfc(-x / sqrt 2) / 2, erfc from the Chebyshev fit of
