@@ -88,10 +88,9 @@ def test_window_attention_matches_oracle(B, heads, T, window, mode, qscale):
 
 
 @pytest.mark.parametrize("window", [777, 64])
-def test_window_attention_eight_wave_workgroups(window):
-    """Sliding windows over a launch of at least 512 workgroups of 256 queries run eight
-    waves a workgroup: 4 sequences x 8 heads x 4000 tokens (a ragged last workgroup), whole
-    heads compared."""
+def test_window_attention_many_workgroups(window):
+    """A launch of a thousand workgroups: 4 sequences x 8 heads x 4000 tokens (a ragged last
+    workgroup per head), whole heads compared."""
     B, heads, T = 4, 8, 4000
     qkv, got = _attention_case(B, heads, T, window, "sliding", 31 + window)
     D = heads * 128

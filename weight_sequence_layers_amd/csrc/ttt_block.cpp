@@ -81,12 +81,7 @@ AttnArgs attention_args(const void* q, const void* k, const void* v, int64_t ld,
   a.heads = heads;
   a.window = window;
   a.mode = mode;
-  // sliding windows: eight waves share each step's K and V tiles where the launch keeps two
-  // such workgroups per CU (1.58 -> 1.45 ms at the LM block's shape; per-image windows
-  // measured the same either way and keep four)
-  const int64_t q8 = (T + 255) / 256 * heads * batch;
-  a.aw = (mode == TTT_WINDOW_SLIDING && q8 >= 512) ? 8 : 4;
-  a.qblocks = (int32_t)((T + 32 * a.aw - 1) / (32 * a.aw));
+  a.qblocks = (int32_t)((T + ATT_Q - 1) / ATT_Q);
   a.total = a.qblocks * heads * batch;
   a.scale2 = (float)(1.4426950408889634 / std::sqrt((double)ATT_D));
   return a;

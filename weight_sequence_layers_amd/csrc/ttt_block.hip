@@ -8,7 +8,7 @@ namespace ttt {
 namespace {
 
 // ------------------------------------------------------------------------ window attention
-// One workgroup: 4 or 8 waves, 32 consecutive queries of one (batch, head) per wave.  The
+// One workgroup: 4 waves, 128 consecutive queries of one (batch, head), 32 per wave.  The
 // keys the window allows for any of them are visited in steps of 64; each step's K and V
 // tiles are loaded straight into LDS one step ahead (two stages).  Per step a wave
 //   S^T = K Q^T  on the MFMA with K as the A operand, so each lane holds one query
@@ -47,11 +47,9 @@ __device__ __forceinline__ bf16x8 read_vt_frag(const char* tile, int dim_base, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// AW waves per workgroup (32 AW queries): the K and V tiles of a step serve all of them.
-template <int AW>
-__global__ __launch_bounds__(64 * AW) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void k_window_attention(AttnArgs a) {
-  constexpr int NT = 64 * AW, QB = 32 * AW;
+  constexpr int NT = 256, QB = ATT_Q;
   __shared__ __attribute__((aligned(1024))) char st0[ATT_STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[ATT_STAGE];
   const int id = xcd_block(blockIdx.x, a.total);
@@ -424,8 +422,7 @@ __global__ __launch_bounds__(256) void k_blk_merge(HeadMergeArgs a) {
 
 hipError_t launch_window_attention(const AttnArgs& a, hipStream_t st) {
   if (a.total == 0) return hipSuccess;
-  if (a.aw == 8) hipLaunchKernelGGL(k_window_attention<8>, dim3(a.total), dim3(512), 0, st, a);
-  else hipLaunchKernelGGL(k_window_attention<4>, dim3(a.total), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_window_attention, dim3(a.total), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

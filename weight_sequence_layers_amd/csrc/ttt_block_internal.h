@@ -19,7 +19,6 @@ struct AttnArgs {
   u16* out;
   int64_t ld, ldo;
   int32_t T, heads, window, mode, qblocks, total;
-  int32_t aw;     // waves per workgroup (4 or 8): a workgroup takes 32 aw queries
   float scale2;   // log2(e) / sqrt(ATT_D)
 };
 
