@@ -27,23 +27,26 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 # stage name -> pattern of the kernels that implement it
+# (stage, kernels, companions): each launch the library brackets for a stage runs one of the
+# `kernels` (several patterns are alternative instantiations, e.g. by plane count) and any
+# of the `companions` (kernels launched inside the same bracket, e.g. a split-K sum)
 STAGE_KERNELS = [
     # k_front<BM, BN, WGM, WGN, FW, MODE, BK>: MODE 0 applies, 1 and 2 take gradients
-    ("front_q", r"k_front<(\d+, ){5}0, \d+>$"),
-    ("front_k", r"k_front<(\d+, ){5}[12], \d+>$"),
-    ("out", r"k_out<.*, 0>$"),
-    ("mse", r"k_out<.*, [12]>$"),
-    ("contract", r"k_contract(_sum)?<"),
-    ("ns_gram", r"k_ns_gram<"),
-    ("ns_poly", r"k_ns_poly<"),
-    ("ns_update", r"k_ns_update<"),
-    ("ns_small", r"k_ns_small<"),
-    ("renorm", r"k_renorm"),
-    ("split", r"k_split"),
-    ("resident", r"k_small_gelu<"),
-    ("dq", r"k_dq<|k_rowgemm<"),
-    ("tfront", r"k_tfront<|k_eta_sum"),
-    ("ns_bwd", r"k_gemm2<|k_ns_fin"),
+    ("front_q", r"k_front<(\d+, ){5}0, \d+>$", None),
+    ("front_k", r"k_front<(\d+, ){5}[12], \d+>$", None),
+    ("out", r"k_out<.*, 0>$", None),
+    ("mse", r"k_out<.*, [12]>$", None),
+    ("contract", r"k_contract<", r"k_contract_sum<"),
+    ("ns_gram", r"k_ns_gram<", None),
+    ("ns_poly", r"k_ns_poly<", None),
+    ("ns_update", r"k_ns_update<", None),
+    ("ns_small", r"k_ns_small<", None),
+    ("renorm", r"k_renorm", None),
+    ("split", r"ttt::k_split", None),
+    ("resident", r"k_small_gelu<", None),
+    ("dq", r"k_dq<|k_rowgemm<", None),
+    ("tfront", r"k_tfront<", r"k_eta_sum"),
+    ("ns_bwd", r"k_gemm2<", r"k_ns_fin"),
 ]
 
 
@@ -116,21 +119,25 @@ def traffic_md(fetch_dir: str, write_dir: str, workload: str, fetch_cmd: str,
            f"{fetch[calib[0]][1]:.0f} KiB on FETCH_SIZE and {write[calib[0]][1]:.0f} KiB on "
            f"WRITE_SIZE, so fetch values are scaled by {f_scale:.4f} and write values by "
            f"{w_scale:.4f}.", "", f"source digest: {source_digest()}", f"block source digest: {source_digest('block')}", "",
-           "Each counter is summed over its instances per dispatch and averaged over "
-           "dispatches; a stage served by several kernels sums them. The last column is "
-           "scaled fetch + write in bytes.", "",
+           "Each counter is summed over its instances per dispatch. Per launch of a stage: "
+           "the bytes of all its dispatches (the alternative instantiations that serve it "
+           "and the companion kernels launched with it) over the number of its launches "
+           "(the dispatches of the alternatives). The last column is scaled fetch + write "
+           "in bytes.", "",
            "| stage | kernels | dispatches | fetch KiB (raw) | write KiB (raw) | HBM bytes per launch |",
            "|---|---|---|---|---|---|"]
-    for stage, pat in STAGE_KERNELS:
+    for stage, pat, comp in STAGE_KERNELS:
         ks = [k for k in fetch if re.search(pat, k)]
         if not ks:
             continue
-        f = sum(fetch[k][1] for k in ks)
-        w = sum(write.get(k, (0, 0.0))[1] for k in ks)
-        n = sum(fetch[k][0] for k in ks)
+        cs = [k for k in fetch if comp and re.search(comp, k)]
+        n = sum(fetch[k][0] for k in ks)   # launches of the stage
+        # KiB over every dispatch of the stage's kernels, per launch
+        f = sum(fetch[k][0] * fetch[k][1] for k in ks + cs) / n
+        w = sum(write.get(k, (0, 0.0))[0] * write.get(k, (0, 0.0))[1] for k in ks + cs) / n
         total = 1024 * (f * f_scale + w * w_scale)
-        out.append(f"| {stage} | {', '.join('`' + k + '`' for k in ks)} | {n} | {f:.0f} | "
-                   f"{w:.0f} | {total:.0f} |")
+        out.append(f"| {stage} | {', '.join('`' + k + '`' for k in ks + cs)} | {n} | "
+                   f"{f:.0f} | {w:.0f} | {total:.0f} |")
     return "\n".join(out) + "\n"
 
 
