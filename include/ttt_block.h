@@ -44,7 +44,8 @@ typedef enum { TTT_WINDOW_SLIDING = 0, TTT_WINDOW_BLOCK = 1 } ttt_window_mode;
  * over the tokens j the window lets t see.  Element e of head h of token t of batch b is
  * at  base + ((b * seq_len + t) * ld + h * 128 + e)  for q, k and v (bf16), and at
  * out + (b * seq_len + t) * ld_out + h * 128 + e  for the output (bf16), so q, k and v
- * may be thirds of one projection's output rows.  Limits: batch, heads >= 1; window >= 1;
+ * may be thirds of one projection's output rows; out may not overlap them (TTT_E_CONFIG).
+ * Limits: batch, heads >= 1; window >= 1;
  * 0 <= seq_len < 2^31; ld, ld_out >= heads * 128 and multiples of 8; ld < 2^24.  The
  * scores and their softmax are fp32; the probabilities are rounded to bf16 for the
  * product with v, and the normaliser sums the rounded values, so each output is a convex

@@ -222,6 +222,10 @@ def test_block_calls_reject_on_the_host():
     assert L.ttt_window_attention(None, p, p, 384, p, 128, 1, 1, 64, 8, 0, None) == 1
     assert L.ttt_window_attention(p + 2, p, p, 384, p, 128, 1, 1, 64, 8, 0, None) == 9
     assert L.ttt_window_attention(None, None, None, 384, None, 128, 1, 1, 0, 8, 0, None) == 0
+    # the output inside the inputs' rows (in place over q, or over v's third of the rows)
+    assert L.ttt_window_attention(p, p + 256, p + 512, 384, p, 128, 1, 1, 64, 8, 0, None) == 4
+    assert L.ttt_window_attention(p, p + 256, p + 512, 384, p + 512, 384, 1, 1, 64, 8, 0,
+                                  None) == 4
     # projections: feature counts multiples of 8; epilogue; residual pointer; overlap
     assert L.ttt_linear(p, p, None, p, 4, 12, 8, 0, None) == 2
     assert L.ttt_linear(p, p, None, p, 4, 8, 12, 0, None) == 2

@@ -227,6 +227,7 @@ def _rel(a, b):
     (2, 192, 256, 2, 64, 48, "sliding", "apply_then_update"),
     (1, 256, 256, 1, 128, 100, "sliding", "apply_then_update"),
     (1, 200, 384, 3, 200, 50, "block", "update_then_apply"),
+    (1, 256, 768, 1, 256, 100, "block", "update_then_apply"),
 ])
 def test_block_matches_oracle(B, T, dim, heads, chunk, window, mode, order):
     tcfg, F, inp, w0, bc = _block_case(B, T, dim, heads, chunk, window, mode, order, 77 + T)

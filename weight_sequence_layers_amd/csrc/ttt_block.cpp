@@ -198,6 +198,14 @@ ttt_status ttt_window_attention(const void* q, const void* k, const void* v, int
   BLK_TRY(need(k, "k"));
   BLK_TRY(need(v, "v"));
   BLK_TRY(need(out, "out"));
+  // every workgroup reads keys and values of other workgroups' queries: the output may not
+  // share memory with the inputs
+  const size_t rows = (size_t)batch * (size_t)seq_len;
+  const size_t in_bytes = ((rows - 1) * (size_t)ld + (size_t)heads * ATT_D) * 2;
+  const size_t out_bytes = ((rows - 1) * (size_t)ld_out + (size_t)heads * ATT_D) * 2;
+  if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+      overlaps(out, out_bytes, v, in_bytes))
+    return failf(TTT_E_CONFIG, "out overlaps q, k or v");
   const AttnArgs a = attention_args(q, k, v, ld, out, ld_out, batch, heads, seq_len, window,
                                     window_mode);
   BLK_HIP(launch_window_attention(a, static_cast<hipStream_t>(stream)));
