@@ -855,7 +855,7 @@ ttt_status ns_backward(ttt_state* s, hipStream_t st) {
     g.alpha = 1.f; g.beta = 0.f;
     g.cout = b.t32; g.pout = apb(b.tp);
     g.spart = first ? s->part : nullptr; g.nspart = s->contract_tiles; g.eps = eps;
-    STAGED(TTT_STAGE_NS_BWD, launch_gemm2(g, false, st));
+    STAGED(TTT_STAGE_NS_BWD, launch_gemm2(g, false, st, true));   // T is symmetric
     // S = b T + c (T A + A T) (A, T symmetric: rows serve as columns); iteration 0 takes
     // the factor s of X0 = s G here, so that the next product can use G's planes
     Gemm2Args h{};
@@ -865,7 +865,7 @@ ttt_status ns_backward(ttt_state* s, hipStream_t st) {
     h.alpha = cc; h.beta = cb; h.cin = b.t32;
     h.pout = apb(b.sp);
     h.spart = first ? s->part : nullptr; h.nspart = s->contract_tiles; h.eps = eps;
-    STAGED(TTT_STAGE_NS_BWD, launch_gemm2(h, false, st));
+    STAGED(TTT_STAGE_NS_BWD, launch_gemm2(h, false, st, true));   // so is S
     // dX_prev = B' dX + S X, the X-side operands read by columns (K = M)
     Gemm2Args u{};
     u.M = M; u.N = N; u.K = M; u.Z = Z;

@@ -209,15 +209,25 @@ __global__ __launch_bounds__(256) void k_step_bwd(StepBwdArgs a) {
 // ------------------------------------------------------------------------ Newton-Schulz
 // out = sc (alpha (A0 B0^T + A1 B1^T) + beta cin), sc the optional per-matrix scale; B
 // operands read by rows (LBM 0) or columns.
-template <int BM, int BN, int WGM, int WGN, int LBM>
+// SYM: the output is symmetric (M = N): only the upper tiles run, and each off-diagonal
+// tile's planes are stored with their mirror (the fp32 output, read back only where the
+// upper tiles lie, is stored as computed).
+template <int BM, int BN, int WGM, int WGN, int LBM, bool SYM = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm2(Gemm2Args a) {
   using G = Gemm<BM, BN, WGM, WGN, 2, 2, 0, LBM, 0, 32, true, 1, -1, true>;
-  GEMM_LDS(G);
+  static_assert(!SYM || BM == BN, "symmetric outputs take square tiles");
+  GEMM_LDS_EPI(G, (SYM ? store_lds_bytes<G, TILE_BOTH, 1>() : G::STORE_LDS));
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int zz = lid / a.tiles, tile = lid % a.tiles;
   const int M = a.M, N = a.N;
-  const int m0 = (tile / a.tiles_n) * BM;
-  const int n0 = (tile % a.tiles_n) * BN;
+  int ti, tj;
+  if (SYM) tri_tile(tile, (M + BM - 1) / BM, ti, tj);
+  else {
+    ti = tile / a.tiles_n;
+    tj = tile % a.tiles_n;
+  }
+  const int m0 = ti * BM;
+  const int n0 = tj * BN;
   G g;
   g.zero();
   g.run(a.a, a.b, m0, n0, zz, a.K, GEMM_STAGES);
@@ -252,7 +262,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm2(Gemm2Args a) {
   });
   if (a.pout.np > 0) {
     const int rl = min(BM, M - m0), cl = min(BN, N - n0);
-    store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.pout, zz, m0, n0, rl, cl);
+    if (SYM && ti != tj)
+      store_planes<G, TILE_BOTH, 1>(g.acc[0], smem, a.pout, zz, m0, n0, rl, cl);
+    else
+      store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.pout, zz, m0, n0, rl, cl);
   }
   if (a.gpart) {
     const float t = block_sum(gs, reinterpret_cast<float*>(smem));
@@ -366,14 +379,16 @@ hipError_t launch_step_bwd(const StepBwdArgs& a, hipStream_t s) {
 
 int gemm2_tiles(int M, int N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
-hipError_t launch_gemm2(const Gemm2Args& a0, bool bcols, hipStream_t s) {
+hipError_t launch_gemm2(const Gemm2Args& a0, bool bcols, hipStream_t s, bool sym) {
   constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4;
   Gemm2Args a = a0;
+  if (sym && (a.M != a.N || bcols || a.gref || a.gpart)) return hipErrorInvalidValue;
   a.tiles_n = (a.N + BN - 1) / BN;
-  a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
+  a.tiles = sym ? ns_tri_tiles(a.M, BM) : ((a.M + BM - 1) / BM) * a.tiles_n;
   if (a.tiles == 0 || a.Z == 0) return hipSuccess;
   const dim3 grid(a.tiles * a.Z), block(WGM * WGN * 64);
-  if (bcols) hipLaunchKernelGGL((k_gemm2<BM, BN, WGM, WGN, 0b11>), grid, block, 0, s, a);
+  if (sym) hipLaunchKernelGGL((k_gemm2<BM, BN, WGM, WGN, 0, true>), grid, block, 0, s, a);
+  else if (bcols) hipLaunchKernelGGL((k_gemm2<BM, BN, WGM, WGN, 0b11>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((k_gemm2<BM, BN, WGM, WGN, 0>), grid, block, 0, s, a);
   return hipGetLastError();
 }

@@ -628,6 +628,16 @@ __device__ __forceinline__ int xcd_block(int id, int total) {
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
+// Upper tile t (row-major over ti <= tj) of an nt x nt grid of tiles.
+__device__ __forceinline__ void tri_tile(int t, int nt, int& ti, int& tj) {
+  ti = 0;
+  while (t >= nt - ti) {
+    t -= nt - ti;
+    ++ti;
+  }
+  tj = ti + t;
+}
+
 // ------------------------------------------------------------------------ tile stores
 // Write one block tile of fp32 values (held in the MFMA accumulator layout of gemm G) as
 // bf16 planes through LDS, so that global stores are 16-byte vectors along the buffer's

@@ -269,7 +269,9 @@ hipError_t launch_eta_sum(const EtaSumArgs& a, int Z, hipStream_t s);
 hipError_t launch_rowgemm(const DqArgs& a, int np, int Z, hipStream_t s);
 hipError_t launch_step_bwd(const StepBwdArgs& a, hipStream_t s);
 // bcols: B operands read by columns (the dX update) or by rows (T and S)
-hipError_t launch_gemm2(const Gemm2Args& a, bool bcols, hipStream_t s);
+// sym: a symmetric output (M = N, no gref / gpart, bcols false): upper tiles only, each
+// off-diagonal one's planes stored with their mirror
+hipError_t launch_gemm2(const Gemm2Args& a, bool bcols, hipStream_t s, bool sym = false);
 hipError_t launch_ns_fin(const NsFinArgs& a, int Z, hipStream_t s);
 hipError_t launch_add3(const Add3Args& a, hipStream_t s);
 int gemm2_tiles(int M, int N);

@@ -416,14 +416,6 @@ __device__ __forceinline__ float ns_scale(const NsArgs& a, int zz) {
   return 1.f / (sqrtf(t) + a.eps);
 }
 
-__device__ __forceinline__ void tri_tile(int t, int nt, int& ti, int& tj) {
-  ti = 0;
-  while (t >= nt - ti) {
-    t -= nt - ti;
-    ++ti;
-  }
-  tj = ti + t;
-}
 
 // Store a tile of a symmetric M x M matrix computed at tile (ti, tj), ti <= tj, as planes
 // of the full matrix (the symmetrised diagonal tile, or an upper tile and its mirror), NP
