@@ -191,6 +191,7 @@ struct ttt_state {
   int* health = nullptr;
   float* neg1 = nullptr;  // [sb] of -1: the apply backward's eta
   int contract_tiles = 0;
+  int part_n = 0;         // sum-of-squares parts per matrix: contract_tiles x CONTRACT_SUM_SUB
   bool resident = false;  // the device-resident chunk loop serves this state (Wpl unused)
   // backward through an update: workspace allocated by the first ttt_chunk_backward call
   struct Bwd {
@@ -270,7 +271,7 @@ size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
   }
   size_t oG = C.take<float>(D.nm * P * d * n);
   const int ctiles = (int)(((d + CONTRACT_BM - 1) / CONTRACT_BM) * ((n + CONTRACT_BN - 1) / CONTRACT_BN));
-  size_t opart = C.take<float>(D.nm * P * ctiles);
+  size_t opart = C.take<float>((int64_t)D.nm * P * ctiles * CONTRACT_SUM_SUB);
   const int ksp = contract_split_max(ctiles, (int)(D.nm * P));
   size_t ogp = ksp > 1 ? C.take<float>(ksp * D.nm * P * d * n) : 0;
   size_t ox[2] = {0, 0}, oa = 0, ob = 0;
@@ -312,6 +313,7 @@ size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
     s->G = F(oG);
     s->part = F(opart);
     s->contract_tiles = ctiles;
+    s->part_n = ctiles * CONTRACT_SUM_SUB;
     s->ksplit = ksp;
     s->gpart = ksp > 1 ? F(ogp) : nullptr;
     if (c.ns_steps > 0) {
@@ -457,7 +459,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
     cg.U = U + (int64_t)m0 * P * d * D.n;
     if (ca.mom) cg.mom = ca.mom + (int64_t)m0 * P * d * D.n;
     if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
-    cg.part = s->part + (int64_t)m0 * P * s->contract_tiles;
+    cg.part = s->part + (int64_t)m0 * P * s->part_n;
     cg.tr_mask = ca.tr_mask >> m0;
     STAGED(TTT_STAGE_CONTRACT, launch_contract(cg, m1 - m0, st));
     m0 = m1;
@@ -604,7 +606,7 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st, u16* const* keep = nullpt
     NsArgs a{};
     a.Z = Z; a.M = M; a.N = N; a.P = D.P;
     a.coef_a = 3.4445f; a.coef_b = -4.7750f; a.coef_c = 2.0315f;
-    a.part = s->part; a.nparts = s->contract_tiles;
+    a.part = s->part; a.nparts = s->part_n;
     a.eps = 1e-7f;
     a.steps = steps;
     a.one = D.ns_one;
@@ -622,7 +624,7 @@ ttt_status newton_schulz(ttt_state* s, hipStream_t st, u16* const* keep = nullpt
     a.pl = pk;
     a.fold = pk == D.np;   // a I folded into B' where B' holds X's precision
     a.coef_a = 3.4445f; a.coef_b = -4.7750f; a.coef_c = 2.0315f;
-    a.part = s->part; a.nparts = s->contract_tiles; a.first = it == 0; a.last = it == steps - 1;
+    a.part = s->part; a.nparts = s->part_n; a.first = it == 0; a.last = it == steps - 1;
     a.eps = 1e-7f;
     a.xin = pbuf(iterate(it), D.np, (int64_t)Z * M * N, (int64_t)M * N, N);
     a.aout = pbuf(s->apl, pk, (int64_t)Z * M * M, (int64_t)M * M, M);
@@ -839,7 +841,7 @@ ttt_status ns_backward(ttt_state* s, hipStream_t st) {
     NsArgs a{};
     a.Z = Z; a.M = M; a.N = N; a.P = D.P; a.pl = np; a.fold = 1;
     a.coef_a = ca; a.coef_b = cb; a.coef_c = cc;
-    a.part = s->part; a.nparts = s->contract_tiles; a.first = first; a.last = 0; a.eps = eps;
+    a.part = s->part; a.nparts = s->part_n; a.first = first; a.last = 0; a.eps = eps;
     a.xin = xpb(b.xit[it]);
     a.aout = apb(s->apl);
     STAGED(TTT_STAGE_NS_GRAM, launch_ns_gram(a, st));
@@ -854,7 +856,7 @@ ttt_status ns_backward(ttt_state* s, hipStream_t st) {
     g.a[0] = dX; g.b[0] = X; g.a[1] = X; g.b[1] = dX;
     g.alpha = 1.f; g.beta = 0.f;
     g.cout = b.t32; g.pout = apb(b.tp);
-    g.spart = first ? s->part : nullptr; g.nspart = s->contract_tiles; g.eps = eps;
+    g.spart = first ? s->part : nullptr; g.nspart = s->part_n; g.eps = eps;
     STAGED(TTT_STAGE_NS_BWD, launch_gemm2(g, false, st, true));   // T is symmetric
     // S = b T + c (T A + A T) (A, T symmetric: rows serve as columns); iteration 0 takes
     // the factor s of X0 = s G here, so that the next product can use G's planes
@@ -864,7 +866,7 @@ ttt_status ns_backward(ttt_state* s, hipStream_t st) {
     h.a[1] = h.b[0]; h.b[1] = h.a[0];
     h.alpha = cc; h.beta = cb; h.cin = b.t32;
     h.pout = apb(b.sp);
-    h.spart = first ? s->part : nullptr; h.nspart = s->contract_tiles; h.eps = eps;
+    h.spart = first ? s->part : nullptr; h.nspart = s->part_n; h.eps = eps;
     STAGED(TTT_STAGE_NS_BWD, launch_gemm2(h, false, st, true));   // so is S
     // dX_prev = B' dX + S X, the X-side operands read by columns (K = M)
     Gemm2Args u{};
@@ -881,7 +883,7 @@ ttt_status ns_backward(ttt_state* s, hipStream_t st) {
   }
   NsFinArgs f{};
   f.G = b.g32; f.dX = dx32;
-  f.ss_part = s->part; f.nss = s->contract_tiles;
+  f.ss_part = s->part; f.nss = s->part_n;
   f.dot_part = b.dotpart; f.ndot = gemm2_tiles(M, N);
   f.per = (int64_t)M * N; f.eps = eps;
   f.dG = b.dg32;

@@ -303,6 +303,11 @@ ttt_status sequence_in_workspace(const ttt_config* cfg, float* w, const void* q,
 // tile sizes used by the contraction and Newton-Schulz stages (the host sizes buffers)
 constexpr int CONTRACT_BM = 128, CONTRACT_BN = 128;
 constexpr int CONTRACT_SPLIT_MAX = 16;   // token ranges of one contraction at most
+// Parts of a contraction tile's sum of squares (the Newton-Schulz input's Frobenius norm):
+// one per band of 16 rows, so that a token-split contraction's second pass spreads a tile
+// over that many workgroups.  An unsplit contraction stores its tile's sum in the first
+// part and zeros in the others, so a reader adding all parts in order gets the same value.
+constexpr int CONTRACT_SUM_SUB = 8;
 int ns_tri_tiles(int M, int tile);
 
 }  // namespace ttt

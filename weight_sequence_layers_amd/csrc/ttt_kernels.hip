@@ -311,29 +311,35 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
     const int rl = min(BM, M - m0), cl = min(BN, N - n0);
     store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.x, zz, m0, n0, rl, cl);
     const float t = block_sum(ss, reinterpret_cast<float*>(smem));
-    if (threadIdx.x == 0) a.part[(int64_t)zz * a.tiles + tile] = t;
+    if (threadIdx.x < CONTRACT_SUM_SUB)
+      a.part[((int64_t)zz * a.tiles + tile) * CONTRACT_SUM_SUB + threadIdx.x] =
+          threadIdx.x == 0 ? t : 0.f;
   }
 }
 
-// Second pass of a token-split contraction: one workgroup per output tile adds the
-// ksplit partial tiles and applies the same epilogue as k_contract (the running sum in G,
-// or the X0 planes with the tile's sum of squares, or U).  Each thread takes runs of 8
-// columns (N is a multiple of 16).
+// Second pass of a token-split contraction: the ksplit partial tiles added in split order,
+// then the same epilogue as k_contract (the running sum in G, or the X0 planes with the
+// sum of squares, or U).  A tile is spread over CONTRACT_SUM_SUB workgroups of 256
+// threads, one per band of 16 rows; each thread takes one run of 8 columns (N is a
+// multiple of 16) and each band stores its own part of the sum of squares.
+constexpr int CONTRACT_SUM_THREADS = 256;
+
 template <int BM, int BN>
-__global__ __launch_bounds__(1024) void k_contract_sum(ContractArgs a) {
-  __shared__ float red[16];
+__global__ __launch_bounds__(CONTRACT_SUM_THREADS) void k_contract_sum(ContractArgs a) {
+  constexpr int RUNS = BN / 8, ROWS = CONTRACT_SUM_THREADS / RUNS;
+  static_assert(BM == ROWS * CONTRACT_SUM_SUB, "one band of ROWS rows per part");
+  __shared__ float red[CONTRACT_SUM_THREADS / 64];
   const int lid = xcd_block(blockIdx.x, gridDim.x);
-  const int zz = lid / a.tiles, tile = lid % a.tiles;
+  const int band = lid % CONTRACT_SUM_SUB, tz = lid / CONTRACT_SUM_SUB;
+  const int zz = tz / a.tiles, tile = tz % a.tiles;
   const int m = zz / a.P;
-  const int m0 = (tile / a.tiles_n) * BM;
-  const int n0 = (tile % a.tiles_n) * BN;
   const int M = a.M, N = a.N;
+  const int row = (tile / a.tiles_n) * BM + band * ROWS + (int)threadIdx.x / RUNS;
+  const int col = (tile % a.tiles_n) * BN + ((int)threadIdx.x % RUNS) * 8;
   const int64_t base = (int64_t)zz * M * N;
   const int tr = (a.tr_mask >> m) & 1;
   float ss = 0.f;
-  for (int gi = threadIdx.x; gi < BM * BN / 8; gi += blockDim.x) {
-    const int row = m0 + gi / (BN / 8), col = n0 + (gi % (BN / 8)) * 8;
-    if (row >= M || col >= N) continue;
+  if (row < M && col < N) {
     const int64_t off = base + (int64_t)row * N + col;
     float x[8];
 #pragma unroll
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(1024) void k_contract_sum(ContractArgs a) {
   }
   if (a.last && a.muon) {
     const float t = block_sum(ss, red);
-    if (threadIdx.x == 0) a.part[(int64_t)zz * a.tiles + tile] = t;
+    if (threadIdx.x == 0) a.part[(int64_t)tz * CONTRACT_SUM_SUB + band] = t;
   }
 }
 
@@ -860,7 +866,7 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 }
 
 // Token ranges: enough for about two workgroups per CU (256 CUs) when the output tiles
-// alone are fewer, at most 8, each range at least 256 tokens.
+// alone are fewer, at most CONTRACT_SPLIT_MAX, each range at least 256 tokens.
 constexpr int CONTRACT_SLOTS = 512, CONTRACT_RANGE_MIN = 256;
 
 int contract_split_max(int tiles, int nz) {
@@ -892,7 +898,8 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   hipLaunchKernelGGL(kern, dim3(a.tiles * a.nz * a.ksplit), dim3(G::NT), 0, s, a);
   if (a.ksplit > 1) {
     auto sum = k_contract_sum<BM, BN>;
-    hipLaunchKernelGGL(sum, dim3(a.tiles * a.nz), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(sum, dim3(a.tiles * a.nz * CONTRACT_SUM_SUB), dim3(CONTRACT_SUM_THREADS),
+                       0, s, a);
   }
   return hipGetLastError();
 }
