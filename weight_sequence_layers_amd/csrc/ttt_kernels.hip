@@ -821,10 +821,23 @@ static hipError_t front_fm(const FrontArgs& a, int Z, hipStream_t s) {
   return front_t<128, 128, 2, 4, FW, MODE, 32>(a, Z, s);
 }
 
+// A launch with fewer 128 x 128 tiles than CUs (few tokens, or a narrow hidden layer) takes
+// 64 x 64 tiles on four waves: four times the workgroups, each with a quarter of the tile's
+// loads per K step and of its epilogue's stores.
+constexpr int SMALL_TILE_BELOW = 256;
+static bool small_tiles(int rows, int cols, int Z) {
+  return (int64_t)((rows + 127) / 128) * ((cols + 127) / 128) * Z < SMALL_TILE_BELOW;
+}
+
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s) {
   if (fw == FW_SWIGLU) {
-    if (mode == FRONT_Q) return front_fm<FW_SWIGLU, FRONT_Q>(a, Z, s);
-    if (mode == FRONT_K_DOT) return front_t<128, 128, 2, 4, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
+    const bool small = small_tiles(a.nrows, a.N, Z);
+    if (mode == FRONT_Q)
+      return small ? front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_Q, 32>(a, Z, s)
+                   : front_fm<FW_SWIGLU, FRONT_Q>(a, Z, s);
+    if (mode == FRONT_K_DOT)
+      return small ? front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_K_DOT>(a, Z, s)
+                   : front_t<128, 128, 2, 4, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
     return front_fm<FW_SWIGLU, FRONT_K_MSE>(a, Z, s);
   }
   if (mode == FRONT_Q) return front_fm<FW_GELU, FRONT_Q>(a, Z, s);
@@ -832,12 +845,11 @@ hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t
   return front_fm<FW_GELU, FRONT_K_MSE>(a, Z, s);
 }
 
-template <int MODE>
+template <int MODE, int BM = 128, int BN = 128, int WGM = 2, int WGN = 4>
 static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
-  using G = Gemm<BM, BN, 2, 4, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
+  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
   OutArgs a = a0;
-  auto kern = k_out<BM, BN, 2, 4, MODE>;
+  auto kern = k_out<BM, BN, WGM, WGN, MODE>;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
@@ -860,7 +872,8 @@ hipError_t launch_dq(const DqArgs& a0, int np, int Z, hipStream_t s) {
 }
 
 hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
-  if (mode == OUT_Q) return out_m<OUT_Q>(a, Z, s);
+  if (mode == OUT_Q)
+    return small_tiles(a.nrows, a.N, Z) ? out_m<OUT_Q, 64, 64, 2, 2>(a, Z, s) : out_m<OUT_Q>(a, Z, s);
   if (mode == OUT_K_MSE) return out_m<OUT_K_MSE>(a, Z, s);
   return out_m<DH_MSE>(a, Z, s);
 }
@@ -879,14 +892,17 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
   using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;   // block size (the same for every instance)
   ContractArgs a = a0;
-  // one bf16 plane on one side and 2 or 3 on the other: plane-resident (NA + NB tiles a
-  // K step instead of two per plane product); else plane pairs as K segments
+  // more than one bf16 plane on either side: plane-resident (NA + NB tiles a K step
+  // instead of two per plane product, one pass over the K range instead of one per pair);
+  // one plane on both sides is a single product
   const int pa = a.a[0].planes, pb = a.b[0].planes;
   auto kern = k_contract<BM, BN, 2, 4, 0, 0>;
   if (pa == 1 && pb == 2) kern = k_contract<BM, BN, 2, 4, 1, 2>;
   else if (pa == 1 && pb == 3) kern = k_contract<BM, BN, 2, 4, 1, 3>;
   else if (pa == 2 && pb == 1) kern = k_contract<BM, BN, 2, 4, 2, 1>;
   else if (pa == 3 && pb == 1) kern = k_contract<BM, BN, 2, 4, 3, 1>;
+  else if (pa == 2 && pb == 2) kern = k_contract<BM, BN, 2, 4, 2, 2>;
+  else if (pa == 3 && pb == 3) kern = k_contract<BM, BN, 2, 4, 3, 3>;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   a.nz = nm * a.P;
