@@ -56,14 +56,34 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Store the fp32 tile value x at (r, c) as `np` planes into planes[q][r * stride + c].
-__device__ __forceinline__ void put_planes(u16* planes, int pstride, int np, int stride, int r,
-                                           int c, float x) {
-  u16 h[3];
-  split_planes(x, np, h);
+// Four consecutive values of one row as `np` planes: planes[q][off .. off + 3], one 8-byte
+// LDS store per plane (off is a multiple of 4).
+__device__ __forceinline__ void put_run(u16* planes, int pstride, int np, int off,
+                                        const float (&x)[4]) {
+  u16 h[4][3];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split_planes(x[e], np, h[e]);
 #pragma unroll
   for (int q = 0; q < 3; ++q)
-    if (q < np) planes[q * pstride + r * stride + c] = h[q];
+    if (q < np)
+      *reinterpret_cast<uint2*>(planes + q * pstride + off) =
+          make_uint2(h[0][q] | ((uint32_t)h[1][q] << 16), h[2][q] | ((uint32_t)h[3][q] << 16));
+}
+
+// The sum of the first np planes of four consecutive values planes[q][off .. off + 3].
+__device__ __forceinline__ void sum_run(const u16* planes, int pstride, int np, int off,
+                                        float (&x)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = 0.f;
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+    if (q < np) {
+      const uint2 w = *reinterpret_cast<const uint2*>(planes + q * pstride + off);
+      x[0] += bf2f((u16)(w.x & 0xffff));
+      x[1] += bf2f((u16)(w.x >> 16));
+      x[2] += bf2f((u16)(w.y & 0xffff));
+      x[3] += bf2f((u16)(w.y >> 16));
+    }
 }
 
 // Partial 32 x 32 tile (ti, tj) of an A B^T-shaped product, both operands read as rows,
@@ -83,40 +103,52 @@ __device__ __forceinline__ f32x16 prod_rows(const u16* A, int apst, int astr, co
   return acc;
 }
 
-// Waves 4..7 hand their partial tiles (NT of them) to waves 0..3 through red (run j of four
-// values of wave tile t at red + ((t 4 NT + j) 64 + lane) 4: consecutive lanes, consecutive
-// 16 bytes); returns with the sums in the accumulators of waves 0..3.  w is wave-uniform.
-// Contains barriers: call from every thread.
+// Waves w and w ^ 4 hold the two K halves of the same NT tiles.  Each keeps half of every
+// tile's accumulator (wave w >> 2 = h keeps elements 8 h .. 8 h + 7, the tile's rows
+// 16 h .. 16 h + 15 in the accumulator layout) and hands the other half to its partner
+// through red (run j of tile u of wave w at red + ((w 2 NT + 2 u + j) 64 + lane) 4:
+// consecutive lanes, consecutive 16 bytes).  On return own[u] holds the full sums of the
+// kept half, the K half 0 partial plus the K half 1 partial.  w is wave-uniform.  Contains
+// a barrier: call from every thread.
 template <int NT>
-__device__ __forceinline__ void reduce_halves(f32x16 (&acc)[NT], float* red, int w, int lane) {
-  float* slot = red + ((w & 3) * 4 * NT * 64 + lane) * 4;
-  if (w >= 4) {
+__device__ __forceinline__ void exchange_halves(const f32x16 (&acc)[NT], float (&own)[NT][8],
+                                                float* red, int w, int lane) {
+  const int kh = w >> 2;
 #pragma unroll
-    for (int u = 0; u < NT; ++u)
+  for (int u = 0; u < NT; ++u)
 #pragma unroll
-      for (int v = 0; v < 16; v += 4)
-        *reinterpret_cast<f32x4*>(slot + (4 * u + v / 4) * 256) =
-            f32x4{acc[u][v], acc[u][v + 1], acc[u][v + 2], acc[u][v + 3]};
-  }
-  __syncthreads();
-  if (w < 4) {
+    for (int j = 0; j < 2; ++j) {
+      f32x4 out;
 #pragma unroll
-    for (int u = 0; u < NT; ++u)
-#pragma unroll
-      for (int v = 0; v < 16; v += 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(slot + (4 * u + v / 4) * 256);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[u][v + e] += x[e];
+      for (int e = 0; e < 4; ++e) {
+        const float lo = acc[u][4 * j + e], hi = acc[u][8 + 4 * j + e];
+        own[u][4 * j + e] = kh ? hi : lo;
+        out[e] = kh ? lo : hi;
       }
-  }
+      *reinterpret_cast<f32x4*>(red + ((w * 2 * NT + 2 * u + j) * 64 + lane) * 4) = out;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < NT; ++u)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f32x4 x =
+          *reinterpret_cast<const f32x4*>(red + (((w ^ 4) * 2 * NT + 2 * u + j) * 64 + lane) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) own[u][4 * j + e] += x[e];
+    }
 }
 
-// One iteration with PK product planes (PK = NP folds a I into B).  Eight waves: wave w
-// computes tile w & 3 of each product over half of its K range (w >> 2 picks the half),
-// and waves 0..3 finish the tiles.  No element needs a bounds check in LDS: X is zero
-// outside [M][N], so A is zero outside [M][M], B outside [M][M] but for a on the padded
-// diagonal (which multiplies zero rows of X), and X' is zero outside [M][N] again; only
-// the store of U to memory checks.
+// One iteration with PK product planes (PK = NP folds a I into B).  Eight waves: waves w and
+// w + 4 compute tile w & 3 of each product over the two halves of its K range and then
+// finish half of the tile each.  In the accumulator layout a lane holds runs of four
+// consecutive rows of one column.  A and B are symmetric, so such a run is stored at the
+// mirror position as four consecutive columns of one row, one 8-byte LDS store a plane
+// (A's planes are read back for b A the same way); the update computes the transposed tile
+// X'^T = X^T B, so that its runs are four consecutive columns of X'.  No element needs a
+// bounds check in LDS: X is zero outside [M][N], so A is zero outside [M][M], B outside
+// [M][M] but for a on the padded diagonal (which multiplies zero rows of X), and X' is zero
+// outside [M][N] again; only the store of U to memory checks.
 template <int NP, int PK>
 __device__ __forceinline__ void ns_iteration(const NsArgs& a, u16* xs, u16* as_, u16* bs,
                                              float* red, int z, float s, bool first,
@@ -127,19 +159,25 @@ __device__ __forceinline__ void ns_iteration(const NsArgs& a, u16* xs, u16* as_,
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wt = w & 3, kh = w >> 2;
   const int ti = wt >> 1, tj = wt & 1;
+  // first row (first column for the update) of run g of this wave's kept half, the column
+  // (row) of this lane
+  auto run0 = [&](int t, int g) { return 32 * t + 16 * kh + 8 * g + 4 * hl; };
+  const int ln = lane & 31;
 
   // A = X X^T (s^2 G G^T in the first iteration)
   {
     f32x16 acc[1] = {prod_rows<PK, SN / 2>(xs, SM * XS, XS, xs, SM * XS, XS, ti, tj,
                                            kh * (SN / 2))};
-    reduce_halves<1>(acc, red, w, lane);
-    if (w < 4) {
-      const float s2 = first ? s * s : 1.f;
+    float own[1][8];
+    exchange_halves<1>(acc, own, red, w, lane);
+    const float s2 = first ? s * s : 1.f;
+    const int c = 32 * tj + ln;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * ti + 8 * (v >> 2) + 4 * hl + (v & 3), c = 32 * tj + (lane & 31);
-        put_planes(as_, SM * AS, PK, AS, r, c, acc[0][v] * s2);
-      }
+    for (int g = 0; g < 2; ++g) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = own[0][4 * g + e] * s2;
+      put_run(as_, SM * AS, PK, c * AS + run0(ti, g), x);   // A[c][r .. r + 3]
     }
   }
   __syncthreads();
@@ -148,23 +186,25 @@ __device__ __forceinline__ void ns_iteration(const NsArgs& a, u16* xs, u16* as_,
   {
     f32x16 acc[1] = {prod_rows<PK, SM / 2>(as_, SM * AS, AS, as_, SM * AS, AS, ti, tj,
                                            kh * (SM / 2))};
-    reduce_halves<1>(acc, red, w, lane);
-    if (w < 4) {
+    float own[1][8];
+    exchange_halves<1>(acc, own, red, w, lane);
+    const int c = 32 * tj + ln;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * ti + 8 * (v >> 2) + 4 * hl + (v & 3), c = 32 * tj + (lane & 31);
-        float av = 0.f;
+    for (int g = 0; g < 2; ++g) {
+      const int r0 = run0(ti, g);
+      float av[4], x[4];
+      sum_run(as_, SM * AS, PK, c * AS + r0, av);   // A[r .. r + 3][c] by symmetry
 #pragma unroll
-        for (int q = 0; q < PK; ++q) av += bf2f(as_[q * SM * AS + r * AS + c]);
-        const float x =
-            a.coef_b * av + a.coef_c * acc[0][v] + (fold && r == c ? a.coef_a : 0.f);
-        put_planes(bs, SM * AS, PK, AS, r, c, x);
-      }
+      for (int e = 0; e < 4; ++e)
+        x[e] = a.coef_b * av[e] + a.coef_c * own[0][4 * g + e] +
+               (fold && r0 + e == c ? a.coef_a : 0.f);
+      put_run(bs, SM * AS, PK, c * AS + r0, x);
     }
   }
   __syncthreads();
 
-  // X' = B X (+ a X from all of X's planes), times s in the first iteration
+  // X'^T = X^T B (+ a X from all of X's planes), times s in the first iteration: tile rows
+  // are columns of X', tile columns rows of X'
   f32x16 acc[2] = {f32x16{}, f32x16{}};
   const int ri = wt & 1, cj = 2 * (wt >> 1);
 #pragma unroll
@@ -174,59 +214,42 @@ __device__ __forceinline__ void ns_iteration(const NsArgs& a, u16* xs, u16* as_,
 #pragma unroll
       for (int k = 0; k < SM / 2; k += 16) {
         const int k0 = kh * (SM / 2) + k;
-        const bf16x8 fa = frag_rows(bs + qa * SM * AS, AS, 32 * ri, k0);
+        const bf16x8 fb = frag_rows(bs + qa * SM * AS, AS, 32 * ri, k0);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          acc[u] = mfma(fa, frag_cols(xs + qb * SM * XS, XS, 32 * (cj + u), k0), acc[u]);
+          acc[u] = mfma(frag_cols(xs + qb * SM * XS, XS, 32 * (cj + u), k0), fb, acc[u]);
       }
-  reduce_halves<2>(acc, red, w, lane);   // every wave has read X once this returns
-  if (w < 4) {
-    const float sc = first ? s : 1.f;
+  float own[2][8];
+  exchange_halves<2>(acc, own, red, w, lane);   // every wave has read X once this returns
+  const float sc = first ? s : 1.f;
+  const int r = 32 * ri + ln;
+  const int tr = (a.tr_mask >> (z / a.P)) & 1;
+  float* U = a.U + (int64_t)z * M * N;
+  // the a X term reads X only where the same lane writes X' below
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 32 * ri + 8 * (v >> 2) + 4 * hl + (v & 3);
-        const int c = 32 * (cj + u) + (lane & 31);
-        float lin = 0.f;
-        if (!fold) {
+    for (int g = 0; g < 2; ++g) {
+      const int c0 = run0(cj + u, g);
+      float lin[4] = {0.f, 0.f, 0.f, 0.f}, x[4];
+      if (!fold) sum_run(xs, SM * XS, NP, r * XS + c0, lin);
 #pragma unroll
-          for (int q = 0; q < NP; ++q) lin += bf2f(xs[q * SM * XS + r * XS + c]);
-        }
-        acc[u][v] = sc * fmaf(a.coef_a, lin, acc[u][v]);
-      }
-    if (last) {
-      const int tr = (a.tr_mask >> (z / a.P)) & 1;
-      float* U = a.U + (int64_t)z * M * N;
-      const bool whole = 32 * (ri + 1) <= M && 32 * (cj + 2) <= N;   // wave-uniform
+      for (int e = 0; e < 4; ++e) x[e] = sc * fmaf(a.coef_a, lin[e], own[u][4 * g + e]);
+      if (last) {
+        // N is a multiple of 16, so a run starting inside the matrix lies inside it
+        if (r < M && c0 < N) {
+          if (tr) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 32 * ri + 8 * (v >> 2) + 4 * hl + (v & 3);
-          const int c = 32 * (cj + u) + (lane & 31);
-          if (whole || (r < M && c < N)) {
-            if (tr) U[(int64_t)c * M + r] = acc[u][v];
-            else U[(int64_t)r * N + c] = acc[u][v];
+            for (int e = 0; e < 4; ++e) U[(int64_t)(c0 + e) * M + r] = x[e];
+          } else {
+            *reinterpret_cast<float4*>(U + (int64_t)r * N + c0) = make_float4(x[0], x[1], x[2], x[3]);
           }
         }
+      } else {
+        put_run(xs, SM * XS, NP, r * XS + c0, x);
+      }
     }
-  }
-  // every wave's products have read X before the barrier in reduce_halves, and the a X
-  // term above reads X only where the same wave writes X' below
-  if (!last) {
-    if (w < 4) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = 32 * ri + 8 * (v >> 2) + 4 * hl + (v & 3);
-          const int c = 32 * (cj + u) + (lane & 31);
-          put_planes(xs, SM * XS, NP, XS, r, c, acc[u][v]);
-        }
-    }
-    __syncthreads();
-  }
+  if (!last) __syncthreads();
 }
 
 template <int NP>
