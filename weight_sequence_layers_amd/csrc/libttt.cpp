@@ -191,7 +191,8 @@ struct ttt_state {
   int* health = nullptr;
   float* neg1 = nullptr;  // [sb] of -1: the apply backward's eta
   int contract_tiles = 0;
-  int part_n = 0;         // sum-of-squares parts per matrix: contract_tiles x CONTRACT_SUM_SUB
+  int part_sub = 1;       // sum-of-squares parts per contraction tile (CONTRACT_SUM_SUB if split)
+  int part_n = 0;         // sum-of-squares parts per matrix: contract_tiles x part_sub
   bool resident = false;  // the device-resident chunk loop serves this state (Wpl unused)
   // backward through an update: workspace allocated by the first ttt_chunk_backward call
   struct Bwd {
@@ -271,8 +272,9 @@ size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
   }
   size_t oG = C.take<float>(D.nm * P * d * n);
   const int ctiles = (int)(((d + CONTRACT_BM - 1) / CONTRACT_BM) * ((n + CONTRACT_BN - 1) / CONTRACT_BN));
-  size_t opart = C.take<float>((int64_t)D.nm * P * ctiles * CONTRACT_SUM_SUB);
   const int ksp = contract_split_max(ctiles, (int)(D.nm * P));
+  const int psub = ksp > 1 ? CONTRACT_SUM_SUB : 1;
+  size_t opart = C.take<float>((int64_t)D.nm * P * ctiles * psub);
   size_t ogp = ksp > 1 ? C.take<float>(ksp * D.nm * P * d * n) : 0;
   size_t ox[2] = {0, 0}, oa = 0, ob = 0;
   if (c.ns_steps > 0) {
@@ -313,7 +315,8 @@ size_t layout(ttt_state* s, char* base, float* ext_w = nullptr) {
     s->G = F(oG);
     s->part = F(opart);
     s->contract_tiles = ctiles;
-    s->part_n = ctiles * CONTRACT_SUM_SUB;
+    s->part_sub = psub;
+    s->part_n = ctiles * psub;
     s->ksplit = ksp;
     s->gpart = ksp > 1 ? F(ogp) : nullptr;
     if (c.ns_steps > 0) {
@@ -442,6 +445,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   const int64_t Z = (int64_t)D.nm * P;
   if (ca.muon) ca.x = pbuf(s->xpl[0], D.np, Z * d * D.n, (int64_t)d * D.n, D.n);
   ca.part = s->part;
+  ca.psub = s->part_sub;
   ca.U = U;
   ca.gpart = s->gpart;
   ca.gpart_stride = (int64_t)D.nm * P * d * D.n;

@@ -234,9 +234,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm2(Gemm2Args a) {
   const int64_t base = (int64_t)zz * M * N;
   float sc = 1.f;
   if (a.spart) {
-    float t = 0.f;
-    for (int i = 0; i < a.nspart; ++i) t += a.spart[(int64_t)zz * a.nspart + i];
-    sc = 1.f / (sqrtf(t) + a.eps);
+    sc = 1.f / (sqrtf(sum_parts(a.spart + (int64_t)zz * a.nspart, a.nspart)) + a.eps);
   }
   const float alpha = a.alpha * sc, beta = a.beta * sc;
   float gs = 0.f;
@@ -277,7 +275,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm2(Gemm2Args a) {
 __global__ __launch_bounds__(256) void k_ns_fin(NsFinArgs a) {
   const int zz = blockIdx.y;
   float ss = 0.f, dot = 0.f;
-  for (int i = 0; i < a.nss; ++i) ss += a.ss_part[(int64_t)zz * a.nss + i];
+  ss = sum_parts(a.ss_part + (int64_t)zz * a.nss, a.nss);
   for (int i = 0; i < a.ndot; ++i) dot += a.dot_part[(int64_t)zz * a.ndot + i];
   const float nrm = sqrtf(ss);
   const float s = 1.f / (nrm + a.eps);

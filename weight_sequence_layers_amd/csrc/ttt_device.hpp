@@ -217,6 +217,22 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The sum of n partial sums p[0 .. n) in one fixed order: eight interleaved running sums
+// (eight loads in flight at a time), the remainder into the first of them, then the eight
+// in order.
+__device__ __forceinline__ float sum_parts(const float* p, int n) {
+  float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int i = 0;
+  for (; i + 8 <= n; i += 8)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] += p[i + j];
+  for (int j = 0; i + j < n; ++j) t[j] += p[i + j];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += t[j];
+  return s;
+}
+
 __device__ __forceinline__ float block_sum(float v, float* scratch) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -170,7 +170,8 @@ struct ContractArgs {
   int last;        // last token block of the chunk
   int muon;        // write X0 planes and per-tile sums of squares
   PlaneBuf x;
-  float* part;     // [nm*P][tiles]
+  float* part;     // [nm*P][tiles][psub]
+  int psub;        // parts per tile: 1, or CONTRACT_SUM_SUB when the launch may split
   float* U;        // plain step: U in weight orientation [nm][P][rows][cols]
   int tr_mask;     // bit m: matrix m's weight is the transpose of its X orientation
   // Token split: with ksplit > 1 the launch sums ksplit token ranges of kchunk tokens in
@@ -303,10 +304,11 @@ ttt_status sequence_in_workspace(const ttt_config* cfg, float* w, const void* q,
 // tile sizes used by the contraction and Newton-Schulz stages (the host sizes buffers)
 constexpr int CONTRACT_BM = 128, CONTRACT_BN = 128;
 constexpr int CONTRACT_SPLIT_MAX = 16;   // token ranges of one contraction at most
-// Parts of a contraction tile's sum of squares (the Newton-Schulz input's Frobenius norm):
-// one per band of 16 rows, so that a token-split contraction's second pass spreads a tile
-// over that many workgroups.  An unsplit contraction stores its tile's sum in the first
-// part and zeros in the others, so a reader adding all parts in order gets the same value.
+// Parts of a contraction tile's sum of squares (the Newton-Schulz input's Frobenius norm)
+// where the contraction may split its tokens: one per band of 16 rows, so that the split's
+// second pass spreads a tile over that many workgroups.  An unsplit launch of such a
+// contraction stores its tile's sum in the first part and zeros in the others.  Where the
+// contraction never splits, a tile has one part.
 constexpr int CONTRACT_SUM_SUB = 8;
 int ns_tri_tiles(int M, int tile);
 

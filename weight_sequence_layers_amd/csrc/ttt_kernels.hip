@@ -311,9 +311,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
     const int rl = min(BM, M - m0), cl = min(BN, N - n0);
     store_tile_planes<G, TILE_NORMAL>(g.acc[0], smem, a.x, zz, m0, n0, rl, cl);
     const float t = block_sum(ss, reinterpret_cast<float*>(smem));
-    if (threadIdx.x < CONTRACT_SUM_SUB)
-      a.part[((int64_t)zz * a.tiles + tile) * CONTRACT_SUM_SUB + threadIdx.x] =
-          threadIdx.x == 0 ? t : 0.f;
+    if ((int)threadIdx.x < a.psub)
+      a.part[((int64_t)zz * a.tiles + tile) * a.psub + threadIdx.x] = threadIdx.x == 0 ? t : 0.f;
   }
 }
 
@@ -417,9 +416,7 @@ __global__ __launch_bounds__(CONTRACT_SUM_THREADS) void k_contract_sum(ContractA
 
 // ------------------------------------------------------------------------ Newton-Schulz
 __device__ __forceinline__ float ns_scale(const NsArgs& a, int zz) {
-  float t = 0.f;
-  for (int i = 0; i < a.nparts; ++i) t += a.part[(int64_t)zz * a.nparts + i];
-  return 1.f / (sqrtf(t) + a.eps);
+  return 1.f / (sqrtf(sum_parts(a.part + (int64_t)zz * a.nparts, a.nparts)) + a.eps);
 }
 
 
@@ -907,7 +904,9 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   a.nz = nm * a.P;
   if (a.tiles == 0 || a.nz == 0 || a.K <= 0) return hipSuccess;
-  int ks = std::min(a.gpart ? a.ksplit : 1, contract_split_max(a.tiles, a.nz));
+  // a split's second pass stores CONTRACT_SUM_SUB parts per tile
+  int ks = std::min(a.gpart && a.psub == CONTRACT_SUM_SUB ? a.ksplit : 1,
+                    contract_split_max(a.tiles, a.nz));
   ks = std::max(1, std::min(ks, a.K / CONTRACT_RANGE_MIN));
   a.kchunk = ks > 1 ? (((a.K + ks - 1) / ks + 63) / 64) * 64 : a.K;
   a.ksplit = (a.K + a.kchunk - 1) / a.kchunk;

@@ -47,9 +47,7 @@ __device__ __forceinline__ bf16x8 frag_cols(const u16* base, int stride, int n0,
 
 // 1 / (|G|_F + eps) from the per-tile sums of squares the contraction left for matrix z
 __device__ __forceinline__ float ns_scale_of(const float* part, int nparts, float eps, int z) {
-  float t = 0.f;
-  for (int i = 0; i < nparts; ++i) t += part[(int64_t)z * nparts + i];
-  return 1.f / (sqrtf(t) + eps);
+  return 1.f / (sqrtf(sum_parts(part + (int64_t)z * nparts, nparts)) + eps);
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
