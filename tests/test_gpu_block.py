@@ -170,15 +170,45 @@ def test_linear_matches_definition(epi, rows, K, N):
     assert np.all(err <= bar), float((err - bar).max())
 
 
-def test_linear_residual_in_place():
+# 8200 x 4104 outputs at 2056 input features give 561 tiles of 256 x 256 and a long K loop,
+# so those launches take the wide-tile kernel, with ragged rows, output features and a
+# partial last K step
+WIDE = (8200, 2056, 4104)
+
+
+@pytest.mark.parametrize("epi", ["plain", "residual", "gelu"])
+def test_linear_wide_tiles_sampled(epi):
+    rows, K, N = WIDE
+    rng = np.random.default_rng(17)
+    xv, xb = _bits(rng.standard_normal((rows, K)))
+    wv, wb = _bits(rng.standard_normal((N, K)) / np.sqrt(K))
+    rv, rb = _bits(rng.standard_normal((rows, N)))
+    x, w, r = _bf16_dev(xb), _bf16_dev(wb), _bf16_dev(rb)
+    y = torch.empty(rows, N, dtype=torch.bfloat16, device=DEV)
+    print(f"linear wide {epi} rows={rows} K={K} N={N}", flush=True)
+    W.ttt_linear(x, w, r if epi == "residual" else None, y, rows, K, N, epi)
+    torch.cuda.synchronize()
+    # rows from every 256-row tile at several offsets, and the ragged last tile
+    sel = np.unique(np.concatenate([np.arange(0, rows, 97), np.arange(rows - 8, rows)]))
+    X, Wt = xv[sel].astype(np.float64), wv.astype(np.float64)
+    acc = X @ Wt.T
+    ref = {"plain": acc, "residual": rv[sel].astype(np.float64) + acc, "gelu": blk.gelu(acc)}[epi]
+    bar = 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * (np.abs(X) @ np.abs(Wt).T) + 1e-6
+    err = np.abs(y.float().cpu().numpy()[sel] - ref)
+    assert np.all(err <= bar), float((err - bar).max())
+
+
+@pytest.mark.parametrize("rows,K,N", [(200, 128, 256), WIDE])
+def test_linear_residual_in_place(rows, K, N):
     rng = np.random.default_rng(9)
-    xv, xb = _bits(rng.standard_normal((200, 128)))
-    wv, wb = _bits(rng.standard_normal((256, 128)) / np.sqrt(128))
-    rv, rb = _bits(rng.standard_normal((200, 256)))
+    xv, xb = _bits(rng.standard_normal((rows, K)))
+    wv, wb = _bits(rng.standard_normal((N, K)) / np.sqrt(K))
+    rv, rb = _bits(rng.standard_normal((rows, N)))
     x, w, r = _bf16_dev(xb), _bf16_dev(wb), _bf16_dev(rb)
     y = torch.empty_like(r)
-    W.ttt_linear(x, w, r, y, 200, 128, 256, "residual")
-    W.ttt_linear(x, w, r, r, 200, 128, 256, "residual")
+    print(f"linear in place rows={rows} K={K} N={N}", flush=True)
+    W.ttt_linear(x, w, r, y, rows, K, N, "residual")
+    W.ttt_linear(x, w, r, r, rows, K, N, "residual")
     torch.cuda.synchronize()
     assert torch.equal(y, r)
 

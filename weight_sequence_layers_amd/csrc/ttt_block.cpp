@@ -110,8 +110,12 @@ LinearArgs linear_args(const void* x, const void* w, const void* resid, void* y,
   a.rows = rows;
   a.K = K;
   a.N = N;
-  a.tiles_n = (N + 127) / 128;
-  a.tiles_m = (int32_t)((rows + 127) / 128);
+  // 256 x 256 tiles where they give at least two workgroups per CU (one fits a CU) and the
+  // K loop is long; shorter ones gain nothing from them (measured at K = 1024)
+  const int64_t wide = ((rows + 255) / 256) * ((N + 255) / 256);
+  a.tile = wide >= LINEAR_WIDE_MIN && K >= LINEAR_WIDE_K ? 256 : 128;
+  a.tiles_n = (N + a.tile - 1) / a.tile;
+  a.tiles_m = (int32_t)((rows + a.tile - 1) / a.tile);
   a.tiles = (int64_t)a.tiles_m * a.tiles_n;
   // row tiles per group: 8 measured best or within a few percent of it for every projection
   // of the block at width 1024 (in 1024 or 4096 features, out 1024 to 4096)

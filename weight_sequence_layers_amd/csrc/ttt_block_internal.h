@@ -11,6 +11,10 @@ constexpr int ATT_D = TTT_ATTN_HEAD_DIM;   // attention head dimension
 constexpr int ATT_Q = 128;                 // queries per workgroup (4 waves x 32)
 constexpr int ATT_KV = 64;                 // keys per step
 constexpr int BLK_MAX_TTT_HEADS = 16;      // step-size projections per row
+// 256 x 256 projection tiles for launches with at least LINEAR_WIDE_MIN of them and at least
+// LINEAR_WIDE_K input features
+constexpr int64_t LINEAR_WIDE_MIN = 512;
+constexpr int32_t LINEAR_WIDE_K = 2048;
 
 struct AttnArgs {
   const u16* q;
@@ -30,6 +34,7 @@ struct LinearArgs {
   int64_t rows;
   int32_t K, N, tiles_n, tiles_m, group_m;
   int64_t tiles;
+  int32_t tile;   // block tile edge: 128, or 256 for launches with many such tiles
 };
 
 // RMS normalisation of rows of x [rows][D] into y; with w_eta, also the TTT step sizes
