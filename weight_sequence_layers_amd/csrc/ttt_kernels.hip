@@ -889,9 +889,10 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
   using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;   // block size (the same for every instance)
   ContractArgs a = a0;
-  // more than one bf16 plane on either side: plane-resident (NA + NB tiles a K step
-  // instead of two per plane product, one pass over the K range instead of one per pair);
-  // one plane on both sides is a single product
+  // plane counts 1 x 2, 1 x 3, 2 x 1, 3 x 1, 2 x 2 and 3 x 3: plane-resident (NA + NB tiles a
+  // K step instead of two per plane product, one pass over the K range instead of one per
+  // pair); one plane on both sides is a single product; other mixes run plane pairs as K
+  // segments
   const int pa = a.a[0].planes, pb = a.b[0].planes;
   auto kern = k_contract<BM, BN, 2, 4, 0, 0>;
   if (pa == 1 && pb == 2) kern = k_contract<BM, BN, 2, 4, 1, 2>;
