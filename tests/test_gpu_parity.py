@@ -96,6 +96,16 @@ def test_single_plane_newton_schulz_one_chunk(shape):
     _check(cfg, planes=(1, 1, 1, 0), problems=problems)
 
 
+@pytest.mark.parametrize("planes", [(1, 1, 1, 0), (1, 2, 2, 0b00011)])
+def test_fused_small_newton_schulz_planes(planes):
+    # matrices of 64 x 128 run every Newton-Schulz iteration in one workgroup: one bf16
+    # plane everywhere, and two planes with iterations 0 and 1 on one plane (B without a I,
+    # a X added from the iterate's two planes). One chunk, as the single-plane tests above.
+    cfg = ti.Config("nss", 2, 2, 256, 256, 64, 128, "swiglu", "dot", 5, True, "bf16",
+                    "apply_then_update", 71)
+    _check(cfg, planes=planes)
+
+
 @pytest.mark.parametrize("case", ["narrow_lead2", "narrow_all_one_chunk", "wide_lead2",
                                   "wide_mixed"])
 def test_one_plane_newton_schulz_iterations(case):
