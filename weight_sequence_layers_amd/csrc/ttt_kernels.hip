@@ -885,22 +885,32 @@ int contract_split_max(int tiles, int nz) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(CONTRACT_SPLIT_MAX, CONTRACT_SLOTS / wgs));
 }
 
+// plane counts 1 x 2, 1 x 3, 2 x 1, 3 x 1, 2 x 2 and 3 x 3: plane-resident (NA + NB tiles a
+// K step instead of two per plane product, one pass over the K range instead of one per
+// pair); one plane on both sides is a single product; other mixes run plane pairs as K
+// segments
+template <int BM>
+static void (*contract_kernel(int pa, int pb))(ContractArgs) {
+  constexpr int BN = CONTRACT_BN;
+  if (pa == 1 && pb == 2) return k_contract<BM, BN, 2, 4, 1, 2>;
+  if (pa == 1 && pb == 3) return k_contract<BM, BN, 2, 4, 1, 3>;
+  if (pa == 2 && pb == 1) return k_contract<BM, BN, 2, 4, 2, 1>;
+  if (pa == 3 && pb == 1) return k_contract<BM, BN, 2, 4, 3, 1>;
+  if (pa == 2 && pb == 2) return k_contract<BM, BN, 2, 4, 2, 2>;
+  if (pa == 3 && pb == 3) return k_contract<BM, BN, 2, 4, 3, 3>;
+  return k_contract<BM, BN, 2, 4, 0, 0>;
+}
+
 hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
-  constexpr int BM = CONTRACT_BM, BN = CONTRACT_BN;
-  using G = Gemm<BM, BN, 2, 4, 1, 1, 1, 1>;   // block size (the same for every instance)
+  constexpr int BN = CONTRACT_BN;
+  using G = Gemm<CONTRACT_BM, BN, 2, 4, 1, 1, 1, 1>;   // block size (the same for every instance)
   ContractArgs a = a0;
-  // plane counts 1 x 2, 1 x 3, 2 x 1, 3 x 1, 2 x 2 and 3 x 3: plane-resident (NA + NB tiles a
-  // K step instead of two per plane product, one pass over the K range instead of one per
-  // pair); one plane on both sides is a single product; other mixes run plane pairs as K
-  // segments
   const int pa = a.a[0].planes, pb = a.b[0].planes;
-  auto kern = k_contract<BM, BN, 2, 4, 0, 0>;
-  if (pa == 1 && pb == 2) kern = k_contract<BM, BN, 2, 4, 1, 2>;
-  else if (pa == 1 && pb == 3) kern = k_contract<BM, BN, 2, 4, 1, 3>;
-  else if (pa == 2 && pb == 1) kern = k_contract<BM, BN, 2, 4, 2, 1>;
-  else if (pa == 3 && pb == 1) kern = k_contract<BM, BN, 2, 4, 3, 1>;
-  else if (pa == 2 && pb == 2) kern = k_contract<BM, BN, 2, 4, 2, 2>;
-  else if (pa == 3 && pb == 3) kern = k_contract<BM, BN, 2, 4, 3, 3>;
+  // matrices of at most 64 rows (dim 64) take 64-row tiles: the same tiles (one row of
+  // them) without the 64 rows of padding a 128-row tile would carry through the MFMAs
+  const bool rows64 = a.M <= 64;
+  const int BM = rows64 ? 64 : CONTRACT_BM;
+  auto kern = rows64 ? contract_kernel<64>(pa, pb) : contract_kernel<CONTRACT_BM>(pa, pb);
   a.tiles_n = (a.N + BN - 1) / BN;
   a.tiles = ((a.M + BM - 1) / BM) * a.tiles_n;
   a.nz = nm * a.P;
@@ -913,7 +923,8 @@ hipError_t launch_contract(const ContractArgs& a0, int nm, hipStream_t s) {
   a.ksplit = (a.K + a.kchunk - 1) / a.kchunk;
   hipLaunchKernelGGL(kern, dim3(a.tiles * a.nz * a.ksplit), dim3(G::NT), 0, s, a);
   if (a.ksplit > 1) {
-    auto sum = k_contract_sum<BM, BN>;
+    // the tiles are those of 128 rows either way (one row of them when rows64)
+    auto sum = k_contract_sum<CONTRACT_BM, BN>;
     hipLaunchKernelGGL(sum, dim3(a.tiles * a.nz * CONTRACT_SUM_SUB), dim3(CONTRACT_SUM_THREADS),
                        0, s, a);
   }
