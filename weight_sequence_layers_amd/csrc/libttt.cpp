@@ -496,12 +496,12 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
   sa.n = R.nr; sa.d = d;
   Operand xk, xv;
   if (c.act == TTT_F32) {
+    SplitArgs sv = sa;
     sa.x = k; sa.out = tok(s->kpl, gi, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    sv.x = v; sv.out = tok(s->vpl, gi, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split2(sa, sv, P, st));
     xk = operand_of(sa.out, gi, R.nr);
-    sa.x = v; sa.out = tok(s->vpl, gi, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
-    xv = operand_of(sa.out, gi, R.nr);
+    xv = operand_of(sv.out, gi, R.nr);
   } else {
     xk = act_operand(k, R.T * d, d, R.nr);
     xv = act_operand(v, R.T * d, d, R.nr);
@@ -670,12 +670,12 @@ ttt_status apply_bwd_rows(ttt_state* s, const Rows& R, bool first, bool last, fl
   if (c.act == TTT_F32) {
     SplitArgs sa{};
     sa.x_zstride = R.T * d; sa.x_bf16 = 0; sa.n = R.nr; sa.d = d;
+    SplitArgs so = sa;
     sa.x = q; sa.out = tok(s->kpl, gi, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    so.x = o; so.out = tok(s->vpl, gi, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split2(sa, so, P, st));
     xq = operand_of(sa.out, gi, R.nr);
-    sa.x = o; sa.out = tok(s->vpl, gi, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
-    xo = operand_of(sa.out, gi, R.nr);
+    xo = operand_of(so.out, gi, R.nr);
   } else {
     xq = act_operand(q, R.T * d, d, R.nr);
     xo = act_operand(o, R.T * d, d, R.nr);
@@ -914,12 +914,12 @@ ttt_status grad_bwd_rows(ttt_state* s, const Rows& R, bool first, bool last, voi
   if (c.act == TTT_F32) {
     SplitArgs sa{};
     sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
+    SplitArgs sv = sa;
     sa.x = k; sa.out = pbuf(s->kpl, D.in_kv, (int64_t)P * SB * d, SB * d, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    sv.x = v; sv.out = pbuf(s->vpl, D.in_kv, (int64_t)P * SB * d, SB * d, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split2(sa, sv, P, st));
     xk = operand_of(sa.out, D.in_kv, R.nr);
-    sa.x = v; sa.out = pbuf(s->vpl, D.in_kv, (int64_t)P * SB * d, SB * d, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
-    xv = operand_of(sa.out, D.in_kv, R.nr);
+    xv = operand_of(sv.out, D.in_kv, R.nr);
   } else {
     xk = act_operand(k, R.T * d, d, R.nr);
     xv = act_operand(v, R.T * d, d, R.nr);

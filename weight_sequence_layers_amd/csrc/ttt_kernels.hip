@@ -782,7 +782,7 @@ __global__ __launch_bounds__(256) void k_renorm(RenormArgs a) {
 
 // Token rows [n][d] (activation dtype) -> bf16 planes in the same layout, optionally with
 // row t scaled by -eta_t.
-__global__ __launch_bounds__(256) void k_split(SplitArgs a) {
+__device__ __forceinline__ void split_rows(const SplitArgs& a) {
   const int z = blockIdx.y;
   const int64_t total = (int64_t)a.n * a.d;
   for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
@@ -790,6 +790,14 @@ __global__ __launch_bounds__(256) void k_split(SplitArgs a) {
     if (a.neg_eta) x *= -a.eta[(int64_t)z * a.eta_zstride + e / a.d];
     put_planes(a.out, z, e, x);
   }
+}
+
+__global__ __launch_bounds__(256) void k_split(SplitArgs a) { split_rows(a); }
+
+// two tensors of the same shape in one launch (blockIdx.z picks the tensor)
+__global__ __launch_bounds__(256) void k_split2(SplitArgs a, SplitArgs b) {
+  if (blockIdx.z == 0) split_rows(a);
+  else split_rows(b);
 }
 
 // ============================================================================ launchers
@@ -1035,6 +1043,16 @@ hipError_t launch_split(const SplitArgs& a, int Z, hipStream_t s) {
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_split, dim3(blocks, Z), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split2(const SplitArgs& a, const SplitArgs& b, int Z, hipStream_t s) {
+  if (a.n != b.n || a.d != b.d) return hipErrorInvalidValue;
+  if (Z == 0 || a.n == 0) return hipSuccess;
+  int64_t total = (int64_t)a.n * a.d;
+  int blocks = (int)((total + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_split2, dim3(blocks, Z, 2), dim3(256), 0, s, a, b);
   return hipGetLastError();
 }
 
