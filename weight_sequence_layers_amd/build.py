@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -35,15 +36,18 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     """Compile every source and link libttt.so next to this file. Always recompiles."""
-    objs = []
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    for src in SOURCES:
-        obj = os.path.join(build_dir, src.replace(".", "_") + ".o")
-        out = _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
-        if verbose and out.strip():
-            print(out)
-        objs.append(obj)
+    objs = [os.path.join(build_dir, src.replace(".", "_") + ".o") for src in SOURCES]
+    # one compiler process per source, a few at a time (each takes about a GB of memory)
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1, 8))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        outs = list(ex.map(lambda so: _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, so[0]),
+                                             "-o", so[1]]), zip(SOURCES, objs)))
+    if verbose:
+        for out in outs:
+            if out.strip():
+                print(out)
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
