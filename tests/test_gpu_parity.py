@@ -115,6 +115,24 @@ def test_fused_small_newton_schulz_planes(planes):
     _check(cfg, planes=planes)
 
 
+@pytest.mark.parametrize("case", ["two_blocks", "gelu_mse_f32"])
+def test_fused_small_newton_schulz_after_split(case):
+    # matrices of at most 64 x 128 (every Newton-Schulz iteration in one launch) after a
+    # token-split contraction.
+    # two_blocks: chunks of 66000 tokens, two token blocks each (the last block's split sum
+    # also adds the first block's running sum); a step size per matrix, no renorm.
+    # gelu_mse_f32: GELU net and MSE loss (two contraction launches), fp32 activations,
+    # weight decay and renorm, dims off the tile grid.
+    if case == "two_blocks":
+        cfg = ti.Config("fss2", 1, 2, 132000, 66000, 64, 128, "swiglu", "dot", 5, False, "bf16",
+                        "apply_then_update", 81, lr=(0.5, 1.0, 0.25))
+        _check(cfg, planes=(1, 3, 3, 0))
+    else:
+        cfg = ti.Config("fssm", 3, 1, 8192, 4096, 48, 96, "gelu", "mse", 5, True, "f32",
+                        "apply_then_update", 82, weight_decay=0.01)
+        _check(cfg, planes=(3, 3, 3, 0))
+
+
 @pytest.mark.parametrize("case", ["narrow_lead2", "narrow_all_one_chunk", "wide_lead2",
                                   "wide_mixed"])
 def test_one_plane_newton_schulz_iterations(case):
