@@ -241,9 +241,11 @@ struct ContractGemm {
 template <int BM, int BN, int WGM, int WGN, int PA, int PB>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
   using CG = ContractGemm<PA, PB>;
-  // both operands token-major (read column-wise)
+  // both operands token-major (read column-wise); the plane-resident form steps K by 32
+  // where two of its workgroups share a CU, and by 64 on 64-row tiles (few workgroups, so
+  // half the steps is worth the LDS of one workgroup per CU)
   using G = Gemm<BM, BN, WGM, WGN, CG::NA, CG::NB, (1 << CG::NA) - 1, (1 << CG::NB) - 1, CG::PL,
-                 PA ? 32 : 64>;
+                 (PA && BM > 64) ? 32 : 64>;
   GEMM_LDS(G);
   // logical block order (token range, matrix and problem, tile)
   const int lid = xcd_block(blockIdx.x, gridDim.x);
@@ -838,7 +840,7 @@ hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t
   if (fw == FW_SWIGLU) {
     const bool small = small_tiles(a.nrows, a.N, Z);
     if (mode == FRONT_Q)
-      return small ? front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_Q, 32>(a, Z, s)
+      return small ? front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_Q, 64>(a, Z, s)
                    : front_fm<FW_SWIGLU, FRONT_Q>(a, Z, s);
     if (mode == FRONT_K_DOT)
       return small ? front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_K_DOT>(a, Z, s)
