@@ -386,6 +386,7 @@ struct Rows {
   int64_t T;    // tokens per problem in the caller's tensors
   int64_t t0;   // first token of the range
   int nr;       // number of tokens
+  bool split;   // fp32 activations: q, k and v of the range already split into their planes
 };
 
 ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
@@ -399,7 +400,7 @@ ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
     SplitArgs sa{};
     sa.x = q; sa.x_zstride = R.T * d; sa.n = R.nr; sa.d = d;
     sa.out = pbuf(s->qpl, D.in_q, (int64_t)P * D.sb * d, D.sb * d, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
+    if (!R.split) STAGED(TTT_STAGE_SPLIT, launch_split(sa, P, st));
     xq = operand_of(sa.out, D.in_q, R.nr);
   } else {
     xq = act_operand(q, R.T * d, d, R.nr);
@@ -499,7 +500,7 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     SplitArgs sv = sa;
     sa.x = k; sa.out = tok(s->kpl, gi, d);
     sv.x = v; sv.out = tok(s->vpl, gi, d);
-    STAGED(TTT_STAGE_SPLIT, launch_split2(sa, sv, P, st));
+    if (!R.split) STAGED(TTT_STAGE_SPLIT, launch_split2(sa, sv, P, st));
     xk = operand_of(sa.out, gi, R.nr);
     xv = operand_of(sv.out, gi, R.nr);
   } else {
@@ -732,11 +733,27 @@ ttt_status apply_bwd_rows(ttt_state* s, const Rows& R, bool first, bool last, fl
 
 // One chunk: apply and update in the configured order, or (update == false) apply only
 // with the state as it stands.
-ttt_status run_chunk(ttt_state* s, const Rows& R0, hipStream_t st, bool update = true) {
+ttt_status run_chunk(ttt_state* s, const Rows& R00, hipStream_t st, bool update = true) {
   const ttt_config& c = s->cfg;
   const Dims& D = s->D;
   const int64_t b = c.chunk;
   ttt_status r;
+  Rows R0 = R00;
+  if (update && c.act == TTT_F32 && b <= D.sb) {
+    // fp32 activations of a chunk in one token block: q, k and v into their bf16 planes in
+    // one launch (the apply and gradient launches then read the planes)
+    const int P = D.P, d = D.d;
+    SplitArgs sq{};
+    sq.x = R0.q + R0.t0 * d * 4; sq.x_zstride = R0.T * d; sq.n = (int)b; sq.d = d;
+    sq.out = pbuf(s->qpl, D.in_q, (int64_t)P * D.sb * d, D.sb * d, d);
+    SplitArgs sk = sq, sv = sq;
+    sk.x = R0.k + R0.t0 * d * 4;
+    sk.out = pbuf(s->kpl, D.in_kv, (int64_t)P * D.sb * d, D.sb * d, d);
+    sv.x = R0.v + R0.t0 * d * 4;
+    sv.out = pbuf(s->vpl, D.in_kv, (int64_t)P * D.sb * d, D.sb * d, d);
+    STAGED(TTT_STAGE_SPLIT, launch_split3(sq, sk, sv, P, st));
+    R0.split = true;
+  }
   auto apply_all = [&]() -> ttt_status {
     for (int64_t o = 0; o < b; o += D.sb) {
       Rows R = R0;

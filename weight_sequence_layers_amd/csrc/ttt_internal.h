@@ -287,6 +287,9 @@ hipError_t launch_renorm(const RenormArgs& a, hipStream_t s);
 hipError_t launch_split(const SplitArgs& a, int Z, hipStream_t s);
 // two tensors of the same rows and width (a.n == b.n, a.d == b.d) in one launch
 hipError_t launch_split2(const SplitArgs& a, const SplitArgs& b, int Z, hipStream_t s);
+// three such tensors in one launch
+hipError_t launch_split3(const SplitArgs& a, const SplitArgs& b, const SplitArgs& c, int Z,
+                         hipStream_t s);
 hipError_t launch_small(const SmallArgs& a, int loss, hipStream_t s);
 bool small_supported(int fw, int ns_steps, int renorm, int act_bf16, int apply_first, int dim,
                      int hidden, int chunk, int ap, int gp);

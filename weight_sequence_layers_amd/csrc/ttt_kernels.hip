@@ -802,6 +802,13 @@ __global__ __launch_bounds__(256) void k_split2(SplitArgs a, SplitArgs b) {
   else split_rows(b);
 }
 
+// three tensors of the same shape in one launch
+__global__ __launch_bounds__(256) void k_split3(SplitArgs a, SplitArgs b, SplitArgs c) {
+  if (blockIdx.z == 0) split_rows(a);
+  else if (blockIdx.z == 1) split_rows(b);
+  else split_rows(c);
+}
+
 // ============================================================================ launchers
 // Every GEMM kernel holds its LDS in static __shared__ arrays (GEMM_LDS): launches pass no
 // dynamic LDS.
@@ -1055,6 +1062,17 @@ hipError_t launch_split2(const SplitArgs& a, const SplitArgs& b, int Z, hipStrea
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_split2, dim3(blocks, Z, 2), dim3(256), 0, s, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_split3(const SplitArgs& a, const SplitArgs& b, const SplitArgs& c, int Z,
+                         hipStream_t s) {
+  if (a.n != b.n || a.d != b.d || a.n != c.n || a.d != c.d) return hipErrorInvalidValue;
+  if (Z == 0 || a.n == 0) return hipSuccess;
+  int64_t total = (int64_t)a.n * a.d;
+  int blocks = (int)((total + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_split3, dim3(blocks, Z, 3), dim3(256), 0, s, a, b, c);
   return hipGetLastError();
 }
 
