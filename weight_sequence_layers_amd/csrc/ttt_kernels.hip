@@ -131,11 +131,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
 }
 
 // ------------------------------------------------------------------------ out / dH
-template <int BM, int BN, int WGM, int WGN, int MODE>
+// PR > 0 (the query output with PR bf16 planes on both operands): the plane-resident
+// product, every plane tile loaded once per K step, for launches too small to fill the GPU.
+template <int BM, int BN, int WGM, int WGN, int MODE, int PR = 0>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   // dH = E W2 reads W2 [dim][hidden] column-wise; the query output (a plane store) takes
   // the swapped accumulator layout
-  using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0, 0, 64, MODE == OUT_Q>;
+  static_assert(PR == 0 || MODE == OUT_Q, "plane-resident form for the query output");
+  constexpr int NP = PR ? PR : 1;
+  using G = Gemm<BM, BN, WGM, WGN, NP, NP, 0, MODE == DH_MSE ? 1 : 0, PR, 64, MODE == OUT_Q>;
   GEMM_LDS(G);
   const int lid = xcd_block(blockIdx.x, gridDim.x);
   const int z = lid / a.tiles, tile = lid % a.tiles;
@@ -143,7 +147,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_out(OutArgs a) {
   const int n0 = (tile % a.tiles_n) * BN;
   G g;
   g.zero();
-  g.run(&a.a, &a.b, m0, n0, z, a.K, GEMM_STAGES);
+  if constexpr (PR == 0) {
+    g.run(&a.a, &a.b, m0, n0, z, a.K, GEMM_STAGES);
+  } else {
+    Operand Aq[PR], Bq[PR];   // one operand per plane
+#pragma unroll
+    for (int q = 0; q < PR; ++q) {
+      Aq[q] = a.a;
+      Aq[q].p += q * a.a.pstride;
+      Aq[q].planes = 1;
+      Bq[q] = a.b;
+      Bq[q].p += q * a.b.pstride;
+      Bq[q].planes = 1;
+    }
+    g.run(Aq, Bq, m0, n0, z, a.K, GEMM_STAGES);
+  }
 
   const int cl = min(BN, a.N - n0);
   const int rn = min(BM, a.nrows - m0);
@@ -860,10 +878,14 @@ hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t
 }
 
 template <int MODE, int BM = 128, int BN = 128, int WGM = 2, int WGN = 4>
-static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s) {
+static hipError_t out_m(const OutArgs& a0, int Z, hipStream_t s, int pr = 0) {
   using G = Gemm<BM, BN, WGM, WGN, 1, 1, 0, MODE == DH_MSE ? 1 : 0>;
   OutArgs a = a0;
   auto kern = k_out<BM, BN, WGM, WGN, MODE>;
+  if constexpr (MODE == OUT_Q && BM == 64) {   // (small tiles only: LDS of all planes)
+    if (pr == 2) kern = k_out<BM, BN, WGM, WGN, MODE, 2>;
+    if (pr == 3) kern = k_out<BM, BN, WGM, WGN, MODE, 3>;
+  }
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
@@ -887,7 +909,10 @@ hipError_t launch_dq(const DqArgs& a0, int np, int Z, hipStream_t s) {
 
 hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
   if (mode == OUT_Q)
-    return small_tiles(a.nrows, a.N, Z) ? out_m<OUT_Q, 64, 64, 2, 2>(a, Z, s) : out_m<OUT_Q>(a, Z, s);
+    // small launches with several planes on both sides take the plane-resident product
+    return small_tiles(a.nrows, a.N, Z)
+               ? out_m<OUT_Q, 64, 64, 2, 2>(a, Z, s, a.a.planes == a.b.planes ? a.a.planes : 0)
+               : out_m<OUT_Q>(a, Z, s);
   if (mode == OUT_K_MSE) return out_m<OUT_K_MSE>(a, Z, s);
   return out_m<DH_MSE>(a, Z, s);
 }
