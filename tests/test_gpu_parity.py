@@ -115,6 +115,17 @@ def test_fused_small_newton_schulz_planes(planes):
     _check(cfg, planes=planes)
 
 
+@pytest.mark.parametrize("planes", [(2, 2, 2, 0), (3, 3, 3, 0)])
+def test_small_plane_resident_products(planes):
+    # launches too small to fill the GPU (fp32 activations, dim 64) with the same number of
+    # bf16 planes on every operand: the query and key-row fronts and the query output take
+    # the plane-resident products (all plane tiles of a K step loaded once). Two planes are
+    # held to the bf16 bar, three to the fp32 one.
+    cfg = ti.Config("prf", 2, 1, 1024, 512, 64, 128, "swiglu", "dot", 0, True, "f32",
+                    "apply_then_update", 91)
+    _check(cfg, planes=planes, tol=2e-2 if planes[0] == 2 else 1e-4)
+
+
 @pytest.mark.parametrize("case", ["two_blocks", "gelu_mse_f32"])
 def test_fused_small_newton_schulz_after_split(case):
     # matrices of at most 64 x 128 (every Newton-Schulz iteration in one launch) after a

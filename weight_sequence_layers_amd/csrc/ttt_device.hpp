@@ -248,7 +248,9 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 // PL > 0 selects the plane-resident product: A[0..NA) and B[0..NB) are the bf16 planes of
 // one A and one B (each operand with planes = 1), PL = max(NA, NB); every K step loads all
 // NA + NB plane tiles once and accumulates the plane products (i, j) with i + j < PL into
-// one accumulator.
+// one accumulator.  With PG > 1 groups: B holds the PL planes of each of PG operands
+// (B[g PL + j]) and A those of NA / PL operands, and accumulator g takes the plane products
+// of B operand g with its A operand (paired as products are below).
 // PL = 0 keeps one accumulator per B operand and runs plane pairs as K segments.
 //
 // SW selects the accumulator layout.  The MFMA computes D = A B with A's fragment giving
@@ -272,7 +274,8 @@ __device__ __forceinline__ float block_sum(float v, float* scratch) {
 // the others A[1]; else with NA == NB product p takes A[p], and otherwise every product
 // takes A[0] except, with NA == 2, the last, which takes A[1].
 template <int BM, int BN, int WGM, int WGN, int NA, int NB, int LAM = 0, int LBM = 0, int PL = 0,
-          int BK_ = 64, bool SW_ = false, int WGK_ = 1, int NB0 = -1, bool SUM = false>
+          int BK_ = 64, bool SW_ = false, int WGK_ = 1, int NB0 = -1, bool SUM = false,
+          int PG = 1>
 struct Gemm {
   static constexpr bool SW = SW_;
   static constexpr int WGK = WGK_;
@@ -305,13 +308,19 @@ struct Gemm {
   // LDS: stage buffer 0 (also the epilogue's staging area) and stage buffer 1, declared as
   // two separate __shared__ arrays by the kernel (GEMM_LDS)
   static_assert(TM >= 1 && TN >= 1, "tile too small for the block");
-  static_assert(PL == 0 || PL == (NA > NB ? NA : NB), "plane-resident mode: PL = max(NA, NB)");
-  static constexpr int NACC = (PL || SUM) ? 1 : NB;
+  static_assert(PL == 0 || (PG == 1 ? PL == (NA > NB ? NA : NB) : NB == PG * PL && NA % PL == 0),
+                "plane-resident mode: PL = max(NA, NB), or PG groups of PL planes");
+  static constexpr int NACC = PL ? PG : SUM ? 1 : NB;
+  static constexpr int NGA = PG > 1 ? NA / PL : 1;   // A operands of grouped plane products
 
   f32x16 acc[NACC][TM][TN];
 
   static __device__ __forceinline__ constexpr int ia(int p) {
     return NB0 >= 0 ? (p < NB0 ? 0 : 1) : NA == NB ? p : (NA == 2 && p == NB - 1) ? 1 : 0;
+  }
+  // A operand of plane group g (the same pairing over operands)
+  static __device__ __forceinline__ constexpr int ga(int g) {
+    return NB0 >= 0 ? (g < NB0 ? 0 : 1) : NGA == PG ? g : (NGA == 2 && g == PG - 1) ? 1 : 0;
   }
 
   // one 32 x 32 x 16 product of an A-tile fragment and a B-tile fragment into c
@@ -487,7 +496,22 @@ struct Gemm {
                                                         wn0 + t * 32, s)
                                : read_frag<false, BN, BK>(st + NA * A_TILE + i * B_TILE,
                                                          wn0 + t * 32, s);
-        if constexpr (PL > 0) {
+        if constexpr (PL > 0 && PG > 1) {
+#pragma unroll
+          for (int g = 0; g < PG; ++g)
+#pragma unroll
+            for (int i = 0; i < PL; ++i)
+#pragma unroll
+              for (int j = 0; j < PL; ++j)
+                if (i + j < PL) {
+#pragma unroll
+                  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+                      acc[g][tm][tn] = mma(fa[ga(g) * PL + i][tm], fb[g * PL + j][tn],
+                                           acc[g][tm][tn]);
+                }
+        } else if constexpr (PL > 0) {
 #pragma unroll
           for (int i = 0; i < NA; ++i)
 #pragma unroll

@@ -14,6 +14,8 @@
 //           writes the bf16 planes every GEMM of the next chunk reads.
 #include <math.h>
 
+#include <type_traits>
+
 #include "ttt_internal.h"
 
 namespace ttt {
@@ -54,13 +56,26 @@ struct FrontShape {
   static constexpr int NP = NB;
 };
 
-template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK>
+// The Gemm of a front: one operand per tensor (plane pairs as K segments), or with PR > 0
+// (every operand in PR bf16 planes) the plane-resident grouped product, all plane tiles of a
+// K step loaded once, for launches too small to fill the GPU.
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK, int PR>
+struct FrontGemm {
+  using FS = FrontShape<FW, MODE>;
+  static constexpr int NA = FS::NA, NB = FS::NB;
+  // the inner-product loss reads W2 [dim][hidden] column-wise for V W2; the epilogue
+  // stores planes only, which the swapped accumulator layout packs
+  using type = std::conditional_t<
+      PR == 0, Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0, 0, BK, true>,
+      Gemm<BM, BN, WGM, WGN, NA * (PR ? PR : 1), NB * (PR ? PR : 1), 0,
+           FS::DOT ? ((1 << PR) - 1) << ((NB - 1) * PR) : 0, PR, BK, true, 1, -1, false, NB>>;
+};
+
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK, int PR = 0>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
   using FS = FrontShape<FW, MODE>;
   constexpr int NA = FS::NA, NB = FS::NB;
-  // the inner-product loss reads W2 [dim][hidden] column-wise for V W2; the epilogue
-  // stores planes only, which the swapped accumulator layout packs
-  using G = Gemm<BM, BN, WGM, WGN, NA, NB, 0, FS::DOT ? (1 << (NB - 1)) : 0, 0, BK, true>;
+  using G = typename FrontGemm<BM, BN, WGM, WGN, FW, MODE, BK, PR>::type;
   GEMM_LDS(G);
   // two planes per store pass where the stage buffer already has room for them
   constexpr int SP = G::STAGE >= store_lds_bytes<G, TILE_NORMAL, 2>() ? 2 : 1;
@@ -71,7 +86,24 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_front(FrontArgs a) {
 
   G g;
   g.zero();
-  g.run(a.A, a.B, m0, n0, z, a.K, GEMM_STAGES);
+  if constexpr (PR == 0) {
+    g.run(a.A, a.B, m0, n0, z, a.K, GEMM_STAGES);
+  } else {
+    Operand Aq[NA * PR], Bq[NB * PR];   // one operand per plane
+#pragma unroll
+    for (int i = 0; i < NA * PR; ++i) {
+      Aq[i] = a.A[i / PR];
+      Aq[i].p += (i % PR) * a.A[i / PR].pstride;
+      Aq[i].planes = 1;
+    }
+#pragma unroll
+    for (int i = 0; i < NB * PR; ++i) {
+      Bq[i] = a.B[i / PR];
+      Bq[i].p += (i % PR) * a.B[i / PR].pstride;
+      Bq[i].planes = 1;
+    }
+    g.run(Aq, Bq, m0, n0, z, a.K, GEMM_STAGES);
+  }
 
   const float* eta = a.eta + (int64_t)z * a.eta_zstride;
   g.for_each([&](int i, int j, int v, int r, int c) __attribute__((always_inline)) {
@@ -831,12 +863,11 @@ __global__ __launch_bounds__(256) void k_split3(SplitArgs a, SplitArgs b, SplitA
 // Every GEMM kernel holds its LDS in static __shared__ arrays (GEMM_LDS): launches pass no
 // dynamic LDS.
 
-template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK = 64>
+template <int BM, int BN, int WGM, int WGN, int FW, int MODE, int BK = 64, int PR = 0>
 static hipError_t front_t(const FrontArgs& a0, int Z, hipStream_t s) {
-  using FS = FrontShape<FW, MODE>;
-  using G = Gemm<BM, BN, WGM, WGN, FS::NA, FS::NB, 0, FS::DOT ? (1 << (FS::NB - 1)) : 0, 0, BK>;
+  using G = typename FrontGemm<BM, BN, WGM, WGN, FW, MODE, BK, PR>::type;
   FrontArgs a = a0;
-  auto kern = k_front<BM, BN, WGM, WGN, FW, MODE, BK>;
+  auto kern = k_front<BM, BN, WGM, WGN, FW, MODE, BK, PR>;
   a.tiles_n = (a.N + BN - 1) / BN;
   const int tiles_m = (a.nrows + BM - 1) / BM;
   a.tiles = tiles_m * a.tiles_n;
@@ -864,12 +895,25 @@ static bool small_tiles(int rows, int cols, int Z) {
 hipError_t launch_front(int fw, int mode, const FrontArgs& a, int Z, hipStream_t s) {
   if (fw == FW_SWIGLU) {
     const bool small = small_tiles(a.nrows, a.N, Z);
-    if (mode == FRONT_Q)
+    // small launches whose operands all hold the same number (2 or 3) of planes: the
+    // plane-resident grouped product (the key-row front steps K by 32 for LDS)
+    const int na = mode == FRONT_K_DOT ? 2 : 1, nb = mode == FRONT_K_DOT ? 3 : 2;
+    int pr = a.A[0].planes;
+    for (int i = 0; i < na; ++i) pr = a.A[i].planes == pr ? pr : 0;
+    for (int i = 0; i < nb; ++i) pr = a.B[i].planes == pr ? pr : 0;
+    if (!small || pr < 2) pr = 0;
+    if (mode == FRONT_Q) {
+      if (pr == 2) return front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_Q, 64, 2>(a, Z, s);
+      if (pr == 3) return front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_Q, 64, 3>(a, Z, s);
       return small ? front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_Q, 64>(a, Z, s)
                    : front_fm<FW_SWIGLU, FRONT_Q>(a, Z, s);
-    if (mode == FRONT_K_DOT)
+    }
+    if (mode == FRONT_K_DOT) {
+      if (pr == 2) return front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_K_DOT, 32, 2>(a, Z, s);
+      if (pr == 3) return front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_K_DOT, 32, 3>(a, Z, s);
       return small ? front_t<64, 64, 2, 2, FW_SWIGLU, FRONT_K_DOT>(a, Z, s)
                    : front_t<128, 128, 2, 4, FW_SWIGLU, FRONT_K_DOT>(a, Z, s);
+    }
     return front_fm<FW_SWIGLU, FRONT_K_MSE>(a, Z, s);
   }
   if (mode == FRONT_Q) return front_fm<FW_GELU, FRONT_Q>(a, Z, s);
