@@ -5,7 +5,7 @@
 // gradient): X0 = G / (|G|_F + eps), then per iteration A = X X^T, B = b A + c A A and
 // X' = a X + B X.  The staged path runs it as three GEMM launches per iteration, which for
 // matrices of a few tens of thousands of elements are bound by each launch's latency; here
-// one workgroup of eight waves holds the whole matrix (X up to 64 x 128) and its A and B as
+// one workgroup of sixteen waves holds the whole matrix (X up to 64 x 128) and its A and B as
 // bf16 planes in LDS and runs every product on the MFMA from there.  The roundings are the
 // staged path's: A and B are stored on the iteration's product planes, X' on the iterate
 // planes, the linear term a X is folded into B as a I when the products keep the iterate's
@@ -101,52 +101,78 @@ __device__ __forceinline__ f32x16 prod_rows(const u16* A, int apst, int astr, co
   return acc;
 }
 
-// Waves w and w ^ 4 hold the two K halves of the same NT tiles.  Each keeps half of every
-// tile's accumulator (wave w >> 2 = h keeps elements 8 h .. 8 h + 7, the tile's rows
-// 16 h .. 16 h + 15 in the accumulator layout) and hands the other half to its partner
-// through red (run j of tile u of wave w at red + ((w 2 NT + 2 u + j) 64 + lane) 4:
-// consecutive lanes, consecutive 16 bytes).  On return own[u] holds the full sums of the
-// kept half, the K half 0 partial plus the K half 1 partial.  w is wave-uniform.  Contains
-// a barrier: call from every thread.
-template <int NT>
-__device__ __forceinline__ void exchange_halves(const f32x16 (&acc)[NT], float (&own)[NT][8],
-                                                float* red, int w, int lane) {
-  const int kh = w >> 2;
+// Waves w and w ^ 8 hold the two K halves of the same tile.  Each keeps half of the tile's
+// accumulator (wave w >> 3 = h keeps elements 8 h .. 8 h + 7, the tile's rows 16 h .. 16 h
+// + 15 in the accumulator layout) and hands the other half to its partner through red (run
+// j of wave w at red + ((2 w + j) 64 + lane) 4: consecutive lanes, consecutive 16 bytes).
+// On return own holds the full sums of the kept half, the K half 0 partial plus the K half
+// 1 partial.  w is wave-uniform.  Contains a barrier: call from every thread.
+__device__ __forceinline__ void exchange_halves(const f32x16& acc, float (&own)[8], float* red,
+                                                int w, int lane) {
+  const int kh = w >> 3;
 #pragma unroll
-  for (int u = 0; u < NT; ++u)
+  for (int j = 0; j < 2; ++j) {
+    f32x4 out;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f32x4 out;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = acc[u][4 * j + e], hi = acc[u][8 + 4 * j + e];
-        own[u][4 * j + e] = kh ? hi : lo;
-        out[e] = kh ? lo : hi;
-      }
-      *reinterpret_cast<f32x4*>(red + ((w * 2 * NT + 2 * u + j) * 64 + lane) * 4) = out;
+    for (int e = 0; e < 4; ++e) {
+      const float lo = acc[4 * j + e], hi = acc[8 + 4 * j + e];
+      own[4 * j + e] = kh ? hi : lo;
+      out[e] = kh ? lo : hi;
     }
+    *reinterpret_cast<f32x4*>(red + ((2 * w + j) * 64 + lane) * 4) = out;
+  }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < NT; ++u)
+  for (int j = 0; j < 2; ++j) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(red + ((2 * (w ^ 8) + j) * 64 + lane) * 4);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const f32x4 x =
-          *reinterpret_cast<const f32x4*>(red + (((w ^ 4) * 2 * NT + 2 * u + j) * 64 + lane) * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) own[u][4 * j + e] += x[e];
-    }
+    for (int e = 0; e < 4; ++e) own[4 * j + e] += x[e];
+  }
 }
 
-// One iteration with PK product planes (PK = NP folds a I into B).  Eight waves: waves w and
-// w + 4 compute tile w & 3 of each product over the two halves of its K range and then
-// finish half of the tile each.  In the accumulator layout a lane holds runs of four
-// consecutive rows of one column.  A and B are symmetric, so such a run is stored at the
-// mirror position as four consecutive columns of one row, one 8-byte LDS store a plane
-// (A's planes are read back for b A the same way); the update computes the transposed tile
-// X'^T = X^T B, so that its runs are four consecutive columns of X'.  No element needs a
-// bounds check in LDS: X is zero outside [M][N], so A is zero outside [M][M], B outside
-// [M][M] but for a on the padded diagonal (which multiplies zero rows of X), and X' is zero
-// outside [M][N] again; only the store of U to memory checks.
+// Waves w & 3 + 4 q, q = 0 .. 3, hold the four K quarters of the same tile.  Wave q = w >> 2
+// keeps run q of the accumulator (elements 4 q .. 4 q + 3, the tile's rows 8 q .. 8 q + 7)
+// and hands each of its three other runs to the wave that keeps it through red (run g of
+// wave w in slot 3 w + (g < q ? g : g - 1), 64 lanes x 16 bytes).  On return own holds the
+// kept run summed over the quarters in K order.  w is wave-uniform.  Contains a barrier:
+// call from every thread.
+__device__ __forceinline__ void exchange_quarters(const f32x16& acc, float (&own)[4],
+                                                  float* red, int w, int lane) {
+  const int kq = w >> 2, wt = w & 3;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    if (g != kq)
+      *reinterpret_cast<f32x4*>(red + ((3 * w + (g < kq ? g : g - 1)) * 64 + lane) * 4) =
+          f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) own[e] = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 x;
+    if (q == kq) {
+      x = f32x4{acc[4 * kq], acc[4 * kq + 1], acc[4 * kq + 2], acc[4 * kq + 3]};
+    } else {
+      const int slot = 3 * (4 * q + wt) + (kq < q ? kq : kq - 1);
+      x = *reinterpret_cast<const f32x4*>(red + (slot * 64 + lane) * 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) own[e] += x[e];
+  }
+}
+
+// One iteration with PK product planes (PK = NP folds a I into B).  Sixteen waves: for the
+// Gram and polynomial products waves w & 3 + 4 q compute tile w & 3 over the four quarters
+// of its K range and then finish a quarter of the tile each; for the update waves w and
+// w + 8 compute tile w & 7 over the two halves of its K range and finish half of it each.
+// In the accumulator layout a lane holds runs of four consecutive rows of one column.  A
+// and B are symmetric, so such a run is stored at the mirror position as four consecutive
+// columns of one row, one 8-byte LDS store a plane (A's planes are read back for b A the
+// same way); the update computes the transposed tile X'^T = X^T B, so that its runs are
+// four consecutive columns of X'.  No element needs a bounds check in LDS: X is zero outside
+// [M][N], so A is zero outside [M][M], B outside [M][M] but for a on the padded diagonal
+// (which multiplies zero rows of X), and X' is zero outside [M][N] again; only the store of
+// U to memory checks.
 template <int NP, int PK>
 __device__ __forceinline__ void ns_iteration(const NsArgs& a, u16* xs, u16* as_, u16* bs,
                                              float* red, int z, float s, bool first,
@@ -155,56 +181,48 @@ __device__ __forceinline__ void ns_iteration(const NsArgs& a, u16* xs, u16* as_,
   const int M = a.M, N = a.N;
   const int lane = threadIdx.x & 63, hl = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int wt = w & 3, kh = w >> 2;
+  const int wt = w & 3, kq = w >> 2;
   const int ti = wt >> 1, tj = wt & 1;
-  // first row (first column for the update) of run g of this wave's kept half, the column
-  // (row) of this lane
-  auto run0 = [&](int t, int g) { return 32 * t + 16 * kh + 8 * g + 4 * hl; };
   const int ln = lane & 31;
+  // first row of this wave's kept run of the Gram and polynomial tiles, the column of this
+  // lane
+  const int rq = 32 * ti + 8 * kq + 4 * hl;
+  const int c = 32 * tj + ln;
 
   // A = X X^T (s^2 G G^T in the first iteration)
   {
-    f32x16 acc[1] = {prod_rows<PK, SN / 2>(xs, SM * XS, XS, xs, SM * XS, XS, ti, tj,
-                                           kh * (SN / 2))};
-    float own[1][8];
-    exchange_halves<1>(acc, own, red, w, lane);
+    const f32x16 acc = prod_rows<PK, SN / 4>(xs, SM * XS, XS, xs, SM * XS, XS, ti, tj,
+                                             kq * (SN / 4));
+    float own[4];
+    exchange_quarters(acc, own, red, w, lane);
     const float s2 = first ? s * s : 1.f;
-    const int c = 32 * tj + ln;
+    float x[4];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = own[0][4 * g + e] * s2;
-      put_run(as_, SM * AS, PK, c * AS + run0(ti, g), x);   // A[c][r .. r + 3]
-    }
+    for (int e = 0; e < 4; ++e) x[e] = own[e] * s2;
+    put_run(as_, SM * AS, PK, c * AS + rq, x);   // A[c][r .. r + 3]
   }
   __syncthreads();
 
   // B = b A + c A A (+ a I folded), the linear term from A's stored planes
   {
-    f32x16 acc[1] = {prod_rows<PK, SM / 2>(as_, SM * AS, AS, as_, SM * AS, AS, ti, tj,
-                                           kh * (SM / 2))};
-    float own[1][8];
-    exchange_halves<1>(acc, own, red, w, lane);
-    const int c = 32 * tj + ln;
+    const f32x16 acc = prod_rows<PK, SM / 4>(as_, SM * AS, AS, as_, SM * AS, AS, ti, tj,
+                                             kq * (SM / 4));
+    float own[4];
+    exchange_quarters(acc, own, red, w, lane);
+    float av[4], x[4];
+    sum_run(as_, SM * AS, PK, c * AS + rq, av);   // A[r .. r + 3][c] by symmetry
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int r0 = run0(ti, g);
-      float av[4], x[4];
-      sum_run(as_, SM * AS, PK, c * AS + r0, av);   // A[r .. r + 3][c] by symmetry
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        x[e] = a.coef_b * av[e] + a.coef_c * own[0][4 * g + e] +
-               (fold && r0 + e == c ? a.coef_a : 0.f);
-      put_run(bs, SM * AS, PK, c * AS + r0, x);
-    }
+    for (int e = 0; e < 4; ++e)
+      x[e] = a.coef_b * av[e] + a.coef_c * own[e] + (fold && rq + e == c ? a.coef_a : 0.f);
+    put_run(bs, SM * AS, PK, c * AS + rq, x);
   }
   __syncthreads();
 
   // X'^T = X^T B (+ a X from all of X's planes), times s in the first iteration: tile rows
   // are columns of X', tile columns rows of X'
-  f32x16 acc[2] = {f32x16{}, f32x16{}};
-  const int ri = wt & 1, cj = 2 * (wt >> 1);
+  const int t8 = w & 7, kh = w >> 3;
+  const int ri = t8 & 1, cj = t8 >> 1;
+  f32x16 acc = f32x16{};
 #pragma unroll
   for (int qa = 0; qa < PK; ++qa)
 #pragma unroll
@@ -212,55 +230,54 @@ __device__ __forceinline__ void ns_iteration(const NsArgs& a, u16* xs, u16* as_,
 #pragma unroll
       for (int k = 0; k < SM / 2; k += 16) {
         const int k0 = kh * (SM / 2) + k;
-        const bf16x8 fb = frag_rows(bs + qa * SM * AS, AS, 32 * ri, k0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          acc[u] = mfma(frag_cols(xs + qb * SM * XS, XS, 32 * (cj + u), k0), fb, acc[u]);
+        acc = mfma(frag_cols(xs + qb * SM * XS, XS, 32 * cj, k0),
+                   frag_rows(bs + qa * SM * AS, AS, 32 * ri, k0), acc);
       }
-  float own[2][8];
-  exchange_halves<2>(acc, own, red, w, lane);   // every wave has read X once this returns
+  float own[8];
+  exchange_halves(acc, own, red, w, lane);   // every wave has read X once this returns
   const float sc = first ? s : 1.f;
   const int r = 32 * ri + ln;
   const int tr = (a.tr_mask >> (z / a.P)) & 1;
   float* U = a.U + (int64_t)z * M * N;
   // the a X term reads X only where the same lane writes X' below
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int g = 0; g < 2; ++g) {
+    const int c0 = 32 * cj + 16 * kh + 8 * g + 4 * hl;
+    float lin[4] = {0.f, 0.f, 0.f, 0.f}, x[4];
+    if (!fold) sum_run(xs, SM * XS, NP, r * XS + c0, lin);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int c0 = run0(cj + u, g);
-      float lin[4] = {0.f, 0.f, 0.f, 0.f}, x[4];
-      if (!fold) sum_run(xs, SM * XS, NP, r * XS + c0, lin);
+    for (int e = 0; e < 4; ++e) x[e] = sc * fmaf(a.coef_a, lin[e], own[4 * g + e]);
+    if (last) {
+      // N is a multiple of 16, so a run starting inside the matrix lies inside it
+      if (r < M && c0 < N) {
+        if (tr) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = sc * fmaf(a.coef_a, lin[e], own[u][4 * g + e]);
-      if (last) {
-        // N is a multiple of 16, so a run starting inside the matrix lies inside it
-        if (r < M && c0 < N) {
-          if (tr) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) U[(int64_t)(c0 + e) * M + r] = x[e];
-          } else {
-            *reinterpret_cast<float4*>(U + (int64_t)r * N + c0) = make_float4(x[0], x[1], x[2], x[3]);
-          }
+          for (int e = 0; e < 4; ++e) U[(int64_t)(c0 + e) * M + r] = x[e];
+        } else {
+          *reinterpret_cast<float4*>(U + (int64_t)r * N + c0) = make_float4(x[0], x[1], x[2], x[3]);
         }
-      } else {
-        put_run(xs, SM * XS, NP, r * XS + c0, x);
       }
+    } else {
+      put_run(xs, SM * XS, NP, r * XS + c0, x);
     }
+  }
   if (!last) __syncthreads();
 }
 
+constexpr int NS_SMALL_THREADS = 1024;   // sixteen waves
+
 template <int NP>
-__global__ __launch_bounds__(512) void k_ns_small(NsArgs a) {
+__global__ __launch_bounds__(NS_SMALL_THREADS) void k_ns_small(NsArgs a) {
   __shared__ __attribute__((aligned(16))) u16 xs[NP * SM * XS];
   __shared__ __attribute__((aligned(16))) u16 as_[NP * SM * AS];
   __shared__ __attribute__((aligned(16))) u16 bs[NP * SM * AS];
-  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 32];
+  // exchange slots: three runs of 64 lanes x 4 floats for each of the sixteen waves
+  __shared__ __attribute__((aligned(16))) float red[3 * 16 * 64 * 4];
   const int z = blockIdx.x;
   const int M = a.M, N = a.N;
 
   // the gradient's planes, zero outside [M][N]
-  for (int i = threadIdx.x; i < NP * SM * (SN / 8); i += 512) {
+  for (int i = threadIdx.x; i < NP * SM * (SN / 8); i += NS_SMALL_THREADS) {
     const int q = i / (SM * (SN / 8)), rem = i % (SM * (SN / 8));
     const int r = rem / (SN / 8), c = (rem % (SN / 8)) * 8;
     uint4 v = make_uint4(0, 0, 0, 0);
@@ -284,9 +301,9 @@ __global__ __launch_bounds__(512) void k_ns_small(NsArgs a) {
 
 hipError_t launch_ns_small(const NsArgs& a, hipStream_t st) {
   if (a.Z == 0 || a.steps == 0) return hipSuccess;
-  if (a.xin.np == 1) hipLaunchKernelGGL(k_ns_small<1>, dim3(a.Z), dim3(512), 0, st, a);
-  else if (a.xin.np == 2) hipLaunchKernelGGL(k_ns_small<2>, dim3(a.Z), dim3(512), 0, st, a);
-  else hipLaunchKernelGGL(k_ns_small<3>, dim3(a.Z), dim3(512), 0, st, a);
+  if (a.xin.np == 1) hipLaunchKernelGGL(k_ns_small<1>, dim3(a.Z), dim3(NS_SMALL_THREADS), 0, st, a);
+  else if (a.xin.np == 2) hipLaunchKernelGGL(k_ns_small<2>, dim3(a.Z), dim3(NS_SMALL_THREADS), 0, st, a);
+  else hipLaunchKernelGGL(k_ns_small<3>, dim3(a.Z), dim3(NS_SMALL_THREADS), 0, st, a);
   return hipGetLastError();
 }
 
