@@ -53,3 +53,26 @@ def test_kernel_names_shortened():
     assert P._short("void ttt::k_ns_gram<128, 4, 4, 2, 1, 1>(ttt::NsArgs)") == \
         "void ttt::k_ns_gram<128, 4, 4, 2, 1, 1>"
     assert P._short("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_stage_of_each_kernel_name():
+    # every stage kernel's name (as rocprofv3 reports it, shortened) maps to one stage
+    import re
+    cases = {
+        "void ttt::k_front<128, 128, 2, 4, 0, 0, 32, 0>": "front_q",
+        "void ttt::k_front<64, 64, 2, 2, 0, 0, 64, 3>": "front_q",
+        "void ttt::k_front<128, 128, 2, 4, 0, 1, 64, 0>": "front_k",
+        "void ttt::k_front<64, 64, 2, 2, 0, 1, 32, 2>": "front_k",
+        "void ttt::k_front<128, 128, 2, 4, 1, 2, 32, 0>": "front_k",
+        "void ttt::k_out<128, 128, 2, 4, 0, 0>": "out",
+        "void ttt::k_out<64, 64, 2, 2, 0, 3>": "out",
+        "void ttt::k_out<128, 128, 2, 4, 1, 0>": "mse",
+        "void ttt::k_out<128, 128, 2, 4, 2, 0>": "mse",
+        "void ttt::k_contract<64, 128, 2, 4, 3, 3>": "contract",
+        "void ttt::k_ns_update<128, 128, 2, 4, 2, 32, 1, 1>": "ns_update",
+        "void ttt::k_renorm<4>": "renorm",
+        "ttt::k_split3": "split",
+    }
+    for name, stage in cases.items():
+        hits = [s for s, pat, _ in P.STAGE_KERNELS if re.search(pat, name)]
+        assert hits == [stage], (name, hits)

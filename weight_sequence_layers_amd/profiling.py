@@ -31,11 +31,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # `kernels` (several patterns are alternative instantiations, e.g. by plane count) and any
 # of the `companions` (kernels launched inside the same bracket, e.g. a split-K sum)
 STAGE_KERNELS = [
-    # k_front<BM, BN, WGM, WGN, FW, MODE, BK>: MODE 0 applies, 1 and 2 take gradients
-    ("front_q", r"k_front<(\d+, ){5}0, \d+>$", None),
-    ("front_k", r"k_front<(\d+, ){5}[12], \d+>$", None),
-    ("out", r"k_out<.*, 0>$", None),
-    ("mse", r"k_out<.*, [12]>$", None),
+    # k_front<BM, BN, WGM, WGN, FW, MODE, BK, PR>: MODE 0 applies, 1 and 2 take gradients
+    ("front_q", r"k_front<(\d+, ){5}0, \d+, \d+>$", None),
+    ("front_k", r"k_front<(\d+, ){5}[12], \d+, \d+>$", None),
+    # k_out<BM, BN, WGM, WGN, MODE, PR>: MODE 0 is the query output, 1 and 2 the MSE error
+    ("out", r"k_out<(\d+, ){4}0, \d+>$", None),
+    ("mse", r"k_out<(\d+, ){4}[12], \d+>$", None),
     ("contract", r"k_contract<", r"k_contract_sum<"),
     ("ns_gram", r"k_ns_gram<", None),
     ("ns_poly", r"k_ns_poly<", None),
