@@ -962,8 +962,8 @@ hipError_t launch_out(int mode, const OutArgs& a, int Z, hipStream_t s) {
 }
 
 // Token ranges: enough for about two workgroups per CU (256 CUs) when the output tiles
-// alone are fewer, at most CONTRACT_SPLIT_MAX, each range at least 256 tokens.
-constexpr int CONTRACT_SLOTS = 512, CONTRACT_RANGE_MIN = 256;
+// alone are fewer, at most CONTRACT_SPLIT_MAX, each range at least 128 tokens.
+constexpr int CONTRACT_SLOTS = 512, CONTRACT_RANGE_MIN = 128;
 
 int contract_split_max(int tiles, int nz) {
   const int64_t wgs = (int64_t)tiles * nz;
