@@ -1,7 +1,7 @@
 """GPU parity of the backward through one chunk (ttt_chunk_backward) against the oracle's
 chunk_vjp on the same seeded inputs and cotangents: the input gradients dq, dk, dv, deta
 and the state cotangent before the chunk, for the SwiGLU net with the inner-product loss,
-with and without Muon and the row renorm, with step sizes and weight decay, fp32 and bf16,
+under both orders, with and without Muon and the row renorm, with step sizes and weight decay, fp32 and bf16,
 at ragged small sizes, at the LaCT language-model chunk, and chained over a short sequence
 (each call from the state before its chunk).  Errors are max relative errors
 |x - y|_inf / |y|_inf per tensor; bars 1e-4 (fp32) and 2e-2 (bf16)."""
@@ -107,6 +107,17 @@ def test_chunk_backward_chained_over_three_chunks():
     _check(cfg)
 
 
+@pytest.mark.parametrize("act,ns,renorm", [("f32", 5, True), ("bf16", 0, True), ("f32", 0, False)])
+def test_chunk_backward_update_then_apply(act, ns, renorm):
+    # the queries see the updated state: the apply backward at the state after the update,
+    # its weight gradient taken back through the update; chained over two chunks, with step
+    # sizes and weight decay in the first case
+    kw = dict(lr=(0.7, 1.2, 0.9), weight_decay=0.02) if ns else {}
+    cfg = ti.Config("cbu2", 2, 1, 256, 128, 64, 128, "swiglu", "dot", ns, renorm, act,
+                    "update_then_apply", 95, **kw)
+    _check(cfg)
+
+
 def test_chunk_backward_lm_chunk():
     # the LaCT language-model layer's shape and precision preset, one chunk of 2048 tokens
     lm = ti.CONFIGS["lm"]
@@ -116,7 +127,7 @@ def test_chunk_backward_lm_chunk():
 
 def test_chunk_backward_refuses_other_configurations():
     for kw in (dict(fw="gelu"), dict(loss="mse", ns_steps=0, renorm=False),
-               dict(order="update_then_apply")):
+               dict(momentum=0.5)):
         cfg = ti.Config("cbu", 1, 1, 128, 128, 64, 128, "swiglu", "dot", 5, True, "bf16",
                         "apply_then_update", 94).replace(**kw)
         c = W.make_config(cfg, path="staged")
@@ -129,3 +140,29 @@ def test_chunk_backward_refuses_other_configurations():
                                  torch.empty_like(q), torch.empty_like(q), torch.empty_like(eta))
         assert e.value.status == 5
         st.destroy()
+
+
+def test_chunk_backward_update_then_apply_leaves_the_state():
+    # the update-then-apply backward forms the updated state in place of the state and
+    # restores it: the state (and its planes, through a forward call) is bitwise unchanged
+    cfg = ti.Config("cbu3", 1, 2, 128, 128, 64, 128, "swiglu", "dot", 5, True, "bf16",
+                    "update_then_apply", 96)
+    c = W.make_config(cfg, path="staged")
+    inp = ti.make_inputs(cfg)
+    q, k, v, eta, w0 = device_inputs(cfg, inp)
+    st = W.ttt_init_state(c, w0)
+    _, before = read_state(c, st)
+    before = before.clone()
+    out0 = torch.empty_like(q)
+    W.ttt_chunk_forward(st, q, k, v, eta, out0)
+    W.ttt_set_state(st, before)
+    dw = torch.ones(W.ttt_state_numel(c), device="cuda")
+    W.ttt_chunk_backward(st, q, k, v, eta, q, dw, torch.empty_like(q), torch.empty_like(q),
+                         torch.empty_like(q), torch.empty_like(eta))
+    _, after = read_state(c, st)
+    assert torch.equal(after, before)
+    out1 = torch.empty_like(q)
+    W.ttt_chunk_forward(st, q, k, v, eta, out1)
+    torch.cuda.synchronize()
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    st.destroy()

@@ -199,6 +199,7 @@ struct ttt_state {
     char* arena = nullptr;
     float *g32 = nullptr, *du = nullptr, *dx32[2] = {}, *t32 = nullptr, *dg32 = nullptr;
     float *dws = nullptr, *dwg = nullptr, *dwa = nullptr;
+    float* wbak = nullptr;          // update-then-apply: the weights before the chunk
     float *dotpart = nullptr, *eta_part = nullptr;
     u16* xit[8] = {};               // Newton-Schulz iterates 1..steps-1 (0 is xpl[0])
     u16 *dxp[2] = {}, *tp = nullptr, *sp = nullptr, *dgp = nullptr;
@@ -810,6 +811,8 @@ ttt_status ensure_bwd(ttt_state* s) {
   size_t odg = C.take<float>(xs), odgp = C.take<u16>(D.gp * xs);
   const int64_t sn = weights_numel(D);
   size_t ows = C.take<float>(sn), owg = C.take<float>(sn), owa = C.take<float>(sn);
+  const bool uta = c.order == TTT_UPDATE_THEN_APPLY;
+  size_t owb = uta ? C.take<float>(sn) : 0;
   size_t oep = C.take<float>(P * sb * ((dh + 63) / 64));
   size_t opd = C.take<u16>(D.gp * P * sb * dh), oa1 = C.take<u16>(D.gp * P * sb * dh),
          oa3 = C.take<u16>(D.gp * P * sb * dh);
@@ -832,6 +835,7 @@ ttt_status ensure_bwd(ttt_state* s) {
   }
   b.dg32 = F(odg); b.dgp = H(odgp);
   b.dws = F(ows); b.dwg = F(owg); b.dwa = F(owa);
+  b.wbak = uta ? F(owb) : nullptr;
   b.eta_part = F(oep);
   b.pd = H(opd); b.a1 = H(oa1); b.a3 = H(oa3);
   return TTT_OK;
@@ -1024,13 +1028,35 @@ ttt_status chunk_backward(ttt_state* s, const void* q, const void* k, const void
     if ((r = grad_rows(s, block(o), o == 0, o + D.sb >= ch, st, muon ? b.g32 : nullptr)) != TTT_OK)
       return r;
   if (muon && (r = newton_schulz(s, st, b.xit)) != TTT_OK) return r;
+  const int64_t sn = weights_numel(D);
+  // dout of the step: the cotangent of the state after the chunk, and under the
+  // update-then-apply order also the apply step's (its queries saw the updated state)
+  const float* dw_after = dw;
+  if (c.order == TTT_UPDATE_THEN_APPLY) {
+    // 1b. the updated state in place of the state (the apply kernels read the state's
+    //     planes), the apply backward with it, then the state before the chunk back
+    HIP_TRY(hipMemcpyAsync(b.wbak, s->W, sn * sizeof(float), hipMemcpyDeviceToDevice, st));
+    if ((r = refresh_planes(s, true, st)) != TTT_OK) return r;
+    for (int64_t o = 0; o < ch; o += D.sb) {
+      Rows R = block(o);
+      R.v = static_cast<const char*>(dout);
+      R.out = static_cast<char*>(dq);
+      if ((r = apply_bwd_rows(s, R, o == 0, o + D.sb >= ch, b.dwa, st)) != TTT_OK) return r;
+    }
+    HIP_TRY(hipMemcpyAsync(s->W, b.wbak, sn * sizeof(float), hipMemcpyDeviceToDevice, st));
+    if ((r = refresh_planes(s, false, st)) != TTT_OK) return r;
+    Add3Args ad{};
+    ad.x = b.dwa; ad.y = dw; ad.out = b.dwa; ad.n = sn;
+    STAGED(TTT_STAGE_RENORM, launch_add3(ad, st));
+    dw_after = b.dwa;
+  }
   // 2. step and renorm: dW_step, and dU in the X orientation
   StepBwdArgs sb{};
   sb.P = D.P; sb.nm = D.nm; sb.renorm = c.row_renorm; sb.keep = 1.f - c.weight_decay;
   int64_t off = 0, xoff = 0;
   for (int m = 0; m < D.nm; ++m) {
     StepBwdMat& M = sb.m[m];
-    M.W = s->Wm[m]; M.U = s->Um[m]; M.dout = dw + off; M.dw = b.dws + off;
+    M.W = s->Wm[m]; M.U = s->Um[m]; M.dout = dw_after + off; M.dw = b.dws + off;
     M.du = b.du + xoff;
     M.rows = D.rows[m]; M.cols = D.cols[m]; M.tr = D.tr[m]; M.lr = c.lr[m];
     sb.max_rows = std::max(sb.max_rows, D.rows[m]);
@@ -1052,15 +1078,18 @@ ttt_status chunk_backward(ttt_state* s, const void* q, const void* k, const void
     if ((r = grad_bwd_rows(s, block(o), o == 0, o + D.sb >= ch, dk, dv, deta, st)) != TTT_OK)
       return r;
   // 5. the apply step (the shifted order answers with the state before the update)
-  for (int64_t o = 0; o < ch; o += D.sb) {
+  const bool shifted = c.order == TTT_APPLY_THEN_UPDATE;
+  for (int64_t o = 0; shifted && o < ch; o += D.sb) {
     Rows R = block(o);
     R.v = static_cast<const char*>(dout);
     R.out = static_cast<char*>(dq);
     if ((r = apply_bwd_rows(s, R, o == 0, o + D.sb >= ch, b.dwa, st)) != TTT_OK) return r;
   }
-  // 6. dW before the chunk
+  // 6. dW before the chunk (the update-then-apply order's apply part went into the step's
+  //    cotangent above)
   Add3Args ad{};
-  ad.x = b.dwa; ad.y = b.dws; ad.w = b.dwg; ad.out = dw; ad.n = weights_numel(D);
+  ad.x = shifted ? b.dwa : b.dws; ad.y = shifted ? b.dws : b.dwg; ad.w = shifted ? b.dwg : nullptr;
+  ad.out = dw; ad.n = sn;
   STAGED(TTT_STAGE_RENORM, launch_add3(ad, st));
   return TTT_OK;
 }
@@ -1338,11 +1367,11 @@ ttt_status ttt_chunk_backward(ttt_state* s, const void* q, const void* k, const 
     return r;
   const ttt_config& c = s->cfg;
   if (s->resident || c.fw != TTT_FW_SWIGLU || c.loss != TTT_LOSS_DOT ||
-      c.order != TTT_APPLY_THEN_UPDATE || c.chunk > SUBBLOCK_MAX || c.momentum > 0.f)
+      c.chunk > SUBBLOCK_MAX || c.momentum > 0.f)
     return fail(TTT_E_UNSUPPORTED,
-                "the chunk backward serves the SwiGLU net with the inner-product loss under "
-                "the shifted (apply-then-update) order, on the staged path, with chunks of "
-                "at most %lld tokens and no momentum", (long long)SUBBLOCK_MAX);
+                "the chunk backward serves the SwiGLU net with the inner-product loss, on the "
+                "staged path, with chunks of at most %lld tokens and no momentum",
+                (long long)SUBBLOCK_MAX);
   hipStream_t st = static_cast<hipStream_t>(stream);
   s->last = st;
   return chunk_backward(s, q, k, v, eta, dout, dw, dq, dk, dv, deta, st);
