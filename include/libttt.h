@@ -238,9 +238,10 @@ ttt_status ttt_apply_backward(ttt_state* s, const void* q, const void* dout, voi
  * order the apply step is taken back with the state before the update; under the
  * update-then-apply order with the updated state, its weight gradient joining dw before the
  * update is taken back (the updated state is formed in place of the state for that and the
- * state before the chunk restored, bit for bit).  Serves the SwiGLU net with the
- * inner-product loss on the staged path, with chunks of at most 65536 tokens and no
- * momentum; other configurations return TTT_E_UNSUPPORTED.  The state is not changed.  The first call on a state allocates the backward's workspace (about
+ * state before the chunk restored, bit for bit).  Chunks longer than 65536 tokens are taken
+ * in token blocks, as the forward takes them.  Serves the SwiGLU net with the inner-product
+ * loss on the staged path, with no momentum; other configurations return
+ * TTT_E_UNSUPPORTED.  The state is not changed.  The first call on a state allocates the backward's workspace (about
  * 3 GB for the LaCT language-model layer; TTT_E_ALLOC if it cannot); later calls allocate
  * nothing.  All pointers device, caller-owned, 16-byte aligned; enqueued on stream.
  */

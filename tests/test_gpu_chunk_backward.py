@@ -118,6 +118,15 @@ def test_chunk_backward_update_then_apply(act, ns, renorm):
     _check(cfg)
 
 
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+def test_chunk_backward_two_token_blocks(order):
+    # a chunk longer than one token block (65536 tokens): the recompute's two contractions
+    # keep separate running sums over the blocks, the backward's launches walk the blocks
+    cfg = ti.Config("cbb", 1, 1, 66000, 66000, 64, 128, "swiglu", "dot", 5, True, "bf16",
+                    order, 97)
+    _check(cfg)
+
+
 def test_chunk_backward_lm_chunk():
     # the LaCT language-model layer's shape and precision preset, one chunk of 2048 tokens
     lm = ti.CONFIGS["lm"]

@@ -436,11 +436,15 @@ ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
 // The chunk-summed contractions of one token block into G, and after the chunk's last
 // block into U (plain step; weight orientation) or the first Newton-Schulz input (muon).
 // ca holds the per-matrix operands and sizes.
+// gsum: the running sum over a chunk's token blocks in another buffer than the state's G
+// (a second contraction of the same blocks, interleaved with the first).
 ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool first,
-                        bool last, hipStream_t st, bool weight_orient = true) {
+                        bool last, hipStream_t st, bool weight_orient = true,
+                        float* gsum = nullptr) {
   const Dims& D = s->D;
   const int P = D.P, d = D.d;
-  ca.G = s->G;
+  float* const G = gsum ? gsum : s->G;
+  ca.G = G;
   ca.accum_in = first ? 0 : 1;
   ca.last = last ? 1 : 0;
   ca.muon = muon;
@@ -460,7 +464,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
     while (m1 < D.nm && ca.a[m1].planes == ca.a[m0].planes && ca.b[m1].planes == ca.b[m0].planes) ++m1;
     ContractArgs cg = ca;
     for (int m = m0; m < m1; ++m) { cg.a[m - m0] = ca.a[m]; cg.b[m - m0] = ca.b[m]; }
-    cg.G = s->G + (int64_t)m0 * P * d * D.n;
+    cg.G = G + (int64_t)m0 * P * d * D.n;
     if (s->gpart) cg.gpart = s->gpart + (int64_t)m0 * P * d * D.n;
     cg.U = U + (int64_t)m0 * P * d * D.n;
     if (ca.mom) cg.mom = ca.mom + (int64_t)m0 * P * d * D.n;
@@ -597,7 +601,9 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
   ttt_status r = contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
   if (r != TTT_OK || !g32) return r;
   ca.mom = nullptr;
-  return contract_all(s, ca, g32, false, first, last, st, false);
+  // the X-orientation sum keeps its own running sum across the chunk's token blocks (in
+  // g32 itself: each element is read and written by the same thread)
+  return contract_all(s, ca, g32, false, first, last, st, false, g32);
 }
 
 // keep: write iterate it + 1 to keep[it + 1] (kept for the backward) instead of the
@@ -1366,12 +1372,10 @@ ttt_status ttt_chunk_backward(ttt_state* s, const void* q, const void* k, const 
       (r = check_ptr(deta, "deta")))
     return r;
   const ttt_config& c = s->cfg;
-  if (s->resident || c.fw != TTT_FW_SWIGLU || c.loss != TTT_LOSS_DOT ||
-      c.chunk > SUBBLOCK_MAX || c.momentum > 0.f)
+  if (s->resident || c.fw != TTT_FW_SWIGLU || c.loss != TTT_LOSS_DOT || c.momentum > 0.f)
     return fail(TTT_E_UNSUPPORTED,
                 "the chunk backward serves the SwiGLU net with the inner-product loss, on the "
-                "staged path, with chunks of at most %lld tokens and no momentum",
-                (long long)SUBBLOCK_MAX);
+                "staged path, with no momentum");
   hipStream_t st = static_cast<hipStream_t>(stream);
   s->last = st;
   return chunk_backward(s, q, k, v, eta, dout, dw, dq, dk, dv, deta, st);
