@@ -548,17 +548,30 @@ def update_state_vjp(Ws, grads, dWs_new, ns_steps: int, renorm: bool,
     return dW_out, dG_out
 
 
+def _split_momentum(cfg, Ws):
+    """(matrices, momentum buffers, beta) of a state list: with cfg.momentum = beta > 0 the
+    list holds the matrices followed by their buffers, else the matrices alone."""
+    beta = float(getattr(cfg, "momentum", 0.0))
+    nm = len(Ws) // 2 if beta else len(Ws)
+    return list(Ws[:nm]), list(Ws[nm:]), beta
+
+
 def chunk_step(cfg, Ws, Q, K, V, eta, update: bool = True):
-    """One chunk of the layer loop (sequence_forward's body): (O, new matrices)."""
+    """One chunk of the layer loop (sequence_forward's body): (O, new state). With momentum
+    the state is the matrices followed by their momentum buffers."""
     Ws = [np.asarray(w, np.float64) for w in Ws]
+    W, M, beta = _split_momentum(cfg, Ws)
     if not update:
-        return fw_apply(cfg.fw, Ws, Q), Ws
-    O = fw_apply(cfg.fw, Ws, Q) if cfg.order == APPLY_THEN_UPDATE else None
-    g = chunk_gradient(cfg.fw, cfg.loss, Ws, K, V, eta)
-    Wn = update_state(Ws, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
+        return fw_apply(cfg.fw, W, Q), Ws
+    O = fw_apply(cfg.fw, W, Q) if cfg.order == APPLY_THEN_UPDATE else None
+    g = chunk_gradient(cfg.fw, cfg.loss, W, K, V, eta)
+    if beta:
+        M = momentum_step(M, g, beta)
+        g = M
+    Wn = update_state(W, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
     if O is None:
         O = fw_apply(cfg.fw, Wn, Q)
-    return O, Wn
+    return O, Wn + M
 
 
 def chunk_vjp(cfg, Ws, Q, K, V, eta, dO, dWs_new, update: bool = True):
@@ -567,39 +580,52 @@ def chunk_vjp(cfg, Ws, Q, K, V, eta, dO, dWs_new, update: bool = True):
     to the chunk's inputs and the state before it. The apply's part comes from apply_vjp
     (with the state the queries saw: before the update under the shifted order, after it
     under the update-then-apply order), the update's from update_state_vjp and
-    gradient_vjp. Returns (dQ, dK, dV, deta, [dW before the chunk])."""
-    if getattr(cfg, "momentum", 0.0):
-        raise ValueError("the chunk backward takes configurations without momentum")
+    gradient_vjp. With momentum the step's input is the new buffer M' = beta M + g: the
+    cotangent of M' (from the step, plus the one given for the buffer after the chunk)
+    reaches the chunk gradient whole and the buffer before the chunk times beta.
+    Returns (dQ, dK, dV, deta, [dW before the chunk]) in the state's layout."""
     Ws = [np.asarray(w, np.float64) for w in Ws]
     dWs_new = [np.asarray(x, np.float64) for x in dWs_new]
+    W, M, beta = _split_momentum(cfg, Ws)
+    dWn, dMn, _ = _split_momentum(cfg, dWs_new)
     n = len(eta)
     if not update:
-        dQ, dWa = apply_vjp(cfg.fw, Ws, Q, dO)
+        dQ, dWa = apply_vjp(cfg.fw, W, Q, dO)
         return (dQ, np.zeros((n, cfg.dim)), np.zeros((n, cfg.dim)), np.zeros(n),
-                [a + b for a, b in zip(dWs_new, dWa)])
-    g = chunk_gradient(cfg.fw, cfg.loss, Ws, K, V, eta)
+                [a + b for a, b in zip(dWn, dWa)] + dMn)
+    g = chunk_gradient(cfg.fw, cfg.loss, W, K, V, eta)
+    if beta:
+        g = momentum_step(M, g, beta)
     if cfg.order == APPLY_THEN_UPDATE:
-        dQ, dW_apply = apply_vjp(cfg.fw, Ws, Q, dO)
-        dW_into_new = dWs_new
+        dQ, dW_apply = apply_vjp(cfg.fw, W, Q, dO)
+        dW_into_new = dWn
     else:
-        Wn = update_state(Ws, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
+        Wn = update_state(W, g, cfg.ns_steps, cfg.renorm, cfg.step_sizes(), cfg.weight_decay)
         dQ, dWa_new = apply_vjp(cfg.fw, Wn, Q, dO)
-        dW_apply = [np.zeros_like(w) for w in Ws]
-        dW_into_new = [a + b for a, b in zip(dWs_new, dWa_new)]
-    dW_step, dG = update_state_vjp(Ws, g, dW_into_new, cfg.ns_steps, cfg.renorm,
+        dW_apply = [np.zeros_like(w) for w in W]
+        dW_into_new = [a + b for a, b in zip(dWn, dWa_new)]
+    dW_step, dG = update_state_vjp(W, g, dW_into_new, cfg.ns_steps, cfg.renorm,
                                    cfg.step_sizes(), cfg.weight_decay)
-    dW_grad, dK, dV, deta = gradient_vjp(cfg.fw, cfg.loss, Ws, K, V, eta, dG)
+    dM = []
+    if beta:
+        dG = [a + b for a, b in zip(dG, dMn)]
+        dM = [beta * x for x in dG]
+    dW_grad, dK, dV, deta = gradient_vjp(cfg.fw, cfg.loss, W, K, V, eta, dG)
     dW = [a + b + c for a, b, c in zip(dW_apply, dW_step, dW_grad)]
-    return dQ, dK, dV, deta, dW
+    return dQ, dK, dV, deta, dW + dM
 
 
 def sequence_vjp(cfg, W0s, Q, K, V, eta, dO, dW_final=None, update_chunks=None):
     """Backward of sequence_forward for one problem: the states before every chunk are
-    recomputed forward, then the chunks are taken back from the last to the first.
+    recomputed forward, then the chunks are taken back from the last to the first. With
+    momentum the buffers start at zero, dW_final covers the matrices and then the buffers,
+    and so does the returned list.
     Returns (dQ, dK, dV, deta, [dW0])."""
     T = len(eta)
     b = cfg.chunk
     Ws = [np.asarray(w, np.float64) for w in W0s]
+    if getattr(cfg, "momentum", 0.0):
+        Ws = Ws + [np.zeros_like(w) for w in Ws]
     states = []
     for c in range(T // b):
         states.append(Ws)

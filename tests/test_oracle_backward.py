@@ -15,14 +15,17 @@ import oracle.ttt_oracle as orc
 from ttt_inputs import Config
 
 
-def _cfg(fw, loss, ns, renorm, order="apply_then_update", chunk=3, d=3, dh=4, lr=(), wd=0.0):
+def _cfg(fw, loss, ns, renorm, order="apply_then_update", chunk=3, d=3, dh=4, lr=(), wd=0.0,
+         mom=0.0):
     return Config("b", 1, 1, chunk, chunk, d, dh, fw, loss, ns, renorm, "f32", order,
-                  lr=tuple(lr), weight_decay=wd)
+                  lr=tuple(lr), weight_decay=wd, momentum=mom)
 
 
 def _problem(cfg, seed, wscale=0.6):
     rng = np.random.default_rng(seed)
     shapes = cfg.matrix_shapes() if cfg.fw != "linear" else [(cfg.dim, cfg.dim)]
+    if cfg.momentum:       # the state: the matrices, then their momentum buffers
+        shapes = shapes + shapes
     Ws = [rng.standard_normal(s) * wscale for s in shapes]
     n, d = cfg.chunk, cfg.dim
     Q, K, V = (rng.standard_normal((n, d)) for _ in range(3))
@@ -170,14 +173,16 @@ def test_renorm_vjp_zero_row_passes_through():
     assert np.array_equal(dY[0], d[0]) and np.array_equal(dW[0], [0.0, 0.0])
 
 
-def sequence_vjp_fd_error(update_chunks=None, seed=3, eps=1e-6):
-    cfg = Config("s", 1, 1, 9, 3, 3, 4, "swiglu", "dot", 5, True, "f32", "apply_then_update")
+def sequence_vjp_fd_error(update_chunks=None, seed=3, eps=1e-6, mom=0.0,
+                          order="apply_then_update"):
+    cfg = Config("s", 1, 1, 9, 3, 3, 4, "swiglu", "dot", 5, True, "f32", order, momentum=mom)
     rng = np.random.default_rng(seed)
     Ws = [rng.standard_normal(s) * 0.6 for s in cfg.matrix_shapes()]
     Q, K, V = (rng.standard_normal((9, 3)) for _ in range(3))
     eta = 0.05 + 0.3 * rng.random(9)
     dO = rng.standard_normal((9, 3))
-    dWf = [rng.standard_normal(s) for s in cfg.matrix_shapes()]
+    # the cotangent of the final state (with momentum: of the buffers too)
+    dWf = [rng.standard_normal(s) for s in cfg.matrix_shapes() * (2 if mom else 1)]
 
     def obj(Ws_, K_):
         O, Wf = orc.sequence_forward(cfg, Ws_, Q, K_, V, eta, update_chunks=update_chunks)
@@ -206,6 +211,37 @@ def test_sequence_vjp_matches_finite_differences(mask):
     assert sequence_vjp_fd_error(mask) < 1e-6
 
 
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+@pytest.mark.parametrize("nsr", [(5, True), (0, False)])
+def test_chunk_vjp_with_momentum_matches_finite_differences(order, nsr):
+    # every entry of the state, the momentum buffers included, perturbed
+    cfg = _cfg("swiglu", "dot", nsr[0], nsr[1], order, lr=(0.7, 1.3, 0.9), wd=0.03, mom=0.6)
+    assert chunk_vjp_fd_error(cfg, seed=4) < 1e-6
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+def test_sequence_vjp_with_momentum_matches_finite_differences(order):
+    # finite differences of sequence_forward itself (its momentum pinned by its own tests)
+    assert sequence_vjp_fd_error((1, 0, 1), seed=5, mom=0.6, order=order) < 1e-6
+    assert sequence_vjp_fd_error(None, seed=6, mom=0.3, order=order) < 1e-6
+
+
+def test_chunk_step_with_momentum_chains_to_the_sequence_forward():
+    cfg = Config("s", 1, 1, 12, 4, 3, 4, "swiglu", "dot", 5, True, "f32", "update_then_apply",
+                 momentum=0.5)
+    rng = np.random.default_rng(8)
+    W0 = [rng.standard_normal(s) * 0.6 for s in cfg.matrix_shapes()]
+    Q, K, V = (rng.standard_normal((12, 3)) for _ in range(3))
+    eta = 0.05 + 0.3 * rng.random(12)
+    O, Wf = orc.sequence_forward(cfg, W0, Q, K, V, eta)
+    state = W0 + [np.zeros_like(w) for w in W0]
+    for c in range(3):
+        S = slice(4 * c, 4 * c + 4)
+        Oc, state = orc.chunk_step(cfg, state, Q[S], K[S], V[S], eta[S])
+        assert np.array_equal(Oc, O[S])
+    assert len(state) == 6 and all(np.array_equal(a, b) for a, b in zip(state, Wf))
+
+
 # ------------------------------------------------------------------ planted mistakes
 def _pins_pass():
     checks = [
@@ -214,6 +250,7 @@ def _pins_pass():
         chunk_vjp_fd_error(_cfg("gelu", "dot", 0, False)) < 1e-6,
         chunk_vjp_fd_error(_cfg("gelu", "mse", 5, False, "update_then_apply")) < 1e-6,
         sequence_vjp_fd_error((1, 0, 1)) < 1e-6,
+        chunk_vjp_fd_error(_cfg("swiglu", "dot", 5, True, mom=0.6), seed=4) < 1e-6,
     ]
     return all(checks)
 
@@ -284,7 +321,29 @@ def _mut_chunk_vjp_old_state(cfg, Ws, Q, K, V, eta, dO, dWs_new, update=True):
     return _ORIG_CHUNK_VJP(cfg, Ws, Q, K, V, eta, dO, dWs_new, update)
 
 
+def _mut_chunk_vjp_momentum_beta(cfg, Ws, Q, K, V, eta, dO, dWs_new, update=True):
+    # the buffer before the chunk given the cotangent of the new buffer without beta
+    out = _ORIG_CHUNK_VJP(cfg, Ws, Q, K, V, eta, dO, dWs_new, update)
+    if not cfg.momentum:
+        return out
+    nm = len(Ws) // 2
+    return out[:4] + (out[4][:nm] + [x / cfg.momentum for x in out[4][nm:]],)
+
+
+def _mut_chunk_vjp_momentum_bypass(cfg, Ws, Q, K, V, eta, dO, dWs_new, update=True):
+    # the new buffer's given cotangent passed to the old buffer only, not to the gradient
+    if not cfg.momentum:
+        return _ORIG_CHUNK_VJP(cfg, Ws, Q, K, V, eta, dO, dWs_new, update)
+    nm = len(Ws) // 2
+    zero = list(dWs_new[:nm]) + [np.zeros_like(x) for x in dWs_new[nm:]]
+    out = _ORIG_CHUNK_VJP(cfg, Ws, Q, K, V, eta, dO, zero, update)
+    return out[:4] + (out[4][:nm] + [a + cfg.momentum * np.asarray(b)
+                                     for a, b in zip(out[4][nm:], dWs_new[nm:])],)
+
+
 @pytest.mark.parametrize("name,target,mut", [
+    ("momentum beta", "chunk_vjp", _mut_chunk_vjp_momentum_beta),
+    ("momentum bypass", "chunk_vjp", _mut_chunk_vjp_momentum_bypass),
     ("silu'' term", "silu_second", _mut_silu_second),
     ("gelu'' term", "gelu_second", _mut_gelu_second),
     ("Gram transpose", "newton_schulz5_vjp", _mut_ns_vjp),
