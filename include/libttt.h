@@ -239,9 +239,12 @@ ttt_status ttt_apply_backward(ttt_state* s, const void* q, const void* dout, voi
  * update-then-apply order with the updated state, its weight gradient joining dw before the
  * update is taken back (the updated state is formed in place of the state for that and the
  * state before the chunk restored, bit for bit).  Chunks longer than 65536 tokens are taken
- * in token blocks, as the forward takes them.  Serves the SwiGLU net with the inner-product
- * loss on the staged path, with no momentum; other configurations return
- * TTT_E_UNSUPPORTED.  The state is not changed.  The first call on a state allocates the backward's workspace (about
+ * in token blocks, as the forward takes them.  With momentum the state holds the
+ * heavy-ball buffers after the matrices, and so do dw in and out: the step's input is the
+ * new buffer beta M + g, whose cotangent (from the step, plus dw's part for the buffer
+ * after the chunk) is taken back into the chunk gradient whole and into the buffer before
+ * the chunk times beta.  Serves the SwiGLU net with the inner-product loss on the staged
+ * path; other configurations return TTT_E_UNSUPPORTED.  The state is not changed.  The first call on a state allocates the backward's workspace (about
  * 3 GB for the LaCT language-model layer; TTT_E_ALLOC if it cannot); later calls allocate
  * nothing.  All pointers device, caller-owned, 16-byte aligned; enqueued on stream.
  */

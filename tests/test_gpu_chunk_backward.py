@@ -1,7 +1,8 @@
 """GPU parity of the backward through one chunk (ttt_chunk_backward) against the oracle's
 chunk_vjp on the same seeded inputs and cotangents: the input gradients dq, dk, dv, deta
 and the state cotangent before the chunk, for the SwiGLU net with the inner-product loss,
-under both orders, with and without Muon and the row renorm, with step sizes and weight decay, fp32 and bf16,
+under both orders, with and without Muon and the row renorm, with step sizes, weight decay
+and momentum, fp32 and bf16,
 at ragged small sizes, at the LaCT language-model chunk, and chained over a short sequence
 (each call from the state before its chunk).  Errors are max relative errors
 |x - y|_inf / |y|_inf per tensor; bars 1e-4 (fp32) and 2e-2 (bf16)."""
@@ -27,8 +28,8 @@ def _cotangents(cfg, seed):
     bits = None
     if cfg.act == "bf16":
         dO, bits = ti.bf16_round(dO)
-    dWs = [rng.standard_normal((cfg.batch, cfg.heads) + s).astype(np.float32)
-           for s in cfg.matrix_shapes()]
+    shapes = cfg.matrix_shapes() * (2 if cfg.momentum else 1)   # with the momentum buffers
+    dWs = [rng.standard_normal((cfg.batch, cfg.heads) + s).astype(np.float32) for s in shapes]
     return dO, bits, dWs
 
 
@@ -134,9 +135,19 @@ def test_chunk_backward_lm_chunk():
     _check(cfg, problems=[(0, 0), (3, 1)])
 
 
+@pytest.mark.parametrize("act,ns,renorm,order", [
+    ("f32", 5, True, "apply_then_update"), ("bf16", 5, True, "update_then_apply"),
+    ("f32", 0, False, "update_then_apply"), ("bf16", 0, True, "apply_then_update")])
+def test_chunk_backward_momentum(act, ns, renorm, order):
+    # heavy-ball buffers in the state: their cotangents in and out, over two chunks, at
+    # ragged sizes (the buffers' transposed tiles cut at the matrix edges)
+    cfg = ti.Config("cbm", 1, 2, 256, 128, 80, 176, "swiglu", "dot", ns, renorm, act, order,
+                    98, lr=(0.8, 1.1, 0.9), weight_decay=0.02, momentum=0.6)
+    _check(cfg)
+
+
 def test_chunk_backward_refuses_other_configurations():
-    for kw in (dict(fw="gelu"), dict(loss="mse", ns_steps=0, renorm=False),
-               dict(momentum=0.5)):
+    for kw in (dict(fw="gelu"), dict(loss="mse", ns_steps=0, renorm=False)):
         cfg = ti.Config("cbu", 1, 1, 128, 128, 64, 128, "swiglu", "dot", 5, True, "bf16",
                         "apply_then_update", 94).replace(**kw)
         c = W.make_config(cfg, path="staged")
@@ -151,11 +162,13 @@ def test_chunk_backward_refuses_other_configurations():
         st.destroy()
 
 
-def test_chunk_backward_update_then_apply_leaves_the_state():
+@pytest.mark.parametrize("momentum", [0.0, 0.5])
+def test_chunk_backward_update_then_apply_leaves_the_state(momentum):
     # the update-then-apply backward forms the updated state in place of the state and
-    # restores it: the state (and its planes, through a forward call) is bitwise unchanged
+    # restores it, and reads the momentum buffers without replacing them: the state (and
+    # its planes, through a forward call) is bitwise unchanged
     cfg = ti.Config("cbu3", 1, 2, 128, 128, 64, 128, "swiglu", "dot", 5, True, "bf16",
-                    "update_then_apply", 96)
+                    "update_then_apply", 96, momentum=momentum)
     c = W.make_config(cfg, path="staged")
     inp = ti.make_inputs(cfg)
     q, k, v, eta, w0 = device_inputs(cfg, inp)

@@ -456,7 +456,9 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   ca.gpart = s->gpart;
   ca.gpart_stride = (int64_t)D.nm * P * d * D.n;
   ca.ksplit = s->ksplit;
-  ca.tr_mask = weight_orient ? (D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2)) : 0;
+  const int wtr = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
+  ca.tr_mask = weight_orient ? wtr : 0;
+  ca.mom_tr = wtr;   // the momentum buffers keep the weight orientation
   // operands of one launch share a plane count per side: group the matrices accordingly
   int m0 = 0;
   while (m0 < D.nm) {
@@ -468,6 +470,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
     if (s->gpart) cg.gpart = s->gpart + (int64_t)m0 * P * d * D.n;
     cg.U = U + (int64_t)m0 * P * d * D.n;
     if (ca.mom) cg.mom = ca.mom + (int64_t)m0 * P * d * D.n;
+    cg.mom_tr = ca.mom_tr >> m0;
     if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
     cg.part = s->part + (int64_t)m0 * P * s->part_n;
     cg.tr_mask = ca.tr_mask >> m0;
@@ -477,10 +480,11 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   return TTT_OK;
 }
 
-// g32: also sum the gradient, in the X orientation, into this fp32 buffer (the backward's
-// Newton-Schulz scaling needs it).
+// g32: also sum the step's input (the gradient, with momentum beta M + the gradient), in the
+// X orientation, into this fp32 buffer (the backward's Newton-Schulz scaling needs it).
+// read_mom: the momentum buffers are read, not replaced (the backward's recompute).
 ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStream_t st,
-                     float* g32 = nullptr) {
+                     float* g32 = nullptr, bool read_mom = false) {
   const Dims& D = s->D;
   const ttt_config& c = s->cfg;
   const size_t es = c.act == TTT_BF16 ? 2 : 4;
@@ -597,10 +601,11 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
   if (D.mom) {   // the chunk's gradient enters the momentum buffers in the last epilogue
     ca.mom = s->Mm[0];
     ca.beta = c.momentum;
+    ca.mom_write = read_mom ? 0 : 1;
   }
   ttt_status r = contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
   if (r != TTT_OK || !g32) return r;
-  ca.mom = nullptr;
+  if (!read_mom) ca.mom = nullptr;
   // the X-orientation sum keeps its own running sum across the chunk's token blocks (in
   // g32 itself: each element is read and written by the same thread)
   return contract_all(s, ca, g32, false, first, last, st, false, g32);
@@ -1031,7 +1036,8 @@ ttt_status chunk_backward(ttt_state* s, const void* q, const void* k, const void
   // 1. the chunk's update again: gradient (and G in the X orientation), Newton-Schulz with
   //    its iterates kept, U in the weight orientation
   for (int64_t o = 0; o < ch; o += D.sb)
-    if ((r = grad_rows(s, block(o), o == 0, o + D.sb >= ch, st, muon ? b.g32 : nullptr)) != TTT_OK)
+    if ((r = grad_rows(s, block(o), o == 0, o + D.sb >= ch, st, muon ? b.g32 : nullptr,
+                       true)) != TTT_OK)
       return r;
   if (muon && (r = newton_schulz(s, st, b.xit)) != TTT_OK) return r;
   const int64_t sn = weights_numel(D);
@@ -1070,12 +1076,28 @@ ttt_status chunk_backward(ttt_state* s, const void* q, const void* k, const void
     xoff += (int64_t)D.P * D.d * D.n;
   }
   STAGED(TTT_STAGE_RENORM, launch_step_bwd(sb, st));
-  // 3. Newton-Schulz backward (or the plain step's dG = dU), planes for the products
-  if (muon) {
-    if ((r = ns_backward(s, st)) != TTT_OK) return r;
-  } else {
+  // 3. Newton-Schulz backward (or the plain step's dG = dU), planes for the products.
+  //    With momentum the step's input is M' = beta M + g: the cotangent given for the
+  //    buffer after the chunk joins dG, which reaches the gradient whole and the buffer
+  //    before the chunk (dw's second half, in place) times beta.
+  if (muon && (r = ns_backward(s, st)) != TTT_OK) return r;
+  float* const dg = muon ? b.dg32 : b.du;
+  if (D.mom) {
+    MomBwdArgs mb{};
+    mb.P = D.P; mb.nm = D.nm; mb.beta = c.momentum;
+    int64_t moff = sn, xo = 0;
+    for (int m = 0; m < D.nm; ++m) {
+      MomBwdMat& M = mb.m[m];
+      M.dg = dg + xo; M.dm = dw + moff;
+      M.rows = D.rows[m]; M.cols = D.cols[m]; M.tr = D.tr[m];
+      moff += (int64_t)D.P * D.rows[m] * D.cols[m];
+      xo += (int64_t)D.P * D.d * D.n;
+    }
+    STAGED(TTT_STAGE_RENORM, launch_mom_bwd(mb, st));
+  }
+  if (!muon || D.mom) {
     SplitArgs sa{};
-    sa.x = b.du; sa.x_zstride = (int64_t)D.d * D.n; sa.n = D.d; sa.d = D.n;
+    sa.x = dg; sa.x_zstride = (int64_t)D.d * D.n; sa.n = D.d; sa.d = D.n;
     sa.out = pbuf(b.dgp, D.gp, (int64_t)D.nm * D.P * D.d * D.n, (int64_t)D.d * D.n, D.n);
     STAGED(TTT_STAGE_SPLIT, launch_split(sa, D.nm * D.P, st));
   }
@@ -1372,10 +1394,10 @@ ttt_status ttt_chunk_backward(ttt_state* s, const void* q, const void* k, const 
       (r = check_ptr(deta, "deta")))
     return r;
   const ttt_config& c = s->cfg;
-  if (s->resident || c.fw != TTT_FW_SWIGLU || c.loss != TTT_LOSS_DOT || c.momentum > 0.f)
+  if (s->resident || c.fw != TTT_FW_SWIGLU || c.loss != TTT_LOSS_DOT)
     return fail(TTT_E_UNSUPPORTED,
                 "the chunk backward serves the SwiGLU net with the inner-product loss, on the "
-                "staged path, with no momentum");
+                "staged path");
   hipStream_t st = static_cast<hipStream_t>(stream);
   s->last = st;
   return chunk_backward(s, q, k, v, eta, dout, dw, dq, dk, dv, deta, st);

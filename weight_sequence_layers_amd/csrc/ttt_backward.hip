@@ -311,6 +311,55 @@ __global__ __launch_bounds__(256) void k_ns_fin(NsFinArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------ momentum
+// One workgroup per 32 x 32 tile of a matrix's weight orientation.  Where the X orientation
+// is the transpose, the tile of dm passes through LDS so that both sides read and write
+// along their own rows.  Every element is read and written by one thread per phase.
+constexpr int MOM_TILE = 32;
+
+__global__ __launch_bounds__(256) void k_mom_bwd(MomBwdArgs a) {
+  const MomBwdMat& M = a.m[blockIdx.z];
+  const int tiles_c = (M.cols + MOM_TILE - 1) / MOM_TILE;
+  if ((int)blockIdx.x >= ((M.rows + MOM_TILE - 1) / MOM_TILE) * tiles_c) return;
+  const int r0 = ((int)blockIdx.x / tiles_c) * MOM_TILE;
+  const int c0 = ((int)blockIdx.x % tiles_c) * MOM_TILE;
+  const int64_t base = (int64_t)blockIdx.y * M.rows * M.cols;
+  const int tx = threadIdx.x % MOM_TILE, ty = threadIdx.x / MOM_TILE;
+  constexpr int STEP = 256 / MOM_TILE;
+  if (!M.tr) {
+    for (int i = ty; i < MOM_TILE; i += STEP) {
+      const int r = r0 + i, c = c0 + tx;
+      if (r < M.rows && c < M.cols) {
+        const int64_t o = base + (int64_t)r * M.cols + c;
+        const float t = M.dg[o] + M.dm[o];
+        M.dg[o] = t;
+        M.dm[o] = a.beta * t;
+      }
+    }
+    return;
+  }
+  __shared__ float sh[MOM_TILE][MOM_TILE + 1];
+  for (int i = ty; i < MOM_TILE; i += STEP) {      // sh[i][j] = dm[r0 + i][c0 + j]
+    const int r = r0 + i, c = c0 + tx;
+    sh[i][tx] = (r < M.rows && c < M.cols) ? M.dm[base + (int64_t)r * M.cols + c] : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < MOM_TILE; i += STEP) {      // X row c0 + i, column r0 + tx
+    const int c = c0 + i, r = r0 + tx;
+    if (r < M.rows && c < M.cols) {
+      const int64_t o = base + (int64_t)c * M.rows + r;
+      const float t = M.dg[o] + sh[tx][i];
+      M.dg[o] = t;
+      sh[tx][i] = t;
+    }
+  }
+  __syncthreads();
+  for (int i = ty; i < MOM_TILE; i += STEP) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < M.rows && c < M.cols) M.dm[base + (int64_t)r * M.cols + c] = a.beta * sh[i][tx];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_add3(Add3Args a) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i * 4 < a.n;
        i += (int64_t)gridDim.x * 256) {
@@ -395,6 +444,17 @@ hipError_t launch_ns_fin(const NsFinArgs& a, int Z, hipStream_t s) {
   if (Z == 0 || a.per == 0) return hipSuccess;
   const int blocks = (int)std::min<int64_t>(256, (a.per / 8 + 255) / 256);
   hipLaunchKernelGGL(k_ns_fin, dim3(blocks, Z), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mom_bwd(const MomBwdArgs& a, hipStream_t s) {
+  if (a.P == 0 || a.nm == 0) return hipSuccess;
+  int tiles = 0;
+  for (int m = 0; m < a.nm; ++m)
+    tiles = std::max(tiles, ((a.m[m].rows + MOM_TILE - 1) / MOM_TILE) *
+                                ((a.m[m].cols + MOM_TILE - 1) / MOM_TILE));
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_mom_bwd, dim3(tiles, a.P, a.nm), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -153,6 +153,20 @@ struct NsFinArgs {
   PlaneBuf pout;        // planes of dG
 };
 
+// Momentum's backward, per matrix and problem: t = dg + dm, dg <- t, dm <- beta t, with dg
+// in the X orientation and dm in the weight orientation [rows][cols] (the X orientation
+// is [cols][rows] where tr).
+struct MomBwdMat {
+  float* dg;
+  float* dm;
+  int rows, cols, tr;
+};
+struct MomBwdArgs {
+  MomBwdMat m[3];
+  int P, nm;
+  float beta;
+};
+
 // out[i] = x[i] + y[i] + w[i] over n values (any of y, w may be null).
 struct Add3Args {
   const float *x, *y, *w;
@@ -182,10 +196,13 @@ struct ContractArgs {
   int64_t gpart_stride;
   int ksplit, kchunk;
   int nz;          // nm * P of the launch (set by launch_contract)
-  // momentum: with mom, the last epilogue replaces the sum x by beta M + x and stores it in
-  // M (weight orientation, like U) before using it
+  // momentum: with mom, the last epilogue replaces the sum x by beta M + x and, with
+  // mom_write, stores it in M before using it (the backward's recompute reads M only).  M
+  // is in the weight orientation: bit m of mom_tr set where matrix m's weight is the
+  // transpose of its X orientation (tr_mask may differ: an X-orientation output)
   float* mom;
   float beta;
+  int mom_tr, mom_write;
 };
 
 // Newton-Schulz stages on Z = nm*P matrices X [M x N] (M <= N).
@@ -275,6 +292,7 @@ hipError_t launch_step_bwd(const StepBwdArgs& a, hipStream_t s);
 hipError_t launch_gemm2(const Gemm2Args& a, bool bcols, hipStream_t s, bool sym = false);
 hipError_t launch_ns_fin(const NsFinArgs& a, int Z, hipStream_t s);
 hipError_t launch_add3(const Add3Args& a, hipStream_t s);
+hipError_t launch_mom_bwd(const MomBwdArgs& a, hipStream_t s);
 int gemm2_tiles(int M, int N);
 // token ranges a contraction of `tiles` output tiles per matrix over nz matrices may split
 // into (the host sizes the partial-sum buffer with it)

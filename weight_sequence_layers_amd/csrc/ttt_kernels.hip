@@ -346,8 +346,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
       const int64_t widx = tr ? base + (int64_t)col * M + row : off;   // weight orientation
       if (accum) x += a.G[off];
       if (last && a.mom) {
-        x = fmaf(a.beta, a.mom[widx], x);
-        a.mom[widx] = x;
+        const int64_t midx = ((a.mom_tr >> m) & 1) ? base + (int64_t)col * M + row : off;
+        x = fmaf(a.beta, a.mom[midx], x);
+        if (a.mom_write) a.mom[midx] = x;
       }
       if (!last) {
         gout[off] = x;
@@ -424,11 +425,12 @@ __global__ __launch_bounds__(CONTRACT_SUM_THREADS) void k_contract_sum(ContractA
       x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
     }
     if (a.last && a.mom) {
+      const int mtr = (a.mom_tr >> m) & 1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int64_t widx = tr ? base + (int64_t)(col + e) * M + row : off + e;
-        x[e] = fmaf(a.beta, a.mom[widx], x[e]);
-        a.mom[widx] = x[e];
+        const int64_t midx = mtr ? base + (int64_t)(col + e) * M + row : off + e;
+        x[e] = fmaf(a.beta, a.mom[midx], x[e]);
+        if (a.mom_write) a.mom[midx] = x[e];
       }
     }
     if (!a.last) {
