@@ -119,12 +119,15 @@ def test_chunk_backward_update_then_apply(act, ns, renorm):
     _check(cfg)
 
 
-@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
-def test_chunk_backward_two_token_blocks(order):
+@pytest.mark.parametrize("order,momentum", [("apply_then_update", 0.0),
+                                            ("update_then_apply", 0.0),
+                                            ("update_then_apply", 0.7)])
+def test_chunk_backward_two_token_blocks(order, momentum):
     # a chunk longer than one token block (65536 tokens): the recompute's two contractions
-    # keep separate running sums over the blocks, the backward's launches walk the blocks
+    # keep separate running sums over the blocks (the momentum buffer joins both at the
+    # last block), the backward's launches walk the blocks
     cfg = ti.Config("cbb", 1, 1, 66000, 66000, 64, 128, "swiglu", "dot", 5, True, "bf16",
-                    order, 97)
+                    order, 97, momentum=momentum)
     _check(cfg)
 
 
@@ -144,6 +147,14 @@ def test_chunk_backward_momentum(act, ns, renorm, order):
     cfg = ti.Config("cbm", 1, 2, 256, 128, 80, 176, "swiglu", "dot", ns, renorm, act, order,
                     98, lr=(0.8, 1.1, 0.9), weight_decay=0.02, momentum=0.6)
     _check(cfg)
+
+
+def test_chunk_backward_lm_chunk_momentum():
+    # the LaCT language-model layer's shape with heavy-ball momentum, chained over two
+    # chunks of 2048 tokens so that the second starts from a buffer that is not zero
+    lm = ti.CONFIGS["lm"]
+    cfg = lm.replace(name="lmm", seq_len=2 * lm.chunk, momentum=0.9)
+    _check(cfg, problems=[(1, 0), (2, 1)])
 
 
 def test_chunk_backward_refuses_other_configurations():
