@@ -33,9 +33,12 @@ def _cotangents(cfg, seed):
     return dO, bits, dWs
 
 
-def _gpu_backward(cfg, inp, dO, bits, dWs, planes=None, chunks=None):
+def _gpu_backward(cfg, inp, dO, bits, dWs, planes=None, update=None):
     """ttt_chunk_backward over the chunks of the sequence, last to first, each from the
-    state before its chunk (taken during a forward pass with ttt_get_state)."""
+    state before its chunk (taken during a forward pass with ttt_get_state). update: one
+    flag per chunk; a chunk that does not update is answered by ttt_sequence_forward_masked
+    and taken back by ttt_apply_backward, its weight gradient added to the state's
+    cotangent (its keys, values and step sizes get none)."""
     c = W.make_config(cfg, planes=planes, path="staged")
     q, k, v, eta, w0 = device_inputs(cfg, inp)
     st = W.ttt_init_state(c, w0)
@@ -44,10 +47,15 @@ def _gpu_backward(cfg, inp, dO, bits, dWs, planes=None, chunks=None):
     states = []
     out = torch.empty_like(q[:, :, :b]).contiguous()
     sl = lambda x, ci: x[:, :, ci * b:(ci + 1) * b].contiguous()
+    up = [True] * nc if update is None else [bool(u) for u in update]
     for ci in range(nc):
         _, flat = read_state(c, st)
         states.append(flat.clone())
-        W.ttt_chunk_forward(st, sl(q, ci), sl(k, ci), sl(v, ci), sl(eta, ci), out)
+        if up[ci]:
+            W.ttt_chunk_forward(st, sl(q, ci), sl(k, ci), sl(v, ci), sl(eta, ci), out)
+        else:
+            W.ttt_sequence_forward_masked(st, sl(q, ci), sl(k, ci), sl(v, ci), sl(eta, ci),
+                                          out, b, [False])
     dw = torch.from_numpy(np.concatenate([x.ravel() for x in dWs])).cuda()
     dOd = to_device(cfg, dO, bits)
     res = {n: np.zeros((cfg.batch, cfg.heads, cfg.seq_len, cfg.dim)) for n in ("dq", "dk", "dv")}
@@ -56,8 +64,16 @@ def _gpu_backward(cfg, inp, dO, bits, dWs, planes=None, chunks=None):
         W.ttt_set_state(st, states[ci])
         g = {n: torch.empty_like(sl(q, ci)) for n in ("dq", "dk", "dv")}
         deta = torch.empty_like(sl(eta, ci))
-        W.ttt_chunk_backward(st, sl(q, ci), sl(k, ci), sl(v, ci), sl(eta, ci), sl(dOd, ci), dw,
-                             g["dq"], g["dk"], g["dv"], deta)
+        if up[ci]:
+            W.ttt_chunk_backward(st, sl(q, ci), sl(k, ci), sl(v, ci), sl(eta, ci), sl(dOd, ci),
+                                 dw, g["dq"], g["dk"], g["dv"], deta)
+        else:
+            dwa = torch.empty_like(dw)
+            W.ttt_apply_backward(st, sl(q, ci), sl(dOd, ci), g["dq"], dwa)
+            dw += dwa
+            for n in ("dk", "dv"):
+                g[n].zero_()
+            deta.zero_()
         torch.cuda.synchronize()
         for n in ("dq", "dk", "dv"):
             res[n][:, :, ci * b:(ci + 1) * b] = g[n].float().cpu().numpy()
@@ -68,17 +84,17 @@ def _gpu_backward(cfg, inp, dO, bits, dWs, planes=None, chunks=None):
     return res
 
 
-def _check(cfg, planes=None, problems=None, seed=5):
+def _check(cfg, planes=None, problems=None, seed=5, update=None):
     inp = ti.make_inputs(cfg)
     dO, bits, dWs = _cotangents(cfg, seed)
-    got = _gpu_backward(cfg, inp, dO, bits, dWs, planes)
+    got = _gpu_backward(cfg, inp, dO, bits, dWs, planes, update)
     tol = TOL[cfg.act]
     probs = problems or [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
     worst = 0.0
     for (b, h) in probs:
         W0s = [w[h] for w in inp["w0"]]
         ref = orc.sequence_vjp(cfg, W0s, inp["q"][b, h], inp["k"][b, h], inp["v"][b, h],
-                               inp["eta"][b, h], dO[b, h], [x[b, h] for x in dWs])
+                               inp["eta"][b, h], dO[b, h], [x[b, h] for x in dWs], update)
         errs = {n: rel_err(got[n][b, h], r) for n, r in zip(("dq", "dk", "dv", "deta"), ref[:4])}
         errs.update({f"dW{m}": rel_err(got["dw"][m][b, h], r) for m, r in enumerate(ref[4])})
         print(f"{cfg.name} problem ({b},{h}): " +
@@ -106,6 +122,14 @@ def test_chunk_backward_chained_over_three_chunks():
     cfg = ti.Config("cbs", 1, 2, 384, 128, 64, 128, "swiglu", "dot", 5, True, "f32",
                     "apply_then_update", 93)
     _check(cfg)
+
+
+@pytest.mark.parametrize("order", ["apply_then_update", "update_then_apply"])
+def test_chunk_backward_chained_with_a_chunk_that_does_not_update(order):
+    # update flags (1, 0, 1): the middle chunk only answers its queries, and its backward is
+    # the apply step's alone
+    cfg = ti.Config("cbf", 1, 2, 384, 128, 64, 128, "swiglu", "dot", 5, True, "f32", order, 99)
+    _check(cfg, update=(1, 0, 1))
 
 
 @pytest.mark.parametrize("act,ns,renorm", [("f32", 5, True), ("bf16", 0, True), ("f32", 0, False)])
