@@ -435,15 +435,12 @@ ttt_status apply_rows(ttt_state* s, const Rows& R, hipStream_t st) {
 // Gradient of one token block; the contraction adds into G (first block writes it).
 // The chunk-summed contractions of one token block into G, and after the chunk's last
 // block into U (plain step; weight orientation) or the first Newton-Schulz input (muon).
-// ca holds the per-matrix operands and sizes.
-// gsum: the running sum over a chunk's token blocks in another buffer than the state's G
-// (a second contraction of the same blocks, interleaved with the first).
+// ca holds the per-matrix operands and sizes (and ca.g32, a copy of the final sum).
 ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool first,
-                        bool last, hipStream_t st, bool weight_orient = true,
-                        float* gsum = nullptr) {
+                        bool last, hipStream_t st) {
   const Dims& D = s->D;
   const int P = D.P, d = D.d;
-  float* const G = gsum ? gsum : s->G;
+  float* const G = s->G;
   ca.G = G;
   ca.accum_in = first ? 0 : 1;
   ca.last = last ? 1 : 0;
@@ -456,9 +453,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   ca.gpart = s->gpart;
   ca.gpart_stride = (int64_t)D.nm * P * d * D.n;
   ca.ksplit = s->ksplit;
-  const int wtr = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
-  ca.tr_mask = weight_orient ? wtr : 0;
-  ca.mom_tr = wtr;   // the momentum buffers keep the weight orientation
+  ca.tr_mask = D.tr[0] | (D.tr[1] << 1) | (D.tr[2] << 2);
   // operands of one launch share a plane count per side: group the matrices accordingly
   int m0 = 0;
   while (m0 < D.nm) {
@@ -470,7 +465,7 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
     if (s->gpart) cg.gpart = s->gpart + (int64_t)m0 * P * d * D.n;
     cg.U = U + (int64_t)m0 * P * d * D.n;
     if (ca.mom) cg.mom = ca.mom + (int64_t)m0 * P * d * D.n;
-    cg.mom_tr = ca.mom_tr >> m0;
+    if (ca.g32) cg.g32 = ca.g32 + (int64_t)m0 * P * d * D.n;
     if (ca.muon) cg.x.base = ca.x.base + (int64_t)m0 * P * ca.x.zstride;
     cg.part = s->part + (int64_t)m0 * P * s->part_n;
     cg.tr_mask = ca.tr_mask >> m0;
@@ -480,8 +475,9 @@ ttt_status contract_all(ttt_state* s, ContractArgs ca, float* U, bool muon, bool
   return TTT_OK;
 }
 
-// g32: also sum the step's input (the gradient, with momentum beta M + the gradient), in the
-// X orientation, into this fp32 buffer (the backward's Newton-Schulz scaling needs it).
+// g32: the last block's epilogue also stores the step's input (the gradient, with momentum
+// beta M + the gradient) in fp32 in the X orientation here (the backward's Newton-Schulz
+// scaling needs it).
 // read_mom: the momentum buffers are read, not replaced (the backward's recompute).
 ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStream_t st,
                      float* g32 = nullptr, bool read_mom = false) {
@@ -603,12 +599,8 @@ ttt_status grad_rows(ttt_state* s, const Rows& R, bool first, bool last, hipStre
     ca.beta = c.momentum;
     ca.mom_write = read_mom ? 0 : 1;
   }
-  ttt_status r = contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
-  if (r != TTT_OK || !g32) return r;
-  if (!read_mom) ca.mom = nullptr;
-  // the X-orientation sum keeps its own running sum across the chunk's token blocks (in
-  // g32 itself: each element is read and written by the same thread)
-  return contract_all(s, ca, g32, false, first, last, st, false, g32);
+  ca.g32 = g32;
+  return contract_all(s, ca, s->U, c.ns_steps > 0, first, last, st);
 }
 
 // keep: write iterate it + 1 to keep[it + 1] (kept for the backward) instead of the

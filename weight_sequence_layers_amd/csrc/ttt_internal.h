@@ -197,12 +197,14 @@ struct ContractArgs {
   int ksplit, kchunk;
   int nz;          // nm * P of the launch (set by launch_contract)
   // momentum: with mom, the last epilogue replaces the sum x by beta M + x and, with
-  // mom_write, stores it in M before using it (the backward's recompute reads M only).  M
-  // is in the weight orientation: bit m of mom_tr set where matrix m's weight is the
-  // transpose of its X orientation (tr_mask may differ: an X-orientation output)
+  // mom_write, stores it in M (weight orientation, like U) before using it (the backward's
+  // recompute reads M only)
   float* mom;
   float beta;
-  int mom_tr, mom_write;
+  int mom_write;
+  // with g32, the last epilogue also stores the final sum (after momentum) in fp32 in the X
+  // orientation [nm][P][M][N] (the backward's Newton-Schulz scaling reads it)
+  float* g32;
 };
 
 // Newton-Schulz stages on Z = nm*P matrices X [M x N] (M <= N).

@@ -346,10 +346,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_contract(ContractArgs a) {
       const int64_t widx = tr ? base + (int64_t)col * M + row : off;   // weight orientation
       if (accum) x += a.G[off];
       if (last && a.mom) {
-        const int64_t midx = ((a.mom_tr >> m) & 1) ? base + (int64_t)col * M + row : off;
-        x = fmaf(a.beta, a.mom[midx], x);
-        if (a.mom_write) a.mom[midx] = x;
+        x = fmaf(a.beta, a.mom[widx], x);
+        if (a.mom_write) a.mom[widx] = x;
       }
+      if (last && a.g32) a.g32[off] = x;
       if (!last) {
         gout[off] = x;
       } else if (a.muon) {
@@ -425,13 +425,17 @@ __global__ __launch_bounds__(CONTRACT_SUM_THREADS) void k_contract_sum(ContractA
       x[4] += w.x; x[5] += w.y; x[6] += w.z; x[7] += w.w;
     }
     if (a.last && a.mom) {
-      const int mtr = (a.mom_tr >> m) & 1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int64_t midx = mtr ? base + (int64_t)(col + e) * M + row : off + e;
-        x[e] = fmaf(a.beta, a.mom[midx], x[e]);
-        if (a.mom_write) a.mom[midx] = x[e];
+        const int64_t widx = tr ? base + (int64_t)(col + e) * M + row : off + e;
+        x[e] = fmaf(a.beta, a.mom[widx], x[e]);
+        if (a.mom_write) a.mom[widx] = x[e];
       }
+    }
+    if (a.last && a.g32) {
+      float4* dst = reinterpret_cast<float4*>(a.g32 + off);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
     }
     if (!a.last) {
       float4* dst = reinterpret_cast<float4*>(a.G + off);
