@@ -245,7 +245,8 @@ def bench_chunk_backward(args, cfg, planes):
         "dtype": "bf16" if cfg.act == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"{cfg.name} (one chunk of {b} tokens, {P} problems)",
                    "bf16_planes_apply_grad_ns": list(planes[:3]),
-                   "ns_one_plane_iterations": [i for i in range(8) if (planes[3] >> i) & 1]},
+                   "ns_one_plane_iterations": [i for i in range(8) if (planes[3] >> i) & 1],
+                   **({"momentum": cfg.momentum} if cfg.momentum else {})},
         "tflops_algorithmic": round(total / dt / 1e12, 2),
         "pct_bf16_peak_algorithmic": round(100 * total / dt / 1e12 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -524,6 +525,8 @@ def main():
     ap.add_argument("--lr", default=None,
                     help="comma-separated step sizes per matrix (state order); default 1")
     ap.add_argument("--weight-decay", type=float, default=0.0)
+    ap.add_argument("--momentum", type=float, default=0.0,
+                    help="heavy-ball coefficient over chunk gradients (the workload's is 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--apply-backward", action="store_true",
                     help="time the apply-step backward on the workload's first chunk instead")
@@ -557,6 +560,8 @@ def main():
     if args.lr or args.weight_decay:
         cfg = cfg.replace(lr=tuple(float(x) for x in (args.lr or "").split(",") if x),
                           weight_decay=args.weight_decay)
+    if args.momentum:
+        cfg = cfg.replace(momentum=args.momentum)
     planes = tuple(int(x) for x in args.planes.split(",")) if args.planes else W.PRECISION[cfg.name]
     if args.apply_backward:
         bench_apply_backward(args, cfg, planes)
@@ -663,7 +668,8 @@ def main():
                    "bf16_planes_apply_grad_ns": list(planes[:3]), "ns_one_plane_iterations": [i for i in range(8) if (planes[3] >> i) & 1],
                    "replay": bool(args.replay),
                    **({"lr": list(cfg.step_sizes()), "weight_decay": cfg.weight_decay}
-                      if (cfg.lr or cfg.weight_decay) else {})},
+                      if (cfg.lr or cfg.weight_decay) else {}),
+                   **({"momentum": cfg.momentum} if cfg.momentum else {})},
         "source_digest": source_digest(),
         "layer_tflops_algorithmic": round(tf_layer, 2),
         "pct_bf16_peak_algorithmic": round(100 * tf_layer / PEAK_BF16_TFLOPS, 2),
