@@ -525,6 +525,8 @@ def main():
     ap.add_argument("--lr", default=None,
                     help="comma-separated step sizes per matrix (state order); default 1")
     ap.add_argument("--weight-decay", type=float, default=0.0)
+    ap.add_argument("--batch", type=int, default=None,
+                    help="another batch size than the workload's (more problems per launch)")
     ap.add_argument("--momentum", type=float, default=0.0,
                     help="heavy-ball coefficient over chunk gradients (the workload's is 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -562,6 +564,8 @@ def main():
                           weight_decay=args.weight_decay)
     if args.momentum:
         cfg = cfg.replace(momentum=args.momentum)
+    if args.batch:
+        cfg = cfg.replace(batch=args.batch)
     planes = tuple(int(x) for x in args.planes.split(",")) if args.planes else W.PRECISION[cfg.name]
     if args.apply_backward:
         bench_apply_backward(args, cfg, planes)
@@ -652,7 +656,10 @@ def main():
     achieved = per_launch / avg_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": recorded_traffic(cfg.name, dom), "kernel": dom,
+                # the recorded bytes hold for the workload as profiled, with no overrides
+                "traffic": None if (args.batch or args.momentum or args.lr or args.weight_decay
+                                    or args.planes) else recorded_traffic(cfg.name, dom),
+                "kernel": dom,
                 "avg_launch_us": round(avg_s * 1e6, 2),
                 "launches": n_dom}
     res = {
