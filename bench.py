@@ -417,6 +417,14 @@ def bench_block(args, cfg, planes):
     print(json.dumps(res), flush=True)
 
 
+def traffic_for(args, workload: str, stage: str):
+    """recorded_traffic for a run of the workload as profiled; None when the command line
+    changes its kernels' work (batch, momentum, step sizes, decay, planes)."""
+    if args.batch or args.momentum or args.lr or args.weight_decay or args.planes:
+        return None
+    return recorded_traffic(workload, stage)
+
+
 def recorded_traffic(workload: str, stage: str):
     """HBM bytes per launch of `stage` from profiles/<workload>_traffic.md, if that summary
     was taken from the current kernel sources; else None."""
@@ -656,10 +664,7 @@ def main():
     achieved = per_launch / avg_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                # the recorded bytes hold for the workload as profiled, with no overrides
-                "traffic": None if (args.batch or args.momentum or args.lr or args.weight_decay
-                                    or args.planes) else recorded_traffic(cfg.name, dom),
-                "kernel": dom,
+                "traffic": traffic_for(args, cfg.name, dom), "kernel": dom,
                 "avg_launch_us": round(avg_s * 1e6, 2),
                 "launches": n_dom}
     res = {

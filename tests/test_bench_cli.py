@@ -50,3 +50,17 @@ def test_chunk_backward_flop_accounting():
     total = sum(bench.chunk_backward_flops(cfg).values())
     expect = P * (58.0 * b * d * dh + 15 * (14.0 * d * d * dh + 8.0 * d ** 3))
     assert abs(total - expect) <= 1e-9 * expect
+
+
+def test_recorded_traffic_only_for_the_workload_as_profiled():
+    # profiles/lm_traffic.md holds the bytes of the default LM run; a command line that
+    # changes the kernels' work gets none
+    import argparse
+    sys.path.insert(0, ROOT)
+    import bench
+    plain = argparse.Namespace(batch=None, momentum=0.0, lr=None, weight_decay=0.0, planes=None)
+    assert bench.traffic_for(plain, "lm", "ns_update") == bench.recorded_traffic("lm", "ns_update")
+    for kw in (dict(batch=8), dict(momentum=0.9), dict(lr="0.5"), dict(weight_decay=0.1),
+               dict(planes="1,1,1,0")):
+        assert bench.traffic_for(argparse.Namespace(**{**vars(plain), **kw}), "lm",
+                                 "ns_update") is None
