@@ -197,13 +197,15 @@ def test_chunk_backward_refuses_other_configurations():
         st.destroy()
 
 
-@pytest.mark.parametrize("momentum", [0.0, 0.5])
-def test_chunk_backward_update_then_apply_leaves_the_state(momentum):
+@pytest.mark.parametrize("order,momentum", [("update_then_apply", 0.0),
+                                            ("update_then_apply", 0.5),
+                                            ("apply_then_update", 0.5)])
+def test_chunk_backward_leaves_the_state(order, momentum):
     # the update-then-apply backward forms the updated state in place of the state and
-    # restores it, and reads the momentum buffers without replacing them: the state (and
-    # its planes, through a forward call) is bitwise unchanged
+    # restores it, and both orders read the momentum buffers without replacing them: the
+    # state (and its planes, through a forward call) is bitwise unchanged
     cfg = ti.Config("cbu3", 1, 2, 128, 128, 64, 128, "swiglu", "dot", 5, True, "bf16",
-                    "update_then_apply", 96, momentum=momentum)
+                    order, 96, momentum=momentum)
     c = W.make_config(cfg, path="staged")
     inp = ti.make_inputs(cfg)
     q, k, v, eta, w0 = device_inputs(cfg, inp)
