@@ -4,7 +4,8 @@ and the state cotangent before the chunk, for the SwiGLU net with the inner-prod
 under both orders, with and without Muon and the row renorm, with step sizes, weight decay
 and momentum, fp32 and bf16,
 at ragged small sizes, at the LaCT language-model chunk, and chained over a short sequence
-(each call from the state before its chunk).  Errors are max relative errors
+(each call from the state before its chunk; a chunk that does not update taken back by the
+apply backward alone).  Errors are max relative errors
 |x - y|_inf / |y|_inf per tensor; bars 1e-4 (fp32) and 2e-2 (bf16)."""
 import numpy as np
 import pytest
